@@ -1,0 +1,145 @@
+/*
+ * ckks_gpu.h -- C ABI of the MI355X (gfx950) RNS-CKKS arithmetic core.
+ *
+ * Scope: the data-parallel hot path of RNS-CKKS as described by the Kestrel
+ * FHE relay pages: batched negacyclic NTT/iNTT over many 60-bit primes,
+ * ciphertext-ciphertext multiply with relinearisation, rescale, Galois
+ * rotation/conjugation with hybrid key switching, and the baby-step
+ * giant-step (BSGS) plaintext-matrix times ciphertext transform that
+ * coeff_to_slot / slot_to_coeff are made of.
+ *
+ * Conventions shared by every call
+ *  - Ring Z_q[X]/(X^n + 1), n a power of two (2048 or 65536 here).
+ *  - Chain: the L + K smallest primes q in (2^59, 2^60) with q = 1 (mod 2n),
+ *    ascending; the first L are the main primes q_0..q_{L-1}, the next K the
+ *    special primes p_0..p_{K-1} used by key switching.  Prime index g in
+ *    [0, L+K) names one of them.
+ *  - psi_g = the smallest primitive 2n-th root of unity modulo prime g.
+ *  - NTT (evaluation) domain: A_j = sum_i a_i psi^(i(2j+1)) mod q, j in
+ *    natural order.  Ciphertexts, keys and plaintexts are passed in this domain.
+ *  - A polynomial at level l is l limbs of n uint64 residues, limb-major
+ *    ([l][n], limb i modulo q_i); a ciphertext is [2][l][n]; a batch of B
+ *    ciphertexts is [B][2][l][n].  Every residue is fully reduced to [0, q)
+ *    on input and is returned fully reduced.
+ *  - Switching key: [dnum][2][L+K][n]; row (j, 0) = b_j, row (j, 1) = a_j,
+ *    limb g modulo prime g (main primes, then special primes).  Digit j
+ *    covers main primes [j*alpha, min((j+1)*alpha, l)), alpha = ceil(L/dnum).
+ *  - Rotation left by k slots uses Galois element 5^k mod 2n; conjugation
+ *    uses 2n - 1.
+ *
+ * Memory and streams
+ *  - Data pointers are DEVICE pointers on the context's device, allocated and
+ *    owned by the caller (8-byte aligned).  Pointer-array arguments
+ *    (BSGS keys) are HOST arrays of device pointers.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue work and return; nothing synchronises with the host, except that
+ *    the first call at a new level builds that level's constant tables
+ *    (blocking upload, done once per level and context).
+ *  - Workspace: ops that need scratch take (ws, ws_bytes); query the size with
+ *    ckks_workspace_size.  The caller owns it; concurrent calls need distinct
+ *    workspaces.  No call allocates device memory after context creation,
+ *    apart from the one-time level tables above.
+ *  - in == out aliasing is allowed for the NTT calls only.
+ *
+ * Errors: every call returns CKKS_OK (0) or a negative CKKS_E* code; arguments
+ * are validated before any launch; nothing is printed.
+ */
+#ifndef CKKS_GPU_H
+#define CKKS_GPU_H
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CKKS_OK 0
+#define CKKS_EINVAL (-1)     /* bad argument (null pointer, size out of range) */
+#define CKKS_ELEVEL (-2)     /* level out of range for this context / op      */
+#define CKKS_ENOMEM (-3)     /* device allocation failed (context creation)   */
+#define CKKS_EHIP (-4)       /* a HIP runtime call or kernel launch failed     */
+#define CKKS_EALIGN (-5)     /* pointer not 8-byte aligned                     */
+#define CKKS_EWORKSPACE (-6) /* workspace missing or smaller than required     */
+#define CKKS_EUNSUPPORTED (-7) /* ring degree / parameter not supported        */
+
+typedef struct ckks_ctx ckks_ctx;
+
+typedef struct {
+    uint32_t n;    /* ring degree: 2048 or 65536                          */
+    uint32_t L;    /* number of main primes (top level)                    */
+    uint32_t K;    /* number of special primes (0: no key switching)      */
+    uint32_t dnum; /* number of key-switching digits (>= 1 when K > 0)    */
+} ckks_params;
+
+/* Create a context on HIP device `device`: generates the chain primes and
+ * roots (Kestrel relay README section 1 / article section 4.1 parameters:
+ * n = 2048, 60-bit primes, 112 or 2100 of them), and uploads twiddle and
+ * base-conversion tables.  Returns CKKS_EUNSUPPORTED for unsupported n. */
+int ckks_ctx_create(ckks_ctx **out, const ckks_params *params, int device);
+void ckks_ctx_destroy(ckks_ctx *ctx);
+/* Copy the chain primes and their psi to host arrays of L+K entries (either may be NULL). */
+int ckks_ctx_primes(const ckks_ctx *ctx, uint64_t *host_primes, uint64_t *host_psi);
+const char *ckks_strerror(int code);
+
+/* Workspace sizes.  op: one of the CKKS_OP_* values; batch = ciphertexts per
+ * call; level = l; for CKKS_OP_BSGS, bs and gs are the baby/giant step counts
+ * (ignored otherwise). */
+#define CKKS_OP_RELIN 1
+#define CKKS_OP_ROTATE 2
+#define CKKS_OP_RESCALE 3
+#define CKKS_OP_BSGS 4
+int ckks_workspace_size(const ckks_ctx *ctx, int op, int batch, int level, int bs, int gs, size_t *bytes);
+
+/* Forward / inverse negacyclic NTT, in place, of `count` polynomials of
+ * `nlimbs` limbs each ([count][nlimbs][n]); limb r uses prime index
+ * first_prime + r.  The "NTT/INTT" multiply accelerator of the Kestrel
+ * article's technique table; natural order in and out. */
+int ckks_ntt_fwd(const ckks_ctx *ctx, uint64_t *x, int count, int first_prime, int nlimbs, void *stream);
+int ckks_ntt_inv(const ckks_ctx *ctx, uint64_t *x, int count, int first_prime, int nlimbs, void *stream);
+
+/* Pointwise product in the NTT domain (the middle step of an NTT-based
+ * negacyclic polynomial multiply): out = a (.) b limb by limb, layouts as
+ * ckks_ntt_fwd ([count][nlimbs][n], limb r modulo prime first_prime + r).
+ * out may alias a or b. */
+int ckks_pointwise_mul(const ckks_ctx *ctx, const uint64_t *a, const uint64_t *b, uint64_t *out, int count,
+                       int first_prime, int nlimbs, void *stream);
+
+/* Ciphertext-ciphertext multiply with relinearisation ("every multiplication
+ * grows the noise", Kestrel article wall 2):  for each of `batch` pairs,
+ * (d0, d1, d2) = (a0 b0, a0 b1 + a1 b0, a1 b1) and
+ * out = (d0, d1) + KeySwitch(d2, rlk).  a, b, out: [batch][2][level][n];
+ * rlk: switching key for s^2. */
+int ckks_mul_tensor_relin(const ckks_ctx *ctx, const uint64_t *a, const uint64_t *b, const uint64_t *rlk,
+                          uint64_t *out, int batch, int level, void *ws, size_t ws_bytes, void *stream);
+
+/* Rescale: drop the last prime q_{l-1} with rounding, out = round(c / q_{l-1})
+ * ("each rescale consumes one prime", Kestrel article wall 2).
+ * in: [batch][2][level][n]; out: [batch][2][level-1][n]. */
+int ckks_rescale(const ckks_ctx *ctx, const uint64_t *in, uint64_t *out, int batch, int level, void *ws,
+                 size_t ws_bytes, void *stream);
+
+/* Galois automorphism X -> X^g followed by hybrid key switching back to s
+ * (Galois rotation / conjugation of the Kestrel article's technique table):
+ * out = (sigma_g(c0), 0) + KeySwitch(sigma_g(c1), key).  g odd, in [1, 2n).
+ * in, out: [batch][2][level][n] (must not alias). */
+int ckks_rotate(const ckks_ctx *ctx, const uint64_t *in, uint64_t *out, int batch, int level, uint32_t galois_elt,
+                const uint64_t *key, void *ws, size_t ws_bytes, void *stream);
+
+/* Baby-step giant-step plaintext-matrix x ciphertext (matmul2 with BB x GG,
+ * Kestrel article technique table and section 4.4; coeff_to_slot /
+ * slot_to_coeff are this transform):
+ *   y = sum_{g<gs} rot_{g*bs}( sum_{b<bs} diags[g][b] (.) rot_b(x) ),
+ * then, if do_rescale, out = Rescale(y).  diags: [gs][bs][level][n]
+ * (encoded pre-rotated diagonals, NTT domain); baby_keys[b] is the key of
+ * rotation by b (b = 1..bs-1, entry 0 ignored); giant_keys[g] the key of
+ * rotation by g*bs (g = 1..gs-1, entry 0 ignored).  in: [batch][2][level][n];
+ * out: [batch][2][level - do_rescale][n]. */
+int ckks_bsgs_linear_transform(const ckks_ctx *ctx, const uint64_t *in, uint64_t *out, int batch, int level,
+                               const uint64_t *diags, int bs, int gs, const uint64_t *const *baby_keys,
+                               const uint64_t *const *giant_keys, int do_rescale, void *ws, size_t ws_bytes,
+                               void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,155 @@
+"""Thin Python binding over the C ABI (include/ckks_gpu.h).
+
+Argument marshalling only: tensors are device tensors (torch.uint64, or
+int64 holding the same bits) in the layouts the C header documents; every
+step of the computation runs in the HIP library.  Calls are enqueued on the
+current torch stream.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import torch
+
+from . import _native as nat
+
+U64 = torch.uint64
+
+
+def _ptr(t: torch.Tensor) -> int:
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    if t.dtype not in (torch.uint64, torch.int64):
+        raise ValueError("expected 64-bit residues")
+    return t.data_ptr()
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+class Context:
+    """Parameter set + device tables: n, L main primes, K special primes, dnum digits."""
+
+    def __init__(self, n: int, L: int, K: int = 0, dnum: int = 1, device: int = 0):
+        self.n, self.L, self.K, self.dnum, self.device = n, L, K, dnum, device
+        self.alpha = (L + dnum - 1) // dnum
+        h = C.c_void_p()
+        nat.check(nat.lib().ckks_ctx_create(C.byref(h), C.byref(nat.Params(n, L, K, dnum)), device),
+                  "ckks_ctx_create")
+        self._h = h
+        import numpy as np
+        self.primes = np.zeros(L + K, dtype=np.uint64)
+        self.psi = np.zeros(L + K, dtype=np.uint64)
+        nat.check(nat.lib().ckks_ctx_primes(h, self.primes.ctypes.data, self.psi.ctypes.data), "ckks_ctx_primes")
+        self._ws = None
+
+    def close(self):
+        if getattr(self, "_h", None):
+            nat.lib().ckks_ctx_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def handle(self):
+        return self._h
+
+    # ------------------------------------------------------------ workspace
+    def workspace_size(self, op: str, batch: int, level: int, bs: int = 0, gs: int = 0) -> int:
+        out = C.c_size_t()
+        nat.check(nat.lib().ckks_workspace_size(self._h, nat.OPS[op], batch, level, bs, gs, C.byref(out)),
+                  "ckks_workspace_size")
+        return out.value
+
+    def workspace(self, nbytes: int) -> torch.Tensor:
+        """A cached device buffer of at least nbytes (grown on demand)."""
+        words = (nbytes + 7) // 8
+        if self._ws is None or self._ws.numel() < words:
+            self._ws = torch.empty(max(words, 1), dtype=U64, device=f"cuda:{self.device}")
+        return self._ws
+
+    def _ws_for(self, op, batch, level, bs=0, gs=0, ws=None):
+        need = self.workspace_size(op, batch, level, bs, gs)
+        if ws is None:
+            ws = self.workspace(need)
+        return ws, need
+
+    # ------------------------------------------------------------ ops
+    def ntt_fwd(self, x: torch.Tensor, first_prime: int = 0) -> torch.Tensor:
+        count, nl = x.numel() // (x.shape[-1] * x.shape[-2]), x.shape[-2]
+        nat.check(nat.lib().ckks_ntt_fwd(self._h, _ptr(x), count, first_prime, nl, _stream()), "ckks_ntt_fwd")
+        return x
+
+    def ntt_inv(self, x: torch.Tensor, first_prime: int = 0) -> torch.Tensor:
+        count, nl = x.numel() // (x.shape[-1] * x.shape[-2]), x.shape[-2]
+        nat.check(nat.lib().ckks_ntt_inv(self._h, _ptr(x), count, first_prime, nl, _stream()), "ckks_ntt_inv")
+        return x
+
+    def pointwise_mul(self, a, b, out=None, first_prime: int = 0):
+        out = torch.empty_like(a) if out is None else out
+        nl = a.shape[-2]
+        count = a.numel() // (a.shape[-1] * nl)
+        nat.check(nat.lib().ckks_pointwise_mul(self._h, _ptr(a), _ptr(b), _ptr(out), count, first_prime, nl,
+                                               _stream()), "ckks_pointwise_mul")
+        return out
+
+    def mul_tensor_relin(self, a, b, rlk, out=None, ws=None):
+        B, _, l, n = a.shape
+        out = torch.empty_like(a) if out is None else out
+        ws, need = self._ws_for("relin", B, l, ws=ws)
+        nat.check(nat.lib().ckks_mul_tensor_relin(self._h, _ptr(a), _ptr(b), _ptr(rlk), _ptr(out), B, l,
+                                                  _ptr(ws), ws.numel() * 8, _stream()), "ckks_mul_tensor_relin")
+        return out
+
+    def rescale(self, x, out=None, ws=None):
+        B, _, l, n = x.shape
+        out = torch.empty((B, 2, l - 1, n), dtype=x.dtype, device=x.device) if out is None else out
+        ws, need = self._ws_for("rescale", B, l, ws=ws)
+        nat.check(nat.lib().ckks_rescale(self._h, _ptr(x), _ptr(out), B, l, _ptr(ws), ws.numel() * 8, _stream()),
+                  "ckks_rescale")
+        return out
+
+    def rotate(self, x, galois_elt: int, key, out=None, ws=None):
+        B, _, l, n = x.shape
+        out = torch.empty_like(x) if out is None else out
+        ws, need = self._ws_for("rotate", B, l, ws=ws)
+        nat.check(nat.lib().ckks_rotate(self._h, _ptr(x), _ptr(out), B, l, galois_elt, _ptr(key), _ptr(ws),
+                                        ws.numel() * 8, _stream()), "ckks_rotate")
+        return out
+
+    def bsgs_linear_transform(self, x, diags, bs: int, gs: int, baby_keys, giant_keys, do_rescale=True,
+                              out=None, ws=None):
+        B, _, l, n = x.shape
+        lo = l - 1 if do_rescale else l
+        out = torch.empty((B, 2, lo, n), dtype=x.dtype, device=x.device) if out is None else out
+        ws, need = self._ws_for("bsgs", B, l, bs, gs, ws=ws)
+        bk = (C.c_void_p * bs)(*[None if k is None else _ptr(k) for k in baby_keys])
+        gk = (C.c_void_p * gs)(*[None if k is None else _ptr(k) for k in giant_keys])
+        nat.check(nat.lib().ckks_bsgs_linear_transform(self._h, _ptr(x), _ptr(out), B, l, _ptr(diags), bs, gs,
+                                                       bk, gk, int(do_rescale), _ptr(ws), ws.numel() * 8,
+                                                       _stream()), "ckks_bsgs_linear_transform")
+        return out
+
+    def fill_uniform(self, dst: torch.Tensor, seed: int, tag: int, stream0: int = 0, first_prime: int = 0):
+        """Seeded uniform residues (SplitMix64 streams, see include/ckks_synth.h)."""
+        nl = dst.shape[-2]
+        count = dst.numel() // (dst.shape[-1] * nl)
+        nat.check(nat.lib().ckks_fill_uniform(self._h, _ptr(dst), count, first_prime, nl, seed, tag, stream0,
+                                              _stream()), "ckks_fill_uniform")
+        return dst
+
+
+def galois_rot(n: int, k: int) -> int:
+    """Galois element of a left rotation by k slots."""
+    return pow(5, k % (n // 2), 2 * n)
+
+
+def galois_conj(n: int) -> int:
+    return 2 * n - 1

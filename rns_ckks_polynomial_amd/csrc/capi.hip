@@ -1,0 +1,163 @@
+// capi.hip -- the extern "C" entry points: argument validation, then launch.
+#include "../../include/ckks_gpu.h"
+#include "../../include/ckks_synth.h"
+#include "ctx_internal.h"
+#include "ops.h"
+
+using namespace ckks;
+
+namespace {
+inline bool aligned(const void *p) { return ((uintptr_t)p & 7) == 0; }
+struct DeviceGuard {
+    int saved = 0;
+    bool ok = false;
+    explicit DeviceGuard(int dev) {
+        hipGetDevice(&saved);
+        ok = hipSetDevice(dev) == hipSuccess;
+    }
+    ~DeviceGuard() { hipSetDevice(saved); }
+};
+int check_ptr(const void *p) {
+    if (!p) return CKKS_EINVAL;
+    if (!aligned(p)) return CKKS_EALIGN;
+    return CKKS_OK;
+}
+int check_level(const ckks_ctx *c, int batch, int level, int min_level) {
+    if (batch < 1) return CKKS_EINVAL;
+    if (level < min_level || (uint32_t)level > c->L) return CKKS_ELEVEL;
+    return CKKS_OK;
+}
+}  // namespace
+
+extern "C" int ckks_workspace_size(const ckks_ctx *c, int op, int batch, int level, int bs, int gs, size_t *bytes) {
+    if (!c || !bytes || batch < 1) return CKKS_EINVAL;
+    if (level < 1 || (uint32_t)level > c->L) return CKKS_ELEVEL;
+    switch (op) {
+        case CKKS_OP_RELIN:
+            if (!c->K) return CKKS_EINVAL;
+            *bytes = ws_bytes_relin(c, batch, level);
+            return CKKS_OK;
+        case CKKS_OP_ROTATE:
+            if (!c->K) return CKKS_EINVAL;
+            *bytes = ws_bytes_rotate(c, batch, level);
+            return CKKS_OK;
+        case CKKS_OP_RESCALE:
+            if (level < 2) return CKKS_ELEVEL;
+            *bytes = ws_bytes_rescale(c, batch, level);
+            return CKKS_OK;
+        case CKKS_OP_BSGS:
+            if (!c->K || bs < 1 || gs < 1) return CKKS_EINVAL;
+            if (level < 2) return CKKS_ELEVEL;
+            *bytes = ws_bytes_bsgs(c, batch, level, bs, gs);
+            return CKKS_OK;
+        default:
+            return CKKS_EINVAL;
+    }
+}
+
+static int ntt_common(const ckks_ctx *c, uint64_t *x, int count, int first, int nlimbs, void *stream, bool inv) {
+    if (!c) return CKKS_EINVAL;
+    if (count < 0 || nlimbs < 0 || first < 0 || (uint64_t)first + nlimbs > c->L + c->K) return CKKS_EINVAL;
+    if (count == 0 || nlimbs == 0) return CKKS_OK;
+    int e = check_ptr(x);
+    if (e) return e;
+    DeviceGuard g(c->device);
+    if (!g.ok) return CKKS_EHIP;
+    return op_ntt(c, x, count, first, nlimbs, inv, (hipStream_t)stream);
+}
+
+extern "C" int ckks_ntt_fwd(const ckks_ctx *c, uint64_t *x, int count, int first, int nlimbs, void *stream) {
+    return ntt_common(c, x, count, first, nlimbs, stream, false);
+}
+extern "C" int ckks_ntt_inv(const ckks_ctx *c, uint64_t *x, int count, int first, int nlimbs, void *stream) {
+    return ntt_common(c, x, count, first, nlimbs, stream, true);
+}
+
+extern "C" int ckks_pointwise_mul(const ckks_ctx *c, const uint64_t *a, const uint64_t *b, uint64_t *out, int count,
+                                  int first, int nlimbs, void *stream) {
+    if (!c) return CKKS_EINVAL;
+    int e;
+    if (count < 0 || nlimbs < 0 || first < 0 || (uint64_t)first + nlimbs > c->L + c->K) return CKKS_EINVAL;
+    if (count == 0 || nlimbs == 0) return CKKS_OK;
+    if ((e = check_ptr(a)) || (e = check_ptr(b)) || (e = check_ptr(out))) return e;
+    DeviceGuard g(c->device);
+    if (!g.ok) return CKKS_EHIP;
+    return op_pointwise_mul(c, a, b, out, count, first, nlimbs, (hipStream_t)stream);
+}
+
+extern "C" int ckks_mul_tensor_relin(const ckks_ctx *c, const uint64_t *a, const uint64_t *b, const uint64_t *rlk,
+                                     uint64_t *out, int batch, int level, void *ws, size_t ws_bytes, void *stream) {
+    if (!c || !c->K) return CKKS_EINVAL;
+    int e;
+    if ((e = check_ptr(a)) || (e = check_ptr(b)) || (e = check_ptr(rlk)) || (e = check_ptr(out))) return e;
+    if ((e = check_level(c, batch, level, 1))) return e;
+    if (!ws || ws_bytes < ws_bytes_relin(c, batch, level)) return CKKS_EWORKSPACE;
+    if (!aligned(ws)) return CKKS_EALIGN;
+    DeviceGuard g(c->device);
+    if (!g.ok) return CKKS_EHIP;
+    return op_mul_tensor_relin(const_cast<ckks_ctx *>(c), a, b, rlk, out, batch, level, ws, (hipStream_t)stream);
+}
+
+extern "C" int ckks_rescale(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int batch, int level, void *ws,
+                            size_t ws_bytes, void *stream) {
+    if (!c) return CKKS_EINVAL;
+    int e;
+    if ((e = check_ptr(in)) || (e = check_ptr(out))) return e;
+    if ((e = check_level(c, batch, level, 2))) return e;
+    if (!ws || ws_bytes < ws_bytes_rescale(c, batch, level)) return CKKS_EWORKSPACE;
+    if (!aligned(ws)) return CKKS_EALIGN;
+    DeviceGuard g(c->device);
+    if (!g.ok) return CKKS_EHIP;
+    return op_rescale(const_cast<ckks_ctx *>(c), in, out, batch, level, ws, (hipStream_t)stream);
+}
+
+extern "C" int ckks_rotate(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int batch, int level,
+                           uint32_t galois_elt, const uint64_t *key, void *ws, size_t ws_bytes, void *stream) {
+    if (!c || !c->K) return CKKS_EINVAL;
+    int e;
+    if ((e = check_ptr(in)) || (e = check_ptr(out)) || (e = check_ptr(key))) return e;
+    if ((e = check_level(c, batch, level, 1))) return e;
+    if ((galois_elt & 1) == 0 || galois_elt >= 2 * c->n) return CKKS_EINVAL;
+    if (in == out) return CKKS_EINVAL;
+    if (!ws || ws_bytes < ws_bytes_rotate(c, batch, level)) return CKKS_EWORKSPACE;
+    if (!aligned(ws)) return CKKS_EALIGN;
+    DeviceGuard g(c->device);
+    if (!g.ok) return CKKS_EHIP;
+    return op_rotate(const_cast<ckks_ctx *>(c), in, out, batch, level, galois_elt, key, ws, false,
+                     (hipStream_t)stream);
+}
+
+extern "C" int ckks_bsgs_linear_transform(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int batch, int level,
+                                          const uint64_t *diags, int bs, int gs, const uint64_t *const *baby_keys,
+                                          const uint64_t *const *giant_keys, int do_rescale, void *ws,
+                                          size_t ws_bytes, void *stream) {
+    if (!c || !c->K) return CKKS_EINVAL;
+    int e;
+    if ((e = check_ptr(in)) || (e = check_ptr(out)) || (e = check_ptr(diags))) return e;
+    if ((e = check_level(c, batch, level, do_rescale ? 2 : 1))) return e;
+    if (bs < 1 || gs < 1 || (uint64_t)bs * gs > c->n / 2) return CKKS_EINVAL;
+    if ((bs > 1 && !baby_keys) || (gs > 1 && !giant_keys)) return CKKS_EINVAL;
+    for (int b = 1; b < bs; b++)
+        if ((e = check_ptr(baby_keys[b]))) return e;
+    for (int g = 1; g < gs; g++)
+        if ((e = check_ptr(giant_keys[g]))) return e;
+    if (in == out) return CKKS_EINVAL;
+    if (!ws || ws_bytes < ws_bytes_bsgs(c, batch, level, bs, gs)) return CKKS_EWORKSPACE;
+    if (!aligned(ws)) return CKKS_EALIGN;
+    DeviceGuard g(c->device);
+    if (!g.ok) return CKKS_EHIP;
+    return op_bsgs(const_cast<ckks_ctx *>(c), in, out, batch, level, diags, bs, gs, baby_keys, giant_keys,
+                   do_rescale != 0, ws, (hipStream_t)stream);
+}
+
+extern "C" int ckks_fill_uniform(const ckks_ctx *c, uint64_t *dst, int count, int first, int nlimbs, uint64_t seed,
+                                 uint64_t tag, uint64_t stream0, void *stream) {
+    if (!c) return CKKS_EINVAL;
+    if (count < 0 || nlimbs < 0 || first < 0 || (uint64_t)first + nlimbs > c->L + c->K) return CKKS_EINVAL;
+    if (count == 0 || nlimbs == 0) return CKKS_OK;
+    int e = check_ptr(dst);
+    if (e) return e;
+    DeviceGuard g(c->device);
+    if (!g.ok) return CKKS_EHIP;
+    return op_fill_uniform(c, dst, count, first, nlimbs, seed, tag, stream0, (hipStream_t)stream);
+}

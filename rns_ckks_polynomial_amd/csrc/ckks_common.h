@@ -1,0 +1,91 @@
+// ckks_common.h -- device arithmetic and table layouts shared by the kernels.
+//
+// All moduli are primes in (2^59, 2^60) with q = 1 (mod 2n) (the 60-bit RNS
+// primes of the Kestrel relay README, section 1).  Residues at API boundaries
+// are fully reduced to [0, q).  Inside kernels values may be "lazy" in
+// [0, 2q) or [0, 4q) (4q < 2^62).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ckks {
+
+typedef unsigned __int128 u128;
+
+// ------------------------------------------------------------------ scalar
+__device__ __forceinline__ uint64_t mulhi64(uint64_t a, uint64_t b) { return __umul64hi(a, b); }
+
+// Shoup product: w < q, wp = floor(w 2^64 / q), any 64-bit x -> x w mod q in [0, 2q).
+__device__ __forceinline__ uint64_t shoup_lazy(uint64_t x, uint64_t w, uint64_t wp, uint64_t q) {
+    return x * w - mulhi64(x, wp) * q;
+}
+__device__ __forceinline__ uint64_t csub(uint64_t x, uint64_t q) { return x >= q ? x - q : x; }
+__device__ __forceinline__ uint64_t shoup(uint64_t x, uint64_t w, uint64_t wp, uint64_t q) {
+    return csub(shoup_lazy(x, w, wp, q), q);
+}
+__device__ __forceinline__ uint64_t addm(uint64_t a, uint64_t b, uint64_t q) { return csub(a + b, q); }
+__device__ __forceinline__ uint64_t subm(uint64_t a, uint64_t b, uint64_t q) { return a >= b ? a - b : a + q - b; }
+
+// Barrett product for a, b < q, q in (2^59, 2^60), mu = floor(2^122 / q).
+// With p = a b < 2^120, qhat = floor((p >> 58) mu / 2^64) is within 1 of
+// floor(p / q), so one conditional subtraction finishes.
+__device__ __forceinline__ uint64_t mulm(uint64_t a, uint64_t b, uint64_t q, uint64_t mu) {
+    u128 p = (u128)a * b;
+    uint64_t x1 = (uint64_t)(p >> 58);
+    uint64_t qh = mulhi64(x1, mu);
+    uint64_t r = (uint64_t)p - qh * q;
+    return csub(r, q);
+}
+
+// Per-prime reduction constants (device arrays indexed by global prime index).
+struct PrimeConsts {
+    uint64_t q;      // the prime
+    uint64_t mu;     // floor(2^122 / q)
+    uint64_t r64;    // 2^64 mod q
+    uint64_t r64p;   // Shoup companion of r64
+    uint64_t m64;    // floor(2^64 / q)  (Shoup companion of 1)
+    uint64_t ninv;   // n^-1 mod q
+    uint64_t ninvp;  // Shoup companion of ninv
+    uint64_t pad;
+};
+
+// Reduce a 128-bit value (hi:lo) modulo q: hi 2^64 + lo = shoup(hi, 2^64 mod q) + shoup(lo, 1).
+__device__ __forceinline__ uint64_t reduce128(uint64_t lo, uint64_t hi, const PrimeConsts &c) {
+    uint64_t a = shoup_lazy(hi, c.r64, c.r64p, c.q);  // [0, 2q)
+    uint64_t b = lo - mulhi64(lo, c.m64) * c.q;       // [0, 2q)
+    uint64_t s = a + b;                               // [0, 4q)
+    s = s >= 2 * c.q ? s - 2 * c.q : s;
+    return csub(s, c.q);
+}
+
+struct Acc128 {
+    uint64_t lo, hi;
+};
+__device__ __forceinline__ void mac(Acc128 &acc, uint64_t a, uint64_t b) {
+    u128 p = (u128)a * b;
+    u128 s = ((u128)acc.hi << 64 | acc.lo) + p;
+    acc.lo = (uint64_t)s;
+    acc.hi = (uint64_t)(s >> 64);
+}
+
+// ------------------------------------------------------------------ tables
+// Exact base conversion from a contiguous run of primes (a "basis": one
+// key-switching digit, or the special primes P) to any other chain prime.
+// The centered CRT value x_c of residues x_i modulo B = prod b_i is
+//   x_c = sum_i y_i Bhat_i - u B,   y_i = [x_i Bhat_i^-1]_{b_i},
+//   u = round(sum_i y_i / b_i)  (= floor(sum) + [x > (B-1)/2]).
+struct BasisDev {
+    uint32_t m;            // number of primes in the basis
+    uint32_t first;        // global index of the first basis prime
+    uint32_t ntot;         // number of chain primes (L + K): row count of H / negB
+    uint32_t pad;
+    const uint64_t *inv_hat;  // [m][2]  Shoup pair of [Bhat_i^-1]_{b_i}
+    const uint64_t *hat_mod;  // [m][2]  Shoup pair of [Bhat_i]_{b_i}   (recovers x_i from y_i)
+    const uint64_t *R;        // [m]     floor(2^123 / b_i)                (fixed-point 1/b_i)
+    const uint64_t *H;        // [ntot][m]  [Bhat_i]_t for every chain prime t
+    const uint64_t *negB;     // [ntot]     [-B]_t
+    const uint64_t *garner;   // [m][m][2]  Shoup pair of b_k^-1 mod b_i (k < i used)
+    const uint64_t *half;     // [m]        mixed-radix digits of (B-1)/2
+};
+
+}  // namespace ckks

@@ -1,0 +1,61 @@
+// ctx_internal.h -- the library context: immutable per-prime tables plus a
+// per-level cache of base-conversion tables, all resident in HBM.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <map>
+#include <mutex>
+#include <vector>
+
+#include "../../include/ckks_gpu.h"
+#include "ckks_common.h"
+
+namespace ckks {
+
+// Tables that depend on the level l (the last key-switching digit may be partial).
+struct LevelTables {
+    uint32_t l = 0, beta = 0;
+    BasisDev *d_digits = nullptr;   // [beta] device copies of the digit bases at level l
+    std::vector<BasisDev> h_digits; // host copies (pointers are device pointers)
+    uint64_t *d_modup_scale = nullptr;  // [l][2] Shoup pair of n^-1 [Bhat_i^-1]_{q_i} (digit of i)
+    uint64_t *d_rescale_inv = nullptr;  // [l-1][2] Shoup pair of q_{l-1}^-1 mod q_i
+    std::vector<void *> owned;          // device allocations owned by this level
+};
+
+struct MultipassPlan;  // large-n NTT tables (n > 2048)
+
+}  // namespace ckks
+
+struct ckks_ctx {
+    uint32_t n = 0, L = 0, K = 0, dnum = 0, alpha = 0, logn = 0;
+    int device = 0;
+    std::vector<uint64_t> primes, psi;  // [L+K]
+    ckks::PrimeConsts *d_pc = nullptr;  // [L+K]
+    uint64_t *d_tw_fwd = nullptr;       // [L+K][n][2]  psi^bitrev(k), Shoup
+    uint64_t *d_tw_inv = nullptr;       // [L+K][n][2]  psi^-bitrev(k), Shoup
+    // base of the special primes P (targets: every chain prime)
+    ckks::BasisDev h_pbasis{};
+    ckks::BasisDev *d_pbasis = nullptr;
+    uint64_t *d_moddown_scale = nullptr;  // [K][2] Shoup pair of n^-1 [Phat_k^-1]_{p_k}
+    uint64_t *d_pinv = nullptr;           // [L][2] Shoup pair of P^-1 mod q_i
+    // full-width digits at the top level (reused by every level where the digit is whole)
+    std::vector<ckks::BasisDev> full_digits;
+    std::vector<void *> owned;
+    std::map<uint32_t, ckks::LevelTables *> levels;
+    std::mutex mu;
+    ckks::MultipassPlan *mp = nullptr;
+};
+
+namespace ckks {
+// host-side number theory (independent of any reference code)
+uint64_t h_mulmod(uint64_t a, uint64_t b, uint64_t q);
+uint64_t h_powmod(uint64_t a, uint64_t e, uint64_t q);
+uint64_t h_invmod(uint64_t a, uint64_t q);
+uint64_t h_shoup(uint64_t w, uint64_t q);
+
+// Fetch (building on first use) the level tables.  Returns nullptr on failure.
+LevelTables *level_tables(ckks_ctx *ctx, uint32_t l, int *err);
+// Build a basis table for primes [first, first + m) with every chain prime as target.
+int build_basis(ckks_ctx *ctx, uint32_t first, uint32_t m, BasisDev *out, std::vector<void *> &owned);
+}  // namespace ckks

@@ -1,0 +1,673 @@
+// kernels.hip -- HIP kernels and their launch sequences for the hot path.
+//
+// Hybrid key switching (the Kestrel article's technique table: RNS base
+// conversion, Galois keys, relinearisation) runs as this kernel sequence on
+// one stream, all data resident in HBM:
+//   prep        d = a1 b1 (relin) or sigma_g(c1) (rotation), NTT domain
+//   iNTT        y_i = iNTT(d)_i [Bhat_i^-1]_{q_i}        (scale folded into n^-1)
+//   u           u = round(sum_i y_i / q_i) per digit, exact
+//   convert     ModUp: each digit to every other prime of Q_l u P (centered CRT)
+//   NTT         of the converted limbs
+//   inner       acc = sum_j ext_j (.) (b_j, a_j) over Q_l u P
+//   iNTT        of the P limbs of acc, scaled by [Phat_k^-1]_{p_k}
+//   u, convert  ModDown: P -> Q_l (centered)
+//   NTT         of the converted limbs
+//   final       out = (acc - conv) P^-1 (+ d0/d1, or sigma_g(c0))
+#include <algorithm>
+
+#include "ctx_internal.h"
+#include "multipass.h"
+#include "multipass_kernels.h"
+#include "ntt2048.h"
+#include "ops.h"
+
+namespace ckks {
+
+#define HIP_TRY(x)                                      \
+    do {                                                \
+        if ((x) != hipSuccess) return CKKS_EHIP;        \
+    } while (0)
+#define LAUNCH_CHECK() HIP_TRY(hipGetLastError())
+
+static inline size_t align_words(size_t w) { return (w + 31) & ~size_t(31); }  // 256-byte units
+static inline dim3 grid_for(size_t total) {
+    size_t b = (total + 255) / 256;
+    return dim3((unsigned)std::min<size_t>(b, 1u << 20));
+}
+
+// =====================================================================
+// Limb maps for the NTT launches.  get(blk, ...) gives the source and
+// destination of limb blk, its prime index, and an optional Shoup pair that
+// replaces n^-1 on the inverse.  src == nullptr skips the block.
+// =====================================================================
+struct MapStrided {  // [count][nl][n], limb r -> prime first + r
+    const uint64_t *src;
+    uint64_t *dst;
+    uint32_t n, nl, first;
+    const uint64_t *scale;  // optional, indexed by prime index
+    __device__ __forceinline__ void get(int blk, const uint64_t *&s, uint64_t *&d, int &prime,
+                                        const uint64_t *&sc) const {
+        prime = first + blk % nl;
+        s = src + (size_t)blk * n;
+        d = dst + (size_t)blk * n;
+        sc = scale ? scale + 2 * prime : nullptr;
+    }
+};
+
+struct MapExt {  // converted limbs [B][beta][l+K][n]; skips the digit's own primes
+    uint64_t *ext;
+    uint32_t n, l, L, K, beta, alpha;
+    __device__ __forceinline__ void get(int blk, const uint64_t *&s, uint64_t *&d, int &prime,
+                                        const uint64_t *&sc) const {
+        const uint32_t el = l + K;
+        const uint32_t e = blk % el, j = (blk / el) % beta;
+        sc = nullptr;
+        if (e >= j * alpha && e < min(l, (j + 1) * alpha)) {
+            s = nullptr;
+            d = nullptr;
+            prime = 0;
+            return;
+        }
+        prime = e < l ? e : L + (e - l);
+        d = ext + (size_t)blk * n;
+        s = d;
+    }
+};
+
+struct MapLast {  // last limb of each polynomial [P][l][n] -> dense [P][n]
+    const uint64_t *src;
+    uint64_t *dst;
+    uint32_t n, l;
+    __device__ __forceinline__ void get(int blk, const uint64_t *&s, uint64_t *&d, int &prime,
+                                        const uint64_t *&sc) const {
+        s = src + ((size_t)blk * l + (l - 1)) * n;
+        d = dst + (size_t)blk * n;
+        prime = l - 1;
+        sc = nullptr;
+    }
+};
+
+struct MapAccP {  // P limbs of acc [B][2][l+K][n], scaled inverse -> ModDown inputs
+    uint64_t *acc;
+    uint32_t n, l, L, K;
+    const uint64_t *scale;  // [K][2]
+    __device__ __forceinline__ void get(int blk, const uint64_t *&s, uint64_t *&d, int &prime,
+                                        const uint64_t *&sc) const {
+        const uint32_t k = blk % K, poly = blk / K;
+        d = acc + ((size_t)poly * (l + K) + l + k) * n;
+        s = d;
+        prime = L + k;
+        sc = scale + 2 * k;
+    }
+};
+
+template <class Map, bool INV>
+__global__ __launch_bounds__(256) void k_ntt2048(Map map, const PrimeConsts *__restrict__ pc,
+                                                  const uint64_t *__restrict__ twf,
+                                                  const uint64_t *__restrict__ twi) {
+    __shared__ uint64_t lds[n2048::LDS_WORDS];
+    const uint64_t *src;
+    uint64_t *dst;
+    int prime;
+    const uint64_t *sc;
+    map.get(blockIdx.x, src, dst, prime, sc);
+    if (!src) return;
+    const uint64_t q = pc[prime].q;
+    const int t = threadIdx.x;
+    uint64_t v[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) v[k] = src[t + 256 * k];
+    if (!INV) {
+        n2048::fwd(v, lds, twf + (size_t)prime * 2048 * 2, q);
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            uint64_t x = v[k];
+            x = x >= 2 * q ? x - 2 * q : x;
+            dst[t + 256 * k] = csub(x, q);
+        }
+    } else {
+        n2048::inv(v, lds, twi + (size_t)prime * 2048 * 2, q);
+        const uint64_t w = sc ? sc[0] : pc[prime].ninv, wp = sc ? sc[1] : pc[prime].ninvp;
+#pragma unroll
+        for (int k = 0; k < 8; k++) dst[t + 256 * k] = shoup(v[k], w, wp, q);
+    }
+}
+
+template <class Map>
+static int launch_ntt(const ckks_ctx *c, const Map &map, int nblk, bool inverse, hipStream_t s) {
+    if (nblk <= 0) return CKKS_OK;
+    if (c->n == 2048) {
+        if (inverse)
+            hipLaunchKernelGGL((k_ntt2048<Map, true>), dim3(nblk), dim3(256), 0, s, map, c->d_pc, c->d_tw_fwd,
+                               c->d_tw_inv);
+        else
+            hipLaunchKernelGGL((k_ntt2048<Map, false>), dim3(nblk), dim3(256), 0, s, map, c->d_pc, c->d_tw_fwd,
+                               c->d_tw_inv);
+        LAUNCH_CHECK();
+        return CKKS_OK;
+    }
+    return multipass_ntt(c, map, nblk, inverse, s);
+}
+
+int op_ntt(const ckks_ctx *c, uint64_t *x, int count, int first, int nlimbs, bool inverse, hipStream_t s) {
+    MapStrided m{x, x, c->n, (uint32_t)nlimbs, (uint32_t)first, nullptr};
+    return launch_ntt(c, m, count * nlimbs, inverse, s);
+}
+
+// =====================================================================
+// Elementwise kernels (grid-stride over [..][l][n] elements)
+// =====================================================================
+__global__ void k_pointwise(const uint64_t *__restrict__ a, const uint64_t *__restrict__ b, uint64_t *__restrict__ o,
+                            const PrimeConsts *__restrict__ pc, uint32_t n, uint32_t nl, uint32_t first,
+                            size_t total) {
+    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
+        const PrimeConsts &P = pc[first + (e / n) % nl];
+        o[e] = mulm(a[e], b[e], P.q, P.mu);
+    }
+}
+__device__ __forceinline__ uint32_t galois_src(uint32_t j, uint32_t g, uint32_t n) {
+    // NTT-domain automorphism: out[j] = in[(g(2j+1) mod 2n - 1) / 2]
+    return (uint32_t)((((uint64_t)g * (2 * j + 1)) & (2ull * n - 1)) >> 1);
+}
+
+int op_pointwise_mul(const ckks_ctx *c, const uint64_t *a, const uint64_t *b, uint64_t *out, int count, int first,
+                     int nlimbs, hipStream_t s) {
+    const size_t total = (size_t)count * nlimbs * c->n;
+    if (!total) return CKKS_OK;
+    hipLaunchKernelGGL(k_pointwise, grid_for(total), dim3(256), 0, s, a, b, out, c->d_pc, c->n, (uint32_t)nlimbs,
+                       (uint32_t)first, total);
+    LAUNCH_CHECK();
+    return CKKS_OK;
+}
+
+// d[b][i][k] = a[b][1][i][k] * b[b][1][i][k]   (tensor component d2)
+__global__ void k_prep_relin(const uint64_t *__restrict__ a, const uint64_t *__restrict__ b, uint64_t *__restrict__ d,
+                             const PrimeConsts *__restrict__ pc, uint32_t n, uint32_t l, size_t total) {
+    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
+        const size_t per = (size_t)l * n;
+        const size_t bi = e / per, r = e % per;
+        const uint32_t i = r / n;
+        const size_t off = (bi * 2 + 1) * per + r;
+        d[e] = mulm(a[off], b[off], pc[i].q, pc[i].mu);
+    }
+}
+
+// d[b][i][j] = in[b][1][i][galois_src(j)]
+__global__ void k_prep_rotate(const uint64_t *__restrict__ in, uint64_t *__restrict__ d, uint32_t g, uint32_t n,
+                              uint32_t l, size_t total) {
+    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
+        const size_t per = (size_t)l * n;
+        const size_t bi = e / per, r = e % per;
+        const uint32_t j = r % n;
+        d[e] = in[(bi * 2 + 1) * per + (r - j) + galois_src(j, g, n)];
+    }
+}
+
+// ---------------------------------------------------------------------
+// u = round(sum_i y_i / b_i) for one coefficient of one basis.
+// Fixed point: f_i = floor((16 y_i) R_i / 2^64) with R_i = floor(2^123 / b_i)
+// lies in (y_i 2^63 / b_i - 2, y_i 2^63 / b_i], so the 2^-63-unit sum S' is
+// below the true sum T by less than 2m units.  round(T) = floor((S' + 2^62) /
+// 2^63) unless the fractional part of S' + 2^62 is within 2m of 2^63; then an
+// exact mixed-radix comparison of x with (B-1)/2 decides.
+// ---------------------------------------------------------------------
+__device__ uint32_t exact_u_slow(const BasisDev &B, uint64_t *ycol, size_t stride, uint32_t floor_s,
+                                 const PrimeConsts *__restrict__ pc) {
+    const uint32_t m = B.m;
+    // x_i = y_i [Bhat_i]_{b_i}, in place
+    for (uint32_t i = 0; i < m; i++) {
+        const uint64_t bi = pc[B.first + i].q;
+        ycol[i * stride] = shoup(ycol[i * stride], B.hat_mod[2 * i], B.hat_mod[2 * i + 1], bi);
+    }
+    // Garner, in place: after step i, slot i holds mixed-radix digit a_i and
+    // slots k > i hold (x - a_0 - ... ) / (b_0 ... b_i) mod b_k.
+    int cmp = 0;
+    for (uint32_t i = 0; i < m; i++) {
+        const uint64_t ai = ycol[i * stride];
+        const uint64_t hi = B.half[i];
+        cmp = ai > hi ? 1 : (ai < hi ? -1 : cmp);
+        for (uint32_t k = i + 1; k < m; k++) {
+            const uint64_t bk = pc[B.first + k].q;
+            const uint64_t a = ai >= bk ? ai - bk : ai;  // a_i < b_i < 2 b_k
+            const uint64_t t = subm(ycol[k * stride], a, bk);
+            const size_t gi = ((size_t)i * m + k) * 2;
+            ycol[k * stride] = shoup(t, B.garner[gi], B.garner[gi + 1], bk);
+        }
+    }
+    // restore y_i: x_i = sum_{k<=i} a_k prod_{t<k} b_t mod b_i (Horner), then y_i = x_i [Bhat_i^-1]
+    for (uint32_t i = m; i-- > 0;) {
+        const PrimeConsts &P = pc[B.first + i];
+        uint64_t r = ycol[i * stride];
+        for (uint32_t k = i; k-- > 0;) {
+            const uint64_t bk = pc[B.first + k].q % P.q;
+            uint64_t ak = ycol[k * stride];
+            ak = ak >= P.q ? ak - P.q : ak;
+            r = addm(mulm(r, bk, P.q, P.mu), ak, P.q);
+        }
+        ycol[i * stride] = shoup(r, B.inv_hat[2 * i], B.inv_hat[2 * i + 1], P.q);
+    }
+    return floor_s + (cmp > 0 ? 1u : 0u);
+}
+
+// Sets s = 0..nsets-1; set s reads m_s limbs at y + (s / inner) * so + (s % inner) * si + off
+// and uses basis bases[per_set_basis ? s % inner : 0].
+struct SetLayout {
+    size_t so, si, off;
+    uint32_t inner, per_set_basis;
+};
+
+__global__ void k_basis_u(const BasisDev *__restrict__ bases, SetLayout lay, uint64_t *__restrict__ y,
+                          uint32_t *__restrict__ u, uint32_t n, const PrimeConsts *__restrict__ pc) {
+    const uint32_t k = blockIdx.x * blockDim.x + threadIdx.x;
+    const uint32_t s = blockIdx.y;
+    if (k >= n) return;
+    const BasisDev &B = bases[lay.per_set_basis ? s % lay.inner : 0];
+    uint64_t *yb = y + (s / lay.inner) * lay.so + (s % lay.inner) * lay.si + lay.off + k;
+    const uint32_t m = B.m;
+    const uint64_t M63 = (1ull << 63) - 1;
+    uint64_t frac = 0;
+    uint32_t ip = 0;
+    for (uint32_t i = 0; i < m; i++) {
+        const uint64_t f = mulhi64(yb[(size_t)i * n] << 4, B.R[i]);
+        frac += f;
+        ip += (uint32_t)(frac >> 63);
+        frac &= M63;
+    }
+    uint64_t t = frac + (1ull << 62);
+    uint32_t uu = ip + (uint32_t)(t >> 63);
+    t &= M63;
+    if (t >= (1ull << 63) - 2ull * m) uu = exact_u_slow(B, yb, n, ip, pc);
+    u[(size_t)s * n + k] = uu;
+}
+
+// ---------------------------------------------------------------------
+// Base conversion: out_t = sum_i y_i [Bhat_i]_t + u [-B]_t mod t.
+// One thread per coefficient, TT targets per block; the table row of a
+// target is wave-uniform (scalar loads).  The 128-bit accumulator takes at
+// most 255 products (< 2^128 for 60-bit operands) before a reduction.
+// ---------------------------------------------------------------------
+constexpr int TT = 8;
+
+struct ConvTargets {
+    // mode 0 (ModUp of digit [lo, lo+m)): targets = [0, lo) u [lo+m, l) u [L, L+K) -> ext slots
+    // mode 1 (ModDown): targets = [0, l) -> slot t
+    uint32_t mode, l, L, K;
+    size_t out_so, out_si;  // output limb base of set s: (s / inner) * out_so + (s % inner) * out_si
+};
+
+__global__ __launch_bounds__(256) void k_convert(const BasisDev *__restrict__ bases, SetLayout lay,
+                                                  const uint64_t *__restrict__ y, const uint32_t *__restrict__ u,
+                                                  ConvTargets ct, uint64_t *__restrict__ out, uint32_t n,
+                                                  const PrimeConsts *__restrict__ pc) {
+    const uint32_t k = blockIdx.x * blockDim.x + threadIdx.x;
+    const uint32_t s = blockIdx.z;
+    const uint32_t si = lay.per_set_basis ? s % lay.inner : 0;
+    const BasisDev &B = bases[si];
+    const uint32_t m = B.m;
+    const uint32_t lo = B.first;
+    const uint32_t ntarget = ct.mode == 0 ? ct.l - m + ct.K : ct.l;
+    const uint32_t tn0 = blockIdx.y * TT;
+    if (tn0 >= ntarget || k >= n) return;
+    uint32_t tg[TT];
+    uint32_t nt = min((uint32_t)TT, ntarget - tn0);
+#pragma unroll
+    for (int a = 0; a < TT; a++) {
+        uint32_t tn = tn0 + (a < (int)nt ? a : 0);
+        uint32_t t;
+        if (ct.mode == 1) t = tn;
+        else if (tn < lo) t = tn;
+        else if (tn < ct.l - m) t = tn + m;
+        else t = ct.L + (tn - (ct.l - m));
+        tg[a] = t;
+    }
+    const uint64_t *yb = y + (s / lay.inner) * lay.so + (s % lay.inner) * lay.si + lay.off + k;
+    Acc128 acc[TT];
+#pragma unroll
+    for (int a = 0; a < TT; a++) acc[a] = {0, 0};
+    uint32_t cnt = 0;
+    for (uint32_t i = 0; i < m; i++) {
+        const uint64_t yv = yb[(size_t)i * n];
+#pragma unroll
+        for (int a = 0; a < TT; a++) mac(acc[a], yv, B.H[(size_t)tg[a] * m + i]);
+        if (++cnt == 255) {
+            cnt = 1;  // the reduced value counts as one term
+#pragma unroll
+            for (int a = 0; a < TT; a++) acc[a] = {reduce128(acc[a].lo, acc[a].hi, pc[tg[a]]), 0};
+        }
+    }
+    const uint64_t uu = u[(size_t)s * n + k];
+    uint64_t *ob = out + (s / lay.inner) * ct.out_so + (s % lay.inner) * ct.out_si + k;
+#pragma unroll
+    for (int a = 0; a < TT; a++) {
+        if (a >= (int)nt) break;
+        const uint32_t t = tg[a];
+        mac(acc[a], uu, B.negB[t]);
+        const uint32_t slot = (ct.mode == 0 && t >= ct.L) ? ct.l + (t - ct.L) : t;
+        ob[(size_t)slot * n] = reduce128(acc[a].lo, acc[a].hi, pc[t]);
+    }
+}
+
+// acc[b][c][e][k] = sum_j v_j key[j][c][gidx(e)][k],  v_j = e in digit j ? d[b][e][k] : ext[b][j][e][k]
+__global__ void k_inner(const uint64_t *__restrict__ d, const uint64_t *__restrict__ ext,
+                        const uint64_t *__restrict__ key, uint64_t *__restrict__ acc,
+                        const PrimeConsts *__restrict__ pc, uint32_t n, uint32_t l, uint32_t L, uint32_t K,
+                        uint32_t beta, uint32_t alpha, size_t total) {
+    const uint32_t el = l + K;
+    for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total;
+         idx += (size_t)gridDim.x * blockDim.x) {
+        const uint32_t k = idx % n;
+        const uint32_t e = (idx / n) % el;
+        const size_t b = idx / ((size_t)n * el);
+        const uint32_t g = e < l ? e : L + (e - l);
+        Acc128 a0{0, 0}, a1{0, 0};
+        for (uint32_t j = 0; j < beta; j++) {
+            const bool own = e >= j * alpha && e < min(l, (j + 1) * alpha);
+            const uint64_t v = own ? d[(b * l + e) * n + k] : ext[((b * beta + j) * el + e) * n + k];
+            const uint64_t *kr = key + ((size_t)j * 2 * (L + K) + g) * n + k;
+            mac(a0, v, kr[0]);
+            mac(a1, v, kr[(size_t)(L + K) * n]);
+        }
+        acc[((b * 2 + 0) * el + e) * n + k] = reduce128(a0.lo, a0.hi, pc[g]);
+        acc[((b * 2 + 1) * el + e) * n + k] = reduce128(a1.lo, a1.hi, pc[g]);
+    }
+}
+
+// out[b][c][i][k] = (acc[b][c][i][k] - conv[b][c][i][k]) P^-1 + extra
+//   MODE 0: no extra; 1: relin (c0: a0 b0, c1: a0 b1 + a1 b0); 2: rotate (c0: in[b][0][i][galois]);
+//   ACCUM: out += result instead of out = result
+template <int MODE, bool ACCUM>
+__global__ void k_moddown_final(const uint64_t *__restrict__ acc, const uint64_t *__restrict__ conv,
+                                const uint64_t *__restrict__ pinv, const PrimeConsts *__restrict__ pc,
+                                const uint64_t *__restrict__ xa, const uint64_t *__restrict__ xb, uint32_t g,
+                                uint64_t *__restrict__ out, uint32_t n, uint32_t l, uint32_t K, size_t total) {
+    const uint32_t el = l + K;
+    for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total;
+         idx += (size_t)gridDim.x * blockDim.x) {
+        const uint32_t k = idx % n;
+        const uint32_t i = (idx / n) % l;
+        const uint32_t c = (idx / ((size_t)n * l)) % 2;
+        const size_t b = idx / ((size_t)n * l * 2);
+        const PrimeConsts &P = pc[i];
+        const uint64_t q = P.q;
+        const uint64_t a = acc[((b * 2 + c) * el + i) * n + k];
+        const uint64_t cv = conv[idx];
+        uint64_t r = shoup(subm(a, cv, q), pinv[2 * i], pinv[2 * i + 1], q);
+        const size_t per = (size_t)l * n;
+        if (MODE == 1) {
+            const size_t o0 = (b * 2) * per + (size_t)i * n + k, o1 = o0 + per;
+            uint64_t x;
+            if (c == 0) x = mulm(xa[o0], xb[o0], q, P.mu);
+            else x = addm(mulm(xa[o0], xb[o1], q, P.mu), mulm(xa[o1], xb[o0], q, P.mu), q);
+            r = addm(r, x, q);
+        } else if (MODE == 2) {
+            if (c == 0) r = addm(r, xa[(b * 2) * per + (size_t)i * n + galois_src(k, g, n)], q);
+        }
+        if (ACCUM) r = addm(r, out[idx], q);
+        out[idx] = r;
+    }
+}
+
+// ---------------------------------------------------------------------
+// Rescale (drop q_{l-1}): r = centered t mod q_i, then out = (c_i - NTT(r)) q_{l-1}^-1.
+// ---------------------------------------------------------------------
+__global__ void k_rescale_lift(const uint64_t *__restrict__ t, uint64_t *__restrict__ r,
+                               const PrimeConsts *__restrict__ pc, uint32_t n, uint32_t l, size_t total) {
+    const uint64_t ql = pc[l - 1].q;
+    for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total;
+         idx += (size_t)gridDim.x * blockDim.x) {
+        const uint32_t k = idx % n;
+        const uint32_t i = (idx / n) % (l - 1);
+        const size_t bc = idx / ((size_t)n * (l - 1));
+        const uint64_t q = pc[i].q;
+        const uint64_t v = t[bc * n + k];
+        // t < q_{l-1} < 2 q_i for all chain primes here; centered: t or t - q_{l-1}
+        uint64_t x = v >= q ? v - q : v;
+        if (v > (ql - 1) / 2) {
+            uint64_t qlm = ql >= q ? ql - q : ql;
+            x = subm(x, qlm, q);
+        }
+        r[idx] = x;
+    }
+}
+
+__global__ void k_rescale_final(const uint64_t *__restrict__ in, const uint64_t *__restrict__ r,
+                                const uint64_t *__restrict__ rinv, const PrimeConsts *__restrict__ pc,
+                                uint64_t *__restrict__ out, uint32_t n, uint32_t l, size_t total) {
+    for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total;
+         idx += (size_t)gridDim.x * blockDim.x) {
+        const uint32_t k = idx % n;
+        const uint32_t i = (idx / n) % (l - 1);
+        const size_t bc = idx / ((size_t)n * (l - 1));
+        const uint64_t q = pc[i].q;
+        const uint64_t c = in[(bc * l + i) * n + k];
+        out[idx] = shoup(subm(c, r[idx], q), rinv[2 * i], rinv[2 * i + 1], q);
+    }
+}
+
+// ---------------------------------------------------------------------
+// BSGS multiply-accumulate: inner[g][b][c][i][k] = sum_bb pt[g][bb][i][k] rot_bb[b][c][i][k]
+// rot_0 is the input itself; rot_bb (bb >= 1) at rot + (bb - 1) * ctsize.
+// ---------------------------------------------------------------------
+__global__ void k_bsgs_mac(const uint64_t *__restrict__ pt, const uint64_t *__restrict__ in,
+                           const uint64_t *__restrict__ rot, uint64_t *__restrict__ inner,
+                           const PrimeConsts *__restrict__ pc, uint32_t n, uint32_t l, uint32_t bs, uint32_t gs,
+                           size_t ctsize /* B*2*l*n */) {
+    for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < ctsize;
+         idx += (size_t)gridDim.x * blockDim.x) {
+        const uint32_t k = idx % n;
+        const uint32_t i = (idx / n) % l;
+        const size_t ik = (size_t)i * n + k;
+        const size_t per = (size_t)l * n;
+        for (uint32_t g = 0; g < gs; g++) {
+            Acc128 a{0, 0};
+            for (uint32_t bb = 0; bb < bs; bb++) {
+                const uint64_t x = bb == 0 ? in[idx] : rot[(size_t)(bb - 1) * ctsize + idx];
+                mac(a, pt[((size_t)g * bs + bb) * per + ik], x);
+            }
+            inner[(size_t)g * ctsize + idx] = reduce128(a.lo, a.hi, pc[i]);
+        }
+    }
+}
+
+__global__ void k_copy(const uint64_t *__restrict__ a, uint64_t *__restrict__ b, size_t total) {
+    for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total;
+         idx += (size_t)gridDim.x * blockDim.x)
+        b[idx] = a[idx];
+}
+
+
+// =====================================================================
+// Key switching core
+// =====================================================================
+struct KsWs {
+    uint64_t *d, *y, *ext, *acc, *conv;
+    uint32_t *u, *uP;
+};
+
+static size_t ks_words(const ckks_ctx *c, int B, int l, KsWs *w, uint64_t *base) {
+    const size_t n = c->n, el = (size_t)l + c->K;
+    const size_t beta = (l + c->alpha - 1) / c->alpha;
+    size_t off = 0;
+    auto take = [&](size_t words) {
+        uint64_t *p = base ? base + off : nullptr;
+        off += align_words(words);
+        return p;
+    };
+    uint64_t *d = take(B * (size_t)l * n);
+    uint64_t *y = take(B * (size_t)l * n);
+    uint64_t *ext = take(B * beta * el * n);
+    uint64_t *acc = take(B * 2 * el * n);
+    uint64_t *conv = take(B * 2 * (size_t)l * n);
+    uint64_t *u = take((B * beta * n + 1) / 2);
+    uint64_t *uP = take((B * 2 * n + 1) / 2);
+    if (w) *w = KsWs{d, y, ext, acc, conv, (uint32_t *)u, (uint32_t *)uP};
+    return off;
+}
+
+// On entry w.d holds the NTT-domain polynomial to switch ([B][l][n]).  On exit
+// w.acc holds the Q-limbs of the accumulators and w.conv the NTT-domain
+// ModDown conversion; the caller runs the final kernel.
+static int keyswitch_core(ckks_ctx *c, LevelTables *lt, int B, int l, const uint64_t *key, const KsWs &w,
+                          hipStream_t s) {
+    const uint32_t n = c->n, K = c->K, L = c->L, el = l + K, beta = lt->beta;
+    int e;
+    // y = iNTT(d) scaled by [Bhat_i^-1]
+    {
+        MapStrided m{w.d, w.y, n, (uint32_t)l, 0, lt->d_modup_scale};
+        if ((e = launch_ntt(c, m, B * l, true, s))) return e;
+    }
+    SetLayout lay_up{(size_t)l * n, (size_t)c->alpha * n, 0, beta, 1};
+    hipLaunchKernelGGL(k_basis_u, dim3((n + 255) / 256, B * beta), dim3(256), 0, s, lt->d_digits, lay_up, w.y, w.u,
+                       n, c->d_pc);
+    LAUNCH_CHECK();
+    {
+        ConvTargets ct{0, (uint32_t)l, L, K, (size_t)beta * el * n, (size_t)el * n};
+        const uint32_t maxt = l + K;  // upper bound on targets per digit
+        hipLaunchKernelGGL(k_convert, dim3((n + 255) / 256, (maxt + TT - 1) / TT, B * beta), dim3(256), 0, s,
+                           lt->d_digits, lay_up, w.y, w.u, ct, w.ext, n, c->d_pc);
+        LAUNCH_CHECK();
+    }
+    {
+        MapExt m{w.ext, n, (uint32_t)l, L, K, beta, c->alpha};
+        if ((e = launch_ntt(c, m, B * beta * el, false, s))) return e;
+    }
+    {
+        size_t total = (size_t)B * el * n;
+        hipLaunchKernelGGL(k_inner, grid_for(total), dim3(256), 0, s, w.d, w.ext, key, w.acc, c->d_pc, n,
+                           (uint32_t)l, L, K, beta, c->alpha, total);
+        LAUNCH_CHECK();
+    }
+    {
+        MapAccP m{w.acc, n, (uint32_t)l, L, K, c->d_moddown_scale};
+        if ((e = launch_ntt(c, m, B * 2 * K, true, s))) return e;
+    }
+    SetLayout lay_dn{(size_t)el * n, 0, (size_t)l * n, 1, 0};
+    hipLaunchKernelGGL(k_basis_u, dim3((n + 255) / 256, B * 2), dim3(256), 0, s, c->d_pbasis, lay_dn, w.acc, w.uP,
+                       n, c->d_pc);
+    LAUNCH_CHECK();
+    {
+        ConvTargets ct{1, (uint32_t)l, L, K, (size_t)l * n, 0};
+        hipLaunchKernelGGL(k_convert, dim3((n + 255) / 256, (l + TT - 1) / TT, B * 2), dim3(256), 0, s,
+                           c->d_pbasis, lay_dn, w.acc, w.uP, ct, w.conv, n, c->d_pc);
+        LAUNCH_CHECK();
+    }
+    {
+        MapStrided m{w.conv, w.conv, n, (uint32_t)l, 0, nullptr};
+        if ((e = launch_ntt(c, m, B * 2 * l, false, s))) return e;
+    }
+    return CKKS_OK;
+}
+
+size_t ws_bytes_relin(const ckks_ctx *c, int B, int l) { return ks_words(c, B, l, nullptr, nullptr) * 8; }
+size_t ws_bytes_rotate(const ckks_ctx *c, int B, int l) { return ks_words(c, B, l, nullptr, nullptr) * 8; }
+size_t ws_bytes_rescale(const ckks_ctx *c, int B, int l) {
+    return (align_words((size_t)B * 2 * c->n) + align_words((size_t)B * 2 * (l - 1) * c->n)) * 8;
+}
+static size_t bsgs_words(const ckks_ctx *c, int B, int l, int bs, int gs) {
+    const size_t ct = (size_t)B * 2 * l * c->n;
+    return align_words(ct * (bs - 1)) + align_words(ct * gs) + ks_words(c, B, l, nullptr, nullptr) +
+           ws_bytes_rescale(c, B, l) / 8;
+}
+size_t ws_bytes_bsgs(const ckks_ctx *c, int B, int l, int bs, int gs) { return bsgs_words(c, B, l, bs, gs) * 8; }
+
+int op_mul_tensor_relin(ckks_ctx *c, const uint64_t *a, const uint64_t *b, const uint64_t *rlk, uint64_t *out, int B,
+                        int l, void *ws, hipStream_t s) {
+    int e = CKKS_OK;
+    LevelTables *lt = level_tables(c, l, &e);
+    if (!lt) return e;
+    KsWs w;
+    ks_words(c, B, l, &w, (uint64_t *)ws);
+    const uint32_t n = c->n;
+    size_t tot = (size_t)B * l * n;
+    hipLaunchKernelGGL(k_prep_relin, grid_for(tot), dim3(256), 0, s, a, b, w.d, c->d_pc, n, (uint32_t)l, tot);
+    LAUNCH_CHECK();
+    if ((e = keyswitch_core(c, lt, B, l, rlk, w, s))) return e;
+    tot = (size_t)B * 2 * l * n;
+    hipLaunchKernelGGL((k_moddown_final<1, false>), grid_for(tot), dim3(256), 0, s, w.acc, w.conv, c->d_pinv,
+                       c->d_pc, a, b, 0u, out, n, (uint32_t)l, c->K, tot);
+    LAUNCH_CHECK();
+    return CKKS_OK;
+}
+
+int op_rotate(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, uint32_t g, const uint64_t *key, void *ws,
+              bool accumulate, hipStream_t s) {
+    int e = CKKS_OK;
+    LevelTables *lt = level_tables(c, l, &e);
+    if (!lt) return e;
+    KsWs w;
+    ks_words(c, B, l, &w, (uint64_t *)ws);
+    const uint32_t n = c->n;
+    size_t tot = (size_t)B * l * n;
+    hipLaunchKernelGGL(k_prep_rotate, grid_for(tot), dim3(256), 0, s, in, w.d, g, n, (uint32_t)l, tot);
+    LAUNCH_CHECK();
+    if ((e = keyswitch_core(c, lt, B, l, key, w, s))) return e;
+    tot = (size_t)B * 2 * l * n;
+    if (accumulate)
+        hipLaunchKernelGGL((k_moddown_final<2, true>), grid_for(tot), dim3(256), 0, s, w.acc, w.conv, c->d_pinv,
+                           c->d_pc, in, (const uint64_t *)nullptr, g, out, n, (uint32_t)l, c->K, tot);
+    else
+        hipLaunchKernelGGL((k_moddown_final<2, false>), grid_for(tot), dim3(256), 0, s, w.acc, w.conv, c->d_pinv,
+                           c->d_pc, in, (const uint64_t *)nullptr, g, out, n, (uint32_t)l, c->K, tot);
+    LAUNCH_CHECK();
+    return CKKS_OK;
+}
+
+int op_rescale(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, void *ws, hipStream_t s) {
+    int e = CKKS_OK;
+    LevelTables *lt = level_tables(c, l, &e);
+    if (!lt) return e;
+    const uint32_t n = c->n;
+    uint64_t *t = (uint64_t *)ws;
+    uint64_t *r = t + align_words((size_t)B * 2 * n);
+    // t[b][c] = iNTT(in[b][c][l-1])
+    {
+        MapLast ml{in, t, n, (uint32_t)l};
+        if ((e = launch_ntt(c, ml, B * 2, true, s))) return e;
+    }
+    size_t tot = (size_t)B * 2 * (l - 1) * n;
+    hipLaunchKernelGGL(k_rescale_lift, grid_for(tot), dim3(256), 0, s, t, r, c->d_pc, n, (uint32_t)l, tot);
+    LAUNCH_CHECK();
+    {
+        MapStrided m{r, r, n, (uint32_t)(l - 1), 0, nullptr};
+        if ((e = launch_ntt(c, m, B * 2 * (l - 1), false, s))) return e;
+    }
+    hipLaunchKernelGGL(k_rescale_final, grid_for(tot), dim3(256), 0, s, in, r, lt->d_rescale_inv, c->d_pc, out, n,
+                       (uint32_t)l, tot);
+    LAUNCH_CHECK();
+    return CKKS_OK;
+}
+
+static uint32_t rot_elt(uint32_t n, uint64_t k) {
+    uint64_t m = 2ull * n, r = 1, b = 5;
+    k %= n / 2;
+    for (; k; k >>= 1, b = b * b % m)
+        if (k & 1) r = r * b % m;
+    return (uint32_t)r;
+}
+
+int op_bsgs(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, const uint64_t *diags, int bs, int gs,
+            const uint64_t *const *baby, const uint64_t *const *giant, bool rescale, void *ws, hipStream_t s) {
+    const size_t ct = (size_t)B * 2 * l * c->n;
+    uint64_t *rot = (uint64_t *)ws;
+    uint64_t *inner = rot + align_words(ct * (bs - 1));
+    uint64_t *ksws = inner + align_words(ct * gs);
+    uint64_t *rsws = ksws + ks_words(c, B, l, nullptr, nullptr);
+    int e;
+    for (int b = 1; b < bs; b++)
+        if ((e = op_rotate(c, in, rot + (size_t)(b - 1) * ct, B, l, rot_elt(c->n, b), baby[b], ksws, false, s)))
+            return e;
+    hipLaunchKernelGGL(k_bsgs_mac, grid_for(ct), dim3(256), 0, s, diags, in, rot, inner, c->d_pc, c->n, (uint32_t)l,
+                       (uint32_t)bs, (uint32_t)gs, ct);
+    LAUNCH_CHECK();
+    // giant steps accumulate into inner[0]
+    for (int g = 1; g < gs; g++)
+        if ((e = op_rotate(c, inner + (size_t)g * ct, inner, B, l, rot_elt(c->n, (uint64_t)g * bs), giant[g], ksws,
+                           true, s)))
+            return e;
+    if (rescale) return op_rescale(c, inner, out, B, l, rsws, s);
+    hipLaunchKernelGGL(k_copy, grid_for(ct), dim3(256), 0, s, inner, out, ct);
+    LAUNCH_CHECK();
+    return CKKS_OK;
+}
+
+}  // namespace ckks

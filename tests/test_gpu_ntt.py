@@ -1,0 +1,110 @@
+"""GPU parity: chain parameters, seeded fill, NTT / iNTT and the config-1
+polynomial multiply, bit-exact against the oracle (through the C ABI)."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import dev, gpu_ctx, host, mismatch, oracle_ctx, require_gpu, torch
+from rns_ckks_polynomial_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+@pytest.mark.parametrize("n,L,K,dnum", [(2048, 4, 0, 1), (2048, 112, 28, 4)])
+def test_chain_primes_and_roots(n, L, K, dnum):
+    g = gpu_ctx(n, L, K, dnum)
+    o = oracle_ctx(n, L, K, dnum)
+    assert np.array_equal(g.primes, o.primes)
+    assert np.array_equal(g.psi, o.psi)
+
+
+def test_fill_uniform_matches_generator():
+    g = gpu_ctx(2048, 112, 28, 4)
+    t = torch.empty((3, 112, 2048), dtype=torch.uint64, device="cuda")
+    g.fill_uniform(t, seed=77, tag=synth.TAG_CT, stream0=5)
+    ref = synth.uniform_mod(77, synth.TAG_CT, np.arange(3 * 112) + 5, np.tile(g.primes[:112], 3), 2048)
+    assert np.array_equal(host(t).reshape(-1, 2048), ref)
+
+
+def _rand(o, seed, count, nl, first=0):
+    return synth.uniform_mod(seed, synth.TAG_POLY, np.arange(count * nl),
+                             np.tile(o.primes[first:first + nl], count), o.n).reshape(count, nl, o.n)
+
+
+def test_ntt_config1_bitexact():
+    """n = 2048, 4 primes, 2 polynomials: forward and inverse against the oracle."""
+    g, o = gpu_ctx(2048, 4), oracle_ctx(2048, 4)
+    x = _rand(o, 0xC0DE0001, 2, 4)
+    t = dev(x)
+    g.ntt_fwd(t)
+    ref = o.ntt(x)
+    got = host(t)
+    assert np.array_equal(got, ref), mismatch(got, ref)
+    g.ntt_inv(t)
+    assert np.array_equal(host(t), x)
+    t2 = dev(ref)
+    g.ntt_inv(t2)
+    assert np.array_equal(host(t2), o.ntt(ref, inverse=True))
+
+
+def test_config1_polynomial_multiply():
+    """forward NTT, pointwise modmul, inverse NTT == schoolbook product mod X^2048 + 1."""
+    g, o = gpu_ctx(2048, 4), oracle_ctx(2048, 4)
+    a = _rand(o, 0xC0DE0001, 1, 4)
+    b = synth.uniform_mod(0xC0DE0001, synth.TAG_POLY, np.arange(4) + 4, o.primes, 2048).reshape(1, 4, 2048)
+    ta, tb = dev(a), dev(b)
+    g.ntt_fwd(ta)
+    g.ntt_fwd(tb)
+    tc = g.pointwise_mul(ta, tb)
+    g.ntt_inv(tc)
+    got = host(tc)[0]
+    for r in range(4):
+        ref = oracle.negacyclic_schoolbook(a[0, r], b[0, r], o.q(r))
+        assert np.array_equal(got[r], ref), (r, mismatch(got[r], ref))
+
+
+def test_ntt_lay_batch_bitexact():
+    """[8][2][112] limbs (one batch of config-2 ciphertexts), and the special primes."""
+    g, o = gpu_ctx(2048, 112, 28, 4), oracle_ctx(2048, 112, 28, 4)
+    x = _rand(o, 3, 16, 112)
+    t = dev(x)
+    g.ntt_fwd(t)
+    got = host(t)
+    ref = o.ntt(x)
+    assert np.array_equal(got, ref), mismatch(got, ref)
+    g.ntt_inv(t)
+    assert np.array_equal(host(t), x)
+    p = _rand(o, 4, 3, 28, first=112)
+    tp = dev(p)
+    g.ntt_fwd(tp, first_prime=112)
+    assert np.array_equal(host(tp), o.ntt(p, first=112))
+
+
+def test_ntt_edge_values():
+    g, o = gpu_ctx(2048, 4), oracle_ctx(2048, 4)
+    x = np.zeros((3, 4, 2048), dtype=np.uint64)
+    x[1] = (o.primes[:4] - 1)[:, None]           # all q - 1
+    x[2, :, 0] = 1                               # the constant 1
+    x[2, :, 2047] = o.primes[:4] - 1             # -X^2047
+    t = dev(x)
+    g.ntt_fwd(t)
+    got = host(t)
+    assert np.array_equal(got, o.ntt(x))
+    assert not got[0].any()
+    g.ntt_inv(t)
+    assert np.array_equal(host(t), x)
+    # count = 0 is a no-op
+    g.ntt_fwd(t[:0])
+
+
+def test_ntt_rejects_bad_arguments():
+    from rns_ckks_polynomial_amd._native import CkksError
+    g = gpu_ctx(2048, 4)
+    t = torch.zeros((1, 5, 2048), dtype=torch.uint64, device="cuda")
+    with pytest.raises(CkksError):
+        g.ntt_fwd(t)  # 5 limbs > 4 primes

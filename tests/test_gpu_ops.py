@@ -1,0 +1,175 @@
+"""GPU parity of the ciphertext operations (tensor + relinearisation, rescale,
+rotation / conjugation, BSGS), bit-exact on every residue against the oracle,
+plus decrypt checks of GPU results and the exact base-conversion boundary."""
+import numpy as np
+import pytest
+
+import oracle
+import pyref
+from ckks_helpers import Keys, galois_conj, galois_rot, rel_err
+from gpu_util import dev, gpu_ctx, host, mismatch, oracle_ctx, require_gpu, torch
+from rns_ckks_polynomial_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+LAY = (2048, 112, 28, 4)  # n, L, K, dnum of the 112-prime layer chain
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def rand_cts(o, seed, B, l, tag=synth.TAG_CT):
+    return synth.uniform_mod(seed, tag, np.arange(B * 2 * l), np.tile(o.primes[:l], 2 * B),
+                             o.n).reshape(B, 2, l, o.n)
+
+
+def rand_key(o, seed, j=0):
+    tot = o.L + o.K
+    return synth.uniform_mod(seed, synth.TAG_KEY, np.arange(o.dnum * 2 * tot) + j * 100_000,
+                             np.tile(o.primes, o.dnum * 2), o.n).reshape(o.dnum, 2, tot, o.n)
+
+
+@pytest.mark.parametrize("l,B", [(112, 2), (100, 1), (29, 1), (1, 1)])
+def test_mul_tensor_relin_bitexact(l, B):
+    g, o = gpu_ctx(*LAY), oracle_ctx(*LAY)
+    a, b = rand_cts(o, 10 + l, B, l), rand_cts(o, 20 + l, B, l)
+    key = rand_key(o, 30)
+    out = host(g.mul_tensor_relin(dev(a), dev(b), dev(key)))
+    for i in range(B):
+        ref = o.mul_tensor_relin(a[i], b[i], key, l)
+        assert np.array_equal(out[i], ref), (i, mismatch(out[i], ref))
+
+
+@pytest.mark.parametrize("l,B", [(112, 2), (2, 3)])
+def test_rescale_bitexact(l, B):
+    g, o = gpu_ctx(*LAY), oracle_ctx(*LAY)
+    x = rand_cts(o, 40 + l, B, l)
+    out = host(g.rescale(dev(x)))
+    for i in range(B):
+        ref = o.rescale(x[i], l)
+        assert np.array_equal(out[i], ref), (i, mismatch(out[i], ref))
+
+
+@pytest.mark.parametrize("kind", ["rot1", "rot5", "rot1000", "conj"])
+def test_rotate_bitexact(kind):
+    g, o = gpu_ctx(*LAY), oracle_ctx(*LAY)
+    l, B = 112, 2
+    gelt = {"rot1": galois_rot(2048, 1), "rot5": galois_rot(2048, 5), "rot1000": galois_rot(2048, 1000),
+            "conj": galois_conj(2048)}[kind]
+    x = rand_cts(o, 50, B, l)
+    key = rand_key(o, 51)
+    out = host(g.rotate(dev(x), gelt, dev(key)))
+    for i in range(B):
+        ref = o.rotate(x[i], gelt, key, l)
+        assert np.array_equal(out[i], ref), (i, mismatch(out[i], ref))
+
+
+def test_modup_exact_boundary():
+    """Digit-0 coefficients set to integers at +-(Q_0 - 1)/2 (+-small): the fixed-point
+    rounding is ambiguous there and the exact fallback must decide."""
+    g, o = gpu_ctx(*LAY), oracle_ctx(*LAY)
+    l = 112
+    alpha = o.alpha
+    Q0 = 1
+    for i in range(alpha):
+        Q0 *= o.q(i)
+    h = (Q0 - 1) // 2
+    vals = [h, h + 1, h - 1, h + 2, Q0 - 1, 0, 1, h - 5, h + 6] + [h + t for t in range(-40, 40)]
+    x = rand_cts(o, 60, 1, l)
+    coef = o.ntt(x[0, 1], inverse=True)
+    for k, v in enumerate(vals):
+        for i in range(alpha):
+            coef[i, k] = v % o.q(i)
+    x[0, 1] = o.ntt(coef)
+    key = rand_key(o, 61)
+    out = host(g.rotate(dev(x), galois_rot(2048, 3), dev(key)))
+    ref = o.rotate(x[0], galois_rot(2048, 3), key, l)
+    assert np.array_equal(out[0], ref), mismatch(out[0], ref)
+    # same through relinearisation (d2 = a1 b1 with b1 = 1)
+    ones = x.copy()
+    ones[0, 1] = o.ntt(np.array([[1] + [0] * 2047] * l, dtype=np.uint64))
+    out = host(g.mul_tensor_relin(dev(x), dev(ones), dev(key)))
+    assert np.array_equal(out[0], o.mul_tensor_relin(x[0], ones[0], key, l))
+
+
+def test_moddown_exact_boundary():
+    """A key whose digit-0 b-row is the constant (P+-1)/2 and d = 1: the P-part of the
+    accumulator sits exactly at the centering boundary."""
+    g, o = gpu_ctx(*LAY), oracle_ctx(*LAY)
+    l, L, K = 112, o.L, o.K
+    P = 1
+    for k in range(K):
+        P *= o.q(L + k)
+    key = np.zeros((o.dnum, 2, L + K, 2048), dtype=np.uint64)
+    for which, c in enumerate([(P - 1) // 2, (P + 1) // 2]):
+        for r in range(L + K):
+            const = np.zeros(2048, dtype=np.uint64)
+            const[0] = c % o.q(r)
+            const[1] = (c + 3) % o.q(r)
+            key[0, which, r] = o.ntt(const[None, :], first=r)[0]
+    x = np.zeros((1, 2, l, 2048), dtype=np.uint64)
+    x[0, 0] = rand_cts(o, 70, 1, l)[0, 0]
+    one = np.zeros((l, 2048), dtype=np.uint64)
+    one[:, 0] = 1
+    one[:, 5] = 2
+    x[0, 1] = o.ntt(one)
+    out = host(g.rotate(dev(x), 1, dev(key)))  # identity automorphism: pure key switch
+    ref = o.rotate(x[0], 1, key, l)
+    assert np.array_equal(out[0], ref), mismatch(out[0], ref)
+
+
+def test_config2_batch8_relin_rescale():
+    """Config 2: 8 pairs at 112 primes, tensor + relinearise + rescale, every residue."""
+    g, o = gpu_ctx(*LAY), oracle_ctx(*LAY)
+    l, B = 112, 8
+    seed = 0xC0DE0002
+    a, b = rand_cts(o, seed, B, l), rand_cts(o, seed + 1, B, l)
+    key = rand_key(o, seed)
+    prod = g.mul_tensor_relin(dev(a), dev(b), dev(key))
+    res = host(g.rescale(prod))
+    prod = host(prod)
+    for i in range(B):
+        ref = o.mul_tensor_relin(a[i], b[i], key, l)
+        assert np.array_equal(prod[i], ref), (i, mismatch(prod[i], ref))
+        assert np.array_equal(res[i], o.rescale(ref, l)), i
+
+
+def _bsgs_inputs(o, seed, B, l, bs, gs):
+    x = rand_cts(o, seed, B, l)
+    pt = synth.uniform_mod(seed, synth.TAG_DIAG, np.arange(gs * bs * l), np.tile(o.primes[:l], gs * bs),
+                           o.n).reshape(gs, bs, l, o.n)
+    baby = [None] + [rand_key(o, seed, 1 + b) for b in range(1, bs)]
+    giant = [None] + [rand_key(o, seed, 100 + j) for j in range(1, gs)]
+    return x, pt, baby, giant
+
+
+@pytest.mark.parametrize("l,B,bs,gs", [(20, 2, 4, 3), (112, 1, 2, 2)])
+def test_bsgs_small_bitexact(l, B, bs, gs):
+    g, o = gpu_ctx(*LAY), oracle_ctx(*LAY)
+    x, pt, baby, giant = _bsgs_inputs(o, 80 + l, B, l, bs, gs)
+    dk = lambda ks: [None if k is None else dev(k) for k in ks]  # noqa: E731
+    out = host(g.bsgs_linear_transform(dev(x), dev(pt), bs, gs, dk(baby), dk(giant), do_rescale=True))
+    for i in range(B):
+        ref = o.bsgs(x[i], pt, bs, gs, baby, giant, l, do_rescale=True)
+        assert np.array_equal(out[i], ref), (i, mismatch(out[i], ref))
+
+
+def test_functional_rotate_and_relin_decrypt():
+    """Encrypt with the oracle, rotate / multiply on the GPU, decrypt with the oracle."""
+    o = oracle_ctx(*LAY)
+    g = gpu_ctx(*LAY)
+    keys = Keys(o, 0xC0DE0002)
+    l, delta = 112, 2.0 ** 60
+    z1 = synth.uniform_reals(9, synth.TAG_SLOTS, 0, 1024, -1, 1).astype(np.complex128)
+    z2 = synth.uniform_reals(9, synth.TAG_SLOTS, 1, 1024, -1, 1).astype(np.complex128)
+    c1, c2 = keys.encrypt(z1, delta, l, 0), keys.encrypt(z2, delta, l, 1)
+    gelt = galois_rot(2048, 7)
+    rk = keys.galois_key(gelt)
+    rot = host(g.rotate(dev(c1[None]), gelt, dev(rk)))[0]
+    assert rel_err(keys.decrypt(rot, delta, l), np.roll(z1, -7)) < 2.0 ** -20
+    rlk = keys.relin_key()
+    prod = g.rescale(g.mul_tensor_relin(dev(c1[None]), dev(c2[None]), dev(rlk)))
+    got = keys.decrypt(host(prod)[0], delta * delta / o.q(l - 1), l - 1)
+    assert rel_err(got, z1 * z2) < 2.0 ** -20
