@@ -282,11 +282,12 @@ __global__ void k_basis_u(const BasisDev *__restrict__ bases, SetLayout lay, uin
 
 // ---------------------------------------------------------------------
 // Base conversion: out_t = sum_i y_i [Bhat_i]_t + u [-B]_t mod t.
-// One thread per coefficient, TT targets per block; the table row of a
-// target is wave-uniform (scalar loads).  The 128-bit accumulator takes at
-// most 255 products (< 2^128 for 60-bit operands) before a reduction.
+// One thread per coefficient and CT targets per workgroup.  The block's
+// table rows (split30 layout) are staged in LDS and read as wave-uniform
+// broadcasts; each product is four v_mad_u64_u32 into split partial sums
+// (see smac), folded into 128 bits every SPLIT_CHUNK inputs.
 // ---------------------------------------------------------------------
-constexpr int TT = 8;
+constexpr int CT = 8;
 
 struct ConvTargets {
     // mode 0 (ModUp of digit [lo, lo+m)): targets = [0, lo) u [lo+m, l) u [L, L+K) -> ext slots
@@ -295,52 +296,61 @@ struct ConvTargets {
     size_t out_so, out_si;  // output limb base of set s: (s / inner) * out_so + (s % inner) * out_si
 };
 
+__device__ __forceinline__ uint32_t conv_target(const ConvTargets &ct, uint32_t tn, uint32_t lo, uint32_t m) {
+    if (ct.mode == 1 || tn < lo) return tn;
+    if (tn < ct.l - m) return tn + m;
+    return ct.L + (tn - (ct.l - m));
+}
+
 __global__ __launch_bounds__(256) void k_convert(const BasisDev *__restrict__ bases, SetLayout lay,
                                                   const uint64_t *__restrict__ y, const uint32_t *__restrict__ u,
                                                   ConvTargets ct, uint64_t *__restrict__ out, uint32_t n,
                                                   const PrimeConsts *__restrict__ pc) {
-    const uint32_t k = blockIdx.x * blockDim.x + threadIdx.x;
+    extern __shared__ uint64_t hs[];  // [m][CT]
     const uint32_t s = blockIdx.z;
-    const uint32_t si = lay.per_set_basis ? s % lay.inner : 0;
-    const BasisDev &B = bases[si];
-    const uint32_t m = B.m;
-    const uint32_t lo = B.first;
+    const BasisDev &B = bases[lay.per_set_basis ? s % lay.inner : 0];
+    const uint32_t m = B.m, lo = B.first;
     const uint32_t ntarget = ct.mode == 0 ? ct.l - m + ct.K : ct.l;
-    const uint32_t tn0 = blockIdx.y * TT;
-    if (tn0 >= ntarget || k >= n) return;
-    uint32_t tg[TT];
-    uint32_t nt = min((uint32_t)TT, ntarget - tn0);
-#pragma unroll
-    for (int a = 0; a < TT; a++) {
-        uint32_t tn = tn0 + (a < (int)nt ? a : 0);
-        uint32_t t;
-        if (ct.mode == 1) t = tn;
-        else if (tn < lo) t = tn;
-        else if (tn < ct.l - m) t = tn + m;
-        else t = ct.L + (tn - (ct.l - m));
-        tg[a] = t;
+    const uint32_t tn0 = blockIdx.y * CT;
+    if (tn0 >= ntarget) return;  // whole workgroup leaves together
+    const uint32_t nt = min((uint32_t)CT, ntarget - tn0);
+    for (uint32_t x = threadIdx.x; x < m * CT; x += blockDim.x) {
+        const uint32_t a = x % CT, i = x / CT;
+        const uint32_t t = conv_target(ct, tn0 + min(a, nt - 1), lo, m);
+        hs[x] = B.H[(size_t)t * m + i];
     }
+    __syncthreads();
+    const uint32_t k = blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= n) return;
     const uint64_t *yb = y + (s / lay.inner) * lay.so + (s % lay.inner) * lay.si + lay.off + k;
-    Acc128 acc[TT];
+    Split3 sp[CT];
+    Acc128 acc[CT];
 #pragma unroll
-    for (int a = 0; a < TT; a++) acc[a] = {0, 0};
-    uint32_t cnt = 0;
-    for (uint32_t i = 0; i < m; i++) {
-        const uint64_t yv = yb[(size_t)i * n];
+    for (int a = 0; a < CT; a++) {
+        sp[a] = {0, 0, 0};
+        acc[a] = {0, 0};
+    }
+    uint64_t ynext = yb[0];
+    for (uint32_t i0 = 0; i0 < m; i0 += SPLIT_CHUNK) {
+        const uint32_t i1 = min(m, i0 + SPLIT_CHUNK);
+#pragma unroll 5
+        for (uint32_t i = i0; i < i1; i++) {
+            const uint64_t yv = ynext;  // loads run one input ahead
+            ynext = yb[(size_t)min(i + 1, m - 1) * n];
+            const uint32_t yl = (uint32_t)(yv & M30), yh = (uint32_t)(yv >> 30);
+            const uint64_t *hr = hs + i * CT;
 #pragma unroll
-        for (int a = 0; a < TT; a++) mac(acc[a], yv, B.H[(size_t)tg[a] * m + i]);
-        if (++cnt == 255) {
-            cnt = 1;  // the reduced value counts as one term
-#pragma unroll
-            for (int a = 0; a < TT; a++) acc[a] = {reduce128(acc[a].lo, acc[a].hi, pc[tg[a]]), 0};
+            for (int a = 0; a < CT; a++) smac(sp[a], yl, yh, hr[a]);
         }
+#pragma unroll
+        for (int a = 0; a < CT; a++) sflush(acc[a], sp[a]);
     }
     const uint64_t uu = u[(size_t)s * n + k];
     uint64_t *ob = out + (s / lay.inner) * ct.out_so + (s % lay.inner) * ct.out_si + k;
 #pragma unroll
-    for (int a = 0; a < TT; a++) {
+    for (int a = 0; a < CT; a++) {
         if (a >= (int)nt) break;
-        const uint32_t t = tg[a];
+        const uint32_t t = __builtin_amdgcn_readfirstlane(conv_target(ct, tn0 + a, lo, m));
         mac(acc[a], uu, B.negB[t]);
         const uint32_t slot = (ct.mode == 0 && t >= ct.L) ? ct.l + (t - ct.L) : t;
         ob[(size_t)slot * n] = reduce128(acc[a].lo, acc[a].hi, pc[t]);
@@ -445,27 +455,53 @@ __global__ void k_rescale_final(const uint64_t *__restrict__ in, const uint64_t 
 }
 
 // ---------------------------------------------------------------------
-// BSGS multiply-accumulate: inner[g][b][c][i][k] = sum_bb pt[g][bb][i][k] rot_bb[b][c][i][k]
-// rot_0 is the input itself; rot_bb (bb >= 1) at rot + (bb - 1) * ctsize.
+// BSGS multiply-accumulate for every giant step at once:
+//   inner[g][col][i][k] = sum_bb pt[g][bb][i][k] rot_bb[col][i][k]
+// (col = ciphertext * 2 + polynomial; rot_0 is the input itself, rot_bb for
+// bb >= 1 at rot + (bb - 1) * ctsize).  Thread (k, col) keeps its rotated
+// inputs for up to MAC_B baby steps in registers (split30) and streams the
+// diagonals: lanes run over 16 consecutive coefficients, so every diagonal
+// read is a 128-byte run shared by the 4 columns of a wave.  Baby steps
+// beyond MAC_B are added in further passes.
 // ---------------------------------------------------------------------
-__global__ void k_bsgs_mac(const uint64_t *__restrict__ pt, const uint64_t *__restrict__ in,
-                           const uint64_t *__restrict__ rot, uint64_t *__restrict__ inner,
-                           const PrimeConsts *__restrict__ pc, uint32_t n, uint32_t l, uint32_t bs, uint32_t gs,
-                           size_t ctsize /* B*2*l*n */) {
-    for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < ctsize;
-         idx += (size_t)gridDim.x * blockDim.x) {
-        const uint32_t k = idx % n;
-        const uint32_t i = (idx / n) % l;
-        const size_t ik = (size_t)i * n + k;
-        const size_t per = (size_t)l * n;
-        for (uint32_t g = 0; g < gs; g++) {
-            Acc128 a{0, 0};
-            for (uint32_t bb = 0; bb < bs; bb++) {
-                const uint64_t x = bb == 0 ? in[idx] : rot[(size_t)(bb - 1) * ctsize + idx];
-                mac(a, pt[((size_t)g * bs + bb) * per + ik], x);
+constexpr int MAC_K = 16, MAC_C = 16, MAC_B = 32;
+
+__global__ __launch_bounds__(256) void k_bsgs_mac(const uint64_t *__restrict__ pt, const uint64_t *__restrict__ in,
+                                                   const uint64_t *__restrict__ rot, uint64_t *__restrict__ inner,
+                                                   const PrimeConsts *__restrict__ pc, uint32_t n, uint32_t l,
+                                                   uint32_t bs, uint32_t gs, uint32_t ncols, size_t ctsize,
+                                                   uint32_t b0) {
+    const uint32_t i = blockIdx.y;
+    const uint32_t k = blockIdx.x * MAC_K + threadIdx.x % MAC_K;
+    const uint32_t col = blockIdx.z * MAC_C + threadIdx.x / MAC_K;
+    if (col >= ncols) return;
+    const PrimeConsts P = pc[i];
+    const uint32_t nb = min((uint32_t)MAC_B, bs - b0);
+    const size_t off = ((size_t)col * l + i) * n + k;
+    uint64_t r[MAC_B];
+#pragma unroll
+    for (int bb = 0; bb < MAC_B; bb++) {
+        const uint32_t b = b0 + bb;
+        r[bb] = bb < (int)nb ? split30(b == 0 ? in[off] : rot[(size_t)(b - 1) * ctsize + off]) : 0;
+    }
+    const size_t pstride = (size_t)l * n;
+    for (uint32_t g = 0; g < gs; g++) {
+        const uint64_t *pg = pt + ((size_t)g * bs + b0) * pstride + (size_t)i * n + k;
+        Split3 sp{0, 0, 0};
+        Acc128 acc{0, 0};
+#pragma unroll
+        for (int bb = 0; bb < MAC_B; bb++) {
+            if (bb < (int)nb) {
+                const uint64_t p = pg[(size_t)bb * pstride];
+                smac(sp, (uint32_t)(p & M30), (uint32_t)(p >> 30), r[bb]);
             }
-            inner[(size_t)g * ctsize + idx] = reduce128(a.lo, a.hi, pc[i]);
+            if (bb % SPLIT_CHUNK == SPLIT_CHUNK - 1) sflush(acc, sp);
         }
+        sflush(acc, sp);
+        uint64_t v = reduce128(acc.lo, acc.hi, P);
+        uint64_t *o = inner + (size_t)g * ctsize + off;
+        if (b0) v = addm(v, *o, P.q);
+        *o = v;
     }
 }
 
@@ -523,8 +559,8 @@ static int keyswitch_core(ckks_ctx *c, LevelTables *lt, int B, int l, const uint
     {
         ConvTargets ct{0, (uint32_t)l, L, K, (size_t)beta * el * n, (size_t)el * n};
         const uint32_t maxt = l + K;  // upper bound on targets per digit
-        hipLaunchKernelGGL(k_convert, dim3((n + 255) / 256, (maxt + TT - 1) / TT, B * beta), dim3(256), 0, s,
-                           lt->d_digits, lay_up, w.y, w.u, ct, w.ext, n, c->d_pc);
+        hipLaunchKernelGGL(k_convert, dim3((n + 255) / 256, (maxt + CT - 1) / CT, B * beta), dim3(256),
+                           (size_t)c->alpha * CT * 8, s, lt->d_digits, lay_up, w.y, w.u, ct, w.ext, n, c->d_pc);
         LAUNCH_CHECK();
     }
     {
@@ -547,8 +583,8 @@ static int keyswitch_core(ckks_ctx *c, LevelTables *lt, int B, int l, const uint
     LAUNCH_CHECK();
     {
         ConvTargets ct{1, (uint32_t)l, L, K, (size_t)l * n, 0};
-        hipLaunchKernelGGL(k_convert, dim3((n + 255) / 256, (l + TT - 1) / TT, B * 2), dim3(256), 0, s,
-                           c->d_pbasis, lay_dn, w.acc, w.uP, ct, w.conv, n, c->d_pc);
+        hipLaunchKernelGGL(k_convert, dim3((n + 255) / 256, (l + CT - 1) / CT, B * 2), dim3(256),
+                           (size_t)K * CT * 8, s, c->d_pbasis, lay_dn, w.acc, w.uP, ct, w.conv, n, c->d_pc);
         LAUNCH_CHECK();
     }
     {
@@ -656,9 +692,12 @@ int op_bsgs(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, const 
     for (int b = 1; b < bs; b++)
         if ((e = op_rotate(c, in, rot + (size_t)(b - 1) * ct, B, l, rot_elt(c->n, b), baby[b], ksws, false, s)))
             return e;
-    hipLaunchKernelGGL(k_bsgs_mac, grid_for(ct), dim3(256), 0, s, diags, in, rot, inner, c->d_pc, c->n, (uint32_t)l,
-                       (uint32_t)bs, (uint32_t)gs, ct);
-    LAUNCH_CHECK();
+    for (int b0 = 0; b0 < bs; b0 += MAC_B) {
+        hipLaunchKernelGGL(k_bsgs_mac, dim3(c->n / MAC_K, l, (2 * B + MAC_C - 1) / MAC_C), dim3(256), 0, s, diags,
+                           in, rot, inner, c->d_pc, c->n, (uint32_t)l, (uint32_t)bs, (uint32_t)gs, (uint32_t)(2 * B),
+                           ct, (uint32_t)b0);
+        LAUNCH_CHECK();
+    }
     // giant steps accumulate into inner[0]
     for (int g = 1; g < gs; g++)
         if ((e = op_rotate(c, inner + (size_t)g * ct, inner, B, l, rot_elt(c->n, (uint64_t)g * bs), giant[g], ksws,

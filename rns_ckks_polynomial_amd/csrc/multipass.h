@@ -1,20 +1,27 @@
 // multipass.h -- NTT for ring degrees whose limb does not fit one workgroup's
-// LDS (n = 65536: 512 KiB per limb).  Four-step split n = n1 * n2: a first
-// pass of n2 column transforms of length n1 (strided), a twiddle by the
-// inner roots, then n1 row transforms of length n2; the last pass writes the
-// result in natural order.
+// LDS (n = 65536: 512 KiB per limb).
+//
+// Four-step split n = n1 n2 (256 x 256), index i = n2 i1 + i2, j = j1 + n1 j2:
+//   A_{j1 + n1 j2} = sum_{i2} psi2^{i2 (2 j2 + 1)} [ T[j1][i2] sum_{i1} a_{n2 i1 + i2} psi1^{i1 (2 j1 + 1)} ]
+// with psi1 = psi^n2, psi2 = psi^n1 (primitive 2*256-th roots) and the cross
+// twiddle T[j1][i2] = psi^{i2 (2 j1 + 1 - n1)}: a column pass of length-256
+// negacyclic NTTs, the twiddle, then a row pass of length-256 negacyclic NTTs
+// whose outputs land transposed in natural order.  The inverse runs the
+// mirror image.  One pass is out of place, through a context-owned scratch,
+// in chunks of MP_CHUNK limbs.
 #pragma once
 #include "ctx_internal.h"
 
 namespace ckks {
 
+constexpr uint32_t MP_N1 = 256, MP_LOG1 = 8;
+constexpr uint32_t MP_CHUNK = 64;  // limbs per scratch pass (64 x 512 KiB = 32 MiB)
+
 struct MultipassPlan {
-    uint32_t n1 = 0, n2 = 0, log1 = 0, log2 = 0;
-    // Per prime: column-stage twiddles (length-n1 merged-psi table of the
-    // 2*n1-th root psi^(n2)), the cross twiddles psi^((2 j1 + 1) i2) ... see multipass.hip
-    uint64_t *d_tw1f = nullptr, *d_tw1i = nullptr;  // [ntot][n1][2]
-    uint64_t *d_tw2f = nullptr, *d_tw2i = nullptr;  // [ntot][n2][2]
-    uint64_t *d_twxf = nullptr, *d_twxi = nullptr;  // [ntot][n][2] cross twiddles
+    uint64_t *d_tw256f = nullptr, *d_tw256i = nullptr;  // [ntot][256][2]  (psi^256)^(+-bitrev8(k)), Shoup
+    uint64_t *d_cross = nullptr;                         // [ntot][256 j1][256 i2][2]  T, Shoup
+    uint64_t *d_crossinvT = nullptr;                     // [ntot][256 i2][256 j1][2]  T^-1 transposed, Shoup
+    uint64_t *d_scratch = nullptr;                       // [MP_CHUNK][n]
     std::vector<void *> owned;
 };
 

@@ -70,21 +70,21 @@ def words(seed: int, tag: int, j, count: int) -> np.ndarray:
 def uniform_mod(seed: int, tag: int, stream_ids, moduli, n: int) -> np.ndarray:
     """Uniform residues: out[r, i] in [0, moduli[r]) for stream stream_ids[r]."""
     stream_ids = np.atleast_1d(np.asarray(stream_ids, dtype=np.uint64))
-    q = np.atleast_1d(np.asarray(moduli, dtype=np.uint64))[:, None]
-    base = words(seed, tag, stream_ids, n)  # [r, n]
-    out = np.zeros_like(base)
-    done = np.zeros(base.shape, dtype=bool)
-    v = base
+    q = np.broadcast_to(np.atleast_1d(np.asarray(moduli, dtype=np.uint64))[:, None], (len(stream_ids), n))
+    base = words(seed, tag, stream_ids, n).ravel()  # [r * n]
+    q = q.ravel()
+    out = np.empty_like(base)
+    pending = np.arange(base.size)
+    v = None
     for r in range(MAX_TRIES):
-        v = splitmix(base, np.uint64(r)) & MASK60
-        take = (~done) & (v < q)
-        out[take] = v[take]
-        done |= take
-        if done.all():
-            return out
-    fallback = ~done
-    out[fallback] = (v % q)[fallback]
-    return out
+        v = splitmix(base[pending], np.uint64(r)) & MASK60
+        take = v < q[pending]
+        out[pending[take]] = v[take]
+        pending = pending[~take]
+        if pending.size == 0:
+            return out.reshape(len(stream_ids), n)
+    out[pending] = v[~take] % q[pending]
+    return out.reshape(len(stream_ids), n)
 
 
 def ternary(seed: int, tag: int, j: int, n: int) -> np.ndarray:

@@ -40,3 +40,21 @@ def mismatch(a, b) -> str:
         return f"shape {a.shape} vs {b.shape}"
     bad = np.argwhere(a != b)
     return f"{len(bad)} mismatches, first at {tuple(bad[0]) if len(bad) else None}"
+
+
+def gfill(g, shape, seed, tag, stream0=0, first_prime=0):
+    """Seeded uniform residues generated on the GPU (the library's fill kernel)."""
+    t = torch.empty(shape, dtype=torch.uint64, device="cuda")
+    g.fill_uniform(t, seed, tag, stream0, first_prime)
+    return t
+
+
+def cfill(o, seed, tag, count, nl, stream0=0, first_prime=0):
+    """The same residues regenerated on the CPU: [count][nl][n]."""
+    from rns_ckks_polynomial_amd import synth
+    mods = np.tile(o.primes[first_prime:first_prime + nl], count)
+    return synth.uniform_mod(seed, tag, np.arange(count * nl) + stream0, mods, o.n).reshape(count, nl, o.n)
+
+
+def say(msg):
+    print(msg, flush=True)
