@@ -1,15 +1,20 @@
 #!/usr/bin/env python3
 """Benchmark of the RNS-CKKS hot path on one MI355X.
 
-Workload (n = 2048, 112 main primes + 28 special primes, dnum = 4, batch of
-8 ciphertexts, all inputs seeded and resident in HBM before timing):
+Workload (ring degree 2048, 112 main primes + 28 special primes, dnum = 4,
+batch of 8 ciphertexts; every input seeded and resident in HBM before the
+timed region):
   one step = ct x ct tensor + relinearise + rescale on 8 pairs
-           + BSGS 32 x 32 plaintext-matrix x ciphertext (1024 diagonals,
-             31 baby + 31 giant rotations per ciphertext) + rescale on 8 cts.
-That is 8 + 8 * 62 = 504 key switches per step, plus every other step of the
-path (NTT/iNTT, tensor, Galois automorphisms, base conversion, rescale, MAC).
+           + BSGS 32 x 32 plaintext-matrix x ciphertext on 8 ciphertexts
+             (1024 diagonals; 31 baby + 31 giant rotations each) + rescale.
+That is 8 + 8 * 62 = 504 key switches per step, and every other step of the
+path (NTT/iNTT, tensor, Galois automorphisms, exact base conversion,
+rescale, plaintext multiply-accumulate).
 
-Prints one JSON line.  `value` = key switches per second over the whole step.
+Output: one JSON line.  value = key switches per second over whole steps.
+After the timed region the same step runs again with the library's
+per-launch event profiler on, giving each kernel's average launch time; the
+dominant kernel's achieved rate is reported against its roofline.
 """
 from __future__ import annotations
 
@@ -23,7 +28,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 N, L, K, DNUM, BATCH, BS, GS = 2048, 112, 28, 4, 8, 32, 32
+ALPHA = (L + DNUM - 1) // DNUM
+BETA = (L + ALPHA - 1) // ALPHA
 HBM_PEAK_GBS = 8000.0
+# VALU: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz; v_mad_u64_u32 (32x32+64) issues at full rate.
+VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
+LIMB = N * 8
 
 
 def parse():
@@ -31,14 +41,17 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--profile-steps", type=int, default=1)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     return p.parse_args()
 
 
 def cpu_baseline(budget_s: float):
-    """The oracle as it stands, timed on this host: key switches at the same
-    shape (relinearisation of ct x ct at 112 primes), repeated until the budget."""
+    """The oracle as it stands, timed on this host: relinearisation key switches
+    at the same shape (ct x ct at 112 primes), repeated until the budget."""
     import numpy as np
 
     import oracle
@@ -49,23 +62,47 @@ def cpu_baseline(budget_s: float):
     b = synth.uniform_mod(2, synth.TAG_CT, np.arange(2 * L), mods, N).reshape(2, L, N)
     key = synth.uniform_mod(3, synth.TAG_KEY, np.arange(DNUM * 2 * (L + K)), np.tile(o.primes, DNUM * 2),
                             N).reshape(DNUM, 2, L + K, N)
+    o.mul_tensor_relin(a, b, key, L)  # warm (thread pool, page faults)
     done, t0 = 0, time.perf_counter()
     while True:
         o.mul_tensor_relin(a, b, key, L)
         done += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or done >= 64:
+        if el >= budget_s or done >= 200:
             break
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = int(os.environ.get("OMP_NUM_THREADS", 0)) or os.cpu_count() or 1
     return {"value": done / el, "unit": "key-switches/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} x (tensor + relinearise) of one ciphertext pair at n=2048, 112+28 primes, "
-                      f"dnum=4 ({el:.1f} s, OpenMP over coefficients/limbs)"}
+            "sample": f"{done} x (tensor + relinearise) of one ciphertext pair at n=2048, 112+28 primes, dnum=4, "
+                      f"{el:.1f} s, OpenMP over limbs/coefficients"}
+
+
+def kernel_work():
+    """Algorithmic work per launch of each kernel at this workload.
+    bytes: residues the step must read + write once (twiddles/tables excluded);
+    mads: 32x32-bit multiply-adds, 4 per 60x60-bit product (the minimum on a 32-bit multiplier)."""
+    B, l = BATCH, L
+    modup_macs = B * BETA * ALPHA * (l - ALPHA + K) * N
+    moddown_macs = B * 2 * K * l * N
+    mac_macs = GS * BS * 2 * B * l * N
+    return {
+        "ks_modup_convert": {"mads": 4 * modup_macs, "bytes": (B * l + B * BETA * (l + K - ALPHA)) * LIMB},
+        "ks_moddown_convert": {"mads": 4 * moddown_macs, "bytes": (B * 2 * K + B * 2 * l) * LIMB},
+        "bsgs_mac": {"mads": 4 * mac_macs, "bytes": (GS * BS * l + BS * 2 * B * l + GS * 2 * B * l) * LIMB},
+        "ks_ntt_ext": {"bytes": 2 * B * BETA * (l + K - ALPHA) * LIMB, "limbs": B * BETA * (l + K - ALPHA)},
+        "ks_intt_modup": {"bytes": 2 * B * l * LIMB, "limbs": B * l},
+        "ks_intt_moddown": {"bytes": 2 * B * 2 * K * LIMB, "limbs": B * 2 * K},
+        "ks_ntt_moddown": {"bytes": 2 * B * 2 * l * LIMB, "limbs": B * 2 * l},
+        "ks_inner_product": {"bytes": (B * BETA * (l + K) + 2 * BETA * (l + K) + 2 * B * (l + K)) * LIMB},
+        "ntt_fwd": {"bytes": 2 * B * 2 * l * LIMB, "limbs": B * 2 * l},
+        "ntt_inv": {"bytes": 2 * B * 2 * l * LIMB, "limbs": B * 2 * l},
+    }
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this build runs on one GPU only: the hot path is measured on one "
+                                   "GPU's share; pass --gpus 1"}))
         sys.exit(2)
     import torch
 
@@ -91,11 +128,22 @@ def main():
     res = torch.empty((BATCH, 2, L - 1, N), dtype=u64, device=dev)
     lt = torch.empty_like(res)
     ws = g.workspace(max(g.workspace_size("bsgs", BATCH, L, BS, GS), g.workspace_size("relin", BATCH, L)))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    parts = {"mul_relin_rescale_ms": 0.0, "bsgs_ms": 0.0}
 
-    def step():
+    def step(timed=False):
+        if timed:
+            ev[0].record()
         g.mul_tensor_relin(a, b, rlk, out=prod, ws=ws)
         g.rescale(prod, out=res, ws=ws)
+        if timed:
+            ev[1].record()
         g.bsgs_linear_transform(a, diags, BS, GS, baby, giant, do_rescale=True, out=lt, ws=ws)
+        if timed:
+            ev[2].record()
+            ev[2].synchronize()
+            parts["mul_relin_rescale_ms"] += ev[0].elapsed_time(ev[1])
+            parts["bsgs_ms"] += ev[1].elapsed_time(ev[2])
 
     for _ in range(args.warmup):
         step()
@@ -108,11 +156,17 @@ def main():
     ms = el / args.steps * 1e3
     ks_per_step = BATCH + BATCH * (BS + GS - 2)
 
-    # standalone limb-NTT throughput on the same batch (forward + inverse of [8][2][112] limbs)
+    # split of the step (separate pass, event-bracketed)
+    for _ in range(2):
+        step(timed=True)
+    mr_ms, bsgs_ms = parts["mul_relin_rescale_ms"] / 2, parts["bsgs_ms"] / 2
+
+    # standalone batched NTT throughput on the same [8][2][112] limbs
     x = a.clone().view(BATCH * 2, L, N)
     reps = 50
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    g.ntt_fwd(x); g.ntt_inv(x)
+    g.ntt_fwd(x)
+    g.ntt_inv(x)
     e0.record()
     for _ in range(reps):
         g.ntt_fwd(x)
@@ -122,26 +176,73 @@ def main():
     ntt_ms = e0.elapsed_time(e1) / (2 * reps)
     limbs = BATCH * 2 * L
     ntt_rate = limbs / (ntt_ms * 1e-3)
-    ntt_bytes = limbs * N * 8 * 2  # read + write each limb once
-    roofline = {"bound": "hbm", "kernel": "k_ntt2048 (fwd, [16][112] limbs)", "achieved": ntt_bytes / (ntt_ms * 1e-3) / 1e9,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None}
-    roofline["frac"] = roofline["achieved"] / roofline["peak"]
+
+    # per-kernel launch times (library event profiler) over profiled steps + the NTT pair
+    g.profile_begin()
+    for _ in range(args.profile_steps):
+        step()
+    g.ntt_fwd(x)
+    g.ntt_inv(x)
+    prof = g.profile_end()
+    work = kernel_work()
+    kernels = {}
+    for name, (cnt, tot, mn, mx) in prof.items():
+        avg = tot / cnt
+        row = {"launches": cnt, "avg_us": avg * 1e3, "total_ms_per_step": tot / args.profile_steps}
+        w = work.get(name, {})
+        if "bytes" in w:
+            row["algo_GBps"] = w["bytes"] / (avg * 1e-3) / 1e9
+        if "mads" in w:
+            row["algo_Tmads"] = w["mads"] / (avg * 1e-3) / 1e12
+        kernels[name] = row
+    for name in ("ntt_fwd", "ntt_inv"):
+        if name in kernels:
+            kernels[name]["total_ms_per_step"] = 0.0  # standalone call, not part of the step
+    step_kernels = {k: v for k, v in kernels.items() if k not in ("ntt_fwd", "ntt_inv")}
+    dom = max(step_kernels, key=lambda k: step_kernels[k]["total_ms_per_step"])
+    dw, drow = work.get(dom, {}), kernels[dom]
+    if "mads" in dw:
+        roofline = {"bound": "alu", "kernel": dom, "achieved": drow["algo_Tmads"], "peak": VALU_PEAK_TOPS,
+                    "unit": "T int32-MAD/s", "traffic": None,
+                    "work_per_launch": f"{dw['mads']} 32x32-bit multiply-adds (4 per 60x60-bit product)"}
+    else:
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": drow.get("algo_GBps"), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "traffic": None, "work_per_launch": f"{dw.get('bytes')} bytes"}
+    roofline["frac"] = roofline["achieved"] / roofline["peak"] if roofline["achieved"] else None
+    roofline["avg_launch_us"] = drow["avg_us"]
+    ntt_row = kernels.get("ntt_fwd", {})
+    ntt_roof = {"bound": "hbm", "kernel": "ntt_fwd [16][112] limbs", "achieved": ntt_row.get("algo_GBps"),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "avg_launch_us": ntt_row.get("avg_us"),
+                "work_per_launch": f"{work['ntt_fwd']['bytes']} bytes (each limb read and written once)"}
+    if ntt_roof["achieved"]:
+        ntt_roof["frac"] = ntt_roof["achieved"] / HBM_PEAK_GBS
 
     out = {
         "metric": "limb-NTTs/s + key-switches/s @n=2048,112 primes; % HBM roofline",
         "value": ks_per_step / (ms * 1e-3),
         "unit": "key-switches/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u64 (exact 60-bit RNS)",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u64",
         "data": "synthetic (seeded SplitMix64 residues, resident in HBM)",
-        "config": {"workload": "config 2 + config 3 shapes: n=2048, 112+28 primes, dnum=4, batch 8; "
-                               "ct x ct tensor+relin+rescale and BSGS 32x32 linear transform + rescale",
+        "config": {"workload": "n=2048, 112+28 primes, dnum=4, batch 8: ct x ct tensor+relin+rescale (config 2) "
+                               "and BSGS 32x32 linear transform + rescale at 112 primes (config 3)",
                    "global_batch": BATCH, "parallelism": "single GPU"},
         "key_switches_per_step": ks_per_step,
         "limb_ntts_per_s": ntt_rate,
-        "linear_transforms_per_s": None,
+        "linear_transforms_per_s": BATCH / (bsgs_ms * 1e-3),
+        "ct_mults_per_s": BATCH / (mr_ms * 1e-3),
+        "step_split_ms": {"mul_relin_rescale": mr_ms, "bsgs": bsgs_ms},
         "roofline": roofline,
+        "ntt_roofline": ntt_roof,
+        "kernels": kernels,
     }
+    if args.calibrate_copy:
+        src = torch.empty(1 << 27, dtype=u64, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = 2 * src.numel() * 8
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out))

@@ -20,6 +20,11 @@ class CkksError(RuntimeError):
         self.code = code
 
 
+class KernelStat(C.Structure):
+    _fields_ = [("name", C.c_char * 48), ("launches", C.c_int), ("total_ms", C.c_double),
+                ("min_ms", C.c_double), ("max_ms", C.c_double)]
+
+
 class Params(C.Structure):
     _fields_ = [("n", C.c_uint32), ("L", C.c_uint32), ("K", C.c_uint32), ("dnum", C.c_uint32)]
 
@@ -47,6 +52,8 @@ SIGNATURES = {
     "ckks_bsgs_linear_transform": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p,
                                              C.c_int, C.c_int, C.POINTER(C.c_void_p), C.POINTER(C.c_void_p),
                                              C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "ckks_profile_begin": (C.c_int, [C.c_void_p]),
+    "ckks_profile_end": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.POINTER(C.c_int)]),
     "ckks_fill_uniform": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_uint64, C.c_uint64,
                                     C.c_uint64, C.c_void_p]),
 }

@@ -137,6 +137,18 @@ class Context:
                                                        _stream()), "ckks_bsgs_linear_transform")
         return out
 
+    # ------------------------------------------------------------ profiling
+    def profile_begin(self):
+        nat.check(nat.lib().ckks_profile_begin(self._h), "ckks_profile_begin")
+
+    def profile_end(self) -> dict:
+        """{kernel name: (launches, total_ms, min_ms, max_ms)} since profile_begin."""
+        buf = (nat.KernelStat * 64)()
+        cnt = C.c_int()
+        nat.check(nat.lib().ckks_profile_end(self._h, buf, 64, C.byref(cnt)), "ckks_profile_end")
+        return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms, buf[i].min_ms, buf[i].max_ms)
+                for i in range(min(cnt.value, 64))}
+
     def fill_uniform(self, dst: torch.Tensor, seed: int, tag: int, stream0: int = 0, first_prime: int = 0):
         """Seeded uniform residues (SplitMix64 streams, see include/ckks_synth.h)."""
         nl = dst.shape[-2]

@@ -357,6 +357,10 @@ extern "C" void ckks_ctx_destroy(ckks_ctx *c) {
         delete kv.second;
     }
     if (c->mp) multipass_free(c);
+    if (c->prof) {
+        for (hipEvent_t e : c->prof->pool) (void)hipEventDestroy(e);
+        delete c->prof;
+    }
     for (void *p : c->owned) hipFree(p);
     hipSetDevice(dev_saved);
     delete c;

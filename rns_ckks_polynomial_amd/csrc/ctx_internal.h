@@ -6,6 +6,7 @@
 
 #include <map>
 #include <mutex>
+#include <string>
 #include <vector>
 
 #include "../../include/ckks_gpu.h"
@@ -24,6 +25,22 @@ struct LevelTables {
 };
 
 struct MultipassPlan;  // large-n NTT tables (n > 2048)
+
+// Optional per-launch timing with HIP events (enabled by ckks_profile_begin).
+struct Profiler {
+    bool on = false;
+    std::vector<std::string> names;
+    struct Rec {
+        int name;
+        hipEvent_t a, b;
+    };
+    std::vector<Rec> recs;
+    std::vector<hipEvent_t> pool;
+    size_t used = 0;
+    std::mutex mu;
+    hipEvent_t take();
+    int name_id(const char *n);
+};
 
 }  // namespace ckks
 
@@ -45,7 +62,31 @@ struct ckks_ctx {
     std::map<uint32_t, ckks::LevelTables *> levels;
     std::mutex mu;
     ckks::MultipassPlan *mp = nullptr;
+    ckks::Profiler *prof = nullptr;
 };
+
+namespace ckks {
+// Records HIP events around the launches made in its scope when profiling is on.
+struct ProfScope {
+    const ckks_ctx *c;
+    hipStream_t s;
+    int name = -1;
+    hipEvent_t b{};
+    ProfScope(const ckks_ctx *ctx, const char *nm, hipStream_t st) : c(ctx), s(st) {
+        if (c->prof && c->prof->on) {
+            std::lock_guard<std::mutex> g(c->prof->mu);
+            name = c->prof->name_id(nm);
+            hipEvent_t a = c->prof->take();
+            b = c->prof->take();
+            (void)hipEventRecord(a, s);
+            c->prof->recs.push_back({name, a, b});
+        }
+    }
+    ~ProfScope() {
+        if (name >= 0) (void)hipEventRecord(b, s);
+    }
+};
+}  // namespace ckks
 
 namespace ckks {
 // host-side number theory (independent of any reference code)

@@ -54,6 +54,22 @@ struct MapStrided {  // [count][nl][n], limb r -> prime first + r
     }
 };
 
+struct MapBatched {  // limb r of ciphertext b at src + b * src_stride + r * n -> dst [B][nl][n]
+    const uint64_t *src;
+    size_t src_stride;
+    uint64_t *dst;
+    uint32_t n, nl;
+    const uint64_t *scale;  // optional, indexed by prime index
+    __device__ __forceinline__ void get(int blk, const uint64_t *&s, uint64_t *&d, int &prime,
+                                        const uint64_t *&sc) const {
+        const uint32_t b = blk / nl, r = blk % nl;
+        prime = r;
+        s = src + b * src_stride + (size_t)r * n;
+        d = dst + (size_t)blk * n;
+        sc = scale ? scale + 2 * prime : nullptr;
+    }
+};
+
 struct MapExt {  // converted limbs [B][beta][l+K][n]; skips the digit's own primes
     uint64_t *ext;
     uint32_t n, l, L, K, beta, alpha;
@@ -134,8 +150,9 @@ __global__ __launch_bounds__(256) void k_ntt2048(Map map, const PrimeConsts *__r
 }
 
 template <class Map>
-static int launch_ntt(const ckks_ctx *c, const Map &map, int nblk, bool inverse, hipStream_t s) {
+static int launch_ntt(const ckks_ctx *c, const Map &map, int nblk, bool inverse, hipStream_t s, const char *name) {
     if (nblk <= 0) return CKKS_OK;
+    ProfScope ps(c, name, s);
     if (c->n == 2048) {
         if (inverse)
             hipLaunchKernelGGL((k_ntt2048<Map, true>), dim3(nblk), dim3(256), 0, s, map, c->d_pc, c->d_tw_fwd,
@@ -151,7 +168,7 @@ static int launch_ntt(const ckks_ctx *c, const Map &map, int nblk, bool inverse,
 
 int op_ntt(const ckks_ctx *c, uint64_t *x, int count, int first, int nlimbs, bool inverse, hipStream_t s) {
     MapStrided m{x, x, c->n, (uint32_t)nlimbs, (uint32_t)first, nullptr};
-    return launch_ntt(c, m, count * nlimbs, inverse, s);
+    return launch_ntt(c, m, count * nlimbs, inverse, s, inverse ? "ntt_inv" : "ntt_fwd");
 }
 
 // =====================================================================
@@ -174,8 +191,11 @@ int op_pointwise_mul(const ckks_ctx *c, const uint64_t *a, const uint64_t *b, ui
                      int nlimbs, hipStream_t s) {
     const size_t total = (size_t)count * nlimbs * c->n;
     if (!total) return CKKS_OK;
-    hipLaunchKernelGGL(k_pointwise, grid_for(total), dim3(256), 0, s, a, b, out, c->d_pc, c->n, (uint32_t)nlimbs,
-                       (uint32_t)first, total);
+    {
+        ProfScope ps_(c, "pointwise_mul", s);
+        hipLaunchKernelGGL(k_pointwise, grid_for(total), dim3(256), 0, s, a, b, out, c->d_pc, c->n, (uint32_t)nlimbs,
+                           (uint32_t)first, total);
+    }
     LAUNCH_CHECK();
     return CKKS_OK;
 }
@@ -189,17 +209,6 @@ __global__ void k_prep_relin(const uint64_t *__restrict__ a, const uint64_t *__r
         const uint32_t i = r / n;
         const size_t off = (bi * 2 + 1) * per + r;
         d[e] = mulm(a[off], b[off], pc[i].q, pc[i].mu);
-    }
-}
-
-// d[b][i][j] = in[b][1][i][galois_src(j)]
-__global__ void k_prep_rotate(const uint64_t *__restrict__ in, uint64_t *__restrict__ d, uint32_t g, uint32_t n,
-                              uint32_t l, size_t total) {
-    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x) {
-        const size_t per = (size_t)l * n;
-        const size_t bi = e / per, r = e % per;
-        const uint32_t j = r % n;
-        d[e] = in[(bi * 2 + 1) * per + (r - j) + galois_src(j, g, n)];
     }
 }
 
@@ -357,28 +366,86 @@ __global__ __launch_bounds__(256) void k_convert(const BasisDev *__restrict__ ba
     }
 }
 
-// acc[b][c][e][k] = sum_j v_j key[j][c][gidx(e)][k],  v_j = e in digit j ? d[b][e][k] : ext[b][j][e][k]
-__global__ void k_inner(const uint64_t *__restrict__ d, const uint64_t *__restrict__ ext,
+// acc[b][c][e][k] = sum_j v_j[e][galois_src(k)] key[j][c][gidx(e)][k], where
+// v_j[e] = d[b][e] (NTT domain, own digit) or ext[b][j][e] (ModUp of digit j).
+// With g = 1 the gather is the identity.  With g != 1 this is the key switch
+// of sigma_g(d): exact centered ModUp commutes with the automorphism, so
+// permuting the extended digits equals extending the permuted polynomial.
+// One workgroup per (ciphertext, extended limb): each digit's limb is loaded
+// into LDS with coalesced reads and permuted from there; the key rows are
+// read in order.  (n = 2048: 8 coefficients per thread.)
+__global__ __launch_bounds__(256) void k_inner2048(const uint64_t *__restrict__ d, size_t d_stride,
+                                                    const uint64_t *__restrict__ ext,
+                                                    const uint64_t *__restrict__ key, uint64_t *__restrict__ acc,
+                                                    const PrimeConsts *__restrict__ pc, uint32_t l, uint32_t L,
+                                                    uint32_t K, uint32_t beta, uint32_t alpha, uint32_t g) {
+    constexpr uint32_t n = 2048;
+    __shared__ uint64_t buf[2][n];
+    const uint32_t el = l + K;
+    const uint32_t e = blockIdx.x % el;
+    const size_t b = blockIdx.x / el;
+    const uint32_t gi = e < l ? e : L + (e - l);
+    const uint32_t t = threadIdx.x;
+    Split3 s0[8], s1[8];
+#pragma unroll
+    for (int m = 0; m < 8; m++) s0[m] = s1[m] = {0, 0, 0};
+    for (uint32_t j = 0; j < beta; j++) {
+        const bool own = e >= j * alpha && e < min(l, (j + 1) * alpha);
+        const uint64_t *src = own ? d + b * d_stride + (size_t)e * n : ext + ((b * beta + j) * el + e) * n;
+        uint64_t *lb = buf[j & 1];
+#pragma unroll
+        for (int m = 0; m < 8; m++) lb[t + 256 * m] = src[t + 256 * m];
+        __syncthreads();
+        const uint64_t *kb = key + ((size_t)j * 2 * (L + K) + gi) * n;
+        const uint64_t *ka = kb + (size_t)(L + K) * n;
+#pragma unroll
+        for (int m = 0; m < 8; m++) {
+            const uint32_t k = t + 256 * m;
+            const uint64_t v = lb[galois_src(k, g, n)];
+            const uint32_t vl = (uint32_t)(v & M30), vh = (uint32_t)(v >> 30);
+            smac(s0[m], vl, vh, split30(kb[k]));
+            smac(s1[m], vl, vh, split30(ka[k]));
+        }
+    }
+    const PrimeConsts P = pc[gi];
+    uint64_t *o0 = acc + ((b * 2 + 0) * el + e) * n, *o1 = acc + ((b * 2 + 1) * el + e) * n;
+#pragma unroll
+    for (int m = 0; m < 8; m++) {
+        Acc128 a0{0, 0}, a1{0, 0};
+        sflush(a0, s0[m]);
+        sflush(a1, s1[m]);
+        o0[t + 256 * m] = reduce128(a0.lo, a0.hi, P);
+        o1[t + 256 * m] = reduce128(a1.lo, a1.hi, P);
+    }
+}
+
+// Generic-n version: one thread per output coefficient, gathered global reads.
+__global__ void k_inner(const uint64_t *__restrict__ d, size_t d_stride, const uint64_t *__restrict__ ext,
                         const uint64_t *__restrict__ key, uint64_t *__restrict__ acc,
                         const PrimeConsts *__restrict__ pc, uint32_t n, uint32_t l, uint32_t L, uint32_t K,
-                        uint32_t beta, uint32_t alpha, size_t total) {
+                        uint32_t beta, uint32_t alpha, uint32_t g, size_t total) {
     const uint32_t el = l + K;
     for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total;
          idx += (size_t)gridDim.x * blockDim.x) {
         const uint32_t k = idx % n;
         const uint32_t e = (idx / n) % el;
         const size_t b = idx / ((size_t)n * el);
-        const uint32_t g = e < l ? e : L + (e - l);
-        Acc128 a0{0, 0}, a1{0, 0};
+        const uint32_t gi = e < l ? e : L + (e - l);
+        const uint32_t ks = galois_src(k, g, n);
+        Split3 s0{0, 0, 0}, s1{0, 0, 0};
         for (uint32_t j = 0; j < beta; j++) {
             const bool own = e >= j * alpha && e < min(l, (j + 1) * alpha);
-            const uint64_t v = own ? d[(b * l + e) * n + k] : ext[((b * beta + j) * el + e) * n + k];
-            const uint64_t *kr = key + ((size_t)j * 2 * (L + K) + g) * n + k;
-            mac(a0, v, kr[0]);
-            mac(a1, v, kr[(size_t)(L + K) * n]);
+            const uint64_t v = own ? d[b * d_stride + (size_t)e * n + ks] : ext[((b * beta + j) * el + e) * n + ks];
+            const uint64_t *kr = key + ((size_t)j * 2 * (L + K) + gi) * n + k;
+            const uint32_t vl = (uint32_t)(v & M30), vh = (uint32_t)(v >> 30);
+            smac(s0, vl, vh, split30(kr[0]));
+            smac(s1, vl, vh, split30(kr[(size_t)(L + K) * n]));
         }
-        acc[((b * 2 + 0) * el + e) * n + k] = reduce128(a0.lo, a0.hi, pc[g]);
-        acc[((b * 2 + 1) * el + e) * n + k] = reduce128(a1.lo, a1.hi, pc[g]);
+        Acc128 a0{0, 0}, a1{0, 0};
+        sflush(a0, s0);
+        sflush(a1, s1);
+        acc[((b * 2 + 0) * el + e) * n + k] = reduce128(a0.lo, a0.hi, pc[gi]);
+        acc[((b * 2 + 1) * el + e) * n + k] = reduce128(a1.lo, a1.hi, pc[gi]);
     }
 }
 
@@ -414,6 +481,97 @@ __global__ void k_moddown_final(const uint64_t *__restrict__ acc, const uint64_t
         }
         if (ACCUM) r = addm(r, out[idx], q);
         out[idx] = r;
+    }
+}
+
+// n = 2048 fused ModDown tail: one workgroup per (ciphertext, polynomial,
+// limb i): NTT of the converted P-part in LDS, then
+//   out = (acc - NTT(conv)) P^-1 + extra   (MODE / ACCUM as k_moddown_final);
+// for rotations c0 is staged in LDS and permuted from there.
+template <int MODE, bool ACCUM>
+__global__ __launch_bounds__(256) void k_final2048(const uint64_t *__restrict__ acc, const uint64_t *__restrict__ conv,
+                                                    const uint64_t *__restrict__ pinv,
+                                                    const PrimeConsts *__restrict__ pc,
+                                                    const uint64_t *__restrict__ twf, const uint64_t *__restrict__ xa,
+                                                    const uint64_t *__restrict__ xb, uint32_t g,
+                                                    uint64_t *__restrict__ out, uint32_t l, uint32_t K) {
+    constexpr uint32_t n = 2048;
+    __shared__ uint64_t lds[n2048::LDS_WORDS];
+    const uint32_t i = blockIdx.x % l;
+    const uint32_t c = (blockIdx.x / l) % 2;
+    const size_t b = blockIdx.x / (2 * l);
+    const uint32_t t = threadIdx.x;
+    const PrimeConsts P = pc[i];
+    const uint64_t q = P.q;
+    const size_t per = (size_t)l * n;
+    uint64_t v[8];
+    const uint64_t *cv = conv + (size_t)blockIdx.x * n;
+#pragma unroll
+    for (int m = 0; m < 8; m++) v[m] = cv[t + 256 * m];
+    n2048::fwd(v, lds, twf + (size_t)i * n * 2, q);
+    if (MODE == 2 && c == 0) {  // stage c0 of this limb for the Galois gather
+        const uint64_t *c0 = xa + (b * 2) * per + (size_t)i * n;
+#pragma unroll
+        for (int m = 0; m < 8; m++) lds[t + 256 * m] = c0[t + 256 * m];
+        __syncthreads();
+    }
+    const uint64_t *ar = acc + ((b * 2 + c) * (l + K) + i) * n;
+    uint64_t *o = out + (size_t)blockIdx.x * n;
+    const uint64_t w = pinv[2 * i], wp = pinv[2 * i + 1];
+#pragma unroll
+    for (int m = 0; m < 8; m++) {
+        const uint32_t k = t + 256 * m;
+        uint64_t x = v[m];
+        x = x >= 2 * q ? x - 2 * q : x;
+        x = csub(x, q);
+        uint64_t r = shoup(subm(ar[k], x, q), w, wp, q);
+        if (MODE == 1) {
+            const size_t o0 = (b * 2) * per + (size_t)i * n + k, o1 = o0 + per;
+            uint64_t y;
+            if (c == 0) y = mulm(xa[o0], xb[o0], q, P.mu);
+            else y = addm(mulm(xa[o0], xb[o1], q, P.mu), mulm(xa[o1], xb[o0], q, P.mu), q);
+            r = addm(r, y, q);
+        } else if (MODE == 2) {
+            if (c == 0) r = addm(r, lds[galois_src(k, g, n)], q);
+        }
+        if (ACCUM) r = addm(r, o[k], q);
+        o[k] = r;
+    }
+}
+
+// n = 2048 fused rescale tail: per (ciphertext, polynomial, limb i < l-1):
+// centered lift of t = iNTT(c_{l-1}) to q_i, NTT in LDS, out = (c_i - .) q_{l-1}^-1.
+__global__ __launch_bounds__(256) void k_rescale2048(const uint64_t *__restrict__ in, const uint64_t *__restrict__ tl,
+                                                      const uint64_t *__restrict__ rinv,
+                                                      const PrimeConsts *__restrict__ pc,
+                                                      const uint64_t *__restrict__ twf, uint64_t *__restrict__ out,
+                                                      uint32_t l) {
+    constexpr uint32_t n = 2048;
+    __shared__ uint64_t lds[n2048::LDS_WORDS];
+    const uint32_t i = blockIdx.x % (l - 1);
+    const size_t bc = blockIdx.x / (l - 1);
+    const uint32_t t = threadIdx.x;
+    const uint64_t q = pc[i].q, ql = pc[l - 1].q;
+    const uint64_t qlm = ql >= q ? ql - q : ql;
+    uint64_t v[8];
+#pragma unroll
+    for (int m = 0; m < 8; m++) {
+        const uint64_t x = tl[bc * n + t + 256 * m];  // in [0, q_{l-1}), q_{l-1} < 2 q_i
+        uint64_t y = x >= q ? x - q : x;
+        if (x > (ql - 1) / 2) y = subm(y, qlm, q);
+        v[m] = y;
+    }
+    n2048::fwd(v, lds, twf + (size_t)i * n * 2, q);
+    const uint64_t *ci = in + (bc * l + i) * n;
+    uint64_t *o = out + (bc * (l - 1) + i) * n;
+    const uint64_t w = rinv[2 * i], wp = rinv[2 * i + 1];
+#pragma unroll
+    for (int m = 0; m < 8; m++) {
+        const uint32_t k = t + 256 * m;
+        uint64_t x = v[m];
+        x = x >= 2 * q ? x - 2 * q : x;
+        x = csub(x, q);
+        o[k] = shoup(subm(ci[k], x, q), w, wp, q);
     }
 }
 
@@ -458,11 +616,12 @@ __global__ void k_rescale_final(const uint64_t *__restrict__ in, const uint64_t 
 // BSGS multiply-accumulate for every giant step at once:
 //   inner[g][col][i][k] = sum_bb pt[g][bb][i][k] rot_bb[col][i][k]
 // (col = ciphertext * 2 + polynomial; rot_0 is the input itself, rot_bb for
-// bb >= 1 at rot + (bb - 1) * ctsize).  Thread (k, col) keeps its rotated
-// inputs for up to MAC_B baby steps in registers (split30) and streams the
-// diagonals: lanes run over 16 consecutive coefficients, so every diagonal
-// read is a 128-byte run shared by the 4 columns of a wave.  Baby steps
-// beyond MAC_B are added in further passes.
+// bb >= 1 at rot + (bb - 1) * ctsize).  A workgroup owns limb i, 16
+// coefficients and 16 columns; thread (k, col) keeps its rotated inputs for up
+// to MAC_B baby steps in registers (split30).  The diagonals of giant step g
+// (MAC_B x 16 values, 128-byte runs) are staged in LDS, double-buffered and
+// prefetched one giant step ahead, and read as broadcasts: every diagonal
+// element leaves HBM once.  Baby steps beyond MAC_B are added in further passes.
 // ---------------------------------------------------------------------
 constexpr int MAC_K = 16, MAC_C = 16, MAC_B = 32;
 
@@ -471,37 +630,54 @@ __global__ __launch_bounds__(256) void k_bsgs_mac(const uint64_t *__restrict__ p
                                                    const PrimeConsts *__restrict__ pc, uint32_t n, uint32_t l,
                                                    uint32_t bs, uint32_t gs, uint32_t ncols, size_t ctsize,
                                                    uint32_t b0) {
+    __shared__ uint64_t ps[2][MAC_B * MAC_K];
     const uint32_t i = blockIdx.y;
-    const uint32_t k = blockIdx.x * MAC_K + threadIdx.x % MAC_K;
+    const uint32_t k0 = blockIdx.x * MAC_K;
+    const uint32_t kl = threadIdx.x % MAC_K;
     const uint32_t col = blockIdx.z * MAC_C + threadIdx.x / MAC_K;
-    if (col >= ncols) return;
+    const bool active = col < ncols;
     const PrimeConsts P = pc[i];
     const uint32_t nb = min((uint32_t)MAC_B, bs - b0);
-    const size_t off = ((size_t)col * l + i) * n + k;
+    const size_t off = ((size_t)(active ? col : 0) * l + i) * n + k0 + kl;
     uint64_t r[MAC_B];
 #pragma unroll
     for (int bb = 0; bb < MAC_B; bb++) {
         const uint32_t b = b0 + bb;
-        r[bb] = bb < (int)nb ? split30(b == 0 ? in[off] : rot[(size_t)(b - 1) * ctsize + off]) : 0;
+        r[bb] = (active && bb < (int)nb) ? split30(b == 0 ? in[off] : rot[(size_t)(b - 1) * ctsize + off]) : 0;
     }
     const size_t pstride = (size_t)l * n;
+    // staging: thread t loads elements x = t and t + 256 of the MAC_B x MAC_K tile
+    auto pt_addr = [&](uint32_t g, uint32_t x) -> const uint64_t * {
+        const uint32_t bb = x / MAC_K, kk = x % MAC_K;
+        return pt + ((size_t)g * bs + b0 + min(bb, nb - 1)) * pstride + (size_t)i * n + k0 + kk;
+    };
+    uint64_t st0 = *pt_addr(0, threadIdx.x), st1 = *pt_addr(0, threadIdx.x + 256);
     for (uint32_t g = 0; g < gs; g++) {
-        const uint64_t *pg = pt + ((size_t)g * bs + b0) * pstride + (size_t)i * n + k;
+        uint64_t *buf = ps[g & 1];
+        buf[threadIdx.x] = st0;
+        buf[threadIdx.x + 256] = st1;
+        __syncthreads();
+        if (g + 1 < gs) {  // prefetch the next giant step's diagonals
+            st0 = *pt_addr(g + 1, threadIdx.x);
+            st1 = *pt_addr(g + 1, threadIdx.x + 256);
+        }
         Split3 sp{0, 0, 0};
         Acc128 acc{0, 0};
 #pragma unroll
         for (int bb = 0; bb < MAC_B; bb++) {
             if (bb < (int)nb) {
-                const uint64_t p = pg[(size_t)bb * pstride];
+                const uint64_t p = buf[bb * MAC_K + kl];
                 smac(sp, (uint32_t)(p & M30), (uint32_t)(p >> 30), r[bb]);
             }
             if (bb % SPLIT_CHUNK == SPLIT_CHUNK - 1) sflush(acc, sp);
         }
         sflush(acc, sp);
-        uint64_t v = reduce128(acc.lo, acc.hi, P);
-        uint64_t *o = inner + (size_t)g * ctsize + off;
-        if (b0) v = addm(v, *o, P.q);
-        *o = v;
+        if (active) {
+            uint64_t v = reduce128(acc.lo, acc.hi, P);
+            uint64_t *o = inner + (size_t)g * ctsize + off;
+            if (b0) v = addm(v, *o, P.q);
+            *o = v;
+        }
     }
 }
 
@@ -540,56 +716,77 @@ static size_t ks_words(const ckks_ctx *c, int B, int l, KsWs *w, uint64_t *base)
     return off;
 }
 
-// On entry w.d holds the NTT-domain polynomial to switch ([B][l][n]).  On exit
-// w.acc holds the Q-limbs of the accumulators and w.conv the NTT-domain
-// ModDown conversion; the caller runs the final kernel.
-static int keyswitch_core(ckks_ctx *c, LevelTables *lt, int B, int l, const uint64_t *key, const KsWs &w,
-                          hipStream_t s) {
+// ModUp of d ([B][l][n], NTT domain, ciphertext b at d + b * d_stride):
+// fills w.y, w.u and the NTT-domain extended digits w.ext.
+static int ks_modup(ckks_ctx *c, LevelTables *lt, int B, int l, const uint64_t *d, size_t d_stride, const KsWs &w,
+                    hipStream_t s) {
     const uint32_t n = c->n, K = c->K, L = c->L, el = l + K, beta = lt->beta;
     int e;
-    // y = iNTT(d) scaled by [Bhat_i^-1]
-    {
-        MapStrided m{w.d, w.y, n, (uint32_t)l, 0, lt->d_modup_scale};
-        if ((e = launch_ntt(c, m, B * l, true, s))) return e;
+    {  // y = iNTT(d) scaled by [Bhat_i^-1]
+        MapBatched m{d, d_stride, w.y, n, (uint32_t)l, lt->d_modup_scale};
+        if ((e = launch_ntt(c, m, B * l, true, s, "ks_intt_modup"))) return e;
     }
     SetLayout lay_up{(size_t)l * n, (size_t)c->alpha * n, 0, beta, 1};
-    hipLaunchKernelGGL(k_basis_u, dim3((n + 255) / 256, B * beta), dim3(256), 0, s, lt->d_digits, lay_up, w.y, w.u,
-                       n, c->d_pc);
+    {
+        ProfScope ps_(c, "ks_modup_u", s);
+        hipLaunchKernelGGL(k_basis_u, dim3((n + 255) / 256, B * beta), dim3(256), 0, s, lt->d_digits, lay_up, w.y,
+                           w.u, n, c->d_pc);
+    }
     LAUNCH_CHECK();
     {
         ConvTargets ct{0, (uint32_t)l, L, K, (size_t)beta * el * n, (size_t)el * n};
         const uint32_t maxt = l + K;  // upper bound on targets per digit
+        ProfScope ps_(c, "ks_modup_convert", s);
         hipLaunchKernelGGL(k_convert, dim3((n + 255) / 256, (maxt + CT - 1) / CT, B * beta), dim3(256),
                            (size_t)c->alpha * CT * 8, s, lt->d_digits, lay_up, w.y, w.u, ct, w.ext, n, c->d_pc);
-        LAUNCH_CHECK();
     }
+    LAUNCH_CHECK();
     {
         MapExt m{w.ext, n, (uint32_t)l, L, K, beta, c->alpha};
-        if ((e = launch_ntt(c, m, B * beta * el, false, s))) return e;
+        if ((e = launch_ntt(c, m, B * beta * el, false, s, "ks_ntt_ext"))) return e;
     }
+    return CKKS_OK;
+}
+
+// Inner product of sigma_g(ModUp(d)) with the key, then ModDown up to the
+// NTT-domain conversion: leaves the Q-limbs of the accumulators in w.acc and
+// the converted P-part in w.conv; the caller runs the final kernel.
+static int ks_inner_moddown(ckks_ctx *c, LevelTables *lt, int B, int l, const uint64_t *d, size_t d_stride,
+                            uint32_t g, const uint64_t *key, const KsWs &w, hipStream_t s) {
+    const uint32_t n = c->n, K = c->K, L = c->L, el = l + K, beta = lt->beta;
+    int e;
     {
         size_t total = (size_t)B * el * n;
-        hipLaunchKernelGGL(k_inner, grid_for(total), dim3(256), 0, s, w.d, w.ext, key, w.acc, c->d_pc, n,
-                           (uint32_t)l, L, K, beta, c->alpha, total);
-        LAUNCH_CHECK();
+        ProfScope ps_(c, "ks_inner_product", s);
+        if (n == 2048)
+            hipLaunchKernelGGL(k_inner2048, dim3(B * el), dim3(256), 0, s, d, d_stride, w.ext, key, w.acc, c->d_pc,
+                               (uint32_t)l, L, K, beta, c->alpha, g);
+        else
+            hipLaunchKernelGGL(k_inner, grid_for(total), dim3(256), 0, s, d, d_stride, w.ext, key, w.acc, c->d_pc, n,
+                               (uint32_t)l, L, K, beta, c->alpha, g, total);
     }
+    LAUNCH_CHECK();
     {
         MapAccP m{w.acc, n, (uint32_t)l, L, K, c->d_moddown_scale};
-        if ((e = launch_ntt(c, m, B * 2 * K, true, s))) return e;
+        if ((e = launch_ntt(c, m, B * 2 * K, true, s, "ks_intt_moddown"))) return e;
     }
     SetLayout lay_dn{(size_t)el * n, 0, (size_t)l * n, 1, 0};
-    hipLaunchKernelGGL(k_basis_u, dim3((n + 255) / 256, B * 2), dim3(256), 0, s, c->d_pbasis, lay_dn, w.acc, w.uP,
-                       n, c->d_pc);
+    {
+        ProfScope ps_(c, "ks_moddown_u", s);
+        hipLaunchKernelGGL(k_basis_u, dim3((n + 255) / 256, B * 2), dim3(256), 0, s, c->d_pbasis, lay_dn, w.acc,
+                           w.uP, n, c->d_pc);
+    }
     LAUNCH_CHECK();
     {
         ConvTargets ct{1, (uint32_t)l, L, K, (size_t)l * n, 0};
+        ProfScope ps_(c, "ks_moddown_convert", s);
         hipLaunchKernelGGL(k_convert, dim3((n + 255) / 256, (l + CT - 1) / CT, B * 2), dim3(256),
                            (size_t)K * CT * 8, s, c->d_pbasis, lay_dn, w.acc, w.uP, ct, w.conv, n, c->d_pc);
-        LAUNCH_CHECK();
     }
-    {
+    LAUNCH_CHECK();
+    if (n != 2048) {  // at n = 2048 the final kernel transforms conv in LDS
         MapStrided m{w.conv, w.conv, n, (uint32_t)l, 0, nullptr};
-        if ((e = launch_ntt(c, m, B * 2 * l, false, s))) return e;
+        if ((e = launch_ntt(c, m, B * 2 * l, false, s, "ks_ntt_moddown"))) return e;
     }
     return CKKS_OK;
 }
@@ -615,16 +812,54 @@ int op_mul_tensor_relin(ckks_ctx *c, const uint64_t *a, const uint64_t *b, const
     ks_words(c, B, l, &w, (uint64_t *)ws);
     const uint32_t n = c->n;
     size_t tot = (size_t)B * l * n;
-    hipLaunchKernelGGL(k_prep_relin, grid_for(tot), dim3(256), 0, s, a, b, w.d, c->d_pc, n, (uint32_t)l, tot);
+    {
+        ProfScope ps_(c, "relin_tensor_d2", s);
+        hipLaunchKernelGGL(k_prep_relin, grid_for(tot), dim3(256), 0, s, a, b, w.d, c->d_pc, n, (uint32_t)l, tot);
+    }
     LAUNCH_CHECK();
-    if ((e = keyswitch_core(c, lt, B, l, rlk, w, s))) return e;
+    const size_t per = (size_t)l * n;
+    if ((e = ks_modup(c, lt, B, l, w.d, per, w, s))) return e;
+    if ((e = ks_inner_moddown(c, lt, B, l, w.d, per, 1, rlk, w, s))) return e;
     tot = (size_t)B * 2 * l * n;
-    hipLaunchKernelGGL((k_moddown_final<1, false>), grid_for(tot), dim3(256), 0, s, w.acc, w.conv, c->d_pinv,
-                       c->d_pc, a, b, 0u, out, n, (uint32_t)l, c->K, tot);
+    {
+        ProfScope ps_(c, "relin_final", s);
+        if (n == 2048)
+            hipLaunchKernelGGL((k_final2048<1, false>), dim3(B * 2 * l), dim3(256), 0, s, w.acc, w.conv, c->d_pinv,
+                               c->d_pc, c->d_tw_fwd, a, b, 0u, out, (uint32_t)l, c->K);
+        else
+            hipLaunchKernelGGL((k_moddown_final<1, false>), grid_for(tot), dim3(256), 0, s, w.acc, w.conv,
+                               c->d_pinv, c->d_pc, a, b, 0u, out, n, (uint32_t)l, c->K, tot);
+    }
     LAUNCH_CHECK();
     return CKKS_OK;
 }
 
+// Final kernel of a rotation: out (+)= (acc - conv) P^-1 + (sigma_g(c0), 0).
+static int rotate_final(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, uint32_t g, const KsWs &w,
+                        bool accumulate, hipStream_t s) {
+    const size_t tot = (size_t)B * 2 * l * c->n;
+    ProfScope ps_(c, accumulate ? "rotate_final_acc" : "rotate_final", s);
+    const uint64_t *nul = nullptr;
+    if (c->n == 2048) {
+        if (accumulate)
+            hipLaunchKernelGGL((k_final2048<2, true>), dim3(B * 2 * l), dim3(256), 0, s, w.acc, w.conv, c->d_pinv,
+                               c->d_pc, c->d_tw_fwd, in, nul, g, out, (uint32_t)l, c->K);
+        else
+            hipLaunchKernelGGL((k_final2048<2, false>), dim3(B * 2 * l), dim3(256), 0, s, w.acc, w.conv, c->d_pinv,
+                               c->d_pc, c->d_tw_fwd, in, nul, g, out, (uint32_t)l, c->K);
+    } else if (accumulate) {
+        hipLaunchKernelGGL((k_moddown_final<2, true>), grid_for(tot), dim3(256), 0, s, w.acc, w.conv, c->d_pinv,
+                           c->d_pc, in, nul, g, out, c->n, (uint32_t)l, c->K, tot);
+    } else {
+        hipLaunchKernelGGL((k_moddown_final<2, false>), grid_for(tot), dim3(256), 0, s, w.acc, w.conv, c->d_pinv,
+                           c->d_pc, in, nul, g, out, c->n, (uint32_t)l, c->K, tot);
+    }
+    LAUNCH_CHECK();
+    return CKKS_OK;
+}
+
+// Rotation: ModUp of c1 as stored (no permuted copy), the automorphism applied
+// as a gather of the extended digits inside the key inner product.
 int op_rotate(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, uint32_t g, const uint64_t *key, void *ws,
               bool accumulate, hipStream_t s) {
     int e = CKKS_OK;
@@ -632,20 +867,11 @@ int op_rotate(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, uint
     if (!lt) return e;
     KsWs w;
     ks_words(c, B, l, &w, (uint64_t *)ws);
-    const uint32_t n = c->n;
-    size_t tot = (size_t)B * l * n;
-    hipLaunchKernelGGL(k_prep_rotate, grid_for(tot), dim3(256), 0, s, in, w.d, g, n, (uint32_t)l, tot);
-    LAUNCH_CHECK();
-    if ((e = keyswitch_core(c, lt, B, l, key, w, s))) return e;
-    tot = (size_t)B * 2 * l * n;
-    if (accumulate)
-        hipLaunchKernelGGL((k_moddown_final<2, true>), grid_for(tot), dim3(256), 0, s, w.acc, w.conv, c->d_pinv,
-                           c->d_pc, in, (const uint64_t *)nullptr, g, out, n, (uint32_t)l, c->K, tot);
-    else
-        hipLaunchKernelGGL((k_moddown_final<2, false>), grid_for(tot), dim3(256), 0, s, w.acc, w.conv, c->d_pinv,
-                           c->d_pc, in, (const uint64_t *)nullptr, g, out, n, (uint32_t)l, c->K, tot);
-    LAUNCH_CHECK();
-    return CKKS_OK;
+    const size_t per = (size_t)l * c->n;
+    const uint64_t *c1 = in + per;
+    if ((e = ks_modup(c, lt, B, l, c1, 2 * per, w, s))) return e;
+    if ((e = ks_inner_moddown(c, lt, B, l, c1, 2 * per, g, key, w, s))) return e;
+    return rotate_final(c, in, out, B, l, g, w, accumulate, s);
 }
 
 int op_rescale(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, void *ws, hipStream_t s) {
@@ -658,17 +884,30 @@ int op_rescale(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, voi
     // t[b][c] = iNTT(in[b][c][l-1])
     {
         MapLast ml{in, t, n, (uint32_t)l};
-        if ((e = launch_ntt(c, ml, B * 2, true, s))) return e;
+        if ((e = launch_ntt(c, ml, B * 2, true, s, "rescale_intt"))) return e;
     }
     size_t tot = (size_t)B * 2 * (l - 1) * n;
-    hipLaunchKernelGGL(k_rescale_lift, grid_for(tot), dim3(256), 0, s, t, r, c->d_pc, n, (uint32_t)l, tot);
+    if (n == 2048) {
+        ProfScope ps_(c, "rescale_final", s);
+        hipLaunchKernelGGL(k_rescale2048, dim3(B * 2 * (l - 1)), dim3(256), 0, s, in, t, lt->d_rescale_inv, c->d_pc,
+                           c->d_tw_fwd, out, (uint32_t)l);
+        LAUNCH_CHECK();
+        return CKKS_OK;
+    }
+    {
+        ProfScope ps_(c, "rescale_lift", s);
+        hipLaunchKernelGGL(k_rescale_lift, grid_for(tot), dim3(256), 0, s, t, r, c->d_pc, n, (uint32_t)l, tot);
+    }
     LAUNCH_CHECK();
     {
         MapStrided m{r, r, n, (uint32_t)(l - 1), 0, nullptr};
-        if ((e = launch_ntt(c, m, B * 2 * (l - 1), false, s))) return e;
+        if ((e = launch_ntt(c, m, B * 2 * (l - 1), false, s, "rescale_ntt"))) return e;
     }
-    hipLaunchKernelGGL(k_rescale_final, grid_for(tot), dim3(256), 0, s, in, r, lt->d_rescale_inv, c->d_pc, out, n,
-                       (uint32_t)l, tot);
+    {
+        ProfScope ps_(c, "rescale_final", s);
+        hipLaunchKernelGGL(k_rescale_final, grid_for(tot), dim3(256), 0, s, in, r, lt->d_rescale_inv, c->d_pc, out, n,
+                           (uint32_t)l, tot);
+    }
     LAUNCH_CHECK();
     return CKKS_OK;
 }
@@ -688,14 +927,28 @@ int op_bsgs(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, const 
     uint64_t *inner = rot + align_words(ct * (bs - 1));
     uint64_t *ksws = inner + align_words(ct * gs);
     uint64_t *rsws = ksws + ks_words(c, B, l, nullptr, nullptr);
-    int e;
-    for (int b = 1; b < bs; b++)
-        if ((e = op_rotate(c, in, rot + (size_t)(b - 1) * ct, B, l, rot_elt(c->n, b), baby[b], ksws, false, s)))
-            return e;
+    int e = CKKS_OK;
+    if (bs > 1) {
+        // baby steps hoisted: one ModUp of c1, then per step a gathered inner product + ModDown
+        LevelTables *lt = level_tables(c, l, &e);
+        if (!lt) return e;
+        KsWs w;
+        ks_words(c, B, l, &w, ksws);
+        const size_t per = (size_t)l * c->n;
+        if ((e = ks_modup(c, lt, B, l, in + per, 2 * per, w, s))) return e;
+        for (int b = 1; b < bs; b++) {
+            const uint32_t g = rot_elt(c->n, b);
+            if ((e = ks_inner_moddown(c, lt, B, l, in + per, 2 * per, g, baby[b], w, s))) return e;
+            if ((e = rotate_final(c, in, rot + (size_t)(b - 1) * ct, B, l, g, w, false, s))) return e;
+        }
+    }
     for (int b0 = 0; b0 < bs; b0 += MAC_B) {
-        hipLaunchKernelGGL(k_bsgs_mac, dim3(c->n / MAC_K, l, (2 * B + MAC_C - 1) / MAC_C), dim3(256), 0, s, diags,
-                           in, rot, inner, c->d_pc, c->n, (uint32_t)l, (uint32_t)bs, (uint32_t)gs, (uint32_t)(2 * B),
-                           ct, (uint32_t)b0);
+        {
+            ProfScope ps_(c, "bsgs_mac", s);
+            hipLaunchKernelGGL(k_bsgs_mac, dim3(c->n / MAC_K, l, (2 * B + MAC_C - 1) / MAC_C), dim3(256), 0, s, diags,
+                               in, rot, inner, c->d_pc, c->n, (uint32_t)l, (uint32_t)bs, (uint32_t)gs, (uint32_t)(2 * B),
+                               ct, (uint32_t)b0);
+        }
         LAUNCH_CHECK();
     }
     // giant steps accumulate into inner[0]
@@ -704,7 +957,10 @@ int op_bsgs(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, const 
                            true, s)))
             return e;
     if (rescale) return op_rescale(c, inner, out, B, l, rsws, s);
-    hipLaunchKernelGGL(k_copy, grid_for(ct), dim3(256), 0, s, inner, out, ct);
+    {
+        ProfScope ps_(c, "copy", s);
+        hipLaunchKernelGGL(k_copy, grid_for(ct), dim3(256), 0, s, inner, out, ct);
+    }
     LAUNCH_CHECK();
     return CKKS_OK;
 }
