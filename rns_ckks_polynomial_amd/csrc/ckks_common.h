@@ -69,29 +69,47 @@ __device__ __forceinline__ void mac(Acc128 &acc, uint64_t a, uint64_t b) {
 }
 
 // Split-operand multiply-accumulate for sums of many 60-bit products.
-// With x = xa 2^30 + xb (xb < 2^30), three 64-bit partial sums
-//   a0 += xb yb,  a1 += xb ya + xa yb,  a2 += xa ya
-// are each one v_mad_u64_u32 per product and need no carry handling: for
-// operands below 2^59 + 2^52 (every chain prime is), 15 products fit in 64
-// bits.  sflush folds a0 + a1 2^30 + a2 2^60 into a 128-bit accumulator.
+// With x = xa 2^30 + xb (xb < 2^30), four 64-bit partial sums
+//   a0 += xb yb,  a1 += xb ya,  a1b += xa yb,  a2 += xa ya
+// are each one v_mad_u64_u32 per product (independent chains, no carry
+// handling): for operands below 2^59 + 2^52 (every chain prime is), 15
+// products fit in 64 bits.  sflush folds a0 + (a1 + a1b) 2^30 + a2 2^60 into a
+// 128-bit accumulator.
 constexpr uint64_t M30 = (1ull << 30) - 1;
 constexpr int SPLIT_CHUNK = 15;
 struct Split3 {
-    uint64_t a0, a1, a2;
+    uint64_t a0, a1, a1b, a2;
 };
 __device__ __forceinline__ uint64_t split30(uint64_t v) { return (v & M30) | ((v >> 30) << 32); }
 __device__ __forceinline__ void smac(Split3 &s, uint32_t xb, uint32_t xa, uint64_t ysplit) {
     const uint32_t yb = (uint32_t)ysplit, ya = (uint32_t)(ysplit >> 32);
     s.a0 += (uint64_t)xb * yb;
     s.a1 += (uint64_t)xb * ya;
-    s.a1 += (uint64_t)xa * yb;
+    s.a1b += (uint64_t)xa * yb;
     s.a2 += (uint64_t)xa * ya;
 }
-__device__ __forceinline__ void sflush(Acc128 &acc, Split3 &s) {
+// Three-sum variant (a1 takes both middle products): two fewer VGPRs per sum,
+// for kernels whose occupancy is register-bound.
+struct Split3c {
+    uint64_t a0, a1, a2;
+};
+__device__ __forceinline__ void smac(Split3c &s, uint32_t xb, uint32_t xa, uint64_t ysplit) {
+    const uint32_t yb = (uint32_t)ysplit, ya = (uint32_t)(ysplit >> 32);
+    s.a0 += (uint64_t)xb * yb;
+    s.a1 += (uint64_t)xb * ya + (uint64_t)xa * yb;
+    s.a2 += (uint64_t)xa * ya;
+}
+__device__ __forceinline__ void sflush(Acc128 &acc, Split3c &s) {
     u128 v = ((u128)acc.hi << 64 | acc.lo) + s.a0 + ((u128)s.a1 << 30) + ((u128)s.a2 << 60);
     acc.lo = (uint64_t)v;
     acc.hi = (uint64_t)(v >> 64);
     s.a0 = s.a1 = s.a2 = 0;
+}
+__device__ __forceinline__ void sflush(Acc128 &acc, Split3 &s) {
+    u128 v = ((u128)acc.hi << 64 | acc.lo) + s.a0 + ((u128)s.a1 << 30) + ((u128)s.a1b << 30) + ((u128)s.a2 << 60);
+    acc.lo = (uint64_t)v;
+    acc.hi = (uint64_t)(v >> 64);
+    s.a0 = s.a1 = s.a1b = s.a2 = 0;
 }
 
 // ------------------------------------------------------------------ tables

@@ -336,7 +336,7 @@ __global__ __launch_bounds__(256) void k_convert(const BasisDev *__restrict__ ba
     Acc128 acc[CT];
 #pragma unroll
     for (int a = 0; a < CT; a++) {
-        sp[a] = {0, 0, 0};
+        sp[a] = {0, 0, 0, 0};
         acc[a] = {0, 0};
     }
     uint64_t ynext = yb[0];
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(256) void k_inner2048(const uint64_t *__restrict__ 
     const uint32_t t = threadIdx.x;
     Split3 s0[8], s1[8];
 #pragma unroll
-    for (int m = 0; m < 8; m++) s0[m] = s1[m] = {0, 0, 0};
+    for (int m = 0; m < 8; m++) s0[m] = s1[m] = {0, 0, 0, 0};
     for (uint32_t j = 0; j < beta; j++) {
         const bool own = e >= j * alpha && e < min(l, (j + 1) * alpha);
         const uint64_t *src = own ? d + b * d_stride + (size_t)e * n : ext + ((b * beta + j) * el + e) * n;
@@ -432,7 +432,7 @@ __global__ void k_inner(const uint64_t *__restrict__ d, size_t d_stride, const u
         const size_t b = idx / ((size_t)n * el);
         const uint32_t gi = e < l ? e : L + (e - l);
         const uint32_t ks = galois_src(k, g, n);
-        Split3 s0{0, 0, 0}, s1{0, 0, 0};
+        Split3 s0{0, 0, 0, 0}, s1{0, 0, 0, 0};
         for (uint32_t j = 0; j < beta; j++) {
             const bool own = e >= j * alpha && e < min(l, (j + 1) * alpha);
             const uint64_t v = own ? d[b * d_stride + (size_t)e * n + ks] : ext[((b * beta + j) * el + e) * n + ks];
@@ -661,7 +661,7 @@ __global__ __launch_bounds__(256) void k_bsgs_mac(const uint64_t *__restrict__ p
             st0 = *pt_addr(g + 1, threadIdx.x);
             st1 = *pt_addr(g + 1, threadIdx.x + 256);
         }
-        Split3 sp{0, 0, 0};
+        Split3c sp{0, 0, 0};
         Acc128 acc{0, 0};
 #pragma unroll
         for (int bb = 0; bb < MAC_B; bb++) {
