@@ -35,6 +35,27 @@ HBM_PEAK_GBS = 8000.0
 VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 LIMB = N * 8
 
+# HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE on this
+# workload (fetch scaled x2.0 and write x1.0 by a 1 GiB copy calibration; see
+# profiles/bench_step_n2048_l112_b8_hbm_counters.md).  Valid only for the
+# kernel sources they were taken on (hash of rns_ckks_polynomial_amd/csrc).
+MEASURED_TRAFFIC = {
+    "source_sha": "9a779d0215045d90",
+    "bytes_per_launch": {"ks_inner_product": 195.8e6, "ks_ntt_ext": 127.8e6, "bsgs_mac": 3758.2e6,
+                         "rotate_final": 106.7e6, "rotate_final_acc": 136.1e6, "ntt_fwd": 62.6e6},
+}
+
+
+def csrc_sha() -> str:
+    import hashlib
+    d = os.path.join(ROOT, "rns_ckks_polynomial_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -210,12 +231,17 @@ def main():
                     "unit": "GB/s", "traffic": None, "work_per_launch": f"{dw.get('bytes')} bytes"}
     roofline["frac"] = roofline["achieved"] / roofline["peak"] if roofline["achieved"] else None
     roofline["avg_launch_us"] = drow["avg_us"]
+    traffic_valid = csrc_sha() == MEASURED_TRAFFIC["source_sha"]
+    if traffic_valid and dom in MEASURED_TRAFFIC["bytes_per_launch"]:
+        roofline["traffic"] = MEASURED_TRAFFIC["bytes_per_launch"][dom]
+        roofline["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     ntt_row = kernels.get("ntt_fwd", {})
     ntt_roof = {"bound": "hbm", "kernel": "ntt_fwd [16][112] limbs", "achieved": ntt_row.get("algo_GBps"),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "avg_launch_us": ntt_row.get("avg_us"),
                 "work_per_launch": f"{work['ntt_fwd']['bytes']} bytes (each limb read and written once)"}
     if ntt_roof["achieved"]:
         ntt_roof["frac"] = ntt_roof["achieved"] / HBM_PEAK_GBS
+    ntt_roof["traffic"] = MEASURED_TRAFFIC["bytes_per_launch"]["ntt_fwd"] if traffic_valid else None
 
     out = {
         "metric": "limb-NTTs/s + key-switches/s @n=2048,112 primes; % HBM roofline",

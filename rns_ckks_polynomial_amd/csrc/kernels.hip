@@ -276,11 +276,24 @@ __global__ void k_basis_u(const BasisDev *__restrict__ bases, SetLayout lay, uin
     const uint64_t M63 = (1ull << 63) - 1;
     uint64_t frac = 0;
     uint32_t ip = 0;
-    for (uint32_t i = 0; i < m; i++) {
-        const uint64_t f = mulhi64(yb[(size_t)i * n] << 4, B.R[i]);
-        frac += f;
-        ip += (uint32_t)(frac >> 63);
-        frac &= M63;
+    // the sum is exact integer arithmetic, so inputs are taken 8 at a time
+    // with all 8 loads in flight before the first is used
+    for (uint32_t i0 = 0; i0 < m; i0 += 8) {
+        uint64_t yv[8], rv[8];
+#pragma unroll
+        for (int a = 0; a < 8; a++) {
+            const uint32_t i = min(i0 + a, m - 1);
+            yv[a] = yb[(size_t)i * n];
+            rv[a] = B.R[i];
+        }
+#pragma unroll
+        for (int a = 0; a < 8; a++) {
+            if (i0 + a < m) {
+                frac += mulhi64(yv[a] << 4, rv[a]);
+                ip += (uint32_t)(frac >> 63);
+                frac &= M63;
+            }
+        }
     }
     uint64_t t = frac + (1ull << 62);
     uint32_t uu = ip + (uint32_t)(t >> 63);
