@@ -41,8 +41,7 @@ LIMB = N * 8
 # kernel sources they were taken on (hash of rns_ckks_polynomial_amd/csrc).
 MEASURED_TRAFFIC = {
     "source_sha": "9a779d0215045d90",
-    "bytes_per_launch": {"ks_inner_product": 195.8e6, "ks_ntt_ext": 127.8e6, "bsgs_mac": 3758.2e6,
-                         "rotate_final": 106.7e6, "rotate_final_acc": 136.1e6, "ntt_fwd": 62.6e6},
+    "bytes_per_step": {},
 }
 
 
@@ -98,24 +97,33 @@ def cpu_baseline(budget_s: float):
 
 
 def kernel_work():
-    """Algorithmic work per launch of each kernel at this workload.
-    bytes: residues the step must read + write once (twiddles/tables excluded);
-    mads: 32x32-bit multiply-adds, 4 per 60x60-bit product (the minimum on a 32-bit multiplier)."""
-    B, l = BATCH, L
-    modup_macs = B * BETA * ALPHA * (l - ALPHA + K) * N
-    moddown_macs = B * 2 * K * l * N
-    mac_macs = GS * BS * 2 * B * l * N
+    """Algorithmic work of each kernel per benchmark step (all launches of that
+    kernel in one step; launches differ in size since BSGS batches its steps).
+    bytes: residues that must be read + written once (twiddles/tables excluded);
+    mads: 32x32-bit multiply-adds, 4 per 60x60-bit product (the minimum on a
+    32-bit multiplier)."""
+    B, l, el, a, beta = BATCH, L, L + K, ALPHA, BETA
+    sb, sg = BS - 1, GS - 1           # baby / giant key switches per ciphertext
+    n_up = (1 + 1 + sg) * B           # ciphertexts through ModUp: relin, hoisted baby, giant
+    n_dn = (1 + sb + sg) * B          # ciphertexts through ModDown
+    limb = LIMB
     return {
-        "ks_modup_convert": {"mads": 4 * modup_macs, "bytes": (B * l + B * BETA * (l + K - ALPHA)) * LIMB},
-        "ks_moddown_convert": {"mads": 4 * moddown_macs, "bytes": (B * 2 * K + B * 2 * l) * LIMB},
-        "bsgs_mac": {"mads": 4 * mac_macs, "bytes": (GS * BS * l + BS * 2 * B * l + GS * 2 * B * l) * LIMB},
-        "ks_ntt_ext": {"bytes": 2 * B * BETA * (l + K - ALPHA) * LIMB, "limbs": B * BETA * (l + K - ALPHA)},
-        "ks_intt_modup": {"bytes": 2 * B * l * LIMB, "limbs": B * l},
-        "ks_intt_moddown": {"bytes": 2 * B * 2 * K * LIMB, "limbs": B * 2 * K},
-        "ks_ntt_moddown": {"bytes": 2 * B * 2 * l * LIMB, "limbs": B * 2 * l},
-        "ks_inner_product": {"bytes": (B * BETA * (l + K) + 2 * BETA * (l + K) + 2 * B * (l + K)) * LIMB},
-        "ntt_fwd": {"bytes": 2 * B * 2 * l * LIMB, "limbs": B * 2 * l},
-        "ntt_inv": {"bytes": 2 * B * 2 * l * LIMB, "limbs": B * 2 * l},
+        "ks_intt_modup": {"bytes": 2 * n_up * l * limb},
+        "ks_modup_u": {"bytes": n_up * l * limb},
+        "ks_modup_convert": {"mads": 4 * n_up * beta * a * (l + K - a) * N,
+                             "bytes": (n_up * l + n_up * beta * (el - a)) * limb},
+        "ks_ntt_ext": {"bytes": 2 * n_up * beta * (el - a) * limb},
+        "ks_inner_product": {"bytes": ((1 + sg) * B * (beta + 2) * el + (1 + sg) * 2 * beta * el) * limb},
+        "ks_inner_product_hoisted": {"bytes": (sb * B * (beta + 2) * el + sb * 2 * beta * el) * limb},
+        "ks_intt_moddown": {"bytes": 2 * n_dn * 2 * K * limb},
+        "ks_moddown_u": {"bytes": n_dn * 2 * K * limb},
+        "ks_moddown_convert": {"mads": 4 * n_dn * 2 * K * l * N, "bytes": (n_dn * 2 * K + n_dn * 2 * l) * limb},
+        "rotate_final": {"bytes": sb * B * 7 * l * limb},
+        "giant_final_sum": {"bytes": (sg * B * 5 * l + B * 4 * l) * limb},
+        "bsgs_mac": {"mads": 4 * GS * BS * 2 * B * l * N,
+                     "bytes": (GS * BS * l + BS * 2 * B * l + GS * 2 * B * l) * limb},
+        "ntt_fwd": {"bytes": 2 * B * 2 * l * limb, "standalone": True},
+        "ntt_inv": {"bytes": 2 * B * 2 * l * limb, "standalone": True},
     }
 
 
@@ -209,12 +217,13 @@ def main():
     kernels = {}
     for name, (cnt, tot, mn, mx) in prof.items():
         avg = tot / cnt
-        row = {"launches": cnt, "avg_us": avg * 1e3, "total_ms_per_step": tot / args.profile_steps}
         w = work.get(name, {})
+        per_step = tot / (1 if w.get("standalone") else args.profile_steps)  # ms of this kernel per step
+        row = {"launches": cnt, "avg_us": avg * 1e3, "total_ms_per_step": per_step}
         if "bytes" in w:
-            row["algo_GBps"] = w["bytes"] / (avg * 1e-3) / 1e9
+            row["algo_GBps"] = w["bytes"] / (per_step * 1e-3) / 1e9
         if "mads" in w:
-            row["algo_Tmads"] = w["mads"] / (avg * 1e-3) / 1e12
+            row["algo_Tmads"] = w["mads"] / (per_step * 1e-3) / 1e12
         kernels[name] = row
     for name in ("ntt_fwd", "ntt_inv"):
         if name in kernels:
@@ -225,23 +234,26 @@ def main():
     if "mads" in dw:
         roofline = {"bound": "alu", "kernel": dom, "achieved": drow["algo_Tmads"], "peak": VALU_PEAK_TOPS,
                     "unit": "T int32-MAD/s", "traffic": None,
-                    "work_per_launch": f"{dw['mads']} 32x32-bit multiply-adds (4 per 60x60-bit product)"}
+                    "work_per_step": f"{dw['mads']} 32x32-bit multiply-adds (4 per 60x60-bit product) "
+                                     f"in {drow['launches'] // args.profile_steps} launch(es)"}
     else:
         roofline = {"bound": "hbm", "kernel": dom, "achieved": drow.get("algo_GBps"), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "traffic": None, "work_per_launch": f"{dw.get('bytes')} bytes"}
+                    "unit": "GB/s", "traffic": None,
+                    "work_per_step": f"{dw.get('bytes')} bytes in {drow['launches'] // args.profile_steps} launch(es)"}
     roofline["frac"] = roofline["achieved"] / roofline["peak"] if roofline["achieved"] else None
     roofline["avg_launch_us"] = drow["avg_us"]
+    roofline["kernel_ms_per_step"] = drow["total_ms_per_step"]
     traffic_valid = csrc_sha() == MEASURED_TRAFFIC["source_sha"]
-    if traffic_valid and dom in MEASURED_TRAFFIC["bytes_per_launch"]:
-        roofline["traffic"] = MEASURED_TRAFFIC["bytes_per_launch"][dom]
-        roofline["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+    if traffic_valid and dom in MEASURED_TRAFFIC["bytes_per_step"]:
+        roofline["traffic"] = MEASURED_TRAFFIC["bytes_per_step"][dom]
+        roofline["traffic_unit"] = "bytes per step (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     ntt_row = kernels.get("ntt_fwd", {})
     ntt_roof = {"bound": "hbm", "kernel": "ntt_fwd [16][112] limbs", "achieved": ntt_row.get("algo_GBps"),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "avg_launch_us": ntt_row.get("avg_us"),
                 "work_per_launch": f"{work['ntt_fwd']['bytes']} bytes (each limb read and written once)"}
     if ntt_roof["achieved"]:
         ntt_roof["frac"] = ntt_roof["achieved"] / HBM_PEAK_GBS
-    ntt_roof["traffic"] = MEASURED_TRAFFIC["bytes_per_launch"]["ntt_fwd"] if traffic_valid else None
+    ntt_roof["traffic"] = MEASURED_TRAFFIC["bytes_per_step"].get("ntt_fwd") if traffic_valid else None
 
     out = {
         "metric": "limb-NTTs/s + key-switches/s @n=2048,112 primes; % HBM roofline",

@@ -379,24 +379,42 @@ __global__ __launch_bounds__(256) void k_convert(const BasisDev *__restrict__ ba
     }
 }
 
-// acc[b][c][e][k] = sum_j v_j[e][galois_src(k)] key[j][c][gidx(e)][k], where
-// v_j[e] = d[b][e] (NTT domain, own digit) or ext[b][j][e] (ModUp of digit j).
+// A batched key switch runs S "steps" of B ciphertexts each: output
+// ciphertext cb = s * B + b uses key[s] and Galois element g[s].  With
+// shared = 1 every step switches the same B inputs (hoisted baby steps);
+// otherwise step s has its own inputs (ciphertext cb).
+constexpr int MAX_STEPS = 32;
+struct Steps {
+    const uint64_t *key[MAX_STEPS];
+    uint32_t g[MAX_STEPS];
+    uint32_t count, B, shared;
+};
+
+// acc[cb][c][e][k] = sum_j v_j[e][galois_src(k)] key[j][c][gidx(e)][k], where
+// v_j[e] = d[ct][e] (NTT domain, own digit) or ext[ct][j][e] (ModUp of digit j).
 // With g = 1 the gather is the identity.  With g != 1 this is the key switch
 // of sigma_g(d): exact centered ModUp commutes with the automorphism, so
 // permuting the extended digits equals extending the permuted polynomial.
-// One workgroup per (ciphertext, extended limb): each digit's limb is loaded
-// into LDS with coalesced reads and permuted from there; the key rows are
-// read in order.  (n = 2048: 8 coefficients per thread.)
+// One workgroup per (output ciphertext, extended limb): each digit's limb is
+// loaded into LDS with coalesced reads and permuted from there; the key rows
+// are read in order.  (n = 2048: 8 coefficients per thread.)
 __global__ __launch_bounds__(256) void k_inner2048(const uint64_t *__restrict__ d, size_t d_stride,
-                                                    const uint64_t *__restrict__ ext,
-                                                    const uint64_t *__restrict__ key, uint64_t *__restrict__ acc,
-                                                    const PrimeConsts *__restrict__ pc, uint32_t l, uint32_t L,
-                                                    uint32_t K, uint32_t beta, uint32_t alpha, uint32_t g) {
+                                                    const uint64_t *__restrict__ ext, const Steps st,
+                                                    uint64_t *__restrict__ acc, const PrimeConsts *__restrict__ pc,
+                                                    uint32_t l, uint32_t L, uint32_t K, uint32_t beta,
+                                                    uint32_t alpha) {
     constexpr uint32_t n = 2048;
     __shared__ uint64_t buf[2][n];
     const uint32_t el = l + K;
-    const uint32_t e = blockIdx.x % el;
-    const size_t b = blockIdx.x / el;
+    // block order: ciphertext fastest, then limb, then step, so the B blocks
+    // reading one key row run together and one step's key is in flight at a time
+    const uint32_t bl = blockIdx.x % st.B;
+    const uint32_t e = (blockIdx.x / st.B) % el;
+    const uint32_t step = blockIdx.x / (st.B * el);
+    const size_t cb = (size_t)step * st.B + bl;
+    const size_t b = st.shared ? bl : cb;  // input ciphertext
+    const uint64_t *key = st.key[step];
+    const uint32_t g = st.g[step];
     const uint32_t gi = e < l ? e : L + (e - l);
     const uint32_t t = threadIdx.x;
     Split3 s0[8], s1[8];
@@ -421,7 +439,7 @@ __global__ __launch_bounds__(256) void k_inner2048(const uint64_t *__restrict__ 
         }
     }
     const PrimeConsts P = pc[gi];
-    uint64_t *o0 = acc + ((b * 2 + 0) * el + e) * n, *o1 = acc + ((b * 2 + 1) * el + e) * n;
+    uint64_t *o0 = acc + ((cb * 2 + 0) * el + e) * n, *o1 = acc + ((cb * 2 + 1) * el + e) * n;
 #pragma unroll
     for (int m = 0; m < 8; m++) {
         Acc128 a0{0, 0}, a1{0, 0};
@@ -497,22 +515,25 @@ __global__ void k_moddown_final(const uint64_t *__restrict__ acc, const uint64_t
     }
 }
 
-// n = 2048 fused ModDown tail: one workgroup per (ciphertext, polynomial,
-// limb i): NTT of the converted P-part in LDS, then
+// n = 2048 fused ModDown tail: one workgroup per (output ciphertext cb,
+// polynomial, limb i): NTT of the converted P-part in LDS, then
 //   out = (acc - NTT(conv)) P^-1 + extra   (MODE / ACCUM as k_moddown_final);
-// for rotations c0 is staged in LDS and permuted from there.
+// for rotations c0 (of the step's input ciphertext) is staged in LDS and
+// permuted with the step's Galois element.
 template <int MODE, bool ACCUM>
 __global__ __launch_bounds__(256) void k_final2048(const uint64_t *__restrict__ acc, const uint64_t *__restrict__ conv,
                                                     const uint64_t *__restrict__ pinv,
                                                     const PrimeConsts *__restrict__ pc,
                                                     const uint64_t *__restrict__ twf, const uint64_t *__restrict__ xa,
-                                                    const uint64_t *__restrict__ xb, uint32_t g,
+                                                    const uint64_t *__restrict__ xb, const Steps st,
                                                     uint64_t *__restrict__ out, uint32_t l, uint32_t K) {
     constexpr uint32_t n = 2048;
     __shared__ uint64_t lds[n2048::LDS_WORDS];
     const uint32_t i = blockIdx.x % l;
     const uint32_t c = (blockIdx.x / l) % 2;
-    const size_t b = blockIdx.x / (2 * l);
+    const size_t cb = blockIdx.x / (2 * l);
+    const size_t b = st.shared ? cb % st.B : cb;  // input ciphertext of the extra term
+    const uint32_t g = st.g[cb / st.B];
     const uint32_t t = threadIdx.x;
     const PrimeConsts P = pc[i];
     const uint64_t q = P.q;
@@ -528,7 +549,7 @@ __global__ __launch_bounds__(256) void k_final2048(const uint64_t *__restrict__ 
         for (int m = 0; m < 8; m++) lds[t + 256 * m] = c0[t + 256 * m];
         __syncthreads();
     }
-    const uint64_t *ar = acc + ((b * 2 + c) * (l + K) + i) * n;
+    const uint64_t *ar = acc + ((cb * 2 + c) * (l + K) + i) * n;
     uint64_t *o = out + (size_t)blockIdx.x * n;
     const uint64_t w = pinv[2 * i], wp = pinv[2 * i + 1];
 #pragma unroll
@@ -550,6 +571,61 @@ __global__ __launch_bounds__(256) void k_final2048(const uint64_t *__restrict__ 
         if (ACCUM) r = addm(r, o[k], q);
         o[k] = r;
     }
+}
+
+// n = 2048 giant-step tail: out[b][c][i] += sum over the S steps of the batch
+// of ((acc_s - NTT(conv_s)) P^-1 + (c == 0 ? sigma_{g_s}(c0 of input s) : 0)),
+// i.e. the rotated giant-step terms are summed without being stored.
+__global__ __launch_bounds__(256) void k_final_sum2048(const uint64_t *__restrict__ acc,
+                                                        const uint64_t *__restrict__ conv,
+                                                        const uint64_t *__restrict__ pinv,
+                                                        const PrimeConsts *__restrict__ pc,
+                                                        const uint64_t *__restrict__ twf,
+                                                        const uint64_t *__restrict__ xa, const Steps st,
+                                                        uint64_t *__restrict__ out, uint32_t l, uint32_t K) {
+    constexpr uint32_t n = 2048;
+    __shared__ uint64_t lds[n2048::LDS_WORDS];
+    const uint32_t i = blockIdx.x % l;
+    const uint32_t c = (blockIdx.x / l) % 2;
+    const size_t b = blockIdx.x / (2 * l);
+    const uint32_t t = threadIdx.x;
+    const PrimeConsts P = pc[i];
+    const uint64_t q = P.q;
+    const size_t per = (size_t)l * n;
+    const uint64_t w = pinv[2 * i], wp = pinv[2 * i + 1];
+    uint64_t sum[8];
+    uint64_t *o = out + ((b * 2 + c) * l + i) * n;
+#pragma unroll
+    for (int m = 0; m < 8; m++) sum[m] = o[t + 256 * m];
+    for (uint32_t step = 0; step < st.count; step++) {
+        const size_t cb = (size_t)step * st.B + b;
+        const uint32_t g = st.g[step];
+        uint64_t v[8];
+        const uint64_t *cv = conv + ((cb * 2 + c) * l + i) * n;
+#pragma unroll
+        for (int m = 0; m < 8; m++) v[m] = cv[t + 256 * m];
+        n2048::fwd(v, lds, twf + (size_t)i * n * 2, q);
+        if (c == 0) {
+            const uint64_t *c0 = xa + (cb * 2) * per + (size_t)i * n;
+#pragma unroll
+            for (int m = 0; m < 8; m++) lds[t + 256 * m] = c0[t + 256 * m];
+            __syncthreads();
+        }
+        const uint64_t *ar = acc + ((cb * 2 + c) * (l + K) + i) * n;
+#pragma unroll
+        for (int m = 0; m < 8; m++) {
+            const uint32_t k = t + 256 * m;
+            uint64_t x = v[m];
+            x = x >= 2 * q ? x - 2 * q : x;
+            x = csub(x, q);
+            uint64_t r = shoup(subm(ar[k], x, q), w, wp, q);
+            if (c == 0) r = addm(r, lds[galois_src(k, g, n)], q);
+            sum[m] = addm(sum[m], r, q);
+        }
+        __syncthreads();  // lds is reused by the next step's NTT
+    }
+#pragma unroll
+    for (int m = 0; m < 8; m++) o[t + 256 * m] = sum[m];
 }
 
 // n = 2048 fused rescale tail: per (ciphertext, polynomial, limb i < l-1):
@@ -764,42 +840,65 @@ static int ks_modup(ckks_ctx *c, LevelTables *lt, int B, int l, const uint64_t *
 // Inner product of sigma_g(ModUp(d)) with the key, then ModDown up to the
 // NTT-domain conversion: leaves the Q-limbs of the accumulators in w.acc and
 // the converted P-part in w.conv; the caller runs the final kernel.
-static int ks_inner_moddown(ckks_ctx *c, LevelTables *lt, int B, int l, const uint64_t *d, size_t d_stride,
-                            uint32_t g, const uint64_t *key, const KsWs &w, hipStream_t s) {
+static Steps one_step(const uint64_t *key, uint32_t g, int B) {
+    Steps st{};
+    st.key[0] = key;
+    st.g[0] = g;
+    st.count = 1;
+    st.B = (uint32_t)B;
+    st.shared = 0;
+    return st;
+}
+
+// Inner product of sigma_g(ModUp(d)) with the keys of a batch of steps:
+// leaves st.count * st.B accumulator pairs in w.acc.
+static int ks_inner(ckks_ctx *c, LevelTables *lt, int l, const uint64_t *d, size_t d_stride, const Steps &st,
+                    const KsWs &w, hipStream_t s) {
     const uint32_t n = c->n, K = c->K, L = c->L, el = l + K, beta = lt->beta;
-    int e;
-    {
-        size_t total = (size_t)B * el * n;
-        ProfScope ps_(c, "ks_inner_product", s);
-        if (n == 2048)
-            hipLaunchKernelGGL(k_inner2048, dim3(B * el), dim3(256), 0, s, d, d_stride, w.ext, key, w.acc, c->d_pc,
-                               (uint32_t)l, L, K, beta, c->alpha, g);
-        else
-            hipLaunchKernelGGL(k_inner, grid_for(total), dim3(256), 0, s, d, d_stride, w.ext, key, w.acc, c->d_pc, n,
-                               (uint32_t)l, L, K, beta, c->alpha, g, total);
+    const size_t nout = (size_t)st.count * st.B;
+    ProfScope ps_(c, st.shared ? "ks_inner_product_hoisted" : "ks_inner_product", s);
+    if (n == 2048) {
+        hipLaunchKernelGGL(k_inner2048, dim3(nout * el), dim3(256), 0, s, d, d_stride, w.ext, st, w.acc, c->d_pc,
+                           (uint32_t)l, L, K, beta, c->alpha);
+    } else {  // generic n: one launch per step
+        for (uint32_t j = 0; j < st.count; j++) {
+            const size_t total = (size_t)st.B * el * n;
+            const size_t in_off = st.shared ? 0 : (size_t)j * st.B;
+            hipLaunchKernelGGL(k_inner, grid_for(total), dim3(256), 0, s, d + in_off * d_stride, d_stride,
+                               w.ext + in_off * beta * el * n, st.key[j], w.acc + (size_t)j * st.B * 2 * el * n,
+                               c->d_pc, n, (uint32_t)l, L, K, beta, c->alpha, st.g[j], total);
+        }
     }
     LAUNCH_CHECK();
+    return CKKS_OK;
+}
+
+// ModDown of nout accumulator pairs up to the converted P-part in w.conv
+// (NTT domain for n != 2048; at n = 2048 the final kernels transform it).
+static int ks_moddown_conv(ckks_ctx *c, size_t nout, int l, const KsWs &w, hipStream_t s) {
+    const uint32_t n = c->n, K = c->K, L = c->L, el = l + K;
+    int e;
     {
         MapAccP m{w.acc, n, (uint32_t)l, L, K, c->d_moddown_scale};
-        if ((e = launch_ntt(c, m, B * 2 * K, true, s, "ks_intt_moddown"))) return e;
+        if ((e = launch_ntt(c, m, (int)(nout * 2 * K), true, s, "ks_intt_moddown"))) return e;
     }
     SetLayout lay_dn{(size_t)el * n, 0, (size_t)l * n, 1, 0};
     {
         ProfScope ps_(c, "ks_moddown_u", s);
-        hipLaunchKernelGGL(k_basis_u, dim3((n + 255) / 256, B * 2), dim3(256), 0, s, c->d_pbasis, lay_dn, w.acc,
-                           w.uP, n, c->d_pc);
+        hipLaunchKernelGGL(k_basis_u, dim3((n + 255) / 256, (unsigned)(nout * 2)), dim3(256), 0, s, c->d_pbasis,
+                           lay_dn, w.acc, w.uP, n, c->d_pc);
     }
     LAUNCH_CHECK();
     {
         ConvTargets ct{1, (uint32_t)l, L, K, (size_t)l * n, 0};
         ProfScope ps_(c, "ks_moddown_convert", s);
-        hipLaunchKernelGGL(k_convert, dim3((n + 255) / 256, (l + CT - 1) / CT, B * 2), dim3(256),
+        hipLaunchKernelGGL(k_convert, dim3((n + 255) / 256, (l + CT - 1) / CT, (unsigned)(nout * 2)), dim3(256),
                            (size_t)K * CT * 8, s, c->d_pbasis, lay_dn, w.acc, w.uP, ct, w.conv, n, c->d_pc);
     }
     LAUNCH_CHECK();
-    if (n != 2048) {  // at n = 2048 the final kernel transforms conv in LDS
+    if (n != 2048) {
         MapStrided m{w.conv, w.conv, n, (uint32_t)l, 0, nullptr};
-        if ((e = launch_ntt(c, m, B * 2 * l, false, s, "ks_ntt_moddown"))) return e;
+        if ((e = launch_ntt(c, m, (int)(nout * 2 * l), false, s, "ks_ntt_moddown"))) return e;
     }
     return CKKS_OK;
 }
@@ -809,9 +908,19 @@ size_t ws_bytes_rotate(const ckks_ctx *c, int B, int l) { return ks_words(c, B, 
 size_t ws_bytes_rescale(const ckks_ctx *c, int B, int l) {
     return (align_words((size_t)B * 2 * c->n) + align_words((size_t)B * 2 * (l - 1) * c->n)) * 8;
 }
+
+// Steps per batched key switch inside BSGS: as many as fit a workspace budget.
+constexpr size_t BSGS_KS_BUDGET = 8ull << 30;
+static int bsgs_chunk(const ckks_ctx *c, int B, int l, int bs, int gs) {
+    if (c->n != 2048) return 1;
+    const size_t per = ks_words(c, B, l, nullptr, nullptr) * 8;
+    int sc = (int)std::max<size_t>(1, BSGS_KS_BUDGET / std::max<size_t>(per, 1));
+    return std::max(1, std::min({sc, MAX_STEPS, std::max(bs, gs) - 1}));
+}
 static size_t bsgs_words(const ckks_ctx *c, int B, int l, int bs, int gs) {
     const size_t ct = (size_t)B * 2 * l * c->n;
-    return align_words(ct * (bs - 1)) + align_words(ct * gs) + ks_words(c, B, l, nullptr, nullptr) +
+    const int sc = bsgs_chunk(c, B, l, bs, gs);
+    return align_words(ct * (bs - 1)) + align_words(ct * gs) + ks_words(c, sc * B, l, nullptr, nullptr) +
            ws_bytes_rescale(c, B, l) / 8;
 }
 size_t ws_bytes_bsgs(const ckks_ctx *c, int B, int l, int bs, int gs) { return bsgs_words(c, B, l, bs, gs) * 8; }
@@ -831,14 +940,16 @@ int op_mul_tensor_relin(ckks_ctx *c, const uint64_t *a, const uint64_t *b, const
     }
     LAUNCH_CHECK();
     const size_t per = (size_t)l * n;
+    const Steps st = one_step(rlk, 1, B);
     if ((e = ks_modup(c, lt, B, l, w.d, per, w, s))) return e;
-    if ((e = ks_inner_moddown(c, lt, B, l, w.d, per, 1, rlk, w, s))) return e;
+    if ((e = ks_inner(c, lt, l, w.d, per, st, w, s))) return e;
+    if ((e = ks_moddown_conv(c, B, l, w, s))) return e;
     tot = (size_t)B * 2 * l * n;
     {
         ProfScope ps_(c, "relin_final", s);
         if (n == 2048)
             hipLaunchKernelGGL((k_final2048<1, false>), dim3(B * 2 * l), dim3(256), 0, s, w.acc, w.conv, c->d_pinv,
-                               c->d_pc, c->d_tw_fwd, a, b, 0u, out, (uint32_t)l, c->K);
+                               c->d_pc, c->d_tw_fwd, a, b, st, out, (uint32_t)l, c->K);
         else
             hipLaunchKernelGGL((k_moddown_final<1, false>), grid_for(tot), dim3(256), 0, s, w.acc, w.conv,
                                c->d_pinv, c->d_pc, a, b, 0u, out, n, (uint32_t)l, c->K, tot);
@@ -847,25 +958,27 @@ int op_mul_tensor_relin(ckks_ctx *c, const uint64_t *a, const uint64_t *b, const
     return CKKS_OK;
 }
 
-// Final kernel of a rotation: out (+)= (acc - conv) P^-1 + (sigma_g(c0), 0).
-static int rotate_final(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, uint32_t g, const KsWs &w,
+// Final kernel of a batch of rotations: out[cb] (+)= (acc - conv) P^-1 + (sigma_g(c0), 0).
+static int rotate_final(ckks_ctx *c, const uint64_t *in, uint64_t *out, int l, const Steps &st, const KsWs &w,
                         bool accumulate, hipStream_t s) {
-    const size_t tot = (size_t)B * 2 * l * c->n;
-    ProfScope ps_(c, accumulate ? "rotate_final_acc" : "rotate_final", s);
+    const size_t nout = (size_t)st.count * st.B;
+    const size_t tot = nout * 2 * l * c->n;
     const uint64_t *nul = nullptr;
+    ProfScope ps_(c, accumulate ? "rotate_final_acc" : "rotate_final", s);
     if (c->n == 2048) {
         if (accumulate)
-            hipLaunchKernelGGL((k_final2048<2, true>), dim3(B * 2 * l), dim3(256), 0, s, w.acc, w.conv, c->d_pinv,
-                               c->d_pc, c->d_tw_fwd, in, nul, g, out, (uint32_t)l, c->K);
+            hipLaunchKernelGGL((k_final2048<2, true>), dim3(nout * 2 * l), dim3(256), 0, s, w.acc, w.conv,
+                               c->d_pinv, c->d_pc, c->d_tw_fwd, in, nul, st, out, (uint32_t)l, c->K);
         else
-            hipLaunchKernelGGL((k_final2048<2, false>), dim3(B * 2 * l), dim3(256), 0, s, w.acc, w.conv, c->d_pinv,
-                               c->d_pc, c->d_tw_fwd, in, nul, g, out, (uint32_t)l, c->K);
-    } else if (accumulate) {
-        hipLaunchKernelGGL((k_moddown_final<2, true>), grid_for(tot), dim3(256), 0, s, w.acc, w.conv, c->d_pinv,
-                           c->d_pc, in, nul, g, out, c->n, (uint32_t)l, c->K, tot);
-    } else {
-        hipLaunchKernelGGL((k_moddown_final<2, false>), grid_for(tot), dim3(256), 0, s, w.acc, w.conv, c->d_pinv,
-                           c->d_pc, in, nul, g, out, c->n, (uint32_t)l, c->K, tot);
+            hipLaunchKernelGGL((k_final2048<2, false>), dim3(nout * 2 * l), dim3(256), 0, s, w.acc, w.conv,
+                               c->d_pinv, c->d_pc, c->d_tw_fwd, in, nul, st, out, (uint32_t)l, c->K);
+    } else {  // generic n: single step
+        if (accumulate)
+            hipLaunchKernelGGL((k_moddown_final<2, true>), grid_for(tot), dim3(256), 0, s, w.acc, w.conv, c->d_pinv,
+                               c->d_pc, in, nul, st.g[0], out, c->n, (uint32_t)l, c->K, tot);
+        else
+            hipLaunchKernelGGL((k_moddown_final<2, false>), grid_for(tot), dim3(256), 0, s, w.acc, w.conv,
+                               c->d_pinv, c->d_pc, in, nul, st.g[0], out, c->n, (uint32_t)l, c->K, tot);
     }
     LAUNCH_CHECK();
     return CKKS_OK;
@@ -882,9 +995,11 @@ int op_rotate(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, uint
     ks_words(c, B, l, &w, (uint64_t *)ws);
     const size_t per = (size_t)l * c->n;
     const uint64_t *c1 = in + per;
+    const Steps st = one_step(key, g, B);
     if ((e = ks_modup(c, lt, B, l, c1, 2 * per, w, s))) return e;
-    if ((e = ks_inner_moddown(c, lt, B, l, c1, 2 * per, g, key, w, s))) return e;
-    return rotate_final(c, in, out, B, l, g, w, accumulate, s);
+    if ((e = ks_inner(c, lt, l, c1, 2 * per, st, w, s))) return e;
+    if ((e = ks_moddown_conv(c, B, l, w, s))) return e;
+    return rotate_final(c, in, out, l, st, w, accumulate, s);
 }
 
 int op_rescale(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, void *ws, hipStream_t s) {
@@ -936,39 +1051,67 @@ static uint32_t rot_elt(uint32_t n, uint64_t k) {
 int op_bsgs(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, const uint64_t *diags, int bs, int gs,
             const uint64_t *const *baby, const uint64_t *const *giant, bool rescale, void *ws, hipStream_t s) {
     const size_t ct = (size_t)B * 2 * l * c->n;
+    const size_t per = (size_t)l * c->n;
+    const int sc = bsgs_chunk(c, B, l, bs, gs);
     uint64_t *rot = (uint64_t *)ws;
     uint64_t *inner = rot + align_words(ct * (bs - 1));
     uint64_t *ksws = inner + align_words(ct * gs);
-    uint64_t *rsws = ksws + ks_words(c, B, l, nullptr, nullptr);
+    uint64_t *rsws = ksws + ks_words(c, sc * B, l, nullptr, nullptr);
     int e = CKKS_OK;
+    LevelTables *lt = level_tables(c, l, &e);
+    if (!lt) return e;
+    KsWs w;
+    ks_words(c, sc * B, l, &w, ksws);
     if (bs > 1) {
-        // baby steps hoisted: one ModUp of c1, then per step a gathered inner product + ModDown
-        LevelTables *lt = level_tables(c, l, &e);
-        if (!lt) return e;
-        KsWs w;
-        ks_words(c, B, l, &w, ksws);
-        const size_t per = (size_t)l * c->n;
+        // baby steps hoisted: one ModUp of c1, then batches of steps sharing it
         if ((e = ks_modup(c, lt, B, l, in + per, 2 * per, w, s))) return e;
-        for (int b = 1; b < bs; b++) {
-            const uint32_t g = rot_elt(c->n, b);
-            if ((e = ks_inner_moddown(c, lt, B, l, in + per, 2 * per, g, baby[b], w, s))) return e;
-            if ((e = rotate_final(c, in, rot + (size_t)(b - 1) * ct, B, l, g, w, false, s))) return e;
+        for (int b0 = 1; b0 < bs; b0 += sc) {
+            Steps st{};
+            st.count = (uint32_t)std::min(sc, bs - b0);
+            st.B = (uint32_t)B;
+            st.shared = 1;
+            for (uint32_t j = 0; j < st.count; j++) {
+                st.key[j] = baby[b0 + j];
+                st.g[j] = rot_elt(c->n, b0 + j);
+            }
+            if ((e = ks_inner(c, lt, l, in + per, 2 * per, st, w, s))) return e;
+            if ((e = ks_moddown_conv(c, (size_t)st.count * B, l, w, s))) return e;
+            if ((e = rotate_final(c, in, rot + (size_t)(b0 - 1) * ct, l, st, w, false, s))) return e;
         }
     }
     for (int b0 = 0; b0 < bs; b0 += MAC_B) {
-        {
-            ProfScope ps_(c, "bsgs_mac", s);
-            hipLaunchKernelGGL(k_bsgs_mac, dim3(c->n / MAC_K, l, (2 * B + MAC_C - 1) / MAC_C), dim3(256), 0, s, diags,
-                               in, rot, inner, c->d_pc, c->n, (uint32_t)l, (uint32_t)bs, (uint32_t)gs, (uint32_t)(2 * B),
-                               ct, (uint32_t)b0);
-        }
+        ProfScope ps_(c, "bsgs_mac", s);
+        hipLaunchKernelGGL(k_bsgs_mac, dim3(c->n / MAC_K, l, (2 * B + MAC_C - 1) / MAC_C), dim3(256), 0, s, diags,
+                           in, rot, inner, c->d_pc, c->n, (uint32_t)l, (uint32_t)bs, (uint32_t)gs, (uint32_t)(2 * B),
+                           ct, (uint32_t)b0);
         LAUNCH_CHECK();
     }
-    // giant steps accumulate into inner[0]
-    for (int g = 1; g < gs; g++)
-        if ((e = op_rotate(c, inner + (size_t)g * ct, inner, B, l, rot_elt(c->n, (uint64_t)g * bs), giant[g], ksws,
-                           true, s)))
-            return e;
+    // giant steps: batches of independent rotations of inner[g], summed into inner[0]
+    for (int g0 = 1; g0 < gs; g0 += sc) {
+        Steps st{};
+        st.count = (uint32_t)std::min(sc, gs - g0);
+        st.B = (uint32_t)B;
+        st.shared = 0;
+        for (uint32_t j = 0; j < st.count; j++) {
+            st.key[j] = giant[g0 + j];
+            st.g[j] = rot_elt(c->n, (uint64_t)(g0 + j) * bs);
+        }
+        const uint64_t *src = inner + (size_t)g0 * ct;  // ciphertexts (g0 + j, b), consecutive
+        const int nb = (int)st.count * B;
+        if (c->n == 2048) {
+            if ((e = ks_modup(c, lt, nb, l, src + per, 2 * per, w, s))) return e;
+            if ((e = ks_inner(c, lt, l, src + per, 2 * per, st, w, s))) return e;
+            if ((e = ks_moddown_conv(c, nb, l, w, s))) return e;
+            ProfScope ps_(c, "giant_final_sum", s);
+            hipLaunchKernelGGL(k_final_sum2048, dim3(B * 2 * l), dim3(256), 0, s, w.acc, w.conv, c->d_pinv, c->d_pc,
+                               c->d_tw_fwd, src, st, inner, (uint32_t)l, c->K);
+            LAUNCH_CHECK();
+        } else {
+            for (uint32_t j = 0; j < st.count; j++)
+                if ((e = op_rotate(c, src + (size_t)j * ct, inner, B, l, st.g[j], st.key[j], ksws, true, s)))
+                    return e;
+        }
+    }
     if (rescale) return op_rescale(c, inner, out, B, l, rsws, s);
     {
         ProfScope ps_(c, "copy", s);
