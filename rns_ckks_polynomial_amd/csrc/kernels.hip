@@ -743,8 +743,8 @@ __global__ __launch_bounds__(256) void k_bsgs_mac(const uint64_t *__restrict__ p
     uint64_t st0 = *pt_addr(0, threadIdx.x), st1 = *pt_addr(0, threadIdx.x + 256);
     for (uint32_t g = 0; g < gs; g++) {
         uint64_t *buf = ps[g & 1];
-        buf[threadIdx.x] = st0;
-        buf[threadIdx.x + 256] = st1;
+        buf[threadIdx.x] = split30(st0);  // stored split: low 30 bits | high 30 bits << 32
+        buf[threadIdx.x + 256] = split30(st1);
         __syncthreads();
         if (g + 1 < gs) {  // prefetch the next giant step's diagonals
             st0 = *pt_addr(g + 1, threadIdx.x);
@@ -754,10 +754,9 @@ __global__ __launch_bounds__(256) void k_bsgs_mac(const uint64_t *__restrict__ p
         Acc128 acc{0, 0};
 #pragma unroll
         for (int bb = 0; bb < MAC_B; bb++) {
-            if (bb < (int)nb) {
-                const uint64_t p = buf[bb * MAC_K + kl];
-                smac(sp, (uint32_t)(p & M30), (uint32_t)(p >> 30), r[bb]);
-            }
+            // rows bb >= nb hold a valid (clamped) diagonal and r[bb] = 0: no guard needed
+            const uint64_t p = buf[bb * MAC_K + kl];
+            smac(sp, (uint32_t)p, (uint32_t)(p >> 32), r[bb]);
             if (bb % SPLIT_CHUNK == SPLIT_CHUNK - 1) sflush(acc, sp);
         }
         sflush(acc, sp);
