@@ -74,7 +74,9 @@ typedef struct {
 /* Create a context on HIP device `device`: generates the chain primes and
  * roots (Kestrel relay README section 1 / article section 4.1 parameters:
  * n = 2048, 60-bit primes, 112 or 2100 of them), and uploads twiddle and
- * base-conversion tables.  Returns CKKS_EUNSUPPORTED for unsupported n. */
+ * base-conversion tables.  Returns CKKS_EUNSUPPORTED for unsupported n, for
+ * a chain prime at or above 2^59 + 2^52, or for a digit width ceil(L/dnum) or
+ * K above 1000 (the bounds of the exact 128-bit base-conversion sums). */
 int ckks_ctx_create(ckks_ctx **out, const ckks_params *params, int device);
 void ckks_ctx_destroy(ckks_ctx *ctx);
 /* Copy the chain primes and their psi to host arrays of L+K entries (either may be NULL). */

@@ -112,12 +112,39 @@ __device__ __forceinline__ void sflush(Acc128 &acc, Split3 &s) {
     s.a0 = s.a1 = s.a1b = s.a2 = 0;
 }
 
+// Carry normalisation inside the 64-bit lanes (value-preserving):
+// afterwards a0, a1 < 2^30 and a1b = 0, so 15 more smac fit before the next
+// snorm; a2 (weight 2^60) gains below 2^62 per round and is moved into a
+// 128-bit high accumulator (units of 2^60) by sfold_hi at least every 4 rounds.
+__device__ __forceinline__ void snorm(Split3 &s) {
+    s.a1 += s.a1b + (s.a0 >> 30);
+    s.a0 &= M30;
+    s.a1b = 0;
+    s.a2 += s.a1 >> 30;
+    s.a1 &= M30;
+}
+__device__ __forceinline__ void sfold_hi(Acc128 &hi, Split3 &s) {
+    u128 v = ((u128)hi.hi << 64 | hi.lo) + s.a2;
+    hi.lo = (uint64_t)v;
+    hi.hi = (uint64_t)(v >> 64);
+    s.a2 = 0;
+}
+// The 128-bit value a0 + 2^30 (a1 + a1b) + 2^60 (a2 + hi).
+__device__ __forceinline__ Acc128 sfinal(const Acc128 &hi, Split3 s) {
+    snorm(s);
+    const u128 h = ((u128)hi.hi << 64 | hi.lo) + s.a2;
+    const u128 v = (h << 60) + (s.a0 | (s.a1 << 30));
+    return Acc128{(uint64_t)v, (uint64_t)(v >> 64)};
+}
+
 // ------------------------------------------------------------------ tables
 // Exact base conversion from a contiguous run of primes (a "basis": one
 // key-switching digit, or the special primes P) to any other chain prime.
 // The centered CRT value x_c of residues x_i modulo B = prod b_i is
 //   x_c = sum_i y_i Bhat_i - u B,   y_i = [x_i Bhat_i^-1]_{b_i},
 //   u = round(sum_i y_i / b_i)  (= floor(sum) + [x > (B-1)/2]).
+constexpr uint32_t CONV_ROW_PAD = 5;
+constexpr uint32_t CONV_COL_PAD = 8;
 struct BasisDev {
     uint32_t m;            // number of primes in the basis
     uint32_t first;        // global index of the first basis prime
@@ -126,7 +153,15 @@ struct BasisDev {
     const uint64_t *inv_hat;  // [m][2]  Shoup pair of [Bhat_i^-1]_{b_i}
     const uint64_t *hat_mod;  // [m][2]  Shoup pair of [Bhat_i]_{b_i}   (recovers x_i from y_i)
     const uint64_t *R;        // [m]     floor(2^123 / b_i)                (fixed-point 1/b_i)
-    const uint64_t *H;        // [ntot][m]  [Bhat_i]_t for every chain prime t, split30 layout
+    // [Bhat_i]_t in split30 layout, row i = input prime, column = target position:
+    // for a chain digit the positions run over the special primes first, then
+    // the chain primes outside the digit (so the targets at any level are a
+    // prefix); for the special basis they run over the chain primes.  Rows are
+    // padded with zeros to a multiple of CONV_ROW_PAD and each row holds
+    // CONV_COL_PAD spare columns, so whole tiles can be read without bounds checks.
+    const uint64_t *HT;
+    uint32_t hstride;         // row length of HT (positions + CONV_COL_PAD)
+    uint32_t mpad;            // row count of HT
     const uint64_t *negB;     // [ntot]     [-B]_t
     const uint64_t *garner;   // [m][m][2]  Shoup pair of b_k^-1 mod b_i (k < i used)
     const uint64_t *half;     // [m]        mixed-radix digits of (B-1)/2

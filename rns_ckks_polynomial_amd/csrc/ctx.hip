@@ -162,9 +162,24 @@ int build_basis(ckks_ctx *ctx, uint32_t first, uint32_t m, BasisDev *out, std::v
     }
     for (uint32_t i = 0; i < m; i++) half[i] = big_divmod(B, b[i]);
 
-    // the conversion kernels read H in the split layout: lo32 = h mod 2^30, hi32 = h >> 30
-    std::vector<uint64_t> Hs(H.size());
-    for (size_t x = 0; x < H.size(); x++) Hs[x] = (H[x] & ((1ull << 30) - 1)) | ((H[x] >> 30) << 32);
+    // the conversion kernels read H transposed, in target-position order and in
+    // the split layout (lo32 = h mod 2^30, hi32 = h >> 30)
+    std::vector<uint32_t> pos;  // position -> target prime
+    if (first < ctx->L) {
+        for (uint32_t t = ctx->L; t < ntot; t++) pos.push_back(t);
+        for (uint32_t t = 0; t < ctx->L; t++)
+            if (t < first || t >= first + m) pos.push_back(t);
+    } else {
+        for (uint32_t t = 0; t < ctx->L; t++) pos.push_back(t);
+    }
+    const uint32_t hstride = (uint32_t)pos.size() + CONV_COL_PAD;
+    const uint32_t mpad = (m + CONV_ROW_PAD - 1) / CONV_ROW_PAD * CONV_ROW_PAD;
+    std::vector<uint64_t> Hs((size_t)mpad * hstride, 0);
+    for (uint32_t i = 0; i < m; i++)
+        for (uint32_t p = 0; p < pos.size(); p++) {
+            const uint64_t h = H[(size_t)pos[p] * m + i];
+            Hs[(size_t)i * hstride + p] = (h & ((1ull << 30) - 1)) | ((h >> 30) << 32);
+        }
     int err = CKKS_OK;
     BasisDev d{};
     d.m = m;
@@ -173,7 +188,9 @@ int build_basis(ckks_ctx *ctx, uint32_t first, uint32_t m, BasisDev *out, std::v
     d.inv_hat = dev_upload(inv_hat, owned, &err);
     d.hat_mod = dev_upload(hat_mod, owned, &err);
     d.R = dev_upload(R, owned, &err);
-    d.H = dev_upload(Hs, owned, &err);
+    d.HT = dev_upload(Hs, owned, &err);
+    d.hstride = hstride;
+    d.mpad = mpad;
     d.negB = dev_upload(negB, owned, &err);
     d.garner = dev_upload(garner, owned, &err);
     d.half = dev_upload(half, owned, &err);
@@ -266,10 +283,11 @@ extern "C" int ckks_ctx_create(ckks_ctx **out, const ckks_params *params, int de
     const uint32_t ntot = p.L + p.K, n = p.n;
     int err = CKKS_OK;
     if (!h_chain(n, ntot, c->primes)) err = CKKS_EINVAL;
-    // the split multiply-accumulate bounds assume every prime is below 2^59 + 2^52
-    // and at most 1023 products per sum (digit width and K)
+    // the split multiply-accumulate bounds assume every prime is below 2^59 + 2^52,
+    // and a base conversion sums at most 1000 products (digit width and K) so
+    // that m (2^59 + 2^52)^2 plus the u [-B]_t term stays below 2^128
     if (!err && c->primes.back() >= (1ull << 59) + (1ull << 52)) err = CKKS_EUNSUPPORTED;
-    if (!err && (c->alpha > 1023 || p.K > 1023)) err = CKKS_EUNSUPPORTED;
+    if (!err && (c->alpha > 1000 || p.K > 1000)) err = CKKS_EUNSUPPORTED;
     if (!err) {
         c->psi.resize(ntot);
         std::vector<PrimeConsts> pc(ntot);

@@ -304,69 +304,86 @@ __global__ void k_basis_u(const BasisDev *__restrict__ bases, SetLayout lay, uin
 
 // ---------------------------------------------------------------------
 // Base conversion: out_t = sum_i y_i [Bhat_i]_t + u [-B]_t mod t.
-// One thread per coefficient and CT targets per workgroup.  The block's
-// table rows (split30 layout) are staged in LDS and read as wave-uniform
-// broadcasts; each product is four v_mad_u64_u32 into split partial sums
-// (see smac), folded into 128 bits every SPLIT_CHUNK inputs.
+// One thread per coefficient and CT targets per workgroup.  The table row of
+// input i for the block's CT targets is contiguous (target-position order),
+// wave-uniform and read-only, so it is fetched with scalar loads and used as
+// SGPR operands; the inputs y_i are prefetched CONV_ROW_PAD rows ahead.  Each
+// product is four v_mad_u64_u32 into split partial sums (see smac), folded
+// into 128 bits every SPLIT_CHUNK inputs.
 // ---------------------------------------------------------------------
 constexpr int CT = 8;
+constexpr int YC = (int)CONV_ROW_PAD;
+static_assert(SPLIT_CHUNK % YC == 0, "flush on a chunk boundary");
+static_assert(CT <= (int)CONV_COL_PAD, "tile reads stay inside a table row");
 
 struct ConvTargets {
-    // mode 0 (ModUp of digit [lo, lo+m)): targets = [0, lo) u [lo+m, l) u [L, L+K) -> ext slots
+    // mode 0 (ModUp of digit [lo, lo+m)): target positions run over [L, L+K),
+    // then [0, lo) u [lo+m, l); the outputs go to ext slots (special t -> l + t - L)
     // mode 1 (ModDown): targets = [0, l) -> slot t
     uint32_t mode, l, L, K;
     size_t out_so, out_si;  // output limb base of set s: (s / inner) * out_so + (s % inner) * out_si
 };
 
 __device__ __forceinline__ uint32_t conv_target(const ConvTargets &ct, uint32_t tn, uint32_t lo, uint32_t m) {
-    if (ct.mode == 1 || tn < lo) return tn;
-    if (tn < ct.l - m) return tn + m;
-    return ct.L + (tn - (ct.l - m));
+    if (ct.mode == 1) return tn;
+    if (tn < ct.K) return ct.L + tn;
+    const uint32_t c = tn - ct.K;
+    return c < lo ? c : c + m;
 }
 
 __global__ __launch_bounds__(256) void k_convert(const BasisDev *__restrict__ bases, SetLayout lay,
                                                   const uint64_t *__restrict__ y, const uint32_t *__restrict__ u,
                                                   ConvTargets ct, uint64_t *__restrict__ out, uint32_t n,
                                                   const PrimeConsts *__restrict__ pc) {
-    extern __shared__ uint64_t hs[];  // [m][CT]
     const uint32_t s = blockIdx.z;
     const BasisDev &B = bases[lay.per_set_basis ? s % lay.inner : 0];
     const uint32_t m = B.m, lo = B.first;
     const uint32_t ntarget = ct.mode == 0 ? ct.l - m + ct.K : ct.l;
     const uint32_t tn0 = blockIdx.y * CT;
-    if (tn0 >= ntarget) return;  // whole workgroup leaves together
+    if (tn0 >= ntarget) return;
     const uint32_t nt = min((uint32_t)CT, ntarget - tn0);
-    for (uint32_t x = threadIdx.x; x < m * CT; x += blockDim.x) {
-        const uint32_t a = x % CT, i = x / CT;
-        const uint32_t t = conv_target(ct, tn0 + min(a, nt - 1), lo, m);
-        hs[x] = B.H[(size_t)t * m + i];
-    }
-    __syncthreads();
     const uint32_t k = blockIdx.x * blockDim.x + threadIdx.x;
     if (k >= n) return;
+    // row i at ht + i * hstride (zero rows past m); the constant address space
+    // lets the compiler fetch these wave-uniform rows with scalar loads
+    const __attribute__((address_space(4))) uint64_t *ht =
+        (const __attribute__((address_space(4))) uint64_t *)(B.HT + tn0);
+    const uint32_t hstride = B.hstride, mpad = B.mpad;
     const uint64_t *yb = y + (s / lay.inner) * lay.so + (s % lay.inner) * lay.si + lay.off + k;
     Split3 sp[CT];
-    Acc128 acc[CT];
+    Acc128 acc[CT];  // units of 2^60 until sfinal
 #pragma unroll
     for (int a = 0; a < CT; a++) {
         sp[a] = {0, 0, 0, 0};
         acc[a] = {0, 0};
     }
-    uint64_t ynext = yb[0];
-    for (uint32_t i0 = 0; i0 < m; i0 += SPLIT_CHUNK) {
-        const uint32_t i1 = min(m, i0 + SPLIT_CHUNK);
-#pragma unroll 5
-        for (uint32_t i = i0; i < i1; i++) {
-            const uint64_t yv = ynext;  // loads run one input ahead
-            ynext = yb[(size_t)min(i + 1, m - 1) * n];
-            const uint32_t yl = (uint32_t)(yv & M30), yh = (uint32_t)(yv >> 30);
-            const uint64_t *hr = hs + i * CT;
+    uint64_t yv[YC], yn[YC];
+#pragma unroll
+    for (int r = 0; r < YC; r++) yv[r] = yb[(size_t)min((uint32_t)r, m - 1) * n];
+    for (uint32_t i0 = 0; i0 < mpad; i0 += YC) {
+#pragma unroll
+        for (int r = 0; r < YC; r++) yn[r] = yb[(size_t)min(i0 + YC + r, m - 1) * n];
+#pragma unroll
+        for (int r = 0; r < YC; r++) {  // rows past m: y repeats row m-1, the table row is zero
+            const uint32_t yl = (uint32_t)(yv[r] & M30), yh = (uint32_t)(yv[r] >> 30);
+            const __attribute__((address_space(4))) uint64_t *hr = ht + (size_t)(i0 + r) * hstride;
 #pragma unroll
             for (int a = 0; a < CT; a++) smac(sp[a], yl, yh, hr[a]);
         }
+        const uint32_t chunk = i0 / YC;
+        if (chunk % (SPLIT_CHUNK / YC) == SPLIT_CHUNK / YC - 1) {
 #pragma unroll
-        for (int a = 0; a < CT; a++) sflush(acc[a], sp[a]);
+            for (int a = 0; a < CT; a++) snorm(sp[a]);
+            if (chunk % (4 * SPLIT_CHUNK / YC) == 4 * SPLIT_CHUNK / YC - 1) {
+#pragma unroll
+                for (int a = 0; a < CT; a++) sfold_hi(acc[a], sp[a]);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < YC; r++) yv[r] = yn[r];
     }
+#pragma unroll
+    for (int a = 0; a < CT; a++) acc[a] = sfinal(acc[a], sp[a]);
     const uint64_t uu = u[(size_t)s * n + k];
     uint64_t *ob = out + (s / lay.inner) * ct.out_so + (s % lay.inner) * ct.out_si + k;
 #pragma unroll
