@@ -113,13 +113,20 @@ def kernel_work():
         "ks_modup_convert": {"mads": 4 * n_up * beta * a * (l + K - a) * N,
                              "bytes": (n_up * l + n_up * beta * (el - a)) * limb},
         "ks_ntt_ext": {"bytes": 2 * n_up * beta * (el - a) * limb},
-        "ks_inner_product": {"bytes": ((1 + sg) * B * (beta + 2) * el + (1 + sg) * 2 * beta * el) * limb},
+        # relinearisation (all limbs) + the giant steps' P-limbs
+        "ks_inner_product": {"bytes": (B * (beta + 2) * el + 2 * beta * el
+                                       + sg * B * (beta + 2) * K + sg * 2 * beta * K) * limb},
+        # giant steps' Q-limbs summed over the steps: digits + c0 in, 4 partial sums out
+        "ks_inner_product_sum": {"bytes": (sg * B * (beta + 1) * l + sg * 2 * beta * l + 4 * B * 2 * l) * limb},
         "ks_inner_product_hoisted": {"bytes": (sb * B * (beta + 2) * el + sb * 2 * beta * el) * limb},
         "ks_intt_moddown": {"bytes": 2 * n_dn * 2 * K * limb},
         "ks_moddown_u": {"bytes": n_dn * 2 * K * limb},
-        "ks_moddown_convert": {"mads": 4 * n_dn * 2 * K * l * N, "bytes": (n_dn * 2 * K + n_dn * 2 * l) * limb},
+        # giant-step conversions are summed in the kernel: one output per ciphertext
+        "ks_moddown_convert": {"mads": 4 * n_dn * 2 * K * l * N,
+                               "bytes": (n_dn * 2 * K + (1 + sb + 1) * B * 2 * l) * limb},
         "rotate_final": {"bytes": sb * B * 7 * l * limb},
-        "giant_final_sum": {"bytes": (sg * B * 5 * l + B * 4 * l) * limb},
+        # conv in, 4 partial sums in, output read + written
+        "giant_final": {"bytes": B * 2 * l * (1 + 4 + 2) * limb},
         "bsgs_mac": {"mads": 4 * GS * BS * 2 * B * l * N,
                      "bytes": (GS * BS * l + BS * 2 * B * l + GS * 2 * B * l) * limb},
         "ntt_fwd": {"bytes": 2 * B * 2 * l * limb, "standalone": True},

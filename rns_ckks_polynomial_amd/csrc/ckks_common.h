@@ -136,6 +136,13 @@ __device__ __forceinline__ Acc128 sfinal(const Acc128 &hi, Split3 s) {
     const u128 v = (h << 60) + (s.a0 | (s.a1 << 30));
     return Acc128{(uint64_t)v, (uint64_t)(v >> 64)};
 }
+// Full reduction of a split sum modulo P.q, left in normalised split form
+// (a0, a1 < 2^30, a2 = 0): restarts the growth bounds of snorm.
+__device__ __forceinline__ void sreduce(Split3 &s, const PrimeConsts &P) {
+    const Acc128 v = sfinal(Acc128{0, 0}, s);
+    const uint64_t r = reduce128(v.lo, v.hi, P);
+    s = Split3{r & M30, r >> 30, 0, 0};
+}
 
 // ------------------------------------------------------------------ tables
 // Exact base conversion from a contiguous run of primes (a "basis": one

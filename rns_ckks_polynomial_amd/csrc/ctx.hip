@@ -337,7 +337,7 @@ extern "C" int ckks_ctx_create(ckks_ctx **out, const ckks_params *params, int de
             c->d_pbasis = dev_upload(one, c->owned, &err);
             std::vector<uint64_t> ih(2 * p.K);
             hipMemcpy(ih.data(), c->h_pbasis.inv_hat, ih.size() * 8, hipMemcpyDeviceToHost);
-            std::vector<uint64_t> sc(2 * p.K), pinv(2 * p.L);
+            std::vector<uint64_t> sc(2 * p.K), pinv(2 * p.L), pmod(p.L);
             for (uint32_t k = 0; k < p.K; k++) {
                 uint64_t q = c->primes[p.L + k], v = h_mulmod(h_invmod(n % q, q), ih[2 * k], q);
                 sc[2 * k] = v;
@@ -347,11 +347,13 @@ extern "C" int ckks_ctx_create(ckks_ctx **out, const ckks_params *params, int de
                 uint64_t q = c->primes[i], P = 1;
                 for (uint32_t k = 0; k < p.K; k++) P = h_mulmod(P, c->primes[p.L + k] % q, q);
                 uint64_t v = h_invmod(P, q);
+                pmod[i] = P;
                 pinv[2 * i] = v;
                 pinv[2 * i + 1] = h_shoup(v, q);
             }
             c->d_moddown_scale = dev_upload(sc, c->owned, &err);
             c->d_pinv = dev_upload(pinv, c->owned, &err);
+            c->d_pmod = dev_upload(pmod, c->owned, &err);
         }
     }
     if (!err && n > 2048) err = multipass_init(c);

@@ -56,6 +56,7 @@ struct ckks_ctx {
     ckks::BasisDev *d_pbasis = nullptr;
     uint64_t *d_moddown_scale = nullptr;  // [K][2] Shoup pair of n^-1 [Phat_k^-1]_{p_k}
     uint64_t *d_pinv = nullptr;           // [L][2] Shoup pair of P^-1 mod q_i
+    uint64_t *d_pmod = nullptr;           // [L]    P mod q_i
     // full-width digits at the top level (reused by every level where the digit is whole)
     std::vector<ckks::BasisDev> full_digits;
     std::vector<void *> owned;

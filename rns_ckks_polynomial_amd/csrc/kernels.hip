@@ -322,6 +322,9 @@ struct ConvTargets {
     // mode 1 (ModDown): targets = [0, l) -> slot t
     uint32_t mode, l, L, K;
     size_t out_so, out_si;  // output limb base of set s: (s / inner) * out_so + (s % inner) * out_si
+    // output set s is the sum of the conversions of input sets s + j * sum_stride, j < nsum
+    // (each converted exactly with its own u; nsum * m <= 1000 keeps the sum in 128 bits)
+    uint32_t nsum = 1, sum_stride = 0;
 };
 
 __device__ __forceinline__ uint32_t conv_target(const ConvTargets &ct, uint32_t tn, uint32_t lo, uint32_t m) {
@@ -349,7 +352,6 @@ __global__ __launch_bounds__(256) void k_convert(const BasisDev *__restrict__ ba
     const __attribute__((address_space(4))) uint64_t *ht =
         (const __attribute__((address_space(4))) uint64_t *)(B.HT + tn0);
     const uint32_t hstride = B.hstride, mpad = B.mpad;
-    const uint64_t *yb = y + (s / lay.inner) * lay.so + (s % lay.inner) * lay.si + lay.off + k;
     Split3 sp[CT];
     Acc128 acc[CT];  // units of 2^60 until sfinal
 #pragma unroll
@@ -357,34 +359,39 @@ __global__ __launch_bounds__(256) void k_convert(const BasisDev *__restrict__ ba
         sp[a] = {0, 0, 0, 0};
         acc[a] = {0, 0};
     }
-    uint64_t yv[YC], yn[YC];
+    uint64_t uu = 0;
+    uint32_t chunk = 0;  // chunks of YC rows done, over all summed sets
+    for (uint32_t js = 0; js < ct.nsum; js++) {
+        const size_t ss = s + (size_t)js * ct.sum_stride;
+        const uint64_t *yb = y + (ss / lay.inner) * lay.so + (ss % lay.inner) * lay.si + lay.off + k;
+        uint64_t yv[YC], yn[YC];
 #pragma unroll
-    for (int r = 0; r < YC; r++) yv[r] = yb[(size_t)min((uint32_t)r, m - 1) * n];
-    for (uint32_t i0 = 0; i0 < mpad; i0 += YC) {
+        for (int r = 0; r < YC; r++) yv[r] = yb[(size_t)min((uint32_t)r, m - 1) * n];
+        for (uint32_t i0 = 0; i0 < mpad; i0 += YC, chunk++) {
 #pragma unroll
-        for (int r = 0; r < YC; r++) yn[r] = yb[(size_t)min(i0 + YC + r, m - 1) * n];
+            for (int r = 0; r < YC; r++) yn[r] = yb[(size_t)min(i0 + YC + r, m - 1) * n];
 #pragma unroll
-        for (int r = 0; r < YC; r++) {  // rows past m: y repeats row m-1, the table row is zero
-            const uint32_t yl = (uint32_t)(yv[r] & M30), yh = (uint32_t)(yv[r] >> 30);
-            const __attribute__((address_space(4))) uint64_t *hr = ht + (size_t)(i0 + r) * hstride;
+            for (int r = 0; r < YC; r++) {  // rows past m: y repeats row m-1, the table row is zero
+                const uint32_t yl = (uint32_t)(yv[r] & M30), yh = (uint32_t)(yv[r] >> 30);
+                const __attribute__((address_space(4))) uint64_t *hr = ht + (size_t)(i0 + r) * hstride;
 #pragma unroll
-            for (int a = 0; a < CT; a++) smac(sp[a], yl, yh, hr[a]);
-        }
-        const uint32_t chunk = i0 / YC;
-        if (chunk % (SPLIT_CHUNK / YC) == SPLIT_CHUNK / YC - 1) {
-#pragma unroll
-            for (int a = 0; a < CT; a++) snorm(sp[a]);
-            if (chunk % (4 * SPLIT_CHUNK / YC) == 4 * SPLIT_CHUNK / YC - 1) {
-#pragma unroll
-                for (int a = 0; a < CT; a++) sfold_hi(acc[a], sp[a]);
+                for (int a = 0; a < CT; a++) smac(sp[a], yl, yh, hr[a]);
             }
-        }
+            if (chunk % (SPLIT_CHUNK / YC) == SPLIT_CHUNK / YC - 1) {
 #pragma unroll
-        for (int r = 0; r < YC; r++) yv[r] = yn[r];
+                for (int a = 0; a < CT; a++) snorm(sp[a]);
+                if (chunk % (4 * SPLIT_CHUNK / YC) == 4 * SPLIT_CHUNK / YC - 1) {
+#pragma unroll
+                    for (int a = 0; a < CT; a++) sfold_hi(acc[a], sp[a]);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < YC; r++) yv[r] = yn[r];
+        }
+        uu += u[ss * n + k];
     }
 #pragma unroll
     for (int a = 0; a < CT; a++) acc[a] = sfinal(acc[a], sp[a]);
-    const uint64_t uu = u[(size_t)s * n + k];
     uint64_t *ob = out + (s / lay.inner) * ct.out_so + (s % lay.inner) * ct.out_si + k;
 #pragma unroll
     for (int a = 0; a < CT; a++) {
@@ -419,15 +426,16 @@ __global__ __launch_bounds__(256) void k_inner2048(const uint64_t *__restrict__ 
                                                     const uint64_t *__restrict__ ext, const Steps st,
                                                     uint64_t *__restrict__ acc, const PrimeConsts *__restrict__ pc,
                                                     uint32_t l, uint32_t L, uint32_t K, uint32_t beta,
-                                                    uint32_t alpha) {
+                                                    uint32_t alpha, uint32_t e0, uint32_t ne) {
     constexpr uint32_t n = 2048;
     __shared__ uint64_t buf[2][n];
     const uint32_t el = l + K;
-    // block order: ciphertext fastest, then limb, then step, so the B blocks
-    // reading one key row run together and one step's key is in flight at a time
+    // block order: ciphertext fastest, then limb (of the range [e0, e0 + ne)),
+    // then step, so the B blocks reading one key row run together and one
+    // step's key is in flight at a time
     const uint32_t bl = blockIdx.x % st.B;
-    const uint32_t e = (blockIdx.x / st.B) % el;
-    const uint32_t step = blockIdx.x / (st.B * el);
+    const uint32_t e = e0 + (blockIdx.x / st.B) % ne;
+    const uint32_t step = blockIdx.x / (st.B * ne);
     const size_t cb = (size_t)step * st.B + bl;
     const size_t b = st.shared ? bl : cb;  // input ciphertext
     const uint64_t *key = st.key[step];
@@ -454,14 +462,128 @@ __global__ __launch_bounds__(256) void k_inner2048(const uint64_t *__restrict__ 
             smac(s0[m], vl, vh, split30(kb[k]));
             smac(s1[m], vl, vh, split30(ka[k]));
         }
+        if ((j + 1) % SPLIT_CHUNK == 0) {  // more than 15 digits: keep the sums in bounds
+#pragma unroll
+            for (int m = 0; m < 8; m++) {
+                snorm(s0[m]);
+                snorm(s1[m]);
+            }
+            if ((j + 1) % (4 * SPLIT_CHUNK) == 0) {
+#pragma unroll
+                for (int m = 0; m < 8; m++) {
+                    sreduce(s0[m], pc[gi]);
+                    sreduce(s1[m], pc[gi]);
+                }
+            }
+        }
     }
     const PrimeConsts P = pc[gi];
     uint64_t *o0 = acc + ((cb * 2 + 0) * el + e) * n, *o1 = acc + ((cb * 2 + 1) * el + e) * n;
 #pragma unroll
     for (int m = 0; m < 8; m++) {
-        Acc128 a0{0, 0}, a1{0, 0};
-        sflush(a0, s0[m]);
-        sflush(a1, s1[m]);
+        const Acc128 a0 = sfinal(Acc128{0, 0}, s0[m]), a1 = sfinal(Acc128{0, 0}, s1[m]);
+        o0[t + 256 * m] = reduce128(a0.lo, a0.hi, P);
+        o1[t + 256 * m] = reduce128(a1.lo, a1.hi, P);
+    }
+}
+
+// Giant-step inner product summed over the steps of a batch (n = 2048, limbs
+// e < l).  Block (part p, ciphertext b, limb e) covers the steps
+// [p * spp, min(count, (p + 1) * spp)) and writes
+//   acc[p B + b][c][e][k] = sum_s ( sum_j v_{s,j}[e][src_s(k)] key_s[j][c][e][k]
+//                                   + [c = 0] [P]_{q_e} c0_s[e][src_s(k)] ),
+// src_s = galois_src(., g_s).  A rotation's result is
+//   (acc_s - NTT(ModDown conversion of acc_s's P-part)) P^-1 + sigma_{g_s}(c0_s),
+// which is linear in acc_s's Q-part and in sigma(c0_s) (carried as P sigma(c0_s)
+// inside the accumulator); only the conversion, which lifts each step's P-part
+// exactly, must stay per step.  So the Q-part of the giant-step sum is formed
+// here without storing the individual rotations.
+__global__ __launch_bounds__(256) void k_inner_sum2048(const uint64_t *__restrict__ d, size_t d_stride,
+                                                        const uint64_t *__restrict__ c0, size_t c0_stride,
+                                                        const uint64_t *__restrict__ ext, const Steps st,
+                                                        uint32_t spp, uint64_t *__restrict__ acc,
+                                                        const PrimeConsts *__restrict__ pc,
+                                                        const uint64_t *__restrict__ pmod, uint32_t l, uint32_t K,
+                                                        uint32_t L, uint32_t beta, uint32_t alpha) {
+    constexpr uint32_t n = 2048;
+    __shared__ uint64_t buf[2][n];
+    const uint32_t el = l + K;
+    const uint32_t bl = blockIdx.x % st.B;
+    const uint32_t e = (blockIdx.x / st.B) % l;
+    const uint32_t part = blockIdx.x / (st.B * l);
+    const uint32_t s_end = min(st.count, (part + 1) * spp);
+    const uint32_t t = threadIdx.x;
+    const PrimeConsts P = pc[e];
+    const uint64_t pm = split30(pmod[e]);
+    Split3 s0[8], s1[8];
+#pragma unroll
+    for (int m = 0; m < 8; m++) s0[m] = s1[m] = {0, 0, 0, 0};
+    uint32_t cnt = 0, rounds = 0, bi = 0;
+    // called before each product: at most 15 products between snorm, at most
+    // 4 snorm rounds between full reductions
+    auto guard = [&]() {
+        if (cnt == SPLIT_CHUNK) {
+#pragma unroll
+            for (int m = 0; m < 8; m++) {
+                snorm(s0[m]);
+                snorm(s1[m]);
+            }
+            cnt = 0;
+            if (++rounds == 4) {
+#pragma unroll
+                for (int m = 0; m < 8; m++) {
+                    sreduce(s0[m], P);
+                    sreduce(s1[m], P);
+                }
+                rounds = 0;
+            }
+        }
+        cnt++;
+    };
+    for (uint32_t step = part * spp; step < s_end; step++) {
+        const size_t cb = (size_t)step * st.B + bl;
+        const uint64_t *key = st.key[step];
+        const uint32_t g = st.g[step];
+        for (uint32_t j = 0; j < beta; j++) {
+            const bool own = e >= j * alpha && e < min(l, (j + 1) * alpha);
+            const uint64_t *src = own ? d + cb * d_stride + (size_t)e * n : ext + ((cb * beta + j) * el + e) * n;
+            uint64_t *lb = buf[bi];
+            bi ^= 1;
+#pragma unroll
+            for (int m = 0; m < 8; m++) lb[t + 256 * m] = src[t + 256 * m];
+            __syncthreads();
+            guard();
+            const uint64_t *kb = key + ((size_t)j * 2 * (L + K) + e) * n;
+            const uint64_t *ka = kb + (size_t)(L + K) * n;
+#pragma unroll
+            for (int m = 0; m < 8; m++) {
+                const uint32_t k = t + 256 * m;
+                const uint64_t v = lb[galois_src(k, g, n)];
+                const uint32_t vl = (uint32_t)(v & M30), vh = (uint32_t)(v >> 30);
+                smac(s0[m], vl, vh, split30(kb[k]));
+                smac(s1[m], vl, vh, split30(ka[k]));
+            }
+        }
+        {  // P sigma_g(c0) joins the c = 0 sum
+            const uint64_t *src = c0 + cb * c0_stride + (size_t)e * n;
+            uint64_t *lb = buf[bi];
+            bi ^= 1;
+#pragma unroll
+            for (int m = 0; m < 8; m++) lb[t + 256 * m] = src[t + 256 * m];
+            __syncthreads();
+            guard();
+#pragma unroll
+            for (int m = 0; m < 8; m++) {
+                const uint64_t v = lb[galois_src(t + 256 * m, g, n)];
+                smac(s0[m], (uint32_t)(v & M30), (uint32_t)(v >> 30), pm);
+            }
+        }
+    }
+    const size_t ob = (size_t)part * st.B + bl;
+    uint64_t *o0 = acc + ((ob * 2 + 0) * el + e) * n, *o1 = acc + ((ob * 2 + 1) * el + e) * n;
+#pragma unroll
+    for (int m = 0; m < 8; m++) {
+        const Acc128 a0 = sfinal(Acc128{0, 0}, s0[m]), a1 = sfinal(Acc128{0, 0}, s1[m]);
         o0[t + 256 * m] = reduce128(a0.lo, a0.hi, P);
         o1[t + 256 * m] = reduce128(a1.lo, a1.hi, P);
     }
@@ -488,10 +610,16 @@ __global__ void k_inner(const uint64_t *__restrict__ d, size_t d_stride, const u
             const uint32_t vl = (uint32_t)(v & M30), vh = (uint32_t)(v >> 30);
             smac(s0, vl, vh, split30(kr[0]));
             smac(s1, vl, vh, split30(kr[(size_t)(L + K) * n]));
+            if ((j + 1) % SPLIT_CHUNK == 0) {  // more than 15 digits: keep the sums in bounds
+                snorm(s0);
+                snorm(s1);
+                if ((j + 1) % (4 * SPLIT_CHUNK) == 0) {
+                    sreduce(s0, pc[gi]);
+                    sreduce(s1, pc[gi]);
+                }
+            }
         }
-        Acc128 a0{0, 0}, a1{0, 0};
-        sflush(a0, s0);
-        sflush(a1, s1);
+        const Acc128 a0 = sfinal(Acc128{0, 0}, s0), a1 = sfinal(Acc128{0, 0}, s1);
         acc[((b * 2 + 0) * el + e) * n + k] = reduce128(a0.lo, a0.hi, pc[gi]);
         acc[((b * 2 + 1) * el + e) * n + k] = reduce128(a1.lo, a1.hi, pc[gi]);
     }
@@ -590,16 +718,18 @@ __global__ __launch_bounds__(256) void k_final2048(const uint64_t *__restrict__ 
     }
 }
 
-// n = 2048 giant-step tail: out[b][c][i] += sum over the S steps of the batch
-// of ((acc_s - NTT(conv_s)) P^-1 + (c == 0 ? sigma_{g_s}(c0 of input s) : 0)),
-// i.e. the rotated giant-step terms are summed without being stored.
-__global__ __launch_bounds__(256) void k_final_sum2048(const uint64_t *__restrict__ acc,
-                                                        const uint64_t *__restrict__ conv,
-                                                        const uint64_t *__restrict__ pinv,
-                                                        const PrimeConsts *__restrict__ pc,
-                                                        const uint64_t *__restrict__ twf,
-                                                        const uint64_t *__restrict__ xa, const Steps st,
-                                                        uint64_t *__restrict__ out, uint32_t l, uint32_t K) {
+// n = 2048 giant-step tail: one workgroup per (ciphertext b, polynomial c, limb i):
+//   out[b][c][i] += (sum_p acc[p B + b][c][i] - NTT(conv[b][c][i])) P^-1
+// with the parts' accumulators from k_inner_sum2048 and conv the ModDown
+// conversions of the batch's steps summed in the coefficient domain (the NTT
+// is linear, so one transform serves the whole batch).
+__global__ __launch_bounds__(256) void k_final_giant2048(const uint64_t *__restrict__ acc,
+                                                          const uint64_t *__restrict__ conv,
+                                                          const uint64_t *__restrict__ pinv,
+                                                          const PrimeConsts *__restrict__ pc,
+                                                          const uint64_t *__restrict__ twf, uint32_t nparts,
+                                                          uint32_t B, uint64_t *__restrict__ out, uint32_t l,
+                                                          uint32_t K) {
     constexpr uint32_t n = 2048;
     __shared__ uint64_t lds[n2048::LDS_WORDS];
     const uint32_t i = blockIdx.x % l;
@@ -608,41 +738,25 @@ __global__ __launch_bounds__(256) void k_final_sum2048(const uint64_t *__restric
     const uint32_t t = threadIdx.x;
     const PrimeConsts P = pc[i];
     const uint64_t q = P.q;
-    const size_t per = (size_t)l * n;
+    uint64_t v[8];
+    const uint64_t *cv = conv + (size_t)blockIdx.x * n;
+#pragma unroll
+    for (int m = 0; m < 8; m++) v[m] = cv[t + 256 * m];
+    n2048::fwd(v, lds, twf + (size_t)i * n * 2, q);
+    const size_t pstride = (size_t)B * 2 * (l + K) * n;
+    const uint64_t *ar = acc + ((b * 2 + c) * (l + K) + i) * n;
+    uint64_t *o = out + (size_t)blockIdx.x * n;
     const uint64_t w = pinv[2 * i], wp = pinv[2 * i + 1];
-    uint64_t sum[8];
-    uint64_t *o = out + ((b * 2 + c) * l + i) * n;
 #pragma unroll
-    for (int m = 0; m < 8; m++) sum[m] = o[t + 256 * m];
-    for (uint32_t step = 0; step < st.count; step++) {
-        const size_t cb = (size_t)step * st.B + b;
-        const uint32_t g = st.g[step];
-        uint64_t v[8];
-        const uint64_t *cv = conv + ((cb * 2 + c) * l + i) * n;
-#pragma unroll
-        for (int m = 0; m < 8; m++) v[m] = cv[t + 256 * m];
-        n2048::fwd(v, lds, twf + (size_t)i * n * 2, q);
-        if (c == 0) {
-            const uint64_t *c0 = xa + (cb * 2) * per + (size_t)i * n;
-#pragma unroll
-            for (int m = 0; m < 8; m++) lds[t + 256 * m] = c0[t + 256 * m];
-            __syncthreads();
-        }
-        const uint64_t *ar = acc + ((cb * 2 + c) * (l + K) + i) * n;
-#pragma unroll
-        for (int m = 0; m < 8; m++) {
-            const uint32_t k = t + 256 * m;
-            uint64_t x = v[m];
-            x = x >= 2 * q ? x - 2 * q : x;
-            x = csub(x, q);
-            uint64_t r = shoup(subm(ar[k], x, q), w, wp, q);
-            if (c == 0) r = addm(r, lds[galois_src(k, g, n)], q);
-            sum[m] = addm(sum[m], r, q);
-        }
-        __syncthreads();  // lds is reused by the next step's NTT
+    for (int m = 0; m < 8; m++) {
+        const uint32_t k = t + 256 * m;
+        uint64_t a = ar[k];
+        for (uint32_t p = 1; p < nparts; p++) a = addm(a, ar[p * pstride + k], q);
+        uint64_t x = v[m];
+        x = x >= 2 * q ? x - 2 * q : x;
+        x = csub(x, q);
+        o[k] = addm(o[k], shoup(subm(a, x, q), w, wp, q), q);
     }
-#pragma unroll
-    for (int m = 0; m < 8; m++) o[t + 256 * m] = sum[m];
 }
 
 // n = 2048 fused rescale tail: per (ciphertext, polynomial, limb i < l-1):
@@ -842,8 +956,8 @@ static int ks_modup(ckks_ctx *c, LevelTables *lt, int B, int l, const uint64_t *
         ConvTargets ct{0, (uint32_t)l, L, K, (size_t)beta * el * n, (size_t)el * n};
         const uint32_t maxt = l + K;  // upper bound on targets per digit
         ProfScope ps_(c, "ks_modup_convert", s);
-        hipLaunchKernelGGL(k_convert, dim3((n + 255) / 256, (maxt + CT - 1) / CT, B * beta), dim3(256),
-                           (size_t)c->alpha * CT * 8, s, lt->d_digits, lay_up, w.y, w.u, ct, w.ext, n, c->d_pc);
+        hipLaunchKernelGGL(k_convert, dim3((n + 255) / 256, (maxt + CT - 1) / CT, B * beta), dim3(256), 0, s,
+                           lt->d_digits, lay_up, w.y, w.u, ct, w.ext, n, c->d_pc);
     }
     LAUNCH_CHECK();
     {
@@ -875,7 +989,7 @@ static int ks_inner(ckks_ctx *c, LevelTables *lt, int l, const uint64_t *d, size
     ProfScope ps_(c, st.shared ? "ks_inner_product_hoisted" : "ks_inner_product", s);
     if (n == 2048) {
         hipLaunchKernelGGL(k_inner2048, dim3(nout * el), dim3(256), 0, s, d, d_stride, w.ext, st, w.acc, c->d_pc,
-                           (uint32_t)l, L, K, beta, c->alpha);
+                           (uint32_t)l, L, K, beta, c->alpha, 0u, el);
     } else {  // generic n: one launch per step
         for (uint32_t j = 0; j < st.count; j++) {
             const size_t total = (size_t)st.B * el * n;
@@ -889,9 +1003,37 @@ static int ks_inner(ckks_ctx *c, LevelTables *lt, int l, const uint64_t *d, size
     return CKKS_OK;
 }
 
+// Giant-step inner products of a batch (n = 2048), x = the steps' input
+// ciphertexts (c0 at x + cb x_stride, c1 one polynomial further): the P-limbs
+// of every step go to w.acc as usual, the Q-limbs are summed over the steps
+// into *nparts partial sums (k_inner_sum2048).
+static int ks_inner_giant(ckks_ctx *c, LevelTables *lt, int l, const uint64_t *x, size_t x_stride, const Steps &st,
+                          const KsWs &w, uint32_t *nparts, hipStream_t s) {
+    const uint32_t K = c->K, L = c->L, beta = lt->beta;
+    const size_t per = (size_t)l * c->n;
+    {
+        ProfScope ps_(c, "ks_inner_product", s);
+        hipLaunchKernelGGL(k_inner2048, dim3(st.count * st.B * K), dim3(256), 0, s, x + per, x_stride, w.ext, st,
+                           w.acc, c->d_pc, (uint32_t)l, L, K, beta, c->alpha, (uint32_t)l, K);
+    }
+    LAUNCH_CHECK();
+    // up to 4 partial sums: enough workgroups to fill the chip at ~1 wave per SIMD each
+    const uint32_t parts = std::min(st.count, 4u), spp = (st.count + parts - 1) / parts;
+    *nparts = (st.count + spp - 1) / spp;
+    {
+        ProfScope ps_(c, "ks_inner_product_sum", s);
+        hipLaunchKernelGGL(k_inner_sum2048, dim3(*nparts * st.B * l), dim3(256), 0, s, x + per, x_stride, x,
+                           x_stride, w.ext, st, spp, w.acc, c->d_pc, c->d_pmod, (uint32_t)l, K, L, beta, c->alpha);
+    }
+    LAUNCH_CHECK();
+    return CKKS_OK;
+}
+
 // ModDown of nout accumulator pairs up to the converted P-part in w.conv
 // (NTT domain for n != 2048; at n = 2048 the final kernels transform it).
-static int ks_moddown_conv(ckks_ctx *c, size_t nout, int l, const KsWs &w, hipStream_t s) {
+// With nsum > 1 the conversions of accumulators o + j (nout / nsum), j < nsum,
+// are summed into output o (n = 2048 giant steps).
+static int ks_moddown_conv(ckks_ctx *c, size_t nout, int l, const KsWs &w, hipStream_t s, uint32_t nsum = 1) {
     const uint32_t n = c->n, K = c->K, L = c->L, el = l + K;
     int e;
     {
@@ -907,9 +1049,11 @@ static int ks_moddown_conv(ckks_ctx *c, size_t nout, int l, const KsWs &w, hipSt
     LAUNCH_CHECK();
     {
         ConvTargets ct{1, (uint32_t)l, L, K, (size_t)l * n, 0};
+        ct.nsum = nsum;
+        ct.sum_stride = (uint32_t)(nout / nsum * 2);
         ProfScope ps_(c, "ks_moddown_convert", s);
-        hipLaunchKernelGGL(k_convert, dim3((n + 255) / 256, (l + CT - 1) / CT, (unsigned)(nout * 2)), dim3(256),
-                           (size_t)K * CT * 8, s, c->d_pbasis, lay_dn, w.acc, w.uP, ct, w.conv, n, c->d_pc);
+        hipLaunchKernelGGL(k_convert, dim3((n + 255) / 256, (l + CT - 1) / CT, (unsigned)(nout / nsum * 2)),
+                           dim3(256), 0, s, c->d_pbasis, lay_dn, w.acc, w.uP, ct, w.conv, n, c->d_pc);
     }
     LAUNCH_CHECK();
     if (n != 2048) {
@@ -931,6 +1075,8 @@ static int bsgs_chunk(const ckks_ctx *c, int B, int l, int bs, int gs) {
     if (c->n != 2048) return 1;
     const size_t per = ks_words(c, B, l, nullptr, nullptr) * 8;
     int sc = (int)std::max<size_t>(1, BSGS_KS_BUDGET / std::max<size_t>(per, 1));
+    // a giant batch sums sc conversions of K inputs each: sc K <= 1000 keeps it in 128 bits
+    sc = std::min<int>(sc, (int)std::max<uint32_t>(1, 1000 / std::max<uint32_t>(c->K, 1)));
     return std::max(1, std::min({sc, MAX_STEPS, std::max(bs, gs) - 1}));
 }
 static size_t bsgs_words(const ckks_ctx *c, int B, int l, int bs, int gs) {
@@ -1115,12 +1261,13 @@ int op_bsgs(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, const 
         const uint64_t *src = inner + (size_t)g0 * ct;  // ciphertexts (g0 + j, b), consecutive
         const int nb = (int)st.count * B;
         if (c->n == 2048) {
+            uint32_t nparts = 0;
             if ((e = ks_modup(c, lt, nb, l, src + per, 2 * per, w, s))) return e;
-            if ((e = ks_inner(c, lt, l, src + per, 2 * per, st, w, s))) return e;
-            if ((e = ks_moddown_conv(c, nb, l, w, s))) return e;
-            ProfScope ps_(c, "giant_final_sum", s);
-            hipLaunchKernelGGL(k_final_sum2048, dim3(B * 2 * l), dim3(256), 0, s, w.acc, w.conv, c->d_pinv, c->d_pc,
-                               c->d_tw_fwd, src, st, inner, (uint32_t)l, c->K);
+            if ((e = ks_inner_giant(c, lt, l, src, 2 * per, st, w, &nparts, s))) return e;
+            if ((e = ks_moddown_conv(c, nb, l, w, s, st.count))) return e;
+            ProfScope ps_(c, "giant_final", s);
+            hipLaunchKernelGGL(k_final_giant2048, dim3(B * 2 * l), dim3(256), 0, s, w.acc, w.conv, c->d_pinv,
+                               c->d_pc, c->d_tw_fwd, nparts, (uint32_t)B, inner, (uint32_t)l, c->K);
             LAUNCH_CHECK();
         } else {
             for (uint32_t j = 0; j < st.count; j++)
