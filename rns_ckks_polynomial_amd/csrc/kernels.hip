@@ -136,11 +136,7 @@ __global__ __launch_bounds__(256) void k_ntt2048(Map map, const PrimeConsts *__r
     if (!INV) {
         n2048::fwd(v, lds, twf + (size_t)prime * 2048 * 2, q);
 #pragma unroll
-        for (int k = 0; k < 8; k++) {
-            uint64_t x = v[k];
-            x = x >= 2 * q ? x - 2 * q : x;
-            dst[t + 256 * k] = csub(x, q);
-        }
+        for (int k = 0; k < 8; k++) dst[t + 256 * k] = n2048::reduce8(v[k], q);
     } else {
         n2048::inv(v, lds, twi + (size_t)prime * 2048 * 2, q);
         const uint64_t w = sc ? sc[0] : pc[prime].ninv, wp = sc ? sc[1] : pc[prime].ninvp;
@@ -700,9 +696,7 @@ __global__ __launch_bounds__(256) void k_final2048(const uint64_t *__restrict__ 
 #pragma unroll
     for (int m = 0; m < 8; m++) {
         const uint32_t k = t + 256 * m;
-        uint64_t x = v[m];
-        x = x >= 2 * q ? x - 2 * q : x;
-        x = csub(x, q);
+        const uint64_t x = n2048::reduce8(v[m], q);
         uint64_t r = shoup(subm(ar[k], x, q), w, wp, q);
         if (MODE == 1) {
             const size_t o0 = (b * 2) * per + (size_t)i * n + k, o1 = o0 + per;
@@ -752,9 +746,7 @@ __global__ __launch_bounds__(256) void k_final_giant2048(const uint64_t *__restr
         const uint32_t k = t + 256 * m;
         uint64_t a = ar[k];
         for (uint32_t p = 1; p < nparts; p++) a = addm(a, ar[p * pstride + k], q);
-        uint64_t x = v[m];
-        x = x >= 2 * q ? x - 2 * q : x;
-        x = csub(x, q);
+        const uint64_t x = n2048::reduce8(v[m], q);
         o[k] = addm(o[k], shoup(subm(a, x, q), w, wp, q), q);
     }
 }
@@ -788,9 +780,7 @@ __global__ __launch_bounds__(256) void k_rescale2048(const uint64_t *__restrict_
 #pragma unroll
     for (int m = 0; m < 8; m++) {
         const uint32_t k = t + 256 * m;
-        uint64_t x = v[m];
-        x = x >= 2 * q ? x - 2 * q : x;
-        x = csub(x, q);
+        const uint64_t x = n2048::reduce8(v[m], q);
         o[k] = shoup(subm(ci[k], x, q), w, wp, q);
     }
 }

@@ -15,7 +15,9 @@
 // input through the same permutation), so no separate reorder pass exists.
 // Twiddles are Shoup pairs (w, floor(w 2^64/q)) of psi^bitrev(k) (forward) and
 // psi^-bitrev(k) (inverse), interleaved [k][2].  Butterflies are Harvey's lazy
-// forms: values stay in [0, 4q) (forward) or [0, 2q) (inverse).
+// forms with a truncated Shoup quotient (see shoup_lazy4): the twiddle product
+// lands in [0, 4q), so values stay in [0, 8q) (forward) or [0, 4q) (inverse),
+// all below 2^63 for q < 2^60.
 #pragma once
 #include "ckks_common.h"
 
@@ -39,20 +41,50 @@ __device__ __forceinline__ int own(int t, int k) {
 
 __device__ __forceinline__ int brev(int i) { return (int)(__builtin_bitreverse32((uint32_t)i) >> (32 - LOGN)); }
 
+// Shoup product with the quotient floor(y wp / 2^64) truncated to the three
+// high 32x32 partial products: the dropped carries make it at most 2 too
+// small, so y w - Q q lands in [0, 4q) (instead of [0, 2q)) for any 64-bit y.
+// The remainder is formed as y w + Q (2^64 - q) mod 2^64 (nq = 2^64 - q), so
+// the subtraction rides on the multiply-adds.
+__device__ __forceinline__ uint64_t shoup_lazy4(uint64_t y, uint64_t w, uint64_t wp, uint64_t nq) {
+    const uint32_t yl = (uint32_t)y, yh = (uint32_t)(y >> 32);
+    const uint32_t pl = (uint32_t)wp, ph = (uint32_t)(wp >> 32);
+    const uint64_t qt = (uint64_t)yh * ph + ((uint64_t)__umulhi(yh, pl) + __umulhi(yl, ph));
+    const uint32_t ql = (uint32_t)qt, qh = (uint32_t)(qt >> 32);
+    const uint32_t wl = (uint32_t)w, wh = (uint32_t)(w >> 32);
+    const uint32_t nl = (uint32_t)nq, nh = (uint32_t)(nq >> 32);
+    const uint64_t r = (uint64_t)ql * nl + (uint64_t)yl * wl;  // mod 2^64
+    const uint32_t hi = (uint32_t)(r >> 32) + yl * wh + yh * wl + ql * nh + qh * nl;
+    return ((uint64_t)hi << 32) | (uint32_t)r;
+}
+
+// x - c if x >= c else x, for x, c < 2^62 (nc = 2^64 - c): add, then select on the sign.
+__device__ __forceinline__ uint64_t csub_sign(uint64_t x, uint64_t nc) {
+    const uint64_t m = x + nc;
+    return (int64_t)m < 0 ? x : m;
+}
+
 __device__ __forceinline__ void bf_ct(uint64_t &x, uint64_t &y, uint64_t w, uint64_t wp, uint64_t q) {
-    uint64_t q2 = 2 * q;
-    uint64_t a = x >= q2 ? x - q2 : x;       // [0, 2q)
-    uint64_t t = shoup_lazy(y, w, wp, q);    // [0, 2q)
-    x = a + t;                               // [0, 4q)
-    y = a - t + q2;                          // [0, 4q)
+    const uint64_t q4 = 4 * q;
+    const uint64_t a = csub_sign(x, 0 - q4);      // [0, 4q)
+    const uint64_t t = shoup_lazy4(y, w, wp, 0 - q); // [0, 4q)
+    x = a + t;                                    // [0, 8q)
+    y = a + q4 - t;                               // (0, 8q)
 }
 
 __device__ __forceinline__ void bf_gs(uint64_t &x, uint64_t &y, uint64_t w, uint64_t wp, uint64_t q) {
-    uint64_t q2 = 2 * q;
-    uint64_t s = x + y;
-    uint64_t d = x - y + q2;                 // (0, 4q)
-    x = s >= q2 ? s - q2 : s;                // [0, 2q)
-    y = shoup_lazy(d, w, wp, q);             // [0, 2q)
+    const uint64_t q4 = 4 * q;
+    const uint64_t s = x + y;                     // [0, 8q)
+    const uint64_t d = x + q4 - y;                // (0, 8q)
+    x = csub_sign(s, 0 - q4);                     // [0, 4q)
+    y = shoup_lazy4(d, w, wp, 0 - q);             // [0, 4q)
+}
+
+// [0, 8q) -> [0, q): the forward transform's outputs fully reduced.
+__device__ __forceinline__ uint64_t reduce8(uint64_t x, uint64_t q) {
+    x = x >= 4 * q ? x - 4 * q : x;
+    x = x >= 2 * q ? x - 2 * q : x;
+    return x >= q ? x - q : x;
 }
 
 // One radix-2 stage (bit BIT of the index) on the 8 registers of a pass owning bits [C, C+3).
@@ -82,8 +114,8 @@ __device__ __forceinline__ void from_lds(const uint64_t *lds, uint64_t (&v)[E], 
     for (int k = 0; k < E; k++) v[k] = lds[slot(own<C>(t, k))];
 }
 
-// Forward NTT.  On entry v[k] = a[t + 256 k] (natural order, values < 4q);
-// on exit v[k] = A[t + 256 k] in [0, 4q).  Uses lds[LDS_WORDS]; ends with a barrier.
+// Forward NTT.  On entry v[k] = a[t + 256 k] (natural order, values < 8q);
+// on exit v[k] = A[t + 256 k] in [0, 8q) (reduce8 finishes).  Uses lds[LDS_WORDS]; ends with a barrier.
 __device__ __forceinline__ void fwd(uint64_t (&v)[E], uint64_t *lds, const uint64_t *__restrict__ tw, uint64_t q) {
     const int t = threadIdx.x;
     stage<8, 10, false>(v, t, tw, q);
@@ -119,7 +151,7 @@ __device__ __forceinline__ void fwd(uint64_t (&v)[E], uint64_t *lds, const uint6
 }
 
 // Inverse NTT without the final n^-1 scaling.  On entry v[k] = A[t + 256 k]
-// (values < 2q); on exit v[k] = n a[t + 256 k] in [0, 2q).
+// (values < 4q); on exit v[k] = n a[t + 256 k] in [0, 4q).
 __device__ __forceinline__ void inv(uint64_t (&v)[E], uint64_t *lds, const uint64_t *__restrict__ tw, uint64_t q) {
     const int t = threadIdx.x;
 #pragma unroll
