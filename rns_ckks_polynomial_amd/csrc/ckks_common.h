@@ -46,7 +46,8 @@ struct PrimeConsts {
     uint64_t m64;    // floor(2^64 / q)  (Shoup companion of 1)
     uint64_t ninv;   // n^-1 mod q
     uint64_t ninvp;  // Shoup companion of ninv
-    uint64_t pad;
+    uint64_t r60;    // 2^60 mod q
+    uint64_t r60p;   // Shoup companion of r60
 };
 
 // Reduce a 128-bit value (hi:lo) modulo q: hi 2^64 + lo = shoup(hi, 2^64 mod q) + shoup(lo, 1).

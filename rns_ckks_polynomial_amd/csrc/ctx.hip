@@ -304,6 +304,8 @@ extern "C" int ckks_ctx_create(ckks_ctx **out, const ckks_params *params, int de
             k.m64 = (uint64_t)(((h128)1 << 64) / q);
             k.ninv = h_invmod(n % q, q);
             k.ninvp = h_shoup(k.ninv, q);
+            k.r60 = (1ull << 60) % q;
+            k.r60p = h_shoup(k.r60, q);
             // powers psi^e for e = 0..n-1, then place at bit-reversed slots
             uint64_t pw = 1, ipw = 1;
             std::vector<uint64_t> fp(n), ip(n);

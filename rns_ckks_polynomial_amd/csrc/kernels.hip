@@ -363,15 +363,24 @@ __global__ __launch_bounds__(256) void k_convert(const BasisDev *__restrict__ ba
         uint64_t yv[YC], yn[YC];
 #pragma unroll
         for (int r = 0; r < YC; r++) yv[r] = yb[(size_t)min((uint32_t)r, m - 1) * n];
+        uint64_t hc[CT];  // table row in use; the next row is fetched one row ahead
+#pragma unroll
+        for (int a = 0; a < CT; a++) hc[a] = ht[a];
         for (uint32_t i0 = 0; i0 < mpad; i0 += YC, chunk++) {
 #pragma unroll
             for (int r = 0; r < YC; r++) yn[r] = yb[(size_t)min(i0 + YC + r, m - 1) * n];
 #pragma unroll
             for (int r = 0; r < YC; r++) {  // rows past m: y repeats row m-1, the table row is zero
-                const uint32_t yl = (uint32_t)(yv[r] & M30), yh = (uint32_t)(yv[r] >> 30);
-                const __attribute__((address_space(4))) uint64_t *hr = ht + (size_t)(i0 + r) * hstride;
+                const __attribute__((address_space(4))) uint64_t *hr =
+                    ht + (size_t)min(i0 + r + 1, mpad - 1) * hstride;
+                uint64_t hn[CT];
 #pragma unroll
-                for (int a = 0; a < CT; a++) smac(sp[a], yl, yh, hr[a]);
+                for (int a = 0; a < CT; a++) hn[a] = hr[a];
+                const uint32_t yl = (uint32_t)(yv[r] & M30), yh = (uint32_t)(yv[r] >> 30);
+#pragma unroll
+                for (int a = 0; a < CT; a++) smac(sp[a], yl, yh, hc[a]);
+#pragma unroll
+                for (int a = 0; a < CT; a++) hc[a] = hn[a];
             }
             if (chunk % (SPLIT_CHUNK / YC) == SPLIT_CHUNK / YC - 1) {
 #pragma unroll
@@ -386,16 +395,29 @@ __global__ __launch_bounds__(256) void k_convert(const BasisDev *__restrict__ ba
         }
         uu += u[ss * n + k];
     }
-#pragma unroll
-    for (int a = 0; a < CT; a++) acc[a] = sfinal(acc[a], sp[a]);
+    // the rows ran in chunks of YC; a fold into acc happened iff 60 rows or more
+    const bool folded = ct.nsum * (mpad / YC) >= 4 * SPLIT_CHUNK / YC;
+    const uint32_t ul = (uint32_t)(uu & M30), uh = (uint32_t)(uu >> 30);
     uint64_t *ob = out + (s / lay.inner) * ct.out_so + (s % lay.inner) * ct.out_si + k;
 #pragma unroll
     for (int a = 0; a < CT; a++) {
         if (a >= (int)nt) break;
         const uint32_t t = __builtin_amdgcn_readfirstlane(conv_target(ct, tn0 + a, lo, m));
-        mac(acc[a], uu, B.negB[t]);
+        const PrimeConsts &P = pc[t];
+        // u [-B]_t joins the sum as one more product (at most 16 since the last snorm)
+        smac(sp[a], ul, uh, split30(B.negB[t]));
+        uint64_t r;
+        if (!folded) {  // value = a0 + 2^30 a1 + 2^60 a2 with a0, a1 < 2^30 after snorm
+            snorm(sp[a]);
+            r = shoup_lazy(sp[a].a2, P.r60, P.r60p, P.q) + (sp[a].a0 | (sp[a].a1 << 30));  // < 2q + 2^60 < 4q
+            r = r >= 2 * P.q ? r - 2 * P.q : r;
+            r = csub(r, P.q);
+        } else {
+            const Acc128 v = sfinal(acc[a], sp[a]);
+            r = reduce128(v.lo, v.hi, P);
+        }
         const uint32_t slot = (ct.mode == 0 && t >= ct.L) ? ct.l + (t - ct.L) : t;
-        ob[(size_t)slot * n] = reduce128(acc[a].lo, acc[a].hi, pc[t]);
+        ob[(size_t)slot * n] = r;
     }
 }
 
