@@ -137,6 +137,24 @@ __device__ __forceinline__ Acc128 sfinal(const Acc128 &hi, Split3 s) {
     const u128 v = (h << 60) + (s.a0 | (s.a1 << 30));
     return Acc128{(uint64_t)v, (uint64_t)(v >> 64)};
 }
+// Three-sum form: a1 takes two products per smac, so at most 15 smac between
+// snorm; a2 stays below 2^64 for up to 60 smac.
+__device__ __forceinline__ void snorm(Split3c &s) {
+    s.a1 += s.a0 >> 30;
+    s.a0 &= M30;
+    s.a2 += s.a1 >> 30;
+    s.a1 &= M30;
+}
+// a0 + 2^30 (a1 + a1b) + 2^60 a2 mod q for a split sum whose a2 never
+// overflowed (no sfold_hi): after snorm the low part is below 2^60 < 2q.
+template <class S>
+__device__ __forceinline__ uint64_t sreduce60(S s, const PrimeConsts &P) {
+    snorm(s);
+    uint64_t r = shoup_lazy(s.a2, P.r60, P.r60p, P.q) + (s.a0 | (s.a1 << 30));  // < 4q
+    r = r >= 2 * P.q ? r - 2 * P.q : r;
+    return csub(r, P.q);
+}
+
 // Full reduction of a split sum modulo P.q, left in normalised split form
 // (a0, a1 < 2^30, a2 = 0): restarts the growth bounds of snorm.
 __device__ __forceinline__ void sreduce(Split3 &s, const PrimeConsts &P) {

@@ -407,11 +407,8 @@ __global__ __launch_bounds__(256) void k_convert(const BasisDev *__restrict__ ba
         // u [-B]_t joins the sum as one more product (at most 16 since the last snorm)
         smac(sp[a], ul, uh, split30(B.negB[t]));
         uint64_t r;
-        if (!folded) {  // value = a0 + 2^30 a1 + 2^60 a2 with a0, a1 < 2^30 after snorm
-            snorm(sp[a]);
-            r = shoup_lazy(sp[a].a2, P.r60, P.r60p, P.q) + (sp[a].a0 | (sp[a].a1 << 30));  // < 2q + 2^60 < 4q
-            r = r >= 2 * P.q ? r - 2 * P.q : r;
-            r = csub(r, P.q);
+        if (!folded) {
+            r = sreduce60(sp[a], P);
         } else {
             const Acc128 v = sfinal(acc[a], sp[a]);
             r = reduce128(v.lo, v.hi, P);
@@ -499,9 +496,8 @@ __global__ __launch_bounds__(256) void k_inner2048(const uint64_t *__restrict__ 
     uint64_t *o0 = acc + ((cb * 2 + 0) * el + e) * n, *o1 = acc + ((cb * 2 + 1) * el + e) * n;
 #pragma unroll
     for (int m = 0; m < 8; m++) {
-        const Acc128 a0 = sfinal(Acc128{0, 0}, s0[m]), a1 = sfinal(Acc128{0, 0}, s1[m]);
-        o0[t + 256 * m] = reduce128(a0.lo, a0.hi, P);
-        o1[t + 256 * m] = reduce128(a1.lo, a1.hi, P);
+        o0[t + 256 * m] = sreduce60(s0[m], P);  // a2 < 2^64: sreduce at least every 60 products
+        o1[t + 256 * m] = sreduce60(s1[m], P);
     }
 }
 
@@ -601,9 +597,8 @@ __global__ __launch_bounds__(256) void k_inner_sum2048(const uint64_t *__restric
     uint64_t *o0 = acc + ((ob * 2 + 0) * el + e) * n, *o1 = acc + ((ob * 2 + 1) * el + e) * n;
 #pragma unroll
     for (int m = 0; m < 8; m++) {
-        const Acc128 a0 = sfinal(Acc128{0, 0}, s0[m]), a1 = sfinal(Acc128{0, 0}, s1[m]);
-        o0[t + 256 * m] = reduce128(a0.lo, a0.hi, P);
-        o1[t + 256 * m] = reduce128(a1.lo, a1.hi, P);
+        o0[t + 256 * m] = sreduce60(s0[m], P);  // a2 < 2^64: sreduce at least every 60 products
+        o1[t + 256 * m] = sreduce60(s1[m], P);
     }
 }
 
@@ -637,9 +632,9 @@ __global__ void k_inner(const uint64_t *__restrict__ d, size_t d_stride, const u
                 }
             }
         }
-        const Acc128 a0 = sfinal(Acc128{0, 0}, s0), a1 = sfinal(Acc128{0, 0}, s1);
-        acc[((b * 2 + 0) * el + e) * n + k] = reduce128(a0.lo, a0.hi, pc[gi]);
-        acc[((b * 2 + 1) * el + e) * n + k] = reduce128(a1.lo, a1.hi, pc[gi]);
+        // a2 stays below 2^64: sreduce runs at least every 60 digits
+        acc[((b * 2 + 0) * el + e) * n + k] = sreduce60(s0, pc[gi]);
+        acc[((b * 2 + 1) * el + e) * n + k] = sreduce60(s1, pc[gi]);
     }
 }
 
@@ -856,6 +851,7 @@ __global__ void k_rescale_final(const uint64_t *__restrict__ in, const uint64_t 
 // element leaves HBM once.  Baby steps beyond MAC_B are added in further passes.
 // ---------------------------------------------------------------------
 constexpr int MAC_K = 16, MAC_C = 16, MAC_B = 32;
+static_assert(MAC_B <= 4 * SPLIT_CHUNK, "one split sum per giant step without a 128-bit fold");
 
 __global__ __launch_bounds__(256) void k_bsgs_mac(const uint64_t *__restrict__ pt, const uint64_t *__restrict__ in,
                                                    const uint64_t *__restrict__ rot, uint64_t *__restrict__ inner,
@@ -894,17 +890,15 @@ __global__ __launch_bounds__(256) void k_bsgs_mac(const uint64_t *__restrict__ p
             st1 = *pt_addr(g + 1, threadIdx.x + 256);
         }
         Split3c sp{0, 0, 0};
-        Acc128 acc{0, 0};
 #pragma unroll
         for (int bb = 0; bb < MAC_B; bb++) {
             // rows bb >= nb hold a valid (clamped) diagonal and r[bb] = 0: no guard needed
             const uint64_t p = buf[bb * MAC_K + kl];
             smac(sp, (uint32_t)p, (uint32_t)(p >> 32), r[bb]);
-            if (bb % SPLIT_CHUNK == SPLIT_CHUNK - 1) sflush(acc, sp);
+            if (bb % SPLIT_CHUNK == SPLIT_CHUNK - 1) snorm(sp);
         }
-        sflush(acc, sp);
         if (active) {
-            uint64_t v = reduce128(acc.lo, acc.hi, P);
+            uint64_t v = sreduce60(sp, P);
             uint64_t *o = inner + (size_t)g * ctsize + off;
             if (b0) v = addm(v, *o, P.q);
             *o = v;
