@@ -115,20 +115,14 @@ __device__ __forceinline__ void sflush(Acc128 &acc, Split3 &s) {
 
 // Carry normalisation inside the 64-bit lanes (value-preserving):
 // afterwards a0, a1 < 2^30 and a1b = 0, so 15 more smac fit before the next
-// snorm; a2 (weight 2^60) gains below 2^62 per round and is moved into a
-// 128-bit high accumulator (units of 2^60) by sfold_hi at least every 4 rounds.
+// snorm; a2 (weight 2^60) gains below 2^62 per round, so a full reduction
+// (sreduce) is due at least every 4 rounds.
 __device__ __forceinline__ void snorm(Split3 &s) {
     s.a1 += s.a1b + (s.a0 >> 30);
     s.a0 &= M30;
     s.a1b = 0;
     s.a2 += s.a1 >> 30;
     s.a1 &= M30;
-}
-__device__ __forceinline__ void sfold_hi(Acc128 &hi, Split3 &s) {
-    u128 v = ((u128)hi.hi << 64 | hi.lo) + s.a2;
-    hi.lo = (uint64_t)v;
-    hi.hi = (uint64_t)(v >> 64);
-    s.a2 = 0;
 }
 // The 128-bit value a0 + 2^30 (a1 + a1b) + 2^60 (a2 + hi).
 __device__ __forceinline__ Acc128 sfinal(const Acc128 &hi, Split3 s) {
@@ -145,14 +139,24 @@ __device__ __forceinline__ void snorm(Split3c &s) {
     s.a2 += s.a1 >> 30;
     s.a1 &= M30;
 }
-// a0 + 2^30 (a1 + a1b) + 2^60 a2 mod q for a split sum whose a2 never
-// overflowed (no sfold_hi): after snorm the low part is below 2^60 < 2q.
+// a0 + 2^30 (a1 + a1b) + 2^60 a2 mod q for a split sum kept within the
+// snorm / sreduce bounds (a2 < 2^64): after snorm the low part is below 2^60 < 2q.
 template <class S>
 __device__ __forceinline__ uint64_t sreduce60(S s, const PrimeConsts &P) {
     snorm(s);
     uint64_t r = shoup_lazy(s.a2, P.r60, P.r60p, P.q) + (s.a0 | (s.a1 << 30));  // < 4q
     r = r >= 2 * P.q ? r - 2 * P.q : r;
     return csub(r, P.q);
+}
+
+// Right after snorm: replace the 2^60-weighted a2 by its residue
+// [2^60 a2]_q (lazy, < 2q < 2^61) spread over a0 and a1, congruent modulo
+// P.q; afterwards a0 < 2^31, a1 < 2^31, a2 = 0, so the snorm bounds restart.
+__device__ __forceinline__ void sfold60(Split3 &s, const PrimeConsts &P) {
+    const uint64_t r = shoup_lazy(s.a2, P.r60, P.r60p, P.q);
+    s.a0 += r & M30;
+    s.a1 += r >> 30;
+    s.a2 = 0;
 }
 
 // Full reduction of a split sum modulo P.q, left in normalised split form

@@ -318,9 +318,11 @@ struct ConvTargets {
     // mode 1 (ModDown): targets = [0, l) -> slot t
     uint32_t mode, l, L, K;
     size_t out_so, out_si;  // output limb base of set s: (s / inner) * out_so + (s % inner) * out_si
-    // output set s is the sum of the conversions of input sets s + j * sum_stride, j < nsum
-    // (each converted exactly with its own u; nsum * m <= 1000 keeps the sum in 128 bits)
-    uint32_t nsum = 1, sum_stride = 0;
+    // Summed conversions (nsum > 1): the input sets s + j * sum_stride, j < nsum,
+    // are split into parts of spp consecutive j; output set p * sum_stride + s
+    // (s < sum_stride) is the sum of part p's conversions, each converted exactly
+    // with its own u.
+    uint32_t nsum = 1, sum_stride = 0, spp = 1;
 };
 
 __device__ __forceinline__ uint32_t conv_target(const ConvTargets &ct, uint32_t tn, uint32_t lo, uint32_t m) {
@@ -330,7 +332,7 @@ __device__ __forceinline__ uint32_t conv_target(const ConvTargets &ct, uint32_t 
     return c < lo ? c : c + m;
 }
 
-__global__ __launch_bounds__(256) void k_convert(const BasisDev *__restrict__ bases, SetLayout lay,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k_convert(const BasisDev *__restrict__ bases, SetLayout lay,
                                                   const uint64_t *__restrict__ y, const uint32_t *__restrict__ u,
                                                   ConvTargets ct, uint64_t *__restrict__ out, uint32_t n,
                                                   const PrimeConsts *__restrict__ pc) {
@@ -349,54 +351,68 @@ __global__ __launch_bounds__(256) void k_convert(const BasisDev *__restrict__ ba
         (const __attribute__((address_space(4))) uint64_t *)(B.HT + tn0);
     const uint32_t hstride = B.hstride, mpad = B.mpad;
     Split3 sp[CT];
-    Acc128 acc[CT];  // units of 2^60 until sfinal
 #pragma unroll
-    for (int a = 0; a < CT; a++) {
-        sp[a] = {0, 0, 0, 0};
-        acc[a] = {0, 0};
-    }
-    uint64_t uu = 0;
-    uint32_t chunk = 0;  // chunks of YC rows done, over all summed sets
-    for (uint32_t js = 0; js < ct.nsum; js++) {
-        const size_t ss = s + (size_t)js * ct.sum_stride;
-        const uint64_t *yb = y + (ss / lay.inner) * lay.so + (ss % lay.inner) * lay.si + lay.off + k;
-        uint64_t yv[YC], yn[YC];
+    for (int a = 0; a < CT; a++) sp[a] = {0, 0, 0, 0};
+    // The summed sets' rows form one stream of chunks (YC rows each, mpad / YC
+    // chunks per set), so the input prefetch runs across set boundaries.
+    const uint32_t part = ct.nsum > 1 ? s / ct.sum_stride : 0;
+    const size_t sfirst = ct.nsum > 1 ? s + (size_t)part * (ct.spp - 1) * ct.sum_stride : s;
+    const uint32_t nsets = ct.nsum > 1 ? min(ct.spp, ct.nsum - part * ct.spp) : 1;
+    auto set_base = [&](uint32_t js) {
+        const size_t ss = sfirst + (size_t)js * ct.sum_stride;
+        return y + (ss / lay.inner) * lay.so + (ss % lay.inner) * lay.si + lay.off + k;
+    };
+    const uint32_t nchunks = nsets * (mpad / YC);
+    const uint64_t *pb = set_base(0);  // set of the chunk being fetched
+    uint32_t pi = 0, pj = 0;           // its first row and set index
+    uint64_t yv[YC], yn[YC];
 #pragma unroll
-        for (int r = 0; r < YC; r++) yv[r] = yb[(size_t)min((uint32_t)r, m - 1) * n];
-        uint64_t hc[CT];  // table row in use; the next row is fetched one row ahead
+    for (int r = 0; r < YC; r++) yv[r] = pb[(size_t)min((uint32_t)r, m - 1) * n];
+    uint64_t hc[CT];  // table row in use; the next row is fetched one row ahead
 #pragma unroll
-        for (int a = 0; a < CT; a++) hc[a] = ht[a];
-        for (uint32_t i0 = 0; i0 < mpad; i0 += YC, chunk++) {
+    for (int a = 0; a < CT; a++) hc[a] = ht[a];
+    uint32_t i0 = 0;  // first table row of the current chunk
+    for (uint32_t chunk = 0; chunk < nchunks; chunk++) {
+        pi += YC;  // advance the fetch position to the next chunk
+        if (pi == mpad) {
+            pi = 0;
+            pj = min(pj + 1, nsets - 1);  // past the end: harmless reload of the last set
+            pb = set_base(pj);
+        }
 #pragma unroll
-            for (int r = 0; r < YC; r++) yn[r] = yb[(size_t)min(i0 + YC + r, m - 1) * n];
+        for (int r = 0; r < YC; r++) yn[r] = pb[(size_t)min(pi + r, m - 1) * n];
 #pragma unroll
-            for (int r = 0; r < YC; r++) {  // rows past m: y repeats row m-1, the table row is zero
-                const __attribute__((address_space(4))) uint64_t *hr =
-                    ht + (size_t)min(i0 + r + 1, mpad - 1) * hstride;
-                uint64_t hn[CT];
+        for (int r = 0; r < YC; r++) {  // rows past m: y repeats row m-1, the table row is zero
+            const uint32_t inext = i0 + r + 1 == mpad ? 0 : i0 + r + 1;
+            const __attribute__((address_space(4))) uint64_t *hr = ht + (size_t)inext * hstride;
+            uint64_t hn[CT];
 #pragma unroll
-                for (int a = 0; a < CT; a++) hn[a] = hr[a];
-                const uint32_t yl = (uint32_t)(yv[r] & M30), yh = (uint32_t)(yv[r] >> 30);
+            for (int a = 0; a < CT; a++) hn[a] = hr[a];
+            const uint32_t yl = (uint32_t)(yv[r] & M30), yh = (uint32_t)(yv[r] >> 30);
 #pragma unroll
-                for (int a = 0; a < CT; a++) smac(sp[a], yl, yh, hc[a]);
+            for (int a = 0; a < CT; a++) smac(sp[a], yl, yh, hc[a]);
 #pragma unroll
-                for (int a = 0; a < CT; a++) hc[a] = hn[a];
-            }
-            if (chunk % (SPLIT_CHUNK / YC) == SPLIT_CHUNK / YC - 1) {
+            for (int a = 0; a < CT; a++) hc[a] = hn[a];
+        }
+        i0 = i0 + YC == mpad ? 0 : i0 + YC;
+        if (chunk % (SPLIT_CHUNK / YC) == SPLIT_CHUNK / YC - 1) {
 #pragma unroll
-                for (int a = 0; a < CT; a++) snorm(sp[a]);
-                if (chunk % (4 * SPLIT_CHUNK / YC) == 4 * SPLIT_CHUNK / YC - 1) {
+            for (int a = 0; a < CT; a++) snorm(sp[a]);
+            if (chunk % (4 * SPLIT_CHUNK / YC) == 4 * SPLIT_CHUNK / YC - 1) {
+                // every 60 rows: fold a2 into the low parts modulo each target (keeps a2 < 2^64)
 #pragma unroll
-                    for (int a = 0; a < CT; a++) sfold_hi(acc[a], sp[a]);
+                for (int a = 0; a < CT; a++) {
+                    const uint32_t t =
+                        __builtin_amdgcn_readfirstlane(conv_target(ct, tn0 + min(a, (int)nt - 1), lo, m));
+                    sfold60(sp[a], pc[t]);
                 }
             }
-#pragma unroll
-            for (int r = 0; r < YC; r++) yv[r] = yn[r];
         }
-        uu += u[ss * n + k];
+#pragma unroll
+        for (int r = 0; r < YC; r++) yv[r] = yn[r];
     }
-    // the rows ran in chunks of YC; a fold into acc happened iff 60 rows or more
-    const bool folded = ct.nsum * (mpad / YC) >= 4 * SPLIT_CHUNK / YC;
+    uint64_t uu = 0;
+    for (uint32_t js = 0; js < nsets; js++) uu += u[(sfirst + (size_t)js * ct.sum_stride) * n + k];
     const uint32_t ul = (uint32_t)(uu & M30), uh = (uint32_t)(uu >> 30);
     uint64_t *ob = out + (s / lay.inner) * ct.out_so + (s % lay.inner) * ct.out_si + k;
 #pragma unroll
@@ -406,13 +422,7 @@ __global__ __launch_bounds__(256) void k_convert(const BasisDev *__restrict__ ba
         const PrimeConsts &P = pc[t];
         // u [-B]_t joins the sum as one more product (at most 16 since the last snorm)
         smac(sp[a], ul, uh, split30(B.negB[t]));
-        uint64_t r;
-        if (!folded) {
-            r = sreduce60(sp[a], P);
-        } else {
-            const Acc128 v = sfinal(acc[a], sp[a]);
-            r = reduce128(v.lo, v.hi, P);
-        }
+        const uint64_t r = sreduce60(sp[a], P);
         const uint32_t slot = (ct.mode == 0 && t >= ct.L) ? ct.l + (t - ct.L) : t;
         ob[(size_t)slot * n] = r;
     }
@@ -730,17 +740,17 @@ __global__ __launch_bounds__(256) void k_final2048(const uint64_t *__restrict__ 
 }
 
 // n = 2048 giant-step tail: one workgroup per (ciphertext b, polynomial c, limb i):
-//   out[b][c][i] += (sum_p acc[p B + b][c][i] - NTT(conv[b][c][i])) P^-1
-// with the parts' accumulators from k_inner_sum2048 and conv the ModDown
-// conversions of the batch's steps summed in the coefficient domain (the NTT
-// is linear, so one transform serves the whole batch).
+//   out[b][c][i] += (sum_p acc[p B + b][c][i] - NTT(sum_p conv[p B + b][c][i])) P^-1
+// with the parts' accumulators from k_inner_sum2048 and the parts of the
+// batch's ModDown conversions, summed in the coefficient domain (the NTT is
+// linear, so one transform serves the whole batch).
 __global__ __launch_bounds__(256) void k_final_giant2048(const uint64_t *__restrict__ acc,
                                                           const uint64_t *__restrict__ conv,
                                                           const uint64_t *__restrict__ pinv,
                                                           const PrimeConsts *__restrict__ pc,
                                                           const uint64_t *__restrict__ twf, uint32_t nparts,
-                                                          uint32_t B, uint64_t *__restrict__ out, uint32_t l,
-                                                          uint32_t K) {
+                                                          uint32_t nconv, uint32_t B, uint64_t *__restrict__ out,
+                                                          uint32_t l, uint32_t K) {
     constexpr uint32_t n = 2048;
     __shared__ uint64_t lds[n2048::LDS_WORDS];
     const uint32_t i = blockIdx.x % l;
@@ -751,8 +761,13 @@ __global__ __launch_bounds__(256) void k_final_giant2048(const uint64_t *__restr
     const uint64_t q = P.q;
     uint64_t v[8];
     const uint64_t *cv = conv + (size_t)blockIdx.x * n;
+    const size_t cstride = (size_t)B * 2 * l * n;
 #pragma unroll
-    for (int m = 0; m < 8; m++) v[m] = cv[t + 256 * m];
+    for (int m = 0; m < 8; m++) {
+        uint64_t x = cv[t + 256 * m];
+        for (uint32_t p = 1; p < nconv; p++) x = addm(x, cv[p * cstride + t + 256 * m], q);
+        v[m] = x;
+    }
     n2048::fwd(v, lds, twf + (size_t)i * n * 2, q);
     const size_t pstride = (size_t)B * 2 * (l + K) * n;
     const uint64_t *ar = acc + ((b * 2 + c) * (l + K) + i) * n;
@@ -1038,8 +1053,10 @@ static int ks_inner_giant(ckks_ctx *c, LevelTables *lt, int l, const uint64_t *x
 // ModDown of nout accumulator pairs up to the converted P-part in w.conv
 // (NTT domain for n != 2048; at n = 2048 the final kernels transform it).
 // With nsum > 1 the conversions of accumulators o + j (nout / nsum), j < nsum,
-// are summed into output o (n = 2048 giant steps).
-static int ks_moddown_conv(ckks_ctx *c, size_t nout, int l, const KsWs &w, hipStream_t s, uint32_t nsum = 1) {
+// are summed (n = 2048 giant steps) in *nparts partial sums: part p of output
+// o at w.conv pair p (nout / nsum) + o.
+static int ks_moddown_conv(ckks_ctx *c, size_t nout, int l, const KsWs &w, hipStream_t s, uint32_t nsum = 1,
+                           uint32_t *nparts = nullptr) {
     const uint32_t n = c->n, K = c->K, L = c->L, el = l + K;
     int e;
     {
@@ -1057,9 +1074,14 @@ static int ks_moddown_conv(ckks_ctx *c, size_t nout, int l, const KsWs &w, hipSt
         ConvTargets ct{1, (uint32_t)l, L, K, (size_t)l * n, 0};
         ct.nsum = nsum;
         ct.sum_stride = (uint32_t)(nout / nsum * 2);
+        // up to 4 parts: long summed workgroups need enough of them to fill the chip
+        const uint32_t parts = std::min(nsum, 4u);
+        ct.spp = (nsum + parts - 1) / parts;
+        const uint32_t np = (nsum + ct.spp - 1) / ct.spp;
+        if (nparts) *nparts = np;
         ProfScope ps_(c, "ks_moddown_convert", s);
-        hipLaunchKernelGGL(k_convert, dim3((n + 255) / 256, (l + CT - 1) / CT, (unsigned)(nout / nsum * 2)),
-                           dim3(256), 0, s, c->d_pbasis, lay_dn, w.acc, w.uP, ct, w.conv, n, c->d_pc);
+        hipLaunchKernelGGL(k_convert, dim3((n + 255) / 256, (l + CT - 1) / CT, np * ct.sum_stride), dim3(256), 0,
+                           s, c->d_pbasis, lay_dn, w.acc, w.uP, ct, w.conv, n, c->d_pc);
     }
     LAUNCH_CHECK();
     if (n != 2048) {
@@ -1267,13 +1289,13 @@ int op_bsgs(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, const 
         const uint64_t *src = inner + (size_t)g0 * ct;  // ciphertexts (g0 + j, b), consecutive
         const int nb = (int)st.count * B;
         if (c->n == 2048) {
-            uint32_t nparts = 0;
+            uint32_t nparts = 0, nconv = 0;
             if ((e = ks_modup(c, lt, nb, l, src + per, 2 * per, w, s))) return e;
             if ((e = ks_inner_giant(c, lt, l, src, 2 * per, st, w, &nparts, s))) return e;
-            if ((e = ks_moddown_conv(c, nb, l, w, s, st.count))) return e;
+            if ((e = ks_moddown_conv(c, nb, l, w, s, st.count, &nconv))) return e;
             ProfScope ps_(c, "giant_final", s);
             hipLaunchKernelGGL(k_final_giant2048, dim3(B * 2 * l), dim3(256), 0, s, w.acc, w.conv, c->d_pinv,
-                               c->d_pc, c->d_tw_fwd, nparts, (uint32_t)B, inner, (uint32_t)l, c->K);
+                               c->d_pc, c->d_tw_fwd, nparts, nconv, (uint32_t)B, inner, (uint32_t)l, c->K);
             LAUNCH_CHECK();
         } else {
             for (uint32_t j = 0; j < st.count; j++)
