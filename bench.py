@@ -35,13 +35,26 @@ HBM_PEAK_GBS = 8000.0
 VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 LIMB = N * 8
 
-# HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE on this
-# workload (fetch scaled x2.0 and write x1.0 by a 1 GiB copy calibration; see
-# profiles/bench_step_n2048_l112_b8_hbm_counters.md).  Valid only for the
-# kernel sources they were taken on (hash of rns_ckks_polynomial_amd/csrc).
+# HBM bytes per launch (average over the launches of the step) measured with
+# rocprofv3 FETCH_SIZE / WRITE_SIZE on this workload; fetch scaled x2.0 and
+# write x1.0, the factors a plain 1 GiB device copy reads from the same
+# counters (profiles/bench_step_n2048_l112_b8_hbm_counters.md).  Valid only for
+# the kernel sources they were taken on (hash of rns_ckks_polynomial_amd/csrc).
 MEASURED_TRAFFIC = {
-    "source_sha": "9a779d0215045d90",
-    "bytes_per_step": {},
+    "source_sha": "22c21f2525cd235a",
+    "bytes_per_launch": {
+        "ks_modup_convert": 895087955,
+        "ks_moddown_convert": 510161668,
+        "bsgs_mac": 3758170250,
+        "ks_ntt_ext": 1322433715,
+        "ks_inner_product_sum": 6033724828,
+        "rotate_final": 3192107452,
+        "ntt_fwd": 62576920,
+        "ntt_inv": 62598935,
+        "giant_final": 297538902,
+        "ks_intt_modup": 326835405,
+        "ks_intt_moddown": 310304870
+    },
 }
 
 
@@ -251,16 +264,19 @@ def main():
     roofline["avg_launch_us"] = drow["avg_us"]
     roofline["kernel_ms_per_step"] = drow["total_ms_per_step"]
     traffic_valid = csrc_sha() == MEASURED_TRAFFIC["source_sha"]
-    if traffic_valid and dom in MEASURED_TRAFFIC["bytes_per_step"]:
-        roofline["traffic"] = MEASURED_TRAFFIC["bytes_per_step"][dom]
-        roofline["traffic_unit"] = "bytes per step (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+    launches = drow["launches"] // args.profile_steps
+    if traffic_valid and dom in MEASURED_TRAFFIC["bytes_per_launch"]:
+        roofline["traffic"] = MEASURED_TRAFFIC["bytes_per_launch"][dom]
+        roofline["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+        if "bytes" in dw:
+            roofline["traffic_over_algorithmic"] = roofline["traffic"] / (dw["bytes"] / launches)"
     ntt_row = kernels.get("ntt_fwd", {})
     ntt_roof = {"bound": "hbm", "kernel": "ntt_fwd [16][112] limbs", "achieved": ntt_row.get("algo_GBps"),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "avg_launch_us": ntt_row.get("avg_us"),
                 "work_per_launch": f"{work['ntt_fwd']['bytes']} bytes (each limb read and written once)"}
     if ntt_roof["achieved"]:
         ntt_roof["frac"] = ntt_roof["achieved"] / HBM_PEAK_GBS
-    ntt_roof["traffic"] = MEASURED_TRAFFIC["bytes_per_step"].get("ntt_fwd") if traffic_valid else None
+    ntt_roof["traffic"] = MEASURED_TRAFFIC["bytes_per_launch"].get("ntt_fwd") if traffic_valid else None
 
     out = {
         "metric": "limb-NTTs/s + key-switches/s @n=2048,112 primes; % HBM roofline",

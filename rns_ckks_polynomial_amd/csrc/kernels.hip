@@ -313,10 +313,10 @@ static_assert(SPLIT_CHUNK % YC == 0, "flush on a chunk boundary");
 static_assert(CT <= (int)CONV_COL_PAD, "tile reads stay inside a table row");
 
 struct ConvTargets {
-    // mode 0 (ModUp of digit [lo, lo+m)): target positions run over [L, L+K),
+    // k_convert<0> (ModUp of digit [lo, lo+m)): target positions run over [L, L+K),
     // then [0, lo) u [lo+m, l); the outputs go to ext slots (special t -> l + t - L)
-    // mode 1 (ModDown): targets = [0, l) -> slot t
-    uint32_t mode, l, L, K;
+    // k_convert<1> (ModDown): targets = [0, l) -> slot t
+    uint32_t l, L, K;
     size_t out_so, out_si;  // output limb base of set s: (s / inner) * out_so + (s % inner) * out_si
     // Summed conversions (nsum > 1): the input sets s + j * sum_stride, j < nsum,
     // are split into parts of spp consecutive j; output set p * sum_stride + s
@@ -325,13 +325,16 @@ struct ConvTargets {
     uint32_t nsum = 1, sum_stride = 0, spp = 1;
 };
 
+template <int MODE>
 __device__ __forceinline__ uint32_t conv_target(const ConvTargets &ct, uint32_t tn, uint32_t lo, uint32_t m) {
-    if (ct.mode == 1) return tn;
+    if (MODE == 1) return tn;
     if (tn < ct.K) return ct.L + tn;
     const uint32_t c = tn - ct.K;
     return c < lo ? c : c + m;
 }
 
+// MODE 0: ModUp targets, MODE 1: ModDown targets.
+template <int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k_convert(const BasisDev *__restrict__ bases, SetLayout lay,
                                                   const uint64_t *__restrict__ y, const uint32_t *__restrict__ u,
                                                   ConvTargets ct, uint64_t *__restrict__ out, uint32_t n,
@@ -339,7 +342,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k
     const uint32_t s = blockIdx.z;
     const BasisDev &B = bases[lay.per_set_basis ? s % lay.inner : 0];
     const uint32_t m = B.m, lo = B.first;
-    const uint32_t ntarget = ct.mode == 0 ? ct.l - m + ct.K : ct.l;
+    const uint32_t ntarget = MODE == 0 ? ct.l - m + ct.K : ct.l;
     const uint32_t tn0 = blockIdx.y * CT;
     if (tn0 >= ntarget) return;
     const uint32_t nt = min((uint32_t)CT, ntarget - tn0);
@@ -403,7 +406,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k
 #pragma unroll
                 for (int a = 0; a < CT; a++) {
                     const uint32_t t =
-                        __builtin_amdgcn_readfirstlane(conv_target(ct, tn0 + min(a, (int)nt - 1), lo, m));
+                        __builtin_amdgcn_readfirstlane(conv_target<MODE>(ct, tn0 + min(a, (int)nt - 1), lo, m));
                     sfold60(sp[a], pc[t]);
                 }
             }
@@ -418,12 +421,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k
 #pragma unroll
     for (int a = 0; a < CT; a++) {
         if (a >= (int)nt) break;
-        const uint32_t t = __builtin_amdgcn_readfirstlane(conv_target(ct, tn0 + a, lo, m));
+        const uint32_t t = __builtin_amdgcn_readfirstlane(conv_target<MODE>(ct, tn0 + a, lo, m));
         const PrimeConsts &P = pc[t];
         // u [-B]_t joins the sum as one more product (at most 16 since the last snorm)
         smac(sp[a], ul, uh, split30(B.negB[t]));
         const uint64_t r = sreduce60(sp[a], P);
-        const uint32_t slot = (ct.mode == 0 && t >= ct.L) ? ct.l + (t - ct.L) : t;
+        const uint32_t slot = (MODE == 0 && t >= ct.L) ? ct.l + (t - ct.L) : t;
         ob[(size_t)slot * n] = r;
     }
 }
@@ -974,10 +977,10 @@ static int ks_modup(ckks_ctx *c, LevelTables *lt, int B, int l, const uint64_t *
     }
     LAUNCH_CHECK();
     {
-        ConvTargets ct{0, (uint32_t)l, L, K, (size_t)beta * el * n, (size_t)el * n};
+        ConvTargets ct{(uint32_t)l, L, K, (size_t)beta * el * n, (size_t)el * n};
         const uint32_t maxt = l + K;  // upper bound on targets per digit
         ProfScope ps_(c, "ks_modup_convert", s);
-        hipLaunchKernelGGL(k_convert, dim3((n + 255) / 256, (maxt + CT - 1) / CT, B * beta), dim3(256), 0, s,
+        hipLaunchKernelGGL(k_convert<0>, dim3((n + 255) / 256, (maxt + CT - 1) / CT, B * beta), dim3(256), 0, s,
                            lt->d_digits, lay_up, w.y, w.u, ct, w.ext, n, c->d_pc);
     }
     LAUNCH_CHECK();
@@ -1071,7 +1074,7 @@ static int ks_moddown_conv(ckks_ctx *c, size_t nout, int l, const KsWs &w, hipSt
     }
     LAUNCH_CHECK();
     {
-        ConvTargets ct{1, (uint32_t)l, L, K, (size_t)l * n, 0};
+        ConvTargets ct{(uint32_t)l, L, K, (size_t)l * n, 0};
         ct.nsum = nsum;
         ct.sum_stride = (uint32_t)(nout / nsum * 2);
         // up to 4 parts: long summed workgroups need enough of them to fill the chip
@@ -1080,7 +1083,7 @@ static int ks_moddown_conv(ckks_ctx *c, size_t nout, int l, const KsWs &w, hipSt
         const uint32_t np = (nsum + ct.spp - 1) / ct.spp;
         if (nparts) *nparts = np;
         ProfScope ps_(c, "ks_moddown_convert", s);
-        hipLaunchKernelGGL(k_convert, dim3((n + 255) / 256, (l + CT - 1) / CT, np * ct.sum_stride), dim3(256), 0,
+        hipLaunchKernelGGL(k_convert<1>, dim3((n + 255) / 256, (l + CT - 1) / CT, np * ct.sum_stride), dim3(256), 0,
                            s, c->d_pbasis, lay_dn, w.acc, w.uP, ct, w.conv, n, c->d_pc);
     }
     LAUNCH_CHECK();
