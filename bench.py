@@ -269,7 +269,7 @@ def main():
         roofline["traffic"] = MEASURED_TRAFFIC["bytes_per_launch"][dom]
         roofline["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
         if "bytes" in dw:
-            roofline["traffic_over_algorithmic"] = roofline["traffic"] / (dw["bytes"] / launches)"
+            roofline["traffic_over_algorithmic"] = roofline["traffic"] / (dw["bytes"] / launches)
     ntt_row = kernels.get("ntt_fwd", {})
     ntt_roof = {"bound": "hbm", "kernel": "ntt_fwd [16][112] limbs", "achieved": ntt_row.get("algo_GBps"),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "avg_launch_us": ntt_row.get("avg_us"),

@@ -431,6 +431,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k
     }
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.
+// Maps dispatch index i to (group g, member j < B) so that the B members of a
+// group (the B ciphertexts that read one key row) run on one XCD back to back:
+// launch xcd_blocks(ngroups, B) workgroups; those with g >= ngroups exit.
+constexpr uint32_t NXCD = 8;
+__device__ __forceinline__ void xcd_group(uint32_t i, uint32_t B, uint32_t &g, uint32_t &j) {
+    const uint32_t x = i % NXCD, k = i / NXCD;
+    g = x + NXCD * (k / B);
+    j = k % B;
+}
+static inline uint32_t xcd_blocks(uint32_t ngroups, uint32_t B) {
+    return (ngroups + NXCD - 1) / NXCD * NXCD * B;
+}
+
 // A batched key switch runs S "steps" of B ciphertexts each: output
 // ciphertext cb = s * B + b uses key[s] and Galois element g[s].  With
 // shared = 1 every step switches the same B inputs (hoisted baby steps);
@@ -458,12 +472,13 @@ __global__ __launch_bounds__(256) void k_inner2048(const uint64_t *__restrict__ 
     constexpr uint32_t n = 2048;
     __shared__ uint64_t buf[2][n];
     const uint32_t el = l + K;
-    // block order: ciphertext fastest, then limb (of the range [e0, e0 + ne)),
-    // then step, so the B blocks reading one key row run together and one
-    // step's key is in flight at a time
-    const uint32_t bl = blockIdx.x % st.B;
-    const uint32_t e = e0 + (blockIdx.x / st.B) % ne;
-    const uint32_t step = blockIdx.x / (st.B * ne);
+    // group = (step, limb of the range [e0, e0 + ne)), member = ciphertext: the
+    // B blocks reading one key row share an XCD's L2, one step's key at a time
+    uint32_t grp, bl;
+    xcd_group(blockIdx.x, st.B, grp, bl);
+    if (grp >= st.count * ne) return;
+    const uint32_t e = e0 + grp % ne;
+    const uint32_t step = grp / ne;
     const size_t cb = (size_t)step * st.B + bl;
     const size_t b = st.shared ? bl : cb;  // input ciphertext
     const uint64_t *key = st.key[step];
@@ -528,16 +543,18 @@ __global__ __launch_bounds__(256) void k_inner2048(const uint64_t *__restrict__ 
 __global__ __launch_bounds__(256) void k_inner_sum2048(const uint64_t *__restrict__ d, size_t d_stride,
                                                         const uint64_t *__restrict__ c0, size_t c0_stride,
                                                         const uint64_t *__restrict__ ext, const Steps st,
-                                                        uint32_t spp, uint64_t *__restrict__ acc,
+                                                        uint32_t spp, uint32_t nparts, uint64_t *__restrict__ acc,
                                                         const PrimeConsts *__restrict__ pc,
                                                         const uint64_t *__restrict__ pmod, uint32_t l, uint32_t K,
                                                         uint32_t L, uint32_t beta, uint32_t alpha) {
     constexpr uint32_t n = 2048;
     __shared__ uint64_t buf[2][n];
     const uint32_t el = l + K;
-    const uint32_t bl = blockIdx.x % st.B;
-    const uint32_t e = (blockIdx.x / st.B) % l;
-    const uint32_t part = blockIdx.x / (st.B * l);
+    uint32_t grp, bl;  // group = (part, limb), member = ciphertext (see xcd_group)
+    xcd_group(blockIdx.x, st.B, grp, bl);
+    if (grp >= nparts * l) return;
+    const uint32_t e = grp % l;
+    const uint32_t part = grp / l;
     const uint32_t s_end = min(st.count, (part + 1) * spp);
     const uint32_t t = threadIdx.x;
     const PrimeConsts P = pc[e];
@@ -1012,8 +1029,8 @@ static int ks_inner(ckks_ctx *c, LevelTables *lt, int l, const uint64_t *d, size
     const size_t nout = (size_t)st.count * st.B;
     ProfScope ps_(c, st.shared ? "ks_inner_product_hoisted" : "ks_inner_product", s);
     if (n == 2048) {
-        hipLaunchKernelGGL(k_inner2048, dim3(nout * el), dim3(256), 0, s, d, d_stride, w.ext, st, w.acc, c->d_pc,
-                           (uint32_t)l, L, K, beta, c->alpha, 0u, el);
+        hipLaunchKernelGGL(k_inner2048, dim3(xcd_blocks(st.count * el, st.B)), dim3(256), 0, s, d, d_stride, w.ext,
+                           st, w.acc, c->d_pc, (uint32_t)l, L, K, beta, c->alpha, 0u, el);
     } else {  // generic n: one launch per step
         for (uint32_t j = 0; j < st.count; j++) {
             const size_t total = (size_t)st.B * el * n;
@@ -1037,8 +1054,8 @@ static int ks_inner_giant(ckks_ctx *c, LevelTables *lt, int l, const uint64_t *x
     const size_t per = (size_t)l * c->n;
     {
         ProfScope ps_(c, "ks_inner_product", s);
-        hipLaunchKernelGGL(k_inner2048, dim3(st.count * st.B * K), dim3(256), 0, s, x + per, x_stride, w.ext, st,
-                           w.acc, c->d_pc, (uint32_t)l, L, K, beta, c->alpha, (uint32_t)l, K);
+        hipLaunchKernelGGL(k_inner2048, dim3(xcd_blocks(st.count * K, st.B)), dim3(256), 0, s, x + per, x_stride,
+                           w.ext, st, w.acc, c->d_pc, (uint32_t)l, L, K, beta, c->alpha, (uint32_t)l, K);
     }
     LAUNCH_CHECK();
     // up to 4 partial sums: enough workgroups to fill the chip at ~1 wave per SIMD each
@@ -1046,8 +1063,9 @@ static int ks_inner_giant(ckks_ctx *c, LevelTables *lt, int l, const uint64_t *x
     *nparts = (st.count + spp - 1) / spp;
     {
         ProfScope ps_(c, "ks_inner_product_sum", s);
-        hipLaunchKernelGGL(k_inner_sum2048, dim3(*nparts * st.B * l), dim3(256), 0, s, x + per, x_stride, x,
-                           x_stride, w.ext, st, spp, w.acc, c->d_pc, c->d_pmod, (uint32_t)l, K, L, beta, c->alpha);
+        hipLaunchKernelGGL(k_inner_sum2048, dim3(xcd_blocks(*nparts * l, st.B)), dim3(256), 0, s, x + per, x_stride,
+                           x, x_stride, w.ext, st, spp, *nparts, w.acc, c->d_pc, c->d_pmod, (uint32_t)l, K, L, beta,
+                           c->alpha);
     }
     LAUNCH_CHECK();
     return CKKS_OK;
