@@ -41,19 +41,19 @@ LIMB = N * 8
 # counters (profiles/bench_step_n2048_l112_b8_hbm_counters.md).  Valid only for
 # the kernel sources they were taken on (hash of rns_ckks_polynomial_amd/csrc).
 MEASURED_TRAFFIC = {
-    "source_sha": "22c21f2525cd235a",
+    "source_sha": "35410c2b2b961681",
     "bytes_per_launch": {
-        "ks_modup_convert": 895087955,
-        "ks_moddown_convert": 510161668,
-        "bsgs_mac": 3758170250,
-        "ks_ntt_ext": 1322433715,
-        "ks_inner_product_sum": 6033724828,
-        "rotate_final": 3192107452,
-        "ntt_fwd": 62576920,
-        "ntt_inv": 62598935,
-        "giant_final": 297538902,
-        "ks_intt_modup": 326835405,
-        "ks_intt_moddown": 310304870
+        "ks_modup_convert": 895086129,
+        "ks_moddown_convert": 510172947,
+        "bsgs_mac": 3758170954,
+        "ks_ntt_ext": 1322224454,
+        "ks_inner_product_sum": 2849251223,
+        "rotate_final": 3192128250,
+        "ntt_fwd": 62574880,
+        "ntt_inv": 62598942,
+        "giant_final": 297537846,
+        "ks_intt_modup": 326834793,
+        "ks_intt_moddown": 310303500
     },
 }
 

@@ -145,7 +145,8 @@ def _bsgs_inputs(o, seed, B, l, bs, gs):
     return x, pt, baby, giant
 
 
-@pytest.mark.parametrize("l,B,bs,gs", [(20, 2, 4, 3), (112, 1, 2, 2)])
+# giant batches of 2, 1, 5 and 7 steps: summed parts of 1, 2 (ragged) and 2/1 steps
+@pytest.mark.parametrize("l,B,bs,gs", [(20, 2, 4, 3), (112, 1, 2, 2), (20, 2, 2, 6), (24, 3, 3, 8)])
 def test_bsgs_small_bitexact(l, B, bs, gs):
     g, o = gpu_ctx(*LAY), oracle_ctx(*LAY)
     x, pt, baby, giant = _bsgs_inputs(o, 80 + l, B, l, bs, gs)
