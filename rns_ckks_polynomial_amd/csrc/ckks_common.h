@@ -20,6 +20,30 @@ __device__ __forceinline__ uint64_t shoup_lazy(uint64_t x, uint64_t w, uint64_t 
     return x * w - mulhi64(x, wp) * q;
 }
 __device__ __forceinline__ uint64_t csub(uint64_t x, uint64_t q) { return x >= q ? x - q : x; }
+
+// Shoup product with the quotient floor(y wp / 2^64) truncated to the three
+// high 32x32 partial products: the dropped carries make it at most 2 too
+// small, so y w - Q q lands in [0, 4q) (instead of [0, 2q)) for any 64-bit y.
+// The remainder is formed as y w + Q (2^64 - q) mod 2^64 (nq = 2^64 - q), so
+// the subtraction rides on the multiply-adds.
+__device__ __forceinline__ uint64_t shoup_lazy4(uint64_t y, uint64_t w, uint64_t wp, uint64_t nq) {
+    const uint32_t yl = (uint32_t)y, yh = (uint32_t)(y >> 32);
+    const uint32_t pl = (uint32_t)wp, ph = (uint32_t)(wp >> 32);
+    const uint64_t qt = (uint64_t)yh * ph + ((uint64_t)__umulhi(yh, pl) + __umulhi(yl, ph));
+    const uint32_t ql = (uint32_t)qt, qh = (uint32_t)(qt >> 32);
+    const uint32_t wl = (uint32_t)w, wh = (uint32_t)(w >> 32);
+    const uint32_t nl = (uint32_t)nq, nh = (uint32_t)(nq >> 32);
+    const uint64_t r = (uint64_t)ql * nl + (uint64_t)yl * wl;  // mod 2^64
+    const uint32_t hi = (uint32_t)(r >> 32) + yl * wh + yh * wl + ql * nh + qh * nl;
+    return ((uint64_t)hi << 32) | (uint32_t)r;
+}
+
+// x - c if x >= c else x, for x, c < 2^63 with |x - c| < 2^63 (nc = 2^64 - c): add, then select on the sign.
+__device__ __forceinline__ uint64_t csub_sign(uint64_t x, uint64_t nc) {
+    const uint64_t m = x + nc;
+    return (int64_t)m < 0 ? x : m;
+}
+
 __device__ __forceinline__ uint64_t shoup(uint64_t x, uint64_t w, uint64_t wp, uint64_t q) {
     return csub(shoup_lazy(x, w, wp, q), q);
 }
@@ -82,6 +106,7 @@ struct Split3 {
     uint64_t a0, a1, a1b, a2;
 };
 __device__ __forceinline__ uint64_t split30(uint64_t v) { return (v & M30) | ((v >> 30) << 32); }
+__device__ __forceinline__ uint64_t unsplit30(uint64_t s) { return (s & M30) | ((s >> 32) << 30); }
 __device__ __forceinline__ void smac(Split3 &s, uint32_t xb, uint32_t xa, uint64_t ysplit) {
     const uint32_t yb = (uint32_t)ysplit, ya = (uint32_t)(ysplit >> 32);
     s.a0 += (uint64_t)xb * yb;
@@ -159,6 +184,32 @@ __device__ __forceinline__ void sfold60(Split3 &s, const PrimeConsts &P) {
     s.a2 = 0;
 }
 
+// Two-level normalisation for long Split3 sums (base conversion): snorm0
+// moves a0's carries into a1 (due every 15 products: a0 < 2^30 afterwards);
+// snorm_hi moves a1's and a1b's carries into a2 (due every 28 products: both
+// take one product below 2^59 + 2^52 per smac plus a0's carries).  a2 gains
+// one product below 2^58.1 per smac: fold it (sfold60) at least every 56.
+__device__ __forceinline__ void snorm0(Split3 &s) {
+    s.a1 += s.a0 >> 30;
+    s.a0 &= M30;
+}
+__device__ __forceinline__ void snorm_hi(Split3 &s) {
+    s.a2 += (s.a1 >> 30) + (s.a1b >> 30);
+    s.a1 &= M30;
+    s.a1b &= M30;
+}
+// a0 + 2^30 (a1 + a1b) + 2^60 a2 mod q for a sum kept within the snorm0 /
+// snorm_hi / sfold60 cadence (each part may be just short of 2^64).
+__device__ __forceinline__ uint64_t sfinal_mod(Split3 s, const PrimeConsts &P) {
+    s.a1 += s.a0 >> 30;
+    const uint64_t hi = s.a2 + (s.a1 >> 30) + (s.a1b >> 30);                     // < 2^64
+    const uint64_t lo = (s.a0 & M30) + (((s.a1 & M30) + (s.a1b & M30)) << 30);  // < 2^61 < 4q
+    uint64_t r = shoup_lazy4(hi, P.r60, P.r60p, 0 - P.q) + lo;                 // < 8q < 2^63
+    r = csub_sign(r, 0 - 4 * P.q);
+    r = csub_sign(r, 0 - 2 * P.q);
+    return csub_sign(r, 0 - P.q);
+}
+
 // Full reduction of a split sum modulo P.q, left in normalised split form
 // (a0, a1 < 2^30, a2 = 0): restarts the growth bounds of snorm.
 __device__ __forceinline__ void sreduce(Split3 &s, const PrimeConsts &P) {
@@ -173,7 +224,7 @@ __device__ __forceinline__ void sreduce(Split3 &s, const PrimeConsts &P) {
 // The centered CRT value x_c of residues x_i modulo B = prod b_i is
 //   x_c = sum_i y_i Bhat_i - u B,   y_i = [x_i Bhat_i^-1]_{b_i},
 //   u = round(sum_i y_i / b_i)  (= floor(sum) + [x > (B-1)/2]).
-constexpr uint32_t CONV_ROW_PAD = 5;
+constexpr uint32_t CONV_ROW_PAD = 7;
 constexpr uint32_t CONV_COL_PAD = 8;
 struct BasisDev {
     uint32_t m;            // number of primes in the basis
@@ -192,7 +243,7 @@ struct BasisDev {
     const uint64_t *HT;
     uint32_t hstride;         // row length of HT (positions + CONV_COL_PAD)
     uint32_t mpad;            // row count of HT
-    const uint64_t *negB;     // [ntot]     [-B]_t
+    const uint64_t *negB;     // [ntot]     [-B]_t, split30 layout
     const uint64_t *garner;   // [m][m][2]  Shoup pair of b_k^-1 mod b_i (k < i used)
     const uint64_t *half;     // [m]        mixed-radix digits of (B-1)/2
 };

@@ -191,6 +191,7 @@ int build_basis(ckks_ctx *ctx, uint32_t first, uint32_t m, BasisDev *out, std::v
     d.HT = dev_upload(Hs, owned, &err);
     d.hstride = hstride;
     d.mpad = mpad;
+    for (auto &v : negB) v = (v & ((1ull << 30) - 1)) | ((v >> 30) << 32);  // split30 for the conversion tail
     d.negB = dev_upload(negB, owned, &err);
     d.garner = dev_upload(garner, owned, &err);
     d.half = dev_upload(half, owned, &err);

@@ -41,6 +41,7 @@ static inline dim3 grid_for(size_t total) {
 // replaces n^-1 on the inverse.  src == nullptr skips the block.
 // =====================================================================
 struct MapStrided {  // [count][nl][n], limb r -> prime first + r
+    static constexpr bool split_out = false;
     const uint64_t *src;
     uint64_t *dst;
     uint32_t n, nl, first;
@@ -55,6 +56,7 @@ struct MapStrided {  // [count][nl][n], limb r -> prime first + r
 };
 
 struct MapBatched {  // limb r of ciphertext b at src + b * src_stride + r * n -> dst [B][nl][n]
+    static constexpr bool split_out = true;  // ModUp inputs y: stored in split30 form
     const uint64_t *src;
     size_t src_stride;
     uint64_t *dst;
@@ -71,6 +73,7 @@ struct MapBatched {  // limb r of ciphertext b at src + b * src_stride + r * n -
 };
 
 struct MapExt {  // converted limbs [B][beta][l+K][n]; skips the digit's own primes
+    static constexpr bool split_out = false;
     uint64_t *ext;
     uint32_t n, l, L, K, beta, alpha;
     __device__ __forceinline__ void get(int blk, const uint64_t *&s, uint64_t *&d, int &prime,
@@ -91,6 +94,7 @@ struct MapExt {  // converted limbs [B][beta][l+K][n]; skips the digit's own pri
 };
 
 struct MapLast {  // last limb of each polynomial [P][l][n] -> dense [P][n]
+    static constexpr bool split_out = false;
     const uint64_t *src;
     uint64_t *dst;
     uint32_t n, l;
@@ -104,6 +108,7 @@ struct MapLast {  // last limb of each polynomial [P][l][n] -> dense [P][n]
 };
 
 struct MapAccP {  // P limbs of acc [B][2][l+K][n], scaled inverse -> ModDown inputs
+    static constexpr bool split_out = true;  // ModDown inputs y: stored in split30 form
     uint64_t *acc;
     uint32_t n, l, L, K;
     const uint64_t *scale;  // [K][2]
@@ -141,7 +146,10 @@ __global__ __launch_bounds__(256) void k_ntt2048(Map map, const PrimeConsts *__r
         n2048::inv(v, lds, twi + (size_t)prime * 2048 * 2, q);
         const uint64_t w = sc ? sc[0] : pc[prime].ninv, wp = sc ? sc[1] : pc[prime].ninvp;
 #pragma unroll
-        for (int k = 0; k < 8; k++) dst[t + 256 * k] = shoup(v[k], w, wp, q);
+        for (int k = 0; k < 8; k++) {
+            const uint64_t r = shoup(v[k], w, wp, q);
+            dst[t + 256 * k] = Map::split_out ? split30(r) : r;
+        }
     }
 }
 
@@ -219,10 +227,10 @@ __global__ void k_prep_relin(const uint64_t *__restrict__ a, const uint64_t *__r
 __device__ uint32_t exact_u_slow(const BasisDev &B, uint64_t *ycol, size_t stride, uint32_t floor_s,
                                  const PrimeConsts *__restrict__ pc) {
     const uint32_t m = B.m;
-    // x_i = y_i [Bhat_i]_{b_i}, in place
+    // x_i = y_i [Bhat_i]_{b_i}, in place (y arrives in split30 form, x is plain)
     for (uint32_t i = 0; i < m; i++) {
         const uint64_t bi = pc[B.first + i].q;
-        ycol[i * stride] = shoup(ycol[i * stride], B.hat_mod[2 * i], B.hat_mod[2 * i + 1], bi);
+        ycol[i * stride] = shoup(unsplit30(ycol[i * stride]), B.hat_mod[2 * i], B.hat_mod[2 * i + 1], bi);
     }
     // Garner, in place: after step i, slot i holds mixed-radix digit a_i and
     // slots k > i hold (x - a_0 - ... ) / (b_0 ... b_i) mod b_k.
@@ -249,7 +257,7 @@ __device__ uint32_t exact_u_slow(const BasisDev &B, uint64_t *ycol, size_t strid
             ak = ak >= P.q ? ak - P.q : ak;
             r = addm(mulm(r, bk, P.q, P.mu), ak, P.q);
         }
-        ycol[i * stride] = shoup(r, B.inv_hat[2 * i], B.inv_hat[2 * i + 1], P.q);
+        ycol[i * stride] = split30(shoup(r, B.inv_hat[2 * i], B.inv_hat[2 * i + 1], P.q));
     }
     return floor_s + (cmp > 0 ? 1u : 0u);
 }
@@ -279,7 +287,7 @@ __global__ void k_basis_u(const BasisDev *__restrict__ bases, SetLayout lay, uin
 #pragma unroll
         for (int a = 0; a < 8; a++) {
             const uint32_t i = min(i0 + a, m - 1);
-            yv[a] = yb[(size_t)i * n];
+            yv[a] = unsplit30(yb[(size_t)i * n]);
             rv[a] = B.R[i];
         }
 #pragma unroll
@@ -308,8 +316,7 @@ __global__ void k_basis_u(const BasisDev *__restrict__ bases, SetLayout lay, uin
 // into 128 bits every SPLIT_CHUNK inputs.
 // ---------------------------------------------------------------------
 constexpr int CT = 8;
-constexpr int YC = (int)CONV_ROW_PAD;
-static_assert(SPLIT_CHUNK % YC == 0, "flush on a chunk boundary");
+constexpr int YC = (int)CONV_ROW_PAD;  // rows per chunk
 static_assert(CT <= (int)CONV_COL_PAD, "tile reads stay inside a table row");
 
 struct ConvTargets {
@@ -335,7 +342,7 @@ __device__ __forceinline__ uint32_t conv_target(const ConvTargets &ct, uint32_t 
 
 // MODE 0: ModUp targets, MODE 1: ModDown targets.
 template <int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k_convert(const BasisDev *__restrict__ bases, SetLayout lay,
+__global__ __launch_bounds__(256) void k_convert(const BasisDev *__restrict__ bases, SetLayout lay,
                                                   const uint64_t *__restrict__ y, const uint32_t *__restrict__ u,
                                                   ConvTargets ct, uint64_t *__restrict__ out, uint32_t n,
                                                   const PrimeConsts *__restrict__ pc) {
@@ -357,17 +364,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k
 #pragma unroll
     for (int a = 0; a < CT; a++) sp[a] = {0, 0, 0, 0};
     // The summed sets' rows form one stream of chunks (YC rows each, mpad / YC
-    // chunks per set), so the input prefetch runs across set boundaries.
+    // chunks per set), so the input prefetch runs across set boundaries; the
+    // next table row is fetched one row ahead.  Inputs arrive in split30 form.
     const uint32_t part = ct.nsum > 1 ? s / ct.sum_stride : 0;
     const size_t sfirst = ct.nsum > 1 ? s + (size_t)part * (ct.spp - 1) * ct.sum_stride : s;
     const uint32_t nsets = ct.nsum > 1 ? min(ct.spp, ct.nsum - part * ct.spp) : 1;
-    auto set_base = [&](uint32_t js) {
-        const size_t ss = sfirst + (size_t)js * ct.sum_stride;
-        return y + (ss / lay.inner) * lay.so + (ss % lay.inner) * lay.si + lay.off + k;
-    };
+    // summed sets use inner == 1 (as the host sets it up): set j + 1 starts set_step words after set j
+    const uint64_t *pb = y + (sfirst / lay.inner) * lay.so + (sfirst % lay.inner) * lay.si + lay.off + k;
+    const size_t set_step = (size_t)ct.sum_stride * lay.so;
     const uint32_t nchunks = nsets * (mpad / YC);
-    const uint64_t *pb = set_base(0);  // set of the chunk being fetched
-    uint32_t pi = 0, pj = 0;           // its first row and set index
+    uint32_t pi = 0, pj = 0;  // first row and set index of the chunk being fetched (set base pb)
     uint64_t yv[YC], yn[YC];
 #pragma unroll
     for (int r = 0; r < YC; r++) yv[r] = pb[(size_t)min((uint32_t)r, m - 1) * n];
@@ -379,8 +385,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k
         pi += YC;  // advance the fetch position to the next chunk
         if (pi == mpad) {
             pi = 0;
-            pj = min(pj + 1, nsets - 1);  // past the end: harmless reload of the last set
-            pb = set_base(pj);
+            if (pj + 1 < nsets) {  // past the end: harmless reload of the last set
+                pj++;
+                pb += set_step;
+            }
         }
 #pragma unroll
         for (int r = 0; r < YC; r++) yn[r] = pb[(size_t)min(pi + r, m - 1) * n];
@@ -391,23 +399,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k
             uint64_t hn[CT];
 #pragma unroll
             for (int a = 0; a < CT; a++) hn[a] = hr[a];
-            const uint32_t yl = (uint32_t)(yv[r] & M30), yh = (uint32_t)(yv[r] >> 30);
+            const uint32_t yl = (uint32_t)yv[r], yh = (uint32_t)(yv[r] >> 32);
 #pragma unroll
             for (int a = 0; a < CT; a++) smac(sp[a], yl, yh, hc[a]);
 #pragma unroll
             for (int a = 0; a < CT; a++) hc[a] = hn[a];
         }
         i0 = i0 + YC == mpad ? 0 : i0 + YC;
-        if (chunk % (SPLIT_CHUNK / YC) == SPLIT_CHUNK / YC - 1) {
+        // every 2 chunks (14 products) snorm0, every 4 snorm_hi, every 8 fold a2
+        if (chunk & 1) {
 #pragma unroll
-            for (int a = 0; a < CT; a++) snorm(sp[a]);
-            if (chunk % (4 * SPLIT_CHUNK / YC) == 4 * SPLIT_CHUNK / YC - 1) {
-                // every 60 rows: fold a2 into the low parts modulo each target (keeps a2 < 2^64)
+            for (int a = 0; a < CT; a++) snorm0(sp[a]);
+            if (chunk & 2) {
 #pragma unroll
-                for (int a = 0; a < CT; a++) {
-                    const uint32_t t =
-                        __builtin_amdgcn_readfirstlane(conv_target<MODE>(ct, tn0 + min(a, (int)nt - 1), lo, m));
-                    sfold60(sp[a], pc[t]);
+                for (int a = 0; a < CT; a++) snorm_hi(sp[a]);
+                if (chunk & 4) {
+#pragma unroll
+                    for (int a = 0; a < CT; a++) {
+                        const uint32_t t =
+                            __builtin_amdgcn_readfirstlane(conv_target<MODE>(ct, tn0 + min(a, (int)nt - 1), lo, m));
+                        sfold60(sp[a], pc[t]);
+                    }
                 }
             }
         }
@@ -423,9 +435,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k
         if (a >= (int)nt) break;
         const uint32_t t = __builtin_amdgcn_readfirstlane(conv_target<MODE>(ct, tn0 + a, lo, m));
         const PrimeConsts &P = pc[t];
-        // u [-B]_t joins the sum as one more product (at most 16 since the last snorm)
-        smac(sp[a], ul, uh, split30(B.negB[t]));
-        const uint64_t r = sreduce60(sp[a], P);
+        // u [-B]_t joins the sum as one more product
+        smac(sp[a], ul, uh, ((const __attribute__((address_space(4))) uint64_t *)B.negB)[t]);
+        const uint64_t r = sfinal_mod(sp[a], P);
         const uint32_t slot = (MODE == 0 && t >= ct.L) ? ct.l + (t - ct.L) : t;
         ob[(size_t)slot * n] = r;
     }
@@ -1093,6 +1105,7 @@ static int ks_moddown_conv(ckks_ctx *c, size_t nout, int l, const KsWs &w, hipSt
     LAUNCH_CHECK();
     {
         ConvTargets ct{(uint32_t)l, L, K, (size_t)l * n, 0};
+        // lay_dn.inner == 1: the summed sets are evenly spaced, as k_convert assumes
         ct.nsum = nsum;
         ct.sum_stride = (uint32_t)(nout / nsum * 2);
         // up to 4 parts: long summed workgroups need enough of them to fill the chip

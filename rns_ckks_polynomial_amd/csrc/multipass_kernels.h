@@ -223,7 +223,10 @@ __global__ __launch_bounds__(256) void k_inv_cols(Map map, uint32_t limb0, const
     inv(x, lds, v, t, tw + (size_t)prime * MP_N1 * 2, q);
     const uint64_t w = sc ? sc[0] : P.ninv, wp = sc ? sc[1] : P.ninvp;
 #pragma unroll
-    for (int k = 0; k < E; k++) dst[(size_t)(t + 16 * k) * MP_N1 + c0 + v] = shoup(x[k], w, wp, q);
+    for (int k = 0; k < E; k++) {
+        const uint64_t r = shoup(x[k], w, wp, q);
+        dst[(size_t)(t + 16 * k) * MP_N1 + c0 + v] = Map::split_out ? split30(r) : r;
+    }
 }
 
 }  // namespace mp

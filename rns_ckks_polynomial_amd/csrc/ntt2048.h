@@ -41,29 +41,6 @@ __device__ __forceinline__ int own(int t, int k) {
 
 __device__ __forceinline__ int brev(int i) { return (int)(__builtin_bitreverse32((uint32_t)i) >> (32 - LOGN)); }
 
-// Shoup product with the quotient floor(y wp / 2^64) truncated to the three
-// high 32x32 partial products: the dropped carries make it at most 2 too
-// small, so y w - Q q lands in [0, 4q) (instead of [0, 2q)) for any 64-bit y.
-// The remainder is formed as y w + Q (2^64 - q) mod 2^64 (nq = 2^64 - q), so
-// the subtraction rides on the multiply-adds.
-__device__ __forceinline__ uint64_t shoup_lazy4(uint64_t y, uint64_t w, uint64_t wp, uint64_t nq) {
-    const uint32_t yl = (uint32_t)y, yh = (uint32_t)(y >> 32);
-    const uint32_t pl = (uint32_t)wp, ph = (uint32_t)(wp >> 32);
-    const uint64_t qt = (uint64_t)yh * ph + ((uint64_t)__umulhi(yh, pl) + __umulhi(yl, ph));
-    const uint32_t ql = (uint32_t)qt, qh = (uint32_t)(qt >> 32);
-    const uint32_t wl = (uint32_t)w, wh = (uint32_t)(w >> 32);
-    const uint32_t nl = (uint32_t)nq, nh = (uint32_t)(nq >> 32);
-    const uint64_t r = (uint64_t)ql * nl + (uint64_t)yl * wl;  // mod 2^64
-    const uint32_t hi = (uint32_t)(r >> 32) + yl * wh + yh * wl + ql * nh + qh * nl;
-    return ((uint64_t)hi << 32) | (uint32_t)r;
-}
-
-// x - c if x >= c else x, for x, c < 2^62 (nc = 2^64 - c): add, then select on the sign.
-__device__ __forceinline__ uint64_t csub_sign(uint64_t x, uint64_t nc) {
-    const uint64_t m = x + nc;
-    return (int64_t)m < 0 ? x : m;
-}
-
 __device__ __forceinline__ void bf_ct(uint64_t &x, uint64_t &y, uint64_t w, uint64_t wp, uint64_t q) {
     const uint64_t q4 = 4 * q;
     const uint64_t a = csub_sign(x, 0 - q4);      // [0, 4q)
