@@ -183,6 +183,12 @@ __device__ __forceinline__ void sfold60(Split3 &s, const PrimeConsts &P) {
     s.a1 += r >> 30;
     s.a2 = 0;
 }
+__device__ __forceinline__ void sfold60(Split3c &s, const PrimeConsts &P) {
+    const uint64_t r = shoup_lazy(s.a2, P.r60, P.r60p, P.q);
+    s.a0 += r & M30;
+    s.a1 += r >> 30;
+    s.a2 = 0;
+}
 
 // Two-level normalisation for long Split3 sums (base conversion): snorm0
 // moves a0's carries into a1 (due every 15 products: a0 < 2^30 afterwards);

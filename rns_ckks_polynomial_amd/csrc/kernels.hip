@@ -926,15 +926,21 @@ __global__ __launch_bounds__(256) void k_bsgs_mac(const uint64_t *__restrict__ p
         const uint32_t bb = x / MAC_K, kk = x % MAC_K;
         return pt + ((size_t)g * bs + b0 + min(bb, nb - 1)) * pstride + (size_t)i * n + k0 + kk;
     };
-    uint64_t st0 = *pt_addr(0, threadIdx.x), st1 = *pt_addr(0, threadIdx.x + 256);
-    for (uint32_t g = 0; g < gs; g++) {
+    // diagonal tiles are prefetched two giant steps ahead (registers a: even g, b: odd g)
+    uint64_t a0 = *pt_addr(0, threadIdx.x), a1 = *pt_addr(0, threadIdx.x + 256);
+    uint64_t b0v = 0, b1v = 0;
+    if (gs > 1) {
+        b0v = *pt_addr(1, threadIdx.x);
+        b1v = *pt_addr(1, threadIdx.x + 256);
+    }
+    auto step = [&](uint32_t g, uint64_t &s0, uint64_t &s1) {
         uint64_t *buf = ps[g & 1];
-        buf[threadIdx.x] = split30(st0);  // stored split: low 30 bits | high 30 bits << 32
-        buf[threadIdx.x + 256] = split30(st1);
+        buf[threadIdx.x] = split30(s0);  // stored split: low 30 bits | high 30 bits << 32
+        buf[threadIdx.x + 256] = split30(s1);
         __syncthreads();
-        if (g + 1 < gs) {  // prefetch the next giant step's diagonals
-            st0 = *pt_addr(g + 1, threadIdx.x);
-            st1 = *pt_addr(g + 1, threadIdx.x + 256);
+        if (g + 2 < gs) {
+            s0 = *pt_addr(g + 2, threadIdx.x);
+            s1 = *pt_addr(g + 2, threadIdx.x + 256);
         }
         Split3c sp{0, 0, 0};
 #pragma unroll
@@ -950,6 +956,11 @@ __global__ __launch_bounds__(256) void k_bsgs_mac(const uint64_t *__restrict__ p
             if (b0) v = addm(v, *o, P.q);
             *o = v;
         }
+    };
+    // the LDS buffer of step g is rewritten at step g + 2, after the barrier of step g + 1
+    for (uint32_t g = 0; g < gs; g += 2) {
+        step(g, a0, a1);
+        if (g + 1 < gs) step(g + 1, b0v, b1v);
     }
 }
 
