@@ -101,7 +101,7 @@ def cpu_baseline(budget_s: float):
         o.mul_tensor_relin(a, b, key, L)
         done += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or done >= 200:
+        if el >= budget_s or done >= 2000:
             break
     threads = int(os.environ.get("OMP_NUM_THREADS", 0)) or os.cpu_count() or 1
     return {"value": done / el, "unit": "key-switches/s", "cores": threads, "kind": "oracle",
