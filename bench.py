@@ -109,6 +109,28 @@ def cpu_baseline(budget_s: float):
                       f"{el:.1f} s, OpenMP over limbs/coefficients"}
 
 
+EM_DEGREE, EM_ANGLES, EM_K = 31, 3, 8.0
+
+
+def eval_mod_timing(g, x, rlk, torch, reps: int = 3):
+    import numpy as np
+    from numpy.polynomial import chebyshev as C
+    cheb = C.chebinterpolate(lambda u: np.cos(2 * np.pi * (EM_K * u - 0.25) / 2 ** EM_ANGLES), EM_DEGREE)
+    ws = g.workspace(g.workspace_size("evalmod", BATCH, L, EM_DEGREE))
+    out, _ = g.eval_mod(x, 2.0 ** 59, cheb, EM_K, EM_ANGLES, 1 / (2 * np.pi), rlk, ws=ws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.eval_mod(x, 2.0 ** 59, cheb, EM_K, EM_ANGLES, 1 / (2 * np.pi), rlk, out=out, ws=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"ms_per_batch": ms, "ciphertexts_per_s": BATCH / (ms * 1e-3),
+            "config": f"batch {BATCH}, level {L} -> {out.shape[2]}, degree {EM_DEGREE} Chebyshev cosine on "
+                      f"[-{EM_K:g}, {EM_K:g}], {EM_ANGLES} double angles, scale 2^59, {EM_DEGREE + EM_ANGLES - 1} "
+                      f"ct x ct products per ciphertext"}
+
+
 def kernel_work():
     """Algorithmic work of each kernel per benchmark step (all launches of that
     kernel in one step; launches differ in size since BSGS batches its steps).
@@ -226,6 +248,10 @@ def main():
     limbs = BATCH * 2 * L
     ntt_rate = limbs / (ntt_ms * 1e-3)
 
+    # EvalMod (bootstrapping's modular reduction, outside the step): batch 8 at
+    # the 112-prime level, degree-31 cosine interpolant on [-8, 8], 3 double angles
+    em = eval_mod_timing(g, a, rlk, torch)
+
     # per-kernel launch times (library event profiler) over profiled steps + the NTT pair
     g.profile_begin()
     for _ in range(args.profile_steps):
@@ -289,6 +315,7 @@ def main():
                                "and BSGS 32x32 linear transform + rescale at 112 primes (config 3)",
                    "global_batch": BATCH, "parallelism": "single GPU"},
         "key_switches_per_step": ks_per_step,
+        "eval_mod": em,
         "limb_ntts_per_s": ntt_rate,
         "linear_transforms_per_s": BATCH / (bsgs_ms * 1e-3),
         "ct_mults_per_s": BATCH / (mr_ms * 1e-3),

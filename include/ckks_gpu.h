@@ -90,6 +90,7 @@ const char *ckks_strerror(int code);
 #define CKKS_OP_ROTATE 2
 #define CKKS_OP_RESCALE 3
 #define CKKS_OP_BSGS 4
+#define CKKS_OP_EVALMOD 5 /* bs = Chebyshev degree */
 int ckks_workspace_size(const ckks_ctx *ctx, int op, int batch, int level, int bs, int gs, size_t *bytes);
 
 /* Forward / inverse negacyclic NTT, in place, of `count` polynomials of
@@ -140,6 +141,38 @@ int ckks_bsgs_linear_transform(const ckks_ctx *ctx, const uint64_t *in, uint64_t
                                const uint64_t *diags, int bs, int gs, const uint64_t *const *baby_keys,
                                const uint64_t *const *giant_keys, int do_rescale, void *ws, size_t ws_bytes,
                                void *stream);
+
+/* EvalMod: the modular-reduction stage of bootstrapping (sin_fold_re /
+ * sin_fold_im of the Kestrel article's section 5.3 boot profile, the second
+ * largest bootstrap cost there), on real slot values x in [-K, K]:
+ *   u = x / K,   p = sum_{k<=degree} cheb[k] T_k(u)   (Chebyshev basis),
+ *   y = p, then y <- 2 y^2 - 1 (double_angles times),   out = out_factor y.
+ * With cheb the interpolant of cos(2 pi (K u - 1/4) / 2^double_angles) on
+ * [-1, 1] and out_factor = 1 / (2 pi), out ~ sin(2 pi x) / (2 pi).
+ * Exact schedule (every step a ciphertext operation; s(.) = tracked scale,
+ * q_j = chain prime j, const(c, t) = the integer nearest c t, ties to even):
+ *   CMul(a, c): multiply by const(c, q_{l_a - 1}), rescale; scale kept;
+ *   Mul(a, b): both truncated to the lower level m, tensor + relinearise,
+ *     rescale; scale s(a) s(b) / q_{m-1};
+ *   T_1 = CMul(in, 1/K); T_2j = 2 Mul(T_j, T_j) + const(-1, s);
+ *   T_2j+1 = 2 Mul(T_j, T_j+1) - T_1 (truncated); scale that of the Mul;
+ *   p: with m = level of T_degree, sum_k const(cheb[k], q_{m-1}) T_k (each
+ *     truncated to m), rescale, scale s(T_degree), then + const(cheb[0], s);
+ *   y <- 2 Mul(y, y) + const(-1, s(Mul));  out = CMul(y, out_factor).
+ * Constants enter c0 of the NTT-domain ciphertext in every coefficient.
+ * Levels consumed: 3 + ceil(log2 degree) + double_angles; out is written at
+ * level *level_out = level minus that, scale *scale_out.  The scales stay
+ * near scale_in only if scale_in is close to the chain primes (e.g. 2^59 for
+ * primes just above 2^59).  in: [batch][2][level][n]; out:
+ * [batch][2][*level_out][n] (may alias in); cheb: host array of degree + 1
+ * doubles, |cheb[k]| < 2; 0.5 <= K; |out_factor| < 2; 1 <= degree <= 1024;
+ * 0 <= double_angles <= 64; scale_in in (0, 2^61); rlk as
+ * ckks_mul_tensor_relin.  Returns CKKS_EINVAL (after queuing the work) if a
+ * constant times its scale reaches 2^62, the output then being invalid. */
+int ckks_eval_mod(const ckks_ctx *ctx, const uint64_t *in, uint64_t *out, int batch, int level, double scale_in,
+                  const double *cheb, int degree, double bound_k, int double_angles, double out_factor,
+                  const uint64_t *rlk, void *ws, size_t ws_bytes, double *scale_out, int *level_out,
+                  void *stream);
 
 #ifdef __cplusplus
 }

@@ -8,7 +8,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libckksgpu.so")
 
-OPS = {"relin": 1, "rotate": 2, "rescale": 3, "bsgs": 4}
+OPS = {"relin": 1, "rotate": 2, "rescale": 3, "bsgs": 4, "evalmod": 5}
 ERRORS = {0: "ok", -1: "invalid argument", -2: "level out of range", -3: "device allocation failed",
           -4: "HIP runtime error", -5: "misaligned pointer", -6: "workspace too small",
           -7: "unsupported parameters"}
@@ -52,6 +52,9 @@ SIGNATURES = {
     "ckks_bsgs_linear_transform": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p,
                                              C.c_int, C.c_int, C.POINTER(C.c_void_p), C.POINTER(C.c_void_p),
                                              C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "ckks_eval_mod": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_double,
+                                C.POINTER(C.c_double), C.c_int, C.c_double, C.c_int, C.c_double, C.c_void_p,
+                                C.c_void_p, C.c_size_t, C.POINTER(C.c_double), C.POINTER(C.c_int), C.c_void_p]),
     "ckks_profile_begin": (C.c_int, [C.c_void_p]),
     "ckks_profile_end": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.POINTER(C.c_int)]),
     "ckks_fill_uniform": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_uint64, C.c_uint64,

@@ -137,6 +137,25 @@ class Context:
                                                        _stream()), "ckks_bsgs_linear_transform")
         return out
 
+    def eval_mod(self, x, scale: float, cheb, bound_k: float, double_angles: int, out_factor: float,
+                 rlk, out=None, ws=None):
+        """EvalMod (see ckks_eval_mod): returns (out, out_scale); out has the
+        level ckks_eval_mod reports (the input level minus the depth)."""
+        B, _, l, n = x.shape
+        cheb = (C.c_double * len(cheb))(*[float(v) for v in cheb])
+        degree = len(cheb) - 1
+        ceil_log2 = max(0, (degree - 1).bit_length())
+        lo = l - (3 + ceil_log2 + double_angles)
+        out = torch.empty((B, 2, max(lo, 1), n), dtype=x.dtype, device=x.device) if out is None else out
+        ws, need = self._ws_for("evalmod", B, l, degree, ws=ws)
+        s_out, l_out = C.c_double(), C.c_int()
+        nat.check(nat.lib().ckks_eval_mod(self._h, _ptr(x), _ptr(out), B, l, float(scale), cheb, degree,
+                                          float(bound_k), int(double_angles), float(out_factor), _ptr(rlk),
+                                          _ptr(ws), ws.numel() * 8, C.byref(s_out), C.byref(l_out), _stream()),
+                  "ckks_eval_mod")
+        assert l_out.value == lo
+        return out, s_out.value
+
     # ------------------------------------------------------------ profiling
     def profile_begin(self):
         nat.check(nat.lib().ckks_profile_begin(self._h), "ckks_profile_begin")

@@ -1,4 +1,6 @@
 // capi.hip -- the extern "C" entry points: argument validation, then launch.
+#include <cmath>
+
 #include "../../include/ckks_gpu.h"
 #include "../../include/ckks_synth.h"
 #include "ctx_internal.h"
@@ -44,6 +46,10 @@ extern "C" int ckks_workspace_size(const ckks_ctx *c, int op, int batch, int lev
         case CKKS_OP_RESCALE:
             if (level < 2) return CKKS_ELEVEL;
             *bytes = ws_bytes_rescale(c, batch, level);
+            return CKKS_OK;
+        case CKKS_OP_EVALMOD:
+            if (!c->K || bs < 1 || bs > 1024) return CKKS_EINVAL;
+            *bytes = ws_bytes_eval_mod(c, batch, level, bs);
             return CKKS_OK;
         case CKKS_OP_BSGS:
             if (!c->K || bs < 1 || gs < 1) return CKKS_EINVAL;
@@ -160,4 +166,26 @@ extern "C" int ckks_fill_uniform(const ckks_ctx *c, uint64_t *dst, int count, in
     DeviceGuard g(c->device);
     if (!g.ok) return CKKS_EHIP;
     return op_fill_uniform(c, dst, count, first, nlimbs, seed, tag, stream0, (hipStream_t)stream);
+}
+
+extern "C" int ckks_eval_mod(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int batch, int level,
+                             double scale_in, const double *cheb, int degree, double bound_k, int double_angles,
+                             double out_factor, const uint64_t *rlk, void *ws, size_t ws_bytes, double *scale_out,
+                             int *level_out, void *stream) {
+    if (!c || !c->K || !cheb) return CKKS_EINVAL;
+    int e;
+    if ((e = check_ptr(in)) || (e = check_ptr(out)) || (e = check_ptr(rlk))) return e;
+    if (degree < 1 || degree > 1024 || double_angles < 0 || double_angles > 64) return CKKS_EINVAL;
+    if (!(bound_k >= 0.5 && bound_k < 1e9) || !(scale_in > 0 && scale_in < 0x1p61) ||
+        !(std::fabs(out_factor) < 2.0))
+        return CKKS_EINVAL;
+    for (int k = 0; k <= degree; k++)
+        if (!(std::fabs(cheb[k]) < 2.0)) return CKKS_EINVAL;
+    if ((e = check_level(c, batch, level, eval_mod_depth(degree, double_angles) + 1))) return e;
+    if (!ws || ws_bytes < ws_bytes_eval_mod(c, batch, level, degree)) return CKKS_EWORKSPACE;
+    if (!aligned(ws)) return CKKS_EALIGN;
+    DeviceGuard g(c->device);
+    if (!g.ok) return CKKS_EHIP;
+    return op_eval_mod(const_cast<ckks_ctx *>(c), in, out, batch, level, scale_in, cheb, degree, bound_k,
+                       double_angles, out_factor, rlk, ws, scale_out, level_out, (hipStream_t)stream);
 }

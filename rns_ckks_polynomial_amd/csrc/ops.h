@@ -22,6 +22,12 @@ int op_rotate(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, uint
               bool accumulate, hipStream_t s);
 int op_bsgs(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, const uint64_t *diags, int bs, int gs,
             const uint64_t *const *baby, const uint64_t *const *giant, bool rescale, void *ws, hipStream_t s);
+// EvalMod (Chebyshev cosine + double angles); levels consumed = eval_mod_depth(degree, double_angles).
+int eval_mod_depth(int degree, int double_angles);
+size_t ws_bytes_eval_mod(const ckks_ctx *c, int B, int l, int degree);
+int op_eval_mod(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, double scale_in, const double *cheb,
+                int degree, double bound_k, int double_angles, double out_factor, const uint64_t *rlk, void *ws,
+                double *scale_out, int *level_out, hipStream_t s);
 int op_fill_uniform(const ckks_ctx *c, uint64_t *dst, int count, int first, int nlimbs, uint64_t seed, uint64_t tag,
                     uint64_t stream0, hipStream_t s);
 
