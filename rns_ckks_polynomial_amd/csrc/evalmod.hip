@@ -127,11 +127,20 @@ int ceil_log2(int d) {
 
 int eval_mod_depth(int degree, int double_angles) { return 3 + ceil_log2(degree) + double_angles; }
 
+// Largest number of Chebyshev products in one generation (k in (2^(g-1), 2^g]).
+static int max_generation(int d) {
+    int m = 1;
+    for (int lo = 2; lo <= d; lo = 2 * lo - 1) m = std::max(m, std::min(2 * (lo - 1), d) - lo + 1);
+    return m;
+}
+
 size_t ws_bytes_eval_mod(const ckks_ctx *c, int B, int l, int degree) {
-    const size_t ct = (size_t)B * 2 * l * c->n * 8;
-    const size_t ks = std::max(ws_bytes_relin(c, B, l), ws_bytes_rescale(c, B, l));
-    // T_1..T_d, the running sum, the double-angle value, three scratch ciphertexts
-    return ((size_t)degree + 5) * ((ct + 255) & ~(size_t)255) + ks;
+    const size_t ct = ((size_t)B * 2 * l * c->n * 8 + 255) & ~(size_t)255;
+    const int G = max_generation(degree);
+    const size_t ks = std::max(ws_bytes_relin(c, G * B, l), ws_bytes_rescale(c, G * B, l));
+    // T_1..T_d, the running sum, the double-angle value, three scratch ciphertexts,
+    // and the stacked left / right factors and products of one generation
+    return ((size_t)degree + 5) * ct + 4 * (size_t)G * ct + ks;
 }
 
 int op_eval_mod(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, double scale_in, const double *cheb,
@@ -139,31 +148,49 @@ int op_eval_mod(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, do
                 double *scale_out, int *level_out, hipStream_t s) {
     const int d = degree;
     const size_t slot = (((size_t)B * 2 * l * c->n * 8) + 255) & ~(size_t)255;
+    const int G = max_generation(d);
     uint8_t *base = (uint8_t *)ws;
-    auto take = [&]() {
+    auto take = [&](size_t slots) {
         uint64_t *p = (uint64_t *)base;
-        base += slot;
+        base += slots * slot;
         return p;
     };
     std::vector<Ct> T(d + 1);
-    for (int k = 1; k <= d; k++) T[k].p = take();
-    Ct acc{take()}, y{take()};
-    Eval ev{c, B, rlk, take(), take(), take(), base, s};
+    for (int k = 1; k <= d; k++) T[k].p = take(1);
+    Ct acc{take(1)}, y{take(1)};
+    uint64_t *ta = take(1), *tb = take(1), *tp = take(1);
+    uint64_t *left = take(G), *right = take(G), *prod = take(G), *prod_r = take(G);
+    Eval ev{c, B, rlk, ta, tb, tp, base, s};
     int e;
     // u = x / K
     if ((e = ev.cmul_rescale(Ct{const_cast<uint64_t *>(in), l, scale_in}, 1.0 / bound_k, T[1]))) return e;
-    // T_2j = 2 T_j^2 - 1,  T_2j+1 = 2 T_j T_j+1 - T_1
-    for (int k = 2; k <= d; k++) {
-        const int j = k / 2;
-        Ct prod{T[k].p};
-        if ((e = ev.mul_rescale(T[j], k % 2 ? T[j + 1] : T[j], prod))) return e;
-        if (k % 2 == 0) {
-            if ((e = ev.lincomb(T[k].p, prod.l, prod, nullptr, 2, 0, ev.enc(-1.0, prod.s)))) return e;
-        } else {
-            if ((e = ev.lincomb(T[k].p, prod.l, prod, &T[1], 2, -1, 0))) return e;
+    // T_2j = 2 T_j^2 - 1,  T_2j+1 = 2 T_j T_j+1 - T_1, one generation k in
+    // (2^(g-1), 2^g] at a time: its products are independent and share the
+    // level T_1 - g + 1, so they go through one batched tensor + relinearise
+    // and one rescale (the residues are those of separate products)
+    for (int lo = 2, g = 1; lo <= d; lo = 2 * lo - 1, g++) {
+        const int hi = std::min(2 * (lo - 1), d), cnt = hi - lo + 1;
+        const int mu = T[1].l - (g - 1);
+        const size_t per = (size_t)B * 2 * mu * c->n;       // words of B ciphertexts at level mu
+        const size_t per_r = (size_t)B * 2 * (mu - 1) * c->n;
+        for (int k = lo; k <= hi; k++) {
+            const int j = k / 2, jr = k - j;
+            if ((e = ev.lincomb(left + (k - lo) * per, mu, T[j], nullptr, 1, 0, 0))) return e;
+            if ((e = ev.lincomb(right + (k - lo) * per, mu, T[jr], nullptr, 1, 0, 0))) return e;
         }
-        T[k].l = prod.l;
-        T[k].s = prod.s;
+        if ((e = op_mul_tensor_relin(c, left, right, rlk, prod, cnt * B, mu, ev.ks_ws, s))) return e;
+        if ((e = op_rescale(c, prod, prod_r, cnt * B, mu, ev.ks_ws, s))) return e;
+        for (int k = lo; k <= hi; k++) {
+            const int j = k / 2, jr = k - j;
+            const Ct pk{prod_r + (k - lo) * per_r, mu - 1, (T[j].s * T[jr].s) / ev.q(mu - 1)};
+            if (k % 2 == 0) {
+                if ((e = ev.lincomb(T[k].p, pk.l, pk, nullptr, 2, 0, ev.enc(-1.0, pk.s)))) return e;
+            } else {
+                if ((e = ev.lincomb(T[k].p, pk.l, pk, &T[1], 2, -1, 0))) return e;
+            }
+            T[k].l = pk.l;
+            T[k].s = pk.s;
+        }
     }
     // p = c_0 + sum_k c_k T_k: every T_k truncated to T_d's level, weighted by
     // c_k at the scale of the prime dropped next, one rescale; scale of T_d
