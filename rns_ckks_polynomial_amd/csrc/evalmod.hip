@@ -81,6 +81,7 @@ struct Eval {
     double q(int idx) const { return (double)c->primes[idx]; }
 
     int lincomb(uint64_t *out, int lo, const Ct &a, const Ct *b, int64_t ma, int64_t mb, int64_t add) {
+        ProfScope ps_(c, "eval_lincomb", s);
         hipLaunchKernelGGL(k_lincomb, dim3(B * 2 * lo), dim3(256), 0, s, a.p, (uint32_t)a.l, b ? b->p : nullptr,
                            b ? (uint32_t)b->l : 0u, out, (uint32_t)lo, c->n, ma, mb, add, c->d_pc);
         return hipGetLastError() == hipSuccess ? CKKS_OK : CKKS_EHIP;
