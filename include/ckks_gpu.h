@@ -91,6 +91,7 @@ const char *ckks_strerror(int code);
 #define CKKS_OP_RESCALE 3
 #define CKKS_OP_BSGS 4
 #define CKKS_OP_EVALMOD 5 /* bs = Chebyshev degree */
+#define CKKS_OP_MODRAISE 6 /* level = the source level */
 int ckks_workspace_size(const ckks_ctx *ctx, int op, int batch, int level, int bs, int gs, size_t *bytes);
 
 /* Forward / inverse negacyclic NTT, in place, of `count` polynomials of
@@ -142,6 +143,17 @@ int ckks_bsgs_linear_transform(const ckks_ctx *ctx, const uint64_t *in, uint64_t
                                const uint64_t *const *giant_keys, int do_rescale, void *ws, size_t ws_bytes,
                                void *stream);
 
+/* ModRaise, the first step of bootstrapping (modraise in the Kestrel
+ * article's section 5.3 boot profile: a ciphertext down to 19 primes is
+ * raised to 2100): every coefficient of both polynomials is lifted exactly to
+ * its centered representative modulo q_0 ... q_{level_in - 1} and reduced
+ * modulo q_0 ... q_{level_out - 1}.  The plaintext becomes m + (q_0...) I
+ * for a small integer polynomial I, which EvalMod later removes.  in:
+ * [batch][2][level_in][n] (NTT domain); out: [batch][2][level_out][n]; no
+ * aliasing; level_in <= min(level_out, 1000). */
+int ckks_mod_raise(const ckks_ctx *ctx, const uint64_t *in, uint64_t *out, int batch, int level_in, int level_out,
+                   void *ws, size_t ws_bytes, void *stream);
+
 /* EvalMod: the modular-reduction stage of bootstrapping (sin_fold_re /
  * sin_fold_im of the Kestrel article's section 5.3 boot profile, the second
  * largest bootstrap cost there), on real slot values x in [-K, K]:
@@ -173,6 +185,48 @@ int ckks_eval_mod(const ckks_ctx *ctx, const uint64_t *in, uint64_t *out, int ba
                   const double *cheb, int degree, double bound_k, int double_angles, double out_factor,
                   const uint64_t *rlk, void *ws, size_t ws_bytes, double *scale_out, int *level_out,
                   void *stream);
+
+/* Bootstrapping (the boot of the Kestrel article's section 5.3, with its
+ * stages modraise, coeff_to_slot, conj_extract, sin_fold_re / sin_fold_im,
+ * restore_merge, slot_to_coeff):
+ *   r  = ModRaise(in, level_in -> level_raise);
+ *   w  = BSGS(r, cts_diags) with rescale                (coeff_to_slot);
+ *   re = CMul(w + conj(w), 1/2),  im = CMul((w - conj(w)) X^(n/2), -1/2)
+ *        (conj = rotation by g = 2n - 1 with conj_key; CMul as ckks_eval_mod;
+ *        X^(n/2) multiplies the slots by the imaginary unit)  (conj_extract);
+ *   re', im' = EvalMod of both (one call on 2 batch ciphertexts, input scale
+ *        evalmod_scale, parameters as ckks_eval_mod)    (sin_fold);
+ *   v  = re' + im' X^(n/2)                               (restore_merge);
+ *   out = BSGS(v, stc_diags) with rescale                (slot_to_coeff).
+ * Both transforms use bs x gs steps and the same rotation keys (as
+ * ckks_bsgs_linear_transform).  The caller builds the diagonals (the slot
+ * <-> coefficient matrices with their scale factors) and the EvalMod
+ * constants.  Output level *level_out = level_raise - 3 - (3 + ceil(log2
+ * degree) + double_angles); *scale_mid = the EvalMod output scale (the scale
+ * entering slot_to_coeff).  in: [batch][2][level_in][n]; cts_diags:
+ * [gs][bs][level_raise][n]; stc_diags: [gs][bs][*level_out + 1][n]; out:
+ * [batch][2][*level_out][n]; no aliasing. */
+typedef struct {
+    int level_raise;
+    const uint64_t *cts_diags;
+    const uint64_t *stc_diags;
+    int bs, gs;
+    const uint64_t *const *baby_keys;
+    const uint64_t *const *giant_keys;
+    const uint64_t *conj_key;
+    const uint64_t *rlk;
+    double evalmod_scale;
+    const double *cheb;
+    int degree;
+    double bound_k;
+    int double_angles;
+    double out_factor;
+} ckks_boot_params;
+int ckks_bootstrap_workspace_size(const ckks_ctx *ctx, int batch, int level_in, const ckks_boot_params *params,
+                                  size_t *bytes);
+int ckks_bootstrap(const ckks_ctx *ctx, const uint64_t *in, uint64_t *out, int batch, int level_in,
+                   const ckks_boot_params *params, void *ws, size_t ws_bytes, double *scale_mid, int *level_out,
+                   void *stream);
 
 #ifdef __cplusplus
 }

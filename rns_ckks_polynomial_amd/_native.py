@@ -8,7 +8,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libckksgpu.so")
 
-OPS = {"relin": 1, "rotate": 2, "rescale": 3, "bsgs": 4, "evalmod": 5}
+OPS = {"relin": 1, "rotate": 2, "rescale": 3, "bsgs": 4, "evalmod": 5, "modraise": 6}
 ERRORS = {0: "ok", -1: "invalid argument", -2: "level out of range", -3: "device allocation failed",
           -4: "HIP runtime error", -5: "misaligned pointer", -6: "workspace too small",
           -7: "unsupported parameters"}
@@ -18,6 +18,15 @@ class CkksError(RuntimeError):
     def __init__(self, code: int, where: str):
         super().__init__(f"{where}: {ERRORS.get(code, 'error')} ({code})")
         self.code = code
+
+
+class BootParams(C.Structure):
+    """ckks_boot_params (include/ckks_gpu.h)."""
+    _fields_ = [("level_raise", C.c_int), ("cts_diags", C.c_void_p), ("stc_diags", C.c_void_p),
+                ("bs", C.c_int), ("gs", C.c_int), ("baby_keys", C.POINTER(C.c_void_p)),
+                ("giant_keys", C.POINTER(C.c_void_p)), ("conj_key", C.c_void_p), ("rlk", C.c_void_p),
+                ("evalmod_scale", C.c_double), ("cheb", C.POINTER(C.c_double)), ("degree", C.c_int),
+                ("bound_k", C.c_double), ("double_angles", C.c_int), ("out_factor", C.c_double)]
 
 
 class KernelStat(C.Structure):
@@ -55,6 +64,12 @@ SIGNATURES = {
     "ckks_eval_mod": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_double,
                                 C.POINTER(C.c_double), C.c_int, C.c_double, C.c_int, C.c_double, C.c_void_p,
                                 C.c_void_p, C.c_size_t, C.POINTER(C.c_double), C.POINTER(C.c_int), C.c_void_p]),
+    "ckks_mod_raise": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p,
+                                 C.c_size_t, C.c_void_p]),
+    "ckks_bootstrap_workspace_size": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_void_p,
+                                                C.POINTER(C.c_size_t)]),
+    "ckks_bootstrap": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_void_p,
+                                 C.c_size_t, C.POINTER(C.c_double), C.POINTER(C.c_int), C.c_void_p]),
     "ckks_profile_begin": (C.c_int, [C.c_void_p]),
     "ckks_profile_end": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.POINTER(C.c_int)]),
     "ckks_fill_uniform": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_uint64, C.c_uint64,

@@ -137,6 +137,38 @@ class Context:
                                                        _stream()), "ckks_bsgs_linear_transform")
         return out
 
+    def mod_raise(self, x, level_out: int, out=None, ws=None):
+        """ModRaise (see ckks_mod_raise): [B][2][l][n] -> [B][2][level_out][n]."""
+        B, _, l, n = x.shape
+        out = torch.empty((B, 2, level_out, n), dtype=x.dtype, device=x.device) if out is None else out
+        ws, need = self._ws_for("modraise", B, l, ws=ws)
+        nat.check(nat.lib().ckks_mod_raise(self._h, _ptr(x), _ptr(out), B, l, level_out, _ptr(ws), ws.numel() * 8,
+                                           _stream()), "ckks_mod_raise")
+        return out
+
+    def bootstrap(self, x, level_raise: int, cts_diags, stc_diags, bs: int, gs: int, baby_keys, giant_keys,
+                  conj_key, rlk, evalmod_scale: float, cheb, bound_k: float, double_angles: int,
+                  out_factor: float, out=None, ws=None):
+        """Bootstrapping (see ckks_bootstrap): returns (out, scale entering slot_to_coeff)."""
+        B, _, l0, n = x.shape
+        cheb_c = (C.c_double * len(cheb))(*[float(v) for v in cheb])
+        bk = (C.c_void_p * bs)(*[None if k is None else _ptr(k) for k in baby_keys])
+        gk = (C.c_void_p * gs)(*[None if k is None else _ptr(k) for k in giant_keys])
+        p = nat.BootParams(level_raise, _ptr(cts_diags), _ptr(stc_diags), bs, gs, bk, gk, _ptr(conj_key), _ptr(rlk),
+                           float(evalmod_scale), cheb_c, len(cheb) - 1, float(bound_k), int(double_angles),
+                           float(out_factor))
+        need = C.c_size_t()
+        nat.check(nat.lib().ckks_bootstrap_workspace_size(self._h, B, l0, C.byref(p), C.byref(need)),
+                  "ckks_bootstrap_workspace_size")
+        ws = self.workspace(need.value) if ws is None else ws
+        lo = level_raise - 3 - (3 + max(0, (len(cheb) - 2).bit_length()) + double_angles)
+        out = torch.empty((B, 2, lo, n), dtype=x.dtype, device=x.device) if out is None else out
+        s_mid, l_out = C.c_double(), C.c_int()
+        nat.check(nat.lib().ckks_bootstrap(self._h, _ptr(x), _ptr(out), B, l0, C.byref(p), _ptr(ws), ws.numel() * 8,
+                                           C.byref(s_mid), C.byref(l_out), _stream()), "ckks_bootstrap")
+        assert l_out.value == lo
+        return out, s_mid.value
+
     def eval_mod(self, x, scale: float, cheb, bound_k: float, double_angles: int, out_factor: float,
                  rlk, out=None, ws=None):
         """EvalMod (see ckks_eval_mod): returns (out, out_scale); out has the

@@ -47,6 +47,9 @@ extern "C" int ckks_workspace_size(const ckks_ctx *c, int op, int batch, int lev
             if (level < 2) return CKKS_ELEVEL;
             *bytes = ws_bytes_rescale(c, batch, level);
             return CKKS_OK;
+        case CKKS_OP_MODRAISE:
+            *bytes = ws_bytes_mod_raise(c, batch, level);
+            return CKKS_OK;
         case CKKS_OP_EVALMOD:
             if (!c->K || bs < 1 || bs > 1024) return CKKS_EINVAL;
             *bytes = ws_bytes_eval_mod(c, batch, level, bs);
@@ -188,4 +191,72 @@ extern "C" int ckks_eval_mod(const ckks_ctx *c, const uint64_t *in, uint64_t *ou
     if (!g.ok) return CKKS_EHIP;
     return op_eval_mod(const_cast<ckks_ctx *>(c), in, out, batch, level, scale_in, cheb, degree, bound_k,
                        double_angles, out_factor, rlk, ws, scale_out, level_out, (hipStream_t)stream);
+}
+
+extern "C" int ckks_mod_raise(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int batch, int level_in,
+                              int level_out, void *ws, size_t ws_bytes, void *stream) {
+    if (!c) return CKKS_EINVAL;
+    int e;
+    if ((e = check_ptr(in)) || (e = check_ptr(out))) return e;
+    if ((e = check_level(c, batch, level_in, 1))) return e;
+    if (level_out < level_in || (uint32_t)level_out > c->L || level_in > 1000) return CKKS_ELEVEL;
+    if (in == out) return CKKS_EINVAL;
+    if (!ws || ws_bytes < ws_bytes_mod_raise(c, batch, level_in)) return CKKS_EWORKSPACE;
+    if (!aligned(ws)) return CKKS_EALIGN;
+    DeviceGuard g(c->device);
+    if (!g.ok) return CKKS_EHIP;
+    return op_mod_raise(const_cast<ckks_ctx *>(c), in, out, batch, level_in, level_out, ws, (hipStream_t)stream);
+}
+
+namespace {
+int check_boot(const ckks_ctx *c, int batch, int level_in, const ckks_boot_params *p) {
+    if (!c || !c->K || !p || batch < 1) return CKKS_EINVAL;
+    int e;
+    if ((e = check_ptr(p->cts_diags)) || (e = check_ptr(p->stc_diags)) || (e = check_ptr(p->conj_key)) ||
+        (e = check_ptr(p->rlk)))
+        return e;
+    if (p->bs < 1 || p->gs < 1 || (uint64_t)p->bs * p->gs > c->n / 2) return CKKS_EINVAL;
+    if ((p->bs > 1 && !p->baby_keys) || (p->gs > 1 && !p->giant_keys)) return CKKS_EINVAL;
+    for (int b = 1; b < p->bs; b++)
+        if ((e = check_ptr(p->baby_keys[b]))) return e;
+    for (int g = 1; g < p->gs; g++)
+        if ((e = check_ptr(p->giant_keys[g]))) return e;
+    if (!p->cheb || p->degree < 1 || p->degree > 1024 || p->double_angles < 0 || p->double_angles > 64)
+        return CKKS_EINVAL;
+    if (!(p->bound_k >= 0.5 && p->bound_k < 1e9) || !(p->evalmod_scale > 0 && p->evalmod_scale < 0x1p61) ||
+        !(std::fabs(p->out_factor) < 2.0))
+        return CKKS_EINVAL;
+    for (int k = 0; k <= p->degree; k++)
+        if (!(std::fabs(p->cheb[k]) < 2.0)) return CKKS_EINVAL;
+    if (level_in < 1 || level_in > 1000 || level_in > p->level_raise || (uint32_t)p->level_raise > c->L)
+        return CKKS_ELEVEL;
+    int lo = 0;
+    boot_levels(p, &lo);
+    if (lo < 1) return CKKS_ELEVEL;
+    return CKKS_OK;
+}
+}  // namespace
+
+extern "C" int ckks_bootstrap_workspace_size(const ckks_ctx *c, int batch, int level_in,
+                                             const ckks_boot_params *p, size_t *bytes) {
+    int e;
+    if (!bytes) return CKKS_EINVAL;
+    if ((e = check_boot(c, batch, level_in, p))) return e;
+    *bytes = ws_bytes_bootstrap(c, batch, level_in, p);
+    return CKKS_OK;
+}
+
+extern "C" int ckks_bootstrap(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int batch, int level_in,
+                              const ckks_boot_params *p, void *ws, size_t ws_bytes, double *scale_mid,
+                              int *level_out, void *stream) {
+    int e;
+    if ((e = check_boot(c, batch, level_in, p))) return e;
+    if ((e = check_ptr(in)) || (e = check_ptr(out))) return e;
+    if (in == out) return CKKS_EINVAL;
+    if (!ws || ws_bytes < ws_bytes_bootstrap(c, batch, level_in, p)) return CKKS_EWORKSPACE;
+    if (!aligned(ws)) return CKKS_EALIGN;
+    DeviceGuard g(c->device);
+    if (!g.ok) return CKKS_EHIP;
+    if (level_out) boot_levels(p, level_out);
+    return op_bootstrap(const_cast<ckks_ctx *>(c), in, out, batch, level_in, p, ws, scale_mid, (hipStream_t)stream);
 }

@@ -115,7 +115,8 @@ static uint64_t big_divmod(std::vector<uint64_t> &a, uint64_t m) {  // a /= m, r
     return (uint64_t)r;
 }
 
-int build_basis(ckks_ctx *ctx, uint32_t first, uint32_t m, BasisDev *out, std::vector<void *> &owned) {
+int build_basis(ckks_ctx *ctx, uint32_t first, uint32_t m, BasisDev *out, std::vector<void *> &owned,
+                bool chain_targets) {
     const uint32_t ntot = ctx->L + ctx->K;
     const uint64_t *b = ctx->primes.data() + first;
     std::vector<uint64_t> inv_hat(2 * m), hat_mod(2 * m), R(m), H((size_t)ntot * m), negB(ntot),
@@ -165,7 +166,7 @@ int build_basis(ckks_ctx *ctx, uint32_t first, uint32_t m, BasisDev *out, std::v
     // the conversion kernels read H transposed, in target-position order and in
     // the split layout (lo32 = h mod 2^30, hi32 = h >> 30)
     std::vector<uint32_t> pos;  // position -> target prime
-    if (first < ctx->L) {
+    if (first < ctx->L && !chain_targets) {
         for (uint32_t t = ctx->L; t < ntot; t++) pos.push_back(t);
         for (uint32_t t = 0; t < ctx->L; t++)
             if (t < first || t >= first + m) pos.push_back(t);
@@ -259,6 +260,36 @@ LevelTables *level_tables(ckks_ctx *ctx, uint32_t l, int *err) {
     return lt;
 }
 
+RaiseTables *raise_tables(ckks_ctx *ctx, uint32_t l0, int *err) {
+    std::lock_guard<std::mutex> g(ctx->mu);
+    auto it = ctx->raise.find(l0);
+    if (it != ctx->raise.end()) return it->second;
+    int dev_saved = 0;
+    hipGetDevice(&dev_saved);
+    hipSetDevice(ctx->device);
+    RaiseTables *rt = new RaiseTables();
+    BasisDev bd{};
+    *err = build_basis(ctx, 0, l0, &bd, rt->owned, true);
+    std::vector<uint64_t> ih(2 * l0), sc(2 * l0);
+    if (!*err) hipMemcpy(ih.data(), bd.inv_hat, ih.size() * 8, hipMemcpyDeviceToHost);
+    for (uint32_t i = 0; i < l0; i++) {
+        const uint64_t q = ctx->primes[i], v = h_mulmod(h_invmod(ctx->n % q, q), ih[2 * i], q);
+        sc[2 * i] = v;
+        sc[2 * i + 1] = h_shoup(v, q);
+    }
+    std::vector<BasisDev> one(1, bd);
+    if (!*err) rt->d_basis = dev_upload(one, rt->owned, err);
+    if (!*err) rt->d_scale = dev_upload(sc, rt->owned, err);
+    hipSetDevice(dev_saved);
+    if (*err != CKKS_OK) {
+        for (void *p : rt->owned) hipFree(p);
+        delete rt;
+        return nullptr;
+    }
+    ctx->raise[l0] = rt;
+    return rt;
+}
+
 }  // namespace ckks
 
 using namespace ckks;
@@ -292,7 +323,7 @@ extern "C" int ckks_ctx_create(ckks_ctx **out, const ckks_params *params, int de
     if (!err) {
         c->psi.resize(ntot);
         std::vector<PrimeConsts> pc(ntot);
-        std::vector<uint64_t> twf((size_t)ntot * n * 2), twi((size_t)ntot * n * 2);
+        std::vector<uint64_t> twf((size_t)ntot * n * 2), twi((size_t)ntot * n * 2), iota(ntot);
         for (uint32_t g = 0; g < ntot; g++) {
             const uint64_t q = c->primes[g];
             const uint64_t psi = h_min_root(n, q), ipsi = h_invmod(psi, q);
@@ -314,6 +345,7 @@ extern "C" int ckks_ctx_create(ckks_ctx **out, const ckks_params *params, int de
                 fp[e] = pw;
                 ip[e] = ipw;
             }
+            iota[g] = fp[n / 2];  // psi^(n/2): a square root of -1
             uint64_t *tf = twf.data() + (size_t)g * n * 2, *ti = twi.data() + (size_t)g * n * 2;
             for (uint32_t k2 = 0; k2 < n; k2++) {
                 uint32_t e = h_bitrev(k2, c->logn);
@@ -326,6 +358,7 @@ extern "C" int ckks_ctx_create(ckks_ctx **out, const ckks_params *params, int de
         c->d_pc = dev_upload(pc, c->owned, &err);
         c->d_tw_fwd = dev_upload(twf, c->owned, &err);
         c->d_tw_inv = dev_upload(twi, c->owned, &err);
+        c->d_iota = dev_upload(iota, c->owned, &err);
     }
     if (!err && p.K > 0) {
         // full digits at the top level, the special-prime basis and its constants
@@ -376,6 +409,10 @@ extern "C" void ckks_ctx_destroy(ckks_ctx *c) {
     hipSetDevice(c->device);
     hipDeviceSynchronize();
     for (auto &kv : c->levels) {
+        for (void *p : kv.second->owned) hipFree(p);
+        delete kv.second;
+    }
+    for (auto &kv : c->raise) {
         for (void *p : kv.second->owned) hipFree(p);
         delete kv.second;
     }

@@ -24,6 +24,14 @@ struct LevelTables {
     std::vector<void *> owned;          // device allocations owned by this level
 };
 
+// ModRaise tables for a source level l0: the basis of primes [0, l0) with
+// every chain prime as a target, and n^-1 [Bhat_i^-1]_{q_i} (Shoup pairs).
+struct RaiseTables {
+    BasisDev *d_basis = nullptr;
+    uint64_t *d_scale = nullptr;  // [l0][2]
+    std::vector<void *> owned;
+};
+
 struct MultipassPlan;  // large-n NTT tables (n > 2048)
 
 // Optional per-launch timing with HIP events (enabled by ckks_profile_begin).
@@ -51,6 +59,7 @@ struct ckks_ctx {
     ckks::PrimeConsts *d_pc = nullptr;  // [L+K]
     uint64_t *d_tw_fwd = nullptr;       // [L+K][n][2]  psi^bitrev(k), Shoup
     uint64_t *d_tw_inv = nullptr;       // [L+K][n][2]  psi^-bitrev(k), Shoup
+    uint64_t *d_iota = nullptr;         // [L+K]        psi^(n/2), the NTT of X^(n/2) is iota (-1)^k
     // base of the special primes P (targets: every chain prime)
     ckks::BasisDev h_pbasis{};
     ckks::BasisDev *d_pbasis = nullptr;
@@ -61,6 +70,7 @@ struct ckks_ctx {
     std::vector<ckks::BasisDev> full_digits;
     std::vector<void *> owned;
     std::map<uint32_t, ckks::LevelTables *> levels;
+    std::map<uint32_t, ckks::RaiseTables *> raise;  // ModRaise tables by source level
     std::mutex mu;
     ckks::MultipassPlan *mp = nullptr;
     ckks::Profiler *prof = nullptr;
@@ -98,6 +108,11 @@ uint64_t h_shoup(uint64_t w, uint64_t q);
 
 // Fetch (building on first use) the level tables.  Returns nullptr on failure.
 LevelTables *level_tables(ckks_ctx *ctx, uint32_t l, int *err);
+// Fetch (building on first use) the ModRaise tables of source level l0.  nullptr on failure.
+RaiseTables *raise_tables(ckks_ctx *ctx, uint32_t l0, int *err);
 // Build a basis table for primes [first, first + m) with every chain prime as target.
-int build_basis(ckks_ctx *ctx, uint32_t first, uint32_t m, BasisDev *out, std::vector<void *> &owned);
+// chain_targets: lay the conversion table over the chain primes [0, L) (as for
+// the special primes) instead of specials-first-then-outside-the-digit.
+int build_basis(ckks_ctx *ctx, uint32_t first, uint32_t m, BasisDev *out, std::vector<void *> &owned,
+                bool chain_targets = false);
 }  // namespace ckks

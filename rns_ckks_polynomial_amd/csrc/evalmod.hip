@@ -26,25 +26,41 @@ __device__ __forceinline__ uint64_t smod(int64_t v, uint64_t q) {
     return (v < 0 && u) ? q - u : u;
 }
 
-// out[p][i][k] = ma a[p][i][k] + mb b[p][i][k] + (p even ? add : 0)  mod q_i,
+// out[p][i][k] = ma a[p][i][k] + mb b'[p][i][k] + (p even ? add : 0)  mod q_i,
 // for polynomials p (2 per ciphertext: even = c0) and limbs i < lo; a has la
 // limbs per polynomial, b lb (b may be null), so inputs above level lo are
-// read truncated.  In the NTT domain a constant polynomial is the constant in
-// every coefficient, so `add` adds a plaintext constant.  out may alias a.
+// read truncated.  b' = b, or with iota (psi_i^(n/2) per prime) b X^(n/2),
+// whose NTT is b[k] iota (-1)^k: multiplying the slots by the imaginary unit.
+// In the NTT domain a constant polynomial is the constant in every
+// coefficient, so `add` adds a plaintext constant.  out may alias a or b.
 __global__ __launch_bounds__(256) void k_lincomb(const uint64_t *a, uint32_t la, const uint64_t *b, uint32_t lb,
                                                  uint64_t *out, uint32_t lo, uint32_t n, int64_t ma, int64_t mb,
-                                                 int64_t add, const PrimeConsts *__restrict__ pc) {
+                                                 int64_t add, const uint64_t *__restrict__ iota,
+                                                 const PrimeConsts *__restrict__ pc) {
     const uint32_t i = blockIdx.x % lo, poly = blockIdx.x / lo;
     const PrimeConsts P = pc[i];
-    const uint64_t wa = smod(ma, P.q), wb = smod(mb, P.q), wc = (poly % 2 == 0) ? smod(add, P.q) : 0;
+    const uint64_t wa = smod(ma, P.q), wc = (poly % 2 == 0) ? smod(add, P.q) : 0;
+    uint64_t wb = smod(mb, P.q), wbn = wb;  // weights of b at even / odd k
+    if (iota) {
+        wb = mulm(wb, iota[i], P.q, P.mu);
+        wbn = wb ? P.q - wb : 0;
+    }
     const uint64_t *ar = a + ((size_t)poly * la + i) * n;
     const uint64_t *br = b ? b + ((size_t)poly * lb + i) * n : nullptr;
     uint64_t *o = out + ((size_t)poly * lo + i) * n;
     for (uint32_t k = threadIdx.x; k < n; k += blockDim.x) {
         uint64_t v = mulm(ar[k], wa, P.q, P.mu);
-        if (br) v = addm(v, mulm(br[k], wb, P.q, P.mu), P.q);
+        if (br) v = addm(v, mulm(br[k], (k & 1) ? wbn : wb, P.q, P.mu), P.q);
         o[k] = addm(v, wc, P.q);
     }
+}
+
+int op_lincomb(const ckks_ctx *c, uint64_t *out, int lo, const uint64_t *a, int la, const uint64_t *b, int lb,
+               int64_t ma, int64_t mb, int64_t add, bool mono_b, int B, hipStream_t s) {
+    ProfScope ps_(c, "lincomb", s);
+    hipLaunchKernelGGL(k_lincomb, dim3(B * 2 * lo), dim3(256), 0, s, a, (uint32_t)la, b, (uint32_t)lb, out,
+                       (uint32_t)lo, c->n, ma, mb, add, mono_b ? (const uint64_t *)c->d_iota : nullptr, c->d_pc);
+    return hipGetLastError() == hipSuccess ? CKKS_OK : CKKS_EHIP;
 }
 
 namespace {
@@ -56,9 +72,11 @@ struct Ct {
     double s = 0;
 };
 
+}  // namespace
+
 // Constant c encoded at scale t: the integer nearest c t (ties to even);
 // |c t| must stay below 2^62 (checked: *ok is cleared otherwise).
-inline int64_t enc_const(double c, double t, bool *ok) {
+int64_t enc_const(double c, double t, bool *ok) {
     const double v = std::nearbyint(c * t);
     if (!(std::fabs(v) < 4611686018427387904.0)) {  // 2^62 (also rejects NaN)
         *ok = false;
@@ -66,6 +84,8 @@ inline int64_t enc_const(double c, double t, bool *ok) {
     }
     return (int64_t)v;
 }
+
+namespace {
 
 struct Eval {
     ckks_ctx *c;
@@ -83,7 +103,8 @@ struct Eval {
     int lincomb(uint64_t *out, int lo, const Ct &a, const Ct *b, int64_t ma, int64_t mb, int64_t add) {
         ProfScope ps_(c, "eval_lincomb", s);
         hipLaunchKernelGGL(k_lincomb, dim3(B * 2 * lo), dim3(256), 0, s, a.p, (uint32_t)a.l, b ? b->p : nullptr,
-                           b ? (uint32_t)b->l : 0u, out, (uint32_t)lo, c->n, ma, mb, add, c->d_pc);
+                           b ? (uint32_t)b->l : 0u, out, (uint32_t)lo, c->n, ma, mb, add, (const uint64_t *)nullptr,
+                           c->d_pc);
         return hipGetLastError() == hipSuccess ? CKKS_OK : CKKS_EHIP;
     }
     // out = Rescale(x * [cst at the scale of the prime the rescale drops]): level -1, scale kept
@@ -135,12 +156,20 @@ static int max_generation(int d) {
     return m;
 }
 
+// Products per batched key switch: a generation, capped so that the stacked
+// key-switch workspace stays within an 8 GiB budget.
+constexpr size_t EVAL_KS_BUDGET = 8ull << 30;
+static int gen_chunk(const ckks_ctx *c, int B, int l, int d) {
+    const size_t per = std::max<size_t>(1, ws_bytes_relin(c, B, l));
+    return std::max(1, std::min(max_generation(d), (int)(EVAL_KS_BUDGET / per)));
+}
+
 size_t ws_bytes_eval_mod(const ckks_ctx *c, int B, int l, int degree) {
     const size_t ct = ((size_t)B * 2 * l * c->n * 8 + 255) & ~(size_t)255;
-    const int G = max_generation(degree);
+    const int G = gen_chunk(c, B, l, degree);
     const size_t ks = std::max(ws_bytes_relin(c, G * B, l), ws_bytes_rescale(c, G * B, l));
     // T_1..T_d, the running sum, the double-angle value, three scratch ciphertexts,
-    // and the stacked left / right factors and products of one generation
+    // and the stacked left / right factors and products of one batch of products
     return ((size_t)degree + 5) * ct + 4 * (size_t)G * ct + ks;
 }
 
@@ -149,7 +178,7 @@ int op_eval_mod(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, do
                 double *scale_out, int *level_out, hipStream_t s) {
     const int d = degree;
     const size_t slot = (((size_t)B * 2 * l * c->n * 8) + 255) & ~(size_t)255;
-    const int G = max_generation(d);
+    const int G = gen_chunk(c, B, l, d);
     uint8_t *base = (uint8_t *)ws;
     auto take = [&](size_t slots) {
         uint64_t *p = (uint64_t *)base;
@@ -169,8 +198,9 @@ int op_eval_mod(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, do
     // (2^(g-1), 2^g] at a time: its products are independent and share the
     // level T_1 - g + 1, so they go through one batched tensor + relinearise
     // and one rescale (the residues are those of separate products)
-    for (int lo = 2, g = 1; lo <= d; lo = 2 * lo - 1, g++) {
-        const int hi = std::min(2 * (lo - 1), d), cnt = hi - lo + 1;
+    for (int glo = 2, g = 1; glo <= d; glo = 2 * glo - 1, g++)
+    for (int lo = glo, ghi = std::min(2 * (glo - 1), d); lo <= ghi; lo += G) {
+        const int hi = std::min(lo + G - 1, ghi), cnt = hi - lo + 1;
         const int mu = T[1].l - (g - 1);
         const size_t per = (size_t)B * 2 * mu * c->n;       // words of B ciphertexts at level mu
         const size_t per_r = (size_t)B * 2 * (mu - 1) * c->n;

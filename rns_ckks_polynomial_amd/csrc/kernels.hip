@@ -1136,6 +1136,42 @@ static int ks_moddown_conv(ckks_ctx *c, size_t nout, int l, const KsWs &w, hipSt
     return CKKS_OK;
 }
 
+// ModRaise: the exact centered lift of every coefficient from the primes
+// [0, l0) to the primes [0, lt) (bootstrapping's first step): scaled iNTT of
+// the l0 limbs, exact u, conversion to every target, NTT of the lt limbs.
+size_t ws_bytes_mod_raise(const ckks_ctx *c, int B, int l0) {
+    return (align_words((size_t)2 * B * l0 * c->n) + align_words(((size_t)2 * B * c->n + 1) / 2)) * 8;
+}
+
+int op_mod_raise(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l0, int lt, void *ws, hipStream_t s) {
+    int e = CKKS_OK;
+    RaiseTables *rt = raise_tables(c, (uint32_t)l0, &e);
+    if (!rt) return e;
+    const uint32_t n = c->n, P = 2 * (uint32_t)B;
+    uint64_t *y = (uint64_t *)ws;
+    uint32_t *u = (uint32_t *)(y + align_words((size_t)P * l0 * n));
+    {
+        MapBatched m{in, (size_t)l0 * n, y, n, (uint32_t)l0, rt->d_scale};
+        if ((e = launch_ntt(c, m, (int)(P * l0), true, s, "raise_intt"))) return e;
+    }
+    SetLayout lay{(size_t)l0 * n, 0, 0, 1, 0};
+    {
+        ProfScope ps_(c, "raise_u", s);
+        hipLaunchKernelGGL(k_basis_u, dim3((n + 255) / 256, P), dim3(256), 0, s, rt->d_basis, lay, y, u, n,
+                           c->d_pc);
+    }
+    LAUNCH_CHECK();
+    {
+        ConvTargets ct{(uint32_t)lt, c->L, c->K, (size_t)lt * n, 0};
+        ProfScope ps_(c, "raise_convert", s);
+        hipLaunchKernelGGL(k_convert<1>, dim3((n + 255) / 256, (lt + CT - 1) / CT, P), dim3(256), 0, s,
+                           rt->d_basis, lay, y, u, ct, out, n, c->d_pc);
+    }
+    LAUNCH_CHECK();
+    MapStrided m2{out, out, n, (uint32_t)lt, 0, nullptr};
+    return launch_ntt(c, m2, (int)(P * lt), false, s, "raise_ntt");
+}
+
 size_t ws_bytes_relin(const ckks_ctx *c, int B, int l) { return ks_words(c, B, l, nullptr, nullptr) * 8; }
 size_t ws_bytes_rotate(const ckks_ctx *c, int B, int l) { return ks_words(c, B, l, nullptr, nullptr) * 8; }
 size_t ws_bytes_rescale(const ckks_ctx *c, int B, int l) {

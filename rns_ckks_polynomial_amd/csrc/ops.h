@@ -1,5 +1,6 @@
 // ops.h -- internal launchers (host side) for the hot-path operations.
 #pragma once
+#include "../../include/ckks_gpu.h"
 #include "ctx_internal.h"
 
 namespace ckks {
@@ -22,12 +23,25 @@ int op_rotate(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, uint
               bool accumulate, hipStream_t s);
 int op_bsgs(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, const uint64_t *diags, int bs, int gs,
             const uint64_t *const *baby, const uint64_t *const *giant, bool rescale, void *ws, hipStream_t s);
+// ModRaise: centered lift of [B][2][l0][n] (primes [0, l0)) to [B][2][lt][n].
+size_t ws_bytes_mod_raise(const ckks_ctx *c, int B, int l0);
+int op_mod_raise(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l0, int lt, void *ws, hipStream_t s);
+// out = ma a + mb b' (+ add on c0) on limbs [0, lo) of B ciphertexts; b' = b X^(n/2) if mono_b.
+int op_lincomb(const ckks_ctx *c, uint64_t *out, int lo, const uint64_t *a, int la, const uint64_t *b, int lb,
+               int64_t ma, int64_t mb, int64_t add, bool mono_b, int B, hipStream_t s);
+// The integer nearest c t (ties to even); clears *ok if |c t| >= 2^62.
+int64_t enc_const(double c, double t, bool *ok);
 // EvalMod (Chebyshev cosine + double angles); levels consumed = eval_mod_depth(degree, double_angles).
 int eval_mod_depth(int degree, int double_angles);
 size_t ws_bytes_eval_mod(const ckks_ctx *c, int B, int l, int degree);
 int op_eval_mod(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, double scale_in, const double *cheb,
                 int degree, double bound_k, int double_angles, double out_factor, const uint64_t *rlk, void *ws,
                 double *scale_out, int *level_out, hipStream_t s);
+// Bootstrapping: ModRaise -> CtS -> conj_extract -> EvalMod (re, im) -> merge -> StC.
+int boot_levels(const ckks_boot_params *p, int *l_out);
+size_t ws_bytes_bootstrap(const ckks_ctx *c, int B, int l0, const ckks_boot_params *p);
+int op_bootstrap(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l0, const ckks_boot_params *p,
+                 void *ws, double *scale_mid, hipStream_t s);
 int op_fill_uniform(const ckks_ctx *c, uint64_t *dst, int count, int first, int nlimbs, uint64_t seed, uint64_t tag,
                     uint64_t stream0, hipStream_t s);
 

@@ -20,6 +20,14 @@ def galois_conj(n: int) -> int:
     return 2 * n - 1
 
 
+def slot_matrix(n: int) -> np.ndarray:
+    """V0[j][k] = zeta^(5^j k) with zeta = exp(i pi / n): slot j of the monomial
+    X^k for k < n/2 (X^(k + n/2) gives i times that, as 5^j = 1 mod 4)."""
+    h, m = n // 2, 2 * n
+    e = np.array([pow(5, j, m) for j in range(h)], dtype=np.int64)
+    return np.exp(1j * np.pi * ((e[:, None] * np.arange(h)[None, :]) % m) / n)
+
+
 class Keys:
     def __init__(self, ctx: oracle.Ctx, seed: int):
         self.ctx, self.seed = ctx, seed
