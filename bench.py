@@ -79,6 +79,10 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    p.add_argument("--boot-config4", action="store_true",
+                   help="only time the bootstrap of 8 ciphertexts on the 2100 + 263 prime chain "
+                        "(19 -> 2100 -> 2083 primes; about 160 GB of HBM)")
+    p.add_argument("--boot-reps", type=int, default=2)
     return p.parse_args()
 
 
@@ -131,6 +135,82 @@ def eval_mod_timing(g, x, rlk, torch, reps: int = 3):
                       f"ct x ct products per ciphertext"}
 
 
+# Bootstrapping's EvalMod: degree-31 cosine interpolant on [-64, 64] (covers the
+# ModRaise overflow of a dense ternary secret at n = 2048) and 6 double angles:
+# depth 14, so a refresh consumes 17 levels (2100 -> 2083 on the 2100-prime chain).
+BOOT_DEGREE, BOOT_ANGLES, BOOT_K = 31, 6, 64.0
+
+
+def boot_stc_level(lt: int) -> int:
+    """Level of slot_to_coeff's input: lt minus coeff_to_slot, conj_extract's 1/2 and EvalMod's depth."""
+    return lt - 2 - (3 + (BOOT_DEGREE - 1).bit_length() + BOOT_ANGLES)
+
+
+def bootstrap_timing(g, torch, lt, l0, cts, stc, baby, giant, conj, rlk, reps, seed):
+    """ms per bootstrap of a batch of 8 ciphertexts at level l0 raised to lt; the
+    per-scope kernel time of one more call from the library's event profiler."""
+    import numpy as np
+    from numpy.polynomial import chebyshev as C
+
+    from rns_ckks_polynomial_amd import synth
+    cheb = C.chebinterpolate(lambda u: np.cos(2 * np.pi * (BOOT_K * u - 0.25) / 2 ** BOOT_ANGLES), BOOT_DEGREE)
+    x = torch.empty((BATCH, 2, l0, N), dtype=torch.uint64, device="cuda:0")
+    g.fill_uniform(x, seed, synth.TAG_CT, 0)
+    args = (x, lt, cts, stc, BS, GS, baby, giant, conj, rlk, 2.0 ** 59, cheb, BOOT_K, BOOT_ANGLES, 1 / (2 * np.pi))
+    out, _ = g.bootstrap(*args)  # first call: ModRaise tables, workspace
+    torch.cuda.synchronize()
+    print(f"bootstrap {l0} -> {lt}: first call done", file=sys.stderr, flush=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.bootstrap(*args, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    g.profile_begin()
+    g.bootstrap(*args, out=out)
+    prof = g.profile_end()
+    scopes = {k: round(v[1], 3) for k, v in sorted(prof.items(), key=lambda kv: -kv[1][1])}
+    return {"ms_per_batch": ms, "ciphertexts_per_s": BATCH / (ms * 1e-3), "s_per_ciphertext": ms * 1e-3 / BATCH,
+            "levels": f"{l0} -> {lt} -> {out.shape[2]}",
+            "config": f"batch {BATCH}, n={N}: ModRaise {l0} -> {lt} primes, coeff_to_slot BSGS {BS}x{GS} + rescale, "
+                      f"conjugation key switch, EvalMod on {2 * BATCH} ciphertexts (degree {BOOT_DEGREE} cosine on "
+                      f"[-{BOOT_K:g}, {BOOT_K:g}], {BOOT_ANGLES} double angles), slot_to_coeff BSGS {BS}x{GS} + "
+                      f"rescale",
+            "kernel_ms_by_scope": scopes}
+
+
+def boot_config4(args):
+    """The 2100 + 263 prime chain (dnum 8): 8 ciphertexts at 19 primes refreshed to 2083."""
+    import torch
+
+    from rns_ckks_polynomial_amd import synth
+    from rns_ckks_polynomial_amd.api import Context
+    n, l, k, dnum, l0 = 2048, 2100, 263, 8, 19
+    tot = l + k
+    g = Context(n, l, k, dnum, device=0)
+    u64, dev = torch.uint64, "cuda:0"
+    l3 = boot_stc_level(l)
+    keys = torch.empty((BS + GS, dnum, 2, tot, n), dtype=u64, device=dev)
+    cts = torch.empty((GS, BS, l, n), dtype=u64, device=dev)
+    stc = torch.empty((GS, BS, l3, n), dtype=u64, device=dev)
+    seed = 0xC0DE0004
+    print("bootstrap 2100-prime chain: filling keys and diagonals", file=sys.stderr, flush=True)
+    g.fill_uniform(keys, seed + 1, synth.TAG_KEY, 0)
+    g.fill_uniform(cts, seed + 2, synth.TAG_DIAG, 0)
+    g.fill_uniform(stc, seed + 3, synth.TAG_DIAG, 0)
+    baby = [None] + [keys[i] for i in range(BS - 1)]
+    giant = [None] + [keys[BS - 1 + i] for i in range(GS - 1)]
+    r = bootstrap_timing(g, torch, l, l0, cts, stc, baby, giant, keys[BS + GS - 2], keys[BS + GS - 1],
+                         args.boot_reps, seed)
+    r["hbm_bytes_allocated"] = torch.cuda.max_memory_allocated()
+    print(json.dumps({"metric": "bootstrap seconds per ciphertext (2100-prime chain)", "value": r["s_per_ciphertext"],
+                      "unit": "s/ciphertext", "higher_is_better": False, "n_gpus": 1, "reps": args.boot_reps,
+                      "dtype": "u64", "data": "synthetic (seeded SplitMix64 residues, resident in HBM)",
+                      "config": {"workload": f"n={n}, {l}+{k} primes, dnum={dnum}, batch {BATCH}: " + r["config"]},
+                      "vs_baseline": None, "bootstrap": r}))
+
+
 def kernel_work():
     """Algorithmic work of each kernel per benchmark step (all launches of that
     kernel in one step; launches differ in size since BSGS batches its steps).
@@ -175,6 +255,9 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only: the hot path is measured on one "
                                    "GPU's share; pass --gpus 1"}))
         sys.exit(2)
+    if args.boot_config4:
+        boot_config4(args)
+        return
     import torch
 
     from rns_ckks_polynomial_amd import synth
@@ -252,6 +335,14 @@ def main():
     # the 112-prime level, degree-31 cosine interpolant on [-8, 8], 3 double angles
     em = eval_mod_timing(g, a, rlk, torch)
 
+    # bootstrapping of 8 ciphertexts on this 112-prime chain (1 -> 112 -> 95 primes; slot_to_coeff's
+    # diagonals at 96 primes), with the
+    # step's rotation keys and a second diagonal set for slot_to_coeff (outside the step)
+    stc = torch.empty((GS, BS, boot_stc_level(L), N), dtype=u64, device=dev)
+    g.fill_uniform(stc, 0xC0DE0005, synth.TAG_DIAG, 0)
+    boot = bootstrap_timing(g, torch, L, 1, diags, stc, baby, giant, keys[0], rlk, 2, 0xC0DE0006)
+    del stc
+
     # per-kernel launch times (library event profiler) over profiled steps + the NTT pair
     g.profile_begin()
     for _ in range(args.profile_steps):
@@ -316,6 +407,7 @@ def main():
                    "global_batch": BATCH, "parallelism": "single GPU"},
         "key_switches_per_step": ks_per_step,
         "eval_mod": em,
+        "bootstrap": boot,
         "limb_ntts_per_s": ntt_rate,
         "linear_transforms_per_s": BATCH / (bsgs_ms * 1e-3),
         "ct_mults_per_s": BATCH / (mr_ms * 1e-3),

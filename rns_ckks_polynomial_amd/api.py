@@ -26,6 +26,12 @@ def _ptr(t: torch.Tensor) -> int:
     return t.data_ptr()
 
 
+def _need(t: torch.Tensor, words: int, what: str):
+    """The C ABI takes bare pointers: refuse a buffer smaller than what the call reads or writes."""
+    if t.numel() < words:
+        raise ValueError(f"{what} holds {t.numel()} residues; the call uses {words}")
+
+
 def _stream():
     return C.c_void_p(torch.cuda.current_stream().cuda_stream)
 
@@ -81,6 +87,14 @@ class Context:
             ws = self.workspace(need)
         return ws, need
 
+    def _key(self, k, what="key"):
+        _need(k, self.dnum * 2 * (self.L + self.K) * self.n, what)
+        return _ptr(k)
+
+    def _cts(self, t, B, l, what):
+        _need(t, B * 2 * l * self.n, what)
+        return _ptr(t)
+
     # ------------------------------------------------------------ ops
     def ntt_fwd(self, x: torch.Tensor, first_prime: int = 0) -> torch.Tensor:
         count, nl = x.numel() // (x.shape[-1] * x.shape[-2]), x.shape[-2]
@@ -96,6 +110,8 @@ class Context:
         out = torch.empty_like(a) if out is None else out
         nl = a.shape[-2]
         count = a.numel() // (a.shape[-1] * nl)
+        _need(b, a.numel(), "b")
+        _need(out, a.numel(), "out")
         nat.check(nat.lib().ckks_pointwise_mul(self._h, _ptr(a), _ptr(b), _ptr(out), count, first_prime, nl,
                                                _stream()), "ckks_pointwise_mul")
         return out
@@ -104,7 +120,8 @@ class Context:
         B, _, l, n = a.shape
         out = torch.empty_like(a) if out is None else out
         ws, need = self._ws_for("relin", B, l, ws=ws)
-        nat.check(nat.lib().ckks_mul_tensor_relin(self._h, _ptr(a), _ptr(b), _ptr(rlk), _ptr(out), B, l,
+        nat.check(nat.lib().ckks_mul_tensor_relin(self._h, _ptr(a), self._cts(b, B, l, "b"), self._key(rlk),
+                                                  self._cts(out, B, l, "out"), B, l,
                                                   _ptr(ws), ws.numel() * 8, _stream()), "ckks_mul_tensor_relin")
         return out
 
@@ -112,7 +129,8 @@ class Context:
         B, _, l, n = x.shape
         out = torch.empty((B, 2, l - 1, n), dtype=x.dtype, device=x.device) if out is None else out
         ws, need = self._ws_for("rescale", B, l, ws=ws)
-        nat.check(nat.lib().ckks_rescale(self._h, _ptr(x), _ptr(out), B, l, _ptr(ws), ws.numel() * 8, _stream()),
+        nat.check(nat.lib().ckks_rescale(self._h, _ptr(x), self._cts(out, B, l - 1, "out"), B, l, _ptr(ws),
+                                         ws.numel() * 8, _stream()),
                   "ckks_rescale")
         return out
 
@@ -120,7 +138,8 @@ class Context:
         B, _, l, n = x.shape
         out = torch.empty_like(x) if out is None else out
         ws, need = self._ws_for("rotate", B, l, ws=ws)
-        nat.check(nat.lib().ckks_rotate(self._h, _ptr(x), _ptr(out), B, l, galois_elt, _ptr(key), _ptr(ws),
+        nat.check(nat.lib().ckks_rotate(self._h, _ptr(x), self._cts(out, B, l, "out"), B, l, galois_elt,
+                                        self._key(key), _ptr(ws),
                                         ws.numel() * 8, _stream()), "ckks_rotate")
         return out
 
@@ -130,9 +149,11 @@ class Context:
         lo = l - 1 if do_rescale else l
         out = torch.empty((B, 2, lo, n), dtype=x.dtype, device=x.device) if out is None else out
         ws, need = self._ws_for("bsgs", B, l, bs, gs, ws=ws)
-        bk = (C.c_void_p * bs)(*[None if k is None else _ptr(k) for k in baby_keys])
-        gk = (C.c_void_p * gs)(*[None if k is None else _ptr(k) for k in giant_keys])
-        nat.check(nat.lib().ckks_bsgs_linear_transform(self._h, _ptr(x), _ptr(out), B, l, _ptr(diags), bs, gs,
+        bk = (C.c_void_p * bs)(*[None if k is None else self._key(k, "baby key") for k in baby_keys])
+        gk = (C.c_void_p * gs)(*[None if k is None else self._key(k, "giant key") for k in giant_keys])
+        _need(diags, gs * bs * l * n, "diags")
+        nat.check(nat.lib().ckks_bsgs_linear_transform(self._h, _ptr(x), self._cts(out, B, lo, "out"), B, l,
+                                                       _ptr(diags), bs, gs,
                                                        bk, gk, int(do_rescale), _ptr(ws), ws.numel() * 8,
                                                        _stream()), "ckks_bsgs_linear_transform")
         return out
@@ -142,7 +163,8 @@ class Context:
         B, _, l, n = x.shape
         out = torch.empty((B, 2, level_out, n), dtype=x.dtype, device=x.device) if out is None else out
         ws, need = self._ws_for("modraise", B, l, ws=ws)
-        nat.check(nat.lib().ckks_mod_raise(self._h, _ptr(x), _ptr(out), B, l, level_out, _ptr(ws), ws.numel() * 8,
+        nat.check(nat.lib().ckks_mod_raise(self._h, _ptr(x), self._cts(out, B, max(level_out, 0), "out"), B, l,
+                                           level_out, _ptr(ws), ws.numel() * 8,
                                            _stream()), "ckks_mod_raise")
         return out
 
@@ -152,17 +174,21 @@ class Context:
         """Bootstrapping (see ckks_bootstrap): returns (out, scale entering slot_to_coeff)."""
         B, _, l0, n = x.shape
         cheb_c = (C.c_double * len(cheb))(*[float(v) for v in cheb])
-        bk = (C.c_void_p * bs)(*[None if k is None else _ptr(k) for k in baby_keys])
-        gk = (C.c_void_p * gs)(*[None if k is None else _ptr(k) for k in giant_keys])
-        p = nat.BootParams(level_raise, _ptr(cts_diags), _ptr(stc_diags), bs, gs, bk, gk, _ptr(conj_key), _ptr(rlk),
+        bk = (C.c_void_p * bs)(*[None if k is None else self._key(k, "baby key") for k in baby_keys])
+        gk = (C.c_void_p * gs)(*[None if k is None else self._key(k, "giant key") for k in giant_keys])
+        lo = level_raise - 3 - (3 + max(0, (len(cheb) - 2).bit_length()) + double_angles)
+        p = nat.BootParams(level_raise, _ptr(cts_diags), _ptr(stc_diags), bs, gs, bk, gk, self._key(conj_key, "conj key"),
+                           self._key(rlk, "rlk"),
                            float(evalmod_scale), cheb_c, len(cheb) - 1, float(bound_k), int(double_angles),
                            float(out_factor))
         need = C.c_size_t()
         nat.check(nat.lib().ckks_bootstrap_workspace_size(self._h, B, l0, C.byref(p), C.byref(need)),
-                  "ckks_bootstrap_workspace_size")
+                  "ckks_bootstrap_workspace_size")   # validates levels and parameters
+        _need(cts_diags, gs * bs * level_raise * n, "cts_diags")
+        _need(stc_diags, gs * bs * (lo + 1) * n, "stc_diags")
         ws = self.workspace(need.value) if ws is None else ws
-        lo = level_raise - 3 - (3 + max(0, (len(cheb) - 2).bit_length()) + double_angles)
         out = torch.empty((B, 2, lo, n), dtype=x.dtype, device=x.device) if out is None else out
+        _need(out, B * 2 * lo * n, "out")
         s_mid, l_out = C.c_double(), C.c_int()
         nat.check(nat.lib().ckks_bootstrap(self._h, _ptr(x), _ptr(out), B, l0, C.byref(p), _ptr(ws), ws.numel() * 8,
                                            C.byref(s_mid), C.byref(l_out), _stream()), "ckks_bootstrap")
@@ -181,8 +207,9 @@ class Context:
         out = torch.empty((B, 2, max(lo, 1), n), dtype=x.dtype, device=x.device) if out is None else out
         ws, need = self._ws_for("evalmod", B, l, degree, ws=ws)
         s_out, l_out = C.c_double(), C.c_int()
-        nat.check(nat.lib().ckks_eval_mod(self._h, _ptr(x), _ptr(out), B, l, float(scale), cheb, degree,
-                                          float(bound_k), int(double_angles), float(out_factor), _ptr(rlk),
+        nat.check(nat.lib().ckks_eval_mod(self._h, _ptr(x), self._cts(out, B, max(lo, 0), "out"), B, l, float(scale),
+                                          cheb, degree, float(bound_k), int(double_angles), float(out_factor),
+                                          self._key(rlk),
                                           _ptr(ws), ws.numel() * 8, C.byref(s_out), C.byref(l_out), _stream()),
                   "ckks_eval_mod")
         assert l_out.value == lo

@@ -154,3 +154,6 @@ def test_bootstrap_rejects_bad_arguments():
         call(16, bs=64, gs=32)
     with pytest.raises(Exception, match="level"):   # mod_raise below the input level
         g.mod_raise(dev(_rand(o, 2, 1, 4)), 3)
+    short = dev(np.zeros((2, 2, 6, o.n), dtype=np.uint64))   # slot_to_coeff runs at 16 - 2 - 7 = 7 primes
+    with pytest.raises(ValueError, match="stc_diags"):
+        g.bootstrap(x, 16, pt, short, 2, 2, [None, k], [None, k], k, k, DELTA, np.zeros(8), 4.0, 1, 0.1)
