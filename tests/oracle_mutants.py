@@ -2,11 +2,14 @@
 
 Plants one plausible mistake at a time in a copy of oracle.c, builds it, and
 runs the CPU test-suite against it (CKKS_ORACLE_LIB points the tests at the
-planted copy).  Every mutant must make at least one pin fail.
+planted copy).  The Python stages of the oracle (EvalMod, bootstrapping) are
+mutated in a copy of the oracle package and the tests, and their pins run
+there.  Every mutant must make at least one pin fail.
 
     python tests/oracle_mutants.py
 """
 import os
+import shutil
 import subprocess
 import sys
 import tempfile
@@ -33,11 +36,76 @@ MUTANTS = {
     "encode_sign": ("uint64_t a = (m - (e[j] * i) % m) % m;", "uint64_t a = (e[j] * i) % m;"),
 }
 
+# (file under oracle/, text, replacement, pin file).  Not listed: which prime a
+# constant is encoded against (neighbouring chain primes differ by less than
+# 2^-45 relative, so the refresh stays correct); GPU parity fixes that rule.
+PY_MUTANTS = {
+    "em_odd_recurrence": ("evalmod.py", "self.lincomb(p.l, p, 2, T[1], -1)", "self.lincomb(p.l, p, 2, T[1], 0)",
+                          "test_oracle_evalmod.py"),
+    "em_even_constant": ("evalmod.py", "self.lincomb(p.l, p, 2, add=const_int(-1.0, p.s))",
+                         "self.lincomb(p.l, p, 2, add=const_int(1.0, p.s))", "test_oracle_evalmod.py"),
+    "em_double_angle": ("evalmod.py", "self.lincomb(sq.l, sq, 2, add=const_int(-1.0, sq.s))",
+                        "self.lincomb(sq.l, sq, 1, add=const_int(-1.0, sq.s))", "test_oracle_evalmod.py"),
+    "em_no_c0": ("evalmod.py", "add=const_int(cheb[0], p.s)", "add=0", "test_oracle_evalmod.py"),
+    "em_no_divide_k": ("evalmod.py", "1.0 / bound_k)", "1.0)", "test_oracle_evalmod.py"),
+    "boot_no_conj": ("bootstrap.py", "re2 = em.lincomb(l1, W, 1, Cj, 1)", "re2 = em.lincomb(l1, W, 2, Cj, 0)",
+                     "test_oracle_bootstrap.py"),
+    "boot_half_sign": ("bootstrap.py", "const_int(-0.5, qd)", "const_int(0.5, qd)", "test_oracle_bootstrap.py"),
+    "boot_im_not_times_i": ("bootstrap.py", "im2 = times_i(o, em.lincomb(l1, W, 1, Cj, -1), l1)",
+                            "im2 = em.lincomb(l1, W, 1, Cj, -1)", "test_oracle_bootstrap.py"),
+    "boot_merge_not_times_i": ("bootstrap.py", "_Ct(times_i(o, im_o, l3), l3, 0.0)", "_Ct(im_o, l3, 0.0)",
+                               "test_oracle_bootstrap.py"),
+    "times_i_cyclic": ("bootstrap.py", "out[c, i, :h] = neg[h:]", "out[c, i, :h] = a[h:]",
+                       "test_oracle_bootstrap.py"),
+    # the CRT value lifted into [0, Q0) instead of (-Q0/2, Q0/2)
+    "modraise_uncentered": ("bootstrap.py",
+                            "out = np.stack([base_convert(coef[c], o.primes[:l0], o.primes[:lt]) for c in range(2)])",
+                            "def _plain(x, bm, tm):\n"
+                            "        Q = 1\n"
+                            "        for q in bm:\n"
+                            "            Q *= int(q)\n"
+                            "        h = [Q // int(q) for q in bm]\n"
+                            "        v = [sum(int(x[i, k]) * h[i] * pow(h[i], -1, int(bm[i])) for i in range(len(bm))) % Q\n"
+                            "             for k in range(x.shape[1])]\n"
+                            "        return np.array([[vk % int(t) for vk in v] for t in tm], dtype=np.uint64)\n"
+                            "    out = np.stack([_plain(coef[c], o.primes[:l0], o.primes[:lt]) for c in range(2)])",
+                            "test_oracle_bootstrap.py"),
+}
+
+
+def py_mutants(tmp):
+    """Each Python mutant in a copy of oracle/, tests/ and the input generator."""
+    failures = 0
+    for name, (fname, a, b, pins) in PY_MUTANTS.items():
+        root = os.path.join(tmp, "py_" + name)
+        shutil.copytree(os.path.join(ROOT, "oracle"), os.path.join(root, "oracle"),
+                        ignore=shutil.ignore_patterns("__pycache__"))
+        shutil.copytree(os.path.join(ROOT, "tests"), os.path.join(root, "tests"),
+                        ignore=shutil.ignore_patterns("__pycache__"))
+        os.makedirs(os.path.join(root, "rns_ckks_polynomial_amd"))
+        for f in ("__init__.py", "synth.py"):
+            shutil.copy(os.path.join(ROOT, "rns_ckks_polynomial_amd", f), os.path.join(root, "rns_ckks_polynomial_amd"))
+        for f in ("pytest.ini",):
+            if os.path.exists(os.path.join(ROOT, f)):
+                shutil.copy(os.path.join(ROOT, f), root)
+        path = os.path.join(root, "oracle", fname)
+        src = open(path).read()
+        assert src.count(a) == 1, name
+        open(path, "w").write(src.replace(a, b))
+        r = subprocess.run([sys.executable, "-m", "pytest", os.path.join(root, "tests", pins), "-x", "-q", "-m",
+                            "not gpu", "-p", "no:cacheprovider"], capture_output=True, text=True, cwd=root,
+                           timeout=600)
+        caught = r.returncode == 1 and " failed" in r.stdout
+        failures += not caught
+        print(f"{name:22s} {'caught' if caught else 'NOT CAUGHT'}", flush=True)
+    return failures
+
 
 def main():
     src = open(SRC).read()
     failures = 0
     with tempfile.TemporaryDirectory() as tmp:
+        failures += py_mutants(tmp)
         for name, (a, b) in MUTANTS.items():
             assert a in src, name
             c = os.path.join(tmp, name + ".c")

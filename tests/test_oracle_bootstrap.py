@@ -52,6 +52,25 @@ def test_mod_raise_adds_multiple_of_q0(env):
     assert max(abs(v) for v in I) <= ctx.n // 2 and any(v != 0 for v in I)
 
 
+def test_mod_raise_lifts_to_centered_values(env):
+    """Each coefficient of both raised polynomials, read over all lt primes, is
+    the representative of the input residue in (-q_0/2, q_0/2) (two input primes:
+    of q_0 q_1)."""
+    ctx, keys = env
+    for l0 in (1, 2):
+        Q0 = 1
+        for i in range(l0):
+            Q0 *= ctx.q(i)
+        ct = keys.encrypt(np.zeros(32, dtype=np.complex128), DELTA_M, l0, 3)
+        r = mod_raise(ctx, ct, l0, 10)
+        for c in range(2):
+            before = centered_coeffs(ctx, ctx.ntt(ct[c][None], inverse=True)[0], l0)
+            after = centered_coeffs(ctx, ctx.ntt(r[c][None], inverse=True)[0], 10)
+            assert all(-Q0 // 2 <= int(v) <= Q0 // 2 for v in after)
+            assert all((int(a) - int(b)) % Q0 == 0 for a, b in zip(after, before))
+            assert any(int(v) < 0 for v in after)
+
+
 def test_times_i_multiplies_slots_by_i(env):
     ctx, keys = env
     z = synth.uniform_reals(2, synth.TAG_SLOTS, 0, 32, -1, 1) + 1j * synth.uniform_reals(2, synth.TAG_SLOTS, 1, 32,
