@@ -211,6 +211,39 @@ def boot_config4(args):
                       "vs_baseline": None, "bootstrap": r}))
 
 
+def seeded_key_timing(g, torch, a, key, reps: int = 40):
+    """Rotation at 112 primes with a stored key vs the same key seed-expanded
+    (b rows + seed), batch 1 and batch 8; each call's inner-product kernel time
+    from the library's event profiler."""
+    from rns_ckks_polynomial_amd.api import galois_rot
+    kb = key[:, 0].contiguous()
+    ge, seed = galois_rot(N, 3), 0x5EED
+    res = {"level": L, "key_bytes_stored": key.numel() * 8, "key_bytes_seeded": kb.numel() * 8}
+    for B in (1, BATCH):
+        x = a[:B]
+        out = torch.empty_like(x)
+        ws = g.workspace(g.workspace_size("rotate", B, L))
+        calls = {"stored": lambda: g.rotate(x, ge, key, out=out, ws=ws),
+                 "seeded": lambda: g.rotate_seeded(x, ge, kb, seed, out=out, ws=ws)}
+        row = {}
+        for name, f in calls.items():
+            f()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            g.profile_begin()
+            f()
+            prof = g.profile_end()
+            ip = prof.get("ks_inner_product", (1, 0.0, 0, 0))
+            row[name] = {"us_per_call": e0.elapsed_time(e1) / reps * 1e3, "inner_product_us": ip[1] / ip[0] * 1e3}
+        row["key_switches_per_s"] = {k: B / (v["us_per_call"] * 1e-6) for k, v in row.items()}
+        res[f"batch{B}"] = row
+    return res
+
+
 def kernel_work():
     """Algorithmic work of each kernel per benchmark step (all launches of that
     kernel in one step; launches differ in size since BSGS batches its steps).
@@ -335,6 +368,9 @@ def main():
     # the 112-prime level, degree-31 cosine interpolant on [-8, 8], 3 double angles
     em = eval_mod_timing(g, a, rlk, torch)
 
+    # seed-expanded switching keys: rotation with the key's a rows regenerated in the kernel
+    seeded = seeded_key_timing(g, torch, a, keys[0])
+
     # bootstrapping of 8 ciphertexts on this 112-prime chain (1 -> 112 -> 95 primes; slot_to_coeff's
     # diagonals at 96 primes), with the
     # step's rotation keys and a second diagonal set for slot_to_coeff (outside the step)
@@ -408,6 +444,7 @@ def main():
         "key_switches_per_step": ks_per_step,
         "eval_mod": em,
         "bootstrap": boot,
+        "seeded_keys": seeded,
         "limb_ntts_per_s": ntt_rate,
         "linear_transforms_per_s": BATCH / (bsgs_ms * 1e-3),
         "ct_mults_per_s": BATCH / (mr_ms * 1e-3),

@@ -129,6 +129,33 @@ int ckks_rescale(const ckks_ctx *ctx, const uint64_t *in, uint64_t *out, int bat
 int ckks_rotate(const ckks_ctx *ctx, const uint64_t *in, uint64_t *out, int batch, int level, uint32_t galois_elt,
                 const uint64_t *key, void *ws, size_t ws_bytes, void *stream);
 
+/* Seed-expanded switching keys (the EncryptedLLM GPU blog, sections 2.5 and
+ * 4.4: switching keys run to hundreds of MB or GB and their size is what to
+ * cut when memory or key loading is the limit).  A switching key's a rows are
+ * uniform; a seeded key stores only its b rows, key_b: [dnum][L + K][n] (NTT
+ * domain, row (j, i) = digit j, key prime i in chain order), and a 64-bit seed
+ * from which the library regenerates every a residue where it is used:
+ *   a_j[i][k] = floor(w q_i / 2^64),  w = S(S(S(seed, 10), j (L + K) + i), k),
+ *   S(s, t) = mix64(s + (t + 1) 0x9e3779b97f4a7c15)
+ * with mix64 the SplitMix64 finaliser (Steele, Lea, Flood, OOPSLA 2014):
+ *   z ^= z >> 30; z *= 0xbf58476d1ce4e5b9; z ^= z >> 27; z *= 0x94d049bb133111eb;
+ *   z ^= z >> 31.
+ * The key switch then reads half the key bytes.  The results are those of
+ * the stored key [dnum][2][L + K][n] with row c = 0 equal to key_b and row
+ * c = 1 the regenerated a (ckks_key_expand writes that key).  Arguments,
+ * workspaces and errors as ckks_mul_tensor_relin / ckks_rotate. */
+int ckks_mul_tensor_relin_seeded(const ckks_ctx *ctx, const uint64_t *a, const uint64_t *b, const uint64_t *rlk_b,
+                                 uint64_t rlk_seed, uint64_t *out, int batch, int level, void *ws, size_t ws_bytes,
+                                 void *stream);
+int ckks_rotate_seeded(const ckks_ctx *ctx, const uint64_t *in, uint64_t *out, int batch, int level,
+                       uint32_t galois_elt, const uint64_t *key_b, uint64_t key_seed, void *ws, size_t ws_bytes,
+                       void *stream);
+/* Expand a seeded key to the stored format: key_out [dnum][2][L + K][n] with
+ * key_out[j][0] = key_b[j] and key_out[j][1] the regenerated a rows (for the
+ * calls that take stored keys: BSGS, EvalMod, bootstrapping).  key_b and
+ * key_out must not overlap. */
+int ckks_key_expand(const ckks_ctx *ctx, const uint64_t *key_b, uint64_t key_seed, uint64_t *key_out, void *stream);
+
 /* Baby-step giant-step plaintext-matrix x ciphertext (matmul2 with BB x GG,
  * Kestrel article technique table and section 4.4; coeff_to_slot /
  * slot_to_coeff are this transform):

@@ -143,6 +143,39 @@ class Context:
                                         ws.numel() * 8, _stream()), "ckks_rotate")
         return out
 
+    def _key_b(self, k, what="key_b"):
+        _need(k, self.dnum * (self.L + self.K) * self.n, what)
+        return _ptr(k)
+
+    def mul_tensor_relin_seeded(self, a, b, rlk_b, rlk_seed: int, out=None, ws=None):
+        """ckks_mul_tensor_relin_seeded: the relinearisation key given as its b rows + seed."""
+        B, _, l, n = a.shape
+        out = torch.empty_like(a) if out is None else out
+        ws, need = self._ws_for("relin", B, l, ws=ws)
+        nat.check(nat.lib().ckks_mul_tensor_relin_seeded(self._h, _ptr(a), self._cts(b, B, l, "b"),
+                                                         self._key_b(rlk_b), int(rlk_seed) & (2 ** 64 - 1),
+                                                         self._cts(out, B, l, "out"), B, l, _ptr(ws), ws.numel() * 8,
+                                                         _stream()), "ckks_mul_tensor_relin_seeded")
+        return out
+
+    def rotate_seeded(self, x, galois_elt: int, key_b, key_seed: int, out=None, ws=None):
+        """ckks_rotate_seeded: the Galois key given as its b rows + seed."""
+        B, _, l, n = x.shape
+        out = torch.empty_like(x) if out is None else out
+        ws, need = self._ws_for("rotate", B, l, ws=ws)
+        nat.check(nat.lib().ckks_rotate_seeded(self._h, _ptr(x), self._cts(out, B, l, "out"), B, l, galois_elt,
+                                               self._key_b(key_b), int(key_seed) & (2 ** 64 - 1), _ptr(ws),
+                                               ws.numel() * 8, _stream()), "ckks_rotate_seeded")
+        return out
+
+    def key_expand(self, key_b, key_seed: int, out=None):
+        """ckks_key_expand: [dnum][L+K][n] b rows + seed -> stored key [dnum][2][L+K][n]."""
+        tot = self.L + self.K
+        out = torch.empty((self.dnum, 2, tot, self.n), dtype=key_b.dtype, device=key_b.device) if out is None else out
+        nat.check(nat.lib().ckks_key_expand(self._h, self._key_b(key_b), int(key_seed) & (2 ** 64 - 1),
+                                            self._key(out, "out"), _stream()), "ckks_key_expand")
+        return out
+
     def bsgs_linear_transform(self, x, diags, bs: int, gs: int, baby_keys, giant_keys, do_rescale=True,
                               out=None, ws=None):
         B, _, l, n = x.shape

@@ -136,6 +136,49 @@ extern "C" int ckks_rotate(const ckks_ctx *c, const uint64_t *in, uint64_t *out,
                      (hipStream_t)stream);
 }
 
+extern "C" int ckks_mul_tensor_relin_seeded(const ckks_ctx *c, const uint64_t *a, const uint64_t *b,
+                                            const uint64_t *rlk_b, uint64_t rlk_seed, uint64_t *out, int batch,
+                                            int level, void *ws, size_t ws_bytes, void *stream) {
+    if (!c || !c->K) return CKKS_EINVAL;
+    int e;
+    if ((e = check_ptr(a)) || (e = check_ptr(b)) || (e = check_ptr(rlk_b)) || (e = check_ptr(out))) return e;
+    if ((e = check_level(c, batch, level, 1))) return e;
+    if (!ws || ws_bytes < ws_bytes_relin(c, batch, level)) return CKKS_EWORKSPACE;
+    if (!aligned(ws)) return CKKS_EALIGN;
+    DeviceGuard g(c->device);
+    if (!g.ok) return CKKS_EHIP;
+    return op_mul_tensor_relin(const_cast<ckks_ctx *>(c), a, b, rlk_b, out, batch, level, ws, (hipStream_t)stream,
+                               &rlk_seed);
+}
+
+extern "C" int ckks_rotate_seeded(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int batch, int level,
+                                  uint32_t galois_elt, const uint64_t *key_b, uint64_t key_seed, void *ws,
+                                  size_t ws_bytes, void *stream) {
+    if (!c || !c->K) return CKKS_EINVAL;
+    int e;
+    if ((e = check_ptr(in)) || (e = check_ptr(out)) || (e = check_ptr(key_b))) return e;
+    if ((e = check_level(c, batch, level, 1))) return e;
+    if ((galois_elt & 1) == 0 || galois_elt >= 2 * c->n) return CKKS_EINVAL;
+    if (in == out) return CKKS_EINVAL;
+    if (!ws || ws_bytes < ws_bytes_rotate(c, batch, level)) return CKKS_EWORKSPACE;
+    if (!aligned(ws)) return CKKS_EALIGN;
+    DeviceGuard g(c->device);
+    if (!g.ok) return CKKS_EHIP;
+    return op_rotate(const_cast<ckks_ctx *>(c), in, out, batch, level, galois_elt, key_b, ws, false,
+                     (hipStream_t)stream, &key_seed);
+}
+
+extern "C" int ckks_key_expand(const ckks_ctx *c, const uint64_t *key_b, uint64_t key_seed, uint64_t *key_out,
+                               void *stream) {
+    if (!c || !c->K) return CKKS_EINVAL;
+    int e;
+    if ((e = check_ptr(key_b)) || (e = check_ptr(key_out))) return e;
+    if (key_b == key_out) return CKKS_EINVAL;
+    DeviceGuard g(c->device);
+    if (!g.ok) return CKKS_EHIP;
+    return op_key_expand(const_cast<ckks_ctx *>(c), key_b, key_seed, key_out, (hipStream_t)stream);
+}
+
 extern "C" int ckks_bsgs_linear_transform(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int batch, int level,
                                           const uint64_t *diags, int bs, int gs, const uint64_t *const *baby_keys,
                                           const uint64_t *const *giant_keys, int do_rescale, void *ws,

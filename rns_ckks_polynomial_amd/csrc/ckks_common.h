@@ -254,4 +254,28 @@ struct BasisDev {
     const uint64_t *half;     // [m]        mixed-radix digits of (B-1)/2
 };
 
+// ------------------------------------------------------------------ SplitMix64
+// Counter-based generator (G. Steele, D. Lea, C. Flood, "Fast splittable
+// pseudorandom number generators", OOPSLA 2014): output i (i = 0, 1, ...) of the
+// generator seeded with s is mix64(s + (i + 1) gamma).  Used by the seeded fill
+// of synthetic inputs and by seed-expanded switching keys.
+__host__ __device__ __forceinline__ uint64_t sm_mix(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    return z ^ (z >> 31);
+}
+__host__ __device__ __forceinline__ uint64_t sm_at(uint64_t s, uint64_t i) {
+    return sm_mix(s + (i + 1) * 0x9e3779b97f4a7c15ull);
+}
+
+// Seed-expanded switching keys: residue k of the a-part row (digit j, key prime
+// i) is floor(w q_i / 2^64), w = sm_at(row, k), row = sm_at(root, j (L + K) + i),
+// root = sm_at(seed, KEY_SEED_TAG).  One mix and one high product per residue:
+// no rejection loop, so a wavefront never diverges.
+constexpr uint64_t KEY_SEED_TAG = 10;
+inline uint64_t key_seed_root(uint64_t seed) { return sm_at(seed, KEY_SEED_TAG); }
+__device__ __forceinline__ uint64_t seeded_a(uint64_t row, uint32_t k, uint64_t q) {
+    return mulhi64(sm_at(row, k), q);
+}
+
 }  // namespace ckks

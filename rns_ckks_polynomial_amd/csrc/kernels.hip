@@ -463,9 +463,10 @@ static inline uint32_t xcd_blocks(uint32_t ngroups, uint32_t B) {
 // otherwise step s has its own inputs (ciphertext cb).
 constexpr int MAX_STEPS = 32;
 struct Steps {
-    const uint64_t *key[MAX_STEPS];
+    const uint64_t *key[MAX_STEPS];  // [dnum][2][L + K][n], or the b rows [dnum][L + K][n] when seeded
     uint32_t g[MAX_STEPS];
-    uint32_t count, B, shared;
+    uint64_t root[MAX_STEPS];        // seeded keys: key_seed_root(seed) of each step's key
+    uint32_t count, B, shared, seeded;
 };
 
 // acc[cb][c][e][k] = sum_j v_j[e][galois_src(k)] key[j][c][gidx(e)][k], where
@@ -475,7 +476,9 @@ struct Steps {
 // permuting the extended digits equals extending the permuted polynomial.
 // One workgroup per (output ciphertext, extended limb): each digit's limb is
 // loaded into LDS with coalesced reads and permuted from there; the key rows
-// are read in order.  (n = 2048: 8 coefficients per thread.)
+// are read in order.  (n = 2048: 8 coefficients per thread.)  SEEDED: the keys
+// hold their b rows only and each a-row residue is regenerated from its seed.
+template <bool SEEDED>
 __global__ __launch_bounds__(256) void k_inner2048(const uint64_t *__restrict__ d, size_t d_stride,
                                                     const uint64_t *__restrict__ ext, const Steps st,
                                                     uint64_t *__restrict__ acc, const PrimeConsts *__restrict__ pc,
@@ -507,15 +510,17 @@ __global__ __launch_bounds__(256) void k_inner2048(const uint64_t *__restrict__ 
 #pragma unroll
         for (int m = 0; m < 8; m++) lb[t + 256 * m] = src[t + 256 * m];
         __syncthreads();
-        const uint64_t *kb = key + ((size_t)j * 2 * (L + K) + gi) * n;
+        const uint64_t *kb = key + ((size_t)j * (SEEDED ? 1 : 2) * (L + K) + gi) * n;
         const uint64_t *ka = kb + (size_t)(L + K) * n;
+        const uint64_t row = SEEDED ? sm_at(st.root[step], (uint64_t)j * (L + K) + gi) : 0;
+        const uint64_t qa = pc[gi].q;
 #pragma unroll
         for (int m = 0; m < 8; m++) {
             const uint32_t k = t + 256 * m;
             const uint64_t v = lb[galois_src(k, g, n)];
             const uint32_t vl = (uint32_t)(v & M30), vh = (uint32_t)(v >> 30);
             smac(s0[m], vl, vh, split30(kb[k]));
-            smac(s1[m], vl, vh, split30(ka[k]));
+            smac(s1[m], vl, vh, split30(SEEDED ? seeded_a(row, k, qa) : ka[k]));
         }
         if ((j + 1) % SPLIT_CHUNK == 0) {  // more than 15 digits: keep the sums in bounds
 #pragma unroll
@@ -645,10 +650,11 @@ __global__ __launch_bounds__(256) void k_inner_sum2048(const uint64_t *__restric
 }
 
 // Generic-n version: one thread per output coefficient, gathered global reads.
+template <bool SEEDED>
 __global__ void k_inner(const uint64_t *__restrict__ d, size_t d_stride, const uint64_t *__restrict__ ext,
                         const uint64_t *__restrict__ key, uint64_t *__restrict__ acc,
                         const PrimeConsts *__restrict__ pc, uint32_t n, uint32_t l, uint32_t L, uint32_t K,
-                        uint32_t beta, uint32_t alpha, uint32_t g, size_t total) {
+                        uint32_t beta, uint32_t alpha, uint32_t g, uint64_t root, size_t total) {
     const uint32_t el = l + K;
     for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total;
          idx += (size_t)gridDim.x * blockDim.x) {
@@ -661,10 +667,12 @@ __global__ void k_inner(const uint64_t *__restrict__ d, size_t d_stride, const u
         for (uint32_t j = 0; j < beta; j++) {
             const bool own = e >= j * alpha && e < min(l, (j + 1) * alpha);
             const uint64_t v = own ? d[b * d_stride + (size_t)e * n + ks] : ext[((b * beta + j) * el + e) * n + ks];
-            const uint64_t *kr = key + ((size_t)j * 2 * (L + K) + gi) * n + k;
+            const uint64_t *kr = key + ((size_t)j * (SEEDED ? 1 : 2) * (L + K) + gi) * n + k;
             const uint32_t vl = (uint32_t)(v & M30), vh = (uint32_t)(v >> 30);
             smac(s0, vl, vh, split30(kr[0]));
-            smac(s1, vl, vh, split30(kr[(size_t)(L + K) * n]));
+            smac(s1, vl, vh,
+                 split30(SEEDED ? seeded_a(sm_at(root, (uint64_t)j * (L + K) + gi), k, pc[gi].q)
+                                : kr[(size_t)(L + K) * n]));
             if ((j + 1) % SPLIT_CHUNK == 0) {  // more than 15 digits: keep the sums in bounds
                 snorm(s0);
                 snorm(s1);
@@ -1034,13 +1042,17 @@ static int ks_modup(ckks_ctx *c, LevelTables *lt, int B, int l, const uint64_t *
 // Inner product of sigma_g(ModUp(d)) with the key, then ModDown up to the
 // NTT-domain conversion: leaves the Q-limbs of the accumulators in w.acc and
 // the converted P-part in w.conv; the caller runs the final kernel.
-static Steps one_step(const uint64_t *key, uint32_t g, int B) {
+static Steps one_step(const uint64_t *key, uint32_t g, int B, const uint64_t *seed = nullptr) {
     Steps st{};
     st.key[0] = key;
     st.g[0] = g;
     st.count = 1;
     st.B = (uint32_t)B;
     st.shared = 0;
+    if (seed) {
+        st.seeded = 1;
+        st.root[0] = key_seed_root(*seed);
+    }
     return st;
 }
 
@@ -1052,15 +1064,17 @@ static int ks_inner(ckks_ctx *c, LevelTables *lt, int l, const uint64_t *d, size
     const size_t nout = (size_t)st.count * st.B;
     ProfScope ps_(c, st.shared ? "ks_inner_product_hoisted" : "ks_inner_product", s);
     if (n == 2048) {
-        hipLaunchKernelGGL(k_inner2048, dim3(xcd_blocks(st.count * el, st.B)), dim3(256), 0, s, d, d_stride, w.ext,
-                           st, w.acc, c->d_pc, (uint32_t)l, L, K, beta, c->alpha, 0u, el);
+        auto kern = st.seeded ? k_inner2048<true> : k_inner2048<false>;
+        hipLaunchKernelGGL(kern, dim3(xcd_blocks(st.count * el, st.B)), dim3(256), 0, s, d, d_stride, w.ext, st,
+                           w.acc, c->d_pc, (uint32_t)l, L, K, beta, c->alpha, 0u, el);
     } else {  // generic n: one launch per step
+        auto kern = st.seeded ? k_inner<true> : k_inner<false>;
         for (uint32_t j = 0; j < st.count; j++) {
             const size_t total = (size_t)st.B * el * n;
             const size_t in_off = st.shared ? 0 : (size_t)j * st.B;
-            hipLaunchKernelGGL(k_inner, grid_for(total), dim3(256), 0, s, d + in_off * d_stride, d_stride,
+            hipLaunchKernelGGL(kern, grid_for(total), dim3(256), 0, s, d + in_off * d_stride, d_stride,
                                w.ext + in_off * beta * el * n, st.key[j], w.acc + (size_t)j * st.B * 2 * el * n,
-                               c->d_pc, n, (uint32_t)l, L, K, beta, c->alpha, st.g[j], total);
+                               c->d_pc, n, (uint32_t)l, L, K, beta, c->alpha, st.g[j], st.root[j], total);
         }
     }
     LAUNCH_CHECK();
@@ -1077,7 +1091,7 @@ static int ks_inner_giant(ckks_ctx *c, LevelTables *lt, int l, const uint64_t *x
     const size_t per = (size_t)l * c->n;
     {
         ProfScope ps_(c, "ks_inner_product", s);
-        hipLaunchKernelGGL(k_inner2048, dim3(xcd_blocks(st.count * K, st.B)), dim3(256), 0, s, x + per, x_stride,
+        hipLaunchKernelGGL(k_inner2048<false>, dim3(xcd_blocks(st.count * K, st.B)), dim3(256), 0, s, x + per, x_stride,
                            w.ext, st, w.acc, c->d_pc, (uint32_t)l, L, K, beta, c->alpha, (uint32_t)l, K);
     }
     LAUNCH_CHECK();
@@ -1197,7 +1211,7 @@ static size_t bsgs_words(const ckks_ctx *c, int B, int l, int bs, int gs) {
 size_t ws_bytes_bsgs(const ckks_ctx *c, int B, int l, int bs, int gs) { return bsgs_words(c, B, l, bs, gs) * 8; }
 
 int op_mul_tensor_relin(ckks_ctx *c, const uint64_t *a, const uint64_t *b, const uint64_t *rlk, uint64_t *out, int B,
-                        int l, void *ws, hipStream_t s) {
+                        int l, void *ws, hipStream_t s, const uint64_t *seed) {
     int e = CKKS_OK;
     LevelTables *lt = level_tables(c, l, &e);
     if (!lt) return e;
@@ -1211,7 +1225,7 @@ int op_mul_tensor_relin(ckks_ctx *c, const uint64_t *a, const uint64_t *b, const
     }
     LAUNCH_CHECK();
     const size_t per = (size_t)l * n;
-    const Steps st = one_step(rlk, 1, B);
+    const Steps st = one_step(rlk, 1, B, seed);
     if ((e = ks_modup(c, lt, B, l, w.d, per, w, s))) return e;
     if ((e = ks_inner(c, lt, l, w.d, per, st, w, s))) return e;
     if ((e = ks_moddown_conv(c, B, l, w, s))) return e;
@@ -1258,7 +1272,7 @@ static int rotate_final(ckks_ctx *c, const uint64_t *in, uint64_t *out, int l, c
 // Rotation: ModUp of c1 as stored (no permuted copy), the automorphism applied
 // as a gather of the extended digits inside the key inner product.
 int op_rotate(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, uint32_t g, const uint64_t *key, void *ws,
-              bool accumulate, hipStream_t s) {
+              bool accumulate, hipStream_t s, const uint64_t *seed) {
     int e = CKKS_OK;
     LevelTables *lt = level_tables(c, l, &e);
     if (!lt) return e;
@@ -1266,11 +1280,36 @@ int op_rotate(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, uint
     ks_words(c, B, l, &w, (uint64_t *)ws);
     const size_t per = (size_t)l * c->n;
     const uint64_t *c1 = in + per;
-    const Steps st = one_step(key, g, B);
+    const Steps st = one_step(key, g, B, seed);
     if ((e = ks_modup(c, lt, B, l, c1, 2 * per, w, s))) return e;
     if ((e = ks_inner(c, lt, l, c1, 2 * per, st, w, s))) return e;
     if ((e = ks_moddown_conv(c, B, l, w, s))) return e;
     return rotate_final(c, in, out, l, st, w, accumulate, s);
+}
+
+// Seed-expanded key -> stored format: out[j][0] = b[j], out[j][1][i][k] = the
+// seeded a-part residue of (digit j, key prime i).
+__global__ void k_key_expand(const uint64_t *__restrict__ kb, uint64_t *__restrict__ out,
+                             const PrimeConsts *__restrict__ pc, uint32_t n, uint32_t tot, uint64_t root,
+                             size_t total) {
+    for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total;
+         idx += (size_t)gridDim.x * blockDim.x) {
+        const uint32_t k = idx % n;
+        const size_t row = idx / n;  // j * tot + i
+        const uint32_t i = row % tot;
+        const size_t j = row / tot;
+        out[((j * 2 + 0) * tot + i) * n + k] = kb[idx];
+        out[((j * 2 + 1) * tot + i) * n + k] = seeded_a(sm_at(root, row), k, pc[i].q);
+    }
+}
+
+int op_key_expand(ckks_ctx *c, const uint64_t *key_b, uint64_t seed, uint64_t *key_out, hipStream_t s) {
+    const uint32_t tot = c->L + c->K;
+    const size_t total = (size_t)c->dnum * tot * c->n;
+    hipLaunchKernelGGL(k_key_expand, grid_for(total), dim3(256), 0, s, key_b, key_out, c->d_pc, c->n, tot,
+                       key_seed_root(seed), total);
+    LAUNCH_CHECK();
+    return CKKS_OK;
 }
 
 int op_rescale(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, void *ws, hipStream_t s) {

@@ -16,11 +16,14 @@ size_t ws_bytes_rotate(const ckks_ctx *c, int B, int l);
 size_t ws_bytes_rescale(const ckks_ctx *c, int B, int l);
 size_t ws_bytes_bsgs(const ckks_ctx *c, int B, int l, int bs, int gs);
 
+// seed: null for a stored key [dnum][2][L + K][n]; else the key holds its b rows
+// only ([dnum][L + K][n]) and its a rows are regenerated from *seed.
 int op_mul_tensor_relin(ckks_ctx *c, const uint64_t *a, const uint64_t *b, const uint64_t *rlk, uint64_t *out, int B,
-                        int l, void *ws, hipStream_t s);
+                        int l, void *ws, hipStream_t s, const uint64_t *seed = nullptr);
 int op_rescale(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, void *ws, hipStream_t s);
 int op_rotate(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, uint32_t g, const uint64_t *key, void *ws,
-              bool accumulate, hipStream_t s);
+              bool accumulate, hipStream_t s, const uint64_t *seed = nullptr);
+int op_key_expand(ckks_ctx *c, const uint64_t *key_b, uint64_t seed, uint64_t *key_out, hipStream_t s);
 int op_bsgs(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, const uint64_t *diags, int bs, int gs,
             const uint64_t *const *baby, const uint64_t *const *giant, bool rescale, void *ws, hipStream_t s);
 // ModRaise: centered lift of [B][2][l0][n] (primes [0, l0)) to [B][2][lt][n].

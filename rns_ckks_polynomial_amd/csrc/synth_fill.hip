@@ -6,17 +6,6 @@
 
 namespace ckks {
 
-__device__ __forceinline__ uint64_t sm_mix(uint64_t z) {
-    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
-    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
-    return z ^ (z >> 31);
-}
-__device__ __forceinline__ uint64_t sm_at(uint64_t s, uint64_t i) { return sm_mix(s + (i + 1) * 0x9e3779b97f4a7c15ull); }
-static uint64_t h_mix(uint64_t z) {
-    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
-    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
-    return z ^ (z >> 31);
-}
 
 __global__ void k_fill_uniform(uint64_t *__restrict__ dst, const PrimeConsts *__restrict__ pc, uint32_t n,
                                uint32_t nl, uint32_t first, uint64_t key, uint64_t stream0, size_t total) {
@@ -38,7 +27,7 @@ __global__ void k_fill_uniform(uint64_t *__restrict__ dst, const PrimeConsts *__
 
 int op_fill_uniform(const ckks_ctx *c, uint64_t *dst, int count, int first, int nlimbs, uint64_t seed, uint64_t tag,
                     uint64_t stream0, hipStream_t s) {
-    const uint64_t key = h_mix(seed + (tag + 1) * 0x9e3779b97f4a7c15ull);
+    const uint64_t key = sm_at(seed, tag);
     const size_t total = (size_t)count * nlimbs * c->n;
     if (!total) return CKKS_OK;
     size_t blocks = std::min<size_t>((total + 255) / 256, 1u << 20);

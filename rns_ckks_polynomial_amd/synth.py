@@ -67,6 +67,32 @@ def words(seed: int, tag: int, j, count: int) -> np.ndarray:
     return splitmix(k[..., None], idx)
 
 
+TAG_KEY_SEEDED = 10  # a rows of seed-expanded switching keys
+
+
+def mulhi_mod(w, q) -> np.ndarray:
+    """floor(w q / 2^64) for 64-bit words w and moduli q < 2^64: a residue in [0, q)."""
+    w = np.asarray(w, dtype=np.uint64)
+    q = np.asarray(q, dtype=np.uint64)
+    lo32 = np.uint64(0xFFFFFFFF)
+    s32 = np.uint64(32)
+    wl, wh, ql, qh = w & lo32, w >> s32, q & lo32, q >> s32
+    with np.errstate(over="ignore"):
+        m1 = wh * ql + ((wl * ql) >> s32)
+        m2 = wl * qh + (m1 & lo32)
+        return wh * qh + (m1 >> s32) + (m2 >> s32)
+
+
+def seeded_key_a(seed: int, dnum: int, moduli, n: int) -> np.ndarray:
+    """The a rows [dnum][len(moduli)][n] of a seed-expanded switching key:
+    residue k of row (j, i) is floor(w q_i / 2^64) with w word k of stream
+    j * len(moduli) + i under TAG_KEY_SEEDED (moduli = all L + K key primes)."""
+    moduli = np.asarray(moduli, dtype=np.uint64)
+    tot = len(moduli)
+    w = words(seed, TAG_KEY_SEEDED, np.arange(dnum * tot, dtype=np.uint64), n).reshape(dnum, tot, n)
+    return mulhi_mod(w, moduli[None, :, None])
+
+
 def uniform_mod(seed: int, tag: int, stream_ids, moduli, n: int) -> np.ndarray:
     """Uniform residues: out[r, i] in [0, moduli[r]) for stream stream_ids[r]."""
     stream_ids = np.atleast_1d(np.asarray(stream_ids, dtype=np.uint64))

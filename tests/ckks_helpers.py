@@ -36,14 +36,15 @@ class Keys:
         self.s_ntt = ctx.coeffs_to_ntt(self.s_coef, np.arange(tot))
         self._key_count = 0
 
-    def swk(self, sp_ntt):
+    def swk(self, sp_ntt, a=None):
         ctx = self.ctx
         tot = ctx.L + ctx.K
         j = self._key_count
         self._key_count += 1
         streams = np.arange(ctx.dnum * tot, dtype=np.uint64) + np.uint64(j * 1_000_003)
         mods = np.tile(ctx.primes, ctx.dnum)
-        a = synth.uniform_mod(self.seed, synth.TAG_KEY_A, streams, mods, ctx.n).reshape(ctx.dnum, tot, ctx.n)
+        if a is None:
+            a = synth.uniform_mod(self.seed, synth.TAG_KEY_A, streams, mods, ctx.n).reshape(ctx.dnum, tot, ctx.n)
         e = np.stack([synth.gaussian_ints(self.seed, synth.TAG_ERROR, 1000 + j * 64 + d, ctx.n)
                       for d in range(ctx.dnum)])
         return ctx.keygen_swk(self.s_ntt, sp_ntt, a, e)
@@ -60,6 +61,13 @@ class Keys:
         tot = self.ctx.L + self.ctx.K
         sp = self.ctx.automorph(self.s_ntt, g, tot)
         return self.swk(sp)
+
+    def seeded_galois_key(self, g: int, key_seed: int):
+        """A Galois key whose a rows are the seed-expanded ones: (b rows, full key)."""
+        ctx = self.ctx
+        a = synth.seeded_key_a(key_seed, ctx.dnum, ctx.primes, ctx.n)
+        key = self.swk(ctx.automorph(self.s_ntt, g, ctx.L + ctx.K), a=a)
+        return np.ascontiguousarray(key[:, 0]), key
 
     def encrypt(self, z, delta: float, l: int, j: int):
         ctx = self.ctx
