@@ -41,19 +41,19 @@ LIMB = N * 8
 # counters (profiles/bench_step_n2048_l112_b8_hbm_counters.md).  Valid only for
 # the kernel sources they were taken on (hash of rns_ckks_polynomial_amd/csrc).
 MEASURED_TRAFFIC = {
-    "source_sha": "35410c2b2b961681",
+    "source_sha": "873818a58232a3ba",
     "bytes_per_launch": {
-        "ks_modup_convert": 895086129,
-        "ks_moddown_convert": 510172947,
-        "bsgs_mac": 3758170954,
-        "ks_ntt_ext": 1322224454,
-        "ks_inner_product_sum": 2849251223,
-        "rotate_final": 3192128250,
-        "ntt_fwd": 62574880,
-        "ntt_inv": 62598942,
-        "giant_final": 297537846,
-        "ks_intt_modup": 326834793,
-        "ks_intt_moddown": 310303500
+        "ks_modup_convert": 813258472,
+        "ks_moddown_convert": 510187579,
+        "bsgs_mac": 3758231861,
+        "ks_ntt_ext": 1322513882,
+        "ks_inner_product_sum": 2848399181,
+        "rotate_final": 3192207429,
+        "ntt_fwd": 62577099,
+        "ntt_inv": 62599113,
+        "giant_final": 297537908,
+        "ks_intt_modup": 326825562,
+        "ks_intt_moddown": 310307628
     },
 }
 
@@ -83,6 +83,8 @@ def parse():
                    help="only time the bootstrap of 8 ciphertexts on the 2100 + 263 prime chain "
                         "(19 -> 2100 -> 2083 primes; about 160 GB of HBM)")
     p.add_argument("--boot-reps", type=int, default=2)
+    p.add_argument("--step-only", action="store_true",
+                   help="skip the EvalMod, bootstrapping and seeded-key legs (profiler runs of the step)")
     return p.parse_args()
 
 
@@ -366,18 +368,17 @@ def main():
 
     # EvalMod (bootstrapping's modular reduction, outside the step): batch 8 at
     # the 112-prime level, degree-31 cosine interpolant on [-8, 8], 3 double angles
-    em = eval_mod_timing(g, a, rlk, torch)
-
-    # seed-expanded switching keys: rotation with the key's a rows regenerated in the kernel
-    seeded = seeded_key_timing(g, torch, a, keys[0])
-
-    # bootstrapping of 8 ciphertexts on this 112-prime chain (1 -> 112 -> 95 primes; slot_to_coeff's
-    # diagonals at 96 primes), with the
-    # step's rotation keys and a second diagonal set for slot_to_coeff (outside the step)
-    stc = torch.empty((GS, BS, boot_stc_level(L), N), dtype=u64, device=dev)
-    g.fill_uniform(stc, 0xC0DE0005, synth.TAG_DIAG, 0)
-    boot = bootstrap_timing(g, torch, L, 1, diags, stc, baby, giant, keys[0], rlk, 2, 0xC0DE0006)
-    del stc
+    em = boot = seeded = None
+    if not args.step_only:
+        em = eval_mod_timing(g, a, rlk, torch)
+        # seed-expanded switching keys: rotation with the key's a rows regenerated in the kernel
+        seeded = seeded_key_timing(g, torch, a, keys[0])
+        # bootstrapping of 8 ciphertexts on this 112-prime chain (1 -> 112 -> 95 primes; slot_to_coeff's
+        # diagonals at 96 primes) with the step's rotation keys and a second diagonal set
+        stc = torch.empty((GS, BS, boot_stc_level(L), N), dtype=u64, device=dev)
+        g.fill_uniform(stc, 0xC0DE0005, synth.TAG_DIAG, 0)
+        boot = bootstrap_timing(g, torch, L, 1, diags, stc, baby, giant, keys[0], rlk, 2, 0xC0DE0006)
+        del stc
 
     # per-kernel launch times (library event profiler) over profiled steps + the NTT pair
     g.profile_begin()
