@@ -33,6 +33,10 @@ BETA = (L + ALPHA - 1) // ALPHA
 HBM_PEAK_GBS = 8000.0
 # VALU: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz; v_mad_u64_u32 (32x32+64) issues at full rate.
 VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
+# MFMA int8 (dense): 5.0 POP/s.  The base conversions run on it: a 60 x 60-bit
+# product is 8 x 8 signed 8-bit digit products, 64 multiply-adds = 128 int8 ops.
+MFMA_I8_PEAK_TOPS = 5000.0
+I8_OPS_PER_PRODUCT = 128
 LIMB = N * 8
 
 # HBM bytes per launch (average over the launches of the step) measured with
@@ -251,7 +255,8 @@ def kernel_work():
     kernel in one step; launches differ in size since BSGS batches its steps).
     bytes: residues that must be read + written once (twiddles/tables excluded);
     mads: 32x32-bit multiply-adds, 4 per 60x60-bit product (the minimum on a
-    32-bit multiplier)."""
+    32-bit multiplier); products: 60x60-bit products of the base conversions,
+    which run on the matrix cores (I8_OPS_PER_PRODUCT int8 ops each)."""
     B, l, el, a, beta = BATCH, L, L + K, ALPHA, BETA
     sb, sg = BS - 1, GS - 1           # baby / giant key switches per ciphertext
     n_up = (1 + 1 + sg) * B           # ciphertexts through ModUp: relin, hoisted baby, giant
@@ -260,7 +265,7 @@ def kernel_work():
     return {
         "ks_intt_modup": {"bytes": 2 * n_up * l * limb},
         "ks_modup_u": {"bytes": n_up * l * limb},
-        "ks_modup_convert": {"mads": 4 * n_up * beta * a * (l + K - a) * N,
+        "ks_modup_convert": {"products": n_up * beta * a * (l + K - a) * N,
                              "bytes": (n_up * l + n_up * beta * (el - a)) * limb},
         "ks_ntt_ext": {"bytes": 2 * n_up * beta * (el - a) * limb},
         # relinearisation (all limbs) + the giant steps' P-limbs
@@ -272,7 +277,7 @@ def kernel_work():
         "ks_intt_moddown": {"bytes": 2 * n_dn * 2 * K * limb},
         "ks_moddown_u": {"bytes": n_dn * 2 * K * limb},
         # giant-step conversions are summed in the kernel: one output per ciphertext
-        "ks_moddown_convert": {"mads": 4 * n_dn * 2 * K * l * N,
+        "ks_moddown_convert": {"products": n_dn * 2 * K * l * N,
                                "bytes": (n_dn * 2 * K + (1 + sb + 1) * B * 2 * l) * limb},
         "rotate_final": {"bytes": sb * B * 7 * l * limb},
         # conv in, 4 partial sums in, output read + written
@@ -398,6 +403,9 @@ def main():
             row["algo_GBps"] = w["bytes"] / (per_step * 1e-3) / 1e9
         if "mads" in w:
             row["algo_Tmads"] = w["mads"] / (per_step * 1e-3) / 1e12
+        if "products" in w:
+            row["algo_Tproducts"] = w["products"] / (per_step * 1e-3) / 1e12
+            row["algo_int8_TOPs"] = row["algo_Tproducts"] * I8_OPS_PER_PRODUCT
         kernels[name] = row
     for name in ("ntt_fwd", "ntt_inv"):
         if name in kernels:
@@ -405,7 +413,12 @@ def main():
     step_kernels = {k: v for k, v in kernels.items() if k not in ("ntt_fwd", "ntt_inv")}
     dom = max(step_kernels, key=lambda k: step_kernels[k]["total_ms_per_step"])
     dw, drow = work.get(dom, {}), kernels[dom]
-    if "mads" in dw:
+    if "products" in dw:
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": drow["algo_int8_TOPs"], "peak": MFMA_I8_PEAK_TOPS,
+                    "unit": "int8 TOP/s", "traffic": None,
+                    "work_per_step": f"{dw['products']} 60x60-bit products x {I8_OPS_PER_PRODUCT} int8 ops "
+                                     f"in {drow['launches'] // args.profile_steps} launch(es)"}
+    elif "mads" in dw:
         roofline = {"bound": "alu", "kernel": dom, "achieved": drow["algo_Tmads"], "peak": VALU_PEAK_TOPS,
                     "unit": "T int32-MAD/s", "traffic": None,
                     "work_per_step": f"{dw['mads']} 32x32-bit multiply-adds (4 per 60x60-bit product) "

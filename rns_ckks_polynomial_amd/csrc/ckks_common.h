@@ -230,29 +230,38 @@ __device__ __forceinline__ void sreduce(Split3 &s, const PrimeConsts &P) {
 // The centered CRT value x_c of residues x_i modulo B = prod b_i is
 //   x_c = sum_i y_i Bhat_i - u B,   y_i = [x_i Bhat_i^-1]_{b_i},
 //   u = round(sum_i y_i / b_i)  (= floor(sum) + [x > (B-1)/2]).
-constexpr uint32_t CONV_ROW_PAD = 7;
-constexpr uint32_t CONV_COL_PAD = 8;
 struct BasisDev {
     uint32_t m;            // number of primes in the basis
     uint32_t first;        // global index of the first basis prime
-    uint32_t ntot;         // number of chain primes (L + K): row count of H / negB
+    uint32_t ntot;         // number of chain primes (L + K)
     uint32_t pad;
     const uint64_t *inv_hat;  // [m][2]  Shoup pair of [Bhat_i^-1]_{b_i}
     const uint64_t *hat_mod;  // [m][2]  Shoup pair of [Bhat_i]_{b_i}   (recovers x_i from y_i)
     const uint64_t *R;        // [m]     floor(2^123 / b_i)                (fixed-point 1/b_i)
-    // [Bhat_i]_t in split30 layout, row i = input prime, column = target position:
-    // for a chain digit the positions run over the special primes first, then
-    // the chain primes outside the digit (so the targets at any level are a
-    // prefix); for the special basis they run over the chain primes.  Rows are
-    // padded with zeros to a multiple of CONV_ROW_PAD and each row holds
-    // CONV_COL_PAD spare columns, so whole tiles can be read without bounds checks.
-    const uint64_t *HT;
-    uint32_t hstride;         // row length of HT (positions + CONV_COL_PAD)
-    uint32_t mpad;            // row count of HT
-    const uint64_t *negB;     // [ntot]     [-B]_t, split30 layout
     const uint64_t *garner;   // [m][m][2]  Shoup pair of b_k^-1 mod b_i (k < i used)
     const uint64_t *half;     // [m]        mixed-radix digits of (B-1)/2
+    // Conversion tables.  Target positions: for a chain digit, the special primes
+    // first, then the chain primes outside the digit (so the targets at any level
+    // are a prefix); for the special basis or a chain prefix, the chain primes.
+    // Rows r < mk (mk = m + 1 rounded up to 32): r < m is [Bhat_r]_t, r = m is
+    // [-B]_t (the u row), the rest zero.
+    //   HD[p][b][r]: signed base-256 digit b of row r's value at target position p
+    //               (positions padded to a multiple of 32 with zero digits);
+    //   RC[p][MF_RC]: the target's reduction constants (see k_convert_mfma).
+    const int8_t *HD;
+    const uint64_t *RC;
+    uint32_t mk;
 };
+// Signed base-256 digits of a value below 2^63: byte a of digit_form(v), read as
+// an int8, is d_a with v = sum_a d_a 256^a and -128 <= d_a <= 127 (adding 128 in
+// every byte position, then flipping each byte's top bit, subtracts it back).
+__host__ __device__ __forceinline__ uint64_t digit_form(uint64_t v) {
+    return (v + 0x8080808080808080ull) ^ 0x8080808080808080ull;
+}
+// RC row: [0..6] 256^s mod t for s = 8..14 (split30 layout), [7] 2^60 mod t,
+// [8] its Shoup quotient, [9] t, [10] 8t - [2^91]_t.
+constexpr uint32_t MF_RC = 11;
+constexpr uint32_t MF_MAX_ROWS = 2048;  // |S_s| <= 8 rows 2^14 <= 2^28
 
 // ------------------------------------------------------------------ SplitMix64
 // Counter-based generator (G. Steele, D. Lea, C. Flood, "Fast splittable

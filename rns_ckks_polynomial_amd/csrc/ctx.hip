@@ -163,8 +163,7 @@ int build_basis(ckks_ctx *ctx, uint32_t first, uint32_t m, BasisDev *out, std::v
     }
     for (uint32_t i = 0; i < m; i++) half[i] = big_divmod(B, b[i]);
 
-    // the conversion kernels read H transposed, in target-position order and in
-    // the split layout (lo32 = h mod 2^30, hi32 = h >> 30)
+    // target positions (see BasisDev)
     std::vector<uint32_t> pos;  // position -> target prime
     if (first < ctx->L && !chain_targets) {
         for (uint32_t t = ctx->L; t < ntot; t++) pos.push_back(t);
@@ -173,27 +172,39 @@ int build_basis(ckks_ctx *ctx, uint32_t first, uint32_t m, BasisDev *out, std::v
     } else {
         for (uint32_t t = 0; t < ctx->L; t++) pos.push_back(t);
     }
-    const uint32_t hstride = (uint32_t)pos.size() + CONV_COL_PAD;
-    const uint32_t mpad = (m + CONV_ROW_PAD - 1) / CONV_ROW_PAD * CONV_ROW_PAD;
-    std::vector<uint64_t> Hs((size_t)mpad * hstride, 0);
-    for (uint32_t i = 0; i < m; i++)
-        for (uint32_t p = 0; p < pos.size(); p++) {
-            const uint64_t h = H[(size_t)pos[p] * m + i];
-            Hs[(size_t)i * hstride + p] = (h & ((1ull << 30) - 1)) | ((h >> 30) << 32);
+    // digit tables and reduction constants of the conversion (see BasisDev)
+    const uint32_t mk = (m + 1 + 31) / 32 * 32, npos = (uint32_t)pos.size(), npad = (npos + 31) / 32 * 32;
+    std::vector<int8_t> hd((size_t)npad * 8 * mk, 0);
+    std::vector<uint64_t> rc((size_t)npad * MF_RC, 0);
+    for (uint32_t p = 0; p < npos; p++) {
+        const uint32_t t = pos[p];
+        const uint64_t qt = ctx->primes[t];
+        for (uint32_t r = 0; r <= m; r++) {
+            const uint64_t v = digit_form(r < m ? H[(size_t)t * m + r] : negB[t]);
+            for (uint32_t b = 0; b < 8; b++) hd[((size_t)p * 8 + b) * mk + r] = (int8_t)(uint8_t)(v >> (8 * b));
         }
+        uint64_t *row = rc.data() + (size_t)p * MF_RC;
+        uint64_t w = h_powmod(2, 64, qt);  // 256^8 mod t
+        for (uint32_t s2 = 0; s2 < 7; s2++) {
+            row[s2] = (w & ((1ull << 30) - 1)) | ((w >> 30) << 32);
+            w = h_mulmod(w, 256, qt);
+        }
+        row[7] = h_powmod(2, 60, qt);
+        row[8] = h_shoup(row[7], qt);
+        row[9] = qt;
+        row[10] = 8 * qt - h_powmod(2, 91, qt);
+    }
     int err = CKKS_OK;
     BasisDev d{};
     d.m = m;
     d.first = first;
     d.ntot = ntot;
+    d.mk = mk;
+    d.HD = dev_upload(hd, owned, &err);
+    d.RC = dev_upload(rc, owned, &err);
     d.inv_hat = dev_upload(inv_hat, owned, &err);
     d.hat_mod = dev_upload(hat_mod, owned, &err);
     d.R = dev_upload(R, owned, &err);
-    d.HT = dev_upload(Hs, owned, &err);
-    d.hstride = hstride;
-    d.mpad = mpad;
-    for (auto &v : negB) v = (v & ((1ull << 30) - 1)) | ((v >> 30) << 32);  // split30 for the conversion tail
-    d.negB = dev_upload(negB, owned, &err);
     d.garner = dev_upload(garner, owned, &err);
     d.half = dev_upload(half, owned, &err);
     *out = d;

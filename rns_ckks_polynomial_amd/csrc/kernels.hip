@@ -307,22 +307,14 @@ __global__ void k_basis_u(const BasisDev *__restrict__ bases, SetLayout lay, uin
 }
 
 // ---------------------------------------------------------------------
-// Base conversion: out_t = sum_i y_i [Bhat_i]_t + u [-B]_t mod t.
-// One thread per coefficient and CT targets per workgroup.  The table row of
-// input i for the block's CT targets is contiguous (target-position order),
-// wave-uniform and read-only, so it is fetched with scalar loads and used as
-// SGPR operands; the inputs y_i are prefetched CONV_ROW_PAD rows ahead.  Each
-// product is four v_mad_u64_u32 into split partial sums (see smac), folded
-// into 128 bits every SPLIT_CHUNK inputs.
+// Exact base conversion, out_t = sum_i y_i [Bhat_i]_t + u [-B]_t mod t, of
+// "sets" of inputs (one per digit and ciphertext, or summed sets of several
+// steps) onto target positions.
 // ---------------------------------------------------------------------
-constexpr int CT = 8;
-constexpr int YC = (int)CONV_ROW_PAD;  // rows per chunk
-static_assert(CT <= (int)CONV_COL_PAD, "tile reads stay inside a table row");
-
 struct ConvTargets {
-    // k_convert<0> (ModUp of digit [lo, lo+m)): target positions run over [L, L+K),
+    // MODE 0 (ModUp of digit [lo, lo+m)): target positions run over [L, L+K),
     // then [0, lo) u [lo+m, l); the outputs go to ext slots (special t -> l + t - L)
-    // k_convert<1> (ModDown): targets = [0, l) -> slot t
+    // MODE 1 (ModDown, ModRaise): targets = [0, l) -> slot t
     uint32_t l, L, K;
     size_t out_so, out_si;  // output limb base of set s: (s / inner) * out_so + (s % inner) * out_si
     // Summed conversions (nsum > 1): the input sets s + j * sum_stride, j < nsum,
@@ -340,106 +332,190 @@ __device__ __forceinline__ uint32_t conv_target(const ConvTargets &ct, uint32_t 
     return c < lo ? c : c + m;
 }
 
-// MODE 0: ModUp targets, MODE 1: ModDown targets.
+// ---------------------------------------------------------------------
+// Base conversion on the matrix cores.  The same sums as k_convert,
+//   out[k][t] = sum_r Y[k][r] H[r][t] mod t,
+// with the rows r of every summed set = its m inputs y_i (H = [Bhat_i]_t), then
+// its u (H = [-B]_t), then zeros up to BasisDev::mk.  Both operands are written
+// in signed base-256 digits (digit_form), so the product is
+//   sum_s 256^s S_s,   S_s = sum_{a+b=s} sum_r dY_a[k][r] dH_b[r][t],
+// and each digit pair (a, b) is one exact int8 x int8 -> int32 16x16x32 MFMA
+// adding into S_{a+b} (|S_s| <= 8 rows 2^14 <= 2^28 for rows <= MF_MAX_ROWS).
+// One wave computes 16 coefficients x 16 target positions at a time: lane l
+// supplies coefficient row l % 16 of Y and target column l % 16 of H, each with
+// the 8 rows 8 (l / 16) + j of a 32-row chunk, and ends with target column
+// l % 16 of the coefficient rows 4 (l / 16) + v (v < 4).
+// ---------------------------------------------------------------------
+typedef int mf_v4i __attribute__((ext_vector_type(4)));
+constexpr uint32_t MF_COEF = 64;  // coefficients per workgroup (4 waves x 16)
+constexpr uint32_t MF_TPB = 8;    // 16-position target tiles per workgroup
+
+// 4x4 byte transpose: o_b holds byte b of x0, x1, x2, x3 (in that order).
+__device__ __forceinline__ void bt4(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3, uint32_t &o0, uint32_t &o1,
+                                    uint32_t &o2, uint32_t &o3) {
+    const uint32_t p01l = __builtin_amdgcn_perm(x1, x0, 0x05010400u), p01h = __builtin_amdgcn_perm(x1, x0, 0x07030602u);
+    const uint32_t p23l = __builtin_amdgcn_perm(x3, x2, 0x05010400u), p23h = __builtin_amdgcn_perm(x3, x2, 0x07030602u);
+    o0 = __builtin_amdgcn_perm(p23l, p01l, 0x05040100u);
+    o1 = __builtin_amdgcn_perm(p23l, p01l, 0x07060302u);
+    o2 = __builtin_amdgcn_perm(p23h, p01h, 0x05040100u);
+    o3 = __builtin_amdgcn_perm(p23h, p01h, 0x07060302u);
+}
+
+constexpr uint32_t MF_HSTRIDE = 272;  // LDS bytes per target position (8 digits x 32 rows + bank padding)
+
 template <int MODE>
-__global__ __launch_bounds__(256) void k_convert(const BasisDev *__restrict__ bases, SetLayout lay,
-                                                  const uint64_t *__restrict__ y, const uint32_t *__restrict__ u,
-                                                  ConvTargets ct, uint64_t *__restrict__ out, uint32_t n,
-                                                  const PrimeConsts *__restrict__ pc) {
+__global__ __launch_bounds__(256, 2) void k_convert_mfma(const BasisDev *__restrict__ bases, SetLayout lay,
+                                                          const uint64_t *__restrict__ y,
+                                                          const uint32_t *__restrict__ u, ConvTargets ct,
+                                                          uint64_t *__restrict__ out, uint32_t n) {
+    // a basis whose rows fit one 32-row block (cps == 1): the workgroup's digit
+    // table rows and reduction constants are staged here once
+    __shared__ __align__(16) int8_t sh_h[MF_TPB * 16 * MF_HSTRIDE];
+    __shared__ uint64_t sh_rc[MF_TPB * 16 * MF_RC];
     const uint32_t s = blockIdx.z;
     const BasisDev &B = bases[lay.per_set_basis ? s % lay.inner : 0];
-    const uint32_t m = B.m, lo = B.first;
+    const uint32_t m = B.m, lo = B.first, mk = B.mk;
     const uint32_t ntarget = MODE == 0 ? ct.l - m + ct.K : ct.l;
-    const uint32_t tn0 = blockIdx.y * CT;
-    if (tn0 >= ntarget) return;
-    const uint32_t nt = min((uint32_t)CT, ntarget - tn0);
-    const uint32_t k = blockIdx.x * blockDim.x + threadIdx.x;
-    if (k >= n) return;
-    // row i at ht + i * hstride (zero rows past m); the constant address space
-    // lets the compiler fetch these wave-uniform rows with scalar loads
-    const __attribute__((address_space(4))) uint64_t *ht =
-        (const __attribute__((address_space(4))) uint64_t *)(B.HT + tn0);
-    const uint32_t hstride = B.hstride, mpad = B.mpad;
-    Split3 sp[CT];
-#pragma unroll
-    for (int a = 0; a < CT; a++) sp[a] = {0, 0, 0, 0};
-    // The summed sets' rows form one stream of chunks (YC rows each, mpad / YC
-    // chunks per set), so the input prefetch runs across set boundaries; the
-    // next table row is fetched one row ahead.  Inputs arrive in split30 form.
+    const uint32_t tile0 = blockIdx.y * MF_TPB;
+    if (tile0 * 16 >= ntarget) return;
+    const uint32_t tile_end = min(tile0 + MF_TPB, (ntarget + 15) / 16), ntile = tile_end - tile0;
+    const uint32_t lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
+    const uint32_t kb = blockIdx.x * MF_COEF + (threadIdx.x >> 6) * 16;
     const uint32_t part = ct.nsum > 1 ? s / ct.sum_stride : 0;
     const size_t sfirst = ct.nsum > 1 ? s + (size_t)part * (ct.spp - 1) * ct.sum_stride : s;
     const uint32_t nsets = ct.nsum > 1 ? min(ct.spp, ct.nsum - part * ct.spp) : 1;
-    // summed sets use inner == 1 (as the host sets it up): set j + 1 starts set_step words after set j
-    const uint64_t *pb = y + (sfirst / lay.inner) * lay.so + (sfirst % lay.inner) * lay.si + lay.off + k;
-    const size_t set_step = (size_t)ct.sum_stride * lay.so;
-    const uint32_t nchunks = nsets * (mpad / YC);
-    uint32_t pi = 0, pj = 0;  // first row and set index of the chunk being fetched (set base pb)
-    uint64_t yv[YC], yn[YC];
-#pragma unroll
-    for (int r = 0; r < YC; r++) yv[r] = pb[(size_t)min((uint32_t)r, m - 1) * n];
-    uint64_t hc[CT];  // table row in use; the next row is fetched one row ahead
-#pragma unroll
-    for (int a = 0; a < CT; a++) hc[a] = ht[a];
-    uint32_t i0 = 0;  // first table row of the current chunk
-    for (uint32_t chunk = 0; chunk < nchunks; chunk++) {
-        pi += YC;  // advance the fetch position to the next chunk
-        if (pi == mpad) {
-            pi = 0;
-            if (pj + 1 < nsets) {  // past the end: harmless reload of the last set
-                pj++;
-                pb += set_step;
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < YC; r++) yn[r] = pb[(size_t)min(pi + r, m - 1) * n];
-#pragma unroll
-        for (int r = 0; r < YC; r++) {  // rows past m: y repeats row m-1, the table row is zero
-            const uint32_t inext = i0 + r + 1 == mpad ? 0 : i0 + r + 1;
-            const __attribute__((address_space(4))) uint64_t *hr = ht + (size_t)inext * hstride;
-            uint64_t hn[CT];
-#pragma unroll
-            for (int a = 0; a < CT; a++) hn[a] = hr[a];
-            const uint32_t yl = (uint32_t)yv[r], yh = (uint32_t)(yv[r] >> 32);
-#pragma unroll
-            for (int a = 0; a < CT; a++) smac(sp[a], yl, yh, hc[a]);
-#pragma unroll
-            for (int a = 0; a < CT; a++) hc[a] = hn[a];
-        }
-        i0 = i0 + YC == mpad ? 0 : i0 + YC;
-        // every 2 chunks (14 products) snorm0, every 4 snorm_hi, every 8 fold a2
-        if (chunk & 1) {
-#pragma unroll
-            for (int a = 0; a < CT; a++) snorm0(sp[a]);
-            if (chunk & 2) {
-#pragma unroll
-                for (int a = 0; a < CT; a++) snorm_hi(sp[a]);
-                if (chunk & 4) {
-#pragma unroll
-                    for (int a = 0; a < CT; a++) {
-                        const uint32_t t =
-                            __builtin_amdgcn_readfirstlane(conv_target<MODE>(ct, tn0 + min(a, (int)nt - 1), lo, m));
-                        sfold60(sp[a], pc[t]);
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < YC; r++) yv[r] = yn[r];
+    const uint32_t cps = mk / 32, nch = nsets * cps;  // 32-row chunks per set, in all
+    const bool staged = cps == 1;
+    if (staged) {
+        // position p's 8 x 32 digit bytes are contiguous in HD (mk = 32): 16-byte copies
+        const uint32_t np = ntile * 16;
+        const int8_t *src = B.HD + (size_t)16 * tile0 * 256;
+        for (uint32_t q = threadIdx.x; q < np * 16; q += 256)
+            *(uint4 *)(sh_h + (q / 16) * MF_HSTRIDE + (q % 16) * 16) = *(const uint4 *)(src + (size_t)q * 16);
+        const uint64_t *rsrc = B.RC + (size_t)16 * tile0 * MF_RC;
+        for (uint32_t q = threadIdx.x; q < np * MF_RC; q += 256) sh_rc[q] = rsrc[q];
+        __syncthreads();
     }
-    uint64_t uu = 0;
-    for (uint32_t js = 0; js < nsets; js++) uu += u[(sfirst + (size_t)js * ct.sum_stride) * n + k];
-    const uint32_t ul = (uint32_t)(uu & M30), uh = (uint32_t)(uu >> 30);
-    uint64_t *ob = out + (s / lay.inner) * ct.out_so + (s % lay.inner) * ct.out_si + k;
+    const uint64_t *yb = y + (sfirst / lay.inner) * lay.so + (sfirst % lay.inner) * lay.si + lay.off + kb + col;
+    const size_t set_step = (size_t)ct.sum_stride * lay.so;
+    // rows 8 grp + j of chunk ch, loaded unconditionally (index clamped; the u row
+    // and the padding rows are substituted when the fragments are built)
+    auto load_rows = [&](uint64_t(&raw)[8], uint32_t &uraw, uint32_t ch) {
+        const uint32_t js = ch / cps, r0 = (ch % cps) * 32 + 8 * grp;
+        const uint64_t *ys = yb + js * set_step;
 #pragma unroll
-    for (int a = 0; a < CT; a++) {
-        if (a >= (int)nt) break;
-        const uint32_t t = __builtin_amdgcn_readfirstlane(conv_target<MODE>(ct, tn0 + a, lo, m));
-        const PrimeConsts &P = pc[t];
-        // u [-B]_t joins the sum as one more product
-        smac(sp[a], ul, uh, ((const __attribute__((address_space(4))) uint64_t *)B.negB)[t]);
-        const uint64_t r = sfinal_mod(sp[a], P);
+        for (int j = 0; j < 8; j++) raw[j] = ys[(size_t)min(r0 + j, m - 1) * n];
+        uraw = u[(sfirst + (size_t)js * ct.sum_stride) * n + kb + col];
+    };
+    long A[8];  // digit plane a of the lane's 8 rows (byte j = row 8 grp + j)
+    auto build_a = [&](const uint64_t(&raw)[8], uint32_t uraw, uint32_t ch) {
+        const uint32_t r0 = (ch % cps) * 32 + 8 * grp;
+        uint64_t z[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const uint32_t r = r0 + j;
+            z[j] = digit_form(r < m ? unsplit30(raw[j]) : (r == m ? (uint64_t)uraw : 0));
+        }
+        uint32_t o[2][8];
+        bt4((uint32_t)z[0], (uint32_t)z[1], (uint32_t)z[2], (uint32_t)z[3], o[0][0], o[0][1], o[0][2], o[0][3]);
+        bt4((uint32_t)(z[0] >> 32), (uint32_t)(z[1] >> 32), (uint32_t)(z[2] >> 32), (uint32_t)(z[3] >> 32), o[0][4],
+            o[0][5], o[0][6], o[0][7]);
+        bt4((uint32_t)z[4], (uint32_t)z[5], (uint32_t)z[6], (uint32_t)z[7], o[1][0], o[1][1], o[1][2], o[1][3]);
+        bt4((uint32_t)(z[4] >> 32), (uint32_t)(z[5] >> 32), (uint32_t)(z[6] >> 32), (uint32_t)(z[7] >> 32), o[1][4],
+            o[1][5], o[1][6], o[1][7]);
+#pragma unroll
+        for (int a = 0; a < 8; a++) A[a] = (long)(((uint64_t)o[1][a] << 32) | o[0][a]);
+    };
+    long Hb[8];
+    auto load_h = [&](uint32_t tile, uint32_t ch) {
+        if (staged) {
+            const int8_t *h = sh_h + ((tile - tile0) * 16 + col) * MF_HSTRIDE + 8 * grp;
+#pragma unroll
+            for (int b = 0; b < 8; b++) Hb[b] = *(const long *)(h + 32 * b);
+        } else {
+            const int8_t *h = B.HD + (size_t)(16 * tile + col) * 8 * mk + (ch % cps) * 32 + 8 * grp;
+#pragma unroll
+            for (int b = 0; b < 8; b++) Hb[b] = *(const long *)(h + (size_t)b * mk);
+        }
+    };
+    // powers of two of the recombination, kept in registers so that each term
+    // is one 32 x 32 + 64-bit multiply-add
+    int32_t w2[7] = {1 << 8, 1 << 16, 1 << 24, 1 << 2, 1 << 10, 1 << 18, 1 << 26};
+#pragma unroll
+    for (int d = 0; d < 7; d++) asm volatile("" : "+v"(w2[d]));
+    mf_v4i acc[15];
+    // the flat sequence g = (tile - tile0) nch + ch; rows are fetched two chunks ahead
+    const uint32_t total = ntile * nch;
+    uint64_t rb[2][8];
+    uint32_t ub[2];
+    load_rows(rb[0], ub[0], 0);
+    if (nch == 1) build_a(rb[0], ub[0], 0);
+    else load_rows(rb[1], ub[1], 1 % nch);
+    auto step = [&](uint64_t(&raw)[8], uint32_t &uraw, uint32_t g) {
+        const uint32_t tile = tile0 + g / nch, ch = g % nch;
+        if (ch == 0) {
+#pragma unroll
+            for (int d = 0; d < 15; d++) acc[d] = mf_v4i{0, 0, 0, 0};
+        }
+        if (nch > 1) {
+            build_a(raw, uraw, ch);
+            if (g + 2 < total) load_rows(raw, uraw, (g + 2) % nch);
+        }
+        if (ch == 0 || cps > 1) load_h(tile, ch);
+#pragma unroll
+        for (int b = 0; b < 8; b++)
+#pragma unroll
+            for (int a = 0; a < 8; a++)
+                acc[a + b] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A[a], Hb[b], acc[a + b], 0, 0, 0);
+        if (ch + 1 < nch) return;
+        const uint32_t p = 16 * tile + col;
+        if (p >= ntarget) return;  // padding columns: every MFMA above ran on the whole wave
+        const uint64_t *rc = staged ? sh_rc + ((tile - tile0) * 16 + col) * MF_RC : B.RC + (size_t)p * MF_RC;
+        int32_t clo[7], chi[7];
+#pragma unroll
+        for (int d = 0; d < 7; d++) {
+            const uint64_t c = rc[d];
+            clo[d] = (int32_t)(uint32_t)c;
+            chi[d] = (int32_t)(uint32_t)(c >> 32);
+        }
+        const uint64_t r60 = rc[7], r60p = rc[8], tq = rc[9], kfix = rc[10];
+        const uint32_t t = conv_target<MODE>(ct, p, lo, m);
         const uint32_t slot = (MODE == 0 && t >= ct.L) ? ct.l + (t - ct.L) : t;
-        ob[(size_t)slot * n] = r;
+        uint64_t *ob = out + (s / lay.inner) * ct.out_so + (s % lay.inner) * ct.out_si + (size_t)slot * n + kb + 4 * grp;
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+            // value = lo + 2^30 hi: lo takes the weights 1 .. 2^24 and the low 30 bits
+            // of 256^s mod t (s >= 8), hi the weights 2^2 .. 2^26 and the high 30 bits;
+            // |S_s| <= 2^28 keeps both below 2^61 in magnitude
+            int64_t lo_s = (int64_t)acc[0][v];
+            lo_s += (int64_t)acc[1][v] * (int64_t)w2[0];
+            lo_s += (int64_t)acc[2][v] * (int64_t)w2[1];
+            lo_s += (int64_t)acc[3][v] * (int64_t)w2[2];
+            int64_t hi_s = (int64_t)acc[4][v] * (int64_t)w2[3];
+            hi_s += (int64_t)acc[5][v] * (int64_t)w2[4];
+            hi_s += (int64_t)acc[6][v] * (int64_t)w2[5];
+            hi_s += (int64_t)acc[7][v] * (int64_t)w2[6];
+#pragma unroll
+            for (int d = 0; d < 7; d++) {
+                lo_s += (int64_t)acc[8 + d][v] * (int64_t)clo[d];
+                hi_s += (int64_t)acc[8 + d][v] * (int64_t)chi[d];
+            }
+            // hi = 2^30 h1 + h0 (0 <= h0 < 2^30, |h1| < 2^31); 2^60 h1 = 2^60 (h1 + 2^31)
+            // - 2^91, and kfix = 8t - [2^91]_t makes the sum positive:
+            // 0 < x = lo + 2^30 h0 + [2^60 (h1 + 2^31)]_lazy + kfix < 2^63
+            const uint64_t h0 = (uint64_t)hi_s & M30;
+            const uint32_t h1b = (uint32_t)(hi_s >> 30) ^ 0x80000000u;
+            const uint64_t x = (uint64_t)lo_s + (h0 << 30) + shoup_lazy(h1b, r60, r60p, tq) + kfix;
+            // t in (2^59, 2^59 + 2^52) and x < 2^63: x >> 59 is floor(x / t) or one more
+            const uint64_t qh = x >> 59;
+            int64_t r = (int64_t)(x - qh * tq);
+            r += (r >> 63) & (int64_t)tq;
+            ob[v] = (uint64_t)r;
+        }
+    };
+    for (uint32_t g = 0; g < total; g += 2) {
+        step(rb[0], ub[0], g);
+        if (g + 1 < total) step(rb[1], ub[1], g + 1);
     }
 }
 
@@ -1009,6 +1085,16 @@ static size_t ks_words(const ckks_ctx *c, int B, int l, KsWs *w, uint64_t *base)
 
 // ModUp of d ([B][l][n], NTT domain, ciphertext b at d + b * d_stride):
 // fills w.y, w.u and the NTT-domain extended digits w.ext.
+// Exact base conversion of `sets` input sets onto up to maxt target positions.
+template <int MODE>
+static void launch_convert(ckks_ctx *c, const BasisDev *bases, const SetLayout &lay, const uint64_t *y,
+                           const uint32_t *u, const ConvTargets &ct, uint64_t *out, uint32_t maxt, uint32_t sets,
+                           hipStream_t s) {
+    const uint32_t n = c->n;
+    hipLaunchKernelGGL(k_convert_mfma<MODE>, dim3(n / MF_COEF, ((maxt + 15) / 16 + MF_TPB - 1) / MF_TPB, sets),
+                       dim3(256), 0, s, bases, lay, y, u, ct, out, n);
+}
+
 static int ks_modup(ckks_ctx *c, LevelTables *lt, int B, int l, const uint64_t *d, size_t d_stride, const KsWs &w,
                     hipStream_t s) {
     const uint32_t n = c->n, K = c->K, L = c->L, el = l + K, beta = lt->beta;
@@ -1028,8 +1114,7 @@ static int ks_modup(ckks_ctx *c, LevelTables *lt, int B, int l, const uint64_t *
         ConvTargets ct{(uint32_t)l, L, K, (size_t)beta * el * n, (size_t)el * n};
         const uint32_t maxt = l + K;  // upper bound on targets per digit
         ProfScope ps_(c, "ks_modup_convert", s);
-        hipLaunchKernelGGL(k_convert<0>, dim3((n + 255) / 256, (maxt + CT - 1) / CT, B * beta), dim3(256), 0, s,
-                           lt->d_digits, lay_up, w.y, w.u, ct, w.ext, n, c->d_pc);
+        launch_convert<0>(c, lt->d_digits, lay_up, w.y, w.u, ct, w.ext, maxt, B * beta, s);
     }
     LAUNCH_CHECK();
     {
@@ -1139,8 +1224,7 @@ static int ks_moddown_conv(ckks_ctx *c, size_t nout, int l, const KsWs &w, hipSt
         const uint32_t np = (nsum + ct.spp - 1) / ct.spp;
         if (nparts) *nparts = np;
         ProfScope ps_(c, "ks_moddown_convert", s);
-        hipLaunchKernelGGL(k_convert<1>, dim3((n + 255) / 256, (l + CT - 1) / CT, np * ct.sum_stride), dim3(256), 0,
-                           s, c->d_pbasis, lay_dn, w.acc, w.uP, ct, w.conv, n, c->d_pc);
+        launch_convert<1>(c, c->d_pbasis, lay_dn, w.acc, w.uP, ct, w.conv, (uint32_t)l, np * ct.sum_stride, s);
     }
     LAUNCH_CHECK();
     if (n != 2048) {
@@ -1178,8 +1262,7 @@ int op_mod_raise(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l0, 
     {
         ConvTargets ct{(uint32_t)lt, c->L, c->K, (size_t)lt * n, 0};
         ProfScope ps_(c, "raise_convert", s);
-        hipLaunchKernelGGL(k_convert<1>, dim3((n + 255) / 256, (lt + CT - 1) / CT, P), dim3(256), 0, s,
-                           rt->d_basis, lay, y, u, ct, out, n, c->d_pc);
+        launch_convert<1>(c, rt->d_basis, lay, y, u, ct, out, (uint32_t)lt, P, s);
     }
     LAUNCH_CHECK();
     MapStrided m2{out, out, n, (uint32_t)lt, 0, nullptr};

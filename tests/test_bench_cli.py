@@ -20,8 +20,8 @@ def test_bench_kernel_work_accounting():
     sys.path.insert(0, ROOT)
     import bench
     work = bench.kernel_work()
-    # every accounted kernel has a positive byte or multiply-add count
+    # every accounted kernel has a positive byte, multiply-add or product count
     for name, w in work.items():
-        assert w.get("bytes", 0) > 0 or w.get("mads", 0) > 0, name
+        assert w.get("bytes", 0) > 0 or w.get("mads", 0) > 0 or w.get("products", 0) > 0, name
     # the measured-traffic table names only accounted kernels
     assert set(bench.MEASURED_TRAFFIC["bytes_per_launch"]) <= set(work)
