@@ -363,8 +363,10 @@ __device__ __forceinline__ void bt4(uint32_t x0, uint32_t x1, uint32_t x2, uint3
 
 constexpr uint32_t MF_HSTRIDE = 272;  // LDS bytes per target position (8 digits x 32 rows + bank padding)
 
-template <int MODE>
-__global__ __launch_bounds__(256, 2) void k_convert_mfma(const BasisDev *__restrict__ bases, SetLayout lay,
+// OCC: waves per SIMD the register budget is sized for (3 when the whole
+// contraction is one 32-row chunk, 2 otherwise).
+template <int MODE, int OCC>
+__global__ __launch_bounds__(256, OCC) void k_convert_mfma(const BasisDev *__restrict__ bases, SetLayout lay,
                                                           const uint64_t *__restrict__ y,
                                                           const uint32_t *__restrict__ u, ConvTargets ct,
                                                           uint64_t *__restrict__ out, uint32_t n) {
@@ -386,16 +388,6 @@ __global__ __launch_bounds__(256, 2) void k_convert_mfma(const BasisDev *__restr
     const uint32_t nsets = ct.nsum > 1 ? min(ct.spp, ct.nsum - part * ct.spp) : 1;
     const uint32_t cps = mk / 32, nch = nsets * cps;  // 32-row chunks per set, in all
     const bool staged = cps == 1;
-    if (staged) {
-        // position p's 8 x 32 digit bytes are contiguous in HD (mk = 32): 16-byte copies
-        const uint32_t np = ntile * 16;
-        const int8_t *src = B.HD + (size_t)16 * tile0 * 256;
-        for (uint32_t q = threadIdx.x; q < np * 16; q += 256)
-            *(uint4 *)(sh_h + (q / 16) * MF_HSTRIDE + (q % 16) * 16) = *(const uint4 *)(src + (size_t)q * 16);
-        const uint64_t *rsrc = B.RC + (size_t)16 * tile0 * MF_RC;
-        for (uint32_t q = threadIdx.x; q < np * MF_RC; q += 256) sh_rc[q] = rsrc[q];
-        __syncthreads();
-    }
     const uint64_t *yb = y + (sfirst / lay.inner) * lay.so + (sfirst % lay.inner) * lay.si + lay.off + kb + col;
     const size_t set_step = (size_t)ct.sum_stride * lay.so;
     // rows 8 grp + j of chunk ch, loaded unconditionally (index clamped; the u row
@@ -407,6 +399,21 @@ __global__ __launch_bounds__(256, 2) void k_convert_mfma(const BasisDev *__restr
         for (int j = 0; j < 8; j++) raw[j] = ys[(size_t)min(r0 + j, m - 1) * n];
         uraw = u[(sfirst + (size_t)js * ct.sum_stride) * n + kb + col];
     };
+    // the first rows are in flight while the tables are staged
+    uint64_t rb[2][8];
+    uint32_t ub[2];
+    load_rows(rb[0], ub[0], 0);
+    if (nch > 1) load_rows(rb[1], ub[1], 1 % nch);
+    if (staged) {
+        // position p's 8 x 32 digit bytes are contiguous in HD (mk = 32): 16-byte copies
+        const uint32_t np = ntile * 16;
+        const int8_t *src = B.HD + (size_t)16 * tile0 * 256;
+        for (uint32_t q = threadIdx.x; q < np * 16; q += 256)
+            *(uint4 *)(sh_h + (q / 16) * MF_HSTRIDE + (q % 16) * 16) = *(const uint4 *)(src + (size_t)q * 16);
+        const uint64_t *rsrc = B.RC + (size_t)16 * tile0 * MF_RC;
+        for (uint32_t q = threadIdx.x; q < np * MF_RC; q += 256) sh_rc[q] = rsrc[q];
+        __syncthreads();
+    }
     long A[8];  // digit plane a of the lane's 8 rows (byte j = row 8 grp + j)
     auto build_a = [&](const uint64_t(&raw)[8], uint32_t uraw, uint32_t ch) {
         const uint32_t r0 = (ch % cps) * 32 + 8 * grp;
@@ -446,11 +453,7 @@ __global__ __launch_bounds__(256, 2) void k_convert_mfma(const BasisDev *__restr
     mf_v4i acc[15];
     // the flat sequence g = (tile - tile0) nch + ch; rows are fetched two chunks ahead
     const uint32_t total = ntile * nch;
-    uint64_t rb[2][8];
-    uint32_t ub[2];
-    load_rows(rb[0], ub[0], 0);
     if (nch == 1) build_a(rb[0], ub[0], 0);
-    else load_rows(rb[1], ub[1], 1 % nch);
     auto step = [&](uint64_t(&raw)[8], uint32_t &uraw, uint32_t g) {
         const uint32_t tile = tile0 + g / nch, ch = g % nch;
         if (ch == 0) {
@@ -1085,14 +1088,18 @@ static size_t ks_words(const ckks_ctx *c, int B, int l, KsWs *w, uint64_t *base)
 
 // ModUp of d ([B][l][n], NTT domain, ciphertext b at d + b * d_stride):
 // fills w.y, w.u and the NTT-domain extended digits w.ext.
-// Exact base conversion of `sets` input sets onto up to maxt target positions.
+// Exact base conversion of `sets` input sets (bases of at most mmax primes)
+// onto up to maxt target positions.
 template <int MODE>
 static void launch_convert(ckks_ctx *c, const BasisDev *bases, const SetLayout &lay, const uint64_t *y,
                            const uint32_t *u, const ConvTargets &ct, uint64_t *out, uint32_t maxt, uint32_t sets,
-                           hipStream_t s) {
+                           uint32_t mmax, hipStream_t s) {
     const uint32_t n = c->n;
-    hipLaunchKernelGGL(k_convert_mfma<MODE>, dim3(n / MF_COEF, ((maxt + 15) / 16 + MF_TPB - 1) / MF_TPB, sets),
-                       dim3(256), 0, s, bases, lay, y, u, ct, out, n);
+    const dim3 grid(n / MF_COEF, ((maxt + 15) / 16 + MF_TPB - 1) / MF_TPB, sets);
+    if (ct.nsum <= 1 && mmax + 1 <= 32)
+        hipLaunchKernelGGL((k_convert_mfma<MODE, 3>), grid, dim3(256), 0, s, bases, lay, y, u, ct, out, n);
+    else
+        hipLaunchKernelGGL((k_convert_mfma<MODE, 2>), grid, dim3(256), 0, s, bases, lay, y, u, ct, out, n);
 }
 
 static int ks_modup(ckks_ctx *c, LevelTables *lt, int B, int l, const uint64_t *d, size_t d_stride, const KsWs &w,
@@ -1114,7 +1121,7 @@ static int ks_modup(ckks_ctx *c, LevelTables *lt, int B, int l, const uint64_t *
         ConvTargets ct{(uint32_t)l, L, K, (size_t)beta * el * n, (size_t)el * n};
         const uint32_t maxt = l + K;  // upper bound on targets per digit
         ProfScope ps_(c, "ks_modup_convert", s);
-        launch_convert<0>(c, lt->d_digits, lay_up, w.y, w.u, ct, w.ext, maxt, B * beta, s);
+        launch_convert<0>(c, lt->d_digits, lay_up, w.y, w.u, ct, w.ext, maxt, B * beta, c->alpha, s);
     }
     LAUNCH_CHECK();
     {
@@ -1224,7 +1231,7 @@ static int ks_moddown_conv(ckks_ctx *c, size_t nout, int l, const KsWs &w, hipSt
         const uint32_t np = (nsum + ct.spp - 1) / ct.spp;
         if (nparts) *nparts = np;
         ProfScope ps_(c, "ks_moddown_convert", s);
-        launch_convert<1>(c, c->d_pbasis, lay_dn, w.acc, w.uP, ct, w.conv, (uint32_t)l, np * ct.sum_stride, s);
+        launch_convert<1>(c, c->d_pbasis, lay_dn, w.acc, w.uP, ct, w.conv, (uint32_t)l, np * ct.sum_stride, c->K, s);
     }
     LAUNCH_CHECK();
     if (n != 2048) {
@@ -1262,7 +1269,7 @@ int op_mod_raise(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l0, 
     {
         ConvTargets ct{(uint32_t)lt, c->L, c->K, (size_t)lt * n, 0};
         ProfScope ps_(c, "raise_convert", s);
-        launch_convert<1>(c, rt->d_basis, lay, y, u, ct, out, (uint32_t)lt, P, s);
+        launch_convert<1>(c, rt->d_basis, lay, y, u, ct, out, (uint32_t)lt, P, (uint32_t)l0, s);
     }
     LAUNCH_CHECK();
     MapStrided m2{out, out, n, (uint32_t)lt, 0, nullptr};
