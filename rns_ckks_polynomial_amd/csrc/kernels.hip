@@ -364,16 +364,17 @@ __device__ __forceinline__ void bt4(uint32_t x0, uint32_t x1, uint32_t x2, uint3
 constexpr uint32_t MF_HSTRIDE = 272;  // LDS bytes per target position (8 digits x 32 rows + bank padding)
 
 // OCC: waves per SIMD the register budget is sized for (3 when the whole
-// contraction is one 32-row chunk, 2 otherwise).
-template <int MODE, int OCC>
+// contraction is one 32-row chunk, 2 otherwise).  STAGED: the basis rows fit
+// one 32-row block (mk = 32), so the workgroup's digit table rows and
+// reduction constants are staged in LDS once; otherwise the fragments come
+// from the global table one chunk ahead of their use.
+template <int MODE, int OCC, bool STAGED>
 __global__ __launch_bounds__(256, OCC) void k_convert_mfma(const BasisDev *__restrict__ bases, SetLayout lay,
                                                           const uint64_t *__restrict__ y,
                                                           const uint32_t *__restrict__ u, ConvTargets ct,
                                                           uint64_t *__restrict__ out, uint32_t n) {
-    // a basis whose rows fit one 32-row block (cps == 1): the workgroup's digit
-    // table rows and reduction constants are staged here once
-    __shared__ __align__(16) int8_t sh_h[MF_TPB * 16 * MF_HSTRIDE];
-    __shared__ uint64_t sh_rc[MF_TPB * 16 * MF_RC];
+    __shared__ __align__(16) int8_t sh_h[STAGED ? MF_TPB * 16 * MF_HSTRIDE : 16];
+    __shared__ uint64_t sh_rc[STAGED ? MF_TPB * 16 * MF_RC : 1];
     const uint32_t s = blockIdx.z;
     const BasisDev &B = bases[lay.per_set_basis ? s % lay.inner : 0];
     const uint32_t m = B.m, lo = B.first, mk = B.mk;
@@ -386,8 +387,8 @@ __global__ __launch_bounds__(256, OCC) void k_convert_mfma(const BasisDev *__res
     const uint32_t part = ct.nsum > 1 ? s / ct.sum_stride : 0;
     const size_t sfirst = ct.nsum > 1 ? s + (size_t)part * (ct.spp - 1) * ct.sum_stride : s;
     const uint32_t nsets = ct.nsum > 1 ? min(ct.spp, ct.nsum - part * ct.spp) : 1;
-    const uint32_t cps = mk / 32, nch = nsets * cps;  // 32-row chunks per set, in all
-    const bool staged = cps == 1;
+    // OCC 3 is launched only for one-chunk contractions (one set, mk = 32)
+    const uint32_t cps = mk / 32, nch = OCC == 3 ? 1 : nsets * cps;  // 32-row chunks per set, in all
     const uint64_t *yb = y + (sfirst / lay.inner) * lay.so + (sfirst % lay.inner) * lay.si + lay.off + kb + col;
     const size_t set_step = (size_t)ct.sum_stride * lay.so;
     // rows 8 grp + j of chunk ch, loaded unconditionally (index clamped; the u row
@@ -403,8 +404,8 @@ __global__ __launch_bounds__(256, OCC) void k_convert_mfma(const BasisDev *__res
     uint64_t rb[2][8];
     uint32_t ub[2];
     load_rows(rb[0], ub[0], 0);
-    if (nch > 1) load_rows(rb[1], ub[1], 1 % nch);
-    if (staged) {
+    if (OCC != 3 && nch > 1) load_rows(rb[1], ub[1], 1 % nch);
+    if constexpr (STAGED) {
         // position p's 8 x 32 digit bytes are contiguous in HD (mk = 32): 16-byte copies
         const uint32_t np = ntile * 16;
         const int8_t *src = B.HD + (size_t)16 * tile0 * 256;
@@ -433,16 +434,18 @@ __global__ __launch_bounds__(256, OCC) void k_convert_mfma(const BasisDev *__res
 #pragma unroll
         for (int a = 0; a < 8; a++) A[a] = (long)(((uint64_t)o[1][a] << 32) | o[0][a]);
     };
-    long Hb[8];
-    auto load_h = [&](uint32_t tile, uint32_t ch) {
-        if (staged) {
+    // H fragments: from LDS when staged (loaded at the tile's first chunk), else
+    // from the global table, one chunk ahead of their use (two register sets)
+    long hb[2][8];
+    auto load_h = [&](long(&H)[8], uint32_t tile, uint32_t ch) {
+        if constexpr (STAGED) {
             const int8_t *h = sh_h + ((tile - tile0) * 16 + col) * MF_HSTRIDE + 8 * grp;
 #pragma unroll
-            for (int b = 0; b < 8; b++) Hb[b] = *(const long *)(h + 32 * b);
+            for (int b = 0; b < 8; b++) H[b] = *(const long *)(h + 32 * b);
         } else {
             const int8_t *h = B.HD + (size_t)(16 * tile + col) * 8 * mk + (ch % cps) * 32 + 8 * grp;
 #pragma unroll
-            for (int b = 0; b < 8; b++) Hb[b] = *(const long *)(h + (size_t)b * mk);
+            for (int b = 0; b < 8; b++) H[b] = *(const long *)(h + (size_t)b * mk);
         }
     };
     // powers of two of the recombination, kept in registers so that each term
@@ -454,17 +457,25 @@ __global__ __launch_bounds__(256, OCC) void k_convert_mfma(const BasisDev *__res
     // the flat sequence g = (tile - tile0) nch + ch; rows are fetched two chunks ahead
     const uint32_t total = ntile * nch;
     if (nch == 1) build_a(rb[0], ub[0], 0);
-    auto step = [&](uint64_t(&raw)[8], uint32_t &uraw, uint32_t g) {
+    if constexpr (!STAGED) load_h(hb[0], tile0, 0);
+    auto step = [&](uint64_t(&raw)[8], uint32_t &uraw, long(&Hg)[8], long(&Hn)[8], uint32_t g) {
+        // staged: one fragment set per tile (loaded at its first chunk); else the
+        // set loaded one chunk earlier
+        long(&Hb)[8] = STAGED ? hb[0] : Hg;
         const uint32_t tile = tile0 + g / nch, ch = g % nch;
         if (ch == 0) {
 #pragma unroll
             for (int d = 0; d < 15; d++) acc[d] = mf_v4i{0, 0, 0, 0};
         }
-        if (nch > 1) {
+        if (OCC != 3 && nch > 1) {
             build_a(raw, uraw, ch);
             if (g + 2 < total) load_rows(raw, uraw, (g + 2) % nch);
         }
-        if (ch == 0 || cps > 1) load_h(tile, ch);
+        if constexpr (STAGED) {
+            if (ch == 0) load_h(Hb, tile, ch);
+        } else if (g + 1 < total) {
+            load_h(Hn, tile0 + (g + 1) / nch, (g + 1) % nch);  // the next chunk's fragments
+        }
 #pragma unroll
         for (int b = 0; b < 8; b++)
 #pragma unroll
@@ -473,7 +484,7 @@ __global__ __launch_bounds__(256, OCC) void k_convert_mfma(const BasisDev *__res
         if (ch + 1 < nch) return;
         const uint32_t p = 16 * tile + col;
         if (p >= ntarget) return;  // padding columns: every MFMA above ran on the whole wave
-        const uint64_t *rc = staged ? sh_rc + ((tile - tile0) * 16 + col) * MF_RC : B.RC + (size_t)p * MF_RC;
+        const uint64_t *rc = STAGED ? sh_rc + ((tile - tile0) * 16 + col) * MF_RC : B.RC + (size_t)p * MF_RC;
         int32_t clo[7], chi[7];
 #pragma unroll
         for (int d = 0; d < 7; d++) {
@@ -517,8 +528,8 @@ __global__ __launch_bounds__(256, OCC) void k_convert_mfma(const BasisDev *__res
         }
     };
     for (uint32_t g = 0; g < total; g += 2) {
-        step(rb[0], ub[0], g);
-        if (g + 1 < total) step(rb[1], ub[1], g + 1);
+        step(rb[0], ub[0], hb[0], hb[1], g);
+        if (g + 1 < total) step(rb[1], ub[1], hb[1], hb[0], g + 1);
     }
 }
 
@@ -1096,10 +1107,13 @@ static void launch_convert(ckks_ctx *c, const BasisDev *bases, const SetLayout &
                            uint32_t mmax, hipStream_t s) {
     const uint32_t n = c->n;
     const dim3 grid(n / MF_COEF, ((maxt + 15) / 16 + MF_TPB - 1) / MF_TPB, sets);
-    if (ct.nsum <= 1 && mmax + 1 <= 32)
-        hipLaunchKernelGGL((k_convert_mfma<MODE, 3>), grid, dim3(256), 0, s, bases, lay, y, u, ct, out, n);
+    // every basis of the launch has at most mmax rows: mk = 32 for all or none
+    if (mmax + 1 > 32)
+        hipLaunchKernelGGL((k_convert_mfma<MODE, 2, false>), grid, dim3(256), 0, s, bases, lay, y, u, ct, out, n);
+    else if (ct.nsum > 1)
+        hipLaunchKernelGGL((k_convert_mfma<MODE, 2, true>), grid, dim3(256), 0, s, bases, lay, y, u, ct, out, n);
     else
-        hipLaunchKernelGGL((k_convert_mfma<MODE, 2>), grid, dim3(256), 0, s, bases, lay, y, u, ct, out, n);
+        hipLaunchKernelGGL((k_convert_mfma<MODE, 3, true>), grid, dim3(256), 0, s, bases, lay, y, u, ct, out, n);
 }
 
 static int ks_modup(ckks_ctx *c, LevelTables *lt, int B, int l, const uint64_t *d, size_t d_stride, const KsWs &w,
