@@ -434,9 +434,12 @@ __global__ __launch_bounds__(256, OCC) void k_convert_mfma(const BasisDev *__res
 #pragma unroll
         for (int a = 0; a < 8; a++) A[a] = (long)(((uint64_t)o[1][a] << 32) | o[0][a]);
     };
-    // H fragments: from LDS when staged (loaded at the tile's first chunk), else
-    // from the global table, one chunk ahead of their use (two register sets)
-    long hb[2][8];
+    // TT target tiles share each chunk's A fragments (2 when the contraction has
+    // several chunks, so the rows are fetched and transposed once per 2 tiles)
+    constexpr uint32_t TT = OCC == 3 ? 1 : 2;
+    // H fragments of a tile: from LDS when staged (loaded at its first chunk and
+    // kept), else from the global table at every chunk
+    long hb[TT][8];
     auto load_h = [&](long(&H)[8], uint32_t tile, uint32_t ch) {
         if constexpr (STAGED) {
             const int8_t *h = sh_h + ((tile - tile0) * 16 + col) * MF_HSTRIDE + 8 * grp;
@@ -453,37 +456,9 @@ __global__ __launch_bounds__(256, OCC) void k_convert_mfma(const BasisDev *__res
     int32_t w2[7] = {1 << 8, 1 << 16, 1 << 24, 1 << 2, 1 << 10, 1 << 18, 1 << 26};
 #pragma unroll
     for (int d = 0; d < 7; d++) asm volatile("" : "+v"(w2[d]));
-    mf_v4i acc[15];
-    // the flat sequence g = (tile - tile0) nch + ch; rows are fetched two chunks ahead
-    const uint32_t total = ntile * nch;
-    if (nch == 1) build_a(rb[0], ub[0], 0);
-    if constexpr (!STAGED) load_h(hb[0], tile0, 0);
-    auto step = [&](uint64_t(&raw)[8], uint32_t &uraw, long(&Hg)[8], long(&Hn)[8], uint32_t g) {
-        // staged: one fragment set per tile (loaded at its first chunk); else the
-        // set loaded one chunk earlier
-        long(&Hb)[8] = STAGED ? hb[0] : Hg;
-        const uint32_t tile = tile0 + g / nch, ch = g % nch;
-        if (ch == 0) {
-#pragma unroll
-            for (int d = 0; d < 15; d++) acc[d] = mf_v4i{0, 0, 0, 0};
-        }
-        if (OCC != 3 && nch > 1) {
-            build_a(raw, uraw, ch);
-            if (g + 2 < total) load_rows(raw, uraw, (g + 2) % nch);
-        }
-        if constexpr (STAGED) {
-            if (ch == 0) load_h(Hb, tile, ch);
-        } else if (g + 1 < total) {
-            load_h(Hn, tile0 + (g + 1) / nch, (g + 1) % nch);  // the next chunk's fragments
-        }
-#pragma unroll
-        for (int b = 0; b < 8; b++)
-#pragma unroll
-            for (int a = 0; a < 8; a++)
-                acc[a + b] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A[a], Hb[b], acc[a + b], 0, 0, 0);
-        if (ch + 1 < nch) return;
+    auto recombine = [&](uint32_t tile, const mf_v4i(&acc)[15]) {
         const uint32_t p = 16 * tile + col;
-        if (p >= ntarget) return;  // padding columns: every MFMA above ran on the whole wave
+        if (p >= ntarget) return;  // padding columns: every MFMA ran on the whole wave
         const uint64_t *rc = STAGED ? sh_rc + ((tile - tile0) * 16 + col) * MF_RC : B.RC + (size_t)p * MF_RC;
         int32_t clo[7], chi[7];
 #pragma unroll
@@ -527,9 +502,41 @@ __global__ __launch_bounds__(256, OCC) void k_convert_mfma(const BasisDev *__res
             ob[v] = (uint64_t)r;
         }
     };
+    mf_v4i acc[TT][15];
+    // the flat sequence g = pass nch + ch over passes of TT tiles; rows are
+    // fetched two chunks ahead
+    const uint32_t total = (ntile + TT - 1) / TT * nch;
+    if (nch == 1) build_a(rb[0], ub[0], 0);
+    auto step = [&](uint64_t(&raw)[8], uint32_t &uraw, uint32_t g) {
+        const uint32_t t0 = tile0 + (g / nch) * TT, ch = g % nch;
+        if (ch == 0) {
+#pragma unroll
+            for (uint32_t tt = 0; tt < TT; tt++)
+#pragma unroll
+                for (int d = 0; d < 15; d++) acc[tt][d] = mf_v4i{0, 0, 0, 0};
+        }
+        if (OCC != 3 && nch > 1) {
+            build_a(raw, uraw, ch);
+            if (g + 2 < total) load_rows(raw, uraw, (g + 2) % nch);
+        }
+#pragma unroll
+        for (uint32_t tt = 0; tt < TT; tt++) {
+            if (t0 + tt >= tile_end) break;  // workgroup-uniform
+            if (!STAGED || ch == 0) load_h(hb[tt], t0 + tt, ch);
+#pragma unroll
+            for (int b = 0; b < 8; b++)
+#pragma unroll
+                for (int a = 0; a < 8; a++)
+                    acc[tt][a + b] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A[a], hb[tt][b], acc[tt][a + b], 0, 0, 0);
+        }
+        if (ch + 1 < nch) return;
+#pragma unroll
+        for (uint32_t tt = 0; tt < TT; tt++)
+            if (t0 + tt < tile_end) recombine(t0 + tt, acc[tt]);
+    };
     for (uint32_t g = 0; g < total; g += 2) {
-        step(rb[0], ub[0], hb[0], hb[1], g);
-        if (g + 1 < total) step(rb[1], ub[1], hb[1], hb[0], g + 1);
+        step(rb[0], ub[0], g);
+        if (g + 1 < total) step(rb[1], ub[1], g + 1);
     }
 }
 
