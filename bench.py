@@ -45,19 +45,19 @@ LIMB = N * 8
 # counters (profiles/bench_step_n2048_l112_b8_hbm_counters.md).  Valid only for
 # the kernel sources they were taken on (hash of rns_ckks_polynomial_amd/csrc).
 MEASURED_TRAFFIC = {
-    "source_sha": "7e1260de268da26f",
+    "source_sha": "220fc1b15e4d663b",
     "bytes_per_launch": {
-        "ks_modup_convert": 812961485,
-        "ks_moddown_convert": 955988335,
-        "bsgs_mac": 3758220758,
-        "ks_ntt_ext": 1322140873,
-        "ks_inner_product_sum": 2848982654,
-        "rotate_final": 3192510826,
-        "ntt_fwd": 62576940,
-        "ntt_inv": 62589739,
-        "giant_final": 297525815,
-        "ks_intt_modup": 326832805,
-        "ks_intt_moddown": 310299374
+        "ks_modup_convert": 812965505,
+        "ks_moddown_convert": 750401312,
+        "bsgs_mac": 3758215926,
+        "ks_ntt_ext": 1322189159,
+        "ks_inner_product_sum": 2848576562,
+        "rotate_final": 3192416977,
+        "ntt_fwd": 62576885,
+        "ntt_inv": 62585588,
+        "giant_final": 297540342,
+        "ks_intt_modup": 326829030,
+        "ks_intt_moddown": 310306868
     },
 }
 
