@@ -643,6 +643,67 @@ __global__ __launch_bounds__(256) void k_inner2048(const uint64_t *__restrict__ 
     }
 }
 
+// Hoisted baby steps (n = 2048): every step of the batch switches the same B
+// inputs, so a workgroup (extended limb e, group of HOIST_SPW steps; member =
+// input ciphertext) stages limb e of the input's beta digits in LDS once and
+// runs its steps on them: each step gathers sigma_g of the digits from LDS and
+// takes the inner product with that step's key rows.  The B members of a group
+// share an XCD, so each key row is fetched once per XCD.  Same sums and output
+// layout as k_inner2048 with shared = 1.
+constexpr uint32_t HOIST_SPW = 8;
+constexpr uint32_t HOIST_MAX_BETA = 4;  // beta digit limbs of 16 KiB in at most 64 KiB of LDS
+__global__ __launch_bounds__(256) void k_inner_hoisted2048(const uint64_t *__restrict__ d, size_t d_stride,
+                                                            const uint64_t *__restrict__ ext, const Steps st,
+                                                            uint64_t *__restrict__ acc,
+                                                            const PrimeConsts *__restrict__ pc, uint32_t l, uint32_t L,
+                                                            uint32_t K, uint32_t beta, uint32_t alpha) {
+    constexpr uint32_t n = 2048;
+    __shared__ uint64_t dig[HOIST_MAX_BETA * n];
+    const uint32_t el = l + K;
+    uint32_t grp, b;
+    xcd_group(blockIdx.x, st.B, grp, b);
+    const uint32_t ngroups = (st.count + HOIST_SPW - 1) / HOIST_SPW;
+    if (grp >= el * ngroups) return;
+    const uint32_t e = grp % el, s0 = (grp / el) * HOIST_SPW, s1 = min(st.count, s0 + HOIST_SPW);
+    const uint32_t gi = e < l ? e : L + (e - l);
+    const uint32_t t = threadIdx.x;
+    for (uint32_t j = 0; j < beta; j++) {
+        const bool own = e >= j * alpha && e < min(l, (j + 1) * alpha);
+        const uint64_t *src = own ? d + b * d_stride + (size_t)e * n : ext + ((b * beta + j) * el + e) * n;
+#pragma unroll
+        for (int m = 0; m < 8; m++) dig[j * n + t + 256 * m] = src[t + 256 * m];
+    }
+    __syncthreads();
+    const PrimeConsts P = pc[gi];
+    for (uint32_t step = s0; step < s1; step++) {
+        const uint64_t *key = st.key[step];
+        const uint32_t g = st.g[step];
+        Split3 a0[8], a1[8];
+#pragma unroll
+        for (int m = 0; m < 8; m++) a0[m] = a1[m] = {0, 0, 0, 0};
+        for (uint32_t j = 0; j < beta; j++) {
+            const uint64_t *kb = key + ((size_t)j * 2 * (L + K) + gi) * n;
+            const uint64_t *ka = kb + (size_t)(L + K) * n;
+#pragma unroll
+            for (int m = 0; m < 8; m++) {
+                const uint32_t k = t + 256 * m;
+                const uint64_t v = dig[j * n + galois_src(k, g, n)];
+                const uint32_t vl = (uint32_t)(v & M30), vh = (uint32_t)(v >> 30);
+                smac(a0[m], vl, vh, split30(kb[k]));
+                smac(a1[m], vl, vh, split30(ka[k]));
+            }
+        }
+        // beta <= HOIST_MAX_BETA products per sum: within the snorm-free bound
+        const size_t cb = (size_t)step * st.B + b;
+        uint64_t *o0 = acc + ((cb * 2 + 0) * el + e) * n, *o1 = acc + ((cb * 2 + 1) * el + e) * n;
+#pragma unroll
+        for (int m = 0; m < 8; m++) {
+            o0[t + 256 * m] = sreduce60(a0[m], P);
+            o1[t + 256 * m] = sreduce60(a1[m], P);
+        }
+    }
+}
+
 // Giant-step inner product summed over the steps of a batch (n = 2048, limbs
 // e < l).  Block (part p, ciphertext b, limb e) covers the steps
 // [p * spp, min(count, (p + 1) * spp)) and writes
@@ -1176,7 +1237,11 @@ static int ks_inner(ckks_ctx *c, LevelTables *lt, int l, const uint64_t *d, size
     const uint32_t n = c->n, K = c->K, L = c->L, el = l + K, beta = lt->beta;
     const size_t nout = (size_t)st.count * st.B;
     ProfScope ps_(c, st.shared ? "ks_inner_product_hoisted" : "ks_inner_product", s);
-    if (n == 2048) {
+    if (n == 2048 && st.shared && !st.seeded && beta <= HOIST_MAX_BETA) {
+        const uint32_t ngroups = (st.count + HOIST_SPW - 1) / HOIST_SPW;
+        hipLaunchKernelGGL(k_inner_hoisted2048, dim3(xcd_blocks(el * ngroups, st.B)), dim3(256), 0, s, d, d_stride,
+                           w.ext, st, w.acc, c->d_pc, (uint32_t)l, L, K, beta, c->alpha);
+    } else if (n == 2048) {
         auto kern = st.seeded ? k_inner2048<true> : k_inner2048<false>;
         hipLaunchKernelGGL(kern, dim3(xcd_blocks(st.count * el, st.B)), dim3(256), 0, s, d, d_stride, w.ext, st,
                            w.acc, c->d_pc, (uint32_t)l, L, K, beta, c->alpha, 0u, el);
