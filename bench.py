@@ -45,19 +45,19 @@ LIMB = N * 8
 # counters (profiles/bench_step_n2048_l112_b8_hbm_counters.md).  Valid only for
 # the kernel sources they were taken on (hash of rns_ckks_polynomial_amd/csrc).
 MEASURED_TRAFFIC = {
-    "source_sha": "220fc1b15e4d663b",
+    "source_sha": "1c12b3800a91db89",
     "bytes_per_launch": {
-        "ks_modup_convert": 812965505,
-        "ks_moddown_convert": 750401312,
-        "bsgs_mac": 3758215926,
-        "ks_ntt_ext": 1322189159,
-        "ks_inner_product_sum": 2848576562,
-        "rotate_final": 3192416977,
-        "ntt_fwd": 62576885,
-        "ntt_inv": 62585588,
-        "giant_final": 297540342,
-        "ks_intt_modup": 326829030,
-        "ks_intt_moddown": 310306868
+        "ks_modup_convert": 812912070,
+        "ks_moddown_convert": 750430192,
+        "bsgs_mac": 3758217878,
+        "ks_ntt_ext": 1321912517,
+        "ks_inner_product_sum": 2848363672,
+        "rotate_final": 3192378036,
+        "ntt_fwd": 62576853,
+        "ntt_inv": 62598867,
+        "giant_final": 297539062,
+        "ks_intt_modup": 326837640,
+        "ks_intt_moddown": 310306602
     },
 }
 

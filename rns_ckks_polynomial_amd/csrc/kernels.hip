@@ -650,7 +650,7 @@ __global__ __launch_bounds__(256) void k_inner2048(const uint64_t *__restrict__ 
 // takes the inner product with that step's key rows.  The B members of a group
 // share an XCD, so each key row is fetched once per XCD.  Same sums and output
 // layout as k_inner2048 with shared = 1.
-constexpr uint32_t HOIST_SPW = 8;
+constexpr uint32_t HOIST_SPW = 16;
 constexpr uint32_t HOIST_MAX_BETA = 4;  // beta digit limbs of 16 KiB in at most 64 KiB of LDS
 __global__ __launch_bounds__(256) void k_inner_hoisted2048(const uint64_t *__restrict__ d, size_t d_stride,
                                                             const uint64_t *__restrict__ ext, const Steps st,
