@@ -373,7 +373,7 @@ __global__ __launch_bounds__(256, OCC) void k_convert_mfma(const BasisDev *__res
                                                           const uint64_t *__restrict__ y,
                                                           const uint32_t *__restrict__ u, ConvTargets ct,
                                                           uint64_t *__restrict__ out, uint32_t n) {
-    __shared__ __align__(16) int8_t sh_h[STAGED ? MF_TPB * 16 * MF_HSTRIDE : 16];
+    __shared__ __align__(16) int8_t sh_h[STAGED ? MF_TPB * 16 * MF_HSTRIDE : 2 * 2 * 16 * MF_HSTRIDE];
     __shared__ uint64_t sh_rc[STAGED ? MF_TPB * 16 * MF_RC : 1];
     const uint32_t s = blockIdx.z;
     const BasisDev &B = bases[lay.per_set_basis ? s % lay.inner : 0];
@@ -437,18 +437,37 @@ __global__ __launch_bounds__(256, OCC) void k_convert_mfma(const BasisDev *__res
     // TT target tiles share each chunk's A fragments (2 when the contraction has
     // several chunks, so the rows are fetched and transposed once per 2 tiles)
     constexpr uint32_t TT = OCC == 3 ? 1 : 2;
-    // H fragments of a tile: from LDS when staged (loaded at its first chunk and
-    // kept), else from the global table at every chunk
+    // H fragments of a tile: from LDS.  Staged: the workgroup's whole table,
+    // loaded once (a tile's fragments are read at its first chunk and kept).
+    // Otherwise the digit-table slice of each (pass, chunk), 2 tiles x 16
+    // positions x 8 digits x 32 rows, goes through a double-buffered LDS slice
+    // that the workgroup fills one step ahead (all its waves run the same steps).
     long hb[TT][8];
-    auto load_h = [&](long(&H)[8], uint32_t tile, uint32_t ch) {
-        if constexpr (STAGED) {
-            const int8_t *h = sh_h + ((tile - tile0) * 16 + col) * MF_HSTRIDE + 8 * grp;
+    auto load_h = [&](long(&H)[8], uint32_t tile, uint32_t buf) {
+        const int8_t *h = STAGED ? sh_h + ((tile - tile0) * 16 + col) * MF_HSTRIDE + 8 * grp
+                                 : sh_h + ((buf * 2 + (tile - tile0) % 2) * 16 + col) * MF_HSTRIDE + 8 * grp;
 #pragma unroll
-            for (int b = 0; b < 8; b++) H[b] = *(const long *)(h + 32 * b);
-        } else {
-            const int8_t *h = B.HD + (size_t)(16 * tile + col) * 8 * mk + (ch % cps) * 32 + 8 * grp;
+        for (int b = 0; b < 8; b++) H[b] = *(const long *)(h + 32 * b);
+    };
+    // the slice of step g: thread x copies 16-byte pieces q = x and x + 256 of the
+    // 2 x 16 x 8 x 32 bytes (tiles past tile_end read padded, in-bounds positions)
+    uint4 hs[2];
+    auto fetch_slice = [&](uint32_t g) {
+        const uint32_t t0 = tile0 + (g / nch) * TT, c0 = (g % nch % cps) * 32;
 #pragma unroll
-            for (int b = 0; b < 8; b++) H[b] = *(const long *)(h + (size_t)b * mk);
+        for (int r = 0; r < 2; r++) {
+            const uint32_t q = threadIdx.x + 256 * r;  // (tile tt, position, digit b, half) = q / 256, ..
+            const uint32_t tt = q / 256, pos = (q / 16) % 16, b = (q / 2) % 8, hf = q % 2;
+            const uint32_t tile = min(t0 + tt, tile_end - 1);
+            hs[r] = *(const uint4 *)(B.HD + ((size_t)(16 * tile + pos) * 8 + b) * mk + c0 + 16 * hf);
+        }
+    };
+    auto store_slice = [&](uint32_t buf) {
+#pragma unroll
+        for (int r = 0; r < 2; r++) {
+            const uint32_t q = threadIdx.x + 256 * r;
+            const uint32_t tt = q / 256, pos = (q / 16) % 16, b = (q / 2) % 8, hf = q % 2;
+            *(uint4 *)(sh_h + ((buf * 2 + tt) * 16 + pos) * MF_HSTRIDE + 32 * b + 16 * hf) = hs[r];
         }
     };
     // powers of two of the recombination, kept in registers so that each term
@@ -507,6 +526,11 @@ __global__ __launch_bounds__(256, OCC) void k_convert_mfma(const BasisDev *__res
     // fetched two chunks ahead
     const uint32_t total = (ntile + TT - 1) / TT * nch;
     if (nch == 1) build_a(rb[0], ub[0], 0);
+    if constexpr (!STAGED) {
+        fetch_slice(0);
+        store_slice(0);
+        __syncthreads();
+    }
     auto step = [&](uint64_t(&raw)[8], uint32_t &uraw, uint32_t g) {
         const uint32_t t0 = tile0 + (g / nch) * TT, ch = g % nch;
         if (ch == 0) {
@@ -519,15 +543,23 @@ __global__ __launch_bounds__(256, OCC) void k_convert_mfma(const BasisDev *__res
             build_a(raw, uraw, ch);
             if (g + 2 < total) load_rows(raw, uraw, (g + 2) % nch);
         }
+        if constexpr (!STAGED)
+            if (g + 1 < total) fetch_slice(g + 1);
 #pragma unroll
         for (uint32_t tt = 0; tt < TT; tt++) {
             if (t0 + tt >= tile_end) break;  // workgroup-uniform
-            if (!STAGED || ch == 0) load_h(hb[tt], t0 + tt, ch);
+            if (!STAGED || ch == 0) load_h(hb[tt], t0 + tt, g & 1);
 #pragma unroll
             for (int b = 0; b < 8; b++)
 #pragma unroll
                 for (int a = 0; a < 8; a++)
                     acc[tt][a + b] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A[a], hb[tt][b], acc[tt][a + b], 0, 0, 0);
+        }
+        if constexpr (!STAGED) {
+            // the next slice goes to the other buffer, whose last readers (step g - 1)
+            // passed the barrier at its end; this barrier publishes it for step g + 1
+            if (g + 1 < total) store_slice((g + 1) & 1);
+            __syncthreads();
         }
         if (ch + 1 < nch) return;
 #pragma unroll
