@@ -174,48 +174,6 @@ __device__ __forceinline__ uint64_t sreduce60(S s, const PrimeConsts &P) {
     return csub(r, P.q);
 }
 
-// Right after snorm: replace the 2^60-weighted a2 by its residue
-// [2^60 a2]_q (lazy, < 2q < 2^61) spread over a0 and a1, congruent modulo
-// P.q; afterwards a0 < 2^31, a1 < 2^31, a2 = 0, so the snorm bounds restart.
-__device__ __forceinline__ void sfold60(Split3 &s, const PrimeConsts &P) {
-    const uint64_t r = shoup_lazy(s.a2, P.r60, P.r60p, P.q);
-    s.a0 += r & M30;
-    s.a1 += r >> 30;
-    s.a2 = 0;
-}
-__device__ __forceinline__ void sfold60(Split3c &s, const PrimeConsts &P) {
-    const uint64_t r = shoup_lazy(s.a2, P.r60, P.r60p, P.q);
-    s.a0 += r & M30;
-    s.a1 += r >> 30;
-    s.a2 = 0;
-}
-
-// Two-level normalisation for long Split3 sums (base conversion): snorm0
-// moves a0's carries into a1 (due every 15 products: a0 < 2^30 afterwards);
-// snorm_hi moves a1's and a1b's carries into a2 (due every 28 products: both
-// take one product below 2^59 + 2^52 per smac plus a0's carries).  a2 gains
-// one product below 2^58.1 per smac: fold it (sfold60) at least every 56.
-__device__ __forceinline__ void snorm0(Split3 &s) {
-    s.a1 += s.a0 >> 30;
-    s.a0 &= M30;
-}
-__device__ __forceinline__ void snorm_hi(Split3 &s) {
-    s.a2 += (s.a1 >> 30) + (s.a1b >> 30);
-    s.a1 &= M30;
-    s.a1b &= M30;
-}
-// a0 + 2^30 (a1 + a1b) + 2^60 a2 mod q for a sum kept within the snorm0 /
-// snorm_hi / sfold60 cadence (each part may be just short of 2^64).
-__device__ __forceinline__ uint64_t sfinal_mod(Split3 s, const PrimeConsts &P) {
-    s.a1 += s.a0 >> 30;
-    const uint64_t hi = s.a2 + (s.a1 >> 30) + (s.a1b >> 30);                     // < 2^64
-    const uint64_t lo = (s.a0 & M30) + (((s.a1 & M30) + (s.a1b & M30)) << 30);  // < 2^61 < 4q
-    uint64_t r = shoup_lazy4(hi, P.r60, P.r60p, 0 - P.q) + lo;                 // < 8q < 2^63
-    r = csub_sign(r, 0 - 4 * P.q);
-    r = csub_sign(r, 0 - 2 * P.q);
-    return csub_sign(r, 0 - P.q);
-}
-
 // Full reduction of a split sum modulo P.q, left in normalised split form
 // (a0, a1 < 2^30, a2 = 0): restarts the growth bounds of snorm.
 __device__ __forceinline__ void sreduce(Split3 &s, const PrimeConsts &P) {
