@@ -1092,68 +1092,82 @@ __global__ void k_rescale_final(const uint64_t *__restrict__ in, const uint64_t 
 // coefficients and 16 columns; thread (k, col) keeps its rotated inputs for up
 // to MAC_B baby steps in registers (split30).  The diagonals of giant step g
 // (MAC_B x 16 values, 128-byte runs) are staged in LDS, double-buffered and
-// prefetched one giant step ahead, and read as broadcasts: every diagonal
-// element leaves HBM once.  Baby steps beyond MAC_B are added in further passes.
+// prefetched two giant steps ahead, and read as broadcasts: every diagonal
+// element leaves HBM once.  Baby steps beyond MAC_B are added in further
+// passes (ACC: the pass adds into inner).  Every global load is issued
+// unconditionally (addresses clamped to valid rows, unused values masked
+// afterwards) so that loads stay in flight together instead of each waiting
+// behind a per-lane branch; FULL marks launches whose columns are all active.
 // ---------------------------------------------------------------------
-constexpr int MAC_K = 16, MAC_C = 16, MAC_B = 32;
+constexpr int MAC_K = 16, MAC_C = 16, MAC_B = 32, MAC_R = 4;
 static_assert(MAC_B <= 4 * SPLIT_CHUNK, "one split sum per giant step without a 128-bit fold");
+static_assert(MAC_B % MAC_R == 0, "diagonal rows are read from LDS in groups of MAC_R");
 
+template <bool FULL, bool ACC>
 __global__ __launch_bounds__(256) void k_bsgs_mac(const uint64_t *__restrict__ pt, const uint64_t *__restrict__ in,
                                                    const uint64_t *__restrict__ rot, uint64_t *__restrict__ inner,
                                                    const PrimeConsts *__restrict__ pc, uint32_t n, uint32_t l,
                                                    uint32_t bs, uint32_t gs, uint32_t ncols, size_t ctsize,
                                                    uint32_t b0) {
     __shared__ uint64_t ps[2][MAC_B * MAC_K];
+    const uint32_t t = threadIdx.x;
     const uint32_t i = blockIdx.y;
     const uint32_t k0 = blockIdx.x * MAC_K;
-    const uint32_t kl = threadIdx.x % MAC_K;
-    const uint32_t col = blockIdx.z * MAC_C + threadIdx.x / MAC_K;
-    const bool active = col < ncols;
+    const uint32_t kl = t % MAC_K;
+    const uint32_t col = blockIdx.z * MAC_C + t / MAC_K;
+    const bool active = FULL || col < ncols;
     const PrimeConsts P = pc[i];
     const uint32_t nb = min((uint32_t)MAC_B, bs - b0);
     const size_t off = ((size_t)(active ? col : 0) * l + i) * n + k0 + kl;
     uint64_t r[MAC_B];
 #pragma unroll
     for (int bb = 0; bb < MAC_B; bb++) {
-        const uint32_t b = b0 + bb;
-        r[bb] = (active && bb < (int)nb) ? split30(b == 0 ? in[off] : rot[(size_t)(b - 1) * ctsize + off]) : 0;
+        const uint32_t b = b0 + min((uint32_t)bb, nb - 1);
+        r[bb] = (b == 0 ? in : rot + (size_t)(b - 1) * ctsize)[off];
     }
+    // the empty asm takes every loaded value, so the loads cannot be sunk into per-row branches
+#pragma unroll
+    for (int bb = 0; bb < MAC_B; bb++) asm volatile("" : "+v"(r[bb]));
+#pragma unroll
+    for (int bb = 0; bb < MAC_B; bb++) r[bb] = (active && bb < (int)nb) ? split30(r[bb]) : 0;
     const size_t pstride = (size_t)l * n;
     // staging: thread t loads elements x = t and t + 256 of the MAC_B x MAC_K tile
     auto pt_addr = [&](uint32_t g, uint32_t x) -> const uint64_t * {
         const uint32_t bb = x / MAC_K, kk = x % MAC_K;
         return pt + ((size_t)g * bs + b0 + min(bb, nb - 1)) * pstride + (size_t)i * n + k0 + kk;
     };
-    // diagonal tiles are prefetched two giant steps ahead (registers a: even g, b: odd g)
-    uint64_t a0 = *pt_addr(0, threadIdx.x), a1 = *pt_addr(0, threadIdx.x + 256);
-    uint64_t b0v = 0, b1v = 0;
-    if (gs > 1) {
-        b0v = *pt_addr(1, threadIdx.x);
-        b1v = *pt_addr(1, threadIdx.x + 256);
-    }
+    // diagonal tiles are prefetched two giant steps ahead (registers a: even g, b: odd g);
+    // past the last giant step the last tile is fetched again, so every step issues its loads
+    const uint32_t g1 = min(1u, gs - 1);
+    uint64_t a0 = *pt_addr(0, t), a1 = *pt_addr(0, t + 256);
+    uint64_t b0v = *pt_addr(g1, t), b1v = *pt_addr(g1, t + 256);
     auto step = [&](uint32_t g, uint64_t &s0, uint64_t &s1) {
         uint64_t *buf = ps[g & 1];
-        buf[threadIdx.x] = split30(s0);  // stored split: low 30 bits | high 30 bits << 32
-        buf[threadIdx.x + 256] = split30(s1);
+        buf[t] = split30(s0);  // stored split: low 30 bits | high 30 bits << 32
+        buf[t + 256] = split30(s1);
         __syncthreads();
-        if (g + 2 < gs) {
-            s0 = *pt_addr(g + 2, threadIdx.x);
-            s1 = *pt_addr(g + 2, threadIdx.x + 256);
-        }
+        const uint32_t gn = min(g + 2, gs - 1);
+        s0 = *pt_addr(gn, t);
+        s1 = *pt_addr(gn, t + 256);
         Split3c sp{0, 0, 0};
 #pragma unroll
-        for (int bb = 0; bb < MAC_B; bb++) {
-            // rows bb >= nb hold a valid (clamped) diagonal and r[bb] = 0: no guard needed
-            const uint64_t p = buf[bb * MAC_K + kl];
-            smac(sp, (uint32_t)p, (uint32_t)(p >> 32), r[bb]);
-            if (bb % SPLIT_CHUNK == SPLIT_CHUNK - 1) snorm(sp);
+        for (int c = 0; c < MAC_B; c += MAC_R) {
+            // rows bb >= nb hold a valid (clamped) diagonal and a zero rotation: no guard needed
+            uint64_t p[MAC_R];
+#pragma unroll
+            for (int j = 0; j < MAC_R; j++) p[j] = buf[(c + j) * MAC_K + kl];
+#pragma unroll
+            for (int j = 0; j < MAC_R; j++) asm volatile("" : "+v"(p[j]));  // the group's reads issue together
+#pragma unroll
+            for (int j = 0; j < MAC_R; j++) {
+                smac(sp, (uint32_t)p[j], (uint32_t)(p[j] >> 32), r[c + j]);
+                if ((c + j) % SPLIT_CHUNK == SPLIT_CHUNK - 1) snorm(sp);
+            }
         }
-        if (active) {
-            uint64_t v = sreduce60(sp, P);
-            uint64_t *o = inner + (size_t)g * ctsize + off;
-            if (b0) v = addm(v, *o, P.q);
-            *o = v;
-        }
+        uint64_t v = sreduce60(sp, P);
+        uint64_t *o = inner + (size_t)g * ctsize + off;
+        if (ACC) v = addm(v, *o, P.q);
+        if (active) *o = v;
     };
     // the LDS buffer of step g is rewritten at step g + 2, after the barrier of step g + 1
     for (uint32_t g = 0; g < gs; g += 2) {
@@ -1599,9 +1613,12 @@ int op_bsgs(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, const 
     }
     for (int b0 = 0; b0 < bs; b0 += MAC_B) {
         ProfScope ps_(c, "bsgs_mac", s);
-        hipLaunchKernelGGL(k_bsgs_mac, dim3(c->n / MAC_K, l, (2 * B + MAC_C - 1) / MAC_C), dim3(256), 0, s, diags,
-                           in, rot, inner, c->d_pc, c->n, (uint32_t)l, (uint32_t)bs, (uint32_t)gs, (uint32_t)(2 * B),
-                           ct, (uint32_t)b0);
+        const dim3 grid(c->n / MAC_K, l, (2 * B + MAC_C - 1) / MAC_C);
+        const bool full = (2 * B) % MAC_C == 0;
+        auto kern = b0 ? (full ? k_bsgs_mac<true, true> : k_bsgs_mac<false, true>)
+                       : (full ? k_bsgs_mac<true, false> : k_bsgs_mac<false, false>);
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, diags, in, rot, inner, c->d_pc, c->n, (uint32_t)l,
+                           (uint32_t)bs, (uint32_t)gs, (uint32_t)(2 * B), ct, (uint32_t)b0);
         LAUNCH_CHECK();
     }
     // giant steps: batches of independent rotations of inner[g], summed into inner[0]

@@ -145,8 +145,11 @@ def _bsgs_inputs(o, seed, B, l, bs, gs):
     return x, pt, baby, giant
 
 
-# giant batches of 2, 1, 5 and 7 steps: summed parts of 1, 2 (ragged) and 2/1 steps
-@pytest.mark.parametrize("l,B,bs,gs", [(20, 2, 4, 3), (112, 1, 2, 2), (20, 2, 2, 6), (24, 3, 3, 8)])
+# giant batches of 2, 1, 5 and 7 steps: summed parts of 1, 2 (ragged) and 2/1 steps; 16 columns
+# (every MAC column active) with an odd giant-step count and with a single giant step; more than 32
+# baby steps (a second MAC pass that adds into the first)
+@pytest.mark.parametrize("l,B,bs,gs", [(20, 2, 4, 3), (112, 1, 2, 2), (20, 2, 2, 6), (24, 3, 3, 8), (6, 8, 3, 5),
+                                       (5, 8, 2, 1), (6, 1, 34, 2), (4, 8, 33, 3)])
 def test_bsgs_small_bitexact(l, B, bs, gs):
     g, o = gpu_ctx(*LAY), oracle_ctx(*LAY)
     x, pt, baby, giant = _bsgs_inputs(o, 80 + l, B, l, bs, gs)
