@@ -940,21 +940,30 @@ __global__ __launch_bounds__(256) void k_final2048(const uint64_t *__restrict__ 
     const uint64_t *cv = conv + (size_t)blockIdx.x * n;
 #pragma unroll
     for (int m = 0; m < 8; m++) v[m] = cv[t + 256 * m];
-    n2048::fwd(v, lds, twf + (size_t)i * n * 2, q);
-    if (MODE == 2 && c == 0) {  // stage c0 of this limb for the Galois gather
+    // the accumulator row (and for rotations c0) are loaded before the transform, so they arrive
+    // while it runs instead of after it (its barriers keep the compiler from hoisting them)
+    const uint64_t *ar = acc + ((cb * 2 + c) * (l + K) + i) * n;
+    uint64_t av[8], c0v[8];
+#pragma unroll
+    for (int m = 0; m < 8; m++) av[m] = ar[t + 256 * m];
+    if (MODE == 2) {  // c == 1 reads the same (valid) row and leaves it unused
         const uint64_t *c0 = xa + (b * 2) * per + (size_t)i * n;
 #pragma unroll
-        for (int m = 0; m < 8; m++) lds[t + 256 * m] = c0[t + 256 * m];
+        for (int m = 0; m < 8; m++) c0v[m] = c0[t + 256 * m];
+    }
+    n2048::fwd(v, lds, twf + (size_t)i * n * 2, q);
+    if (MODE == 2 && c == 0) {  // stage c0 of this limb for the Galois gather
+#pragma unroll
+        for (int m = 0; m < 8; m++) lds[t + 256 * m] = c0v[m];
         __syncthreads();
     }
-    const uint64_t *ar = acc + ((cb * 2 + c) * (l + K) + i) * n;
     uint64_t *o = out + (size_t)blockIdx.x * n;
     const uint64_t w = pinv[2 * i], wp = pinv[2 * i + 1];
 #pragma unroll
     for (int m = 0; m < 8; m++) {
         const uint32_t k = t + 256 * m;
         const uint64_t x = n2048::reduce8(v[m], q);
-        uint64_t r = shoup(subm(ar[k], x, q), w, wp, q);
+        uint64_t r = shoup(subm(av[m], x, q), w, wp, q);
         if (MODE == 1) {
             const size_t o0 = (b * 2) * per + (size_t)i * n + k, o1 = o0 + per;
             uint64_t y;

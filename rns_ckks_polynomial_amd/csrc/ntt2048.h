@@ -41,20 +41,30 @@ __device__ __forceinline__ int own(int t, int k) {
 
 __device__ __forceinline__ int brev(int i) { return (int)(__builtin_bitreverse32((uint32_t)i) >> (32 - LOGN)); }
 
-__device__ __forceinline__ void bf_ct(uint64_t &x, uint64_t &y, uint64_t w, uint64_t wp, uint64_t q) {
-    const uint64_t q4 = 4 * q;
-    const uint64_t a = csub_sign(x, 0 - q4);      // [0, 4q)
-    const uint64_t t = shoup_lazy4(y, w, wp, 0 - q); // [0, 4q)
-    x = a + t;                                    // [0, 8q)
-    y = a + q4 - t;                               // (0, 8q)
+// Per-prime constants of the butterflies.  -4q passes through an empty asm so
+// that x - 4q stays one 64-bit add (v_lshl_add_u64) instead of being turned
+// back into a subtract with borrow.
+struct BfConsts {
+    uint64_t q, q4, nq4;
+};
+__device__ __forceinline__ BfConsts bf_consts(uint64_t q) {
+    BfConsts c{q, 4 * q, 0 - 4 * q};
+    asm volatile("" : "+v"(c.nq4));
+    return c;
 }
 
-__device__ __forceinline__ void bf_gs(uint64_t &x, uint64_t &y, uint64_t w, uint64_t wp, uint64_t q) {
-    const uint64_t q4 = 4 * q;
-    const uint64_t s = x + y;                     // [0, 8q)
-    const uint64_t d = x + q4 - y;                // (0, 8q)
-    x = csub_sign(s, 0 - q4);                     // [0, 4q)
-    y = shoup_lazy4(d, w, wp, 0 - q);             // [0, 4q)
+__device__ __forceinline__ void bf_ct(uint64_t &x, uint64_t &y, uint64_t w, uint64_t wp, const BfConsts &c) {
+    const uint64_t a = csub_sign(x, c.nq4);           // [0, 4q)
+    const uint64_t t = shoup_lazy4(y, w, wp, 0 - c.q); // [0, 4q)
+    x = a + t;                                        // [0, 8q)
+    y = a + c.q4 - t;                                 // (0, 8q)
+}
+
+__device__ __forceinline__ void bf_gs(uint64_t &x, uint64_t &y, uint64_t w, uint64_t wp, const BfConsts &c) {
+    const uint64_t s = x + y;                         // [0, 8q)
+    const uint64_t d = x + c.q4 - y;                  // (0, 8q)
+    x = csub_sign(s, c.nq4);                          // [0, 4q)
+    y = shoup_lazy4(d, w, wp, 0 - c.q);               // [0, 4q)
 }
 
 // [0, 8q) -> [0, q): the forward transform's outputs fully reduced.
@@ -66,7 +76,7 @@ __device__ __forceinline__ uint64_t reduce8(uint64_t x, uint64_t q) {
 
 // One radix-2 stage (bit BIT of the index) on the 8 registers of a pass owning bits [C, C+3).
 template <int C, int BIT, bool INV>
-__device__ __forceinline__ void stage(uint64_t (&v)[E], int t, const uint64_t *__restrict__ tw, uint64_t q) {
+__device__ __forceinline__ void stage(uint64_t (&v)[E], int t, const uint64_t *__restrict__ tw, const BfConsts &q) {
     constexpr int s = LOGN - 1 - BIT;  // stage number in the Cooley-Tukey order
     constexpr int kb = 1 << (BIT - C);
 #pragma unroll
@@ -93,8 +103,9 @@ __device__ __forceinline__ void from_lds(const uint64_t *lds, uint64_t (&v)[E], 
 
 // Forward NTT.  On entry v[k] = a[t + 256 k] (natural order, values < 8q);
 // on exit v[k] = A[t + 256 k] in [0, 8q) (reduce8 finishes).  Uses lds[LDS_WORDS]; ends with a barrier.
-__device__ __forceinline__ void fwd(uint64_t (&v)[E], uint64_t *lds, const uint64_t *__restrict__ tw, uint64_t q) {
+__device__ __forceinline__ void fwd(uint64_t (&v)[E], uint64_t *lds, const uint64_t *__restrict__ tw, uint64_t qv) {
     const int t = threadIdx.x;
+    const BfConsts q = bf_consts(qv);
     stage<8, 10, false>(v, t, tw, q);
     stage<8, 9, false>(v, t, tw, q);
     stage<8, 8, false>(v, t, tw, q);
@@ -129,8 +140,9 @@ __device__ __forceinline__ void fwd(uint64_t (&v)[E], uint64_t *lds, const uint6
 
 // Inverse NTT without the final n^-1 scaling.  On entry v[k] = A[t + 256 k]
 // (values < 4q); on exit v[k] = n a[t + 256 k] in [0, 4q).
-__device__ __forceinline__ void inv(uint64_t (&v)[E], uint64_t *lds, const uint64_t *__restrict__ tw, uint64_t q) {
+__device__ __forceinline__ void inv(uint64_t (&v)[E], uint64_t *lds, const uint64_t *__restrict__ tw, uint64_t qv) {
     const int t = threadIdx.x;
+    const BfConsts q = bf_consts(qv);
 #pragma unroll
     for (int k = 0; k < E; k++) lds[slot(brev(t + NT * k))] = v[k];
     __syncthreads();
