@@ -181,6 +181,10 @@ __device__ __forceinline__ void sreduce(Split3 &s, const PrimeConsts &P) {
     const uint64_t r = reduce128(v.lo, v.hi, P);
     s = Split3{r & M30, r >> 30, 0, 0};
 }
+__device__ __forceinline__ void sreduce(Split3c &s, const PrimeConsts &P) {
+    const uint64_t r = sreduce60(s, P);
+    s = Split3c{r & M30, r >> 30, 0};
+}
 
 // ------------------------------------------------------------------ tables
 // Exact base conversion from a contiguous run of primes (a "basis": one

@@ -699,40 +699,74 @@ __global__ __launch_bounds__(256) void k_inner_hoisted2048(const uint64_t *__res
     const uint32_t e = grp % el, s0 = (grp / el) * HOIST_SPW, s1 = min(st.count, s0 + HOIST_SPW);
     const uint32_t gi = e < l ? e : L + (e - l);
     const uint32_t t = threadIdx.x;
-    for (uint32_t j = 0; j < beta; j++) {
-        const bool own = e >= j * alpha && e < min(l, (j + 1) * alpha);
-        const uint64_t *src = own ? d + b * d_stride + (size_t)e * n : ext + ((b * beta + j) * el + e) * n;
+    {  // every digit row is requested before the first is stored (rows past beta repeat the last)
+        uint64_t dv[HOIST_MAX_BETA][8];
 #pragma unroll
-        for (int m = 0; m < 8; m++) dig[j * n + t + 256 * m] = src[t + 256 * m];
+        for (uint32_t j = 0; j < HOIST_MAX_BETA; j++) {
+            const uint32_t jj = min(j, beta - 1);
+            const bool own = e >= jj * alpha && e < min(l, (jj + 1) * alpha);
+            const uint64_t *src = own ? d + b * d_stride + (size_t)e * n : ext + ((b * beta + jj) * el + e) * n;
+#pragma unroll
+            for (int m = 0; m < 8; m++) dv[j][m] = src[t + 256 * m];
+        }
+#pragma unroll
+        for (uint32_t j = 0; j < HOIST_MAX_BETA; j++)
+#pragma unroll
+            for (int m = 0; m < 8; m++) dig[j * n + t + 256 * m] = dv[j][m];
     }
     __syncthreads();
     const PrimeConsts P = pc[gi];
-    for (uint32_t step = s0; step < s1; step++) {
-        const uint64_t *key = st.key[step];
-        const uint32_t g = st.g[step];
-        Split3 a0[8], a1[8];
-#pragma unroll
-        for (int m = 0; m < 8; m++) a0[m] = a1[m] = {0, 0, 0, 0};
-        for (uint32_t j = 0; j < beta; j++) {
-            const uint64_t *kb = key + ((size_t)j * 2 * (L + K) + gi) * n;
-            const uint64_t *ka = kb + (size_t)(L + K) * n;
-#pragma unroll
-            for (int m = 0; m < 8; m++) {
-                const uint32_t k = t + 256 * m;
-                const uint64_t v = dig[j * n + galois_src(k, g, n)];
-                const uint32_t vl = (uint32_t)(v & M30), vh = (uint32_t)(v >> 30);
-                smac(a0[m], vl, vh, split30(kb[k]));
-                smac(a1[m], vl, vh, split30(ka[k]));
-            }
-        }
-        // beta <= HOIST_MAX_BETA products per sum: within the snorm-free bound
-        const size_t cb = (size_t)step * st.B + b;
-        uint64_t *o0 = acc + ((cb * 2 + 0) * el + e) * n, *o1 = acc + ((cb * 2 + 1) * el + e) * n;
+    // (step, digit) pairs run flattened, it = (step - s0) beta + j; the key rows of pair it + 1 are
+    // in flight while pair it is multiplied (buffers A / B alternate; past the last pair the last
+    // rows are fetched again)
+    const uint32_t T = (s1 - s0) * beta;
+    Split3c a0[8], a1[8];
+    auto kload = [&](uint32_t it, uint64_t (&kbv)[8], uint64_t (&kav)[8]) {
+        it = min(it, T - 1);
+        const uint32_t step = s0 + it / beta, j = it % beta;
+        const uint64_t *kb = st.key[step] + ((size_t)j * 2 * (L + K) + gi) * n;
+        const uint64_t *ka = kb + (size_t)(L + K) * n;
 #pragma unroll
         for (int m = 0; m < 8; m++) {
-            o0[t + 256 * m] = sreduce60(a0[m], P);
-            o1[t + 256 * m] = sreduce60(a1[m], P);
+            kbv[m] = kb[t + 256 * m];
+            kav[m] = ka[t + 256 * m];
         }
+    };
+    auto pair = [&](uint32_t it, const uint64_t (&kbv)[8], const uint64_t (&kav)[8]) {
+        const uint32_t step = s0 + it / beta, j = it % beta;
+        if (j == 0) {
+#pragma unroll
+            for (int m = 0; m < 8; m++) a0[m] = a1[m] = {0, 0, 0};
+        }
+        const uint32_t g = st.g[step];
+#pragma unroll
+        for (int m = 0; m < 8; m++) {
+            const uint64_t v = dig[j * n + galois_src(t + 256 * m, g, n)];
+            const uint32_t vl = (uint32_t)(v & M30), vh = (uint32_t)(v >> 30);
+            smac(a0[m], vl, vh, split30(kbv[m]));
+            smac(a1[m], vl, vh, split30(kav[m]));
+        }
+        if (j == beta - 1 && it < T) {  // beta <= HOIST_MAX_BETA products per sum: within the snorm-free bound
+            const size_t cb = (size_t)step * st.B + b;
+            uint64_t *o0 = acc + ((cb * 2 + 0) * el + e) * n, *o1 = acc + ((cb * 2 + 1) * el + e) * n;
+#pragma unroll
+            for (int m = 0; m < 8; m++) {
+                o0[t + 256 * m] = sreduce60(a0[m], P);
+                o1[t + 256 * m] = sreduce60(a1[m], P);
+            }
+        }
+    };
+    // the empty asm with a memory clobber is a compiler-only fence: the prefetch stays ahead of
+    // the pair it overlaps instead of being sunk next to its use
+    uint64_t kbA[8], kaA[8], kbB[8], kaB[8];
+    kload(0, kbA, kaA);
+    for (uint32_t it = 0; it < T; it += 2) {
+        kload(it + 1, kbB, kaB);
+        asm volatile("" ::: "memory");
+        pair(it, kbA, kaA);
+        kload(it + 2, kbA, kaA);
+        asm volatile("" ::: "memory");
+        pair(it + 1, kbB, kaB);  // it + 1 = T (T odd) multiplies the repeated last rows and stores nothing
     }
 }
 
@@ -766,9 +800,9 @@ __global__ __launch_bounds__(256) void k_inner_sum2048(const uint64_t *__restric
     const uint32_t t = threadIdx.x;
     const PrimeConsts P = pc[e];
     const uint64_t pm = split30(pmod[e]);
-    Split3 s0[8], s1[8];
+    Split3c s0[8], s1[8];
 #pragma unroll
-    for (int m = 0; m < 8; m++) s0[m] = s1[m] = {0, 0, 0, 0};
+    for (int m = 0; m < 8; m++) s0[m] = s1[m] = {0, 0, 0};
     uint32_t cnt = 0, rounds = 0, bi = 0;
     // called before each product: at most 15 products between snorm, at most
     // 4 snorm rounds between full reductions
@@ -798,21 +832,31 @@ __global__ __launch_bounds__(256) void k_inner_sum2048(const uint64_t *__restric
         for (uint32_t j = 0; j < beta; j++) {
             const bool own = e >= j * alpha && e < min(l, (j + 1) * alpha);
             const uint64_t *src = own ? d + cb * d_stride + (size_t)e * n : ext + ((cb * beta + j) * el + e) * n;
+            const uint64_t *kb = key + ((size_t)j * 2 * (L + K) + e) * n;
+            const uint64_t *ka = kb + (size_t)(L + K) * n;
+            // the key rows are requested with the digit row, before the barrier (which the
+            // compiler does not move loads across), so both arrive in one memory latency
+            uint64_t sv[8], kbv[8], kav[8];
+#pragma unroll
+            for (int m = 0; m < 8; m++) sv[m] = src[t + 256 * m];
+#pragma unroll
+            for (int m = 0; m < 8; m++) {
+                kbv[m] = kb[t + 256 * m];
+                kav[m] = ka[t + 256 * m];
+            }
             uint64_t *lb = buf[bi];
             bi ^= 1;
 #pragma unroll
-            for (int m = 0; m < 8; m++) lb[t + 256 * m] = src[t + 256 * m];
+            for (int m = 0; m < 8; m++) lb[t + 256 * m] = sv[m];
             __syncthreads();
             guard();
-            const uint64_t *kb = key + ((size_t)j * 2 * (L + K) + e) * n;
-            const uint64_t *ka = kb + (size_t)(L + K) * n;
 #pragma unroll
             for (int m = 0; m < 8; m++) {
                 const uint32_t k = t + 256 * m;
                 const uint64_t v = lb[galois_src(k, g, n)];
                 const uint32_t vl = (uint32_t)(v & M30), vh = (uint32_t)(v >> 30);
-                smac(s0[m], vl, vh, split30(kb[k]));
-                smac(s1[m], vl, vh, split30(ka[k]));
+                smac(s0[m], vl, vh, split30(kbv[m]));
+                smac(s1[m], vl, vh, split30(kav[m]));
             }
         }
         {  // P sigma_g(c0) joins the c = 0 sum
