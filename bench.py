@@ -45,19 +45,19 @@ LIMB = N * 8
 # counters (profiles/bench_step_n2048_l112_b8_hbm_counters.md).  Valid only for
 # the kernel sources they were taken on (hash of rns_ckks_polynomial_amd/csrc).
 MEASURED_TRAFFIC = {
-    "source_sha": "1c12b3800a91db89",
+    "source_sha": "da13f575719406c0",
     "bytes_per_launch": {
-        "ks_modup_convert": 812912070,
-        "ks_moddown_convert": 750430192,
-        "bsgs_mac": 3758217878,
-        "ks_ntt_ext": 1321912517,
-        "ks_inner_product_sum": 2848363672,
-        "rotate_final": 3192378036,
-        "ntt_fwd": 62576853,
-        "ntt_inv": 62598867,
-        "giant_final": 297539062,
-        "ks_intt_modup": 326837640,
-        "ks_intt_moddown": 310306602
+        "ks_modup_convert": 812860195,
+        "ks_moddown_convert": 750522262,
+        "bsgs_mac": 3758215478,
+        "ks_ntt_ext": 1324535143,
+        "ks_inner_product_sum": 2848517735,
+        "rotate_final": 3190058933,
+        "ntt_fwd": 62572920,
+        "ntt_inv": 62598338,
+        "giant_final": 297544053,
+        "ks_intt_modup": 326832678,
+        "ks_intt_moddown": 310299923
     },
 }
 
