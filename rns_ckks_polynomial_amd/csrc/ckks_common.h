@@ -29,12 +29,20 @@ __device__ __forceinline__ uint64_t csub(uint64_t x, uint64_t q) { return x >= q
 __device__ __forceinline__ uint64_t shoup_lazy4(uint64_t y, uint64_t w, uint64_t wp, uint64_t nq) {
     const uint32_t yl = (uint32_t)y, yh = (uint32_t)(y >> 32);
     const uint32_t pl = (uint32_t)wp, ph = (uint32_t)(wp >> 32);
-    const uint64_t qt = (uint64_t)yh * ph + ((uint64_t)__umulhi(yh, pl) + __umulhi(yl, ph));
+    // the two high halves are summed with an explicit carry (add, add-with-carry) into the
+    // 64-bit addend of the yh ph multiply-add, instead of two zero-extended 64-bit adds
+    uint32_t c;
+    const uint32_t hs = __builtin_addc(__umulhi(yh, pl), __umulhi(yl, ph), 0u, &c);
+    const uint64_t qt = (uint64_t)yh * ph + (((uint64_t)c << 32) | hs);
     const uint32_t ql = (uint32_t)qt, qh = (uint32_t)(qt >> 32);
     const uint32_t wl = (uint32_t)w, wh = (uint32_t)(w >> 32);
     const uint32_t nl = (uint32_t)nq, nh = (uint32_t)(nq >> 32);
     const uint64_t r = (uint64_t)ql * nl + (uint64_t)yl * wl;  // mod 2^64
-    const uint32_t hi = (uint32_t)(r >> 32) + yl * wh + yh * wl + ql * nh + qh * nl;
+    // the high word is a 32-bit sum (the empty asm keeps it from being rewritten as a
+    // 64-bit add of a shifted value)
+    uint32_t rh = (uint32_t)(r >> 32);
+    asm("" : "+v"(rh));
+    const uint32_t hi = rh + yl * wh + yh * wl + ql * nh + qh * nl;
     return ((uint64_t)hi << 32) | (uint32_t)r;
 }
 
