@@ -119,6 +119,22 @@ def cpu_baseline(budget_s: float):
                       f"{el:.1f} s, OpenMP over limbs/coefficients"}
 
 
+def cpu_baseline_one_core(budget_s: float):
+    """The same oracle sample on one core: a child process (OpenMP reads its
+    thread count at start-up) that touches no GPU."""
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    code = (f"import json, sys; sys.path.insert(0, {ROOT!r}); import bench; "
+            f"print(json.dumps(bench.cpu_baseline({budget_s!r})))")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=600)
+    if r.returncode != 0:
+        return {"error": r.stderr.strip().splitlines()[-1:] or ["child failed"]}
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    d["cores"] = 1
+    d["sample"] = d["sample"].replace("OpenMP over limbs/coefficients", "one OpenMP thread")
+    return d
+
+
 EM_DEGREE, EM_ANGLES, EM_K = 31, 3, 8.0
 
 
@@ -350,10 +366,14 @@ def main():
     ms = el / args.steps * 1e3
     ks_per_step = BATCH + BATCH * (BS + GS - 2)
 
-    # split of the step (separate pass, event-bracketed)
-    for _ in range(2):
+    # split of the step (separate pass, event-bracketed); also each step's own time
+    nsplit, step_times = 5, []
+    for _ in range(nsplit):
+        before = parts["mul_relin_rescale_ms"] + parts["bsgs_ms"]
         step(timed=True)
-    mr_ms, bsgs_ms = parts["mul_relin_rescale_ms"] / 2, parts["bsgs_ms"] / 2
+        step_times.append(parts["mul_relin_rescale_ms"] + parts["bsgs_ms"] - before)
+    mr_ms, bsgs_ms = parts["mul_relin_rescale_ms"] / nsplit, parts["bsgs_ms"] / nsplit
+    step_times.sort()
 
     # standalone batched NTT throughput on the same [8][2][112] limbs
     x = a.clone().view(BATCH * 2, L, N)
@@ -370,6 +390,39 @@ def main():
     ntt_ms = e0.elapsed_time(e1) / (2 * reps)
     limbs = BATCH * 2 * L
     ntt_rate = limbs / (ntt_ms * 1e-3)
+
+    # forward-NTT batch sweep at the 4-prime shape of the standalone NTT workload (the chain's
+    # first 4 primes): polynomials x 4 limbs, to show where the launch saturates the chip
+    sweep = []
+    for polys in (1, 4, 16, 64, 256, 1024, 4096):
+        y = torch.empty((polys, 4, N), dtype=u64, device=dev)
+        g.fill_uniform(y.view(polys, 4, N), 0xC0DE0001, synth.TAG_CT, 0)
+        g.ntt_fwd(y)
+        r = max(5, min(200, 20000 // polys))
+        e0.record()
+        for _ in range(r):
+            g.ntt_fwd(y)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / r * 1e3
+        sweep.append({"polys": polys, "limbs": 4 * polys, "us_per_launch": us,
+                      "limb_ntts_per_s": 4 * polys / (us * 1e-6),
+                      "algo_GBps": 4 * polys * 2 * LIMB / (us * 1e-6) / 1e9})
+        del y
+
+    # pointwise product (an HBM-bound step on its own): [8][2][112] limbs, 2 read + 1 written
+    pw = torch.empty_like(x)
+    g.pointwise_mul(x, x, out=pw)
+    e0.record()
+    for _ in range(reps):
+        g.pointwise_mul(x, x, out=pw)
+    e1.record()
+    torch.cuda.synchronize()
+    pw_us = e0.elapsed_time(e1) / reps * 1e3
+    pw_gbs = 3 * limbs * LIMB / (pw_us * 1e-6) / 1e9
+    pointwise = {"limbs": limbs, "us_per_launch": pw_us, "algo_GBps": pw_gbs, "frac_of_8TBps": pw_gbs / HBM_PEAK_GBS,
+                 "work": "a * b mod q elementwise: 2 limbs read + 1 written per limb"}
+    del pw
 
     # EvalMod (bootstrapping's modular reduction, outside the step): batch 8 at
     # the 112-prime level, degree-31 cosine interpolant on [-8, 8], 3 double angles
@@ -463,6 +516,9 @@ def main():
         "linear_transforms_per_s": BATCH / (bsgs_ms * 1e-3),
         "ct_mults_per_s": BATCH / (mr_ms * 1e-3),
         "step_split_ms": {"mul_relin_rescale": mr_ms, "bsgs": bsgs_ms},
+        "step_ms_events": {"median": step_times[nsplit // 2], "min": step_times[0], "steps": nsplit},
+        "ntt_sweep": sweep,
+        "pointwise": pointwise,
         "roofline": roofline,
         "ntt_roofline": ntt_roof,
         "kernels": kernels,
@@ -476,6 +532,7 @@ def main():
         out["copy_calibration_bytes"] = 2 * src.numel() * 8
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        out["cpu_baseline"]["one_core"] = cpu_baseline_one_core(min(5.0, args.cpu_seconds))
     print(json.dumps(out))
 
 
