@@ -442,12 +442,50 @@ __global__ __launch_bounds__(256, OCC) void k_convert_mfma(const BasisDev *__res
     // Otherwise the digit-table slice of each (pass, chunk), 2 tiles x 16
     // positions x 8 digits x 32 rows, goes through a double-buffered LDS slice
     // that the workgroup fills one step ahead (all its waves run the same steps).
+    // H fragments are kept in reverse digit order, Hr[7 - b] = digit plane b, so that the pair
+    // (b, b - 1) a 64-deep product takes is one ascending register tuple
     long hb[TT][8];
-    auto load_h = [&](long(&H)[8], uint32_t tile, uint32_t buf) {
+    auto load_h = [&](long(&Hr)[8], uint32_t tile, uint32_t buf) {
         const int8_t *h = STAGED ? sh_h + ((tile - tile0) * 16 + col) * MF_HSTRIDE + 8 * grp
                                  : sh_h + ((buf * 2 + (tile - tile0) % 2) * 16 + col) * MF_HSTRIDE + 8 * grp;
 #pragma unroll
-        for (int b = 0; b < 8; b++) H[b] = *(const long *)(h + 32 * b);
+        for (int b = 0; b < 8; b++) Hr[7 - b] = *(const long *)(h + 32 * b);
+    };
+    // S_s += sum_{a+b=s} dA_a dH_b.  Two digit pairs of one diagonal, (a, s-a) and (a+1, s-a-1),
+    // go through one 16x16x64 product of the concatenated fragments {A_a | A_a+1} and
+    // {H_s-a | H_s-a-1} (both operands take the same K positions, so the product is the sum of
+    // the two 32-deep ones); a diagonal with an odd number of pairs ends with one 16x16x32.  That
+    // is 36 instructions per tile and chunk instead of 64, at the rate of the 64-deep form.
+    // Rounds run over the diagonals, so consecutive products go to different accumulators.
+    // The staged two-wave variant (summed sets) keeps the 64 32-deep products: the pairs'
+    // operand tuples would push its register budget into spills.
+    constexpr bool PAIRED = OCC == 3 || !STAGED;
+    auto mac_tile = [&](mf_v4i(&ac)[15], const long(&Hr)[8]) {
+        typedef long mf_v2l __attribute__((ext_vector_type(2)));
+        if constexpr (!PAIRED) {
+#pragma unroll
+            for (int b = 0; b < 8; b++)
+#pragma unroll
+                for (int a = 0; a < 8; a++)
+                    ac[a + b] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A[a], Hr[7 - b], ac[a + b], 0, 0, 0);
+            return;
+        }
+#pragma unroll
+        for (int rd = 0; rd < 4; rd++)
+#pragma unroll
+            for (int sd = 0; sd < 15; sd++) {
+                const int a0 = sd > 7 ? sd - 7 : 0, a1 = sd < 7 ? sd : 7, a = a0 + 2 * rd;
+                if (a + 1 > a1) continue;
+                const mf_v2l av = {A[a], A[a + 1]}, hv = {Hr[7 - (sd - a)], Hr[8 - (sd - a)]};
+                ac[sd] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(mf_v4i, av),
+                                                              __builtin_bit_cast(mf_v4i, hv), ac[sd], 0, 0, 0);
+            }
+#pragma unroll
+        for (int sd = 0; sd < 15; sd++) {
+            const int a0 = sd > 7 ? sd - 7 : 0, a1 = sd < 7 ? sd : 7;
+            if ((a1 - a0) % 2 == 0)
+                ac[sd] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A[a1], Hr[7 - (sd - a1)], ac[sd], 0, 0, 0);
+        }
     };
     // the slice of step g: thread x copies 16-byte pieces q = x and x + 256 of the
     // 2 x 16 x 8 x 32 bytes (tiles past tile_end read padded, in-bounds positions)
@@ -549,11 +587,7 @@ __global__ __launch_bounds__(256, OCC) void k_convert_mfma(const BasisDev *__res
         for (uint32_t tt = 0; tt < TT; tt++) {
             if (t0 + tt >= tile_end) break;  // workgroup-uniform
             if (!STAGED || ch == 0) load_h(hb[tt], t0 + tt, g & 1);
-#pragma unroll
-            for (int b = 0; b < 8; b++)
-#pragma unroll
-                for (int a = 0; a < 8; a++)
-                    acc[tt][a + b] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A[a], hb[tt][b], acc[tt][a + b], 0, 0, 0);
+            mac_tile(acc[tt], hb[tt]);
         }
         if constexpr (!STAGED) {
             // the next slice goes to the other buffer, whose last readers (step g - 1)
