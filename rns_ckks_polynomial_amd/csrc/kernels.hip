@@ -415,7 +415,11 @@ __global__ __launch_bounds__(256, OCC) void k_convert_mfma(const BasisDev *__res
         for (uint32_t q = threadIdx.x; q < np * MF_RC; q += 256) sh_rc[q] = rsrc[q];
         __syncthreads();
     }
-    long A[8];  // digit plane a of the lane's 8 rows (byte j = row 8 grp + j)
+    // digit plane a of the lane's 8 rows (byte j = row 8 grp + j) is half a % 2 of AP[a / 2]: the
+    // planes 2i, 2i + 1 form one register tuple, the A operand of a 64-deep product
+    mf_v4i AP[4];
+    typedef long mf_v2l __attribute__((ext_vector_type(2)));
+    auto plane_a = [&](int a) -> long { return __builtin_bit_cast(mf_v2l, AP[a / 2])[a % 2]; };
     auto build_a = [&](const uint64_t(&raw)[8], uint32_t uraw, uint32_t ch) {
         const uint32_t r0 = (ch % cps) * 32 + 8 * grp;
         uint64_t z[8];
@@ -432,7 +436,11 @@ __global__ __launch_bounds__(256, OCC) void k_convert_mfma(const BasisDev *__res
         bt4((uint32_t)(z[4] >> 32), (uint32_t)(z[5] >> 32), (uint32_t)(z[6] >> 32), (uint32_t)(z[7] >> 32), o[1][4],
             o[1][5], o[1][6], o[1][7]);
 #pragma unroll
-        for (int a = 0; a < 8; a++) A[a] = (long)(((uint64_t)o[1][a] << 32) | o[0][a]);
+        for (int i = 0; i < 4; i++) {
+            const mf_v2l pr = {(long)(((uint64_t)o[1][2 * i] << 32) | o[0][2 * i]),
+                               (long)(((uint64_t)o[1][2 * i + 1] << 32) | o[0][2 * i + 1])};
+            AP[i] = __builtin_bit_cast(mf_v4i, pr);
+        }
     };
     // TT target tiles share each chunk's A fragments (2 when the contraction has
     // several chunks, so the rows are fetched and transposed once per 2 tiles)
@@ -442,49 +450,53 @@ __global__ __launch_bounds__(256, OCC) void k_convert_mfma(const BasisDev *__res
     // Otherwise the digit-table slice of each (pass, chunk), 2 tiles x 16
     // positions x 8 digits x 32 rows, goes through a double-buffered LDS slice
     // that the workgroup fills one step ahead (all its waves run the same steps).
-    // H fragments are kept in reverse digit order, Hr[7 - b] = digit plane b, so that the pair
-    // (b, b - 1) a 64-deep product takes is one ascending register tuple
-    long hb[TT][8];
-    auto load_h = [&](long(&Hr)[8], uint32_t tile, uint32_t buf) {
+    // The product of a tile and chunk, S_s += sum_{a+b=s} dA_a dH_b, runs on 64-deep MFMAs where
+    // it can: the digit pairs (2i, s-2i) and (2i+1, s-2i-1) of diagonal s go through one
+    // 16x16x64 product of the tuples {A_2i | A_2i+1} = AP[i] and {H_b | H_b-1} = HP[7 - b],
+    // b = s - 2i (both operands take the same K positions, so the product is the sum of the two
+    // 32-deep ones).  The planes left over (a = s for even s <= 6, b = 7 for even s >= 8) take
+    // one 16x16x32 each: 28 + 8 instructions per tile and chunk instead of 64, at the rate of
+    // the 64-deep form.  HP's seven tuples overlap in content.  The staged two-wave variant
+    // (summed sets) keeps 64 32-deep products on 8 fragments: the tuples would push it into
+    // spills.
+    constexpr bool PAIRED = OCC == 3 || !STAGED;
+    constexpr int NH = PAIRED ? 7 : 4;  // 4-VGPR H registers per tile
+    mf_v4i hb[TT][NH];
+    auto load_h = [&](mf_v4i(&H)[NH], uint32_t tile, uint32_t buf) {
         const int8_t *h = STAGED ? sh_h + ((tile - tile0) * 16 + col) * MF_HSTRIDE + 8 * grp
                                  : sh_h + ((buf * 2 + (tile - tile0) % 2) * 16 + col) * MF_HSTRIDE + 8 * grp;
+        auto pl = [&](int bb) -> long { return *(const long *)(h + 32 * bb); };
 #pragma unroll
-        for (int b = 0; b < 8; b++) Hr[7 - b] = *(const long *)(h + 32 * b);
+        for (int j = 0; j < NH; j++) {
+            const mf_v2l v = PAIRED ? mf_v2l{pl(7 - j), pl(6 - j)} : mf_v2l{pl(2 * j), pl(2 * j + 1)};
+            H[j] = __builtin_bit_cast(mf_v4i, v);
+        }
     };
-    // S_s += sum_{a+b=s} dA_a dH_b.  Two digit pairs of one diagonal, (a, s-a) and (a+1, s-a-1),
-    // go through one 16x16x64 product of the concatenated fragments {A_a | A_a+1} and
-    // {H_s-a | H_s-a-1} (both operands take the same K positions, so the product is the sum of
-    // the two 32-deep ones); a diagonal with an odd number of pairs ends with one 16x16x32.  That
-    // is 36 instructions per tile and chunk instead of 64, at the rate of the 64-deep form.
-    // Rounds run over the diagonals, so consecutive products go to different accumulators.
-    // The staged two-wave variant (summed sets) keeps the 64 32-deep products: the pairs'
-    // operand tuples would push its register budget into spills.
-    constexpr bool PAIRED = OCC == 3 || !STAGED;
-    auto mac_tile = [&](mf_v4i(&ac)[15], const long(&Hr)[8]) {
-        typedef long mf_v2l __attribute__((ext_vector_type(2)));
+    auto mac_tile = [&](mf_v4i(&ac)[15], const mf_v4i(&H)[NH]) {
         if constexpr (!PAIRED) {
 #pragma unroll
-            for (int b = 0; b < 8; b++)
+            for (int bb = 0; bb < 8; bb++)
 #pragma unroll
-                for (int a = 0; a < 8; a++)
-                    ac[a + b] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A[a], Hr[7 - b], ac[a + b], 0, 0, 0);
+                for (int aa = 0; aa < 8; aa++)
+                    ac[aa + bb] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                        plane_a(aa), __builtin_bit_cast(mf_v2l, H[bb / 2])[bb % 2], ac[aa + bb], 0, 0, 0);
             return;
         }
+        auto hsing = [&](int bb) -> long {  // plane b inside HP: HP[7 - b] = {H_b, H_b-1}, HP[6] = {H_1, H_0}
+            return bb > 0 ? __builtin_bit_cast(mf_v2l, H[7 - bb])[0] : __builtin_bit_cast(mf_v2l, H[6])[1];
+        };
 #pragma unroll
-        for (int rd = 0; rd < 4; rd++)
+        for (int i = 0; i < 4; i++)
 #pragma unroll
             for (int sd = 0; sd < 15; sd++) {
-                const int a0 = sd > 7 ? sd - 7 : 0, a1 = sd < 7 ? sd : 7, a = a0 + 2 * rd;
-                if (a + 1 > a1) continue;
-                const mf_v2l av = {A[a], A[a + 1]}, hv = {Hr[7 - (sd - a)], Hr[8 - (sd - a)]};
-                ac[sd] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(mf_v4i, av),
-                                                              __builtin_bit_cast(mf_v4i, hv), ac[sd], 0, 0, 0);
+                const int bb = sd - 2 * i;  // pair (2i, b), (2i+1, b-1)
+                if (bb < 1 || bb > 7) continue;
+                ac[sd] = __builtin_amdgcn_mfma_i32_16x16x64_i8(AP[i], H[7 - bb], ac[sd], 0, 0, 0);
             }
 #pragma unroll
-        for (int sd = 0; sd < 15; sd++) {
-            const int a0 = sd > 7 ? sd - 7 : 0, a1 = sd < 7 ? sd : 7;
-            if ((a1 - a0) % 2 == 0)
-                ac[sd] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A[a1], Hr[7 - (sd - a1)], ac[sd], 0, 0, 0);
+        for (int sd = 0; sd < 15; sd += 2) {  // leftovers: a = s (b = 0) for s <= 6, a = s - 7 (b = 7) for s >= 8
+            const int aa = sd <= 6 ? sd : sd - 7, bb = sd - aa;
+            ac[sd] = __builtin_amdgcn_mfma_i32_16x16x32_i8(plane_a(aa), hsing(bb), ac[sd], 0, 0, 0);
         }
     };
     // the slice of step g: thread x copies 16-byte pieces q = x and x + 256 of the
