@@ -339,8 +339,9 @@ __device__ __forceinline__ uint32_t conv_target(const ConvTargets &ct, uint32_t 
 // its u (H = [-B]_t), then zeros up to BasisDev::mk.  Both operands are written
 // in signed base-256 digits (digit_form), so the product is
 //   sum_s 256^s S_s,   S_s = sum_{a+b=s} sum_r dY_a[k][r] dH_b[r][t],
-// and each digit pair (a, b) is one exact int8 x int8 -> int32 16x16x32 MFMA
-// adding into S_{a+b} (|S_s| <= 8 rows 2^14 <= 2^28 for rows <= MF_MAX_ROWS).
+// and each digit pair (a, b) is an exact int8 x int8 -> int32 product on the
+// matrix cores adding into S_{a+b} (|S_s| <= 8 rows 2^14 <= 2^28 for rows <=
+// MF_MAX_ROWS); two pairs of a diagonal share one 16x16x64 MFMA (mac_tile).
 // One wave computes 16 coefficients x 16 target positions at a time: lane l
 // supplies coefficient row l % 16 of Y and target column l % 16 of H, each with
 // the 8 rows 8 (l / 16) + j of a 32-row chunk, and ends with target column
