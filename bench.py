@@ -45,19 +45,19 @@ LIMB = N * 8
 # counters (profiles/bench_step_n2048_l112_b8_hbm_counters.md).  Valid only for
 # the kernel sources they were taken on (hash of rns_ckks_polynomial_amd/csrc).
 MEASURED_TRAFFIC = {
-    "source_sha": "da13f575719406c0",
+    "source_sha": "b35b164e71e2719b",
     "bytes_per_launch": {
-        "ks_modup_convert": 812860195,
-        "ks_moddown_convert": 750522262,
-        "bsgs_mac": 3758215478,
-        "ks_ntt_ext": 1324535143,
-        "ks_inner_product_sum": 2848517735,
-        "rotate_final": 3190058933,
-        "ntt_fwd": 62572920,
-        "ntt_inv": 62598338,
-        "giant_final": 297544053,
-        "ks_intt_modup": 326832678,
-        "ks_intt_moddown": 310299923
+        "ks_modup_convert": 812993425,
+        "ks_moddown_convert": 750635204,
+        "bsgs_mac": 3758189791,
+        "ks_ntt_ext": 1335473098,
+        "ks_inner_product_sum": 2848554102,
+        "rotate_final": 3190246645,
+        "ntt_fwd": 62554458,
+        "ntt_inv": 62597334,
+        "giant_final": 297546375,
+        "ks_intt_modup": 326830530,
+        "ks_intt_moddown": 310297659
     },
 }
 
@@ -88,7 +88,7 @@ def parse():
                         "(19 -> 2100 -> 2083 primes; about 160 GB of HBM)")
     p.add_argument("--boot-reps", type=int, default=2)
     p.add_argument("--step-only", action="store_true",
-                   help="skip the EvalMod, bootstrapping and seeded-key legs (profiler runs of the step)")
+                   help="skip the EvalMod, bootstrapping, seeded-key, NTT-sweep and pointwise legs (profiler runs of the step)")
     return p.parse_args()
 
 
@@ -394,7 +394,7 @@ def main():
     # forward-NTT batch sweep at the 4-prime shape of the standalone NTT workload (the chain's
     # first 4 primes): polynomials x 4 limbs, to show where the launch saturates the chip
     sweep = []
-    for polys in (1, 4, 16, 64, 256, 1024, 4096):
+    for polys in (() if args.step_only else (1, 4, 16, 64, 256, 1024, 4096)):
         y = torch.empty((polys, 4, N), dtype=u64, device=dev)
         g.fill_uniform(y.view(polys, 4, N), 0xC0DE0001, synth.TAG_CT, 0)
         g.ntt_fwd(y)
@@ -411,18 +411,21 @@ def main():
         del y
 
     # pointwise product (an HBM-bound step on its own): [8][2][112] limbs, 2 read + 1 written
-    pw = torch.empty_like(x)
-    g.pointwise_mul(x, x, out=pw)
-    e0.record()
-    for _ in range(reps):
+    pointwise = None
+    pw = torch.empty_like(x) if not args.step_only else None
+    if pw is not None:
         g.pointwise_mul(x, x, out=pw)
-    e1.record()
-    torch.cuda.synchronize()
-    pw_us = e0.elapsed_time(e1) / reps * 1e3
-    pw_gbs = 3 * limbs * LIMB / (pw_us * 1e-6) / 1e9
-    pointwise = {"limbs": limbs, "us_per_launch": pw_us, "algo_GBps": pw_gbs, "frac_of_8TBps": pw_gbs / HBM_PEAK_GBS,
-                 "work": "a * b mod q elementwise: 2 limbs read + 1 written per limb"}
-    del pw
+        e0.record()
+        for _ in range(reps):
+            g.pointwise_mul(x, x, out=pw)
+        e1.record()
+        torch.cuda.synchronize()
+        pw_us = e0.elapsed_time(e1) / reps * 1e3
+        pw_gbs = 3 * limbs * LIMB / (pw_us * 1e-6) / 1e9
+        pointwise = {"limbs": limbs, "us_per_launch": pw_us, "algo_GBps": pw_gbs,
+                     "frac_of_8TBps": pw_gbs / HBM_PEAK_GBS,
+                     "work": "a * b mod q elementwise: 2 limbs read + 1 written per limb"}
+        del pw
 
     # EvalMod (bootstrapping's modular reduction, outside the step): batch 8 at
     # the 112-prime level, degree-31 cosine interpolant on [-8, 8], 3 double angles
