@@ -83,7 +83,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
-    p.add_argument("--boot-config4", action="store_true",
+    p.add_argument("--boot-chain2100", action="store_true",
                    help="only time the bootstrap of 8 ciphertexts on the 2100 + 263 prime chain "
                         "(19 -> 2100 -> 2083 primes; about 160 GB of HBM)")
     p.add_argument("--boot-reps", type=int, default=2)
@@ -202,7 +202,7 @@ def bootstrap_timing(g, torch, lt, l0, cts, stc, baby, giant, conj, rlk, reps, s
             "kernel_ms_by_scope": scopes}
 
 
-def boot_config4(args):
+def boot_chain2100(args):
     """The 2100 + 263 prime chain (dnum 8): 8 ciphertexts at 19 primes refreshed to 2083."""
     import torch
 
@@ -308,11 +308,11 @@ def kernel_work():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the hot path is measured on one "
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the hot path is measured on one "
                                    "GPU's share; pass --gpus 1"}))
         sys.exit(2)
-    if args.boot_config4:
-        boot_config4(args)
+    if args.boot_chain2100:
+        boot_chain2100(args)
         return
     import torch
 
@@ -508,8 +508,8 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u64",
         "data": "synthetic (seeded SplitMix64 residues, resident in HBM)",
-        "config": {"workload": "n=2048, 112+28 primes, dnum=4, batch 8: ct x ct tensor+relin+rescale (config 2) "
-                               "and BSGS 32x32 linear transform + rescale at 112 primes (config 3)",
+        "config": {"workload": "n=2048, 112+28 primes, dnum=4, batch 8: ct x ct tensor+relin+rescale "
+                               "and BSGS 32x32 linear transform + rescale at 112 primes",
                    "global_batch": BATCH, "parallelism": "single GPU"},
         "key_switches_per_step": ks_per_step,
         "eval_mod": em,

@@ -333,7 +333,7 @@ __device__ __forceinline__ uint32_t conv_target(const ConvTargets &ct, uint32_t 
 }
 
 // ---------------------------------------------------------------------
-// Base conversion on the matrix cores.  The same sums as k_convert,
+// Base conversion on the matrix cores: the exact conversion sums
 //   out[k][t] = sum_r Y[k][r] H[r][t] mod t,
 // with the rows r of every summed set = its m inputs y_i (H = [Bhat_i]_t), then
 // its u (H = [-B]_t), then zeros up to BasisDev::mk.  Both operands are written
@@ -1454,7 +1454,7 @@ static int ks_moddown_conv(ckks_ctx *c, size_t nout, int l, const KsWs &w, hipSt
     LAUNCH_CHECK();
     {
         ConvTargets ct{(uint32_t)l, L, K, (size_t)l * n, 0};
-        // lay_dn.inner == 1: the summed sets are evenly spaced, as k_convert assumes
+        // lay_dn.inner == 1: the summed sets are evenly spaced, as k_convert_mfma assumes
         ct.nsum = nsum;
         ct.sum_stride = (uint32_t)(nout / nsum * 2);
         // up to 4 parts: long summed workgroups need enough of them to fill the chip

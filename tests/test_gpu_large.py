@@ -30,7 +30,7 @@ def _gpu():
     torch.cuda.empty_cache()
 
 
-def test_config3_bsgs_full_batch8():
+def test_bsgs_32x32_l112_batch8_full():
     P = (2048, 112, 28, 4)
     g, o = gpu_ctx(*P), oracle_ctx(*P)
     l, B, bs, gs, tot = 112, 8, 32, 32, 140
@@ -40,9 +40,9 @@ def test_config3_bsgs_full_batch8():
     keys = gfill(g, (bs + gs - 2, 4, 2, tot, 2048), seed, synth.TAG_KEY)
     baby = [None] + [keys[b - 1] for b in range(1, bs)]
     giant = [None] + [keys[bs - 2 + j] for j in range(1, gs)]
-    say("config3: GPU BSGS 32x32, batch 8, l=112")
+    say("bsgs 32x32 l=112 batch 8: GPU")
     out = host(g.bsgs_linear_transform(x, pt, bs, gs, baby, giant, do_rescale=True))
-    say("config3: oracle for ciphertext 0")
+    say("bsgs 32x32 l=112 batch 8: oracle for ciphertext 0")
     xc = cfill(o, seed, synth.TAG_CT, 2, l).reshape(2, l, 2048)
     ptc = cfill(o, seed, synth.TAG_DIAG, gs * bs, l).reshape(gs, bs, l, 2048)
     kc = cfill(o, seed, synth.TAG_KEY, (bs + gs - 2) * 8, tot).reshape(bs + gs - 2, 4, 2, tot, 2048)
@@ -50,7 +50,7 @@ def test_config3_bsgs_full_batch8():
                  [None] + [kc[bs - 2 + j] for j in range(1, gs)], l, do_rescale=True)
     assert np.array_equal(out[0], ref), mismatch(out[0], ref)
     # ciphertext 7 on a few output limbs: recompute its own full result
-    say("config3: oracle for ciphertext 7")
+    say("bsgs 32x32 l=112 batch 8: oracle for ciphertext 7")
     x7 = cfill(o, seed, synth.TAG_CT, 2, l, stream0=7 * 2 * l).reshape(2, l, 2048)
     ref7 = o.bsgs(x7, ptc, bs, gs, [None] + [kc[b - 1] for b in range(1, bs)],
                   [None] + [kc[bs - 2 + j] for j in range(1, gs)], l, do_rescale=True)
@@ -85,7 +85,7 @@ def test_ring65536_ntt_round_trip():
     assert np.array_equal(host(p), o.ntt(pc, first=40))
 
 
-def test_config5_relin_rotations_rescale():
+def test_ring65536_l40_relin_rotations_rescale():
     """4 pairs at l=40: p = relin(tensor(x, y)); r_i = rotate(p, 2^i), i < 16; rescale all."""
     g, o = gpu_ctx(*C5), oracle_ctx(*C5)
     l, B, n, tot = 40, 4, 65536, 48
@@ -94,7 +94,7 @@ def test_config5_relin_rotations_rescale():
     b = gfill(g, (B, 2, l, n), seed + 1, synth.TAG_CT)
     rlk = gfill(g, (5, 2, tot, n), seed, synth.TAG_KEY)
     rkeys = [gfill(g, (5, 2, tot, n), seed + 10 + j, synth.TAG_KEY) for j in range(4)]
-    say("config5: GPU")
+    say("n=65536 l=40: GPU")
     p = g.mul_tensor_relin(a, b, rlk)
     ph = host(p)
     rs = host(g.rescale(p))
@@ -103,7 +103,7 @@ def test_config5_relin_rotations_rescale():
         r = g.rotate(p, galois_rot(n, 1 << i), rkeys[i % 4])
         rots.append(host(r)[0])
         rrs.append(host(g.rescale(r))[0])
-    say("config5: oracle, ciphertext 0")
+    say("n=65536 l=40: oracle, ciphertext 0")
     a0 = cfill(o, seed, synth.TAG_CT, 2, l).reshape(2, l, n)
     b0 = cfill(o, seed + 1, synth.TAG_CT, 2, l).reshape(2, l, n)
     rl = cfill(o, seed, synth.TAG_KEY, 10, tot).reshape(5, 2, tot, n)
@@ -115,7 +115,7 @@ def test_config5_relin_rotations_rescale():
         ref = o.rotate(p0, galois_rot(n, 1 << i), rk[i % 4], l)
         assert np.array_equal(rots[i], ref), (i, mismatch(rots[i], ref))
         assert np.array_equal(rrs[i], o.rescale(ref, l)), i
-    say("config5: oracle, ciphertext 3 (relin)")
+    say("n=65536 l=40: oracle, ciphertext 3 (relin)")
     a3 = cfill(o, seed, synth.TAG_CT, 2, l, stream0=3 * 2 * l).reshape(2, l, n)
     b3 = cfill(o, seed + 1, synth.TAG_CT, 2, l, stream0=3 * 2 * l).reshape(2, l, n)
     assert np.array_equal(ph[3], o.mul_tensor_relin(a3, b3, rl, l))
@@ -124,7 +124,7 @@ def test_config5_relin_rotations_rescale():
 C4 = (2048, 2100, 263, 8)
 
 
-def test_config4_keyswitch_ops():
+def test_chain2100_keyswitch_ops():
     """Rotation (2100 primes), conjugation (2099), relinearisation (2084: partial last digit), rescale."""
     g, o = gpu_ctx(*C4), oracle_ctx(*C4)
     n, tot = 2048, 2363
@@ -132,7 +132,7 @@ def test_config4_keyswitch_ops():
     key = gfill(g, (8, 2, tot, n), seed, synth.TAG_KEY)
     kc = cfill(o, seed, synth.TAG_KEY, 16, tot).reshape(8, 2, tot, n)
     for l, kind in [(2100, "rot"), (2099, "conj"), (2084, "relin")]:
-        say(f"config4: {kind} at l={l}")
+        say(f"2100-prime chain: {kind} at l={l}")
         x = gfill(g, (1, 2, l, n), seed + l, synth.TAG_CT)
         xc = cfill(o, seed + l, synth.TAG_CT, 2, l).reshape(2, l, n)
         if kind == "relin":
@@ -149,7 +149,7 @@ def test_config4_keyswitch_ops():
             assert np.array_equal(host(g.rescale(x))[0], o.rescale(xc, l))
 
 
-def test_config4_bsgs_sparse_diagonals():
+def test_chain2100_bsgs_sparse_diagonals():
     """Full 32 x 32 BSGS at 2100 primes (every rotation key-switched, as benchmarked) with
     two non-zero plaintext diagonals (g1, b1), (g2, b2): the result is
     Rescale(rot_{32 g1}(pt1 . rot_b1(x)) + rot_{32 g2}(pt2 . rot_b2(x)))."""
@@ -157,7 +157,7 @@ def test_config4_bsgs_sparse_diagonals():
     n, l, tot, bs, gs = 2048, 2100, 2363, 32, 32
     seed = 0xC0DE0004
     picks = [(5, 7), (0, 3)]
-    say("config4 bsgs: generating keys and diagonals on the GPU")
+    say("2100-prime bsgs: generating keys and diagonals on the GPU")
     keys = gfill(g, (bs + gs - 2, 8, 2, tot, n), seed + 1, synth.TAG_KEY)
     pt = torch.zeros((gs, bs, l, n), dtype=torch.uint64, device="cuda")
     for (gg, bb) in picks:
@@ -165,10 +165,10 @@ def test_config4_bsgs_sparse_diagonals():
     x = gfill(g, (1, 2, l, n), seed, synth.TAG_CT)
     baby = [None] + [keys[b - 1] for b in range(1, bs)]
     giant = [None] + [keys[bs - 2 + j] for j in range(1, gs)]
-    say("config4 bsgs: GPU")
+    say("2100-prime bsgs: GPU")
     got = host(g.bsgs_linear_transform(x, pt, bs, gs, baby, giant, do_rescale=True))[0]
     del keys, pt
-    say("config4 bsgs: oracle")
+    say("2100-prime bsgs: oracle")
     xc = cfill(o, seed, synth.TAG_CT, 2, l).reshape(2, l, n)
     acc = np.zeros((2, l, n), dtype=np.uint64)
     q = o.primes[:l].astype(object)[None, :, None]

@@ -1,5 +1,5 @@
-"""GPU parity: chain parameters, seeded fill, NTT / iNTT and the config-1
-polynomial multiply, bit-exact against the oracle (through the C ABI)."""
+"""GPU parity: chain parameters, seeded fill, NTT / iNTT and the 4-prime
+polynomial multiply at n = 2048, bit-exact against the oracle (through the C ABI)."""
 import numpy as np
 import pytest
 
@@ -36,7 +36,7 @@ def _rand(o, seed, count, nl, first=0):
                              np.tile(o.primes[first:first + nl], count), o.n).reshape(count, nl, o.n)
 
 
-def test_ntt_config1_bitexact():
+def test_ntt_4primes_bitexact():
     """n = 2048, 4 primes, 2 polynomials: forward and inverse against the oracle."""
     g, o = gpu_ctx(2048, 4), oracle_ctx(2048, 4)
     x = _rand(o, 0xC0DE0001, 2, 4)
@@ -52,7 +52,7 @@ def test_ntt_config1_bitexact():
     assert np.array_equal(host(t2), o.ntt(ref, inverse=True))
 
 
-def test_config1_polynomial_multiply():
+def test_4prime_polynomial_multiply():
     """forward NTT, pointwise modmul, inverse NTT == schoolbook product mod X^2048 + 1."""
     g, o = gpu_ctx(2048, 4), oracle_ctx(2048, 4)
     a = _rand(o, 0xC0DE0001, 1, 4)
@@ -69,7 +69,7 @@ def test_config1_polynomial_multiply():
 
 
 def test_ntt_lay_batch_bitexact():
-    """[8][2][112] limbs (one batch of config-2 ciphertexts), and the special primes."""
+    """[8][2][112] limbs (a batch of 8 ciphertexts at 112 primes), and the special primes."""
     g, o = gpu_ctx(2048, 112, 28, 4), oracle_ctx(2048, 112, 28, 4)
     x = _rand(o, 3, 16, 112)
     t = dev(x)

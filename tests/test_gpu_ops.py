@@ -120,8 +120,8 @@ def test_moddown_exact_boundary():
     assert np.array_equal(out[0], ref), mismatch(out[0], ref)
 
 
-def test_config2_batch8_relin_rescale():
-    """Config 2: 8 pairs at 112 primes, tensor + relinearise + rescale, every residue."""
+def test_relin_rescale_l112_batch8():
+    """8 pairs at 112 primes, tensor + relinearise + rescale, every residue."""
     g, o = gpu_ctx(*LAY), oracle_ctx(*LAY)
     l, B = 112, 8
     seed = 0xC0DE0002

@@ -97,7 +97,7 @@ def test_schoolbook_is_exact_negacyclic_product():
     assert [int(x) for x in oracle.negacyclic_schoolbook(a, b, q)] == [v % q for v in exact]
 
 
-def test_config1_poly_multiply_convolution_theorem():
+def test_4prime_poly_multiply_convolution_theorem():
     """Negacyclic multiply mod X^2048 + 1 over the 4 smallest chain primes:
     iNTT(NTT(a) * NTT(b)) equals the schoolbook product, bit for bit."""
     n = 2048
