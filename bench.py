@@ -88,7 +88,8 @@ def parse():
                         "(19 -> 2100 -> 2083 primes; about 160 GB of HBM)")
     p.add_argument("--boot-reps", type=int, default=2)
     p.add_argument("--step-only", action="store_true",
-                   help="skip the EvalMod, bootstrapping, seeded-key, NTT-sweep and pointwise legs (profiler runs of the step)")
+                   help="skip the EvalMod, bootstrapping, seeded-key, ring-65536, NTT-sweep and pointwise legs "
+                        "(profiler runs of the step)")
     return p.parse_args()
 
 
@@ -266,6 +267,54 @@ def seeded_key_timing(g, torch, a, key, reps: int = 40):
     return res
 
 
+def ring65536_timing(torch, reps: int = 5):
+    """The ring-65536 workload: n = 65536, 40 + 8 primes, dnum 5, 4 ciphertext pairs.  Batched NTT /
+    iNTT over the [4][2][40] limbs, tensor + relinearise of the 4 pairs (4 key switches) and rotations
+    of the 4 products (4 key switches each, one rotation key reused)."""
+    from rns_ckks_polynomial_amd import synth
+    from rns_ckks_polynomial_amd.api import Context, galois_rot
+    n, l, k, dnum, b = 65536, 40, 8, 5, 4
+    g = Context(n, l, k, dnum, device=0)
+    u64 = torch.uint64
+    x = torch.empty((b, 2, l, n), dtype=u64, device="cuda")
+    y = torch.empty_like(x)
+    rlk = torch.empty((dnum, 2, l + k, n), dtype=u64, device="cuda")
+    rk = torch.empty_like(rlk)
+    g.fill_uniform(x, 0xC0DE0005, synth.TAG_CT, 0)
+    g.fill_uniform(y, 0xC0DE0006, synth.TAG_CT, 0)
+    g.fill_uniform(rlk, 0xC0DE0005, synth.TAG_KEY, 0)
+    g.fill_uniform(rk, 0xC0DE0007, synth.TAG_KEY, 0)
+    ws = g.workspace(max(g.workspace_size("relin", b, l), g.workspace_size("rotate", b, l)))
+    prod, rot = torch.empty_like(x), torch.empty_like(x)
+    limbs = x.clone().view(b * 2, l, n)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn(0)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(reps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ntt_ms = timed(lambda i: (g.ntt_fwd(limbs), g.ntt_inv(limbs))) / 2
+    relin_ms = timed(lambda i: g.mul_tensor_relin(x, y, rlk, out=prod, ws=ws))
+    rot_ms = timed(lambda i: g.rotate(prod, galois_rot(n, 1 << (i % 16)), rk, out=rot, ws=ws))
+    nl = b * 2 * l
+    out = {"limb_ntts_per_s": nl / (ntt_ms * 1e-3),
+           "ntt_algo_GBps": nl * 2 * n * 8 / (ntt_ms * 1e-3) / 1e9,
+           "ntt_ms_per_direction": ntt_ms,
+           "key_switches_per_s_relin": b / (relin_ms * 1e-3), "relin_ms": relin_ms,
+           "key_switches_per_s_rotate": b / (rot_ms * 1e-3), "rotate_ms": rot_ms,
+           "config": "n=65536, 40+8 primes, dnum=5, 4 ciphertext pairs: NTT/iNTT of [4][2][40] limbs, "
+                     "tensor+relin (4 key switches), rotation by 2^i (4 key switches)"}
+    del x, y, rlk, rk, ws, prod, rot, limbs, g
+    torch.cuda.empty_cache()
+    return out
+
+
 def kernel_work():
     """Algorithmic work of each kernel per benchmark step (all launches of that
     kernel in one step; launches differ in size since BSGS batches its steps).
@@ -429,7 +478,7 @@ def main():
 
     # EvalMod (bootstrapping's modular reduction, outside the step): batch 8 at
     # the 112-prime level, degree-31 cosine interpolant on [-8, 8], 3 double angles
-    em = boot = seeded = None
+    em = boot = seeded = ring = None
     if not args.step_only:
         em = eval_mod_timing(g, a, rlk, torch)
         # seed-expanded switching keys: rotation with the key's a rows regenerated in the kernel
@@ -440,6 +489,7 @@ def main():
         g.fill_uniform(stc, 0xC0DE0005, synth.TAG_DIAG, 0)
         boot = bootstrap_timing(g, torch, L, 1, diags, stc, baby, giant, keys[0], rlk, 2, 0xC0DE0006)
         del stc
+        ring = ring65536_timing(torch)
 
     # per-kernel launch times (library event profiler) over profiled steps + the NTT pair
     g.profile_begin()
@@ -515,6 +565,7 @@ def main():
         "eval_mod": em,
         "bootstrap": boot,
         "seeded_keys": seeded,
+        "ring65536": ring,
         "limb_ntts_per_s": ntt_rate,
         "linear_transforms_per_s": BATCH / (bsgs_ms * 1e-3),
         "ct_mults_per_s": BATCH / (mr_ms * 1e-3),

@@ -930,42 +930,82 @@ __global__ __launch_bounds__(256) void k_inner_sum2048(const uint64_t *__restric
     }
 }
 
-// Generic-n version: one thread per output coefficient, gathered global reads.
+// Generic-n version: one thread per (extended limb, coefficient) for all B
+// ciphertexts of the step, gathered global reads.  The thread loads its key
+// values once and reuses them for every ciphertext (consecutive threads take
+// consecutive coefficients, so the reads stay coalesced and each key row
+// leaves memory once per launch instead of once per ciphertext).
+constexpr uint32_t INNER_UNROLL = 8;  // digits held in registers (beta up to this; larger beta loops)
 template <bool SEEDED>
 __global__ void k_inner(const uint64_t *__restrict__ d, size_t d_stride, const uint64_t *__restrict__ ext,
                         const uint64_t *__restrict__ key, uint64_t *__restrict__ acc,
                         const PrimeConsts *__restrict__ pc, uint32_t n, uint32_t l, uint32_t L, uint32_t K,
-                        uint32_t beta, uint32_t alpha, uint32_t g, uint64_t root, size_t total) {
+                        uint32_t beta, uint32_t alpha, uint32_t g, uint64_t root, uint32_t B) {
     const uint32_t el = l + K;
+    const size_t total = (size_t)el * n;
     for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total;
          idx += (size_t)gridDim.x * blockDim.x) {
         const uint32_t k = idx % n;
-        const uint32_t e = (idx / n) % el;
-        const size_t b = idx / ((size_t)n * el);
+        const uint32_t e = idx / n;
         const uint32_t gi = e < l ? e : L + (e - l);
         const uint32_t ks = galois_src(k, g, n);
-        Split3 s0{0, 0, 0, 0}, s1{0, 0, 0, 0};
-        for (uint32_t j = 0; j < beta; j++) {
+        auto digit = [&](size_t b, uint32_t j) -> uint64_t {
             const bool own = e >= j * alpha && e < min(l, (j + 1) * alpha);
-            const uint64_t v = own ? d[b * d_stride + (size_t)e * n + ks] : ext[((b * beta + j) * el + e) * n + ks];
-            const uint64_t *kr = key + ((size_t)j * (SEEDED ? 1 : 2) * (L + K) + gi) * n + k;
-            const uint32_t vl = (uint32_t)(v & M30), vh = (uint32_t)(v >> 30);
-            smac(s0, vl, vh, split30(kr[0]));
-            smac(s1, vl, vh,
-                 split30(SEEDED ? seeded_a(sm_at(root, (uint64_t)j * (L + K) + gi), k, pc[gi].q)
-                                : kr[(size_t)(L + K) * n]));
-            if ((j + 1) % SPLIT_CHUNK == 0) {  // more than 15 digits: keep the sums in bounds
-                snorm(s0);
-                snorm(s1);
-                if ((j + 1) % (4 * SPLIT_CHUNK) == 0) {
-                    sreduce(s0, pc[gi]);
-                    sreduce(s1, pc[gi]);
+            return own ? d[b * d_stride + (size_t)e * n + ks] : ext[((b * beta + j) * el + e) * n + ks];
+        };
+        auto key_b = [&](uint32_t j) -> uint64_t {
+            return key[((size_t)j * (SEEDED ? 1 : 2) * (L + K) + gi) * n + k];
+        };
+        auto key_a = [&](uint32_t j) -> uint64_t {
+            return SEEDED ? seeded_a(sm_at(root, (uint64_t)j * (L + K) + gi), k, pc[gi].q)
+                          : key[((size_t)j * 2 * (L + K) + gi) * n + k + (size_t)(L + K) * n];
+        };
+        if (beta <= INNER_UNROLL) {
+            // rows past beta repeat the last digit's (in-bounds) and are zeroed before the product
+            uint64_t kb[INNER_UNROLL], ka[INNER_UNROLL];
+#pragma unroll
+            for (uint32_t j = 0; j < INNER_UNROLL; j++) {
+                const uint32_t jj = min(j, beta - 1);
+                kb[j] = key_b(jj);
+                ka[j] = key_a(jj);
+            }
+            for (uint32_t b = 0; b < B; b++) {
+                uint64_t v[INNER_UNROLL];
+#pragma unroll
+                for (uint32_t j = 0; j < INNER_UNROLL; j++) v[j] = digit(b, min(j, beta - 1));
+                Split3 s0{0, 0, 0, 0}, s1{0, 0, 0, 0};
+#pragma unroll
+                for (uint32_t j = 0; j < INNER_UNROLL; j++) {
+                    const uint64_t x = j < beta ? v[j] : 0;  // at most 8 products: within the snorm-free bound
+                    const uint32_t vl = (uint32_t)(x & M30), vh = (uint32_t)(x >> 30);
+                    smac(s0, vl, vh, split30(kb[j]));
+                    smac(s1, vl, vh, split30(ka[j]));
+                }
+                acc[((b * 2 + 0) * el + e) * n + k] = sreduce60(s0, pc[gi]);
+                acc[((b * 2 + 1) * el + e) * n + k] = sreduce60(s1, pc[gi]);
+            }
+            continue;
+        }
+        for (uint32_t b = 0; b < B; b++) {
+            Split3 s0{0, 0, 0, 0}, s1{0, 0, 0, 0};
+            for (uint32_t j = 0; j < beta; j++) {
+                const uint64_t v = digit(b, j);
+                const uint32_t vl = (uint32_t)(v & M30), vh = (uint32_t)(v >> 30);
+                smac(s0, vl, vh, split30(key_b(j)));
+                smac(s1, vl, vh, split30(key_a(j)));
+                if ((j + 1) % SPLIT_CHUNK == 0) {  // more than 15 digits: keep the sums in bounds
+                    snorm(s0);
+                    snorm(s1);
+                    if ((j + 1) % (4 * SPLIT_CHUNK) == 0) {
+                        sreduce(s0, pc[gi]);
+                        sreduce(s1, pc[gi]);
+                    }
                 }
             }
+            // a2 stays below 2^64: sreduce runs at least every 60 digits
+            acc[((b * 2 + 0) * el + e) * n + k] = sreduce60(s0, pc[gi]);
+            acc[((b * 2 + 1) * el + e) * n + k] = sreduce60(s1, pc[gi]);
         }
-        // a2 stays below 2^64: sreduce runs at least every 60 digits
-        acc[((b * 2 + 0) * el + e) * n + k] = sreduce60(s0, pc[gi]);
-        acc[((b * 2 + 1) * el + e) * n + k] = sreduce60(s1, pc[gi]);
     }
 }
 
@@ -1394,11 +1434,10 @@ static int ks_inner(ckks_ctx *c, LevelTables *lt, int l, const uint64_t *d, size
     } else {  // generic n: one launch per step
         auto kern = st.seeded ? k_inner<true> : k_inner<false>;
         for (uint32_t j = 0; j < st.count; j++) {
-            const size_t total = (size_t)st.B * el * n;
             const size_t in_off = st.shared ? 0 : (size_t)j * st.B;
-            hipLaunchKernelGGL(kern, grid_for(total), dim3(256), 0, s, d + in_off * d_stride, d_stride,
+            hipLaunchKernelGGL(kern, grid_for((size_t)el * n), dim3(256), 0, s, d + in_off * d_stride, d_stride,
                                w.ext + in_off * beta * el * n, st.key[j], w.acc + (size_t)j * st.B * 2 * el * n,
-                               c->d_pc, n, (uint32_t)l, L, K, beta, c->alpha, st.g[j], st.root[j], total);
+                               c->d_pc, n, (uint32_t)l, L, K, beta, c->alpha, st.g[j], st.root[j], st.B);
         }
     }
     LAUNCH_CHECK();
