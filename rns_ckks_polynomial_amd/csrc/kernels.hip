@@ -682,12 +682,22 @@ __global__ __launch_bounds__(256) void k_inner2048(const uint64_t *__restrict__ 
     for (uint32_t j = 0; j < beta; j++) {
         const bool own = e >= j * alpha && e < min(l, (j + 1) * alpha);
         const uint64_t *src = own ? d + b * d_stride + (size_t)e * n : ext + ((b * beta + j) * el + e) * n;
-        uint64_t *lb = buf[j & 1];
-#pragma unroll
-        for (int m = 0; m < 8; m++) lb[t + 256 * m] = src[t + 256 * m];
-        __syncthreads();
         const uint64_t *kb = key + ((size_t)j * (SEEDED ? 1 : 2) * (L + K) + gi) * n;
         const uint64_t *ka = kb + (size_t)(L + K) * n;
+        // the key rows are requested with the digit row, before the barrier (which the
+        // compiler does not move loads across), so both arrive in one memory latency
+        uint64_t sv[8], kbv[8], kav[8];
+#pragma unroll
+        for (int m = 0; m < 8; m++) sv[m] = src[t + 256 * m];
+#pragma unroll
+        for (int m = 0; m < 8; m++) {
+            kbv[m] = kb[t + 256 * m];
+            if (!SEEDED) kav[m] = ka[t + 256 * m];
+        }
+        uint64_t *lb = buf[j & 1];
+#pragma unroll
+        for (int m = 0; m < 8; m++) lb[t + 256 * m] = sv[m];
+        __syncthreads();
         const uint64_t row = SEEDED ? sm_at(st.root[step], (uint64_t)j * (L + K) + gi) : 0;
         const uint64_t qa = pc[gi].q;
 #pragma unroll
@@ -695,8 +705,8 @@ __global__ __launch_bounds__(256) void k_inner2048(const uint64_t *__restrict__ 
             const uint32_t k = t + 256 * m;
             const uint64_t v = lb[galois_src(k, g, n)];
             const uint32_t vl = (uint32_t)(v & M30), vh = (uint32_t)(v >> 30);
-            smac(s0[m], vl, vh, split30(kb[k]));
-            smac(s1[m], vl, vh, split30(SEEDED ? seeded_a(row, k, qa) : ka[k]));
+            smac(s0[m], vl, vh, split30(kbv[m]));
+            smac(s1[m], vl, vh, split30(SEEDED ? seeded_a(row, k, qa) : kav[m]));
         }
         if ((j + 1) % SPLIT_CHUNK == 0) {  // more than 15 digits: keep the sums in bounds
 #pragma unroll
