@@ -1142,24 +1142,31 @@ __global__ __launch_bounds__(256) void k_final_giant2048(const uint64_t *__restr
     uint64_t v[8];
     const uint64_t *cv = conv + (size_t)blockIdx.x * n;
     const size_t cstride = (size_t)B * 2 * l * n;
+    // parts outer, coefficients inner: each part's 8 loads are in flight together; the
+    // accumulator parts and the output row are requested before the transform starts
 #pragma unroll
-    for (int m = 0; m < 8; m++) {
-        uint64_t x = cv[t + 256 * m];
-        for (uint32_t p = 1; p < nconv; p++) x = addm(x, cv[p * cstride + t + 256 * m], q);
-        v[m] = x;
-    }
-    n2048::fwd(v, lds, twf + (size_t)i * n * 2, q);
+    for (int m = 0; m < 8; m++) v[m] = cv[t + 256 * m];
+    for (uint32_t p = 1; p < nconv; p++)
+#pragma unroll
+        for (int m = 0; m < 8; m++) v[m] = addm(v[m], cv[p * cstride + t + 256 * m], q);
     const size_t pstride = (size_t)B * 2 * (l + K) * n;
     const uint64_t *ar = acc + ((b * 2 + c) * (l + K) + i) * n;
     uint64_t *o = out + (size_t)blockIdx.x * n;
+    uint64_t a[8], ov[8];
+#pragma unroll
+    for (int m = 0; m < 8; m++) {
+        a[m] = ar[t + 256 * m];
+        ov[m] = o[t + 256 * m];
+    }
+    for (uint32_t p = 1; p < nparts; p++)
+#pragma unroll
+        for (int m = 0; m < 8; m++) a[m] = addm(a[m], ar[p * pstride + t + 256 * m], q);
+    n2048::fwd(v, lds, twf + (size_t)i * n * 2, q);
     const uint64_t w = pinv[2 * i], wp = pinv[2 * i + 1];
 #pragma unroll
     for (int m = 0; m < 8; m++) {
-        const uint32_t k = t + 256 * m;
-        uint64_t a = ar[k];
-        for (uint32_t p = 1; p < nparts; p++) a = addm(a, ar[p * pstride + k], q);
         const uint64_t x = n2048::reduce8(v[m], q);
-        o[k] = addm(o[k], shoup(subm(a, x, q), w, wp, q), q);
+        o[t + 256 * m] = addm(ov[m], shoup(subm(a[m], x, q), w, wp, q), q);
     }
 }
 
