@@ -45,19 +45,19 @@ LIMB = N * 8
 # counters (profiles/bench_step_n2048_l112_b8_hbm_counters.md).  Valid only for
 # the kernel sources they were taken on (hash of rns_ckks_polynomial_amd/csrc).
 MEASURED_TRAFFIC = {
-    "source_sha": "b35b164e71e2719b",
+    "source_sha": "4129506c4849908b",
     "bytes_per_launch": {
-        "ks_modup_convert": 812993425,
-        "ks_moddown_convert": 750635204,
-        "bsgs_mac": 3758189791,
-        "ks_ntt_ext": 1335473098,
-        "ks_inner_product_sum": 2848554102,
-        "rotate_final": 3190246645,
-        "ntt_fwd": 62554458,
-        "ntt_inv": 62597334,
-        "giant_final": 297546375,
-        "ks_intt_modup": 326830530,
-        "ks_intt_moddown": 310297659
+        "ks_modup_convert": 813026646,
+        "ks_moddown_convert": 750632275,
+        "bsgs_mac": 3758174003,
+        "ks_ntt_ext": 1335808882,
+        "ks_inner_product_sum": 2848475688,
+        "rotate_final": 3190219943,
+        "ntt_fwd": 62570793,
+        "ntt_inv": 62597287,
+        "giant_final": 304260401,
+        "ks_intt_modup": 326816355,
+        "ks_intt_moddown": 310297314
     },
 }
 
