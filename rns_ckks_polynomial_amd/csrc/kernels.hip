@@ -778,6 +778,9 @@ __global__ __launch_bounds__(256) void k_inner_hoisted2048(const uint64_t *__res
     // rows are fetched again)
     const uint32_t T = (s1 - s0) * beta;
     Split3c a0[8], a1[8];
+    // byte offsets of sigma_g's sources in a digit row, computed once per step
+    // (at its first digit) and shared by its beta digits
+    uint32_t sidx[8];
     auto kload = [&](uint32_t it, uint64_t (&kbv)[8], uint64_t (&kav)[8]) {
         it = min(it, T - 1);
         const uint32_t step = s0 + it / beta, j = it % beta;
@@ -792,13 +795,17 @@ __global__ __launch_bounds__(256) void k_inner_hoisted2048(const uint64_t *__res
     auto pair = [&](uint32_t it, const uint64_t (&kbv)[8], const uint64_t (&kav)[8]) {
         const uint32_t step = s0 + it / beta, j = it % beta;
         if (j == 0) {
+            const uint32_t g = st.g[step];
 #pragma unroll
-            for (int m = 0; m < 8; m++) a0[m] = a1[m] = {0, 0, 0};
+            for (int m = 0; m < 8; m++) {
+                a0[m] = a1[m] = {0, 0, 0};
+                sidx[m] = galois_src(t + 256 * m, g, n) * 8;
+            }
         }
-        const uint32_t g = st.g[step];
+        const char *row = (const char *)(dig + j * n);
 #pragma unroll
         for (int m = 0; m < 8; m++) {
-            const uint64_t v = dig[j * n + galois_src(t + 256 * m, g, n)];
+            const uint64_t v = *(const uint64_t *)(row + sidx[m]);
             const uint32_t vl = (uint32_t)(v & M30), vh = (uint32_t)(v >> 30);
             smac(a0[m], vl, vh, split30(kbv[m]));
             smac(a1[m], vl, vh, split30(kav[m]));
