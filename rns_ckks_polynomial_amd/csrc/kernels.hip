@@ -447,7 +447,8 @@ __global__ __launch_bounds__(256, OCC) void k_convert_mfma(const BasisDev *__res
     // several chunks, so the rows are fetched and transposed once per 2 tiles)
     constexpr uint32_t TT = OCC == 3 ? 1 : 2;
     // H fragments of a tile: from LDS.  Staged: the workgroup's whole table,
-    // loaded once (a tile's fragments are read at its first chunk and kept).
+    // loaded once (the one-chunk variant reads a tile's fragments once, the
+    // two-wave variant at every chunk).
     // Otherwise the digit-table slice of each (pass, chunk), 2 tiles x 16
     // positions x 8 digits x 32 rows, goes through a double-buffered LDS slice
     // that the workgroup fills one step ahead (all its waves run the same steps).
@@ -458,31 +459,18 @@ __global__ __launch_bounds__(256, OCC) void k_convert_mfma(const BasisDev *__res
     // 32-deep ones).  The planes left over (a = s for even s <= 6, b = 7 for even s >= 8) take
     // one 16x16x32 each: 28 + 8 instructions per tile and chunk instead of 64, at the rate of
     // the 64-deep form.  HP's seven tuples overlap in content.  The staged two-wave variant
-    // (summed sets) keeps 64 32-deep products on 8 fragments: the tuples would push it into
-    // spills.
-    constexpr bool PAIRED = OCC == 3 || !STAGED;
-    constexpr int NH = PAIRED ? 7 : 4;  // 4-VGPR H registers per tile
+    // (summed sets) reads a tile's tuples from LDS again at every chunk rather than keeping both
+    // tiles' tuples for the whole pass, which keeps it within 256 VGPRs.
+    constexpr int NH = 7;  // 4-VGPR H registers per tile
     mf_v4i hb[TT][NH];
     auto load_h = [&](mf_v4i(&H)[NH], uint32_t tile, uint32_t buf) {
         const int8_t *h = STAGED ? sh_h + ((tile - tile0) * 16 + col) * MF_HSTRIDE + 8 * grp
                                  : sh_h + ((buf * 2 + (tile - tile0) % 2) * 16 + col) * MF_HSTRIDE + 8 * grp;
         auto pl = [&](int bb) -> long { return *(const long *)(h + 32 * bb); };
 #pragma unroll
-        for (int j = 0; j < NH; j++) {
-            const mf_v2l v = PAIRED ? mf_v2l{pl(7 - j), pl(6 - j)} : mf_v2l{pl(2 * j), pl(2 * j + 1)};
-            H[j] = __builtin_bit_cast(mf_v4i, v);
-        }
+        for (int j = 0; j < NH; j++) H[j] = __builtin_bit_cast(mf_v4i, mf_v2l{pl(7 - j), pl(6 - j)});
     };
     auto mac_tile = [&](mf_v4i(&ac)[15], const mf_v4i(&H)[NH]) {
-        if constexpr (!PAIRED) {
-#pragma unroll
-            for (int bb = 0; bb < 8; bb++)
-#pragma unroll
-                for (int aa = 0; aa < 8; aa++)
-                    ac[aa + bb] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
-                        plane_a(aa), __builtin_bit_cast(mf_v2l, H[bb / 2])[bb % 2], ac[aa + bb], 0, 0, 0);
-            return;
-        }
         auto hsing = [&](int bb) -> long {  // plane b inside HP: HP[7 - b] = {H_b, H_b-1}, HP[6] = {H_1, H_0}
             return bb > 0 ? __builtin_bit_cast(mf_v2l, H[7 - bb])[0] : __builtin_bit_cast(mf_v2l, H[6])[1];
         };
@@ -599,7 +587,7 @@ __global__ __launch_bounds__(256, OCC) void k_convert_mfma(const BasisDev *__res
 #pragma unroll
         for (uint32_t tt = 0; tt < TT; tt++) {
             if (t0 + tt >= tile_end) break;  // workgroup-uniform
-            if (!STAGED || ch == 0) load_h(hb[tt], t0 + tt, g & 1);
+            if (!STAGED || ch == 0 || OCC == 2) load_h(hb[tt], t0 + tt, g & 1);  // OCC 2: see NH
             mac_tile(acc[tt], hb[tt]);
         }
         if constexpr (!STAGED) {
