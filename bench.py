@@ -45,19 +45,19 @@ LIMB = N * 8
 # counters (profiles/bench_step_n2048_l112_b8_hbm_counters.md).  Valid only for
 # the kernel sources they were taken on (hash of rns_ckks_polynomial_amd/csrc).
 MEASURED_TRAFFIC = {
-    "source_sha": "9b372141a14fe457",
+    "source_sha": "fc9c0f6982dc83f3",
     "bytes_per_launch": {
-        "ks_modup_convert": 812988003,
-        "ks_moddown_convert": 750642724,
-        "bsgs_mac": 3758173175,
-        "ks_ntt_ext": 1335519918,
-        "ks_inner_product_sum": 2848568052,
-        "rotate_final": 3190274699,
-        "ntt_fwd": 62570801,
-        "ntt_inv": 62597294,
-        "giant_final": 304285078,
-        "ks_intt_modup": 326816687,
-        "ks_intt_moddown": 310297382
+        "ks_modup_convert": 813103915,
+        "ks_moddown_convert": 733192773,
+        "bsgs_mac": 3758184678,
+        "ks_ntt_ext": 1335773956,
+        "ks_inner_product_sum": 2848559395,
+        "rotate_final": 3190163070,
+        "ntt_fwd": 62570749,
+        "ntt_inv": 62597243,
+        "giant_final": 304299773,
+        "ks_intt_modup": 326816967,
+        "ks_intt_moddown": 310297189
     },
 }
 
