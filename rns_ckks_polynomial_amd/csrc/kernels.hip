@@ -350,6 +350,11 @@ __device__ __forceinline__ uint32_t conv_target(const ConvTargets &ct, uint32_t 
 typedef int mf_v4i __attribute__((ext_vector_type(4)));
 constexpr uint32_t MF_COEF = 64;  // coefficients per workgroup (4 waves x 16)
 constexpr uint32_t MF_TPB = 8;    // 16-position target tiles per workgroup
+// The one-chunk variant stages 7 tiles (112 target positions): its 40320 bytes of tables let
+// four workgroups share a CU's 160 KiB of LDS, matching its 128-VGPR budget of four waves per SIMD.
+constexpr uint32_t MF_TPB1 = 7;
+template <int OCC>
+constexpr uint32_t mf_tpb() { return OCC == 3 ? MF_TPB1 : MF_TPB; }
 
 // 4x4 byte transpose: o_b holds byte b of x0, x1, x2, x3 (in that order).
 __device__ __forceinline__ void bt4(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3, uint32_t &o0, uint32_t &o1,
@@ -364,25 +369,27 @@ __device__ __forceinline__ void bt4(uint32_t x0, uint32_t x1, uint32_t x2, uint3
 
 constexpr uint32_t MF_HSTRIDE = 272;  // LDS bytes per target position (8 digits x 32 rows + bank padding)
 
-// OCC: waves per SIMD the register budget is sized for (3 when the whole
-// contraction is one 32-row chunk, 2 otherwise).  STAGED: the basis rows fit
+// OCC selects the variant: 3 when the whole contraction is one 32-row chunk
+// (128 VGPRs and 7 staged tiles, so four waves per SIMD fit), 2 otherwise (two
+// waves per SIMD).  STAGED: the basis rows fit
 // one 32-row block (mk = 32), so the workgroup's digit table rows and
 // reduction constants are staged in LDS once; otherwise the fragments come
 // from the global table one chunk ahead of their use.
 template <int MODE, int OCC, bool STAGED>
-__global__ __launch_bounds__(256, OCC) void k_convert_mfma(const BasisDev *__restrict__ bases, SetLayout lay,
+__global__ __launch_bounds__(256, OCC == 3 ? 4 : OCC) void k_convert_mfma(const BasisDev *__restrict__ bases, SetLayout lay,
                                                           const uint64_t *__restrict__ y,
                                                           const uint32_t *__restrict__ u, ConvTargets ct,
                                                           uint64_t *__restrict__ out, uint32_t n) {
-    __shared__ __align__(16) int8_t sh_h[STAGED ? MF_TPB * 16 * MF_HSTRIDE : 2 * 2 * 16 * MF_HSTRIDE];
-    __shared__ uint64_t sh_rc[STAGED ? MF_TPB * 16 * MF_RC : 1];
+    constexpr uint32_t TPB = mf_tpb<OCC>();
+    __shared__ __align__(16) int8_t sh_h[STAGED ? TPB * 16 * MF_HSTRIDE : 2 * 2 * 16 * MF_HSTRIDE];
+    __shared__ uint64_t sh_rc[STAGED ? TPB * 16 * MF_RC : 1];
     const uint32_t s = blockIdx.z;
     const BasisDev &B = bases[lay.per_set_basis ? s % lay.inner : 0];
     const uint32_t m = B.m, lo = B.first, mk = B.mk;
     const uint32_t ntarget = MODE == 0 ? ct.l - m + ct.K : ct.l;
-    const uint32_t tile0 = blockIdx.y * MF_TPB;
+    const uint32_t tile0 = blockIdx.y * TPB;
     if (tile0 * 16 >= ntarget) return;
-    const uint32_t tile_end = min(tile0 + MF_TPB, (ntarget + 15) / 16), ntile = tile_end - tile0;
+    const uint32_t tile_end = min(tile0 + TPB, (ntarget + 15) / 16), ntile = tile_end - tile0;
     const uint32_t lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
     const uint32_t kb = blockIdx.x * MF_COEF + (threadIdx.x >> 6) * 16;
     const uint32_t part = ct.nsum > 1 ? s / ct.sum_stride : 0;
@@ -1372,8 +1379,9 @@ static void launch_convert(ckks_ctx *c, const BasisDev *bases, const SetLayout &
                            const uint32_t *u, const ConvTargets &ct, uint64_t *out, uint32_t maxt, uint32_t sets,
                            uint32_t mmax, hipStream_t s) {
     const uint32_t n = c->n;
-    const dim3 grid(n / MF_COEF, ((maxt + 15) / 16 + MF_TPB - 1) / MF_TPB, sets);
     // every basis of the launch has at most mmax rows: mk = 32 for all or none
+    const uint32_t tpb = mmax + 1 > 32 || ct.nsum > 1 ? mf_tpb<2>() : mf_tpb<3>();
+    const dim3 grid(n / MF_COEF, ((maxt + 15) / 16 + tpb - 1) / tpb, sets);
     if (mmax + 1 > 32)
         hipLaunchKernelGGL((k_convert_mfma<MODE, 2, false>), grid, dim3(256), 0, s, bases, lay, y, u, ct, out, n);
     else if (ct.nsum > 1)
