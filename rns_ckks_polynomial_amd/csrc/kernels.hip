@@ -280,9 +280,26 @@ __global__ void k_basis_u(const BasisDev *__restrict__ bases, SetLayout lay, uin
     const uint64_t M63 = (1ull << 63) - 1;
     uint64_t frac = 0;
     uint32_t ip = 0;
+    auto add = [&](uint64_t y, uint64_t r) {
+        frac += mulhi64(y << 4, r);
+        ip += (uint32_t)(frac >> 63);
+        frac &= M63;
+    };
+    if (m <= 32) {
+        // bases of up to 32 primes: every row is requested before the first is used
+        uint64_t yv[32];
+#pragma unroll
+        for (int a = 0; a < 32; a++) yv[a] = yb[(size_t)min((uint32_t)a, m - 1) * n];
+        // the empty asm takes every loaded value, so the loads cannot be sunk into the row guards
+#pragma unroll
+        for (int a = 0; a < 32; a++) asm volatile("" : "+v"(yv[a]));
+#pragma unroll
+        for (int a = 0; a < 32; a++)
+            if ((uint32_t)a < m) add(unsplit30(yv[a]), B.R[a]);
+    }
     // the sum is exact integer arithmetic, so inputs are taken 8 at a time
     // with all 8 loads in flight before the first is used
-    for (uint32_t i0 = 0; i0 < m; i0 += 8) {
+    for (uint32_t i0 = m <= 32 ? m : 0; i0 < m; i0 += 8) {
         uint64_t yv[8], rv[8];
 #pragma unroll
         for (int a = 0; a < 8; a++) {
@@ -291,13 +308,8 @@ __global__ void k_basis_u(const BasisDev *__restrict__ bases, SetLayout lay, uin
             rv[a] = B.R[i];
         }
 #pragma unroll
-        for (int a = 0; a < 8; a++) {
-            if (i0 + a < m) {
-                frac += mulhi64(yv[a] << 4, rv[a]);
-                ip += (uint32_t)(frac >> 63);
-                frac &= M63;
-            }
-        }
+        for (int a = 0; a < 8; a++)
+            if (i0 + a < m) add(yv[a], rv[a]);
     }
     uint64_t t = frac + (1ull << 62);
     uint32_t uu = ip + (uint32_t)(t >> 63);
