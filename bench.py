@@ -45,19 +45,19 @@ LIMB = N * 8
 # counters (profiles/bench_step_n2048_l112_b8_hbm_counters.md).  Valid only for
 # the kernel sources they were taken on (hash of rns_ckks_polynomial_amd/csrc).
 MEASURED_TRAFFIC = {
-    "source_sha": "a4a786bebf88b6f6",
+    "source_sha": "4f114efab59696aa",
     "bytes_per_launch": {
-        "ks_modup_convert": 812116491,
-        "ks_moddown_convert": 733192724,
-        "bsgs_mac": 3758201740,
-        "ks_ntt_ext": 1335528558,
-        "ks_inner_product_sum": 2848664604,
-        "rotate_final": 3190185342,
-        "ntt_fwd": 62570951,
-        "ntt_inv": 62597445,
-        "giant_final": 304329583,
-        "ks_intt_modup": 326817485,
-        "ks_intt_moddown": 310298174
+        "ks_modup_convert": 812080786,
+        "ks_moddown_convert": 733236013,
+        "bsgs_mac": 3758192646,
+        "ks_ntt_ext": 1335593752,
+        "ks_inner_product_sum": 2848518456,
+        "rotate_final": 3190134720,
+        "ntt_fwd": 62570852,
+        "ntt_inv": 62590179,
+        "giant_final": 304298430,
+        "ks_intt_modup": 326831241,
+        "ks_intt_moddown": 310288366
     },
 }
 
