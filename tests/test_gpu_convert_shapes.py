@@ -31,8 +31,11 @@ def _key(o, seed, j=0):
                              np.tile(o.primes, o.dnum * 2), o.n).reshape(o.dnum, 2, tot, o.n)
 
 
-# (L, K, dnum): digit width alpha = K = 31, 32, 33; levels with a full and a partial last digit
-@pytest.mark.parametrize("L,K,dnum,l", [(62, 31, 2, 62), (62, 31, 2, 40), (64, 32, 2, 64), (66, 33, 2, 50)])
+# (L, K, dnum): digit width alpha = K = 31, 32, 33; levels with a full and a partial last digit.
+# L = 150, K = 30: one-chunk digits with 150 targets, i.e. 10 target tiles, which the one-chunk
+# conversion covers with a full and a partial workgroup along the target axis.
+@pytest.mark.parametrize("L,K,dnum,l", [(62, 31, 2, 62), (62, 31, 2, 40), (64, 32, 2, 64), (66, 33, 2, 50),
+                                        (150, 30, 5, 150), (150, 30, 5, 131)])
 def test_keyswitch_conversion_shapes(L, K, dnum, l):
     P = (2048, L, K, dnum)
     g, o = gpu_ctx(*P), oracle_ctx(*P)
