@@ -42,6 +42,19 @@ def times_i(o, ct, l: int):
     return o.ntt(out)
 
 
+def conj_extract(o, em, w, cj, l1: int):
+    """Real and imaginary parts of the slots of w (conj = cj, both at level l1):
+    re = (w + cj) / 2 and im = (w - cj) X^(n/2) (-1/2), each a constant multiply
+    at the prime the following rescale drops, then that rescale (level l1 - 1)."""
+    W, Cj = _Ct(w, l1, 0.0), _Ct(cj, l1, 0.0)
+    re2 = em.lincomb(l1, W, 1, Cj, 1)
+    im2 = times_i(o, em.lincomb(l1, W, 1, Cj, -1), l1)
+    qd = float(o.primes[l1 - 1])
+    re = o.rescale(em.lincomb(l1, _Ct(re2, l1, 0.0), const_int(0.5, qd)), l1)
+    im = o.rescale(em.lincomb(l1, _Ct(im2, l1, 0.0), const_int(-0.5, qd)), l1)
+    return re, im
+
+
 def bootstrap(o, ct, l0: int, lt: int, cts_pt, stc_pt, bs: int, gs: int, baby, giant, conj_key, rlk,
               evalmod_scale: float, cheb, bound_k: float, double_angles: int, out_factor: float):
     """One ciphertext [2][l0][n] -> (out [2][l_out][n], l_out, scale entering slot_to_coeff)."""
@@ -50,12 +63,7 @@ def bootstrap(o, ct, l0: int, lt: int, cts_pt, stc_pt, bs: int, gs: int, baby, g
     w = o.bsgs(r, cts_pt, bs, gs, baby, giant, lt, do_rescale=True)              # level lt - 1
     l1 = lt - 1
     cj = o.rotate(w, 2 * o.n - 1, conj_key, l1)
-    W, Cj = _Ct(w, l1, 0.0), _Ct(cj, l1, 0.0)
-    re2 = em.lincomb(l1, W, 1, Cj, 1)
-    im2 = times_i(o, em.lincomb(l1, W, 1, Cj, -1), l1)
-    qd = float(o.primes[l1 - 1])
-    re = o.rescale(em.lincomb(l1, _Ct(re2, l1, 0.0), const_int(0.5, qd)), l1)
-    im = o.rescale(em.lincomb(l1, _Ct(im2, l1, 0.0), const_int(-0.5, qd)), l1)
+    re, im = conj_extract(o, em, w, cj, l1)
     l2 = l1 - 1
     re_o, l3, s3 = em.eval_mod(re, l2, evalmod_scale, cheb, bound_k, double_angles, out_factor)
     im_o, _, _ = em.eval_mod(im, l2, evalmod_scale, cheb, bound_k, double_angles, out_factor)

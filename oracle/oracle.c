@@ -524,6 +524,33 @@ void or_bsgs(const or_params *pp, uint32_t l, const uint64_t *in, const uint64_t
     free(rot); free(acc); free(inner); free(tmp);
 }
 
+/* The two element-wise steps of the BSGS sum above, as separate calls (a
+ * caller that streams diagonals and keys composes the same sum from them):
+ * acc[c][i][k] += pt[i][k] ct[c][i][k] mod q_i for both polynomials c, and
+ * out = a + b mod q_i over [count][l][n] arrays. */
+void or_mul_acc(const or_params *pp, uint32_t l, const uint64_t *pt, const uint64_t *ct, uint64_t *acc) {
+    const uint32_t n = pp->n;
+    const size_t ln = (size_t)l * n;
+#pragma omp parallel for schedule(static)
+    for (uint32_t i = 0; i < l; i++)
+        for (uint32_t c = 0; c < 2; c++)
+            for (uint32_t k = 0; k < n; k++) {
+                size_t o = (size_t)i * n + k;
+                acc[c * ln + o] = addmod(acc[c * ln + o], or_mulmod(pt[o], ct[c * ln + o], pp->primes[i]),
+                                         pp->primes[i]);
+            }
+}
+
+void or_add(const or_params *pp, uint32_t l, uint32_t count, const uint64_t *a, const uint64_t *b, uint64_t *out) {
+    const uint32_t n = pp->n;
+#pragma omp parallel for schedule(static)
+    for (uint32_t r = 0; r < count * l; r++)
+        for (uint32_t k = 0; k < n; k++) {
+            size_t o = (size_t)r * n + k;
+            out[o] = addmod(a[o], b[o], pp->primes[r % l]);
+        }
+}
+
 /* ======================================================================
  * Encoding, keys, encryption (used by the functional checks only)
  * ====================================================================== */

@@ -105,6 +105,11 @@ void or_bsgs(const or_params *pp, uint32_t l, const uint64_t *in, const uint64_t
              uint32_t Bs, uint32_t G, const uint64_t *const *baby_keys,
              const uint64_t *const *giant_keys, int do_rescale, uint64_t *out);
 
+/* The element-wise steps of or_bsgs: acc[c] += pt (.) ct[c] (c = 0, 1; pt
+ * [l][n], ct and acc [2][l][n]), and out = a + b over [count][l][n]. */
+void or_mul_acc(const or_params *pp, uint32_t l, const uint64_t *pt, const uint64_t *ct, uint64_t *acc);
+void or_add(const or_params *pp, uint32_t l, uint32_t count, const uint64_t *a, const uint64_t *b, uint64_t *out);
+
 /* ---------- encoding / keys / encryption (functional checks only) ---------- */
 /* Integer coefficients of the encoding of z (slots = n/2) at scale delta,
  * rounded half away from zero.  z_re/z_im: [n/2]. */

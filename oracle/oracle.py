@@ -71,6 +71,8 @@ def lib():
             "or_rotate": (None, [C.POINTER(Params), u32, u64, U64P, U64P, U64P]),
             "or_bsgs": (None, [C.POINTER(Params), u32, U64P, U64P, u32, u32, C.POINTER(U64P),
                                C.POINTER(U64P), C.c_int, U64P]),
+            "or_mul_acc": (None, [C.POINTER(Params), u32, U64P, U64P, U64P]),
+            "or_add": (None, [C.POINTER(Params), u32, u32, U64P, U64P, U64P]),
             "or_encode_coeffs": (None, [u32, F64P, F64P, C.c_double, I64P]),
             "or_coeffs_to_ntt": (None, [C.POINTER(Params), u32, U32P, I64P, U64P]),
             "or_decode": (None, [C.POINTER(Params), u32, U64P, C.c_double, F64P, F64P]),
@@ -215,6 +217,18 @@ class Ctx:
         out = np.zeros((2, lo, self.n), dtype=np.uint64)
         lib().or_bsgs(self.ref, l, _p(ct), _p(pt), Bs, G, bk, gk, int(do_rescale), _p(out))
         return out
+
+    def mul_acc(self, pt, ct, acc, l):
+        """acc[c] += pt (.) ct[c] for both polynomials, in place (acc: contiguous uint64 [2][l][n])."""
+        pt = _u64(pt); ct = _u64(ct)
+        assert acc.dtype == np.uint64 and acc.flags["C_CONTIGUOUS"]
+        lib().or_mul_acc(self.ref, l, _p(pt), _p(ct), _p(acc))
+        return acc
+
+    def add(self, a, b, l):
+        """a + b limb by limb over [..][l][n] arrays."""
+        a = _u64(a); b = _u64(b); out = np.zeros_like(a)
+        lib().or_add(self.ref, l, a.size // (l * self.n), _p(a), _p(b), _p(out)); return out
 
     # ---- functional helpers
     def encode_coeffs(self, z, delta):

@@ -67,41 +67,12 @@ def words(seed: int, tag: int, j, count: int) -> np.ndarray:
     return splitmix(k[..., None], idx)
 
 
-TAG_KEY_SEEDED = 10  # a rows of seed-expanded switching keys
-
-
-def mulhi_mod(w, q) -> np.ndarray:
-    """floor(w q / 2^64) for 64-bit words w and moduli q < 2^64: a residue in [0, q)."""
-    w = np.asarray(w, dtype=np.uint64)
-    q = np.asarray(q, dtype=np.uint64)
-    lo32 = np.uint64(0xFFFFFFFF)
-    s32 = np.uint64(32)
-    wl, wh, ql, qh = w & lo32, w >> s32, q & lo32, q >> s32
-    with np.errstate(over="ignore"):
-        m1 = wh * ql + ((wl * ql) >> s32)
-        m2 = wl * qh + (m1 & lo32)
-        return wh * qh + (m1 >> s32) + (m2 >> s32)
-
-
-def seeded_key_a(seed: int, dnum: int, moduli, n: int) -> np.ndarray:
-    """The a rows [dnum][len(moduli)][n] of a seed-expanded switching key:
-    residue k of row (j, i) is floor(w q_i / 2^64) with w word k of stream
-    j * len(moduli) + i under TAG_KEY_SEEDED (moduli = all L + K key primes)."""
-    moduli = np.asarray(moduli, dtype=np.uint64)
-    tot = len(moduli)
-    w = words(seed, TAG_KEY_SEEDED, np.arange(dnum * tot, dtype=np.uint64), n).reshape(dnum, tot, n)
-    return mulhi_mod(w, moduli[None, :, None])
-
-
-def uniform_mod(seed: int, tag: int, stream_ids, moduli, n: int) -> np.ndarray:
-    """Uniform residues: out[r, i] in [0, moduli[r]) for stream stream_ids[r]."""
-    stream_ids = np.atleast_1d(np.asarray(stream_ids, dtype=np.uint64))
-    q = np.broadcast_to(np.atleast_1d(np.asarray(moduli, dtype=np.uint64))[:, None], (len(stream_ids), n))
+def _uniform_rows(seed: int, tag: int, stream_ids: np.ndarray, q: np.ndarray, n: int) -> np.ndarray:
     base = words(seed, tag, stream_ids, n).ravel()  # [r * n]
-    q = q.ravel()
+    q = np.broadcast_to(q[:, None], (len(stream_ids), n)).ravel()
     out = np.empty_like(base)
     pending = np.arange(base.size)
-    v = None
+    v = take = None
     for r in range(MAX_TRIES):
         v = splitmix(base[pending], np.uint64(r)) & MASK60
         take = v < q[pending]
@@ -111,6 +82,32 @@ def uniform_mod(seed: int, tag: int, stream_ids, moduli, n: int) -> np.ndarray:
             return out.reshape(len(stream_ids), n)
     out[pending] = v[~take] % q[pending]
     return out.reshape(len(stream_ids), n)
+
+
+ROWS_PER_TASK = 64  # large draws are split into row blocks drawn on a thread pool
+
+
+def uniform_mod(seed: int, tag: int, stream_ids, moduli, n: int) -> np.ndarray:
+    """Uniform residues: out[r, i] in [0, moduli[r]) for stream stream_ids[r].
+    Every element depends only on (seed, tag, stream, i), so drawing row blocks
+    on several threads (numpy releases the interpreter lock inside its loops)
+    gives the same array."""
+    stream_ids = np.atleast_1d(np.asarray(stream_ids, dtype=np.uint64))
+    q = np.broadcast_to(np.atleast_1d(np.asarray(moduli, dtype=np.uint64)), (len(stream_ids),))
+    rows = len(stream_ids)
+    if rows * n <= ROWS_PER_TASK * 2048:
+        return _uniform_rows(seed, tag, stream_ids, q, n)
+    import concurrent.futures as cf
+    import os
+    out = np.empty((rows, n), dtype=np.uint64)
+
+    def block(r0):
+        r1 = min(rows, r0 + ROWS_PER_TASK)
+        out[r0:r1] = _uniform_rows(seed, tag, stream_ids[r0:r1], q[r0:r1], n)
+
+    with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(block, range(0, rows, ROWS_PER_TASK)))
+    return out
 
 
 def ternary(seed: int, tag: int, j: int, n: int) -> np.ndarray:

@@ -8,6 +8,7 @@ from __future__ import annotations
 import numpy as np
 
 import oracle
+from oracle import seeded_keys
 from rns_ckks_polynomial_amd import synth
 
 
@@ -65,7 +66,7 @@ class Keys:
     def seeded_galois_key(self, g: int, key_seed: int):
         """A Galois key whose a rows are the seed-expanded ones: (b rows, full key)."""
         ctx = self.ctx
-        a = synth.seeded_key_a(key_seed, ctx.dnum, ctx.primes, ctx.n)
+        a = seeded_keys.seeded_key_a(key_seed, ctx.dnum, ctx.primes, ctx.n)
         key = self.swk(ctx.automorph(self.s_ntt, g, ctx.L + ctx.K), a=a)
         return np.ascontiguousarray(key[:, 0]), key
 

@@ -6,7 +6,7 @@ planted copy).  The Python stages of the oracle (EvalMod, bootstrapping) are
 mutated in a copy of the oracle package and the tests, and their pins run
 there.  Every mutant must make at least one pin fail.
 
-    python tests/oracle_mutants.py
+    python tests/oracle_mutants.py [mutant names...]
 """
 import os
 import shutil
@@ -36,10 +36,19 @@ MUTANTS = {
     "encode_sign": ("uint64_t a = (m - (e[j] * i) % m) % m;", "uint64_t a = (e[j] * i) % m;"),
 }
 
-# (file under oracle/, text, replacement, pin file).  Not listed: which prime a
-# constant is encoded against (neighbouring chain primes differ by less than
-# 2^-45 relative, so the refresh stays correct); GPU parity fixes that rule.
+# (file under oracle/, text, replacement, pin file).  The prime a constant is
+# encoded against and the scale update are invisible to decryption (chain
+# primes lie within 2^-45 of each other and 2^-40 of 2^59); the big-integer
+# pins of test_oracle_evalmod_exact.py catch them.
 PY_MUTANTS = {
+    "em_const_prime_below": ("evalmod.py", "w = const_int(c, float(self._q(a.l - 1)))",
+                             "w = const_int(c, float(self._q(a.l - 2)))", "test_oracle_evalmod_exact.py"),
+    "em_scale_2_59": ("evalmod.py", "(a.s * b.s) / float(self._q(m - 1))", "(a.s * b.s) / 2.0 ** 59",
+                      "test_oracle_evalmod_exact.py"),
+    "em_sum_prime_below": ("evalmod.py", "wq = float(self._q(m - 1))", "wq = float(self._q(m - 2))",
+                           "test_oracle_evalmod_exact.py"),
+    "boot_half_prime_below": ("bootstrap.py", "qd = float(o.primes[l1 - 1])", "qd = float(o.primes[l1 - 2])",
+                              "test_oracle_evalmod_exact.py"),
     "em_odd_recurrence": ("evalmod.py", "self.lincomb(p.l, p, 2, T[1], -1)", "self.lincomb(p.l, p, 2, T[1], 0)",
                           "test_oracle_evalmod.py"),
     "em_even_constant": ("evalmod.py", "self.lincomb(p.l, p, 2, add=const_int(-1.0, p.s))",
@@ -73,10 +82,12 @@ PY_MUTANTS = {
 }
 
 
-def py_mutants(tmp):
+def py_mutants(tmp, only=()):
     """Each Python mutant in a copy of oracle/, tests/ and the input generator."""
     failures = 0
     for name, (fname, a, b, pins) in PY_MUTANTS.items():
+        if only and name not in only:
+            continue
         root = os.path.join(tmp, "py_" + name)
         shutil.copytree(os.path.join(ROOT, "oracle"), os.path.join(root, "oracle"),
                         ignore=shutil.ignore_patterns("__pycache__"))
@@ -102,11 +113,14 @@ def py_mutants(tmp):
 
 
 def main():
+    only = set(sys.argv[1:])  # optional subset of mutant names
     src = open(SRC).read()
     failures = 0
     with tempfile.TemporaryDirectory() as tmp:
-        failures += py_mutants(tmp)
+        failures += py_mutants(tmp, only)
         for name, (a, b) in MUTANTS.items():
+            if only and name not in only:
+                continue
             assert a in src, name
             c = os.path.join(tmp, name + ".c")
             so = os.path.join(tmp, name + ".so")

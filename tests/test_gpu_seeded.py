@@ -1,6 +1,6 @@
 """GPU seed-expanded switching keys (ckks_key_expand, ckks_rotate_seeded,
 ckks_mul_tensor_relin_seeded): the expanded a rows equal the input generator's
-(synth.seeded_key_a) bit for bit, and a seeded key switch equals the oracle's
+(oracle seeded_keys.seeded_key_a) bit for bit, and a seeded key switch equals the oracle's
 key switch with the expanded key on every residue, at n = 2048 (LDS inner
 product) and n = 65536 (generic inner product), plus a decrypt check with a
 real seeded Galois key."""
@@ -9,6 +9,7 @@ import pytest
 
 from ckks_helpers import Keys, galois_rot, rel_err
 from gpu_util import dev, gpu_ctx, host, mismatch, oracle_ctx, require_gpu, say
+from oracle import seeded_keys
 from rns_ckks_polynomial_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -28,7 +29,7 @@ def _key_b(o, seed):
 
 
 def _full(o, kb, key_seed):
-    return np.ascontiguousarray(np.stack([kb, synth.seeded_key_a(key_seed, o.dnum, o.primes, o.n)], axis=1))
+    return np.ascontiguousarray(np.stack([kb, seeded_keys.seeded_key_a(key_seed, o.dnum, o.primes, o.n)], axis=1))
 
 
 def _cts(o, seed, B, l):

@@ -174,20 +174,20 @@ def test_rescale_rounds_to_nearest():
         assert exp % Q1 == pyref.crt([int(out[0, k]), int(out[1, k])], [ctx.q(0), ctx.q(1)])[0]
 
 
-def test_bsgs_bruteforce_n16(tiny):
-    ctx, l, Bs, G = tiny, 3, 2, 4
+def _bsgs_case(ctx, seed, l, Bs, G):
+    """Two ciphertexts, G x Bs diagonals and seeded keys, with the BSGS result
+    recomputed on integer polynomials (no RNS): [expected [2][l-1][n] residues]."""
     n, tot = ctx.n, ctx.L + ctx.K
-    ct = np.stack([rand_ntt(ctx, 26, 0, list(range(l))), rand_ntt(ctx, 26, 10, list(range(l)))])
-    pt = synth.uniform_mod(26, synth.TAG_DIAG, np.arange(G * Bs * l), np.tile(ctx.primes[:l], G * Bs),
+    cts = [np.stack([rand_ntt(ctx, seed + t, 0, list(range(l))), rand_ntt(ctx, seed + t, 10, list(range(l)))])
+           for t in range(2)]
+    pt = synth.uniform_mod(seed, synth.TAG_DIAG, np.arange(G * Bs * l), np.tile(ctx.primes[:l], G * Bs),
                            n).reshape(G, Bs, l, n)
 
     def key(i):
-        return synth.uniform_mod(26, synth.TAG_KEY, np.arange(ctx.dnum * 2 * tot) + 100 * i,
+        return synth.uniform_mod(seed, synth.TAG_KEY, np.arange(ctx.dnum * 2 * tot) + 100 * i,
                                  np.tile(ctx.primes, ctx.dnum * 2), n).reshape(ctx.dnum, 2, tot, n)
     baby = [None] + [key(b) for b in range(1, Bs)]
     giant = [None] + [key(10 + g) for g in range(1, G)]
-    got = ctx.bsgs(ct, pt, Bs, G, baby, giant, l, do_rescale=True)
-
     Q = prod(ctx.q(i) for i in range(l))
 
     def rot_int(c0, c1, g, k):
@@ -195,23 +195,65 @@ def test_bsgs_bruteforce_n16(tiny):
         ks = py_keyswitch(ctx, [v % Q for v in a1], k, l)
         return [(x + y) % Q for x, y in zip(a0, ks[0])], ks[1]
 
-    x0, x1 = to_int_poly(ctx, ct[0], range(l)), to_int_poly(ctx, ct[1], range(l))
-    rots = [(x0, x1)] + [rot_int(x0, x1, galois_rot(n, b), baby[b]) for b in range(1, Bs)]
-    acc = [[0] * n, [0] * n]
-    for g in range(G):
-        inner = [[0] * n, [0] * n]
-        for b in range(Bs):
-            p = to_int_poly(ctx, pt[g, b], range(l))
-            for c in range(2):
-                inner[c] = [(u + v) % Q for u, v in zip(inner[c], pyref.negacyclic_int(p, rots[b][c]))]
-        if g:
-            inner = list(rot_int(inner[0], inner[1], galois_rot(n, g * Bs), giant[g]))
-        acc = [[(u + v) % Q for u, v in zip(acc[c], inner[c])] for c in range(2)]
-    ql = ctx.q(l - 1)
-    Q1 = Q // ql
-    for c in range(2):
-        ref = [((v - pyref.centered(v % ql, ql)) // ql) % Q1 for v in acc[c]]
-        assert np.array_equal(got[c], to_ntt(ctx, ref, range(l - 1)))
+    expected = []
+    for ct in cts:
+        x0, x1 = to_int_poly(ctx, ct[0], range(l)), to_int_poly(ctx, ct[1], range(l))
+        rots = [(x0, x1)] + [rot_int(x0, x1, galois_rot(n, b), baby[b]) for b in range(1, Bs)]
+        acc = [[0] * n, [0] * n]
+        for g in range(G):
+            inner = [[0] * n, [0] * n]
+            for b in range(Bs):
+                p = to_int_poly(ctx, pt[g, b], range(l))
+                for c in range(2):
+                    inner[c] = [(u + v) % Q for u, v in zip(inner[c], pyref.negacyclic_int(p, rots[b][c]))]
+            if g:
+                inner = list(rot_int(inner[0], inner[1], galois_rot(n, g * Bs), giant[g]))
+            acc = [[(u + v) % Q for u, v in zip(acc[c], inner[c])] for c in range(2)]
+        ql = ctx.q(l - 1)
+        Q1 = Q // ql
+        expected.append(np.stack([to_ntt(ctx, [((v - pyref.centered(v % ql, ql)) // ql) % Q1 for v in acc[c]],
+                                         range(l - 1)) for c in range(2)]))
+    return cts, pt, baby, giant, expected
+
+
+def test_bsgs_bruteforce_n16(tiny):
+    ctx, l, Bs, G = tiny, 3, 2, 4
+    cts, pt, baby, giant, expected = _bsgs_case(ctx, 26, l, Bs, G)
+    for ct, exp in zip(cts, expected):
+        assert np.array_equal(ctx.bsgs(ct, pt, Bs, G, baby, giant, l, do_rescale=True), exp)
+
+
+def test_bsgs_stream_bruteforce_n16(tiny):
+    """The streamed BSGS (diagonals and keys handed over one at a time, sums by
+    or_mul_acc / or_add) gives the brute-force residues for every ciphertext."""
+    from oracle.bsgs_stream import bsgs_stream
+    ctx, l, Bs, G = tiny, 3, 3, 3
+    cts, pt, baby, giant, expected = _bsgs_case(ctx, 27, l, Bs, G)
+    got = bsgs_stream(ctx, cts, l, Bs, G, lambda g, b: pt[g, b], lambda b: baby[b], lambda g: giant[g])
+    for t in range(2):
+        assert np.array_equal(got[t], expected[t])
+
+
+def test_negation_is_exact(small):
+    """Centered rounding is odd (every modulus is odd, so no value sits on a
+    tie): rotation, rescale and the BSGS transform of -x are exactly -(result
+    of x), residue by residue."""
+    from oracle.bsgs_stream import bsgs_stream
+    ctx, _ = small
+    l, n, tot, Bs, G = 6, ctx.n, ctx.L + ctx.K, 2, 2
+    mods = ctx.primes[:l].astype(np.uint64)[None, :, None]
+    neg = lambda x: np.where(x == 0, x, mods - x)  # noqa: E731
+    x = np.stack([rand_ntt(ctx, 28, 0, list(range(l))), rand_ntt(ctx, 28, 10, list(range(l)))])
+    key = synth.uniform_mod(28, synth.TAG_KEY, np.arange(ctx.dnum * 2 * tot), np.tile(ctx.primes, ctx.dnum * 2),
+                            n).reshape(ctx.dnum, 2, tot, n)
+    pt = synth.uniform_mod(28, synth.TAG_DIAG, np.arange(G * Bs * l), np.tile(ctx.primes[:l], G * Bs),
+                           n).reshape(G, Bs, l, n)
+    r = ctx.rotate(x, galois_rot(n, 3), key, l)
+    assert np.array_equal(ctx.rotate(neg(x), galois_rot(n, 3), key, l), neg(r))
+    s = ctx.rescale(x, l)
+    assert np.array_equal(ctx.rescale(neg(x), l), np.where(s == 0, s, mods[:, :l - 1] - s))
+    y, yn = bsgs_stream(ctx, [x, neg(x)], l, Bs, G, lambda g, b: pt[g, b], lambda b: key, lambda g: key)
+    assert np.array_equal(yn, np.where(y == 0, y, mods[:, :l - 1] - y))
 
 
 # ----------------------------------------------------------------- functional

@@ -1,8 +1,10 @@
 """Pins of the seeded input generator (rns_ckks_polynomial_amd/synth.py): its
-SplitMix64 against the generator's published outputs, and the mapping of
-seed-expanded key residues, floor(w q / 2^64), against exact integers."""
+SplitMix64 against the generator's published outputs, and its threaded draw
+against the single-block one.  Pins of the oracle's seed-expanded key rows
+(oracle/seeded_keys.py): the mapping floor(w q / 2^64) against exact integers."""
 import numpy as np
 
+from oracle import seeded_keys
 from rns_ckks_polynomial_amd import synth
 
 
@@ -18,7 +20,7 @@ def test_mulhi_mod_is_the_exact_high_product():
     q = rng.integers(2 ** 59, 2 ** 60, 4096, dtype=np.uint64)
     w[:3] = [2 ** 64 - 1, 0, 2 ** 63]
     q[:3] = [2 ** 60 - 1, 2 ** 59 + 1, 2 ** 64 - 1]
-    got = synth.mulhi_mod(w, q)
+    got = seeded_keys.mulhi_mod(w, q)
     ref = [(int(a) * int(b)) >> 64 for a, b in zip(w, q)]
     assert [int(v) for v in got] == ref
     assert all(int(v) < int(b) for v, b in zip(got, q))
@@ -28,10 +30,18 @@ def test_seeded_key_rows_follow_their_streams():
     """Row (j, i) is stream j (L + K) + i of the TAG_KEY_SEEDED generator, mapped
     by the high product; values are uniform over [0, q_i)."""
     moduli = np.array([(1 << 59) + 4097 + 4096 * t for t in range(5)], dtype=np.uint64)
-    a = synth.seeded_key_a(0x5EED, 3, moduli, 64)
+    a = seeded_keys.seeded_key_a(0x5EED, 3, moduli, 64)
     assert a.shape == (3, 5, 64)
     for (j, i, k) in [(0, 0, 0), (2, 4, 63), (1, 3, 17)]:
-        w = int(synth.words(0x5EED, synth.TAG_KEY_SEEDED, np.array([j * 5 + i], dtype=np.uint64), 64)[0, k])
+        w = int(synth.words(0x5EED, seeded_keys.TAG_KEY_SEEDED, np.array([j * 5 + i], dtype=np.uint64), 64)[0, k])
         assert int(a[j, i, k]) == (w * int(moduli[i])) >> 64
-    big = synth.seeded_key_a(3, 1, moduli[:1], 1 << 14)[0, 0].astype(np.float64) / float(moduli[0])
+    big = seeded_keys.seeded_key_a(3, 1, moduli[:1], 1 << 14)[0, 0].astype(np.float64) / float(moduli[0])
     assert abs(big.mean() - 0.5) < 0.02 and big.min() >= 0 and big.max() < 1
+
+
+def test_threaded_draw_equals_one_block():
+    moduli = np.array([(1 << 59) + 4097 + 4096 * t for t in range(200)], dtype=np.uint64)
+    ids = np.arange(200, dtype=np.uint64) + 7
+    a = synth.uniform_mod(0xC0DE, synth.TAG_KEY, ids, moduli, 2048)
+    b = synth._uniform_rows(0xC0DE, synth.TAG_KEY, ids, moduli, 2048)
+    assert np.array_equal(a, b) and bool((a < moduli[:, None]).all())
