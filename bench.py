@@ -80,13 +80,15 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--profile-steps", type=int, default=1)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    p.add_argument("--cpu-seconds", type=float, default=8.0, help="budget of the oracle's key-switch sample")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     p.add_argument("--boot-chain2100", action="store_true",
                    help="only time the bootstrap of 8 ciphertexts on the 2100 + 263 prime chain "
                         "(19 -> 2100 -> 2083 primes; about 160 GB of HBM)")
     p.add_argument("--boot-reps", type=int, default=2)
+    p.add_argument("--no-c4", action="store_true",
+                   help="skip the 2100-prime coeff_to_slot / slot_to_coeff leg (about 150 GB of HBM)")
     p.add_argument("--step-only", action="store_true",
                    help="skip the EvalMod, bootstrapping, seeded-key, ring-65536, NTT-sweep and pointwise legs "
                         "(profiler runs of the step)")
@@ -134,6 +136,54 @@ def cpu_baseline_one_core(budget_s: float):
     d["cores"] = 1
     d["sample"] = d["sample"].replace("OpenMP over limbs/coefficients", "one OpenMP thread")
     return d
+
+
+def cpu_baseline_units(skip_c4: bool = False):
+    """The oracle as it stands on this host, in the GPU's other units (one sample each):
+    limb-NTTs/s (its textbook O(n log n) NTT, one limb per call from Python, one
+    thread), BSGS 32 x 32 linear transforms/s at 112 primes (one ciphertext; its
+    key switches use OpenMP, its multiply-accumulate one thread), and one key
+    switch at 2100 primes (the bootstrap chain: ciphertext 0 of its coeff_to_slot)."""
+    import numpy as np
+
+    import oracle
+    from rns_ckks_polynomial_amd import synth
+    threads = int(os.environ.get("OMP_NUM_THREADS", 0)) or os.cpu_count() or 1
+    o = oracle.Ctx(N, L, K, DNUM)
+    res = {}
+    x = synth.uniform_mod(11, synth.TAG_POLY, np.arange(2 * L), np.tile(o.primes[:L], 2), N).reshape(2, L, N)
+    t0 = time.perf_counter()
+    o.ntt(x)
+    el = time.perf_counter() - t0
+    res["limb_ntt"] = {"value": 2 * L / el, "unit": "limb-NTTs/s", "cores": 1,
+                       "sample": f"{2 * L} forward limb-NTTs at n={N}, {el:.2f} s"}
+    tot = L + K
+    ct = synth.uniform_mod(12, synth.TAG_CT, np.arange(2 * L), np.tile(o.primes[:L], 2), N).reshape(2, L, N)
+    pt = synth.uniform_mod(13, synth.TAG_DIAG, np.arange(GS * BS * L), np.tile(o.primes[:L], GS * BS),
+                           N).reshape(GS, BS, L, N)
+    keys = synth.uniform_mod(14, synth.TAG_KEY, np.arange((BS + GS - 2) * DNUM * 2 * tot),
+                             np.tile(o.primes, (BS + GS - 2) * DNUM * 2), N).reshape(BS + GS - 2, DNUM, 2, tot, N)
+    t0 = time.perf_counter()
+    o.bsgs(ct, pt, BS, GS, [None] + [keys[b - 1] for b in range(1, BS)],
+           [None] + [keys[BS - 2 + j] for j in range(1, GS)], L, do_rescale=True)
+    el = time.perf_counter() - t0
+    res["linear_transform_c3"] = {"value": 1 / el, "unit": "linear-transforms/s", "cores": threads,
+                                  "sample": f"one BSGS {BS}x{GS} + rescale of one ciphertext at {L} primes "
+                                            f"({BS + GS - 2} key switches), {el:.1f} s"}
+    del pt, keys
+    if not skip_c4:
+        l4, t4 = C4_L, C4_L + C4_K
+        o4 = oracle.Ctx(C4_N, C4_L, C4_K, C4_DNUM)
+        d = synth.uniform_mod(15, synth.TAG_CT, np.arange(l4), o4.primes[:l4], C4_N)
+        k4 = synth.uniform_mod(16, synth.TAG_KEY, np.arange(C4_DNUM * 2 * t4), np.tile(o4.primes, C4_DNUM * 2),
+                               C4_N).reshape(C4_DNUM, 2, t4, C4_N)
+        t0 = time.perf_counter()
+        o4.keyswitch(d, k4, l4)
+        el = time.perf_counter() - t0
+        res["key_switch_c4"] = {"value": 1 / el, "unit": "key-switches/s", "cores": threads,
+                                "sample": f"one key switch at {l4} + {C4_K} primes, dnum {C4_DNUM} (ciphertext 0 of "
+                                          f"a coeff_to_slot step), {el:.1f} s"}
+    return res
 
 
 EM_DEGREE, EM_ANGLES, EM_K = 31, 3, 8.0
@@ -214,6 +264,8 @@ def boot_chain2100(args):
     g = Context(n, l, k, dnum, device=0)
     u64, dev = torch.uint64, "cuda:0"
     l3 = boot_stc_level(l)
+    g.prepare_levels(l3, l)  # the levels the refresh passes through (long chains prepare the top one only)
+    g.prepare_raise(l0)
     keys = torch.empty((BS + GS, dnum, 2, tot, n), dtype=u64, device=dev)
     cts = torch.empty((GS, BS, l, n), dtype=u64, device=dev)
     stc = torch.empty((GS, BS, l3, n), dtype=u64, device=dev)
@@ -264,6 +316,130 @@ def seeded_key_timing(g, torch, a, key, reps: int = 40):
             row[name] = {"us_per_call": e0.elapsed_time(e1) / reps * 1e3, "inner_product_us": ip[1] / ip[0] * 1e3}
         row["key_switches_per_s"] = {k: B / (v["us_per_call"] * 1e-6) for k, v in row.items()}
         res[f"batch{B}"] = row
+    return res
+
+
+C4_N, C4_L, C4_K, C4_DNUM, C4_L_STC = 2048, 2100, 263, 8, 2084
+
+
+def c4_work(l: int, B: int, conj: bool):
+    """Algorithmic work of one 32 x 32 BSGS + rescale at level l on B ciphertexts
+    (hoisted baby steps: one ModUp; 31 giant rotations; every key switch
+    converts exactly), plus one conjugation key switch at l - 1 if `conj`."""
+    K, alpha = C4_K, (C4_L + C4_DNUM - 1) // C4_DNUM
+
+    def digits(lv):
+        return [min(alpha, lv - j * alpha) for j in range((lv + alpha - 1) // alpha)]
+
+    def up(lv):  # ModUp products per coefficient of one ciphertext
+        return sum(m * (lv + K - m) for m in digits(lv))
+
+    def ext_limbs(lv):
+        return sum(lv + K - m for m in digits(lv))
+
+    sb, sg = BS - 1, GS - 1
+    lc = l - 1
+    n_up = [(l, B), (l, sg * B)] + ([(lc, B)] if conj else [])
+    n_dn = [(l, (sb + sg) * B)] + ([(lc, B)] if conj else [])
+    return {
+        "ks_modup_convert": {"products": sum(up(lv) * c * N for lv, c in n_up)},
+        "ks_moddown_convert": {"products": sum(2 * K * lv * c * N for lv, c in n_dn)},
+        "ks_ntt_ext": {"bytes": sum(2 * ext_limbs(lv) * c * LIMB for lv, c in n_up)},
+        "bsgs_mac": {"mads": 4 * GS * BS * 2 * B * l * N,
+                     "bytes": (GS * BS * l + BS * 2 * B * l + GS * 2 * B * l) * LIMB},
+    }
+
+
+def c4_timing(torch, reps: int = 3):
+    """The bootstrap-scale linear transforms at their real shape (2100 + 263
+    primes, dnum 8, batch 8, BSGS 32 x 32, seeded dense diagonals and keys):
+    coeff_to_slot = BSGS + rescale at 2100 primes, then the conjugation key
+    switch at 2099; slot_to_coeff = BSGS + rescale at 2084 primes.  Each timed
+    over `reps` runs after one untimed run; per-kernel times from one more
+    profiled run of each."""
+    from rns_ckks_polynomial_amd import synth
+    from rns_ckks_polynomial_amd.api import Context
+    n, l, k, dnum, lst = C4_N, C4_L, C4_K, C4_DNUM, C4_L_STC
+    tot = l + k
+    g = Context(n, l, k, dnum, device=0)
+    g.prepare_levels(lst, l)
+    u64, dev = torch.uint64, "cuda:0"
+    seed = 0xC0DE0004
+    print("c4: drawing keys and diagonals (110 GB)", file=sys.stderr, flush=True)
+    keys = torch.empty((BS + GS - 1, dnum, 2, tot, n), dtype=u64, device=dev)
+    g.fill_uniform(keys, seed + 1, synth.TAG_KEY, 0)
+    cts_d = torch.empty((GS, BS, l, n), dtype=u64, device=dev)
+    stc_d = torch.empty((GS, BS, lst, n), dtype=u64, device=dev)
+    g.fill_uniform(cts_d, seed + 2, synth.TAG_DIAG, 0)
+    g.fill_uniform(stc_d, seed + 3, synth.TAG_DIAG, 0)
+    x = torch.empty((BATCH, 2, l, n), dtype=u64, device=dev)
+    xs = torch.empty((BATCH, 2, lst, n), dtype=u64, device=dev)
+    g.fill_uniform(x, seed + 4, synth.TAG_CT, 0)
+    g.fill_uniform(xs, seed + 5, synth.TAG_CT, 0)
+    baby = [None] + [keys[b - 1] for b in range(1, BS)]
+    giant = [None] + [keys[BS - 2 + j] for j in range(1, GS)]
+    conj = keys[BS + GS - 2]
+    w = torch.empty((BATCH, 2, l - 1, n), dtype=u64, device=dev)
+    cj, y = torch.empty_like(w), torch.empty((BATCH, 2, lst - 1, n), dtype=u64, device=dev)
+    ws = g.workspace(max(g.workspace_size("bsgs", BATCH, l, BS, GS), g.workspace_size("rotate", BATCH, l - 1)))
+
+    def cts():
+        g.bsgs_linear_transform(x, cts_d, BS, GS, baby, giant, do_rescale=True, out=w, ws=ws)
+        g.rotate(w, 2 * n - 1, conj, out=cj, ws=ws)
+
+    def stc():
+        g.bsgs_linear_transform(xs, stc_d, BS, GS, baby, giant, do_rescale=True, out=y, ws=ws)
+
+    res = {}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for name, fn, lv, conj_ks in (("coeff_to_slot", cts, l, True), ("slot_to_coeff", stc, lst, False)):
+        fn()
+        torch.cuda.synchronize()
+        print(f"c4 {name}: first run done", file=sys.stderr, flush=True)
+        times = []
+        for _ in range(reps):
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        times.sort()
+        ms = times[len(times) // 2]
+        g.profile_begin()
+        fn()
+        prof = g.profile_end()
+        ks = BATCH * (BS + GS - 2 + (1 if conj_ks else 0))
+        work = c4_work(lv, BATCH, conj_ks)
+        kern = {}
+        for kn, (cnt, tot_ms, mn, mx) in prof.items():
+            row = {"launches": cnt, "avg_us": tot_ms / cnt * 1e3, "total_ms": tot_ms}
+            wk = work.get(kn, {})
+            if "products" in wk:
+                row["algo_int8_TOPs"] = wk["products"] * I8_OPS_PER_PRODUCT / (tot_ms * 1e-3) / 1e12
+            if "bytes" in wk:
+                row["algo_GBps"] = wk["bytes"] / (tot_ms * 1e-3) / 1e9
+            if "mads" in wk:
+                row["algo_Tmads"] = wk["mads"] / (tot_ms * 1e-3) / 1e12
+            kern[kn] = row
+        dom = max(kern, key=lambda kk: kern[kk]["total_ms"])
+        d = kern[dom]
+        if "algo_int8_TOPs" in d:
+            roof = {"bound": "mfma", "achieved": d["algo_int8_TOPs"], "peak": MFMA_I8_PEAK_TOPS, "unit": "int8 TOP/s"}
+        elif "algo_Tmads" in d:
+            roof = {"bound": "alu", "achieved": d["algo_Tmads"], "peak": VALU_PEAK_TOPS, "unit": "T int32-MAD/s"}
+        else:
+            roof = {"bound": "hbm", "achieved": d.get("algo_GBps"), "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        roof.update({"kernel": dom, "frac": roof["achieved"] / roof["peak"] if roof["achieved"] else None,
+                     "avg_launch_us": d["avg_us"], "kernel_ms": d["total_ms"]})
+        res[name] = {"ms_per_batch": ms, "ms_all": times, "linear_transforms_per_s": BATCH / (ms * 1e-3),
+                     "key_switches_per_s": ks / (ms * 1e-3), "key_switches": ks, "level": lv,
+                     "roofline": roof, "kernels": kern}
+        print(f"c4 {name}: {ms:.1f} ms per batch", file=sys.stderr, flush=True)
+    res["config"] = (f"n={n}, {l}+{k} primes, dnum={dnum}, batch {BATCH}, BSGS {BS}x{GS}, dense seeded diagonals: "
+                     f"coeff_to_slot at {l} (+ conjugation key switch at {l - 1}), slot_to_coeff at {lst}")
+    res["hbm_bytes_allocated"] = torch.cuda.max_memory_allocated()
+    del keys, cts_d, stc_d, x, xs, w, cj, y, ws, g
+    torch.cuda.empty_cache()
     return res
 
 
@@ -487,7 +663,7 @@ def main():
 
     # EvalMod (bootstrapping's modular reduction, outside the step): batch 8 at
     # the 112-prime level, degree-31 cosine interpolant on [-8, 8], 3 double angles
-    em = boot = seeded = ring = None
+    em = boot = seeded = ring = c4 = None
     if not args.step_only:
         em = eval_mod_timing(g, a, rlk, torch)
         # seed-expanded switching keys: rotation with the key's a rows regenerated in the kernel
@@ -499,6 +675,10 @@ def main():
         boot = bootstrap_timing(g, torch, L, 1, diags, stc, baby, giant, keys[0], rlk, 2, 0xC0DE0006)
         del stc
         ring = ring65536_timing(torch)
+    if not args.step_only and not args.no_c4:
+        del x
+        torch.cuda.empty_cache()
+        c4 = c4_timing(torch)
 
     work = kernel_work()
     kernels = {}
@@ -568,6 +748,7 @@ def main():
         "bootstrap": boot,
         "seeded_keys": seeded,
         "ring65536": ring,
+        "c4": c4,
         "limb_ntts_per_s": ntt_rate,
         "linear_transforms_per_s": BATCH / (bsgs_ms * 1e-3),
         "ct_mults_per_s": BATCH / (mr_ms * 1e-3),
@@ -589,6 +770,7 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
         out["cpu_baseline"]["one_core"] = cpu_baseline_one_core(min(5.0, args.cpu_seconds))
+        out["cpu_baseline"]["units"] = cpu_baseline_units(skip_c4=args.no_c4 or args.step_only)
     print(json.dumps(out))
 
 

@@ -30,16 +30,27 @@
  * Memory and streams
  *  - Data pointers are DEVICE pointers on the context's device, allocated and
  *    owned by the caller (8-byte aligned).  Pointer-array arguments
- *    (BSGS keys) are HOST arrays of device pointers.
+ *    (BSGS keys) are HOST arrays of key descriptors.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
- *    enqueue work and return; nothing synchronises with the host, except that
- *    the first call at a new level builds that level's constant tables
- *    (blocking upload, done once per level and context).
+ *    enqueue work and return; nothing synchronises with the host and no call
+ *    allocates device memory after context creation and level preparation.
+ *  - Levels: an operation at level l uses constant tables of that level (the
+ *    partial last key-switching digit, rescale inverses).  ckks_ctx_create
+ *    builds them for every level when L <= CKKS_PREPARE_ALL_MAX_L; for longer
+ *    chains the caller builds the levels it will use with ckks_prepare_levels
+ *    (and ckks_prepare_raise for ModRaise) before the first call there.  A
+ *    call at a level that is not prepared returns CKKS_ENOTREADY.  The
+ *    context is read-only after that: concurrent calls on different streams
+ *    are safe given distinct workspaces (preparation must not run concurrently
+ *    with other calls on the same context).
  *  - Workspace: ops that need scratch take (ws, ws_bytes); query the size with
- *    ckks_workspace_size.  The caller owns it; concurrent calls need distinct
- *    workspaces.  No call allocates device memory after context creation,
- *    apart from the one-time level tables above.
- *  - in == out aliasing is allowed for the NTT calls only.
+ *    ckks_workspace_size.  The caller owns it.  At n = 65536 the workspace also
+ *    holds the four-step NTT's transpose buffer; the bare NTT calls, which take
+ *    no workspace, share one context buffer and are ordered across streams by
+ *    a context event (at n = 2048 every transform stays in LDS).
+ *  - Aliasing: the NTT calls work in place; ckks_pointwise_mul accepts
+ *    out == a or out == b exactly; every other call rejects (CKKS_EINVAL) an
+ *    output whose byte range overlaps an input's.
  *
  * Errors: every call returns CKKS_OK (0) or a negative CKKS_E* code; arguments
  * are validated before any launch; nothing is printed.
@@ -61,6 +72,12 @@ extern "C" {
 #define CKKS_EALIGN (-5)     /* pointer not 8-byte aligned                     */
 #define CKKS_EWORKSPACE (-6) /* workspace missing or smaller than required     */
 #define CKKS_EUNSUPPORTED (-7) /* ring degree / parameter not supported        */
+#define CKKS_EKEY (-8)       /* switching key made for another parameter set,  */
+                             /* or a seeded key where a stored one is needed    */
+#define CKKS_ENOTREADY (-9)  /* level tables not prepared (ckks_prepare_levels) */
+
+/* Chains up to this many main primes get every level's tables at creation. */
+#define CKKS_PREPARE_ALL_MAX_L 256
 
 typedef struct ckks_ctx ckks_ctx;
 
@@ -74,14 +91,50 @@ typedef struct {
 /* Create a context on HIP device `device`: generates the chain primes and
  * roots (Kestrel relay README section 1 / article section 4.1 parameters:
  * n = 2048, 60-bit primes, 112 or 2100 of them), and uploads twiddle and
- * base-conversion tables.  Returns CKKS_EUNSUPPORTED for unsupported n, for
- * a chain prime at or above 2^59 + 2^52, or for a digit width ceil(L/dnum) or
- * K above 1000 (the bounds of the exact 128-bit base-conversion sums). */
+ * base-conversion tables; with L <= CKKS_PREPARE_ALL_MAX_L also every level's
+ * tables and every ModRaise source level's.  Returns CKKS_EUNSUPPORTED for
+ * unsupported n, for a chain prime at or above 2^59 + 2^52, or for a digit
+ * width ceil(L/dnum) or K above 1000 (the bounds of the exact 128-bit
+ * base-conversion sums).  Blocking; allocates. */
 int ckks_ctx_create(ckks_ctx **out, const ckks_params *params, int device);
 void ckks_ctx_destroy(ckks_ctx *ctx);
+/* Build the tables of levels level_lo..level_hi (inclusive; levels already
+ * built are kept).  Blocking; allocates; not concurrent with other calls on
+ * the context.  CKKS_ELEVEL for a range outside [1, L]. */
+int ckks_prepare_levels(ckks_ctx *ctx, int level_lo, int level_hi);
+/* Build the ModRaise tables of source level level_in (ckks_mod_raise,
+ * ckks_bootstrap).  Same rules as ckks_prepare_levels; level_in <= min(L, 1000). */
+int ckks_prepare_raise(ckks_ctx *ctx, int level_in);
 /* Copy the chain primes and their psi to host arrays of L+K entries (either may be NULL). */
 int ckks_ctx_primes(const ckks_ctx *ctx, uint64_t *host_primes, uint64_t *host_psi);
 const char *ckks_strerror(int code);
+
+/* Switching key descriptor (hybrid key switching, Kestrel article technique
+ * table: relinearisation and Galois keys; EncryptedLLM GPU blog section 2.5:
+ * keys of hundreds of MB to GB, preloaded on the device).
+ *  - Stored key (seeded = 0): data = [dnum][2][L+K][n], NTT domain; row
+ *    (j, 0) = b_j, row (j, 1) = a_j, limb g modulo chain prime g.
+ *  - Seeded key (seeded = 1, EncryptedLLM blog section 4.4: cut key size when
+ *    memory or key loading is the limit): data = the b rows [dnum][L+K][n];
+ *    the a rows are regenerated from `seed` where they are used:
+ *      a_j[i][k] = floor(w q_i / 2^64),  w = S(S(S(seed, 10), j (L+K) + i), k),
+ *      S(s, t) = mix64(s + (t + 1) 0x9e3779b97f4a7c15),
+ *    mix64 the SplitMix64 finaliser (Steele, Lea, Flood, OOPSLA 2014):
+ *      z ^= z >> 30; z *= 0xbf58476d1ce4e5b9; z ^= z >> 27; z *= 0x94d049bb133111eb;
+ *      z ^= z >> 31.
+ *    Relinearisation and rotation take seeded keys; BSGS, EvalMod and
+ *    bootstrapping need stored ones (ckks_key_expand converts).
+ * (n, L, K, dnum) name the parameter set the key was generated for: every
+ * call checks them against its context and returns CKKS_EKEY on a mismatch.
+ * The descriptor is read during the call only; `data` must stay valid until
+ * the stream work completes. */
+typedef struct {
+    const uint64_t *data;
+    uint32_t n, L, K, dnum;
+    uint32_t seeded;
+    uint32_t reserved; /* 0 */
+    uint64_t seed;
+} ckks_swk;
 
 /* Workspace sizes.  op: one of the CKKS_OP_* values; batch = ciphertexts per
  * call; level = l; for CKKS_OP_BSGS, bs and gs are the baby/giant step counts
@@ -104,57 +157,37 @@ int ckks_ntt_inv(const ckks_ctx *ctx, uint64_t *x, int count, int first_prime, i
 /* Pointwise product in the NTT domain (the middle step of an NTT-based
  * negacyclic polynomial multiply): out = a (.) b limb by limb, layouts as
  * ckks_ntt_fwd ([count][nlimbs][n], limb r modulo prime first_prime + r).
- * out may alias a or b. */
+ * out may equal a or b (the same pointer); partial overlap is rejected. */
 int ckks_pointwise_mul(const ckks_ctx *ctx, const uint64_t *a, const uint64_t *b, uint64_t *out, int count,
                        int first_prime, int nlimbs, void *stream);
 
-/* Ciphertext-ciphertext multiply with relinearisation ("every multiplication
- * grows the noise", Kestrel article wall 2):  for each of `batch` pairs,
+/* Ciphertext-ciphertext multiply with relinearisation (the Kestrel
+ * article's wall 2: a product's noise grows, and relinearisation brings the
+ * degree-2 ciphertext back to two polynomials): for each of `batch` pairs,
  * (d0, d1, d2) = (a0 b0, a0 b1 + a1 b0, a1 b1) and
  * out = (d0, d1) + KeySwitch(d2, rlk).  a, b, out: [batch][2][level][n];
- * rlk: switching key for s^2. */
-int ckks_mul_tensor_relin(const ckks_ctx *ctx, const uint64_t *a, const uint64_t *b, const uint64_t *rlk,
+ * rlk: switching key for s^2 (stored or seeded); out must not overlap a or b. */
+int ckks_mul_tensor_relin(const ckks_ctx *ctx, const uint64_t *a, const uint64_t *b, const ckks_swk *rlk,
                           uint64_t *out, int batch, int level, void *ws, size_t ws_bytes, void *stream);
 
 /* Rescale: drop the last prime q_{l-1} with rounding, out = round(c / q_{l-1})
- * ("each rescale consumes one prime", Kestrel article wall 2).
- * in: [batch][2][level][n]; out: [batch][2][level-1][n]. */
+ * (Kestrel article wall 2: every rescale uses up one prime of the chain).
+ * in: [batch][2][level][n]; out: [batch][2][level-1][n], not overlapping in. */
 int ckks_rescale(const ckks_ctx *ctx, const uint64_t *in, uint64_t *out, int batch, int level, void *ws,
                  size_t ws_bytes, void *stream);
 
 /* Galois automorphism X -> X^g followed by hybrid key switching back to s
  * (Galois rotation / conjugation of the Kestrel article's technique table):
  * out = (sigma_g(c0), 0) + KeySwitch(sigma_g(c1), key).  g odd, in [1, 2n).
- * in, out: [batch][2][level][n] (must not alias). */
+ * in, out: [batch][2][level][n] (no overlap); key stored or seeded. */
 int ckks_rotate(const ckks_ctx *ctx, const uint64_t *in, uint64_t *out, int batch, int level, uint32_t galois_elt,
-                const uint64_t *key, void *ws, size_t ws_bytes, void *stream);
+                const ckks_swk *key, void *ws, size_t ws_bytes, void *stream);
 
-/* Seed-expanded switching keys (the EncryptedLLM GPU blog, sections 2.5 and
- * 4.4: switching keys run to hundreds of MB or GB and their size is what to
- * cut when memory or key loading is the limit).  A switching key's a rows are
- * uniform; a seeded key stores only its b rows, key_b: [dnum][L + K][n] (NTT
- * domain, row (j, i) = digit j, key prime i in chain order), and a 64-bit seed
- * from which the library regenerates every a residue where it is used:
- *   a_j[i][k] = floor(w q_i / 2^64),  w = S(S(S(seed, 10), j (L + K) + i), k),
- *   S(s, t) = mix64(s + (t + 1) 0x9e3779b97f4a7c15)
- * with mix64 the SplitMix64 finaliser (Steele, Lea, Flood, OOPSLA 2014):
- *   z ^= z >> 30; z *= 0xbf58476d1ce4e5b9; z ^= z >> 27; z *= 0x94d049bb133111eb;
- *   z ^= z >> 31.
- * The key switch then reads half the key bytes.  The results are those of
- * the stored key [dnum][2][L + K][n] with row c = 0 equal to key_b and row
- * c = 1 the regenerated a (ckks_key_expand writes that key).  Arguments,
- * workspaces and errors as ckks_mul_tensor_relin / ckks_rotate. */
-int ckks_mul_tensor_relin_seeded(const ckks_ctx *ctx, const uint64_t *a, const uint64_t *b, const uint64_t *rlk_b,
-                                 uint64_t rlk_seed, uint64_t *out, int batch, int level, void *ws, size_t ws_bytes,
-                                 void *stream);
-int ckks_rotate_seeded(const ckks_ctx *ctx, const uint64_t *in, uint64_t *out, int batch, int level,
-                       uint32_t galois_elt, const uint64_t *key_b, uint64_t key_seed, void *ws, size_t ws_bytes,
-                       void *stream);
 /* Expand a seeded key to the stored format: key_out [dnum][2][L + K][n] with
- * key_out[j][0] = key_b[j] and key_out[j][1] the regenerated a rows (for the
- * calls that take stored keys: BSGS, EvalMod, bootstrapping).  key_b and
- * key_out must not overlap. */
-int ckks_key_expand(const ckks_ctx *ctx, const uint64_t *key_b, uint64_t key_seed, uint64_t *key_out, void *stream);
+ * key_out[j][0] = the b rows and key_out[j][1] the regenerated a rows (for
+ * the calls that take stored keys: BSGS, EvalMod, bootstrapping).  key_out
+ * must not overlap the key's data. */
+int ckks_key_expand(const ckks_ctx *ctx, const ckks_swk *seeded_key, uint64_t *key_out, void *stream);
 
 /* Baby-step giant-step plaintext-matrix x ciphertext (matmul2 with BB x GG,
  * Kestrel article technique table and section 4.4; coeff_to_slot /
@@ -163,11 +196,11 @@ int ckks_key_expand(const ckks_ctx *ctx, const uint64_t *key_b, uint64_t key_see
  * then, if do_rescale, out = Rescale(y).  diags: [gs][bs][level][n]
  * (encoded pre-rotated diagonals, NTT domain); baby_keys[b] is the key of
  * rotation by b (b = 1..bs-1, entry 0 ignored); giant_keys[g] the key of
- * rotation by g*bs (g = 1..gs-1, entry 0 ignored).  in: [batch][2][level][n];
- * out: [batch][2][level - do_rescale][n]. */
+ * rotation by g*bs (g = 1..gs-1, entry 0 ignored); stored keys.  in:
+ * [batch][2][level][n]; out: [batch][2][level - do_rescale][n], no overlap. */
 int ckks_bsgs_linear_transform(const ckks_ctx *ctx, const uint64_t *in, uint64_t *out, int batch, int level,
-                               const uint64_t *diags, int bs, int gs, const uint64_t *const *baby_keys,
-                               const uint64_t *const *giant_keys, int do_rescale, void *ws, size_t ws_bytes,
+                               const uint64_t *diags, int bs, int gs, const ckks_swk *const *baby_keys,
+                               const ckks_swk *const *giant_keys, int do_rescale, void *ws, size_t ws_bytes,
                                void *stream);
 
 /* ModRaise, the first step of bootstrapping (modraise in the Kestrel
@@ -177,7 +210,8 @@ int ckks_bsgs_linear_transform(const ckks_ctx *ctx, const uint64_t *in, uint64_t
  * modulo q_0 ... q_{level_out - 1}.  The plaintext becomes m + (q_0...) I
  * for a small integer polynomial I, which EvalMod later removes.  in:
  * [batch][2][level_in][n] (NTT domain); out: [batch][2][level_out][n]; no
- * aliasing; level_in <= min(level_out, 1000). */
+ * aliasing; level_in <= min(level_out, 1000); ModRaise tables of level_in
+ * prepared (ckks_prepare_raise). */
 int ckks_mod_raise(const ckks_ctx *ctx, const uint64_t *in, uint64_t *out, int batch, int level_in, int level_out,
                    void *ws, size_t ws_bytes, void *stream);
 
@@ -203,14 +237,15 @@ int ckks_mod_raise(const ckks_ctx *ctx, const uint64_t *in, uint64_t *out, int b
  * level *level_out = level minus that, scale *scale_out.  The scales stay
  * near scale_in only if scale_in is close to the chain primes (e.g. 2^59 for
  * primes just above 2^59).  in: [batch][2][level][n]; out:
- * [batch][2][*level_out][n] (may alias in); cheb: host array of degree + 1
+ * [batch][2][*level_out][n] (may alias in exactly); cheb: host array of degree + 1
  * doubles, |cheb[k]| < 2; 0.5 <= K; |out_factor| < 2; 1 <= degree <= 1024;
  * 0 <= double_angles <= 64; scale_in in (0, 2^61); rlk as
- * ckks_mul_tensor_relin.  Returns CKKS_EINVAL (after queuing the work) if a
+ * ckks_mul_tensor_relin (stored key); every level from level down to
+ * *level_out + 1 prepared.  Returns CKKS_EINVAL (after queuing the work) if a
  * constant times its scale reaches 2^62, the output then being invalid. */
 int ckks_eval_mod(const ckks_ctx *ctx, const uint64_t *in, uint64_t *out, int batch, int level, double scale_in,
                   const double *cheb, int degree, double bound_k, int double_angles, double out_factor,
-                  const uint64_t *rlk, void *ws, size_t ws_bytes, double *scale_out, int *level_out,
+                  const ckks_swk *rlk, void *ws, size_t ws_bytes, double *scale_out, int *level_out,
                   void *stream);
 
 /* Bootstrapping (the boot of the Kestrel article's section 5.3, with its
@@ -232,16 +267,18 @@ int ckks_eval_mod(const ckks_ctx *ctx, const uint64_t *in, uint64_t *out, int ba
  * degree) + double_angles); *scale_mid = the EvalMod output scale (the scale
  * entering slot_to_coeff).  in: [batch][2][level_in][n]; cts_diags:
  * [gs][bs][level_raise][n]; stc_diags: [gs][bs][*level_out + 1][n]; out:
- * [batch][2][*level_out][n]; no aliasing. */
+ * [batch][2][*level_out][n]; no aliasing; stored keys; the ModRaise tables
+ * of level_in and every level from level_raise down to *level_out + 1
+ * prepared. */
 typedef struct {
     int level_raise;
     const uint64_t *cts_diags;
     const uint64_t *stc_diags;
     int bs, gs;
-    const uint64_t *const *baby_keys;
-    const uint64_t *const *giant_keys;
-    const uint64_t *conj_key;
-    const uint64_t *rlk;
+    const ckks_swk *const *baby_keys;
+    const ckks_swk *const *giant_keys;
+    const ckks_swk *conj_key;
+    const ckks_swk *rlk;
     double evalmod_scale;
     const double *cheb;
     int degree;

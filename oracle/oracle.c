@@ -428,7 +428,7 @@ void or_mul_tensor_relin(const or_params *pp, uint32_t l, const uint64_t *a, con
     free(d); free(ks);
 }
 
-/* Rescale ("each rescale consumes one prime", Kestrel article, wall 2):
+/* Rescale (Kestrel article, wall 2: every rescale uses up one prime of the chain):
  * out = round(c / q_{l-1}) = (c - [c]_{q_{l-1}, centered}) * q_{l-1}^-1. */
 void or_rescale(const or_params *pp, uint32_t l, const uint64_t *in, uint64_t *out) {
     const uint32_t n = pp->n;

@@ -12,7 +12,7 @@
  *  - The Kestrel article on encrypted 2B-model inference, section 3 (technique
  *    table: NTT/INTT, RNS decomposition, modulus chain + rescale, RNS base
  *    conversion, Galois rotation/conjugation, baby-step giant-step matmul),
- *    section 4.1 (key parameters), "wall 2" (each rescale consumes one prime)
+ *    section 4.1 (key parameters), wall 2 (every rescale uses up one prime)
  *    and "wall 3" (boot profile: coeff_to_slot / slot_to_coeff).
  *  - The EncryptedLLM GPU blog, section 3.4 (NTT kernel, base conversion
  *    between prime sets).

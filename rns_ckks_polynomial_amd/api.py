@@ -36,6 +36,21 @@ def _stream():
     return C.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+class SwitchKey:
+    """A switching key on the device with the parameter set it was made for
+    (the ckks_swk descriptor).  Stored: data [dnum][2][L+K][n]; seeded: data =
+    the b rows [dnum][L+K][n] and `seed` regenerates the a rows."""
+
+    def __init__(self, data: torch.Tensor, n: int, L: int, K: int, dnum: int, seeded: bool = False, seed: int = 0):
+        self.data, self.n, self.L, self.K, self.dnum = data, n, L, K, dnum
+        self.seeded, self.seed = bool(seeded), int(seed) & (2 ** 64 - 1)
+
+    def descriptor(self) -> nat.Swk:
+        rows = self.dnum * (1 if self.seeded else 2) * (self.L + self.K) * self.n
+        _need(self.data, rows, "seeded key" if self.seeded else "key")
+        return nat.Swk(_ptr(self.data), self.n, self.L, self.K, self.dnum, int(self.seeded), 0, self.seed)
+
+
 class Context:
     """Parameter set + device tables: n, L main primes, K special primes, dnum digits."""
 
@@ -87,9 +102,25 @@ class Context:
             ws = self.workspace(need)
         return ws, need
 
-    def _key(self, k, what="key"):
-        _need(k, self.dnum * 2 * (self.L + self.K) * self.n, what)
-        return _ptr(k)
+    def key(self, data: torch.Tensor, seeded: bool = False, seed: int = 0) -> SwitchKey:
+        """Wrap a key tensor made for this context's parameters."""
+        return SwitchKey(data, self.n, self.L, self.K, self.dnum, seeded, seed)
+
+    def _swk(self, k) -> nat.Swk:
+        """A ckks_swk for a SwitchKey, or for a bare stored-key tensor of this context."""
+        return (k if isinstance(k, SwitchKey) else self.key(k)).descriptor()
+
+    def _swk_array(self, keys, count):
+        """(array of descriptor addresses for the C call, the descriptors kept alive)."""
+        descs = [None if k is None else self._swk(k) for k in keys]
+        arr = (C.c_void_p * count)(*[None if d is None else C.addressof(d) for d in descs[:count]])
+        return arr, descs
+
+    def prepare_levels(self, lo: int, hi: int):
+        nat.check(nat.lib().ckks_prepare_levels(self._h, lo, hi), "ckks_prepare_levels")
+
+    def prepare_raise(self, level_in: int):
+        nat.check(nat.lib().ckks_prepare_raise(self._h, level_in), "ckks_prepare_raise")
 
     def _cts(self, t, B, l, what):
         _need(t, B * 2 * l * self.n, what)
@@ -120,7 +151,8 @@ class Context:
         B, _, l, n = a.shape
         out = torch.empty_like(a) if out is None else out
         ws, need = self._ws_for("relin", B, l, ws=ws)
-        nat.check(nat.lib().ckks_mul_tensor_relin(self._h, _ptr(a), self._cts(b, B, l, "b"), self._key(rlk),
+        k = self._swk(rlk)
+        nat.check(nat.lib().ckks_mul_tensor_relin(self._h, _ptr(a), self._cts(b, B, l, "b"), C.byref(k),
                                                   self._cts(out, B, l, "out"), B, l,
                                                   _ptr(ws), ws.numel() * 8, _stream()), "ckks_mul_tensor_relin")
         return out
@@ -138,42 +170,27 @@ class Context:
         B, _, l, n = x.shape
         out = torch.empty_like(x) if out is None else out
         ws, need = self._ws_for("rotate", B, l, ws=ws)
+        k = self._swk(key)
         nat.check(nat.lib().ckks_rotate(self._h, _ptr(x), self._cts(out, B, l, "out"), B, l, galois_elt,
-                                        self._key(key), _ptr(ws),
+                                        C.byref(k), _ptr(ws),
                                         ws.numel() * 8, _stream()), "ckks_rotate")
         return out
 
-    def _key_b(self, k, what="key_b"):
-        _need(k, self.dnum * (self.L + self.K) * self.n, what)
-        return _ptr(k)
-
     def mul_tensor_relin_seeded(self, a, b, rlk_b, rlk_seed: int, out=None, ws=None):
-        """ckks_mul_tensor_relin_seeded: the relinearisation key given as its b rows + seed."""
-        B, _, l, n = a.shape
-        out = torch.empty_like(a) if out is None else out
-        ws, need = self._ws_for("relin", B, l, ws=ws)
-        nat.check(nat.lib().ckks_mul_tensor_relin_seeded(self._h, _ptr(a), self._cts(b, B, l, "b"),
-                                                         self._key_b(rlk_b), int(rlk_seed) & (2 ** 64 - 1),
-                                                         self._cts(out, B, l, "out"), B, l, _ptr(ws), ws.numel() * 8,
-                                                         _stream()), "ckks_mul_tensor_relin_seeded")
-        return out
+        """Relinearisation with the key given as its b rows + seed (a seeded ckks_swk)."""
+        return self.mul_tensor_relin(a, b, self.key(rlk_b, seeded=True, seed=rlk_seed), out=out, ws=ws)
 
     def rotate_seeded(self, x, galois_elt: int, key_b, key_seed: int, out=None, ws=None):
-        """ckks_rotate_seeded: the Galois key given as its b rows + seed."""
-        B, _, l, n = x.shape
-        out = torch.empty_like(x) if out is None else out
-        ws, need = self._ws_for("rotate", B, l, ws=ws)
-        nat.check(nat.lib().ckks_rotate_seeded(self._h, _ptr(x), self._cts(out, B, l, "out"), B, l, galois_elt,
-                                               self._key_b(key_b), int(key_seed) & (2 ** 64 - 1), _ptr(ws),
-                                               ws.numel() * 8, _stream()), "ckks_rotate_seeded")
-        return out
+        """Rotation with the Galois key given as its b rows + seed (a seeded ckks_swk)."""
+        return self.rotate(x, galois_elt, self.key(key_b, seeded=True, seed=key_seed), out=out, ws=ws)
 
     def key_expand(self, key_b, key_seed: int, out=None):
         """ckks_key_expand: [dnum][L+K][n] b rows + seed -> stored key [dnum][2][L+K][n]."""
         tot = self.L + self.K
         out = torch.empty((self.dnum, 2, tot, self.n), dtype=key_b.dtype, device=key_b.device) if out is None else out
-        nat.check(nat.lib().ckks_key_expand(self._h, self._key_b(key_b), int(key_seed) & (2 ** 64 - 1),
-                                            self._key(out, "out"), _stream()), "ckks_key_expand")
+        _need(out, self.dnum * 2 * tot * self.n, "out")
+        k = self.key(key_b, seeded=True, seed=key_seed).descriptor()
+        nat.check(nat.lib().ckks_key_expand(self._h, C.byref(k), _ptr(out), _stream()), "ckks_key_expand")
         return out
 
     def bsgs_linear_transform(self, x, diags, bs: int, gs: int, baby_keys, giant_keys, do_rescale=True,
@@ -182,8 +199,8 @@ class Context:
         lo = l - 1 if do_rescale else l
         out = torch.empty((B, 2, lo, n), dtype=x.dtype, device=x.device) if out is None else out
         ws, need = self._ws_for("bsgs", B, l, bs, gs, ws=ws)
-        bk = (C.c_void_p * bs)(*[None if k is None else self._key(k, "baby key") for k in baby_keys])
-        gk = (C.c_void_p * gs)(*[None if k is None else self._key(k, "giant key") for k in giant_keys])
+        bk, _keep_b = self._swk_array(baby_keys, bs)
+        gk, _keep_g = self._swk_array(giant_keys, gs)
         _need(diags, gs * bs * l * n, "diags")
         nat.check(nat.lib().ckks_bsgs_linear_transform(self._h, _ptr(x), self._cts(out, B, lo, "out"), B, l,
                                                        _ptr(diags), bs, gs,
@@ -207,11 +224,12 @@ class Context:
         """Bootstrapping (see ckks_bootstrap): returns (out, scale entering slot_to_coeff)."""
         B, _, l0, n = x.shape
         cheb_c = (C.c_double * len(cheb))(*[float(v) for v in cheb])
-        bk = (C.c_void_p * bs)(*[None if k is None else self._key(k, "baby key") for k in baby_keys])
-        gk = (C.c_void_p * gs)(*[None if k is None else self._key(k, "giant key") for k in giant_keys])
+        bk, _keep_b = self._swk_array(baby_keys, bs)
+        gk, _keep_g = self._swk_array(giant_keys, gs)
+        ck, rk = self._swk(conj_key), self._swk(rlk)
         lo = level_raise - 3 - (3 + max(0, (len(cheb) - 2).bit_length()) + double_angles)
-        p = nat.BootParams(level_raise, _ptr(cts_diags), _ptr(stc_diags), bs, gs, bk, gk, self._key(conj_key, "conj key"),
-                           self._key(rlk, "rlk"),
+        p = nat.BootParams(level_raise, _ptr(cts_diags), _ptr(stc_diags), bs, gs, bk, gk, C.addressof(ck),
+                           C.addressof(rk),
                            float(evalmod_scale), cheb_c, len(cheb) - 1, float(bound_k), int(double_angles),
                            float(out_factor))
         need = C.c_size_t()
@@ -240,9 +258,10 @@ class Context:
         out = torch.empty((B, 2, max(lo, 1), n), dtype=x.dtype, device=x.device) if out is None else out
         ws, need = self._ws_for("evalmod", B, l, degree, ws=ws)
         s_out, l_out = C.c_double(), C.c_int()
+        rk = self._swk(rlk)
         nat.check(nat.lib().ckks_eval_mod(self._h, _ptr(x), self._cts(out, B, max(lo, 0), "out"), B, l, float(scale),
                                           cheb, degree, float(bound_k), int(double_angles), float(out_factor),
-                                          self._key(rlk),
+                                          C.byref(rk),
                                           _ptr(ws), ws.numel() * 8, C.byref(s_out), C.byref(l_out), _stream()),
                   "ckks_eval_mod")
         assert l_out.value == lo

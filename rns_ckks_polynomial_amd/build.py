@@ -24,16 +24,24 @@ FLAGS = [
 ]
 
 
+CXX = os.environ.get("CXX", "g++")
+CXXFLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall"]
+
+
 def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    """HIP sources, and the plain C++ host sources (built with the host compiler)."""
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [CXX, *CXXFLAGS, "-c", src, "-o", obj]
+    else:
+        cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        raise RuntimeError(f"{cmd[0]} failed for {src}:\n{r.stderr}")
     return obj
 
 

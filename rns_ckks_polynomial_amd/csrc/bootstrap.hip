@@ -49,7 +49,7 @@ size_t ws_bytes_bootstrap(const ckks_ctx *c, int B, int l0, const ckks_boot_para
     return boot_layout(c, B, l0, p).total();
 }
 
-int op_bootstrap(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l0, const ckks_boot_params *p,
+int op_bootstrap(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l0, const ckks_boot_params *p,
                  void *ws, double *scale_mid, hipStream_t s) {
     const BootLayout L = boot_layout(c, B, l0, p);
     uint8_t *base = (uint8_t *)ws;

@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "host_tables.h"  // PrimeConsts, MF_RC
+
 namespace ckks {
 
 typedef unsigned __int128 u128;
@@ -68,19 +70,6 @@ __device__ __forceinline__ uint64_t mulm(uint64_t a, uint64_t b, uint64_t q, uin
     uint64_t r = (uint64_t)p - qh * q;
     return csub(r, q);
 }
-
-// Per-prime reduction constants (device arrays indexed by global prime index).
-struct PrimeConsts {
-    uint64_t q;      // the prime
-    uint64_t mu;     // floor(2^122 / q)
-    uint64_t r64;    // 2^64 mod q
-    uint64_t r64p;   // Shoup companion of r64
-    uint64_t m64;    // floor(2^64 / q)  (Shoup companion of 1)
-    uint64_t ninv;   // n^-1 mod q
-    uint64_t ninvp;  // Shoup companion of ninv
-    uint64_t r60;    // 2^60 mod q
-    uint64_t r60p;   // Shoup companion of r60
-};
 
 // Reduce a 128-bit value (hi:lo) modulo q: hi 2^64 + lo = shoup(hi, 2^64 mod q) + shoup(lo, 1).
 __device__ __forceinline__ uint64_t reduce128(uint64_t lo, uint64_t hi, const PrimeConsts &c) {
@@ -228,9 +217,6 @@ struct BasisDev {
 __host__ __device__ __forceinline__ uint64_t digit_form(uint64_t v) {
     return (v + 0x8080808080808080ull) ^ 0x8080808080808080ull;
 }
-// RC row: [0..6] 256^s mod t for s = 8..14 (split30 layout), [7] 2^60 mod t,
-// [8] its Shoup quotient, [9] t, [10] 8t - [2^91]_t.
-constexpr uint32_t MF_RC = 11;
 constexpr uint32_t MF_MAX_ROWS = 2048;  // |S_s| <= 8 rows 2^14 <= 2^28
 
 // ------------------------------------------------------------------ SplitMix64

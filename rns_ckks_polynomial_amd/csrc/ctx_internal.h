@@ -1,5 +1,5 @@
-// ctx_internal.h -- the library context: immutable per-prime tables plus a
-// per-level cache of base-conversion tables, all resident in HBM.
+// ctx_internal.h -- the library context: per-prime tables plus the tables of
+// every prepared level, all resident in HBM; read-only once prepared.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -68,10 +68,10 @@ struct ckks_ctx {
     uint64_t *d_pmod = nullptr;           // [L]    P mod q_i
     // full-width digits at the top level (reused by every level where the digit is whole)
     std::vector<ckks::BasisDev> full_digits;
+    std::vector<std::vector<uint64_t>> full_inv_hat;  // host Shoup pairs of each full digit's [Bhat_i^-1]
     std::vector<void *> owned;
-    std::map<uint32_t, ckks::LevelTables *> levels;
-    std::map<uint32_t, ckks::RaiseTables *> raise;  // ModRaise tables by source level
-    std::mutex mu;
+    std::map<uint32_t, ckks::LevelTables *> levels;  // prepared levels
+    std::map<uint32_t, ckks::RaiseTables *> raise;   // ModRaise tables by prepared source level
     ckks::MultipassPlan *mp = nullptr;
     ckks::Profiler *prof = nullptr;
 };
@@ -106,13 +106,17 @@ uint64_t h_powmod(uint64_t a, uint64_t e, uint64_t q);
 uint64_t h_invmod(uint64_t a, uint64_t q);
 uint64_t h_shoup(uint64_t w, uint64_t q);
 
-// Fetch (building on first use) the level tables.  Returns nullptr on failure.
-LevelTables *level_tables(ckks_ctx *ctx, uint32_t l, int *err);
-// Fetch (building on first use) the ModRaise tables of source level l0.  nullptr on failure.
-RaiseTables *raise_tables(ckks_ctx *ctx, uint32_t l0, int *err);
+// Build (blocking, allocating) the tables of level l / of ModRaise source level l0;
+// a level already built is kept.
+int prepare_level(ckks_ctx *ctx, uint32_t l);
+int prepare_raise(ckks_ctx *ctx, uint32_t l0);
+// The prepared tables, or nullptr when the level was not prepared (lookups only).
+const LevelTables *find_level(const ckks_ctx *ctx, uint32_t l);
+const RaiseTables *find_raise(const ckks_ctx *ctx, uint32_t l0);
 // Build a basis table for primes [first, first + m) with every chain prime as target.
 // chain_targets: lay the conversion table over the chain primes [0, L) (as for
 // the special primes) instead of specials-first-then-outside-the-digit.
+// inv_hat_host (optional) receives the Shoup pairs of [Bhat_i^-1]_{b_i}.
 int build_basis(ckks_ctx *ctx, uint32_t first, uint32_t m, BasisDev *out, std::vector<void *> &owned,
-                bool chain_targets = false);
+                bool chain_targets = false, std::vector<uint64_t> *inv_hat_host = nullptr);
 }  // namespace ckks

@@ -88,9 +88,9 @@ int64_t enc_const(double c, double t, bool *ok) {
 namespace {
 
 struct Eval {
-    ckks_ctx *c;
+    const ckks_ctx *c;
     int B;
-    const uint64_t *rlk;
+    const ckks_swk *rlk;
     uint64_t *tmp_a, *tmp_b, *tmp_p;  // scratch ciphertexts, up to the input level
     void *ks_ws;                      // key-switch / rescale workspace
     hipStream_t s;
@@ -173,8 +173,8 @@ size_t ws_bytes_eval_mod(const ckks_ctx *c, int B, int l, int degree) {
     return ((size_t)degree + 5) * ct + 4 * (size_t)G * ct + ks;
 }
 
-int op_eval_mod(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, double scale_in, const double *cheb,
-                int degree, double bound_k, int double_angles, double out_factor, const uint64_t *rlk, void *ws,
+int op_eval_mod(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, double scale_in, const double *cheb,
+                int degree, double bound_k, int double_angles, double out_factor, const ckks_swk *rlk, void *ws,
                 double *scale_out, int *level_out, hipStream_t s) {
     const int d = degree;
     const size_t slot = (((size_t)B * 2 * l * c->n * 8) + 255) & ~(size_t)255;

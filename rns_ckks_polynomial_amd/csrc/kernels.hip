@@ -153,8 +153,11 @@ __global__ __launch_bounds__(256) void k_ntt2048(Map map, const PrimeConsts *__r
     }
 }
 
+// mp_scratch: the operation's transpose buffer for rings above one LDS tile
+// (mp_scratch_words words), or null for the context's (the bare NTT calls).
 template <class Map>
-static int launch_ntt(const ckks_ctx *c, const Map &map, int nblk, bool inverse, hipStream_t s, const char *name) {
+static int launch_ntt(const ckks_ctx *c, const Map &map, int nblk, bool inverse, hipStream_t s, const char *name,
+                      uint64_t *mp_scratch) {
     if (nblk <= 0) return CKKS_OK;
     ProfScope ps(c, name, s);
     if (c->n == 2048) {
@@ -167,12 +170,12 @@ static int launch_ntt(const ckks_ctx *c, const Map &map, int nblk, bool inverse,
         LAUNCH_CHECK();
         return CKKS_OK;
     }
-    return multipass_ntt(c, map, nblk, inverse, s);
+    return multipass_ntt(c, map, nblk, inverse, s, mp_scratch);
 }
 
 int op_ntt(const ckks_ctx *c, uint64_t *x, int count, int first, int nlimbs, bool inverse, hipStream_t s) {
     MapStrided m{x, x, c->n, (uint32_t)nlimbs, (uint32_t)first, nullptr};
-    return launch_ntt(c, m, count * nlimbs, inverse, s, inverse ? "ntt_inv" : "ntt_fwd");
+    return launch_ntt(c, m, count * nlimbs, inverse, s, inverse ? "ntt_inv" : "ntt_fwd", nullptr);
 }
 
 // =====================================================================
@@ -1360,6 +1363,7 @@ __global__ void k_copy(const uint64_t *__restrict__ a, uint64_t *__restrict__ b,
 struct KsWs {
     uint64_t *d, *y, *ext, *acc, *conv;
     uint32_t *u, *uP;
+    uint64_t *mp;  // transpose buffer of the n > 2048 NTT
 };
 
 static size_t ks_words(const ckks_ctx *c, int B, int l, KsWs *w, uint64_t *base) {
@@ -1378,7 +1382,8 @@ static size_t ks_words(const ckks_ctx *c, int B, int l, KsWs *w, uint64_t *base)
     uint64_t *conv = take(B * 2 * (size_t)l * n);
     uint64_t *u = take((B * beta * n + 1) / 2);
     uint64_t *uP = take((B * 2 * n + 1) / 2);
-    if (w) *w = KsWs{d, y, ext, acc, conv, (uint32_t *)u, (uint32_t *)uP};
+    uint64_t *mp = take(mp_scratch_words(c->n));
+    if (w) *w = KsWs{d, y, ext, acc, conv, (uint32_t *)u, (uint32_t *)uP, mp};
     return off;
 }
 
@@ -1387,7 +1392,7 @@ static size_t ks_words(const ckks_ctx *c, int B, int l, KsWs *w, uint64_t *base)
 // Exact base conversion of `sets` input sets (bases of at most mmax primes)
 // onto up to maxt target positions.
 template <int MODE>
-static void launch_convert(ckks_ctx *c, const BasisDev *bases, const SetLayout &lay, const uint64_t *y,
+static void launch_convert(const ckks_ctx *c, const BasisDev *bases, const SetLayout &lay, const uint64_t *y,
                            const uint32_t *u, const ConvTargets &ct, uint64_t *out, uint32_t maxt, uint32_t sets,
                            uint32_t mmax, hipStream_t s) {
     const uint32_t n = c->n;
@@ -1402,13 +1407,13 @@ static void launch_convert(ckks_ctx *c, const BasisDev *bases, const SetLayout &
         hipLaunchKernelGGL((k_convert_mfma<MODE, 3, true>), grid, dim3(256), 0, s, bases, lay, y, u, ct, out, n);
 }
 
-static int ks_modup(ckks_ctx *c, LevelTables *lt, int B, int l, const uint64_t *d, size_t d_stride, const KsWs &w,
+static int ks_modup(const ckks_ctx *c, const LevelTables *lt, int B, int l, const uint64_t *d, size_t d_stride, const KsWs &w,
                     hipStream_t s) {
     const uint32_t n = c->n, K = c->K, L = c->L, el = l + K, beta = lt->beta;
     int e;
     {  // y = iNTT(d) scaled by [Bhat_i^-1]
         MapBatched m{d, d_stride, w.y, n, (uint32_t)l, lt->d_modup_scale};
-        if ((e = launch_ntt(c, m, B * l, true, s, "ks_intt_modup"))) return e;
+        if ((e = launch_ntt(c, m, B * l, true, s, "ks_intt_modup", w.mp))) return e;
     }
     SetLayout lay_up{(size_t)l * n, (size_t)c->alpha * n, 0, beta, 1};
     {
@@ -1426,7 +1431,7 @@ static int ks_modup(ckks_ctx *c, LevelTables *lt, int B, int l, const uint64_t *
     LAUNCH_CHECK();
     {
         MapExt m{w.ext, n, (uint32_t)l, L, K, beta, c->alpha};
-        if ((e = launch_ntt(c, m, B * beta * el, false, s, "ks_ntt_ext"))) return e;
+        if ((e = launch_ntt(c, m, B * beta * el, false, s, "ks_ntt_ext", w.mp))) return e;
     }
     return CKKS_OK;
 }
@@ -1434,23 +1439,23 @@ static int ks_modup(ckks_ctx *c, LevelTables *lt, int B, int l, const uint64_t *
 // Inner product of sigma_g(ModUp(d)) with the key, then ModDown up to the
 // NTT-domain conversion: leaves the Q-limbs of the accumulators in w.acc and
 // the converted P-part in w.conv; the caller runs the final kernel.
-static Steps one_step(const uint64_t *key, uint32_t g, int B, const uint64_t *seed = nullptr) {
+static Steps one_step(const ckks_swk *key, uint32_t g, int B) {
     Steps st{};
-    st.key[0] = key;
+    st.key[0] = key->data;
     st.g[0] = g;
     st.count = 1;
     st.B = (uint32_t)B;
     st.shared = 0;
-    if (seed) {
+    if (key->seeded) {
         st.seeded = 1;
-        st.root[0] = key_seed_root(*seed);
+        st.root[0] = key_seed_root(key->seed);
     }
     return st;
 }
 
 // Inner product of sigma_g(ModUp(d)) with the keys of a batch of steps:
 // leaves st.count * st.B accumulator pairs in w.acc.
-static int ks_inner(ckks_ctx *c, LevelTables *lt, int l, const uint64_t *d, size_t d_stride, const Steps &st,
+static int ks_inner(const ckks_ctx *c, const LevelTables *lt, int l, const uint64_t *d, size_t d_stride, const Steps &st,
                     const KsWs &w, hipStream_t s) {
     const uint32_t n = c->n, K = c->K, L = c->L, el = l + K, beta = lt->beta;
     const size_t nout = (size_t)st.count * st.B;
@@ -1480,7 +1485,7 @@ static int ks_inner(ckks_ctx *c, LevelTables *lt, int l, const uint64_t *d, size
 // ciphertexts (c0 at x + cb x_stride, c1 one polynomial further): the P-limbs
 // of every step go to w.acc as usual, the Q-limbs are summed over the steps
 // into *nparts partial sums (k_inner_sum2048).
-static int ks_inner_giant(ckks_ctx *c, LevelTables *lt, int l, const uint64_t *x, size_t x_stride, const Steps &st,
+static int ks_inner_giant(const ckks_ctx *c, const LevelTables *lt, int l, const uint64_t *x, size_t x_stride, const Steps &st,
                           const KsWs &w, uint32_t *nparts, hipStream_t s) {
     const uint32_t K = c->K, L = c->L, beta = lt->beta;
     const size_t per = (size_t)l * c->n;
@@ -1508,13 +1513,13 @@ static int ks_inner_giant(ckks_ctx *c, LevelTables *lt, int l, const uint64_t *x
 // With nsum > 1 the conversions of accumulators o + j (nout / nsum), j < nsum,
 // are summed (n = 2048 giant steps) in *nparts partial sums: part p of output
 // o at w.conv pair p (nout / nsum) + o.
-static int ks_moddown_conv(ckks_ctx *c, size_t nout, int l, const KsWs &w, hipStream_t s, uint32_t nsum = 1,
+static int ks_moddown_conv(const ckks_ctx *c, size_t nout, int l, const KsWs &w, hipStream_t s, uint32_t nsum = 1,
                            uint32_t *nparts = nullptr) {
     const uint32_t n = c->n, K = c->K, L = c->L, el = l + K;
     int e;
     {
         MapAccP m{w.acc, n, (uint32_t)l, L, K, c->d_moddown_scale};
-        if ((e = launch_ntt(c, m, (int)(nout * 2 * K), true, s, "ks_intt_moddown"))) return e;
+        if ((e = launch_ntt(c, m, (int)(nout * 2 * K), true, s, "ks_intt_moddown", w.mp))) return e;
     }
     SetLayout lay_dn{(size_t)el * n, 0, (size_t)l * n, 1, 0};
     {
@@ -1539,7 +1544,7 @@ static int ks_moddown_conv(ckks_ctx *c, size_t nout, int l, const KsWs &w, hipSt
     LAUNCH_CHECK();
     if (n != 2048) {
         MapStrided m{w.conv, w.conv, n, (uint32_t)l, 0, nullptr};
-        if ((e = launch_ntt(c, m, (int)(nout * 2 * l), false, s, "ks_ntt_moddown"))) return e;
+        if ((e = launch_ntt(c, m, (int)(nout * 2 * l), false, s, "ks_ntt_moddown", w.mp))) return e;
     }
     return CKKS_OK;
 }
@@ -1548,19 +1553,22 @@ static int ks_moddown_conv(ckks_ctx *c, size_t nout, int l, const KsWs &w, hipSt
 // [0, l0) to the primes [0, lt) (bootstrapping's first step): scaled iNTT of
 // the l0 limbs, exact u, conversion to every target, NTT of the lt limbs.
 size_t ws_bytes_mod_raise(const ckks_ctx *c, int B, int l0) {
-    return (align_words((size_t)2 * B * l0 * c->n) + align_words(((size_t)2 * B * c->n + 1) / 2)) * 8;
+    return (align_words((size_t)2 * B * l0 * c->n) + align_words(((size_t)2 * B * c->n + 1) / 2) +
+            mp_scratch_words(c->n)) * 8;
 }
 
-int op_mod_raise(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l0, int lt, void *ws, hipStream_t s) {
+int op_mod_raise(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l0, int lt, void *ws,
+                 hipStream_t s) {
     int e = CKKS_OK;
-    RaiseTables *rt = raise_tables(c, (uint32_t)l0, &e);
-    if (!rt) return e;
+    const RaiseTables *rt = find_raise(c, (uint32_t)l0);
+    if (!rt) return CKKS_ENOTREADY;
     const uint32_t n = c->n, P = 2 * (uint32_t)B;
     uint64_t *y = (uint64_t *)ws;
     uint32_t *u = (uint32_t *)(y + align_words((size_t)P * l0 * n));
+    uint64_t *mp = y + align_words((size_t)P * l0 * n) + align_words(((size_t)P * n + 1) / 2);
     {
         MapBatched m{in, (size_t)l0 * n, y, n, (uint32_t)l0, rt->d_scale};
-        if ((e = launch_ntt(c, m, (int)(P * l0), true, s, "raise_intt"))) return e;
+        if ((e = launch_ntt(c, m, (int)(P * l0), true, s, "raise_intt", mp))) return e;
     }
     SetLayout lay{(size_t)l0 * n, 0, 0, 1, 0};
     {
@@ -1576,13 +1584,14 @@ int op_mod_raise(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l0, 
     }
     LAUNCH_CHECK();
     MapStrided m2{out, out, n, (uint32_t)lt, 0, nullptr};
-    return launch_ntt(c, m2, (int)(P * lt), false, s, "raise_ntt");
+    return launch_ntt(c, m2, (int)(P * lt), false, s, "raise_ntt", mp);
 }
 
 size_t ws_bytes_relin(const ckks_ctx *c, int B, int l) { return ks_words(c, B, l, nullptr, nullptr) * 8; }
 size_t ws_bytes_rotate(const ckks_ctx *c, int B, int l) { return ks_words(c, B, l, nullptr, nullptr) * 8; }
 size_t ws_bytes_rescale(const ckks_ctx *c, int B, int l) {
-    return (align_words((size_t)B * 2 * c->n) + align_words((size_t)B * 2 * (l - 1) * c->n)) * 8;
+    return (align_words((size_t)B * 2 * c->n) + align_words((size_t)B * 2 * (l - 1) * c->n) +
+            mp_scratch_words(c->n)) * 8;
 }
 
 // Steps per batched key switch inside BSGS: as many as fit a workspace budget.
@@ -1603,11 +1612,11 @@ static size_t bsgs_words(const ckks_ctx *c, int B, int l, int bs, int gs) {
 }
 size_t ws_bytes_bsgs(const ckks_ctx *c, int B, int l, int bs, int gs) { return bsgs_words(c, B, l, bs, gs) * 8; }
 
-int op_mul_tensor_relin(ckks_ctx *c, const uint64_t *a, const uint64_t *b, const uint64_t *rlk, uint64_t *out, int B,
-                        int l, void *ws, hipStream_t s, const uint64_t *seed) {
+int op_mul_tensor_relin(const ckks_ctx *c, const uint64_t *a, const uint64_t *b, const ckks_swk *rlk, uint64_t *out,
+                        int B, int l, void *ws, hipStream_t s) {
     int e = CKKS_OK;
-    LevelTables *lt = level_tables(c, l, &e);
-    if (!lt) return e;
+    const LevelTables *lt = find_level(c, l);
+    if (!lt) return CKKS_ENOTREADY;
     KsWs w;
     ks_words(c, B, l, &w, (uint64_t *)ws);
     const uint32_t n = c->n;
@@ -1618,7 +1627,7 @@ int op_mul_tensor_relin(ckks_ctx *c, const uint64_t *a, const uint64_t *b, const
     }
     LAUNCH_CHECK();
     const size_t per = (size_t)l * n;
-    const Steps st = one_step(rlk, 1, B, seed);
+    const Steps st = one_step(rlk, 1, B);
     if ((e = ks_modup(c, lt, B, l, w.d, per, w, s))) return e;
     if ((e = ks_inner(c, lt, l, w.d, per, st, w, s))) return e;
     if ((e = ks_moddown_conv(c, B, l, w, s))) return e;
@@ -1637,7 +1646,7 @@ int op_mul_tensor_relin(ckks_ctx *c, const uint64_t *a, const uint64_t *b, const
 }
 
 // Final kernel of a batch of rotations: out[cb] (+)= (acc - conv) P^-1 + (sigma_g(c0), 0).
-static int rotate_final(ckks_ctx *c, const uint64_t *in, uint64_t *out, int l, const Steps &st, const KsWs &w,
+static int rotate_final(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int l, const Steps &st, const KsWs &w,
                         bool accumulate, hipStream_t s) {
     const size_t nout = (size_t)st.count * st.B;
     const size_t tot = nout * 2 * l * c->n;
@@ -1664,16 +1673,16 @@ static int rotate_final(ckks_ctx *c, const uint64_t *in, uint64_t *out, int l, c
 
 // Rotation: ModUp of c1 as stored (no permuted copy), the automorphism applied
 // as a gather of the extended digits inside the key inner product.
-int op_rotate(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, uint32_t g, const uint64_t *key, void *ws,
-              bool accumulate, hipStream_t s, const uint64_t *seed) {
+int op_rotate(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, uint32_t g, const ckks_swk *key,
+              void *ws, bool accumulate, hipStream_t s) {
     int e = CKKS_OK;
-    LevelTables *lt = level_tables(c, l, &e);
-    if (!lt) return e;
+    const LevelTables *lt = find_level(c, l);
+    if (!lt) return CKKS_ENOTREADY;
     KsWs w;
     ks_words(c, B, l, &w, (uint64_t *)ws);
     const size_t per = (size_t)l * c->n;
     const uint64_t *c1 = in + per;
-    const Steps st = one_step(key, g, B, seed);
+    const Steps st = one_step(key, g, B);
     if ((e = ks_modup(c, lt, B, l, c1, 2 * per, w, s))) return e;
     if ((e = ks_inner(c, lt, l, c1, 2 * per, st, w, s))) return e;
     if ((e = ks_moddown_conv(c, B, l, w, s))) return e;
@@ -1696,26 +1705,27 @@ __global__ void k_key_expand(const uint64_t *__restrict__ kb, uint64_t *__restri
     }
 }
 
-int op_key_expand(ckks_ctx *c, const uint64_t *key_b, uint64_t seed, uint64_t *key_out, hipStream_t s) {
+int op_key_expand(const ckks_ctx *c, const ckks_swk *key, uint64_t *key_out, hipStream_t s) {
     const uint32_t tot = c->L + c->K;
     const size_t total = (size_t)c->dnum * tot * c->n;
-    hipLaunchKernelGGL(k_key_expand, grid_for(total), dim3(256), 0, s, key_b, key_out, c->d_pc, c->n, tot,
-                       key_seed_root(seed), total);
+    hipLaunchKernelGGL(k_key_expand, grid_for(total), dim3(256), 0, s, key->data, key_out, c->d_pc, c->n, tot,
+                       key_seed_root(key->seed), total);
     LAUNCH_CHECK();
     return CKKS_OK;
 }
 
-int op_rescale(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, void *ws, hipStream_t s) {
+int op_rescale(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, void *ws, hipStream_t s) {
     int e = CKKS_OK;
-    LevelTables *lt = level_tables(c, l, &e);
-    if (!lt) return e;
+    const LevelTables *lt = find_level(c, l);
+    if (!lt) return CKKS_ENOTREADY;
     const uint32_t n = c->n;
     uint64_t *t = (uint64_t *)ws;
     uint64_t *r = t + align_words((size_t)B * 2 * n);
+    uint64_t *mp = r + align_words((size_t)B * 2 * (l - 1) * n);
     // t[b][c] = iNTT(in[b][c][l-1])
     {
         MapLast ml{in, t, n, (uint32_t)l};
-        if ((e = launch_ntt(c, ml, B * 2, true, s, "rescale_intt"))) return e;
+        if ((e = launch_ntt(c, ml, B * 2, true, s, "rescale_intt", mp))) return e;
     }
     size_t tot = (size_t)B * 2 * (l - 1) * n;
     if (n == 2048) {
@@ -1732,7 +1742,7 @@ int op_rescale(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, voi
     LAUNCH_CHECK();
     {
         MapStrided m{r, r, n, (uint32_t)(l - 1), 0, nullptr};
-        if ((e = launch_ntt(c, m, B * 2 * (l - 1), false, s, "rescale_ntt"))) return e;
+        if ((e = launch_ntt(c, m, B * 2 * (l - 1), false, s, "rescale_ntt", mp))) return e;
     }
     {
         ProfScope ps_(c, "rescale_final", s);
@@ -1751,8 +1761,8 @@ static uint32_t rot_elt(uint32_t n, uint64_t k) {
     return (uint32_t)r;
 }
 
-int op_bsgs(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, const uint64_t *diags, int bs, int gs,
-            const uint64_t *const *baby, const uint64_t *const *giant, bool rescale, void *ws, hipStream_t s) {
+int op_bsgs(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, const uint64_t *diags, int bs, int gs,
+            const ckks_swk *const *baby, const ckks_swk *const *giant, bool rescale, void *ws, hipStream_t s) {
     const size_t ct = (size_t)B * 2 * l * c->n;
     const size_t per = (size_t)l * c->n;
     const int sc = bsgs_chunk(c, B, l, bs, gs);
@@ -1761,8 +1771,8 @@ int op_bsgs(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, const 
     uint64_t *ksws = inner + align_words(ct * gs);
     uint64_t *rsws = ksws + ks_words(c, sc * B, l, nullptr, nullptr);
     int e = CKKS_OK;
-    LevelTables *lt = level_tables(c, l, &e);
-    if (!lt) return e;
+    const LevelTables *lt = find_level(c, l);
+    if (!lt) return CKKS_ENOTREADY;
     KsWs w;
     ks_words(c, sc * B, l, &w, ksws);
     if (bs > 1) {
@@ -1774,7 +1784,7 @@ int op_bsgs(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, const 
             st.B = (uint32_t)B;
             st.shared = 1;
             for (uint32_t j = 0; j < st.count; j++) {
-                st.key[j] = baby[b0 + j];
+                st.key[j] = baby[b0 + j]->data;
                 st.g[j] = rot_elt(c->n, b0 + j);
             }
             if ((e = ks_inner(c, lt, l, in + per, 2 * per, st, w, s))) return e;
@@ -1799,7 +1809,7 @@ int op_bsgs(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, const 
         st.B = (uint32_t)B;
         st.shared = 0;
         for (uint32_t j = 0; j < st.count; j++) {
-            st.key[j] = giant[g0 + j];
+            st.key[j] = giant[g0 + j]->data;
             st.g[j] = rot_elt(c->n, (uint64_t)(g0 + j) * bs);
         }
         const uint64_t *src = inner + (size_t)g0 * ct;  // ciphertexts (g0 + j, b), consecutive
@@ -1815,7 +1825,7 @@ int op_bsgs(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, const 
             LAUNCH_CHECK();
         } else {
             for (uint32_t j = 0; j < st.count; j++)
-                if ((e = op_rotate(c, src + (size_t)j * ct, inner, B, l, st.g[j], st.key[j], ksws, true, s)))
+                if ((e = op_rotate(c, src + (size_t)j * ct, inner, B, l, st.g[j], giant[g0 + j], ksws, true, s)))
                     return e;
         }
     }

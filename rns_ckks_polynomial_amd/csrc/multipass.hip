@@ -50,11 +50,13 @@ int multipass_init(ckks_ctx *c) {
         return e;
     if (hipMalloc((void **)&mp->d_scratch, (size_t)MP_CHUNK * n * 8) != hipSuccess) return CKKS_ENOMEM;
     mp->owned.push_back(mp->d_scratch);
+    if (hipEventCreateWithFlags(&mp->scratch_done, hipEventDisableTiming) != hipSuccess) return CKKS_EHIP;
     return CKKS_OK;
 }
 
 void multipass_free(ckks_ctx *c) {
     if (!c->mp) return;
+    if (c->mp->scratch_done) (void)hipEventDestroy(c->mp->scratch_done);
     for (void *p : c->mp->owned) (void)hipFree(p);
     delete c->mp;
     c->mp = nullptr;

@@ -232,26 +232,40 @@ __global__ __launch_bounds__(256) void k_inv_cols(Map map, uint32_t limb0, const
 }  // namespace mp
 
 template <class Map>
-int multipass_ntt(const ckks_ctx *c, const Map &map, int nblk, bool inverse, hipStream_t s) {
+static int multipass_launch(const ckks_ctx *c, const Map &map, int nblk, bool inverse, hipStream_t s,
+                            uint64_t *scratch) {
     const MultipassPlan *p = c->mp;
-    if (!p) return CKKS_EUNSUPPORTED;
     const dim3 blk(256);
     for (int l0 = 0; l0 < nblk; l0 += MP_CHUNK) {
         const dim3 grid(MP_N1 / mp::V, (unsigned)std::min<int>(MP_CHUNK, nblk - l0));
         if (!inverse) {
             hipLaunchKernelGGL(mp::k_fwd_cols<Map>, grid, blk, 0, s, map, (uint32_t)l0, c->d_pc, p->d_tw256f,
-                               p->d_cross, p->d_scratch);
+                               p->d_cross, scratch);
             hipLaunchKernelGGL(mp::k_fwd_rows<Map>, grid, blk, 0, s, map, (uint32_t)l0, c->d_pc, p->d_tw256f,
-                               (const uint64_t *)p->d_scratch);
+                               (const uint64_t *)scratch);
         } else {
             hipLaunchKernelGGL(mp::k_inv_rows<Map>, grid, blk, 0, s, map, (uint32_t)l0, c->d_pc, p->d_tw256i,
-                               p->d_crossinvT, p->d_scratch);
+                               p->d_crossinvT, scratch);
             hipLaunchKernelGGL(mp::k_inv_cols<Map>, grid, blk, 0, s, map, (uint32_t)l0, c->d_pc, p->d_tw256i,
-                               (const uint64_t *)p->d_scratch);
+                               (const uint64_t *)scratch);
         }
         if (hipGetLastError() != hipSuccess) return CKKS_EHIP;
     }
     return CKKS_OK;
+}
+
+// scratch: the caller's transpose buffer of mp_scratch_words(n) words, or null for
+// the context's, whose users wait for the previous user's event on their stream.
+template <class Map>
+int multipass_ntt(const ckks_ctx *c, const Map &map, int nblk, bool inverse, hipStream_t s, uint64_t *scratch) {
+    MultipassPlan *p = c->mp;
+    if (!p) return CKKS_EUNSUPPORTED;
+    if (scratch) return multipass_launch(c, map, nblk, inverse, s, scratch);
+    std::lock_guard<std::mutex> g(p->scratch_mu);
+    if (hipStreamWaitEvent(s, p->scratch_done, 0) != hipSuccess) return CKKS_EHIP;
+    const int e = multipass_launch(c, map, nblk, inverse, s, p->d_scratch);
+    if (hipEventRecord(p->scratch_done, s) != hipSuccess) return CKKS_EHIP;
+    return e;
 }
 
 }  // namespace ckks

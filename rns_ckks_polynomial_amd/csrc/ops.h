@@ -16,19 +16,19 @@ size_t ws_bytes_rotate(const ckks_ctx *c, int B, int l);
 size_t ws_bytes_rescale(const ckks_ctx *c, int B, int l);
 size_t ws_bytes_bsgs(const ckks_ctx *c, int B, int l, int bs, int gs);
 
-// seed: null for a stored key [dnum][2][L + K][n]; else the key holds its b rows
-// only ([dnum][L + K][n]) and its a rows are regenerated from *seed.
-int op_mul_tensor_relin(ckks_ctx *c, const uint64_t *a, const uint64_t *b, const uint64_t *rlk, uint64_t *out, int B,
-                        int l, void *ws, hipStream_t s, const uint64_t *seed = nullptr);
-int op_rescale(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, void *ws, hipStream_t s);
-int op_rotate(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, uint32_t g, const uint64_t *key, void *ws,
-              bool accumulate, hipStream_t s, const uint64_t *seed = nullptr);
-int op_key_expand(ckks_ctx *c, const uint64_t *key_b, uint64_t seed, uint64_t *key_out, hipStream_t s);
-int op_bsgs(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, const uint64_t *diags, int bs, int gs,
-            const uint64_t *const *baby, const uint64_t *const *giant, bool rescale, void *ws, hipStream_t s);
+// Keys are validated descriptors (stored, or seeded where the caller allows it).
+// Every op returns CKKS_ENOTREADY when a level it needs was not prepared.
+int op_mul_tensor_relin(const ckks_ctx *c, const uint64_t *a, const uint64_t *b, const ckks_swk *rlk, uint64_t *out,
+                        int B, int l, void *ws, hipStream_t s);
+int op_rescale(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, void *ws, hipStream_t s);
+int op_rotate(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, uint32_t g, const ckks_swk *key,
+              void *ws, bool accumulate, hipStream_t s);
+int op_key_expand(const ckks_ctx *c, const ckks_swk *key, uint64_t *key_out, hipStream_t s);
+int op_bsgs(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, const uint64_t *diags, int bs, int gs,
+            const ckks_swk *const *baby, const ckks_swk *const *giant, bool rescale, void *ws, hipStream_t s);
 // ModRaise: centered lift of [B][2][l0][n] (primes [0, l0)) to [B][2][lt][n].
 size_t ws_bytes_mod_raise(const ckks_ctx *c, int B, int l0);
-int op_mod_raise(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l0, int lt, void *ws, hipStream_t s);
+int op_mod_raise(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l0, int lt, void *ws, hipStream_t s);
 // out = ma a + mb b' (+ add on c0) on limbs [0, lo) of B ciphertexts; b' = b X^(n/2) if mono_b.
 int op_lincomb(const ckks_ctx *c, uint64_t *out, int lo, const uint64_t *a, int la, const uint64_t *b, int lb,
                int64_t ma, int64_t mb, int64_t add, bool mono_b, int B, hipStream_t s);
@@ -37,13 +37,13 @@ int64_t enc_const(double c, double t, bool *ok);
 // EvalMod (Chebyshev cosine + double angles); levels consumed = eval_mod_depth(degree, double_angles).
 int eval_mod_depth(int degree, int double_angles);
 size_t ws_bytes_eval_mod(const ckks_ctx *c, int B, int l, int degree);
-int op_eval_mod(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, double scale_in, const double *cheb,
-                int degree, double bound_k, int double_angles, double out_factor, const uint64_t *rlk, void *ws,
+int op_eval_mod(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, double scale_in, const double *cheb,
+                int degree, double bound_k, int double_angles, double out_factor, const ckks_swk *rlk, void *ws,
                 double *scale_out, int *level_out, hipStream_t s);
 // Bootstrapping: ModRaise -> CtS -> conj_extract -> EvalMod (re, im) -> merge -> StC.
 int boot_levels(const ckks_boot_params *p, int *l_out);
 size_t ws_bytes_bootstrap(const ckks_ctx *c, int B, int l0, const ckks_boot_params *p);
-int op_bootstrap(ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l0, const ckks_boot_params *p,
+int op_bootstrap(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l0, const ckks_boot_params *p,
                  void *ws, double *scale_mid, hipStream_t s);
 int op_fill_uniform(const ckks_ctx *c, uint64_t *dst, int count, int first, int nlimbs, uint64_t seed, uint64_t tag,
                     uint64_t stream0, hipStream_t s);

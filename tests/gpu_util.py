@@ -39,7 +39,7 @@ def mismatch(a, b) -> str:
     if a.shape != b.shape:
         return f"shape {a.shape} vs {b.shape}"
     bad = np.argwhere(a != b)
-    return f"{len(bad)} mismatches, first at {tuple(bad[0]) if len(bad) else None}"
+    return f"{len(bad)} mismatches, first at {tuple(int(v) for v in bad[0]) if len(bad) else None}"
 
 
 def gfill(g, shape, seed, tag, stream0=0, first_prime=0):

@@ -121,12 +121,55 @@ def test_ring65536_l40_relin_rotations_rescale():
     assert np.array_equal(ph[3], o.mul_tensor_relin(a3, b3, rl, l))
 
 
+def test_ring65536_two_streams():
+    """Two streams at n = 65536 at once, each with its own workspace: a rotation
+    + rescale on one, a bare NTT round trip and a relinearisation on the other.
+    The four-step NTT's transpose buffer comes from each call's workspace (the
+    bare NTT calls share the context's, ordered by an event), so neither
+    stream's results may depend on the other's."""
+    g, o = gpu_ctx(*C5), oracle_ctx(*C5)
+    l, n, tot = 40, 65536, 48
+    seed = 0xC0DE0015
+    x = gfill(g, (1, 2, l, n), seed, synth.TAG_CT)
+    y = gfill(g, (1, 2, l, n), seed + 1, synth.TAG_CT)
+    z = gfill(g, (2, l, n), seed + 2, synth.TAG_POLY)
+    key = gfill(g, (5, 2, tot, n), seed, synth.TAG_KEY)
+    wa = torch.empty(g.workspace_size("rotate", 1, l) // 8 + 1, dtype=torch.uint64, device="cuda")
+    wr = torch.empty(g.workspace_size("rescale", 1, l) // 8 + 1, dtype=torch.uint64, device="cuda")
+    wb = torch.empty(g.workspace_size("relin", 1, l) // 8 + 1, dtype=torch.uint64, device="cuda")
+    rot, prod = torch.empty_like(x), torch.empty_like(x)
+    zt = z.clone()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    say("n=65536 two streams: GPU")
+    ge = galois_rot(n, 5)
+    for _ in range(2):  # the second round overlaps the first's tail
+        with torch.cuda.stream(sa):
+            g.rotate(x, ge, key, out=rot, ws=wa)
+            res = g.rescale(rot, ws=wr)
+        with torch.cuda.stream(sb):
+            g.ntt_fwd(zt)
+            g.mul_tensor_relin(x, y, key, out=prod, ws=wb)
+            g.ntt_inv(zt)
+    torch.cuda.synchronize()
+    say("n=65536 two streams: oracle")
+    xc = cfill(o, seed, synth.TAG_CT, 2, l).reshape(2, l, n)
+    yc = cfill(o, seed + 1, synth.TAG_CT, 2, l).reshape(2, l, n)
+    kc = cfill(o, seed, synth.TAG_KEY, 10, tot).reshape(5, 2, tot, n)
+    ref_rot = o.rotate(xc, ge, kc, l)
+    assert np.array_equal(host(rot)[0], ref_rot), mismatch(host(rot)[0], ref_rot)
+    assert np.array_equal(host(res)[0], o.rescale(ref_rot, l))
+    assert np.array_equal(host(prod)[0], o.mul_tensor_relin(xc, yc, kc, l))
+    assert np.array_equal(host(zt), host(z))
+
+
 C4 = (2048, 2100, 263, 8)
 
 
 def test_chain2100_keyswitch_ops():
     """Rotation (2100 primes), conjugation (2099), relinearisation (2084: partial last digit), rescale."""
     g, o = gpu_ctx(*C4), oracle_ctx(*C4)
+    g.prepare_levels(2084, 2100)  # a 2100-prime chain prepares its top level only
     n, tot = 2048, 2363
     seed = 0xC0DE0004
     key = gfill(g, (8, 2, tot, n), seed, synth.TAG_KEY)

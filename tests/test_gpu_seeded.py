@@ -1,6 +1,6 @@
-"""GPU seed-expanded switching keys (ckks_key_expand, ckks_rotate_seeded,
-ckks_mul_tensor_relin_seeded): the expanded a rows equal the input generator's
-(oracle seeded_keys.seeded_key_a) bit for bit, and a seeded key switch equals the oracle's
+"""GPU seed-expanded switching keys (ckks_key_expand, and ckks_rotate /
+ckks_mul_tensor_relin given a seeded key descriptor): the expanded a rows equal
+the oracle's (oracle/seeded_keys.py) bit for bit, and a seeded key switch equals the oracle's
 key switch with the expanded key on every residue, at n = 2048 (LDS inner
 product) and n = 65536 (generic inner product), plus a decrypt check with a
 real seeded Galois key."""
@@ -95,7 +95,7 @@ def test_seeded_rejects_bad_arguments():
     g, o = gpu_ctx(*LAY), oracle_ctx(*LAY)
     x = dev(_cts(o, 1, 1, 8))
     short = dev(np.zeros((o.dnum, o.L + o.K - 1, o.n), dtype=np.uint64))
-    with pytest.raises(ValueError, match="key_b"):
+    with pytest.raises(ValueError, match="seeded key"):
         g.rotate_seeded(x, galois_rot(o.n, 1), short, 1)
     kb = dev(_key_b(o, 2))
     with pytest.raises(Exception, match="invalid"):   # even Galois element
