@@ -189,6 +189,19 @@ int ckks_rotate(const ckks_ctx *ctx, const uint64_t *in, uint64_t *out, int batc
  * must not overlap the key's data. */
 int ckks_key_expand(const ckks_ctx *ctx, const ckks_swk *seeded_key, uint64_t *key_out, void *stream);
 
+/* Rotation for callers that cannot allocate device memory (code under stream
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation, arguments and errors as ckks_rotate, with no workspace argument.
+ * Its workspace is a device array of CKKS_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, held until the process ends; a call needing more
+ * (ckks_workspace_size with CKKS_OP_ROTATE) returns CKKS_EWORKSPACE.  All
+ * calls on one GPU share that array: calls that overlap on a GPU (other
+ * streams, other threads, other contexts) race, so the caller serialises
+ * them. */
+#define CKKS_NOALLOC_SCRATCH_BYTES (256ull << 20)
+int ckks_rotate_noalloc(const ckks_ctx *ctx, const uint64_t *in, uint64_t *out, int batch, int level,
+                        uint32_t galois_elt, const ckks_swk *key, void *stream);
+
 /* Baby-step giant-step plaintext-matrix x ciphertext (matmul2 with BB x GG,
  * Kestrel article technique table and section 4.4; coeff_to_slot /
  * slot_to_coeff are this transform):

@@ -69,6 +69,8 @@ SIGNATURES = {
     "ckks_rotate": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_uint32, C.POINTER(Swk),
                               C.c_void_p, C.c_size_t, C.c_void_p]),
     "ckks_key_expand": (C.c_int, [C.c_void_p, C.POINTER(Swk), C.c_void_p, C.c_void_p]),
+    "ckks_rotate_noalloc": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_uint32,
+                                      C.POINTER(Swk), C.c_void_p]),
     "ckks_bsgs_linear_transform": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p,
                                              C.c_int, C.c_int, C.POINTER(C.c_void_p), C.POINTER(C.c_void_p),
                                              C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),

@@ -176,6 +176,15 @@ class Context:
                                         ws.numel() * 8, _stream()), "ckks_rotate")
         return out
 
+    def rotate_noalloc(self, x, galois_elt: int, key, out=None):
+        """ckks_rotate_noalloc: ckks_rotate with the library's device array as workspace."""
+        B, _, l, n = x.shape
+        out = torch.empty_like(x) if out is None else out
+        k = self._swk(key)
+        nat.check(nat.lib().ckks_rotate_noalloc(self._h, _ptr(x), self._cts(out, B, l, "out"), B, l, galois_elt,
+                                                C.byref(k), _stream()), "ckks_rotate_noalloc")
+        return out
+
     def mul_tensor_relin_seeded(self, a, b, rlk_b, rlk_seed: int, out=None, ws=None):
         """Relinearisation with the key given as its b rows + seed (a seeded ckks_swk)."""
         return self.mul_tensor_relin(a, b, self.key(rlk_b, seeded=True, seed=rlk_seed), out=out, ws=ws)

@@ -7,6 +7,7 @@
 
 #include "ctx_internal.h"
 #include "multipass.h"
+#include "ops.h"
 
 namespace ckks {
 
@@ -209,6 +210,7 @@ extern "C" int ckks_ctx_create(ckks_ctx **out, const ckks_params *params, int de
         }
     }
     if (!err && n > 2048) err = multipass_init(c);
+    if (!err) err = noalloc_init(device);
     if (!err && p.L <= CKKS_PREPARE_ALL_MAX_L) {  // short chains: every level up front
         for (uint32_t l = 1; l <= p.L && !err; l++) err = prepare_level(c, l);
         for (uint32_t l = 1; l <= p.L && l <= 1000 && !err; l++) err = prepare_raise(c, l);

@@ -45,6 +45,9 @@ int boot_levels(const ckks_boot_params *p, int *l_out);
 size_t ws_bytes_bootstrap(const ckks_ctx *c, int B, int l0, const ckks_boot_params *p);
 int op_bootstrap(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l0, const ckks_boot_params *p,
                  void *ws, double *scale_mid, hipStream_t s);
+// Look up (once per device, with that device current) the device address of the
+// no-allocation workspace array.
+int noalloc_init(int device);
 int op_fill_uniform(const ckks_ctx *c, uint64_t *dst, int count, int first, int nlimbs, uint64_t seed, uint64_t tag,
                     uint64_t stream0, hipStream_t s);
 
