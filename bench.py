@@ -87,6 +87,9 @@ def parse():
                    help="only time the bootstrap of 8 ciphertexts on the 2100 + 263 prime chain "
                         "(19 -> 2100 -> 2083 primes; about 160 GB of HBM)")
     p.add_argument("--boot-reps", type=int, default=2)
+    p.add_argument("--c4-only", action="store_true",
+                   help="only the 2100-prime coeff_to_slot / slot_to_coeff leg (profiler runs of it)")
+    p.add_argument("--c4-reps", type=int, default=3)
     p.add_argument("--no-c4", action="store_true",
                    help="skip the 2100-prime coeff_to_slot / slot_to_coeff leg (about 150 GB of HBM)")
     p.add_argument("--step-only", action="store_true",
@@ -538,6 +541,13 @@ def main():
         sys.exit(2)
     if args.boot_chain2100:
         boot_chain2100(args)
+        return
+    if args.c4_only:
+        import torch
+        r = c4_timing(torch, args.c4_reps)
+        print(json.dumps({"metric": "BSGS 32x32 linear transforms/s at 2100 primes", "unit": "linear-transforms/s",
+                          "value": r["coeff_to_slot"]["linear_transforms_per_s"], "n_gpus": 1, "dtype": "u64",
+                          "data": "synthetic", "config": {"workload": r["config"]}, "c4": r}))
         return
     import torch
 

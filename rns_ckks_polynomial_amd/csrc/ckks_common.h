@@ -48,6 +48,15 @@ __device__ __forceinline__ uint64_t shoup_lazy4(uint64_t y, uint64_t w, uint64_t
     return ((uint64_t)hi << 32) | (uint32_t)r;
 }
 
+// x mod q for x < 2^64 - 2^59 with q in (2^59, 2^59 + 2^52) (every chain prime): x >> 59 is
+// floor(x / q) or one more, so x - (x >> 59) q lies in [-q, q) and one conditional add of q
+// finishes.  nq = 2^64 - q.
+__device__ __forceinline__ uint64_t reduce59(uint64_t x, uint64_t q, uint64_t nq) {
+    const uint32_t qt = (uint32_t)(x >> 59);
+    const int64_t r = (int64_t)(x + (uint64_t)qt * nq);
+    return r < 0 ? (uint64_t)r + q : (uint64_t)r;
+}
+
 // x - c if x >= c else x, for x, c < 2^63 with |x - c| < 2^63 (nc = 2^64 - c): add, then select on the sign.
 __device__ __forceinline__ uint64_t csub_sign(uint64_t x, uint64_t nc) {
     const uint64_t m = x + nc;

@@ -16,8 +16,8 @@
 // Twiddles are Shoup pairs (w, floor(w 2^64/q)) of psi^bitrev(k) (forward) and
 // psi^-bitrev(k) (inverse), interleaved [k][2].  Butterflies are Harvey's lazy
 // forms with a truncated Shoup quotient (see shoup_lazy4): the twiddle product
-// lands in [0, 4q), so values stay in [0, 8q) (forward) or [0, 4q) (inverse),
-// all below 2^63 for q < 2^60.
+// lands in [0, 4q); the forward transform reduces its top inputs only every
+// third stage (values below 28q < 2^64), the inverse keeps them below 4q.
 #pragma once
 #include "ckks_common.h"
 
@@ -41,41 +41,53 @@ __device__ __forceinline__ int own(int t, int k) {
 
 __device__ __forceinline__ int brev(int i) { return (int)(__builtin_bitreverse32((uint32_t)i) >> (32 - LOGN)); }
 
-// Per-prime constants of the butterflies.  -4q passes through an empty asm so
-// that x - 4q stays one 64-bit add (v_lshl_add_u64) instead of being turned
-// back into a subtract with borrow.
+// Per-prime constants of the butterflies.  The negated thresholds pass through an
+// empty asm so that x - c stays one 64-bit add (v_lshl_add_u64) instead of being
+// turned back into a subtract with borrow.
 struct BfConsts {
-    uint64_t q, q4, nq4;
+    uint64_t q, q4, n4, n8, n16;
 };
 __device__ __forceinline__ BfConsts bf_consts(uint64_t q) {
-    BfConsts c{q, 4 * q, 0 - 4 * q};
-    asm volatile("" : "+v"(c.nq4));
+    BfConsts c{q, 4 * q, 0 - 4 * q, 0 - 8 * q, 0 - 16 * q};
+    asm volatile("" : "+v"(c.n4));
+    asm volatile("" : "+v"(c.n8));
+    asm volatile("" : "+v"(c.n16));
     return c;
 }
 
+// x - c if x >= c else x (nc = 2^64 - c): one add, one unsigned compare, a select.
+__device__ __forceinline__ uint64_t csub_n(uint64_t x, uint64_t c, uint64_t nc) {
+    const uint64_t m = x + nc;
+    return x >= c ? m : x;
+}
+
+// Cooley-Tukey butterfly (x, y) -> (a + t, a + 4q - t), a = x reduced by RED (0: as is,
+// else x - RED q when x >= RED q), t = y w in [0, 4q).  Without a reduction the bound of
+// the outputs grows by 4q per stage, so the forward transform reduces only where its
+// bounds require (see fwd).
+template <int RED>
 __device__ __forceinline__ void bf_ct(uint64_t &x, uint64_t &y, uint64_t w, uint64_t wp, const BfConsts &c) {
-    const uint64_t a = csub_sign(x, c.nq4);           // [0, 4q)
-    const uint64_t t = shoup_lazy4(y, w, wp, 0 - c.q); // [0, 4q)
-    x = a + t;                                        // [0, 8q)
-    y = a + c.q4 - t;                                 // (0, 8q)
+    uint64_t a = x;
+    if (RED == 4) a = csub_n(x, c.q4, c.n4);
+    if (RED == 8) a = csub_n(x, 2 * c.q4, c.n8);
+    if (RED == 16) a = csub_n(x, 4 * c.q4, c.n16);
+    const uint64_t t = shoup_lazy4(y, w, wp, 0 - c.q);  // [0, 4q)
+    x = a + t;
+    y = a + c.q4 - t;
 }
 
 __device__ __forceinline__ void bf_gs(uint64_t &x, uint64_t &y, uint64_t w, uint64_t wp, const BfConsts &c) {
     const uint64_t s = x + y;                         // [0, 8q)
     const uint64_t d = x + c.q4 - y;                  // (0, 8q)
-    x = csub_sign(s, c.nq4);                          // [0, 4q)
+    x = csub_n(s, c.q4, c.n4);                        // [0, 4q)
     y = shoup_lazy4(d, w, wp, 0 - c.q);               // [0, 4q)
 }
 
-// [0, 8q) -> [0, q): the forward transform's outputs fully reduced.
-__device__ __forceinline__ uint64_t reduce8(uint64_t x, uint64_t q) {
-    x = x >= 4 * q ? x - 4 * q : x;
-    x = x >= 2 * q ? x - 2 * q : x;
-    return x >= q ? x - q : x;
-}
+// The forward transform's outputs ([0, 24q)) fully reduced.
+__device__ __forceinline__ uint64_t reduce_out(uint64_t x, uint64_t q) { return reduce59(x, q, 0 - q); }
 
 // One radix-2 stage (bit BIT of the index) on the 8 registers of a pass owning bits [C, C+3).
-template <int C, int BIT, bool INV>
+template <int C, int BIT, bool INV, int RED = 4>
 __device__ __forceinline__ void stage(uint64_t (&v)[E], int t, const uint64_t *__restrict__ tw, const BfConsts &q) {
     constexpr int s = LOGN - 1 - BIT;  // stage number in the Cooley-Tukey order
     constexpr int kb = 1 << (BIT - C);
@@ -86,7 +98,7 @@ __device__ __forceinline__ void stage(uint64_t (&v)[E], int t, const uint64_t *_
         const int ti = (1 << s) + (j >> (LOGN - s));
         const uint64_t w = tw[2 * ti], wp = tw[2 * ti + 1];
         if (INV) bf_gs(v[k], v[k | kb], w, wp, q);
-        else bf_ct(v[k], v[k | kb], w, wp, q);
+        else bf_ct<RED>(v[k], v[k | kb], w, wp, q);
     }
 }
 
@@ -102,32 +114,35 @@ __device__ __forceinline__ void from_lds(const uint64_t *lds, uint64_t (&v)[E], 
 }
 
 // Forward NTT.  On entry v[k] = a[t + 256 k] (natural order, values < 8q);
-// on exit v[k] = A[t + 256 k] in [0, 8q) (reduce8 finishes).  Uses lds[LDS_WORDS]; ends with a barrier.
+// on exit v[k] = A[t + 256 k] in [0, 24q) (reduce_out finishes).  Uses lds[LDS_WORDS]; ends with a barrier.
+// Bounds: a stage without reduction maps inputs below B q to outputs below (B + 4) q; the
+// top input is reduced at the first stage of each register pass (below 4q, 8q, 16q, 16q),
+// so no value reaches 28q and a + 4q stays below 2^64 (28 q < 2^64 for every chain prime).
 __device__ __forceinline__ void fwd(uint64_t (&v)[E], uint64_t *lds, const uint64_t *__restrict__ tw, uint64_t qv) {
     const int t = threadIdx.x;
     const BfConsts q = bf_consts(qv);
-    stage<8, 10, false>(v, t, tw, q);
-    stage<8, 9, false>(v, t, tw, q);
-    stage<8, 8, false>(v, t, tw, q);
+    stage<8, 10, false, 4>(v, t, tw, q);   // a < 4q,  outputs < 8q
+    stage<8, 9, false, 0>(v, t, tw, q);    //          < 12q
+    stage<8, 8, false, 0>(v, t, tw, q);    //          < 16q
     to_lds<8>(lds, v, t);
     __syncthreads();
     from_lds<5>(lds, v, t);
-    stage<5, 7, false>(v, t, tw, q);
-    stage<5, 6, false>(v, t, tw, q);
-    stage<5, 5, false>(v, t, tw, q);
+    stage<5, 7, false, 8>(v, t, tw, q);    // a < 8q,  < 12q
+    stage<5, 6, false, 0>(v, t, tw, q);    //          < 16q
+    stage<5, 5, false, 0>(v, t, tw, q);    //          < 20q
     __syncthreads();
     to_lds<5>(lds, v, t);
     __syncthreads();
     from_lds<2>(lds, v, t);
-    stage<2, 4, false>(v, t, tw, q);
-    stage<2, 3, false>(v, t, tw, q);
-    stage<2, 2, false>(v, t, tw, q);
+    stage<2, 4, false, 16>(v, t, tw, q);   // a < 16q, < 20q
+    stage<2, 3, false, 0>(v, t, tw, q);    //          < 24q
+    stage<2, 2, false, 0>(v, t, tw, q);    //          < 28q
     __syncthreads();
     to_lds<2>(lds, v, t);
     __syncthreads();
     from_lds<0>(lds, v, t);
-    stage<0, 1, false>(v, t, tw, q);
-    stage<0, 0, false>(v, t, tw, q);
+    stage<0, 1, false, 16>(v, t, tw, q);   // a < 16q, < 20q
+    stage<0, 0, false, 0>(v, t, tw, q);    //          < 24q
     __syncthreads();
     // coefficient own<0>(t,k) = 8t + k now holds A_{brev(8t+k)}: write back in natural order
 #pragma unroll
