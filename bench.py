@@ -90,6 +90,8 @@ def parse():
     p.add_argument("--c4-only", action="store_true",
                    help="only the 2100-prime coeff_to_slot / slot_to_coeff leg (profiler runs of it)")
     p.add_argument("--c4-reps", type=int, default=3)
+    p.add_argument("--ring-only", action="store_true",
+                   help="only the ring-65536 leg (profiler runs of it)")
     p.add_argument("--no-c4", action="store_true",
                    help="skip the 2100-prime coeff_to_slot / slot_to_coeff leg (about 150 GB of HBM)")
     p.add_argument("--step-only", action="store_true",
@@ -541,6 +543,13 @@ def main():
         sys.exit(2)
     if args.boot_chain2100:
         boot_chain2100(args)
+        return
+    if args.ring_only:
+        import torch
+        r = ring65536_timing(torch)
+        print(json.dumps({"metric": "limb-NTTs/s at n=65536", "unit": "limb-NTTs/s", "value": r["limb_ntts_per_s"],
+                          "n_gpus": 1, "dtype": "u64", "data": "synthetic", "config": {"workload": r["config"]},
+                          "ring65536": r}))
         return
     if args.c4_only:
         import torch

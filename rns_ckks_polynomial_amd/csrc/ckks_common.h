@@ -14,6 +14,16 @@ namespace ckks {
 
 typedef unsigned __int128 u128;
 
+// Loads through table pointers that the kernels read from device structs (BasisDev):
+// such pointers are generic to the compiler, which then emits flat loads; these count
+// against the LDS counter as well, so every LDS wait also waits for them.  Reading
+// through the global address space gives global loads.
+template <class T>
+__device__ __forceinline__ T gload(const T *p) {
+    return *(const T __attribute__((address_space(1))) *)p;
+}
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 // ------------------------------------------------------------------ scalar
 __device__ __forceinline__ uint64_t mulhi64(uint64_t a, uint64_t b) { return __umul64hi(a, b); }
 

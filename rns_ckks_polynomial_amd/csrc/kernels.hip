@@ -298,7 +298,7 @@ __global__ void k_basis_u(const BasisDev *__restrict__ bases, SetLayout lay, uin
         for (int a = 0; a < 32; a++) asm volatile("" : "+v"(yv[a]));
 #pragma unroll
         for (int a = 0; a < 32; a++)
-            if ((uint32_t)a < m) add(unsplit30(yv[a]), B.R[a]);
+            if ((uint32_t)a < m) add(unsplit30(yv[a]), gload(B.R + a));
     }
     // the sum is exact integer arithmetic, so inputs are taken 8 at a time
     // with all 8 loads in flight before the first is used
@@ -308,7 +308,7 @@ __global__ void k_basis_u(const BasisDev *__restrict__ bases, SetLayout lay, uin
         for (int a = 0; a < 8; a++) {
             const uint32_t i = min(i0 + a, m - 1);
             yv[a] = unsplit30(yb[(size_t)i * n]);
-            rv[a] = B.R[i];
+            rv[a] = gload(B.R + i);
         }
 #pragma unroll
         for (int a = 0; a < 8; a++)
@@ -427,7 +427,11 @@ __global__ __launch_bounds__(256, OCC == 3 ? 4 : OCC) void k_convert_mfma(const 
     uint64_t rb[2][8];
     uint32_t ub[2];
     load_rows(rb[0], ub[0], 0);
-    if (OCC != 3 && nch > 1) load_rows(rb[1], ub[1], 1 % nch);
+    // rows are prefetched two chunks ahead whenever a set may have several chunks: always in
+    // the unstaged variant (a compile-time condition there, so that no branch joins differing
+    // load histories; a set of its launch with one chunk then reloads that chunk)
+    const bool rows_ahead = OCC != 3 && (!STAGED || nch > 1);
+    if (rows_ahead) load_rows(rb[1], ub[1], 1 % nch);
     if constexpr (STAGED) {
         // position p's 8 x 32 digit bytes are contiguous in HD (mk = 32): 16-byte copies
         const uint32_t np = ntile * 16;
@@ -445,11 +449,16 @@ __global__ __launch_bounds__(256, OCC == 3 ? 4 : OCC) void k_convert_mfma(const 
     auto plane_a = [&](int a) -> long { return __builtin_bit_cast(mf_v2l, AP[a / 2])[a % 2]; };
     auto build_a = [&](const uint64_t(&raw)[8], uint32_t uraw, uint32_t ch) {
         const uint32_t r0 = (ch % cps) * 32 + 8 * grp;
+        // row r < m is input y_r, row m the u row, the rest zero: selected without branches, so
+        // that no lane-divergent block waits for every load in flight (the prefetched chunks)
         uint64_t z[8];
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             const uint32_t r = r0 + j;
-            z[j] = digit_form(r < m ? unsplit30(raw[j]) : (r == m ? (uint64_t)uraw : 0));
+            const uint64_t yv = unsplit30(raw[j]);
+            uint64_t v = r < m ? yv : (uint64_t)uraw;
+            v = r <= m ? v : 0;
+            z[j] = digit_form(v);
         }
         uint32_t o[2][8];
         bt4((uint32_t)z[0], (uint32_t)z[1], (uint32_t)z[2], (uint32_t)z[3], o[0][0], o[0][1], o[0][2], o[0][3]);
@@ -511,25 +520,22 @@ __global__ __launch_bounds__(256, OCC == 3 ? 4 : OCC) void k_convert_mfma(const 
         }
     };
     // the slice of step g: thread x copies 16-byte pieces q = x and x + 256 of the
-    // 2 x 16 x 8 x 32 bytes (tiles past tile_end read padded, in-bounds positions)
-    uint4 hs[2];
+    // 2 x 16 x 8 x 32 bytes (tiles past tile_end read padded, in-bounds positions).  The two
+    // pieces live in named registers (an array captured by the lambdas went to scratch memory,
+    // and its store waited for every load in flight), read through a global-address-space
+    // pointer (a generic one makes flat loads, which count against the LDS counter too).
+    u32x4 hs0{}, hs1{};
+    const uint32_t sl_pos = (threadIdx.x / 16) % 16, sl_b = (threadIdx.x / 2) % 8, sl_hf = threadIdx.x % 2;
     auto fetch_slice = [&](uint32_t g) {
         const uint32_t t0 = tile0 + (g / nch) * TT, c0 = (g % nch % cps) * 32;
-#pragma unroll
-        for (int r = 0; r < 2; r++) {
-            const uint32_t q = threadIdx.x + 256 * r;  // (tile tt, position, digit b, half) = q / 256, ..
-            const uint32_t tt = q / 256, pos = (q / 16) % 16, b = (q / 2) % 8, hf = q % 2;
-            const uint32_t tile = min(t0 + tt, tile_end - 1);
-            hs[r] = *(const uint4 *)(B.HD + ((size_t)(16 * tile + pos) * 8 + b) * mk + c0 + 16 * hf);
-        }
+        const uint32_t ta = min(t0, tile_end - 1), tb = min(t0 + 1, tile_end - 1);
+        hs0 = gload((const u32x4 *)(B.HD + ((size_t)(16 * ta + sl_pos) * 8 + sl_b) * mk + c0 + 16 * sl_hf));
+        hs1 = gload((const u32x4 *)(B.HD + ((size_t)(16 * tb + sl_pos) * 8 + sl_b) * mk + c0 + 16 * sl_hf));
     };
     auto store_slice = [&](uint32_t buf) {
-#pragma unroll
-        for (int r = 0; r < 2; r++) {
-            const uint32_t q = threadIdx.x + 256 * r;
-            const uint32_t tt = q / 256, pos = (q / 16) % 16, b = (q / 2) % 8, hf = q % 2;
-            *(uint4 *)(sh_h + ((buf * 2 + tt) * 16 + pos) * MF_HSTRIDE + 32 * b + 16 * hf) = hs[r];
-        }
+        const uint32_t o = sl_pos * MF_HSTRIDE + 32 * sl_b + 16 * sl_hf;
+        *(u32x4 *)(sh_h + ((buf * 2 + 0) * 16) * MF_HSTRIDE + o) = hs0;
+        *(u32x4 *)(sh_h + ((buf * 2 + 1) * 16) * MF_HSTRIDE + o) = hs1;
     };
     // powers of two of the recombination, kept in registers so that each term
     // is one 32 x 32 + 64-bit multiply-add
@@ -540,14 +546,15 @@ __global__ __launch_bounds__(256, OCC == 3 ? 4 : OCC) void k_convert_mfma(const 
         const uint32_t p = 16 * tile + col;
         if (p >= ntarget) return;  // padding columns: every MFMA ran on the whole wave
         const uint64_t *rc = STAGED ? sh_rc + ((tile - tile0) * 16 + col) * MF_RC : B.RC + (size_t)p * MF_RC;
+        auto rcv = [&](int d) -> uint64_t { return STAGED ? rc[d] : gload(rc + d); };
         int32_t clo[7], chi[7];
 #pragma unroll
         for (int d = 0; d < 7; d++) {
-            const uint64_t c = rc[d];
+            const uint64_t c = rcv(d);
             clo[d] = (int32_t)(uint32_t)c;
             chi[d] = (int32_t)(uint32_t)(c >> 32);
         }
-        const uint64_t r60 = rc[7], r60p = rc[8], tq = rc[9], kfix = rc[10];
+        const uint64_t r60 = rcv(7), r60p = rcv(8), tq = rcv(9), kfix = rcv(10);
         const uint32_t t = conv_target<MODE>(ct, p, lo, m);
         const uint32_t slot = (MODE == 0 && t >= ct.L) ? ct.l + (t - ct.L) : t;
         uint64_t *ob = out + (s / lay.inner) * ct.out_so + (s % lay.inner) * ct.out_si + (size_t)slot * n + kb + 4 * grp;
@@ -586,7 +593,7 @@ __global__ __launch_bounds__(256, OCC == 3 ? 4 : OCC) void k_convert_mfma(const 
     // the flat sequence g = pass nch + ch over passes of TT tiles; rows are
     // fetched two chunks ahead
     const uint32_t total = (ntile + TT - 1) / TT * nch;
-    if (nch == 1) build_a(rb[0], ub[0], 0);
+    if (!rows_ahead) build_a(rb[0], ub[0], 0);
     if constexpr (!STAGED) {
         fetch_slice(0);
         store_slice(0);
@@ -600,12 +607,14 @@ __global__ __launch_bounds__(256, OCC == 3 ? 4 : OCC) void k_convert_mfma(const 
 #pragma unroll
                 for (int d = 0; d < 15; d++) acc[tt][d] = mf_v4i{0, 0, 0, 0};
         }
-        if (OCC != 3 && nch > 1) {
-            build_a(raw, uraw, ch);
-            if (g + 2 < total) load_rows(raw, uraw, (g + 2) % nch);
-        }
-        if constexpr (!STAGED)
-            if (g + 1 < total) fetch_slice(g + 1);
+        if (rows_ahead) build_a(raw, uraw, ch);
+        // the next slice is requested before the row prefetch: loads complete in order, so
+        // storing the slice then leaves the prefetched rows in flight.  Both are issued on every
+        // step (past the end they fetch clamped, valid addresses that nobody uses): branches
+        // around them make the compiler drain every load in flight at the loop's joins.
+        if constexpr (!STAGED) fetch_slice(g + 1);
+        asm volatile("" ::: "memory");  // keeps the slice loads ahead of the row loads
+        if (rows_ahead) load_rows(raw, uraw, (g + 2) % nch);
 #pragma unroll
         for (uint32_t tt = 0; tt < TT; tt++) {
             if (t0 + tt >= tile_end) break;  // workgroup-uniform
@@ -615,7 +624,7 @@ __global__ __launch_bounds__(256, OCC == 3 ? 4 : OCC) void k_convert_mfma(const 
         if constexpr (!STAGED) {
             // the next slice goes to the other buffer, whose last readers (step g - 1)
             // passed the barrier at its end; this barrier publishes it for step g + 1
-            if (g + 1 < total) store_slice((g + 1) & 1);
+            store_slice((g + 1) & 1);
             __syncthreads();
         }
         if (ch + 1 < nch) return;
