@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256) void k_ntt2048(Map map, const PrimeConsts *__r
     if (!INV) {
         n2048::fwd(v, lds, twf + (size_t)prime * 2048 * 2, q);
 #pragma unroll
-        for (int k = 0; k < 8; k++) dst[t + 256 * k] = n2048::reduce_out(v[k], q);
+        for (int k = 0; k < 8; k++) dst[t + 256 * k] = reduce_out(v[k], q);
     } else {
         n2048::inv(v, lds, twi + (size_t)prime * 2048 * 2, q);
         const uint64_t w = sc ? sc[0] : pc[prime].ninv, wp = sc ? sc[1] : pc[prime].ninvp;
@@ -1129,7 +1129,7 @@ __global__ __launch_bounds__(256) void k_final2048(const uint64_t *__restrict__ 
 #pragma unroll
     for (int m = 0; m < 8; m++) {
         const uint32_t k = t + 256 * m;
-        const uint64_t x = n2048::reduce_out(v[m], q);
+        const uint64_t x = reduce_out(v[m], q);
         uint64_t r = shoup(subm(av[m], x, q), w, wp, q);
         if (MODE == 1) {
             const size_t o0 = (b * 2) * per + (size_t)i * n + k, o1 = o0 + per;
@@ -1191,7 +1191,7 @@ __global__ __launch_bounds__(256) void k_final_giant2048(const uint64_t *__restr
     const uint64_t w = pinv[2 * i], wp = pinv[2 * i + 1];
 #pragma unroll
     for (int m = 0; m < 8; m++) {
-        const uint64_t x = n2048::reduce_out(v[m], q);
+        const uint64_t x = reduce_out(v[m], q);
         o[t + 256 * m] = addm(ov[m], shoup(subm(a[m], x, q), w, wp, q), q);
     }
 }
@@ -1225,7 +1225,7 @@ __global__ __launch_bounds__(256) void k_rescale2048(const uint64_t *__restrict_
 #pragma unroll
     for (int m = 0; m < 8; m++) {
         const uint32_t k = t + 256 * m;
-        const uint64_t x = n2048::reduce_out(v[m], q);
+        const uint64_t x = reduce_out(v[m], q);
         o[k] = shoup(subm(ci[k], x, q), w, wp, q);
     }
 }

@@ -19,7 +19,7 @@
 // lands in [0, 4q); the forward transform reduces its top inputs only every
 // third stage (values below 28q < 2^64), the inverse keeps them below 4q.
 #pragma once
-#include "ckks_common.h"
+#include "butterfly.h"
 
 namespace ckks {
 namespace n2048 {
@@ -40,51 +40,6 @@ __device__ __forceinline__ int own(int t, int k) {
 }
 
 __device__ __forceinline__ int brev(int i) { return (int)(__builtin_bitreverse32((uint32_t)i) >> (32 - LOGN)); }
-
-// Per-prime constants of the butterflies.  The negated thresholds pass through an
-// empty asm so that x - c stays one 64-bit add (v_lshl_add_u64) instead of being
-// turned back into a subtract with borrow.
-struct BfConsts {
-    uint64_t q, q4, n4, n8, n16;
-};
-__device__ __forceinline__ BfConsts bf_consts(uint64_t q) {
-    BfConsts c{q, 4 * q, 0 - 4 * q, 0 - 8 * q, 0 - 16 * q};
-    asm volatile("" : "+v"(c.n4));
-    asm volatile("" : "+v"(c.n8));
-    asm volatile("" : "+v"(c.n16));
-    return c;
-}
-
-// x - c if x >= c else x (nc = 2^64 - c): one add, one unsigned compare, a select.
-__device__ __forceinline__ uint64_t csub_n(uint64_t x, uint64_t c, uint64_t nc) {
-    const uint64_t m = x + nc;
-    return x >= c ? m : x;
-}
-
-// Cooley-Tukey butterfly (x, y) -> (a + t, a + 4q - t), a = x reduced by RED (0: as is,
-// else x - RED q when x >= RED q), t = y w in [0, 4q).  Without a reduction the bound of
-// the outputs grows by 4q per stage, so the forward transform reduces only where its
-// bounds require (see fwd).
-template <int RED>
-__device__ __forceinline__ void bf_ct(uint64_t &x, uint64_t &y, uint64_t w, uint64_t wp, const BfConsts &c) {
-    uint64_t a = x;
-    if (RED == 4) a = csub_n(x, c.q4, c.n4);
-    if (RED == 8) a = csub_n(x, 2 * c.q4, c.n8);
-    if (RED == 16) a = csub_n(x, 4 * c.q4, c.n16);
-    const uint64_t t = shoup_lazy4(y, w, wp, 0 - c.q);  // [0, 4q)
-    x = a + t;
-    y = a + c.q4 - t;
-}
-
-__device__ __forceinline__ void bf_gs(uint64_t &x, uint64_t &y, uint64_t w, uint64_t wp, const BfConsts &c) {
-    const uint64_t s = x + y;                         // [0, 8q)
-    const uint64_t d = x + c.q4 - y;                  // (0, 8q)
-    x = csub_n(s, c.q4, c.n4);                        // [0, 4q)
-    y = shoup_lazy4(d, w, wp, 0 - c.q);               // [0, 4q)
-}
-
-// The forward transform's outputs ([0, 24q)) fully reduced.
-__device__ __forceinline__ uint64_t reduce_out(uint64_t x, uint64_t q) { return reduce59(x, q, 0 - q); }
 
 // One radix-2 stage (bit BIT of the index) on the 8 registers of a pass owning bits [C, C+3).
 template <int C, int BIT, bool INV, int RED = 4>
