@@ -178,6 +178,9 @@ extern "C" int ckks_ctx_create(ckks_ctx **out, const ckks_params *params, int de
         c->d_tw_fwd = dev_upload(twf, c->owned, &err);
         c->d_tw_inv = dev_upload(twi, c->owned, &err);
         c->d_iota = dev_upload(iota, c->owned, &err);
+        std::vector<uint64_t> prc((size_t)ntot * MF_RC);
+        for (uint32_t g = 0; g < ntot; g++) host::recomb_row(c->primes[g], prc.data() + (size_t)g * MF_RC);
+        c->d_prc = dev_upload(prc, c->owned, &err);
     }
     if (!err && p.K > 0) {
         // full digits at the top level, the special-prime basis and its constants

@@ -60,6 +60,7 @@ struct ckks_ctx {
     uint64_t *d_tw_fwd = nullptr;       // [L+K][n][2]  psi^bitrev(k), Shoup
     uint64_t *d_tw_inv = nullptr;       // [L+K][n][2]  psi^-bitrev(k), Shoup
     uint64_t *d_iota = nullptr;         // [L+K]        psi^(n/2), the NTT of X^(n/2) is iota (-1)^k
+    uint64_t *d_prc = nullptr;          // [L+K][MF_RC] matrix-core reduction constants of each prime
     // base of the special primes P (targets: every chain prime)
     ckks::BasisDev h_pbasis{};
     ckks::BasisDev *d_pbasis = nullptr;

@@ -202,17 +202,20 @@ void basis_tables(const std::vector<uint64_t> &primes, uint32_t L, uint32_t K, u
             const uint64_t v = digit_form(r < m ? H[(size_t)t * m + r] : negB[t]);
             for (uint32_t d = 0; d < 8; d++) o.HD[((size_t)p * 8 + d) * o.mk + r] = (int8_t)(uint8_t)(v >> (8 * d));
         }
-        uint64_t *row = o.RC.data() + (size_t)p * MF_RC;
-        uint64_t w = powmod(2, 64, qt);  // 256^8 mod t
-        for (uint32_t s2 = 0; s2 < 7; s2++) {
-            row[s2] = (w & ((1ull << 30) - 1)) | ((w >> 30) << 32);
-            w = mulmod(w, 256, qt);
-        }
-        row[7] = powmod(2, 60, qt);
-        row[8] = shoup(row[7], qt);
-        row[9] = qt;
-        row[10] = 8 * qt - powmod(2, 91, qt);
+        recomb_row(qt, o.RC.data() + (size_t)p * MF_RC);
     }
+}
+
+void recomb_row(uint64_t q, uint64_t *row) {
+    uint64_t w = powmod(2, 64, q);  // 256^8 mod q
+    for (uint32_t s2 = 0; s2 < 7; s2++) {
+        row[s2] = (w & ((1ull << 30) - 1)) | ((w >> 30) << 32);
+        w = mulmod(w, 256, q);
+    }
+    row[7] = powmod(2, 60, q);
+    row[8] = shoup(row[7], q);
+    row[9] = q;
+    row[10] = 8 * q - powmod(2, 91, q);
 }
 
 }  // namespace host

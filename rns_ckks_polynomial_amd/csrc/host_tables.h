@@ -24,9 +24,10 @@ struct PrimeConsts {
     uint64_t r60p;   // Shoup companion of r60
 };
 
-// Reduction constants per target position of the matrix-core base
-// conversion: [0..6] 256^s mod t for s = 8..14 (low 30 bits | high 30 bits
-// << 32), [7] 2^60 mod t, [8] its Shoup quotient, [9] t, [10] 8t - [2^91]_t.
+// Reduction constants of a modulus t for the matrix-core products (the base
+// conversion's targets, the multiply-accumulate's chain primes): [0..6] 256^s
+// mod t for s = 8..14 (low 30 bits | high 30 bits << 32), [7] 2^60 mod t, [8]
+// its Shoup quotient, [9] t, [10] 8t - [2^91]_t.
 constexpr uint32_t MF_RC = 11;
 
 namespace host {
@@ -41,6 +42,8 @@ bool chain(uint32_t n, uint32_t count, std::vector<uint64_t> &out);
 // The smallest primitive 2n-th root of unity modulo q.
 uint64_t min_root(uint32_t n, uint64_t q);
 uint32_t bitrev(uint32_t x, uint32_t bits);
+// The MF_RC reduction constants of modulus q (row[0 .. MF_RC)).
+void recomb_row(uint64_t q, uint64_t *row);
 // Signed base-256 digits of v < 2^63: byte a of the result, read as an int8,
 // is d_a with v = sum_a d_a 256^a, -128 <= d_a <= 127.
 inline uint64_t digit_form(uint64_t v) { return (v + 0x8080808080808080ull) ^ 0x8080808080808080ull; }

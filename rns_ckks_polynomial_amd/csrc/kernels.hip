@@ -18,6 +18,7 @@
 #include "ctx_internal.h"
 #include "multipass.h"
 #include "multipass_kernels.h"
+#include "mfma_digits.h"
 #include "ntt2048.h"
 #include "ops.h"
 
@@ -362,7 +363,6 @@ __device__ __forceinline__ uint32_t conv_target(const ConvTargets &ct, uint32_t 
 // the 8 rows 8 (l / 16) + j of a 32-row chunk, and ends with target column
 // l % 16 of the coefficient rows 4 (l / 16) + v (v < 4).
 // ---------------------------------------------------------------------
-typedef int mf_v4i __attribute__((ext_vector_type(4)));
 constexpr uint32_t MF_COEF = 64;  // coefficients per workgroup (4 waves x 16)
 constexpr uint32_t MF_TPB = 8;    // 16-position target tiles per workgroup
 // The one-chunk variant stages 7 tiles (112 target positions): its 40320 bytes of tables let
@@ -370,17 +370,6 @@ constexpr uint32_t MF_TPB = 8;    // 16-position target tiles per workgroup
 constexpr uint32_t MF_TPB1 = 7;
 template <int OCC>
 constexpr uint32_t mf_tpb() { return OCC == 3 ? MF_TPB1 : MF_TPB; }
-
-// 4x4 byte transpose: o_b holds byte b of x0, x1, x2, x3 (in that order).
-__device__ __forceinline__ void bt4(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3, uint32_t &o0, uint32_t &o1,
-                                    uint32_t &o2, uint32_t &o3) {
-    const uint32_t p01l = __builtin_amdgcn_perm(x1, x0, 0x05010400u), p01h = __builtin_amdgcn_perm(x1, x0, 0x07030602u);
-    const uint32_t p23l = __builtin_amdgcn_perm(x3, x2, 0x05010400u), p23h = __builtin_amdgcn_perm(x3, x2, 0x07030602u);
-    o0 = __builtin_amdgcn_perm(p23l, p01l, 0x05040100u);
-    o1 = __builtin_amdgcn_perm(p23l, p01l, 0x07060302u);
-    o2 = __builtin_amdgcn_perm(p23h, p01h, 0x05040100u);
-    o3 = __builtin_amdgcn_perm(p23h, p01h, 0x07060302u);
-}
 
 constexpr uint32_t MF_HSTRIDE = 272;  // LDS bytes per target position (8 digits x 32 rows + bank padding)
 
@@ -445,8 +434,6 @@ __global__ __launch_bounds__(256, OCC == 3 ? 4 : OCC) void k_convert_mfma(const 
     // digit plane a of the lane's 8 rows (byte j = row 8 grp + j) is half a % 2 of AP[a / 2]: the
     // planes 2i, 2i + 1 form one register tuple, the A operand of a 64-deep product
     mf_v4i AP[4];
-    typedef long mf_v2l __attribute__((ext_vector_type(2)));
-    auto plane_a = [&](int a) -> long { return __builtin_bit_cast(mf_v2l, AP[a / 2])[a % 2]; };
     auto build_a = [&](const uint64_t(&raw)[8], uint32_t uraw, uint32_t ch) {
         const uint32_t r0 = (ch % cps) * 32 + 8 * grp;
         // row r < m is input y_r, row m the u row, the rest zero: selected without branches, so
@@ -460,39 +447,23 @@ __global__ __launch_bounds__(256, OCC == 3 ? 4 : OCC) void k_convert_mfma(const 
             v = r <= m ? v : 0;
             z[j] = digit_form(v);
         }
-        uint32_t o[2][8];
-        bt4((uint32_t)z[0], (uint32_t)z[1], (uint32_t)z[2], (uint32_t)z[3], o[0][0], o[0][1], o[0][2], o[0][3]);
-        bt4((uint32_t)(z[0] >> 32), (uint32_t)(z[1] >> 32), (uint32_t)(z[2] >> 32), (uint32_t)(z[3] >> 32), o[0][4],
-            o[0][5], o[0][6], o[0][7]);
-        bt4((uint32_t)z[4], (uint32_t)z[5], (uint32_t)z[6], (uint32_t)z[7], o[1][0], o[1][1], o[1][2], o[1][3]);
-        bt4((uint32_t)(z[4] >> 32), (uint32_t)(z[5] >> 32), (uint32_t)(z[6] >> 32), (uint32_t)(z[7] >> 32), o[1][4],
-            o[1][5], o[1][6], o[1][7]);
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const mf_v2l pr = {(long)(((uint64_t)o[1][2 * i] << 32) | o[0][2 * i]),
-                               (long)(((uint64_t)o[1][2 * i + 1] << 32) | o[0][2 * i + 1])};
-            AP[i] = __builtin_bit_cast(mf_v4i, pr);
-        }
+        long pl[8];
+        mf_planes(z, pl);
+        mf_left(pl, AP);
     };
     // TT target tiles share each chunk's A fragments (2 when the contraction has
     // several chunks, so the rows are fetched and transposed once per 2 tiles)
     constexpr uint32_t TT = OCC == 3 ? 1 : 2;
-    // H fragments of a tile: from LDS.  Staged: the workgroup's whole table,
-    // loaded once (the one-chunk variant reads a tile's fragments once, the
+    // H fragments of a tile (mf_right's tuples): from LDS.  Staged: the workgroup's whole
+    // table, loaded once (the one-chunk variant reads a tile's fragments once, the
     // two-wave variant at every chunk).
     // Otherwise the digit-table slice of each (pass, chunk), 2 tiles x 16
     // positions x 8 digits x 32 rows, goes through a double-buffered LDS slice
     // that the workgroup fills one step ahead (all its waves run the same steps).
-    // The product of a tile and chunk, S_s += sum_{a+b=s} dA_a dH_b, runs on 64-deep MFMAs where
-    // it can: the digit pairs (2i, s-2i) and (2i+1, s-2i-1) of diagonal s go through one
-    // 16x16x64 product of the tuples {A_2i | A_2i+1} = AP[i] and {H_b | H_b-1} = HP[7 - b],
-    // b = s - 2i (both operands take the same K positions, so the product is the sum of the two
-    // 32-deep ones).  The planes left over (a = s for even s <= 6, b = 7 for even s >= 8) take
-    // one 16x16x32 each: 28 + 8 instructions per tile and chunk instead of 64, at the rate of
-    // the 64-deep form.  HP's seven tuples overlap in content.  The staged two-wave variant
-    // (summed sets) reads a tile's tuples from LDS again at every chunk rather than keeping both
-    // tiles' tuples for the whole pass, which keeps it within 256 VGPRs.
-    constexpr int NH = 7;  // 4-VGPR H registers per tile
+    // The staged two-wave variant (summed sets) reads a tile's tuples from LDS again at every
+    // chunk rather than keeping both tiles' tuples for the whole pass, which keeps it within
+    // 256 VGPRs.
+    constexpr int NH = MF_NH;  // 4-VGPR H registers per tile
     mf_v4i hb[TT][NH];
     auto load_h = [&](mf_v4i(&H)[NH], uint32_t tile, uint32_t buf) {
         const int8_t *h = STAGED ? sh_h + ((tile - tile0) * 16 + col) * MF_HSTRIDE + 8 * grp
@@ -500,24 +471,6 @@ __global__ __launch_bounds__(256, OCC == 3 ? 4 : OCC) void k_convert_mfma(const 
         auto pl = [&](int bb) -> long { return *(const long *)(h + 32 * bb); };
 #pragma unroll
         for (int j = 0; j < NH; j++) H[j] = __builtin_bit_cast(mf_v4i, mf_v2l{pl(7 - j), pl(6 - j)});
-    };
-    auto mac_tile = [&](mf_v4i(&ac)[15], const mf_v4i(&H)[NH]) {
-        auto hsing = [&](int bb) -> long {  // plane b inside HP: HP[7 - b] = {H_b, H_b-1}, HP[6] = {H_1, H_0}
-            return bb > 0 ? __builtin_bit_cast(mf_v2l, H[7 - bb])[0] : __builtin_bit_cast(mf_v2l, H[6])[1];
-        };
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-#pragma unroll
-            for (int sd = 0; sd < 15; sd++) {
-                const int bb = sd - 2 * i;  // pair (2i, b), (2i+1, b-1)
-                if (bb < 1 || bb > 7) continue;
-                ac[sd] = __builtin_amdgcn_mfma_i32_16x16x64_i8(AP[i], H[7 - bb], ac[sd], 0, 0, 0);
-            }
-#pragma unroll
-        for (int sd = 0; sd < 15; sd += 2) {  // leftovers: a = s (b = 0) for s <= 6, a = s - 7 (b = 7) for s >= 8
-            const int aa = sd <= 6 ? sd : sd - 7, bb = sd - aa;
-            ac[sd] = __builtin_amdgcn_mfma_i32_16x16x32_i8(plane_a(aa), hsing(bb), ac[sd], 0, 0, 0);
-        }
     };
     // the slice of step g: thread x copies 16-byte pieces q = x and x + 256 of the
     // 2 x 16 x 8 x 32 bytes (tiles past tile_end read padded, in-bounds positions).  The two
@@ -537,57 +490,17 @@ __global__ __launch_bounds__(256, OCC == 3 ? 4 : OCC) void k_convert_mfma(const 
         *(u32x4 *)(sh_h + ((buf * 2 + 0) * 16) * MF_HSTRIDE + o) = hs0;
         *(u32x4 *)(sh_h + ((buf * 2 + 1) * 16) * MF_HSTRIDE + o) = hs1;
     };
-    // powers of two of the recombination, kept in registers so that each term
-    // is one 32 x 32 + 64-bit multiply-add
-    int32_t w2[7] = {1 << 8, 1 << 16, 1 << 24, 1 << 2, 1 << 10, 1 << 18, 1 << 26};
-#pragma unroll
-    for (int d = 0; d < 7; d++) asm volatile("" : "+v"(w2[d]));
+    const MfW2 w2 = mf_w2();
     auto recombine = [&](uint32_t tile, const mf_v4i(&acc)[15]) {
         const uint32_t p = 16 * tile + col;
         if (p >= ntarget) return;  // padding columns: every MFMA ran on the whole wave
         const uint64_t *rc = STAGED ? sh_rc + ((tile - tile0) * 16 + col) * MF_RC : B.RC + (size_t)p * MF_RC;
-        auto rcv = [&](int d) -> uint64_t { return STAGED ? rc[d] : gload(rc + d); };
-        int32_t clo[7], chi[7];
-#pragma unroll
-        for (int d = 0; d < 7; d++) {
-            const uint64_t c = rcv(d);
-            clo[d] = (int32_t)(uint32_t)c;
-            chi[d] = (int32_t)(uint32_t)(c >> 32);
-        }
-        const uint64_t r60 = rcv(7), r60p = rcv(8), tq = rcv(9), kfix = rcv(10);
+        const MfRecomb k = mf_recomb_consts([&](int d) -> uint64_t { return STAGED ? rc[d] : gload(rc + d); });
         const uint32_t t = conv_target<MODE>(ct, p, lo, m);
         const uint32_t slot = (MODE == 0 && t >= ct.L) ? ct.l + (t - ct.L) : t;
         uint64_t *ob = out + (s / lay.inner) * ct.out_so + (s % lay.inner) * ct.out_si + (size_t)slot * n + kb + 4 * grp;
 #pragma unroll
-        for (int v = 0; v < 4; v++) {
-            // value = lo + 2^30 hi: lo takes the weights 1 .. 2^24 and the low 30 bits
-            // of 256^s mod t (s >= 8), hi the weights 2^2 .. 2^26 and the high 30 bits;
-            // |S_s| <= 2^28 keeps both below 2^61 in magnitude
-            int64_t lo_s = (int64_t)acc[0][v];
-            lo_s += (int64_t)acc[1][v] * (int64_t)w2[0];
-            lo_s += (int64_t)acc[2][v] * (int64_t)w2[1];
-            lo_s += (int64_t)acc[3][v] * (int64_t)w2[2];
-            int64_t hi_s = (int64_t)acc[4][v] * (int64_t)w2[3];
-            hi_s += (int64_t)acc[5][v] * (int64_t)w2[4];
-            hi_s += (int64_t)acc[6][v] * (int64_t)w2[5];
-            hi_s += (int64_t)acc[7][v] * (int64_t)w2[6];
-#pragma unroll
-            for (int d = 0; d < 7; d++) {
-                lo_s += (int64_t)acc[8 + d][v] * (int64_t)clo[d];
-                hi_s += (int64_t)acc[8 + d][v] * (int64_t)chi[d];
-            }
-            // hi = 2^30 h1 + h0 (0 <= h0 < 2^30, |h1| < 2^31); 2^60 h1 = 2^60 (h1 + 2^31)
-            // - 2^91, and kfix = 8t - [2^91]_t makes the sum positive:
-            // 0 < x = lo + 2^30 h0 + [2^60 (h1 + 2^31)]_lazy + kfix < 2^63
-            const uint64_t h0 = (uint64_t)hi_s & M30;
-            const uint32_t h1b = (uint32_t)(hi_s >> 30) ^ 0x80000000u;
-            const uint64_t x = (uint64_t)lo_s + (h0 << 30) + shoup_lazy(h1b, r60, r60p, tq) + kfix;
-            // t in (2^59, 2^59 + 2^52) and x < 2^63: x >> 59 is floor(x / t) or one more
-            const uint64_t qh = x >> 59;
-            int64_t r = (int64_t)(x - qh * tq);
-            r += (r >> 63) & (int64_t)tq;
-            ob[v] = (uint64_t)r;
-        }
+        for (int v = 0; v < 4; v++) ob[v] = mf_recombine(acc, v, w2, k);
     };
     mf_v4i acc[TT][15];
     // the flat sequence g = pass nch + ch over passes of TT tiles; rows are
@@ -619,7 +532,7 @@ __global__ __launch_bounds__(256, OCC == 3 ? 4 : OCC) void k_convert_mfma(const 
         for (uint32_t tt = 0; tt < TT; tt++) {
             if (t0 + tt >= tile_end) break;  // workgroup-uniform
             if (!STAGED || ch == 0 || OCC == 2) load_h(hb[tt], t0 + tt, g & 1);  // OCC 2: see NH
-            mac_tile(acc[tt], hb[tt]);
+            mf_mac_tile(acc[tt], AP, hb[tt]);
         }
         if constexpr (!STAGED) {
             // the next slice goes to the other buffer, whose last readers (step g - 1)
@@ -1359,6 +1272,135 @@ __global__ __launch_bounds__(256) void k_bsgs_mac(const uint64_t *__restrict__ p
     }
 }
 
+// ---------------------------------------------------------------------
+// The same multiply-accumulate on the matrix cores: for limb i and coefficient k,
+//   inner[g][c][i][k] (+)= sum_{bb < nb} P[g][b0 + bb][i][k] R[b0 + bb][c][i][k]  mod q_i,
+// a (gs x 32) x (32 x cols) product per (i, k), taken in signed base-256 digits
+// (mfma_digits.h): the rows of a 16 x 16 tile are giant steps, its columns the
+// ciphertext polynomials c < cols <= 16, the contraction the baby steps.  A
+// workgroup takes 16 consecutive coefficients of one limb, wave w the
+// coefficients 4w .. 4w + 3.  Every global access is a 128-byte run of 16
+// coefficients, turned in one LDS buffer: first the rotations (whose digit
+// planes then stay in registers), then per tile of 16 giant steps the diagonals
+// (16 x 32 x 16 values), read back in the operand layout, and the tile's sums on
+// their way out.  Two workgroups share a CU, so one's loads overlap the other's
+// products.
+// ---------------------------------------------------------------------
+constexpr int MM_K = 16;                  // coefficients per workgroup
+constexpr int MM_ROW = 34;                // LDS words per staged (k, row) run of 32 + 2 pad
+constexpr int MM_SLAB = 16 * MM_ROW + 2;  // LDS words per staged coefficient (16 rows) + 2 pad
+constexpr int MM_OC = 17;                 // LDS words per (g, c) row of the sums: 16 + 1 pad
+
+template <bool ACC>
+__global__ __launch_bounds__(256, 2) void k_bsgs_mac_mfma(const uint64_t *__restrict__ pt,
+                                                           const uint64_t *__restrict__ in,
+                                                           const uint64_t *__restrict__ rot,
+                                                           uint64_t *__restrict__ inner,
+                                                           const uint64_t *__restrict__ prc, uint32_t n, uint32_t l,
+                                                           uint32_t bs, uint32_t gs, uint32_t ncols, size_t ctsize,
+                                                           uint32_t b0) {
+    __shared__ __align__(16) uint64_t sp[MM_K * MM_SLAB];
+    const uint32_t i = blockIdx.y, k0 = blockIdx.x * MM_K;
+    const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t col = lane & 15, grp = lane >> 4;
+    const uint32_t nb = min(32u, bs - b0);
+    const size_t pstride = (size_t)l * n;
+    // staging lanes: coefficient k0 + kk_s and runs r_s + 16 mm (r_s < 16)
+    const uint32_t kk_s = threadIdx.x % 16, r_s = threadIdx.x / 16;
+    uint64_t *const sdst = sp + kk_s * MM_SLAB + r_s;
+    // the rotations: run (c = r_s, baby step mm) at sp[k][c][bb]; rows past nb and columns
+    // past ncols are zero (their loads clamped)
+    {
+        const size_t rofs = ((size_t)min(r_s, ncols - 1) * l + i) * n + k0 + kk_s;
+        uint64_t x[32];
+#pragma unroll
+        for (int mm = 0; mm < 32; mm++) {
+            const uint32_t b = b0 + min((uint32_t)mm, nb - 1);
+            x[mm] = (b == 0 ? in : rot + (size_t)(b - 1) * ctsize)[rofs];
+        }
+        const bool colok = r_s < ncols;
+        uint64_t *d = sp + kk_s * MM_SLAB + r_s * MM_ROW;
+#pragma unroll
+        for (int mm = 0; mm < 32; mm++) d[mm] = (colok && (uint32_t)mm < nb) ? x[mm] : 0;
+    }
+    __syncthreads();
+    // right operand: digit planes of baby steps 8 grp + j of polynomial col at this wave's 4
+    // coefficients, in reverse plane order (rp[q][7 - a] = plane a), so that the tuples
+    // {plane b | plane b - 1} are consecutive registers
+    long rp[4][8];
+#pragma unroll
+    for (int qk = 0; qk < 4; qk++) {
+        const uint64_t *a = sp + (4 * wave + qk) * MM_SLAB + col * MM_ROW + 8 * grp;
+        uint64_t z[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) z[j] = digit_form(a[j]);
+        long pl[8];
+        mf_planes(z, pl);
+#pragma unroll
+        for (int a2 = 0; a2 < 8; a2++) rp[qk][7 - a2] = pl[a2];
+    }
+    const MfW2 w2 = mf_w2();
+    const MfRecomb rk = mf_recomb_consts([&](int d) -> uint64_t { return prc[(size_t)i * MF_RC + d]; });
+    // diagonal runs of a tile: r_s + 16 mm = giant step mm >> 1, baby step r_s + 16 (mm & 1)
+    const size_t gstride = (size_t)bs * pstride;
+    const uint64_t *pb0 = pt + (size_t)(b0 + min(r_s, nb - 1)) * pstride + (size_t)i * n + k0 + kk_s;
+    const uint64_t *pb1 = pt + (size_t)(b0 + min(r_s + 16, nb - 1)) * pstride + (size_t)i * n + k0 + kk_s;
+    for (uint32_t g0 = 0; g0 < gs; g0 += 16) {
+        __syncthreads();  // sp is free: the previous contents are all read
+        {
+            uint64_t x[32];
+#pragma unroll
+            for (int mm = 0; mm < 32; mm++) {
+                const size_t g = min(g0 + (uint32_t)(mm >> 1), gs - 1);
+                x[mm] = ((mm & 1) ? pb1 : pb0)[g * gstride];
+            }
+#pragma unroll
+            for (int mm = 0; mm < 32; mm++) sdst[(mm >> 1) * MM_ROW + 16 * (mm & 1)] = x[mm];
+        }
+        __syncthreads();
+        uint64_t res[4][4];
+#pragma unroll
+        for (int qk = 0; qk < 4; qk++) {
+            // left operand: giant step g0 + col, baby steps 8 grp + j
+            const uint64_t *a = sp + (4 * wave + qk) * MM_SLAB + col * MM_ROW + 8 * grp;
+            uint64_t z[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) z[j] = digit_form(a[j]);
+            long pl[8];
+            mf_planes(z, pl);
+            mf_v4i AP[4], H[MF_NH];
+            mf_left(pl, AP);
+#pragma unroll
+            for (int j = 0; j < MF_NH; j++) H[j] = __builtin_bit_cast(mf_v4i, mf_v2l{rp[qk][j], rp[qk][j + 1]});
+            mf_v4i acc[15];
+#pragma unroll
+            for (int d = 0; d < 15; d++) acc[d] = mf_v4i{0, 0, 0, 0};
+            mf_mac_tile(acc, AP, H);
+#pragma unroll
+            for (int v = 0; v < 4; v++) res[qk][v] = mf_recombine(acc, v, w2, rk);
+        }
+        __syncthreads();  // every wave is done with the diagonals
+        // the sums of (giant step g0 + 4 grp + v, polynomial col) at sp[(g c)][k]
+#pragma unroll
+        for (int qk = 0; qk < 4; qk++)
+#pragma unroll
+            for (int v = 0; v < 4; v++) sp[((4 * grp + v) * 16 + col) * MM_OC + 4 * wave + qk] = res[qk][v];
+        __syncthreads();
+        // out: polynomial r_s, giant steps g0 + mm
+        if (r_s < ncols) {
+            uint64_t *ob = inner + ((size_t)r_s * l + i) * n + k0 + kk_s;
+#pragma unroll 4
+            for (int mm = 0; mm < 16; mm++) {
+                if (g0 + mm >= gs) break;
+                uint64_t *o = ob + (size_t)(g0 + mm) * ctsize;
+                uint64_t v = sp[(mm * 16 + r_s) * MM_OC + kk_s];
+                if (ACC) v = addm(v, *o, rk.tq);
+                *o = v;
+            }
+        }
+    }
+}
+
 __global__ void k_copy(const uint64_t *__restrict__ a, uint64_t *__restrict__ b, size_t total) {
     for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total;
          idx += (size_t)gridDim.x * blockDim.x)
@@ -1803,12 +1845,19 @@ int op_bsgs(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, 
     }
     for (int b0 = 0; b0 < bs; b0 += MAC_B) {
         ProfScope ps_(c, "bsgs_mac", s);
-        const dim3 grid(c->n / MAC_K, l, (2 * B + MAC_C - 1) / MAC_C);
-        const bool full = (2 * B) % MAC_C == 0;
-        auto kern = b0 ? (full ? k_bsgs_mac<true, true> : k_bsgs_mac<false, true>)
-                       : (full ? k_bsgs_mac<true, false> : k_bsgs_mac<false, false>);
-        hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, diags, in, rot, inner, c->d_pc, c->n, (uint32_t)l,
-                           (uint32_t)bs, (uint32_t)gs, (uint32_t)(2 * B), ct, (uint32_t)b0);
+        if (2 * B <= 16) {  // the polynomials fit the columns of one matrix-core tile
+            const dim3 grid(c->n / MM_K, l);
+            hipLaunchKernelGGL(b0 ? k_bsgs_mac_mfma<true> : k_bsgs_mac_mfma<false>, grid, dim3(256), 0, s, diags, in,
+                               rot, inner, c->d_prc, c->n, (uint32_t)l, (uint32_t)bs, (uint32_t)gs, (uint32_t)(2 * B),
+                               ct, (uint32_t)b0);
+        } else {
+            const dim3 grid(c->n / MAC_K, l, (2 * B + MAC_C - 1) / MAC_C);
+            const bool full = (2 * B) % MAC_C == 0;
+            auto kern = b0 ? (full ? k_bsgs_mac<true, true> : k_bsgs_mac<false, true>)
+                           : (full ? k_bsgs_mac<true, false> : k_bsgs_mac<false, false>);
+            hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, diags, in, rot, inner, c->d_pc, c->n, (uint32_t)l,
+                               (uint32_t)bs, (uint32_t)gs, (uint32_t)(2 * B), ct, (uint32_t)b0);
+        }
         LAUNCH_CHECK();
     }
     // giant steps: batches of independent rotations of inner[g], summed into inner[0]

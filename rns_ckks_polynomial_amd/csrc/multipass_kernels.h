@@ -15,6 +15,7 @@ namespace ckks {
 namespace mp {
 
 constexpr int LOG = 8, E = 16, V = 16;
+constexpr int NT = 16 * V;  // threads per workgroup: 16 per vector
 constexpr int VSTRIDE = 264;  // LDS words per vector (256 + padding)
 
 __device__ __forceinline__ int slot(int v, int i) { return v * VSTRIDE + i + (i >> 5); }
@@ -94,7 +95,7 @@ __device__ __forceinline__ void inv(uint64_t (&x)[E], uint64_t *lds, int v, int 
 
 // ---- forward pass 1: columns i2 in [16 bx, +16) of limb; times TA -> scratch (< 4q)
 template <class Map>
-__global__ __launch_bounds__(256) void k_fwd_cols(Map map, uint32_t limb0, const PrimeConsts *__restrict__ pc,
+__global__ __launch_bounds__(NT) void k_fwd_cols(Map map, uint32_t limb0, const PrimeConsts *__restrict__ pc,
                                                    const uint64_t *__restrict__ tw, const uint64_t *__restrict__ taf,
                                                    uint64_t *__restrict__ scratch) {
     __shared__ uint64_t lds[V * VSTRIDE];
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(256) void k_fwd_cols(Map map, uint32_t limb0, const
 
 // ---- forward pass 2: rows j1 in [16 bx, +16) of scratch (k = bx); outputs A[j1 + 256 j2] -> dst
 template <class Map>
-__global__ __launch_bounds__(256) void k_fwd_rows(Map map, uint32_t limb0, const PrimeConsts *__restrict__ pc,
+__global__ __launch_bounds__(NT) void k_fwd_rows(Map map, uint32_t limb0, const PrimeConsts *__restrict__ pc,
                                                    const uint64_t *__restrict__ rowf,
                                                    const uint64_t *__restrict__ scratch) {
     __shared__ uint64_t lds[V * VSTRIDE];
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(256) void k_fwd_rows(Map map, uint32_t limb0, const
         uint64_t x[E];
 #pragma unroll
         for (int k = 0; k < E; k++) x[k] = in[(size_t)(r0 + v) * MP_N1 + t + 16 * k];
-        fwd(x, lds, v, t, rowf + ((size_t)prime * 16 + blockIdx.x) * MP_N1 * 2, c);
+        fwd(x, lds, v, t, rowf + ((size_t)prime * 16 + (r0 >> 4)) * MP_N1 * 2, c);
     }
     const int v = threadIdx.x % V, t = threadIdx.x / V;  // lanes across rows for the transposed store
 #pragma unroll
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(256) void k_fwd_rows(Map map, uint32_t limb0, const
 
 // ---- inverse pass 1: rows j1 = 16 bx + v: gather A[j1 + 256 j2], inverse row transform -> scratch[j1][i2]
 template <class Map>
-__global__ __launch_bounds__(256) void k_inv_rows(Map map, uint32_t limb0, const PrimeConsts *__restrict__ pc,
+__global__ __launch_bounds__(NT) void k_inv_rows(Map map, uint32_t limb0, const PrimeConsts *__restrict__ pc,
                                                    const uint64_t *__restrict__ rowi, uint64_t *__restrict__ scratch) {
     __shared__ uint64_t lds[V * VSTRIDE];
     const uint64_t *src;
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(256) void k_inv_rows(Map map, uint32_t limb0, const
         uint64_t x[E];
 #pragma unroll
         for (int k = 0; k < E; k++) x[k] = src[(size_t)(r0 + v) + (size_t)MP_N1 * (t + 16 * k)];
-        inv(x, lds, v, t, rowi + ((size_t)prime * 16 + blockIdx.x) * MP_N1 * 2, c);
+        inv(x, lds, v, t, rowi + ((size_t)prime * 16 + (r0 >> 4)) * MP_N1 * 2, c);
 #pragma unroll
         for (int k = 0; k < E; k++) lds[slot(v, t + 16 * k)] = x[k];
     }
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(256) void k_inv_rows(Map map, uint32_t limb0, const
 
 // ---- inverse pass 2: columns i2 = 16 bx + v of scratch; times TA^-1, inverse; scale -> dst[256 i1 + i2]
 template <class Map>
-__global__ __launch_bounds__(256) void k_inv_cols(Map map, uint32_t limb0, const PrimeConsts *__restrict__ pc,
+__global__ __launch_bounds__(NT) void k_inv_cols(Map map, uint32_t limb0, const PrimeConsts *__restrict__ pc,
                                                    const uint64_t *__restrict__ tw, const uint64_t *__restrict__ tai,
                                                    const uint64_t *__restrict__ scratch) {
     __shared__ uint64_t lds[V * VSTRIDE];
@@ -223,7 +224,7 @@ template <class Map>
 static int multipass_launch(const ckks_ctx *c, const Map &map, int nblk, bool inverse, hipStream_t s,
                             uint64_t *scratch) {
     const MultipassPlan *p = c->mp;
-    const dim3 blk(256);
+    const dim3 blk(mp::NT);
     for (int l0 = 0; l0 < nblk; l0 += MP_CHUNK) {
         const dim3 grid(MP_N1 / mp::V, (unsigned)std::min<int>(MP_CHUNK, nblk - l0));
         if (!inverse) {
