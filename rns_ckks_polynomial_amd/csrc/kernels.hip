@@ -228,8 +228,8 @@ __global__ void k_prep_relin(const uint64_t *__restrict__ a, const uint64_t *__r
 // 2^63) unless the fractional part of S' + 2^62 is within 2m of 2^63; then an
 // exact mixed-radix comparison of x with (B-1)/2 decides.
 // ---------------------------------------------------------------------
-__device__ uint32_t exact_u_slow(const BasisDev &B, uint64_t *ycol, size_t stride, uint32_t floor_s,
-                                 const PrimeConsts *__restrict__ pc) {
+__device__ __attribute__((noinline)) uint32_t exact_u_slow(const BasisDev &B, uint64_t *ycol, size_t stride,
+                                                          uint32_t floor_s, const PrimeConsts *__restrict__ pc) {
     const uint32_t m = B.m;
     // x_i = y_i [Bhat_i]_{b_i}, in place (y arrives in split30 form, x is plain)
     for (uint32_t i = 0; i < m; i++) {
@@ -383,10 +383,12 @@ template <int MODE, int OCC, bool STAGED>
 __global__ __launch_bounds__(256, OCC == 3 ? 4 : OCC) void k_convert_mfma(const BasisDev *__restrict__ bases, SetLayout lay,
                                                           const uint64_t *__restrict__ y,
                                                           const uint32_t *__restrict__ u, ConvTargets ct,
-                                                          uint64_t *__restrict__ out, uint32_t n) {
+                                                          uint64_t *__restrict__ out, uint32_t n,
+                                                          const PrimeConsts *__restrict__ pc) {
     constexpr uint32_t TPB = mf_tpb<OCC>();
     __shared__ __align__(16) int8_t sh_h[STAGED ? TPB * 16 * MF_HSTRIDE : 2 * 2 * 16 * MF_HSTRIDE];
     __shared__ uint64_t sh_rc[STAGED ? TPB * 16 * MF_RC : 1];
+    constexpr bool FOLD_U = OCC == 3;  // u computed here rather than read (k_basis_u)
     const uint32_t s = blockIdx.z;
     const BasisDev &B = bases[lay.per_set_basis ? s % lay.inner : 0];
     const uint32_t m = B.m, lo = B.first, mk = B.mk;
@@ -410,7 +412,43 @@ __global__ __launch_bounds__(256, OCC == 3 ? 4 : OCC) void k_convert_mfma(const 
         const uint64_t *ys = yb + js * set_step;
 #pragma unroll
         for (int j = 0; j < 8; j++) raw[j] = ys[(size_t)min(r0 + j, m - 1) * n];
-        uraw = u[(sfirst + (size_t)js * ct.sum_stride) * n + kb + col];
+        if constexpr (!FOLD_U) uraw = u[(sfirst + (size_t)js * ct.sum_stride) * n + kb + col];
+    };
+    // One-chunk launches (a single set of at most 31 rows) take the set's u from its rows, as
+    // k_basis_u does: the 4 lanes of a coefficient sum the fixed-point y_r / b_r of their 8 rows
+    // and exchange the partial sums; a sum too close to a rounding boundary goes to the exact
+    // path on a private copy of the column (other workgroups read the same rows).
+    auto exact_u = [&](const uint64_t(&raw)[8], uint32_t ch) -> uint32_t {
+        const uint64_t M63 = (1ull << 63) - 1;
+        const uint32_t r0 = 8 * grp;
+        uint64_t frac = 0;
+        uint32_t ip = 0;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const uint32_t r = min(r0 + j, m - 1);
+            const uint64_t rr = r0 + j < m ? gload(B.R + r) : 0;
+            frac += mulhi64(unsplit30(raw[j]) << 4, rr);
+            ip += (uint32_t)(frac >> 63);
+            frac &= M63;
+        }
+#pragma unroll
+        for (int off = 16; off <= 32; off *= 2) {
+            const uint64_t f2 = __shfl_xor(frac, off);
+            const uint32_t i2 = __shfl_xor(ip, off);
+            const uint64_t sum = frac + f2;  // both below 2^63
+            ip += i2 + (uint32_t)(sum >> 63);
+            frac = sum & M63;
+        }
+        uint64_t t = frac + (1ull << 62);
+        uint32_t uu = ip + (uint32_t)(t >> 63);
+        t &= M63;
+        if (t >= (1ull << 63) - 2ull * m) {
+            uint64_t colv[32];
+            const uint64_t *ys = yb + (ch / cps) * set_step;
+            for (uint32_t r = 0; r < m; r++) colv[r] = ys[(size_t)r * n];
+            uu = exact_u_slow(B, colv, 1, ip, pc);
+        }
+        return uu;
     };
     // the first rows are in flight while the tables are staged
     uint64_t rb[2][8];
@@ -435,6 +473,7 @@ __global__ __launch_bounds__(256, OCC == 3 ? 4 : OCC) void k_convert_mfma(const 
     // planes 2i, 2i + 1 form one register tuple, the A operand of a 64-deep product
     mf_v4i AP[4];
     auto build_a = [&](const uint64_t(&raw)[8], uint32_t uraw, uint32_t ch) {
+        if constexpr (FOLD_U) uraw = exact_u(raw, ch);
         const uint32_t r0 = (ch % cps) * 32 + 8 * grp;
         // row r < m is input y_r, row m the u row, the rest zero: selected without branches, so
         // that no lane-divergent block waits for every load in flight (the prefetched chunks)
@@ -1441,7 +1480,10 @@ static size_t ks_words(const ckks_ctx *c, int B, int l, KsWs *w, uint64_t *base)
 // ModUp of d ([B][l][n], NTT domain, ciphertext b at d + b * d_stride):
 // fills w.y, w.u and the NTT-domain extended digits w.ext.
 // Exact base conversion of `sets` input sets (bases of at most mmax primes)
-// onto up to maxt target positions.
+// onto up to maxt target positions.  The one-chunk conversion (bases of up to
+// 31 primes, no summed sets) takes its correction u itself; the others read it
+// from k_basis_u.
+static inline bool conv_needs_u(uint32_t mmax, uint32_t nsum = 1) { return mmax + 1 > 32 || nsum > 1; }
 template <int MODE>
 static void launch_convert(const ckks_ctx *c, const BasisDev *bases, const SetLayout &lay, const uint64_t *y,
                            const uint32_t *u, const ConvTargets &ct, uint64_t *out, uint32_t maxt, uint32_t sets,
@@ -1451,11 +1493,14 @@ static void launch_convert(const ckks_ctx *c, const BasisDev *bases, const SetLa
     const uint32_t tpb = mmax + 1 > 32 || ct.nsum > 1 ? mf_tpb<2>() : mf_tpb<3>();
     const dim3 grid(n / MF_COEF, ((maxt + 15) / 16 + tpb - 1) / tpb, sets);
     if (mmax + 1 > 32)
-        hipLaunchKernelGGL((k_convert_mfma<MODE, 2, false>), grid, dim3(256), 0, s, bases, lay, y, u, ct, out, n);
+        hipLaunchKernelGGL((k_convert_mfma<MODE, 2, false>), grid, dim3(256), 0, s, bases, lay, y, u, ct, out, n,
+                           c->d_pc);
     else if (ct.nsum > 1)
-        hipLaunchKernelGGL((k_convert_mfma<MODE, 2, true>), grid, dim3(256), 0, s, bases, lay, y, u, ct, out, n);
+        hipLaunchKernelGGL((k_convert_mfma<MODE, 2, true>), grid, dim3(256), 0, s, bases, lay, y, u, ct, out, n,
+                           c->d_pc);
     else
-        hipLaunchKernelGGL((k_convert_mfma<MODE, 3, true>), grid, dim3(256), 0, s, bases, lay, y, u, ct, out, n);
+        hipLaunchKernelGGL((k_convert_mfma<MODE, 3, true>), grid, dim3(256), 0, s, bases, lay, y, u, ct, out, n,
+                           c->d_pc);
 }
 
 static int ks_modup(const ckks_ctx *c, const LevelTables *lt, int B, int l, const uint64_t *d, size_t d_stride, const KsWs &w,
@@ -1467,12 +1512,12 @@ static int ks_modup(const ckks_ctx *c, const LevelTables *lt, int B, int l, cons
         if ((e = launch_ntt(c, m, B * l, true, s, "ks_intt_modup", w.mp))) return e;
     }
     SetLayout lay_up{(size_t)l * n, (size_t)c->alpha * n, 0, beta, 1};
-    {
+    if (conv_needs_u(c->alpha)) {
         ProfScope ps_(c, "ks_modup_u", s);
         hipLaunchKernelGGL(k_basis_u, dim3((n + 255) / 256, B * beta), dim3(256), 0, s, lt->d_digits, lay_up, w.y,
                            w.u, n, c->d_pc);
+        LAUNCH_CHECK();
     }
-    LAUNCH_CHECK();
     {
         ConvTargets ct{(uint32_t)l, L, K, (size_t)beta * el * n, (size_t)el * n};
         const uint32_t maxt = l + K;  // upper bound on targets per digit
@@ -1573,12 +1618,12 @@ static int ks_moddown_conv(const ckks_ctx *c, size_t nout, int l, const KsWs &w,
         if ((e = launch_ntt(c, m, (int)(nout * 2 * K), true, s, "ks_intt_moddown", w.mp))) return e;
     }
     SetLayout lay_dn{(size_t)el * n, 0, (size_t)l * n, 1, 0};
-    {
+    if (conv_needs_u(K, nsum)) {
         ProfScope ps_(c, "ks_moddown_u", s);
         hipLaunchKernelGGL(k_basis_u, dim3((n + 255) / 256, (unsigned)(nout * 2)), dim3(256), 0, s, c->d_pbasis,
                            lay_dn, w.acc, w.uP, n, c->d_pc);
+        LAUNCH_CHECK();
     }
-    LAUNCH_CHECK();
     {
         ConvTargets ct{(uint32_t)l, L, K, (size_t)l * n, 0};
         // lay_dn.inner == 1: the summed sets are evenly spaced, as k_convert_mfma assumes
@@ -1622,12 +1667,12 @@ int op_mod_raise(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, in
         if ((e = launch_ntt(c, m, (int)(P * l0), true, s, "raise_intt", mp))) return e;
     }
     SetLayout lay{(size_t)l0 * n, 0, 0, 1, 0};
-    {
+    if (conv_needs_u((uint32_t)l0)) {
         ProfScope ps_(c, "raise_u", s);
         hipLaunchKernelGGL(k_basis_u, dim3((n + 255) / 256, P), dim3(256), 0, s, rt->d_basis, lay, y, u, n,
                            c->d_pc);
+        LAUNCH_CHECK();
     }
-    LAUNCH_CHECK();
     {
         ConvTargets ct{(uint32_t)lt, c->L, c->K, (size_t)lt * n, 0};
         ProfScope ps_(c, "raise_convert", s);
