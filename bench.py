@@ -62,6 +62,21 @@ MEASURED_TRAFFIC = {
 }
 
 
+# VALU instructions per launch (all waves, rocprofv3 SQ_INSTS_VALU) of the step's kernels, from the
+# counter run summarised in profiles/bench_step_n2048_l112_b8_sq_counters.md; like the traffic, valid
+# only for the kernel sources they were taken on.  A wave's VALU instruction issues in 4 cycles on
+# its SIMD (wave64 on 16 lanes; the 32-bit multiplies included, as measured on this GPU), so
+# 1024 SIMDs x 2.4 GHz / 4 = 614.4 G wave-instructions/s is the issue ceiling.
+MEASURED_SQ = {
+    "source_sha": None,
+    "valu_per_launch": {},
+}
+VALU_ISSUE_PEAK_G = 1024 * 2.4e9 / 4 / 1e9
+# Algorithmic bytes of one key switch of the step's shape (112 primes, K = 28, 4 digits) with the
+# key amortised over the batch of 8: input polynomial + key / 8 + two output polynomials.
+KS_BYTES = 7.44 * 2**20
+
+
 def csrc_sha() -> str:
     import hashlib
     d = os.path.join(ROOT, "rns_ckks_polynomial_amd", "csrc")
@@ -737,8 +752,21 @@ def main():
     roofline["frac"] = roofline["achieved"] / roofline["peak"] if roofline["achieved"] else None
     roofline["avg_launch_us"] = drow["avg_us"]
     roofline["kernel_ms_per_step"] = drow["total_ms_per_step"]
-    traffic_valid = csrc_sha() == MEASURED_TRAFFIC["source_sha"]
+    sha = csrc_sha()
+    traffic_valid = sha == MEASURED_TRAFFIC["source_sha"]
     launches = drow["launches"] // args.profile_steps
+    # VALU issue: the counted instructions of the dominant kernel over its live launch time.  When it
+    # exceeds the fraction above, the kernel is bound by the vector ALU: reported as such, with the
+    # HBM fraction kept beside it.
+    if sha == MEASURED_SQ["source_sha"] and dom in MEASURED_SQ["valu_per_launch"]:
+        vi = MEASURED_SQ["valu_per_launch"][dom]
+        rate = vi / (drow["avg_us"] * 1e-6) / 1e9
+        roofline["valu_issue"] = rate / VALU_ISSUE_PEAK_G
+        if roofline["frac"] is None or roofline["valu_issue"] > roofline["frac"]:
+            roofline["frac_" + roofline["bound"]] = roofline["frac"]
+            roofline.update({"bound": "alu", "achieved": rate, "peak": VALU_ISSUE_PEAK_G,
+                             "unit": "G VALU wave-instructions/s", "frac": roofline["valu_issue"],
+                             "work_per_launch": f"{vi} VALU wave-instructions (rocprofv3 SQ_INSTS_VALU)"})
     if traffic_valid and dom in MEASURED_TRAFFIC["bytes_per_launch"]:
         roofline["traffic"] = MEASURED_TRAFFIC["bytes_per_launch"][dom]
         roofline["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
@@ -763,6 +791,9 @@ def main():
                                "and BSGS 32x32 linear transform + rescale at 112 primes",
                    "global_batch": BATCH, "parallelism": "single GPU"},
         "key_switches_per_step": ks_per_step,
+        "key_switch_hbm": {"algorithmic_bytes": KS_BYTES,
+                           "GBps": ks_per_step / (ms * 1e-3) * KS_BYTES / 1e9,
+                           "frac": ks_per_step / (ms * 1e-3) * KS_BYTES / (HBM_PEAK_GBS * 1e9)},
         "eval_mod": em,
         "bootstrap": boot,
         "seeded_keys": seeded,
