@@ -1065,7 +1065,7 @@ __global__ __launch_bounds__(256) void k_final2048(const uint64_t *__restrict__ 
     uint64_t av[8], c0v[8];
 #pragma unroll
     for (int m = 0; m < 8; m++) av[m] = ar[t + 256 * m];
-    if (MODE == 2) {  // c == 1 reads the same (valid) row and leaves it unused
+    if (MODE == 2 && c == 0) {  // workgroup-uniform: only the c0 rows take the rotated input
         const uint64_t *c0 = xa + (b * 2) * per + (size_t)i * n;
 #pragma unroll
         for (int m = 0; m < 8; m++) c0v[m] = c0[t + 256 * m];
