@@ -45,19 +45,24 @@ LIMB = N * 8
 # counters (profiles/bench_step_n2048_l112_b8_hbm_counters.md).  Valid only for
 # the kernel sources they were taken on (hash of rns_ckks_polynomial_amd/csrc).
 MEASURED_TRAFFIC = {
-    "source_sha": "4f114efab59696aa",
+    "source_sha": "912f85cd1fe51aac",
     "bytes_per_launch": {
-        "ks_modup_convert": 812080786,
-        "ks_moddown_convert": 733236013,
-        "bsgs_mac": 3758192646,
-        "ks_ntt_ext": 1335593752,
-        "ks_inner_product_sum": 2848518456,
-        "rotate_final": 3190134720,
-        "ntt_fwd": 62570852,
-        "ntt_inv": 62590179,
-        "giant_final": 304298430,
-        "ks_intt_modup": 326831241,
-        "ks_intt_moddown": 310288366
+        "ks_ntt_ext": 1350414757,
+        "ks_modup_convert": 855285937,
+        "bsgs_mac": 4095323483,
+        "rotate_final": 3190067438,
+        "ks_inner_product_sum": 2848772334,
+        "ks_inner_product_hoisted": 1870289097,
+        "giant_final": 304433993,
+        "ks_intt_modup": 326845105,
+        "ks_intt_moddown": 310310278,
+        "ks_inner_product": 462667502,
+        "ntt_fwd": 62560256,
+        "ntt_inv": 62600064,
+        "ks_moddown_u": 231752741,
+        "relin_final": 155666213,
+        "rescale_final": 118597111,
+        "ks_moddown_convert": 772462238
     },
 }
 
@@ -68,8 +73,25 @@ MEASURED_TRAFFIC = {
 # its SIMD (wave64 on 16 lanes; the 32-bit multiplies included, as measured on this GPU), so
 # 1024 SIMDs x 2.4 GHz / 4 = 614.4 G wave-instructions/s is the issue ceiling.
 MEASURED_SQ = {
-    "source_sha": None,
-    "valu_per_launch": {},
+    "source_sha": "912f85cd1fe51aac",
+    "valu_per_launch": {
+        "ks_ntt_ext": 166290432,
+        "ks_modup_convert": 109711360,
+        "bsgs_mac": 173752320,
+        "rotate_final": 321090560,
+        "ks_inner_product_sum": 111356672,
+        "ks_inner_product_hoisted": 179894400,
+        "giant_final": 12565504,
+        "ks_intt_modup": 51606016,
+        "ks_intt_moddown": 48996864,
+        "ks_inner_product": 24222464,
+        "ntt_fwd": 7562240,
+        "ntt_inv": 9210880,
+        "ks_moddown_u": 10110464,
+        "relin_final": 13712384,
+        "rescale_final": 10471296,
+        "ks_moddown_convert": 81438037
+    },
 }
 VALU_ISSUE_PEAK_G = 1024 * 2.4e9 / 4 / 1e9
 # Algorithmic bytes of one key switch of the step's shape (112 primes, K = 28, 4 digits) with the
@@ -779,6 +801,9 @@ def main():
     if ntt_roof["achieved"]:
         ntt_roof["frac"] = ntt_roof["achieved"] / HBM_PEAK_GBS
     ntt_roof["traffic"] = MEASURED_TRAFFIC["bytes_per_launch"].get("ntt_fwd") if traffic_valid else None
+    if sha == MEASURED_SQ["source_sha"] and ntt_row.get("avg_us") and "ntt_fwd" in MEASURED_SQ["valu_per_launch"]:
+        ntt_roof["valu_issue"] = (MEASURED_SQ["valu_per_launch"]["ntt_fwd"] / (ntt_row["avg_us"] * 1e-6) / 1e9
+                                  / VALU_ISSUE_PEAK_G)
 
     out = {
         "metric": "limb-NTTs/s + key-switches/s @n=2048,112 primes; % HBM roofline",
