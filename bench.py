@@ -563,6 +563,10 @@ def kernel_work():
         "ks_moddown_convert": {"products": n_dn * 2 * K * l * N,
                                "bytes": (n_dn * 2 * K + (1 + sb + 1) * B * 2 * l) * limb},
         "rotate_final": {"bytes": sb * B * 7 * l * limb},
+        # accumulators, converted P-part, both input ciphertexts in, the product out
+        "relin_final": {"bytes": B * 2 * l * 5 * limb},
+        # two rescales per step (the product and the transform's output): 2l limbs in, 2(l - 1) out
+        "rescale_final": {"bytes": 2 * B * 2 * (2 * l - 1) * limb},
         # conv in, 4 partial sums in, output read + written
         "giant_final": {"bytes": B * 2 * l * (1 + 4 + 2) * limb},
         "bsgs_mac": {"mads": 4 * GS * BS * 2 * B * l * N,

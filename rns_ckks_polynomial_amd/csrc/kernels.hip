@@ -157,11 +157,13 @@ __global__ __launch_bounds__(256) void k_ntt2048(Map map, const PrimeConsts *__r
 // mp_scratch: the operation's transpose buffer for rings above one LDS tile
 // (mp_scratch_words words), or null for the context's (the bare NTT calls).
 template <class Map>
+// gal != 1 (forward, n > 2048 only): outputs permuted by the automorphism of that Galois element.
 static int launch_ntt(const ckks_ctx *c, const Map &map, int nblk, bool inverse, hipStream_t s, const char *name,
-                      uint64_t *mp_scratch) {
+                      uint64_t *mp_scratch, uint32_t gal = 1) {
     if (nblk <= 0) return CKKS_OK;
     ProfScope ps(c, name, s);
     if (c->n == 2048) {
+        if (gal != 1) return CKKS_EUNSUPPORTED;
         if (inverse)
             hipLaunchKernelGGL((k_ntt2048<Map, true>), dim3(nblk), dim3(256), 0, s, map, c->d_pc, c->d_tw_fwd,
                                c->d_tw_inv);
@@ -171,7 +173,7 @@ static int launch_ntt(const ckks_ctx *c, const Map &map, int nblk, bool inverse,
         LAUNCH_CHECK();
         return CKKS_OK;
     }
-    return multipass_ntt(c, map, nblk, inverse, s, mp_scratch);
+    return multipass_ntt(c, map, nblk, inverse, s, mp_scratch, gal);
 }
 
 int op_ntt(const ckks_ctx *c, uint64_t *x, int count, int first, int nlimbs, bool inverse, hipStream_t s) {
@@ -928,7 +930,7 @@ template <bool SEEDED>
 __global__ void k_inner(const uint64_t *__restrict__ d, size_t d_stride, const uint64_t *__restrict__ ext,
                         const uint64_t *__restrict__ key, uint64_t *__restrict__ acc,
                         const PrimeConsts *__restrict__ pc, uint32_t n, uint32_t l, uint32_t L, uint32_t K,
-                        uint32_t beta, uint32_t alpha, uint32_t g, uint64_t root, uint32_t B) {
+                        uint32_t beta, uint32_t alpha, uint32_t g, uint32_t ge, uint64_t root, uint32_t B) {
     const uint32_t el = l + K;
     const size_t total = (size_t)el * n;
     for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total;
@@ -936,10 +938,10 @@ __global__ void k_inner(const uint64_t *__restrict__ d, size_t d_stride, const u
         const uint32_t k = idx % n;
         const uint32_t e = idx / n;
         const uint32_t gi = e < l ? e : L + (e - l);
-        const uint32_t ks = galois_src(k, g, n);
+        const uint32_t ks = galois_src(k, g, n), kx = galois_src(k, ge, n);
         auto digit = [&](size_t b, uint32_t j) -> uint64_t {
             const bool own = e >= j * alpha && e < min(l, (j + 1) * alpha);
-            return own ? d[b * d_stride + (size_t)e * n + ks] : ext[((b * beta + j) * el + e) * n + ks];
+            return own ? d[b * d_stride + (size_t)e * n + ks] : ext[((b * beta + j) * el + e) * n + kx];
         };
         auto key_b = [&](uint32_t j) -> uint64_t {
             return key[((size_t)j * (SEEDED ? 1 : 2) * (L + K) + gi) * n + k];
@@ -997,39 +999,81 @@ __global__ void k_inner(const uint64_t *__restrict__ d, size_t d_stride, const u
     }
 }
 
-// out[b][c][i][k] = (acc[b][c][i][k] - conv[b][c][i][k]) P^-1 + extra
-//   MODE 0: no extra; 1: relin (c0: a0 b0, c1: a0 b1 + a1 b0); 2: rotate (c0: in[b][0][i][galois]);
-//   ACCUM: out += result instead of out = result
+// Fused ModDown tail for n > 2048 (four-step NTT): the row pass of the converted
+// P-part's forward NTT (its column pass left it in the transpose buffer), then
+//   out[b][c][i][k] = (acc[b][c][i][k] - NTT(conv)[b][c][i][k]) P^-1 + extra
+//   MODE 1: relin (c0: a0 b0, c1: a0 b1 + a1 b0); 2: rotate (c0: in[b][0][i][galois]);
+//   ACCUM: out += result instead of out = result.
+// blockIdx.y: limb limb0 + y of the [nout][2][l][n] set; the NTT values meet
+// their accumulator in registers instead of a round trip through memory.
 template <int MODE, bool ACCUM>
-__global__ void k_moddown_final(const uint64_t *__restrict__ acc, const uint64_t *__restrict__ conv,
-                                const uint64_t *__restrict__ pinv, const PrimeConsts *__restrict__ pc,
-                                const uint64_t *__restrict__ xa, const uint64_t *__restrict__ xb, uint32_t g,
-                                uint64_t *__restrict__ out, uint32_t n, uint32_t l, uint32_t K, size_t total) {
-    const uint32_t el = l + K;
-    for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total;
-         idx += (size_t)gridDim.x * blockDim.x) {
-        const uint32_t k = idx % n;
-        const uint32_t i = (idx / n) % l;
-        const uint32_t c = (idx / ((size_t)n * l)) % 2;
-        const size_t b = idx / ((size_t)n * l * 2);
-        const PrimeConsts &P = pc[i];
-        const uint64_t q = P.q;
-        const uint64_t a = acc[((b * 2 + c) * el + i) * n + k];
-        const uint64_t cv = conv[idx];
-        uint64_t r = shoup(subm(a, cv, q), pinv[2 * i], pinv[2 * i + 1], q);
-        const size_t per = (size_t)l * n;
-        if (MODE == 1) {
-            const size_t o0 = (b * 2) * per + (size_t)i * n + k, o1 = o0 + per;
-            uint64_t x;
-            if (c == 0) x = mulm(xa[o0], xb[o0], q, P.mu);
-            else x = addm(mulm(xa[o0], xb[o1], q, P.mu), mulm(xa[o1], xb[o0], q, P.mu), q);
-            r = addm(r, x, q);
-        } else if (MODE == 2) {
-            if (c == 0) r = addm(r, xa[(b * 2) * per + (size_t)i * n + galois_src(k, g, n)], q);
-        }
-        if (ACCUM) r = addm(r, out[idx], q);
-        out[idx] = r;
+__global__ __launch_bounds__(mp::NT) void k_rows_final(uint32_t limb0, const PrimeConsts *__restrict__ pc,
+                                                       const uint64_t *__restrict__ rowf,
+                                                       const uint64_t *__restrict__ scratch,
+                                                       const uint64_t *__restrict__ acc,
+                                                       const uint64_t *__restrict__ pinv,
+                                                       const uint64_t *__restrict__ xa,
+                                                       const uint64_t *__restrict__ xb, uint32_t g,
+                                                       uint64_t *__restrict__ out, uint32_t l, uint32_t K) {
+    using namespace mp;
+    constexpr uint32_t n = MP_N1 * MP_N1;
+    __shared__ uint64_t lds[V * VSTRIDE];
+    const uint32_t limb = limb0 + blockIdx.y;
+    const uint32_t i = limb % l, c = (limb / l) % 2;
+    const size_t b = limb / (2 * l);
+    const uint64_t q = pc[i].q, mu = pc[i].mu;
+    const int r0 = blockIdx.x * V;
+    {
+        const BfConsts bc = bf_consts(q);
+        const uint64_t *in = scratch + (size_t)blockIdx.y * n;
+        const int t = threadIdx.x % 16, v = threadIdx.x / 16;  // lanes along a row
+        uint64_t x[E];
+#pragma unroll
+        for (int k = 0; k < E; k++) x[k] = in[sidx(r0 + v, t + 16 * k)];
+        fwd(x, lds, v, t, rowf + ((size_t)i * 16 + ((r0 + v) >> 4)) * MP_N1 * 2, bc);
     }
+    const int v = threadIdx.x % V, t = threadIdx.x / V;  // lanes across rows: 128-byte runs of the limb
+    const size_t per = (size_t)l * n;
+    const uint64_t *ap = acc + ((b * 2 + c) * (l + K) + i) * n;
+    const uint64_t *x0 = xa + (b * 2) * per + (size_t)i * n;  // MODE 1: a0 (a1 one polynomial on); 2: c0
+    const uint64_t *y0 = MODE == 1 ? xb + (b * 2) * per + (size_t)i * n : nullptr;
+    uint64_t *op = out + (size_t)limb * n;
+    const uint64_t w = pinv[2 * i], wp = pinv[2 * i + 1];
+#pragma unroll 4
+    for (int k = 0; k < E; k++) {
+        const uint32_t j = (uint32_t)(r0 + v) + MP_N1 * (uint32_t)(t + 16 * k);
+        const uint64_t nt = reduce_out(lds[slot(v, t + 16 * k)], q);
+        uint64_t r = shoup(subm(ap[j], nt, q), w, wp, q);
+        if (MODE == 1) {
+            uint64_t e;
+            if (c == 0) e = mulm(x0[j], y0[j], q, mu);
+            else e = addm(mulm(x0[j], y0[j + per], q, mu), mulm(x0[j + per], y0[j], q, mu), q);
+            r = addm(r, e, q);
+        } else if (MODE == 2) {
+            if (c == 0) r = addm(r, x0[galois_src(j, g, n)], q);
+        }
+        if (ACCUM) r = addm(r, op[j], q);
+        op[j] = r;
+    }
+}
+
+// conv, acc: the key switch's converted P-part and accumulators; mps: its transpose buffer.
+template <int MODE, bool ACCUM>
+static int moddown_final_mp(const ckks_ctx *c, uint64_t *conv, const uint64_t *acc, uint64_t *mps, size_t nout,
+                            int l, const uint64_t *xa, const uint64_t *xb, uint32_t g, uint64_t *out, hipStream_t s) {
+    const MultipassPlan *p = c->mp;
+    if (!p || !mps) return CKKS_EUNSUPPORTED;
+    const int nblk = (int)(nout * 2 * l);
+    MapStrided m{conv, conv, c->n, (uint32_t)l, 0, nullptr};
+    for (int l0 = 0; l0 < nblk; l0 += MP_CHUNK) {
+        const dim3 grid(MP_N1 / mp::V, (unsigned)std::min<int>(MP_CHUNK, nblk - l0)), blk(mp::NT);
+        hipLaunchKernelGGL(mp::k_fwd_cols<MapStrided>, grid, blk, 0, s, m, (uint32_t)l0, c->d_pc, p->d_tw256f,
+                           p->d_taf, mps);
+        hipLaunchKernelGGL((k_rows_final<MODE, ACCUM>), grid, blk, 0, s, (uint32_t)l0, c->d_pc, p->d_rowf,
+                           (const uint64_t *)mps, acc, c->d_pinv, xa, xb, g, out, (uint32_t)l, c->K);
+        LAUNCH_CHECK();
+    }
+    return CKKS_OK;
 }
 
 // n = 2048 fused ModDown tail: one workgroup per (output ciphertext cb,
@@ -1503,8 +1547,10 @@ static void launch_convert(const ckks_ctx *c, const BasisDev *bases, const SetLa
                            c->d_pc);
 }
 
+// gal != 1 (n > 2048): the extended digits come out of their NTT already permuted by that
+// automorphism (the own-prime limbs, which the NTT does not touch, stay unpermuted).
 static int ks_modup(const ckks_ctx *c, const LevelTables *lt, int B, int l, const uint64_t *d, size_t d_stride, const KsWs &w,
-                    hipStream_t s) {
+                    hipStream_t s, uint32_t gal = 1) {
     const uint32_t n = c->n, K = c->K, L = c->L, el = l + K, beta = lt->beta;
     int e;
     {  // y = iNTT(d) scaled by [Bhat_i^-1]
@@ -1527,7 +1573,7 @@ static int ks_modup(const ckks_ctx *c, const LevelTables *lt, int B, int l, cons
     LAUNCH_CHECK();
     {
         MapExt m{w.ext, n, (uint32_t)l, L, K, beta, c->alpha};
-        if ((e = launch_ntt(c, m, B * beta * el, false, s, "ks_ntt_ext", w.mp))) return e;
+        if ((e = launch_ntt(c, m, B * beta * el, false, s, "ks_ntt_ext", w.mp, gal))) return e;
     }
     return CKKS_OK;
 }
@@ -1551,8 +1597,10 @@ static Steps one_step(const ckks_swk *key, uint32_t g, int B) {
 
 // Inner product of sigma_g(ModUp(d)) with the keys of a batch of steps:
 // leaves st.count * st.B accumulator pairs in w.acc.
+// ext_permuted (generic n, one step): ks_modup already applied the step's automorphism
+// to the extended digits, which are then read in place.
 static int ks_inner(const ckks_ctx *c, const LevelTables *lt, int l, const uint64_t *d, size_t d_stride, const Steps &st,
-                    const KsWs &w, hipStream_t s) {
+                    const KsWs &w, hipStream_t s, bool ext_permuted = false) {
     const uint32_t n = c->n, K = c->K, L = c->L, el = l + K, beta = lt->beta;
     const size_t nout = (size_t)st.count * st.B;
     ProfScope ps_(c, st.shared ? "ks_inner_product_hoisted" : "ks_inner_product", s);
@@ -1565,12 +1613,14 @@ static int ks_inner(const ckks_ctx *c, const LevelTables *lt, int l, const uint6
         hipLaunchKernelGGL(kern, dim3(xcd_blocks(st.count * el, st.B)), dim3(256), 0, s, d, d_stride, w.ext, st,
                            w.acc, c->d_pc, (uint32_t)l, L, K, beta, c->alpha, 0u, el);
     } else {  // generic n: one launch per step
+        if (ext_permuted && st.count != 1) return CKKS_EINVAL;
         auto kern = st.seeded ? k_inner<true> : k_inner<false>;
         for (uint32_t j = 0; j < st.count; j++) {
             const size_t in_off = st.shared ? 0 : (size_t)j * st.B;
             hipLaunchKernelGGL(kern, grid_for((size_t)el * n), dim3(256), 0, s, d + in_off * d_stride, d_stride,
                                w.ext + in_off * beta * el * n, st.key[j], w.acc + (size_t)j * st.B * 2 * el * n,
-                               c->d_pc, n, (uint32_t)l, L, K, beta, c->alpha, st.g[j], st.root[j], st.B);
+                               c->d_pc, n, (uint32_t)l, L, K, beta, c->alpha, st.g[j], ext_permuted ? 1u : st.g[j],
+                               st.root[j], st.B);
         }
     }
     LAUNCH_CHECK();
@@ -1604,8 +1654,9 @@ static int ks_inner_giant(const ckks_ctx *c, const LevelTables *lt, int l, const
     return CKKS_OK;
 }
 
-// ModDown of nout accumulator pairs up to the converted P-part in w.conv
-// (NTT domain for n != 2048; at n = 2048 the final kernels transform it).
+// ModDown of nout accumulator pairs up to the converted P-part in w.conv, in
+// coefficient form: the final kernels transform it (k_final2048, or the fused
+// row pass of moddown_final_mp).
 // With nsum > 1 the conversions of accumulators o + j (nout / nsum), j < nsum,
 // are summed (n = 2048 giant steps) in *nparts partial sums: part p of output
 // o at w.conv pair p (nout / nsum) + o.
@@ -1638,10 +1689,6 @@ static int ks_moddown_conv(const ckks_ctx *c, size_t nout, int l, const KsWs &w,
         launch_convert<1>(c, c->d_pbasis, lay_dn, w.acc, w.uP, ct, w.conv, (uint32_t)l, np * ct.sum_stride, c->K, s);
     }
     LAUNCH_CHECK();
-    if (n != 2048) {
-        MapStrided m{w.conv, w.conv, n, (uint32_t)l, 0, nullptr};
-        if ((e = launch_ntt(c, m, (int)(nout * 2 * l), false, s, "ks_ntt_moddown", w.mp))) return e;
-    }
     return CKKS_OK;
 }
 
@@ -1727,15 +1774,13 @@ int op_mul_tensor_relin(const ckks_ctx *c, const uint64_t *a, const uint64_t *b,
     if ((e = ks_modup(c, lt, B, l, w.d, per, w, s))) return e;
     if ((e = ks_inner(c, lt, l, w.d, per, st, w, s))) return e;
     if ((e = ks_moddown_conv(c, B, l, w, s))) return e;
-    tot = (size_t)B * 2 * l * n;
     {
         ProfScope ps_(c, "relin_final", s);
         if (n == 2048)
             hipLaunchKernelGGL((k_final2048<1, false>), dim3(B * 2 * l), dim3(256), 0, s, w.acc, w.conv, c->d_pinv,
                                c->d_pc, c->d_tw_fwd, a, b, st, out, (uint32_t)l, c->K);
-        else
-            hipLaunchKernelGGL((k_moddown_final<1, false>), grid_for(tot), dim3(256), 0, s, w.acc, w.conv,
-                               c->d_pinv, c->d_pc, a, b, 0u, out, n, (uint32_t)l, c->K, tot);
+        else if ((e = moddown_final_mp<1, false>(c, w.conv, w.acc, w.mp, B, l, a, b, 0u, out, s)))
+            return e;
     }
     LAUNCH_CHECK();
     return CKKS_OK;
@@ -1745,7 +1790,6 @@ int op_mul_tensor_relin(const ckks_ctx *c, const uint64_t *a, const uint64_t *b,
 static int rotate_final(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int l, const Steps &st, const KsWs &w,
                         bool accumulate, hipStream_t s) {
     const size_t nout = (size_t)st.count * st.B;
-    const size_t tot = nout * 2 * l * c->n;
     const uint64_t *nul = nullptr;
     ProfScope ps_(c, accumulate ? "rotate_final_acc" : "rotate_final", s);
     if (c->n == 2048) {
@@ -1755,20 +1799,20 @@ static int rotate_final(const ckks_ctx *c, const uint64_t *in, uint64_t *out, in
         else
             hipLaunchKernelGGL((k_final2048<2, false>), dim3(nout * 2 * l), dim3(256), 0, s, w.acc, w.conv,
                                c->d_pinv, c->d_pc, c->d_tw_fwd, in, nul, st, out, (uint32_t)l, c->K);
-    } else {  // generic n: single step
-        if (accumulate)
-            hipLaunchKernelGGL((k_moddown_final<2, true>), grid_for(tot), dim3(256), 0, s, w.acc, w.conv, c->d_pinv,
-                               c->d_pc, in, nul, st.g[0], out, c->n, (uint32_t)l, c->K, tot);
-        else
-            hipLaunchKernelGGL((k_moddown_final<2, false>), grid_for(tot), dim3(256), 0, s, w.acc, w.conv,
-                               c->d_pinv, c->d_pc, in, nul, st.g[0], out, c->n, (uint32_t)l, c->K, tot);
+    } else {  // larger rings: single step
+        const int e = accumulate ? moddown_final_mp<2, true>(c, w.conv, w.acc, w.mp, nout, l, in, nul, st.g[0], out, s)
+                                 : moddown_final_mp<2, false>(c, w.conv, w.acc, w.mp, nout, l, in, nul, st.g[0], out, s);
+        if (e) return e;
     }
     LAUNCH_CHECK();
     return CKKS_OK;
 }
 
-// Rotation: ModUp of c1 as stored (no permuted copy), the automorphism applied
-// as a gather of the extended digits inside the key inner product.
+// Rotation: ModUp of c1 as stored (no permuted copy).  At n = 2048 the automorphism
+// is a gather of the extended digits inside the key inner product; for larger rings
+// the row pass of the extended digits' NTT writes them permuted (a gather there
+// would touch a different line per residue), and only the digit's own limbs, read
+// from c1, are gathered.
 int op_rotate(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l, uint32_t g, const ckks_swk *key,
               void *ws, bool accumulate, hipStream_t s) {
     int e = CKKS_OK;
@@ -1779,8 +1823,9 @@ int op_rotate(const ckks_ctx *c, const uint64_t *in, uint64_t *out, int B, int l
     const size_t per = (size_t)l * c->n;
     const uint64_t *c1 = in + per;
     const Steps st = one_step(key, g, B);
-    if ((e = ks_modup(c, lt, B, l, c1, 2 * per, w, s))) return e;
-    if ((e = ks_inner(c, lt, l, c1, 2 * per, st, w, s))) return e;
+    const bool fold = c->n > 2048;
+    if ((e = ks_modup(c, lt, B, l, c1, 2 * per, w, s, fold ? g : 1u))) return e;
+    if ((e = ks_inner(c, lt, l, c1, 2 * per, st, w, s, fold))) return e;
     if ((e = ks_moddown_conv(c, B, l, w, s))) return e;
     return rotate_final(c, in, out, l, st, w, accumulate, s);
 }

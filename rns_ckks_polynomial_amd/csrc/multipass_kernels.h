@@ -5,8 +5,10 @@
 // register passes with one LDS exchange (forward: bits 7..4 then 3..0,
 // merged-psi Cooley-Tukey; inverse: Gentleman-Sande in the mirror order).
 // The thread -> (vector, lane) assignment is chosen per kernel so that every
-// global access is a run of 16 consecutive uint64 (128 bytes).  Butterflies are
-// the lazy forms of butterfly.h.
+// global access is a run of at least 16 consecutive uint64 (128 bytes).  The
+// transpose buffer is blocked by V columns (sidx), so the column kernels move one
+// contiguous block and the row kernels 2 KiB runs.
+// Butterflies are the lazy forms of butterfly.h.
 #pragma once
 #include "butterfly.h"
 #include "multipass.h"
@@ -16,9 +18,20 @@ namespace mp {
 
 constexpr int LOG = 8, E = 16, V = 16;
 constexpr int NT = 16 * V;  // threads per workgroup: 16 per vector
-constexpr int VSTRIDE = 264;  // LDS words per vector (256 + padding)
+// LDS words per vector: 256 + one pad word per 16.  The column kernels put consecutive
+// vectors in consecutive lanes, the row kernels consecutive elements of one vector; with
+// this stride and padding every exchange pattern of both (own<4>, own<0> and their bit
+// reversals) spreads a half-wave's 64-bit accesses evenly over the banks (264 with a pad
+// per 32, the stride for the row layout alone, put 8 to 16 lanes of a column kernel on one
+// bank).
+constexpr int VSTRIDE = 273;
 
-__device__ __forceinline__ int slot(int v, int i) { return v * VSTRIDE + i + (i >> 5); }
+// Word of element (row j1, column i2) of a limb in the transpose buffer: blocks of V columns.
+__device__ __forceinline__ uint32_t sidx(uint32_t j1, uint32_t i2) {
+    return (i2 / V) * (MP_N1 * V) + j1 * V + i2 % V;
+}
+
+__device__ __forceinline__ int slot(int v, int i) { return v * VSTRIDE + i + (i >> 4); }
 template <int C>
 __device__ __forceinline__ int own(int t, int k) {  // element k of lane t in a pass owning bits [C, C+4)
     return (t & ((1 << C) - 1)) | (k << C) | ((t >> C) << (C + 4));
@@ -120,15 +133,20 @@ __global__ __launch_bounds__(NT) void k_fwd_cols(Map map, uint32_t limb0, const 
 #pragma unroll
     for (int k = 0; k < E; k++) {
         const int j1 = t + 16 * k;
-        o[(size_t)j1 * MP_N1 + c0 + v] = shoup_lazy4(lds[slot(v, j1)], w, wp, 0 - c.q);  // [0, 4q)
+        o[sidx(j1, c0 + v)] = shoup_lazy4(lds[slot(v, j1)], w, wp, 0 - c.q);  // [0, 4q)
     }
 }
 
-// ---- forward pass 2: rows j1 in [16 bx, +16) of scratch (k = bx); outputs A[j1 + 256 j2] -> dst
-template <class Map>
+// ---- forward pass 2: rows j1 in [16 bx, +16) of scratch (k = bx); outputs A[j1 + 256 j2] -> dst.
+// GAL: the outputs come out permuted by the automorphism X -> X^g (odd g < 2n), out[j] = A[g j + (g-1)/2
+// mod n].  With j = j1 + 256 j2 the source index splits as j1' = (g j1 + (g-1)/2) mod 256 and
+// j2' = (g j2 + floor((g j1 + (g-1)/2) / 256)) mod 256, so output row j1 is the transform of row j1'
+// read in a permuted order: the workgroup transforms the rows j1' of its 16 output rows (each with the
+// twiddles of its own group j1' / 16) and gathers from LDS.
+template <class Map, bool GAL>
 __global__ __launch_bounds__(NT) void k_fwd_rows(Map map, uint32_t limb0, const PrimeConsts *__restrict__ pc,
                                                    const uint64_t *__restrict__ rowf,
-                                                   const uint64_t *__restrict__ scratch) {
+                                                   const uint64_t *__restrict__ scratch, uint32_t g) {
     __shared__ uint64_t lds[V * VSTRIDE];
     const uint64_t *src;
     uint64_t *dst;
@@ -143,16 +161,19 @@ __global__ __launch_bounds__(NT) void k_fwd_rows(Map map, uint32_t limb0, const 
     const uint64_t *in = scratch + (size_t)blockIdx.y * MP_N1 * MP_N1;
     {
         const int t = threadIdx.x % 16, v = threadIdx.x / 16;  // lanes along a row
+        const uint32_t row = GAL ? ((g * (uint32_t)(r0 + v) + (g >> 1)) & (MP_N1 - 1)) : (uint32_t)(r0 + v);
         uint64_t x[E];
 #pragma unroll
-        for (int k = 0; k < E; k++) x[k] = in[(size_t)(r0 + v) * MP_N1 + t + 16 * k];
-        fwd(x, lds, v, t, rowf + ((size_t)prime * 16 + (r0 >> 4)) * MP_N1 * 2, c);
+        for (int k = 0; k < E; k++) x[k] = in[sidx(row, t + 16 * k)];
+        fwd(x, lds, v, t, rowf + ((size_t)prime * 16 + (row >> 4)) * MP_N1 * 2, c);
     }
     const int v = threadIdx.x % V, t = threadIdx.x / V;  // lanes across rows for the transposed store
+    const uint32_t carry = GAL ? (g * (uint32_t)(r0 + v) + (g >> 1)) >> MP_LOG1 : 0;
 #pragma unroll
     for (int k = 0; k < E; k++) {
-        const int j2 = t + 16 * k;
-        dst[(size_t)(r0 + v) + (size_t)MP_N1 * j2] = reduce_out(lds[slot(v, j2)], q);
+        const uint32_t j2 = t + 16 * k;
+        const uint32_t from = GAL ? ((g * j2 + carry) & (MP_N1 - 1)) : j2;
+        dst[(size_t)(r0 + v) + (size_t)MP_N1 * j2] = reduce_out(lds[slot(v, from)], q);
     }
 }
 
@@ -175,7 +196,7 @@ __global__ __launch_bounds__(NT) void k_inv_rows(Map map, uint32_t limb0, const 
         uint64_t x[E];
 #pragma unroll
         for (int k = 0; k < E; k++) x[k] = src[(size_t)(r0 + v) + (size_t)MP_N1 * (t + 16 * k)];
-        inv(x, lds, v, t, rowi + ((size_t)prime * 16 + (r0 >> 4)) * MP_N1 * 2, c);
+        inv(x, lds, v, t, rowi + ((size_t)prime * 16 + ((r0 + v) >> 4)) * MP_N1 * 2, c);
 #pragma unroll
         for (int k = 0; k < E; k++) lds[slot(v, t + 16 * k)] = x[k];
     }
@@ -183,7 +204,7 @@ __global__ __launch_bounds__(NT) void k_inv_rows(Map map, uint32_t limb0, const 
     const int t = threadIdx.x % 16, v = threadIdx.x / 16;
     uint64_t *o = scratch + (size_t)blockIdx.y * MP_N1 * MP_N1;
 #pragma unroll
-    for (int k = 0; k < E; k++) o[(size_t)(r0 + v) * MP_N1 + t + 16 * k] = lds[slot(v, t + 16 * k)];
+    for (int k = 0; k < E; k++) o[sidx(r0 + v, t + 16 * k)] = lds[slot(v, t + 16 * k)];
 }
 
 // ---- inverse pass 2: columns i2 = 16 bx + v of scratch; times TA^-1, inverse; scale -> dst[256 i1 + i2]
@@ -208,7 +229,7 @@ __global__ __launch_bounds__(NT) void k_inv_cols(Map map, uint32_t limb0, const 
     const uint64_t *in = scratch + (size_t)blockIdx.y * MP_N1 * MP_N1;
     uint64_t x[E];
 #pragma unroll
-    for (int k = 0; k < E; k++) x[k] = shoup_lazy4(in[(size_t)(t + 16 * k) * MP_N1 + c0 + v], wa, wap, 0 - c.q);
+    for (int k = 0; k < E; k++) x[k] = shoup_lazy4(in[sidx(t + 16 * k, c0 + v)], wa, wap, 0 - c.q);
     inv(x, lds, v, t, tw + (size_t)prime * MP_N1 * 2, c);
     const uint64_t w = sc ? sc[0] : P.ninv, wp = sc ? sc[1] : P.ninvp;
 #pragma unroll
@@ -222,7 +243,7 @@ __global__ __launch_bounds__(NT) void k_inv_cols(Map map, uint32_t limb0, const 
 
 template <class Map>
 static int multipass_launch(const ckks_ctx *c, const Map &map, int nblk, bool inverse, hipStream_t s,
-                            uint64_t *scratch) {
+                            uint64_t *scratch, uint32_t gal) {
     const MultipassPlan *p = c->mp;
     const dim3 blk(mp::NT);
     for (int l0 = 0; l0 < nblk; l0 += MP_CHUNK) {
@@ -230,8 +251,12 @@ static int multipass_launch(const ckks_ctx *c, const Map &map, int nblk, bool in
         if (!inverse) {
             hipLaunchKernelGGL(mp::k_fwd_cols<Map>, grid, blk, 0, s, map, (uint32_t)l0, c->d_pc, p->d_tw256f,
                                p->d_taf, scratch);
-            hipLaunchKernelGGL(mp::k_fwd_rows<Map>, grid, blk, 0, s, map, (uint32_t)l0, c->d_pc, p->d_rowf,
-                               (const uint64_t *)scratch);
+            if (gal == 1)
+                hipLaunchKernelGGL((mp::k_fwd_rows<Map, false>), grid, blk, 0, s, map, (uint32_t)l0, c->d_pc,
+                                   p->d_rowf, (const uint64_t *)scratch, 1u);
+            else
+                hipLaunchKernelGGL((mp::k_fwd_rows<Map, true>), grid, blk, 0, s, map, (uint32_t)l0, c->d_pc,
+                                   p->d_rowf, (const uint64_t *)scratch, gal);
         } else {
             hipLaunchKernelGGL(mp::k_inv_rows<Map>, grid, blk, 0, s, map, (uint32_t)l0, c->d_pc, p->d_rowi,
                                scratch);
@@ -245,14 +270,17 @@ static int multipass_launch(const ckks_ctx *c, const Map &map, int nblk, bool in
 
 // scratch: the caller's transpose buffer of mp_scratch_words(n) words, or null for
 // the context's, whose users wait for the previous user's event on their stream.
+// gal: an odd Galois element whose automorphism permutes the forward outputs
+// (1: natural order; ignored by the inverse).
 template <class Map>
-int multipass_ntt(const ckks_ctx *c, const Map &map, int nblk, bool inverse, hipStream_t s, uint64_t *scratch) {
+int multipass_ntt(const ckks_ctx *c, const Map &map, int nblk, bool inverse, hipStream_t s, uint64_t *scratch,
+                  uint32_t gal = 1) {
     MultipassPlan *p = c->mp;
     if (!p) return CKKS_EUNSUPPORTED;
-    if (scratch) return multipass_launch(c, map, nblk, inverse, s, scratch);
-    std::lock_guard<std::mutex> g(p->scratch_mu);
+    if (scratch) return multipass_launch(c, map, nblk, inverse, s, scratch, gal);
+    std::lock_guard<std::mutex> lk(p->scratch_mu);
     if (hipStreamWaitEvent(s, p->scratch_done, 0) != hipSuccess) return CKKS_EHIP;
-    const int e = multipass_launch(c, map, nblk, inverse, s, p->d_scratch);
+    const int e = multipass_launch(c, map, nblk, inverse, s, p->d_scratch, gal);
     if (hipEventRecord(p->scratch_done, s) != hipSuccess) return CKKS_EHIP;
     return e;
 }

@@ -86,7 +86,9 @@ def test_ring65536_ntt_round_trip():
 
 
 def test_ring65536_l40_relin_rotations_rescale():
-    """4 pairs at l=40: p = relin(tensor(x, y)); r_i = rotate(p, 2^i), i < 16; rescale all."""
+    """4 pairs at l=40: p = relin(tensor(x, y)); r_i = rotate(p, 2^i), i < 16; the
+    conjugation of p; rescale all.  Ciphertext 0 of every result and ciphertext 3
+    of the product, of one rotation and of the conjugation against the oracle."""
     g, o = gpu_ctx(*C5), oracle_ctx(*C5)
     l, B, n, tot = 40, 4, 65536, 48
     seed = 0xC0DE0005
@@ -103,6 +105,9 @@ def test_ring65536_l40_relin_rotations_rescale():
         r = g.rotate(p, galois_rot(n, 1 << i), rkeys[i % 4])
         rots.append(host(r)[0])
         rrs.append(host(g.rescale(r))[0])
+        if i == 5:
+            r5_3 = host(r)[3]
+    cj = host(g.rotate(p, galois_conj(n), rkeys[1]))
     say("n=65536 l=40: oracle, ciphertext 0")
     a0 = cfill(o, seed, synth.TAG_CT, 2, l).reshape(2, l, n)
     b0 = cfill(o, seed + 1, synth.TAG_CT, 2, l).reshape(2, l, n)
@@ -118,7 +123,12 @@ def test_ring65536_l40_relin_rotations_rescale():
     say("n=65536 l=40: oracle, ciphertext 3 (relin)")
     a3 = cfill(o, seed, synth.TAG_CT, 2, l, stream0=3 * 2 * l).reshape(2, l, n)
     b3 = cfill(o, seed + 1, synth.TAG_CT, 2, l, stream0=3 * 2 * l).reshape(2, l, n)
-    assert np.array_equal(ph[3], o.mul_tensor_relin(a3, b3, rl, l))
+    p3 = o.mul_tensor_relin(a3, b3, rl, l)
+    assert np.array_equal(ph[3], p3)
+    assert np.array_equal(r5_3, o.rotate(p3, galois_rot(n, 1 << 5), rk[1], l))
+    say("n=65536 l=40: oracle, conjugation of ciphertexts 0 and 3")
+    assert np.array_equal(cj[0], o.rotate(p0, galois_conj(n), rk[1], l))
+    assert np.array_equal(cj[3], o.rotate(p3, galois_conj(n), rk[1], l))
 
 
 def test_ring65536_two_streams():
