@@ -94,6 +94,20 @@ struct MapExt {  // converted limbs [B][beta][l+K][n]; skips the digit's own pri
     }
 };
 
+struct MapPolyPairs {  // [B][2][l][n] in place, visited as u = (b l + i) 2 + c (the two polynomials adjacent)
+    static constexpr bool split_out = false;
+    uint64_t *x;
+    uint32_t n, l;
+    __device__ __forceinline__ void get(int blk, const uint64_t *&s, uint64_t *&d, int &prime,
+                                        const uint64_t *&sc) const {
+        const uint32_t c = blk % 2, i = (blk / 2) % l, b = blk / (2 * l);
+        prime = i;
+        d = x + ((size_t)(b * 2 + c) * l + i) * n;
+        s = d;
+        sc = nullptr;
+    }
+};
+
 struct MapLast {  // last limb of each polynomial [P][l][n] -> dense [P][n]
     static constexpr bool split_out = false;
     const uint64_t *src;
@@ -1004,8 +1018,11 @@ __global__ void k_inner(const uint64_t *__restrict__ d, size_t d_stride, const u
 //   out[b][c][i][k] = (acc[b][c][i][k] - NTT(conv)[b][c][i][k]) P^-1 + extra
 //   MODE 1: relin (c0: a0 b0, c1: a0 b1 + a1 b0); 2: rotate (c0: in[b][0][i][galois]);
 //   ACCUM: out += result instead of out = result.
-// blockIdx.y: limb limb0 + y of the [nout][2][l][n] set; the NTT values meet
-// their accumulator in registers instead of a round trip through memory.
+// blockIdx.y: pair index u = limb0 + y (MapPolyPairs order: the two polynomials of
+// one (ciphertext, limb) are neighbours, so the workgroups that both read a0 and b0
+// of a relinearisation run back to back on one XCD and the second finds them in
+// L2); the NTT values meet their accumulator in registers instead of a round trip
+// through memory.
 template <int MODE, bool ACCUM>
 __global__ __launch_bounds__(mp::NT) void k_rows_final(uint32_t limb0, const PrimeConsts *__restrict__ pc,
                                                        const uint64_t *__restrict__ rowf,
@@ -1018,9 +1035,9 @@ __global__ __launch_bounds__(mp::NT) void k_rows_final(uint32_t limb0, const Pri
     using namespace mp;
     constexpr uint32_t n = MP_N1 * MP_N1;
     __shared__ uint64_t lds[V * VSTRIDE];
-    const uint32_t limb = limb0 + blockIdx.y;
-    const uint32_t i = limb % l, c = (limb / l) % 2;
-    const size_t b = limb / (2 * l);
+    const uint32_t u = limb0 + blockIdx.y, c = u % 2, i = (u / 2) % l;
+    const size_t b = u / (2 * l);
+    const size_t limb = (b * 2 + c) * l + i;
     const uint64_t q = pc[i].q, mu = pc[i].mu;
     const int r0 = blockIdx.x * V;
     {
@@ -1037,12 +1054,13 @@ __global__ __launch_bounds__(mp::NT) void k_rows_final(uint32_t limb0, const Pri
     const uint64_t *ap = acc + ((b * 2 + c) * (l + K) + i) * n;
     const uint64_t *x0 = xa + (b * 2) * per + (size_t)i * n;  // MODE 1: a0 (a1 one polynomial on); 2: c0
     const uint64_t *y0 = MODE == 1 ? xb + (b * 2) * per + (size_t)i * n : nullptr;
-    uint64_t *op = out + (size_t)limb * n;
+    uint64_t *op = out + limb * n;
     const uint64_t w = pinv[2 * i], wp = pinv[2 * i + 1];
+    const uint64_t *lb = lds + slot(v, t);
 #pragma unroll 4
     for (int k = 0; k < E; k++) {
         const uint32_t j = (uint32_t)(r0 + v) + MP_N1 * (uint32_t)(t + 16 * k);
-        const uint64_t nt = reduce_out(lds[slot(v, t + 16 * k)], q);
+        const uint64_t nt = reduce_out(lb[islot(16 * k)], q);
         uint64_t r = shoup(subm(ap[j], nt, q), w, wp, q);
         if (MODE == 1) {
             uint64_t e;
@@ -1064,10 +1082,10 @@ static int moddown_final_mp(const ckks_ctx *c, uint64_t *conv, const uint64_t *a
     const MultipassPlan *p = c->mp;
     if (!p || !mps) return CKKS_EUNSUPPORTED;
     const int nblk = (int)(nout * 2 * l);
-    MapStrided m{conv, conv, c->n, (uint32_t)l, 0, nullptr};
+    MapPolyPairs m{conv, c->n, (uint32_t)l};
     for (int l0 = 0; l0 < nblk; l0 += MP_CHUNK) {
         const dim3 grid(MP_N1 / mp::V, (unsigned)std::min<int>(MP_CHUNK, nblk - l0)), blk(mp::NT);
-        hipLaunchKernelGGL(mp::k_fwd_cols<MapStrided>, grid, blk, 0, s, m, (uint32_t)l0, c->d_pc, p->d_tw256f,
+        hipLaunchKernelGGL(mp::k_fwd_cols<MapPolyPairs>, grid, blk, 0, s, m, (uint32_t)l0, c->d_pc, p->d_tw256f,
                            p->d_taf, mps);
         hipLaunchKernelGGL((k_rows_final<MODE, ACCUM>), grid, blk, 0, s, (uint32_t)l0, c->d_pc, p->d_rowf,
                            (const uint64_t *)mps, acc, c->d_pinv, xa, xb, g, out, (uint32_t)l, c->K);

@@ -31,12 +31,15 @@ __device__ __forceinline__ uint32_t sidx(uint32_t j1, uint32_t i2) {
     return (i2 / V) * (MP_N1 * V) + j1 * V + i2 % V;
 }
 
-__device__ __forceinline__ int slot(int v, int i) { return v * VSTRIDE + i + (i >> 4); }
+// islot(a | b) = islot(a) + islot(b) for a and b without common bits, so the exchanges
+// are a per-thread base plus a compile-time offset per register.
+__device__ __forceinline__ constexpr int islot(int i) { return i + (i >> 4); }
+__device__ __forceinline__ int slot(int v, int i) { return v * VSTRIDE + islot(i); }
 template <int C>
 __device__ __forceinline__ int own(int t, int k) {  // element k of lane t in a pass owning bits [C, C+4)
     return (t & ((1 << C) - 1)) | (k << C) | ((t >> C) << (C + 4));
 }
-__device__ __forceinline__ int brev8(int i) { return (int)(__builtin_bitreverse32((uint32_t)i) >> 24); }
+__device__ __forceinline__ constexpr int brev8(int i) { return (int)(__builtin_bitreverse32((uint32_t)i) >> 24); }
 
 // One radix-2 stage (bit BIT) on the 16 registers of a pass owning bits [C, C+4);
 // tw holds the heap-ordered twiddles (index 2^s + b at stage s).
@@ -54,29 +57,37 @@ __device__ __forceinline__ void stage(uint64_t (&x)[E], int t, const uint64_t *_
     }
 }
 
-// Forward: x[k] = element t + 16k (natural, < 8q) of vector v on entry; on
+// Forward: x[k] = element t + 16k (natural, < 4q) of vector v on entry; on
 // exit the transform sits in lds in natural order, values < 24q.
 // Bounds: a stage without reduction maps inputs below B q to outputs below (B + 4) q;
-// the top input is reduced below 4q at the first stage and below 16q at stages 3 and 1,
-// so no value reaches 24q.
+// the top input is reduced below 16q at stages 3 and 1, so no value reaches 24q.
 __device__ __forceinline__ void fwd(uint64_t (&x)[E], uint64_t *lds, int v, int t, const uint64_t *__restrict__ tw,
                                     const BfConsts &c) {
-    stage<4, 7, false, 4>(x, t, tw, c);   // < 8q
+    stage<4, 7, false>(x, t, tw, c);      // < 8q
     stage<4, 6, false>(x, t, tw, c);      // < 12q
     stage<4, 5, false>(x, t, tw, c);      // < 16q
     stage<4, 4, false>(x, t, tw, c);      // < 20q
+    {  // own<4>(t, k) = t | 16k, own<0>(t, k) = 16t | k (t < 16)
+        uint64_t *b = lds + slot(v, t);
 #pragma unroll
-    for (int k = 0; k < E; k++) lds[slot(v, own<4>(t, k))] = x[k];
+        for (int k = 0; k < E; k++) b[islot(16 * k)] = x[k];
+    }
     __syncthreads();
+    {
+        const uint64_t *b = lds + slot(v, 16 * t);
 #pragma unroll
-    for (int k = 0; k < E; k++) x[k] = lds[slot(v, own<0>(t, k))];
+        for (int k = 0; k < E; k++) x[k] = b[islot(k)];
+    }
     stage<0, 3, false, 16>(x, t, tw, c);  // < 20q
     stage<0, 2, false>(x, t, tw, c);      // < 24q
     stage<0, 1, false, 16>(x, t, tw, c);  // < 20q
     stage<0, 0, false>(x, t, tw, c);      // < 24q
     __syncthreads();
+    {  // brev8(16t | k) = brev8(16t) | brev8(k)
+        uint64_t *b = lds + slot(v, brev8(16 * t));
 #pragma unroll
-    for (int k = 0; k < E; k++) lds[slot(v, brev8(own<0>(t, k)))] = x[k];
+        for (int k = 0; k < E; k++) b[islot(brev8(k))] = x[k];
+    }
     __syncthreads();
 }
 
@@ -84,21 +95,33 @@ __device__ __forceinline__ void fwd(uint64_t (&x)[E], uint64_t *lds, int v, int 
 // and on exit (values < 4q).  Ends with a barrier.
 __device__ __forceinline__ void inv(uint64_t (&x)[E], uint64_t *lds, int v, int t, const uint64_t *__restrict__ tw,
                                     const BfConsts &c) {
+    {  // brev8(t | 16k) = brev8(t) | brev8(16k)
+        uint64_t *b = lds + slot(v, brev8(t));
 #pragma unroll
-    for (int k = 0; k < E; k++) lds[slot(v, brev8(own<4>(t, k)))] = x[k];
+        for (int k = 0; k < E; k++) b[islot(brev8(16 * k))] = x[k];
+    }
     __syncthreads();
+    {
+        const uint64_t *b = lds + slot(v, 16 * t);
 #pragma unroll
-    for (int k = 0; k < E; k++) x[k] = lds[slot(v, own<0>(t, k))];
+        for (int k = 0; k < E; k++) x[k] = b[islot(k)];
+    }
     stage<0, 0, true>(x, t, tw, c);
     stage<0, 1, true>(x, t, tw, c);
     stage<0, 2, true>(x, t, tw, c);
     stage<0, 3, true>(x, t, tw, c);
     __syncthreads();
+    {
+        uint64_t *b = lds + slot(v, 16 * t);
 #pragma unroll
-    for (int k = 0; k < E; k++) lds[slot(v, own<0>(t, k))] = x[k];
+        for (int k = 0; k < E; k++) b[islot(k)] = x[k];
+    }
     __syncthreads();
+    {
+        const uint64_t *b = lds + slot(v, t);
 #pragma unroll
-    for (int k = 0; k < E; k++) x[k] = lds[slot(v, own<4>(t, k))];
+        for (int k = 0; k < E; k++) x[k] = b[islot(16 * k)];
+    }
     stage<4, 4, true>(x, t, tw, c);
     stage<4, 5, true>(x, t, tw, c);
     stage<4, 6, true>(x, t, tw, c);
@@ -130,10 +153,11 @@ __global__ __launch_bounds__(NT) void k_fwd_cols(Map map, uint32_t limb0, const 
     for (int k = 0; k < E; k++) x[k] = src[(size_t)(t + 16 * k) * MP_N1 + c0 + v];
     fwd(x, lds, v, t, tw + (size_t)prime * MP_N1 * 2, c);
     uint64_t *o = scratch + (size_t)blockIdx.y * MP_N1 * MP_N1;
+    const uint64_t *lb = lds + slot(v, t);
 #pragma unroll
     for (int k = 0; k < E; k++) {
         const int j1 = t + 16 * k;
-        o[sidx(j1, c0 + v)] = shoup_lazy4(lds[slot(v, j1)], w, wp, 0 - c.q);  // [0, 4q)
+        o[sidx(j1, c0 + v)] = shoup_lazy4(lb[islot(16 * k)], w, wp, 0 - c.q);  // [0, 4q)
     }
 }
 
@@ -169,11 +193,12 @@ __global__ __launch_bounds__(NT) void k_fwd_rows(Map map, uint32_t limb0, const 
     }
     const int v = threadIdx.x % V, t = threadIdx.x / V;  // lanes across rows for the transposed store
     const uint32_t carry = GAL ? (g * (uint32_t)(r0 + v) + (g >> 1)) >> MP_LOG1 : 0;
+    const uint64_t *lb = lds + slot(v, t);
 #pragma unroll
     for (int k = 0; k < E; k++) {
         const uint32_t j2 = t + 16 * k;
-        const uint32_t from = GAL ? ((g * j2 + carry) & (MP_N1 - 1)) : j2;
-        dst[(size_t)(r0 + v) + (size_t)MP_N1 * j2] = reduce_out(lds[slot(v, from)], q);
+        const uint64_t y = GAL ? lds[slot(v, (g * j2 + carry) & (MP_N1 - 1))] : lb[islot(16 * k)];
+        dst[(size_t)(r0 + v) + (size_t)MP_N1 * j2] = reduce_out(y, q);
     }
 }
 
@@ -197,14 +222,16 @@ __global__ __launch_bounds__(NT) void k_inv_rows(Map map, uint32_t limb0, const 
 #pragma unroll
         for (int k = 0; k < E; k++) x[k] = src[(size_t)(r0 + v) + (size_t)MP_N1 * (t + 16 * k)];
         inv(x, lds, v, t, rowi + ((size_t)prime * 16 + ((r0 + v) >> 4)) * MP_N1 * 2, c);
+        uint64_t *lb = lds + slot(v, t);
 #pragma unroll
-        for (int k = 0; k < E; k++) lds[slot(v, t + 16 * k)] = x[k];
+        for (int k = 0; k < E; k++) lb[islot(16 * k)] = x[k];
     }
     __syncthreads();
     const int t = threadIdx.x % 16, v = threadIdx.x / 16;
     uint64_t *o = scratch + (size_t)blockIdx.y * MP_N1 * MP_N1;
+    const uint64_t *lb = lds + slot(v, t);
 #pragma unroll
-    for (int k = 0; k < E; k++) o[sidx(r0 + v, t + 16 * k)] = lds[slot(v, t + 16 * k)];
+    for (int k = 0; k < E; k++) o[sidx(r0 + v, t + 16 * k)] = lb[islot(16 * k)];
 }
 
 // ---- inverse pass 2: columns i2 = 16 bx + v of scratch; times TA^-1, inverse; scale -> dst[256 i1 + i2]

@@ -16,8 +16,9 @@
 // Twiddles are Shoup pairs (w, floor(w 2^64/q)) of psi^bitrev(k) (forward) and
 // psi^-bitrev(k) (inverse), interleaved [k][2].  Butterflies are Harvey's lazy
 // forms with a truncated Shoup quotient (see shoup_lazy4): the twiddle product
-// lands in [0, 4q); the forward transform reduces its top inputs only every
-// third stage (values below 28q < 2^64), the inverse keeps them below 4q.
+// lands in [0, 4q); the forward transform (inputs below 4q) reduces its top
+// inputs at two of its eleven stages (values below 28q < 2^64), the inverse
+// keeps them below 4q.
 #pragma once
 #include "butterfly.h"
 
@@ -31,7 +32,10 @@ constexpr int E = 8;     // coefficients per thread
 constexpr int LDS_WORDS = N + N / 32;
 
 // LDS slot of coefficient index i (one pad word per 32 breaks power-of-two strides).
-__device__ __forceinline__ int slot(int i) { return i + (i >> 5); }
+// slot(a | b) = slot(a) + slot(b) when a and b have no bit in common, so every
+// exchange below is a per-thread base plus a compile-time offset per register
+// (one address computation per exchange instead of one per access).
+__device__ __forceinline__ constexpr int slot(int i) { return i + (i >> 5); }
 
 // Index of the k-th coefficient owned by thread t in a pass that owns bits [C, C+3).
 template <int C>
@@ -39,7 +43,7 @@ __device__ __forceinline__ int own(int t, int k) {
     return (t & ((1 << C) - 1)) | (k << C) | ((t >> C) << (C + 3));
 }
 
-__device__ __forceinline__ int brev(int i) { return (int)(__builtin_bitreverse32((uint32_t)i) >> (32 - LOGN)); }
+__device__ __forceinline__ constexpr int brev(int i) { return (int)(__builtin_bitreverse32((uint32_t)i) >> (32 - LOGN)); }
 
 // One radix-2 stage (bit BIT of the index) on the 8 registers of a pass owning bits [C, C+3).
 template <int C, int BIT, bool INV, int RED = 4>
@@ -57,41 +61,45 @@ __device__ __forceinline__ void stage(uint64_t (&v)[E], int t, const uint64_t *_
     }
 }
 
+// own<C>(t, k) = own<C>(t, 0) | (k << C), two disjoint bit fields
 template <int C>
 __device__ __forceinline__ void to_lds(uint64_t *lds, const uint64_t (&v)[E], int t) {
+    uint64_t *b = lds + slot(own<C>(t, 0));
 #pragma unroll
-    for (int k = 0; k < E; k++) lds[slot(own<C>(t, k))] = v[k];
+    for (int k = 0; k < E; k++) b[slot(k << C)] = v[k];
 }
 template <int C>
 __device__ __forceinline__ void from_lds(const uint64_t *lds, uint64_t (&v)[E], int t) {
+    const uint64_t *b = lds + slot(own<C>(t, 0));
 #pragma unroll
-    for (int k = 0; k < E; k++) v[k] = lds[slot(own<C>(t, k))];
+    for (int k = 0; k < E; k++) v[k] = b[slot(k << C)];
 }
 
-// Forward NTT.  On entry v[k] = a[t + 256 k] (natural order, values < 8q);
+// Forward NTT.  On entry v[k] = a[t + 256 k] (natural order, values < 4q);
 // on exit v[k] = A[t + 256 k] in [0, 24q) (reduce_out finishes).  Uses lds[LDS_WORDS]; ends with a barrier.
-// Bounds: a stage without reduction maps inputs below B q to outputs below (B + 4) q; the
-// top input is reduced at the first stage of each register pass (below 4q, 8q, 16q, 16q),
-// so no value reaches 28q and a + 4q stays below 2^64 (28 q < 2^64 for every chain prime).
+// Bounds: a stage without reduction maps inputs below B q to outputs below (B + 4) q.
+// From below 4q, six stages run unreduced (below 28q); the first stage of each of the
+// last two register passes reduces its top input below 16q, so no value reaches 28q
+// and a + 4q stays below 2^64 (28 q < 2^64 for every chain prime).
 __device__ __forceinline__ void fwd(uint64_t (&v)[E], uint64_t *lds, const uint64_t *__restrict__ tw, uint64_t qv) {
     const int t = threadIdx.x;
     const BfConsts q = bf_consts(qv);
-    stage<8, 10, false, 4>(v, t, tw, q);   // a < 4q,  outputs < 8q
-    stage<8, 9, false, 0>(v, t, tw, q);    //          < 12q
-    stage<8, 8, false, 0>(v, t, tw, q);    //          < 16q
+    stage<8, 10, false, 0>(v, t, tw, q);   // outputs < 8q
+    stage<8, 9, false, 0>(v, t, tw, q);    //         < 12q
+    stage<8, 8, false, 0>(v, t, tw, q);    //         < 16q
     to_lds<8>(lds, v, t);
     __syncthreads();
     from_lds<5>(lds, v, t);
-    stage<5, 7, false, 8>(v, t, tw, q);    // a < 8q,  < 12q
-    stage<5, 6, false, 0>(v, t, tw, q);    //          < 16q
-    stage<5, 5, false, 0>(v, t, tw, q);    //          < 20q
+    stage<5, 7, false, 0>(v, t, tw, q);    //          < 20q
+    stage<5, 6, false, 0>(v, t, tw, q);    //          < 24q
+    stage<5, 5, false, 0>(v, t, tw, q);    //          < 28q
     __syncthreads();
     to_lds<5>(lds, v, t);
     __syncthreads();
     from_lds<2>(lds, v, t);
     stage<2, 4, false, 16>(v, t, tw, q);   // a < 16q, < 20q
     stage<2, 3, false, 0>(v, t, tw, q);    //          < 24q
-    stage<2, 2, false, 0>(v, t, tw, q);    //          < 28q
+    stage<2, 2, false, 0>(v, t, tw, q);    //          < 28q (a + 4q < 28q)
     __syncthreads();
     to_lds<2>(lds, v, t);
     __syncthreads();
@@ -100,11 +108,18 @@ __device__ __forceinline__ void fwd(uint64_t (&v)[E], uint64_t *lds, const uint6
     stage<0, 0, false, 0>(v, t, tw, q);    //          < 24q
     __syncthreads();
     // coefficient own<0>(t,k) = 8t + k now holds A_{brev(8t+k)}: write back in natural order
+    // (brev(8t + k) = brev(8t) | brev(k))
+    {
+        uint64_t *b = lds + slot(brev(8 * t));
 #pragma unroll
-    for (int k = 0; k < E; k++) lds[slot(brev(8 * t + k))] = v[k];
+        for (int k = 0; k < E; k++) b[slot(brev(k))] = v[k];
+    }
     __syncthreads();
+    {
+        const uint64_t *b = lds + slot(t);
 #pragma unroll
-    for (int k = 0; k < E; k++) v[k] = lds[slot(t + NT * k)];
+        for (int k = 0; k < E; k++) v[k] = b[slot(NT * k)];
+    }
     __syncthreads();
 }
 
@@ -113,8 +128,11 @@ __device__ __forceinline__ void fwd(uint64_t (&v)[E], uint64_t *lds, const uint6
 __device__ __forceinline__ void inv(uint64_t (&v)[E], uint64_t *lds, const uint64_t *__restrict__ tw, uint64_t qv) {
     const int t = threadIdx.x;
     const BfConsts q = bf_consts(qv);
+    {
+        uint64_t *b = lds + slot(brev(t));  // brev(t + 256 k) = brev(t) | brev(256 k)
 #pragma unroll
-    for (int k = 0; k < E; k++) lds[slot(brev(t + NT * k))] = v[k];
+        for (int k = 0; k < E; k++) b[slot(brev(NT * k))] = v[k];
+    }
     __syncthreads();
     from_lds<0>(lds, v, t);
     stage<0, 0, true>(v, t, tw, q);
