@@ -388,6 +388,9 @@ template <int OCC>
 constexpr uint32_t mf_tpb() { return OCC == 3 ? MF_TPB1 : MF_TPB; }
 
 constexpr uint32_t MF_HSTRIDE = 272;  // LDS bytes per target position (8 digits x 32 rows + bank padding)
+// Byte offset, within a position, of the 8 rows of lane group g of digit b: the rows of digits
+// 2h and 2h + 1 are adjacent, so mf_right's tuple h of a lane is one 16-byte read.
+__device__ __forceinline__ constexpr uint32_t h_slot(uint32_t b, uint32_t g) { return 64 * (b / 2) + 16 * g + 8 * (b % 2); }
 
 // OCC selects the variant: 3 when the whole contraction is one 32-row chunk
 // (128 VGPRs and 7 staged tiles, so four waves per SIMD fit), 2 otherwise (two
@@ -476,18 +479,23 @@ __global__ __launch_bounds__(256, OCC == 3 ? 4 : OCC) void k_convert_mfma(const 
     const bool rows_ahead = OCC != 3 && (!STAGED || nch > 1);
     if (rows_ahead) load_rows(rb[1], ub[1], 1 % nch);
     if constexpr (STAGED) {
-        // position p's 8 x 32 digit bytes are contiguous in HD (mk = 32): 16-byte copies
+        // position p's 8 x 32 digit bytes are contiguous in HD (mk = 32), [digit b][row]; in LDS the
+        // 8 rows of lane group grp of digits 2h and 2h + 1 sit together (h_slot): 8-byte copies
         const uint32_t np = ntile * 16;
         const int8_t *src = B.HD + (size_t)16 * tile0 * 256;
-        for (uint32_t q = threadIdx.x; q < np * 16; q += 256)
-            *(uint4 *)(sh_h + (q / 16) * MF_HSTRIDE + (q % 16) * 16) = *(const uint4 *)(src + (size_t)q * 16);
+        for (uint32_t q = threadIdx.x; q < np * 32; q += 256) {
+            const uint32_t b = (q % 32) / 4, gq = q % 4;
+            *(uint2 *)(sh_h + (q / 32) * MF_HSTRIDE + h_slot(b, gq)) = *(const uint2 *)(src + (size_t)q * 8);
+        }
         const uint64_t *rsrc = B.RC + (size_t)16 * tile0 * MF_RC;
         for (uint32_t q = threadIdx.x; q < np * MF_RC; q += 256) sh_rc[q] = rsrc[q];
         __syncthreads();
     }
-    // digit plane a of the lane's 8 rows (byte j = row 8 grp + j) is half a % 2 of AP[a / 2]: the
-    // planes 2i, 2i + 1 form one register tuple, the A operand of a 64-deep product
-    mf_v4i AP[4];
+    // the digit planes of the lane's 8 rows (byte j = row 8 grp + j) as the A operands of the
+    // 64-deep products: mf_left's windows, except in the 128-VGPR one-chunk variant, which keeps
+    // the windows on the per-tile operand (see mfma_digits.h)
+    constexpr bool WIN_A = OCC != 3;
+    mf_v4i AW[WIN_A ? MF_NW : MF_NT];
     auto build_a = [&](const uint64_t(&raw)[8], uint32_t uraw, uint32_t ch) {
         if constexpr (FOLD_U) uraw = exact_u(raw, ch);
         const uint32_t r0 = (ch % cps) * 32 + 8 * grp;
@@ -504,7 +512,7 @@ __global__ __launch_bounds__(256, OCC == 3 ? 4 : OCC) void k_convert_mfma(const 
         }
         long pl[8];
         mf_planes(z, pl);
-        mf_left(pl, AP);
+        mf_left(pl, AW);
     };
     // TT target tiles share each chunk's A fragments (2 when the contraction has
     // several chunks, so the rows are fetched and transposed once per 2 tiles)
@@ -518,14 +526,20 @@ __global__ __launch_bounds__(256, OCC == 3 ? 4 : OCC) void k_convert_mfma(const 
     // The staged two-wave variant (summed sets) reads a tile's tuples from LDS again at every
     // chunk rather than keeping both tiles' tuples for the whole pass, which keeps it within
     // 256 VGPRs.
-    constexpr int NH = MF_NH;  // 4-VGPR H registers per tile
+    constexpr int NH = WIN_A ? MF_NT : MF_NW;  // 4-VGPR H registers per tile
     mf_v4i hb[TT][NH];
     auto load_h = [&](mf_v4i(&H)[NH], uint32_t tile, uint32_t buf) {
-        const int8_t *h = STAGED ? sh_h + ((tile - tile0) * 16 + col) * MF_HSTRIDE + 8 * grp
-                                 : sh_h + ((buf * 2 + (tile - tile0) % 2) * 16 + col) * MF_HSTRIDE + 8 * grp;
-        auto pl = [&](int bb) -> long { return *(const long *)(h + 32 * bb); };
+        const int8_t *h = STAGED ? sh_h + ((tile - tile0) * 16 + col) * MF_HSTRIDE
+                                 : sh_h + ((buf * 2 + (tile - tile0) % 2) * 16 + col) * MF_HSTRIDE;
+        if constexpr (WIN_A) {
 #pragma unroll
-        for (int j = 0; j < NH; j++) H[j] = __builtin_bit_cast(mf_v4i, mf_v2l{pl(7 - j), pl(6 - j)});
+            for (int p = 0; p < NH; p++) H[p] = *(const mf_v4i *)(h + h_slot(2 * p, grp));
+        } else {
+            long pl[8];
+#pragma unroll
+            for (int b = 0; b < 8; b++) pl[b] = *(const long *)(h + h_slot(b, grp));
+            mf_right(pl, H);
+        }
     };
     // the slice of step g: thread x copies 16-byte pieces q = x and x + 256 of the
     // 2 x 16 x 8 x 32 bytes (tiles past tile_end read padded, in-bounds positions).  The two
@@ -540,10 +554,13 @@ __global__ __launch_bounds__(256, OCC == 3 ? 4 : OCC) void k_convert_mfma(const 
         hs0 = gload((const u32x4 *)(B.HD + ((size_t)(16 * ta + sl_pos) * 8 + sl_b) * mk + c0 + 16 * sl_hf));
         hs1 = gload((const u32x4 *)(B.HD + ((size_t)(16 * tb + sl_pos) * 8 + sl_b) * mk + c0 + 16 * sl_hf));
     };
-    auto store_slice = [&](uint32_t buf) {
-        const uint32_t o = sl_pos * MF_HSTRIDE + 32 * sl_b + 16 * sl_hf;
-        *(u32x4 *)(sh_h + ((buf * 2 + 0) * 16) * MF_HSTRIDE + o) = hs0;
-        *(u32x4 *)(sh_h + ((buf * 2 + 1) * 16) * MF_HSTRIDE + o) = hs1;
+    auto store_slice = [&](uint32_t buf) {  // the piece's rows 16 sl_hf .. + 16 are lane groups 2 sl_hf, + 1
+        const uint32_t o0 = sl_pos * MF_HSTRIDE + h_slot(sl_b, 2 * sl_hf), o1 = o0 + h_slot(0, 1);
+        int8_t *d0 = sh_h + ((buf * 2 + 0) * 16) * MF_HSTRIDE, *d1 = sh_h + ((buf * 2 + 1) * 16) * MF_HSTRIDE;
+        *(uint2 *)(d0 + o0) = uint2{hs0.x, hs0.y};
+        *(uint2 *)(d0 + o1) = uint2{hs0.z, hs0.w};
+        *(uint2 *)(d1 + o0) = uint2{hs1.x, hs1.y};
+        *(uint2 *)(d1 + o1) = uint2{hs1.z, hs1.w};
     };
     const MfW2 w2 = mf_w2();
     auto recombine = [&](uint32_t tile, const mf_v4i(&acc)[15]) {
@@ -587,7 +604,7 @@ __global__ __launch_bounds__(256, OCC == 3 ? 4 : OCC) void k_convert_mfma(const 
         for (uint32_t tt = 0; tt < TT; tt++) {
             if (t0 + tt >= tile_end) break;  // workgroup-uniform
             if (!STAGED || ch == 0 || OCC == 2) load_h(hb[tt], t0 + tt, g & 1);  // OCC 2: see NH
-            mf_mac_tile(acc[tt], AP, hb[tt]);
+            mf_mac_tile(acc[tt], AW, hb[tt]);
         }
         if constexpr (!STAGED) {
             // the next slice goes to the other buffer, whose last readers (step g - 1)
@@ -1426,8 +1443,8 @@ __global__ __launch_bounds__(256, 2) void k_bsgs_mac_mfma(const uint64_t *__rest
     }
     __syncthreads();
     // right operand: digit planes of baby steps 8 grp + j of polynomial col at this wave's 4
-    // coefficients, in reverse plane order (rp[q][7 - a] = plane a), so that the tuples
-    // {plane b | plane b - 1} are consecutive registers
+    // coefficients (rp[q][a] = plane a), so that mf_right's tuples {plane 2p | plane 2p + 1}
+    // are consecutive registers
     long rp[4][8];
 #pragma unroll
     for (int qk = 0; qk < 4; qk++) {
@@ -1438,7 +1455,7 @@ __global__ __launch_bounds__(256, 2) void k_bsgs_mac_mfma(const uint64_t *__rest
         long pl[8];
         mf_planes(z, pl);
 #pragma unroll
-        for (int a2 = 0; a2 < 8; a2++) rp[qk][7 - a2] = pl[a2];
+        for (int a2 = 0; a2 < 8; a2++) rp[qk][a2] = pl[a2];
     }
     const MfW2 w2 = mf_w2();
     const MfRecomb rk = mf_recomb_consts([&](int d) -> uint64_t { return prc[(size_t)i * MF_RC + d]; });
@@ -1469,14 +1486,13 @@ __global__ __launch_bounds__(256, 2) void k_bsgs_mac_mfma(const uint64_t *__rest
             for (int j = 0; j < 8; j++) z[j] = digit_form(a[j]);
             long pl[8];
             mf_planes(z, pl);
-            mf_v4i AP[4], H[MF_NH];
-            mf_left(pl, AP);
-#pragma unroll
-            for (int j = 0; j < MF_NH; j++) H[j] = __builtin_bit_cast(mf_v4i, mf_v2l{rp[qk][j], rp[qk][j + 1]});
+            mf_v4i AW[MF_NW], H[MF_NT];
+            mf_left(pl, AW);
+            mf_right(rp[qk], H);
             mf_v4i acc[15];
 #pragma unroll
             for (int d = 0; d < 15; d++) acc[d] = mf_v4i{0, 0, 0, 0};
-            mf_mac_tile(acc, AP, H);
+            mf_mac_tile(acc, AW, H);
 #pragma unroll
             for (int v = 0; v < 4; v++) res[qk][v] = mf_recombine(acc, v, w2, rk);
         }

@@ -42,35 +42,67 @@ __device__ __forceinline__ void mf_planes(const uint64_t (&z)[8], long (&pl)[8])
     for (int a = 0; a < 8; a++) pl[a] = (long)(((uint64_t)o[1][a] << 32) | o[0][a]);
 }
 
-// Left operand tuples: AP[i] = {plane 2i | plane 2i+1}, the A operand of a 64-deep product.
-__device__ __forceinline__ void mf_left(const long (&pl)[8], mf_v4i (&AP)[4]) {
+// Operand register tuples.  A 16x16x64 product of {X_a | X_a'} and {Y_b | Y_b'} adds the digit
+// pairs (a, b) and (a', b') (the two halves of each operand take the same K positions, so the
+// product is the sum of the two 32-deep ones); both pairs must lie on one diagonal s.  Two
+// pairings do that with 36 instructions per tile and chunk instead of 64:
+//  - windows on the left, tuples on the right: {A_a | A_a-1} x {H_2p | H_2p+1} adds (a, 2p) and
+//    (a-1, 2p+1), s = a + 2p; the 7 windows are built once per left operand and the 4 tuples of
+//    each tile are four 16-byte reads when its planes are stored pairwise (h_slot);
+//  - tuples on the left, windows on the right: {A_2i | A_2i+1} x {H_b | H_b-1} adds (2i, b) and
+//    (2i+1, b-1); the per-tile windows are transient, which suits a 128-VGPR budget in which
+//    the left windows would stay live across the tiles and spill.
+// The mf_left / mf_right / mf_mac_tile overloads pick the pairing from the array sizes.
+constexpr int MF_NW = 7, MF_NT = 4;
+__device__ __forceinline__ void mf_left(const long (&pl)[8], mf_v4i (&AW)[MF_NW]) {  // windows {w+1 | w}
 #pragma unroll
-    for (int i = 0; i < 4; i++) AP[i] = __builtin_bit_cast(mf_v4i, mf_v2l{pl[2 * i], pl[2 * i + 1]});
+    for (int w = 0; w < MF_NW; w++) AW[w] = __builtin_bit_cast(mf_v4i, mf_v2l{pl[w + 1], pl[w]});
 }
-// Right operand tuples: H[j] = {plane 7-j | plane 6-j} (j < 7); they overlap in content.
-constexpr int MF_NH = 7;
-__device__ __forceinline__ void mf_right(const long (&pl)[8], mf_v4i (&H)[MF_NH]) {
+__device__ __forceinline__ void mf_left(const long (&pl)[8], mf_v4i (&AT)[MF_NT]) {  // tuples {2i | 2i+1}
 #pragma unroll
-    for (int j = 0; j < MF_NH; j++) H[j] = __builtin_bit_cast(mf_v4i, mf_v2l{pl[7 - j], pl[6 - j]});
+    for (int i = 0; i < MF_NT; i++) AT[i] = __builtin_bit_cast(mf_v4i, mf_v2l{pl[2 * i], pl[2 * i + 1]});
+}
+__device__ __forceinline__ void mf_right(const long (&pl)[8], mf_v4i (&HT)[MF_NT]) {  // tuples {2p | 2p+1}
+#pragma unroll
+    for (int p = 0; p < MF_NT; p++) HT[p] = __builtin_bit_cast(mf_v4i, mf_v2l{pl[2 * p], pl[2 * p + 1]});
+}
+__device__ __forceinline__ void mf_right(const long (&pl)[8], mf_v4i (&HW)[MF_NW]) {  // windows {7-j | 6-j}
+#pragma unroll
+    for (int j = 0; j < MF_NW; j++) HW[j] = __builtin_bit_cast(mf_v4i, mf_v2l{pl[7 - j], pl[6 - j]});
 }
 
-// ac[s] += S_s of one 16 x 16 tile over one 32-row chunk.  The digit pairs (2i, s-2i) and
-// (2i+1, s-2i-1) of diagonal s go through one 16x16x64 product of AP[i] and H[7 - b],
-// b = s - 2i (both operands take the same K positions, so the product is the sum of the two
-// 32-deep ones).  The planes left over (a = s for even s <= 6, b = 7 for even s >= 8) take
-// one 16x16x32 each: 28 + 8 instructions per tile and chunk instead of 64.
-__device__ __forceinline__ void mf_mac_tile(mf_v4i (&ac)[15], const mf_v4i (&AP)[4], const mf_v4i (&H)[MF_NH]) {
-    auto plane_a = [&](int a) -> long { return __builtin_bit_cast(mf_v2l, AP[a / 2])[a % 2]; };
-    auto hsing = [&](int bb) -> long {  // plane b inside H: H[7 - b] = {H_b, H_b-1}, H[6] = {H_1, H_0}
-        return bb > 0 ? __builtin_bit_cast(mf_v2l, H[7 - bb])[0] : __builtin_bit_cast(mf_v2l, H[6])[1];
+// ac[s] += S_s of one 16 x 16 tile over one 32-row chunk, left windows x right tuples: 28
+// paired products (a = 1..7, p = 0..3) and the pairs left over, (0, 2p) and (7, 2p+1), one
+// 16x16x32 each.
+__device__ __forceinline__ void mf_mac_tile(mf_v4i (&ac)[15], const mf_v4i (&AW)[MF_NW], const mf_v4i (&HT)[MF_NT]) {
+#pragma unroll
+    for (int a = 1; a < 8; a++)
+#pragma unroll
+        for (int p = 0; p < MF_NT; p++)
+            ac[a + 2 * p] = __builtin_amdgcn_mfma_i32_16x16x64_i8(AW[a - 1], HT[p], ac[a + 2 * p], 0, 0, 0);
+    const long a0 = __builtin_bit_cast(mf_v2l, AW[0])[1], a7 = __builtin_bit_cast(mf_v2l, AW[MF_NW - 1])[0];
+#pragma unroll
+    for (int p = 0; p < MF_NT; p++) {
+        const mf_v2l h = __builtin_bit_cast(mf_v2l, HT[p]);
+        ac[2 * p] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a0, h[0], ac[2 * p], 0, 0, 0);
+        ac[8 + 2 * p] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a7, h[1], ac[8 + 2 * p], 0, 0, 0);
+    }
+}
+// Left tuples x right windows: AT[i] x HW[7 - b] adds (2i, b) and (2i+1, b-1) for b = 1..7 (28
+// products); the planes left over (a = s for even s <= 6, b = 7 for even s >= 8) take one
+// 16x16x32 each.
+__device__ __forceinline__ void mf_mac_tile(mf_v4i (&ac)[15], const mf_v4i (&AT)[MF_NT], const mf_v4i (&HW)[MF_NW]) {
+    auto plane_a = [&](int a) -> long { return __builtin_bit_cast(mf_v2l, AT[a / 2])[a % 2]; };
+    auto hsing = [&](int bb) -> long {  // plane b inside HW: HW[7 - b] = {H_b, H_b-1}, HW[6] = {H_1, H_0}
+        return bb > 0 ? __builtin_bit_cast(mf_v2l, HW[7 - bb])[0] : __builtin_bit_cast(mf_v2l, HW[6])[1];
     };
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < MF_NT; i++)
 #pragma unroll
         for (int sd = 0; sd < 15; sd++) {
             const int bb = sd - 2 * i;  // pair (2i, b), (2i+1, b-1)
             if (bb < 1 || bb > 7) continue;
-            ac[sd] = __builtin_amdgcn_mfma_i32_16x16x64_i8(AP[i], H[7 - bb], ac[sd], 0, 0, 0);
+            ac[sd] = __builtin_amdgcn_mfma_i32_16x16x64_i8(AT[i], HW[7 - bb], ac[sd], 0, 0, 0);
         }
 #pragma unroll
     for (int sd = 0; sd < 15; sd += 2) {  // leftovers: a = s (b = 0) for s <= 6, a = s - 7 (b = 7) for s >= 8
