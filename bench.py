@@ -45,24 +45,24 @@ LIMB = N * 8
 # counters (profiles/bench_step_n2048_l112_b8_hbm_counters.md).  Valid only for
 # the kernel sources they were taken on (hash of rns_ckks_polynomial_amd/csrc).
 MEASURED_TRAFFIC = {
-    "source_sha": "912f85cd1fe51aac",
+    "source_sha": "352d02af60ba394d",
     "bytes_per_launch": {
-        "ks_ntt_ext": 1350414757,
-        "ks_modup_convert": 855285937,
-        "bsgs_mac": 4095323483,
-        "rotate_final": 3190067438,
-        "ks_inner_product_sum": 2848772334,
-        "ks_inner_product_hoisted": 1870289097,
-        "giant_final": 304433993,
-        "ks_intt_modup": 326845105,
-        "ks_intt_moddown": 310310278,
-        "ks_inner_product": 462667502,
-        "ntt_fwd": 62560256,
-        "ntt_inv": 62600064,
-        "ks_moddown_u": 231752741,
-        "relin_final": 155666213,
-        "rescale_final": 118597111,
-        "ks_moddown_convert": 772462238
+        "ks_ntt_ext": 1355515234,
+        "ks_modup_convert": 855358269,
+        "bsgs_mac": 3758581193,
+        "rotate_final": 3191033746,
+        "ks_inner_product_sum": 2849037952,
+        "ks_inner_product_hoisted": 1871167214,
+        "giant_final": 304297143,
+        "ks_intt_modup": 326834371,
+        "ks_intt_moddown": 310297192,
+        "ks_inner_product": 462654510,
+        "ntt_fwd": 62548992,
+        "ntt_inv": 62589824,
+        "ks_moddown_u": 231735241,
+        "relin_final": 154927982,
+        "rescale_final": 118128128,
+        "ks_moddown_convert": 768957312
     },
 }
 
@@ -73,24 +73,24 @@ MEASURED_TRAFFIC = {
 # its SIMD (wave64 on 16 lanes; the 32-bit multiplies included, as measured on this GPU), so
 # 1024 SIMDs x 2.4 GHz / 4 = 614.4 G wave-instructions/s is the issue ceiling.
 MEASURED_SQ = {
-    "source_sha": "912f85cd1fe51aac",
+    "source_sha": "352d02af60ba394d",
     "valu_per_launch": {
-        "ks_ntt_ext": 166290432,
-        "ks_modup_convert": 109711360,
-        "bsgs_mac": 173752320,
-        "rotate_final": 321090560,
+        "ks_ntt_ext": 146736128,
+        "ks_modup_convert": 111828992,
+        "bsgs_mac": 176504832,
+        "rotate_final": 293981184,
         "ks_inner_product_sum": 111356672,
         "ks_inner_product_hoisted": 179894400,
-        "giant_final": 12565504,
-        "ks_intt_modup": 51606016,
-        "ks_intt_moddown": 48996864,
+        "giant_final": 11655168,
+        "ks_intt_modup": 47900160,
+        "ks_intt_moddown": 45421824,
         "ks_inner_product": 24222464,
-        "ntt_fwd": 7562240,
-        "ntt_inv": 9210880,
+        "ntt_fwd": 6673408,
+        "ntt_inv": 8529920,
         "ks_moddown_u": 10110464,
-        "relin_final": 13712384,
-        "rescale_final": 10471296,
-        "ks_moddown_convert": 81438037
+        "relin_final": 12830720,
+        "rescale_final": 9590400,
+        "ks_moddown_convert": 80157355
     },
 }
 VALU_ISSUE_PEAK_G = 1024 * 2.4e9 / 4 / 1e9
