@@ -1042,13 +1042,13 @@ __global__ void k_inner(const uint64_t *__restrict__ d, size_t d_stride, const u
 // through memory.
 template <int MODE, bool ACCUM>
 __global__ __launch_bounds__(mp::NT) void k_rows_final(uint32_t limb0, const PrimeConsts *__restrict__ pc,
-                                                       const uint64_t *__restrict__ rowf,
-                                                       const uint64_t *__restrict__ scratch,
-                                                       const uint64_t *__restrict__ acc,
-                                                       const uint64_t *__restrict__ pinv,
-                                                       const uint64_t *__restrict__ xa,
-                                                       const uint64_t *__restrict__ xb, uint32_t g,
-                                                       uint64_t *__restrict__ out, uint32_t l, uint32_t K) {
+                                                          const uint64_t *__restrict__ rowf,
+                                                          const uint64_t *__restrict__ scratch,
+                                                          const uint64_t *__restrict__ acc,
+                                                          const uint64_t *__restrict__ pinv,
+                                                          const uint64_t *__restrict__ xa,
+                                                          const uint64_t *__restrict__ xb, uint32_t g,
+                                                          uint64_t *__restrict__ out, uint32_t l, uint32_t K) {
     using namespace mp;
     constexpr uint32_t n = MP_N1 * MP_N1;
     __shared__ uint64_t lds[V * VSTRIDE];
@@ -1057,6 +1057,33 @@ __global__ __launch_bounds__(mp::NT) void k_rows_final(uint32_t limb0, const Pri
     const size_t limb = (b * 2 + c) * l + i;
     const uint64_t q = pc[i].q, mu = pc[i].mu;
     const int r0 = blockIdx.x * V;
+    // output lanes run across rows (128-byte runs of the limb); their accumulator values and extra
+    // terms are requested and formed before the row transform, so the loads are in flight while
+    // its butterflies run (its barriers keep the compiler from sinking them)
+    const int vo = threadIdx.x % V, to = threadIdx.x / V;
+    const size_t per = (size_t)l * n;
+    const uint64_t *ap = acc + ((b * 2 + c) * (l + K) + i) * n;
+    const uint64_t *x0 = xa + (b * 2) * per + (size_t)i * n;  // MODE 1: a0 (a1 one polynomial on); 2: c0
+    const uint64_t *y0 = MODE == 1 ? xb + (b * 2) * per + (size_t)i * n : nullptr;
+    auto pos = [&](int k) -> uint32_t { return (uint32_t)(r0 + vo) + MP_N1 * (uint32_t)(to + 16 * k); };
+    uint64_t av[E], ex[E];
+#pragma unroll
+    for (int k = 0; k < E; k++) av[k] = ap[pos(k)];
+    if (MODE == 1) {
+        if (c == 0) {  // workgroup-uniform
+#pragma unroll
+            for (int k = 0; k < E; k++) ex[k] = mulm(x0[pos(k)], y0[pos(k)], q, mu);
+        } else {
+#pragma unroll
+            for (int k = 0; k < E; k++) {
+                const uint32_t j = pos(k);
+                ex[k] = addm(mulm(x0[j], y0[j + per], q, mu), mulm(x0[j + per], y0[j], q, mu), q);
+            }
+        }
+    } else if (MODE == 2 && c == 0) {
+#pragma unroll
+        for (int k = 0; k < E; k++) ex[k] = x0[galois_src(pos(k), g, n)];
+    }
     {
         const BfConsts bc = bf_consts(q);
         const uint64_t *in = scratch + (size_t)blockIdx.y * n;
@@ -1066,27 +1093,15 @@ __global__ __launch_bounds__(mp::NT) void k_rows_final(uint32_t limb0, const Pri
         for (int k = 0; k < E; k++) x[k] = in[sidx(r0 + v, t + 16 * k)];
         fwd(x, lds, v, t, rowf + ((size_t)i * 16 + ((r0 + v) >> 4)) * MP_N1 * 2, bc);
     }
-    const int v = threadIdx.x % V, t = threadIdx.x / V;  // lanes across rows: 128-byte runs of the limb
-    const size_t per = (size_t)l * n;
-    const uint64_t *ap = acc + ((b * 2 + c) * (l + K) + i) * n;
-    const uint64_t *x0 = xa + (b * 2) * per + (size_t)i * n;  // MODE 1: a0 (a1 one polynomial on); 2: c0
-    const uint64_t *y0 = MODE == 1 ? xb + (b * 2) * per + (size_t)i * n : nullptr;
     uint64_t *op = out + limb * n;
     const uint64_t w = pinv[2 * i], wp = pinv[2 * i + 1];
-    const uint64_t *lb = lds + slot(v, t);
-#pragma unroll 4
+    const uint64_t *lb = lds + slot(vo, to);
+#pragma unroll
     for (int k = 0; k < E; k++) {
-        const uint32_t j = (uint32_t)(r0 + v) + MP_N1 * (uint32_t)(t + 16 * k);
+        const uint32_t j = pos(k);
         const uint64_t nt = reduce_out(lb[islot(16 * k)], q);
-        uint64_t r = shoup(subm(ap[j], nt, q), w, wp, q);
-        if (MODE == 1) {
-            uint64_t e;
-            if (c == 0) e = mulm(x0[j], y0[j], q, mu);
-            else e = addm(mulm(x0[j], y0[j + per], q, mu), mulm(x0[j + per], y0[j], q, mu), q);
-            r = addm(r, e, q);
-        } else if (MODE == 2) {
-            if (c == 0) r = addm(r, x0[galois_src(j, g, n)], q);
-        }
+        uint64_t r = shoup(subm(av[k], nt, q), w, wp, q);
+        if (MODE == 1 || (MODE == 2 && c == 0)) r = addm(r, ex[k], q);
         if (ACCUM) r = addm(r, op[j], q);
         op[j] = r;
     }
