@@ -45,24 +45,24 @@ LIMB = N * 8
 # counters (profiles/bench_step_n2048_l112_b8_hbm_counters.md).  Valid only for
 # the kernel sources they were taken on (hash of rns_ckks_polynomial_amd/csrc).
 MEASURED_TRAFFIC = {
-    "source_sha": "352d02af60ba394d",
+    "source_sha": "75b1e769a2f64b19",
     "bytes_per_launch": {
-        "ks_ntt_ext": 1355515234,
-        "ks_modup_convert": 855358269,
-        "bsgs_mac": 3758581193,
-        "rotate_final": 3191033746,
-        "ks_inner_product_sum": 2849037952,
-        "ks_inner_product_hoisted": 1871167214,
-        "giant_final": 304297143,
-        "ks_intt_modup": 326834371,
-        "ks_intt_moddown": 310297192,
-        "ks_inner_product": 462654510,
+        "ks_ntt_ext": 1356502888,
+        "ks_modup_convert": 855353490,
+        "bsgs_mac": 3758581303,
+        "rotate_final": 3191146496,
+        "ks_inner_product_sum": 2848770981,
+        "ks_inner_product_hoisted": 1872568869,
+        "giant_final": 304385042,
+        "ks_intt_modup": 326834688,
+        "ks_intt_moddown": 310297240,
+        "ks_inner_product": 462655077,
         "ntt_fwd": 62548992,
         "ntt_inv": 62589824,
-        "ks_moddown_u": 231735241,
-        "relin_final": 154927982,
-        "rescale_final": 118128128,
-        "ks_moddown_convert": 768957312
+        "ks_moddown_u": 231735186,
+        "relin_final": 154741614,
+        "rescale_final": 118295726,
+        "ks_moddown_convert": 768873679
     },
 }
 
@@ -73,24 +73,9 @@ MEASURED_TRAFFIC = {
 # its SIMD (wave64 on 16 lanes; the 32-bit multiplies included, as measured on this GPU), so
 # 1024 SIMDs x 2.4 GHz / 4 = 614.4 G wave-instructions/s is the issue ceiling.
 MEASURED_SQ = {
-    "source_sha": "352d02af60ba394d",
+    "source_sha": "75b1e769a2f64b19",
     "valu_per_launch": {
-        "ks_ntt_ext": 146736128,
-        "ks_modup_convert": 111828992,
-        "bsgs_mac": 176504832,
-        "rotate_final": 293981184,
-        "ks_inner_product_sum": 111356672,
-        "ks_inner_product_hoisted": 179894400,
-        "giant_final": 11655168,
-        "ks_intt_modup": 47900160,
-        "ks_intt_moddown": 45421824,
-        "ks_inner_product": 24222464,
-        "ntt_fwd": 6673408,
-        "ntt_inv": 8529920,
-        "ks_moddown_u": 10110464,
-        "relin_final": 12830720,
-        "rescale_final": 9590400,
-        "ks_moddown_convert": 80157355
+        "ks_modup_convert": 105840640
     },
 }
 VALU_ISSUE_PEAK_G = 1024 * 2.4e9 / 4 / 1e9
