@@ -161,6 +161,17 @@ int ckks_ntt_inv(const ckks_ctx *ctx, uint64_t *x, int count, int first_prime, i
 int ckks_pointwise_mul(const ckks_ctx *ctx, const uint64_t *a, const uint64_t *b, uint64_t *out, int count,
                        int first_prime, int nlimbs, void *stream);
 
+/* Range check of residues: writes to *out_count (device memory, 8-byte
+ * aligned) the number of residues of x ([count][nlimbs][n], limb r modulo
+ * prime first_prime + r) that are not below their prime.  The operations
+ * take residues as reduced and do not check them (that would cost one more
+ * read of every input); a caller whose residues come from outside (files,
+ * other processes) runs this first and rejects a non-zero count.  count = 0
+ * or nlimbs = 0 writes 0.  Stream-ordered: the count is ready when the work
+ * queued before it on `stream` is. */
+int ckks_count_unreduced(const ckks_ctx *ctx, const uint64_t *x, int count, int first_prime, int nlimbs,
+                         uint32_t *out_count, void *stream);
+
 /* Ciphertext-ciphertext multiply with relinearisation (the Kestrel
  * article's wall 2: a product's noise grows, and relinearisation brings the
  * degree-2 ciphertext back to two polynomials): for each of `batch` pairs,

@@ -62,6 +62,7 @@ SIGNATURES = {
     "ckks_ntt_inv": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p]),
     "ckks_pointwise_mul": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int,
                                      C.c_void_p]),
+    "ckks_count_unreduced": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p]),
     "ckks_mul_tensor_relin": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.POINTER(Swk), C.c_void_p, C.c_int,
                                         C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
     "ckks_rescale": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_size_t,

@@ -147,6 +147,15 @@ class Context:
                                                _stream()), "ckks_pointwise_mul")
         return out
 
+    def count_unreduced(self, x, first_prime: int = 0) -> int:
+        """Number of residues of x ([..][nlimbs][n]) at or above their prime (ckks_count_unreduced)."""
+        nl = x.shape[-2]
+        count = x.numel() // (x.shape[-1] * nl)
+        cnt = torch.empty(2, dtype=torch.int32, device=x.device)  # 8-byte aligned counter
+        nat.check(nat.lib().ckks_count_unreduced(self._h, _ptr(x), count, first_prime, nl, cnt.data_ptr(),
+                                                 _stream()), "ckks_count_unreduced")
+        return int(cnt[0].item())
+
     def mul_tensor_relin(self, a, b, rlk, out=None, ws=None):
         B, _, l, n = a.shape
         out = torch.empty_like(a) if out is None else out

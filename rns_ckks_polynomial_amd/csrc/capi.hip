@@ -122,6 +122,18 @@ extern "C" int ckks_pointwise_mul(const ckks_ctx *c, const uint64_t *a, const ui
     return op_pointwise_mul(c, a, b, out, count, first, nlimbs, (hipStream_t)stream);
 }
 
+extern "C" int ckks_count_unreduced(const ckks_ctx *c, const uint64_t *x, int count, int first, int nlimbs,
+                                    uint32_t *out_count, void *stream) {
+    if (!c) return CKKS_EINVAL;
+    int e;
+    if (count < 0 || nlimbs < 0 || first < 0 || (uint64_t)first + nlimbs > c->L + c->K) return CKKS_EINVAL;
+    if ((e = check_ptr(out_count))) return e;  // 4-byte counter: the 8-byte alignment rule holds for it too
+    if (count > 0 && nlimbs > 0 && (e = check_ptr(x))) return e;
+    DeviceGuard g(c->device);
+    if (!g.ok) return CKKS_EHIP;
+    return op_count_unreduced(c, x, count, first, nlimbs, out_count, (hipStream_t)stream);
+}
+
 extern "C" int ckks_mul_tensor_relin(const ckks_ctx *c, const uint64_t *a, const uint64_t *b, const ckks_swk *rlk,
                                      uint64_t *out, int batch, int level, void *ws, size_t ws_bytes, void *stream) {
     if (!c || !c->K) return CKKS_EINVAL;

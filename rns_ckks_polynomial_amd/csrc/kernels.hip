@@ -211,6 +211,30 @@ __device__ __forceinline__ uint32_t galois_src(uint32_t j, uint32_t g, uint32_t 
     return (uint32_t)((((uint64_t)g * (2 * j + 1)) & (2ull * n - 1)) >> 1);
 }
 
+// Residues at or above their prime in [count][nl][n] (limb r modulo prime first + r): the
+// count is added to *cnt (cleared by the first kernel, so the pair works under stream capture).
+__global__ void k_clear_u32(uint32_t *p) { *p = 0; }
+__global__ void k_count_unreduced(const uint64_t *__restrict__ x, const PrimeConsts *__restrict__ pc, uint32_t n,
+                                  uint32_t nl, uint32_t first, size_t total, uint32_t *__restrict__ cnt) {
+    uint32_t mine = 0;
+    for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < total; e += (size_t)gridDim.x * blockDim.x)
+        mine += x[e] >= pc[first + (e / n) % nl].q;
+    if (mine) atomicAdd(cnt, mine);
+}
+
+int op_count_unreduced(const ckks_ctx *c, const uint64_t *x, int count, int first, int nlimbs, uint32_t *out,
+                       hipStream_t s) {
+    const size_t total = (size_t)count * nlimbs * c->n;
+    hipLaunchKernelGGL(k_clear_u32, dim3(1), dim3(1), 0, s, out);
+    LAUNCH_CHECK();
+    if (total) {
+        hipLaunchKernelGGL(k_count_unreduced, grid_for(total), dim3(256), 0, s, x, c->d_pc, c->n, (uint32_t)nlimbs,
+                           (uint32_t)first, total, out);
+        LAUNCH_CHECK();
+    }
+    return CKKS_OK;
+}
+
 int op_pointwise_mul(const ckks_ctx *c, const uint64_t *a, const uint64_t *b, uint64_t *out, int count, int first,
                      int nlimbs, hipStream_t s) {
     const size_t total = (size_t)count * nlimbs * c->n;

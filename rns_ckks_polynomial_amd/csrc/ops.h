@@ -10,6 +10,9 @@ int op_ntt(const ckks_ctx *c, uint64_t *x, int count, int first, int nlimbs, boo
 
 int op_pointwise_mul(const ckks_ctx *c, const uint64_t *a, const uint64_t *b, uint64_t *out, int count, int first,
                      int nlimbs, hipStream_t s);
+// Residues >= their prime in [count][nlimbs][n] (limb r modulo prime first + r), written to *out.
+int op_count_unreduced(const ckks_ctx *c, const uint64_t *x, int count, int first, int nlimbs, uint32_t *out,
+                       hipStream_t s);
 
 size_t ws_bytes_relin(const ckks_ctx *c, int B, int l);
 size_t ws_bytes_rotate(const ckks_ctx *c, int B, int l);

@@ -6,7 +6,7 @@ import ctypes as C
 
 import pytest
 
-from gpu_util import gpu_ctx, host, require_gpu, say, torch
+from gpu_util import dev, gpu_ctx, host, require_gpu, say, torch
 from rns_ckks_polynomial_amd import _native as nat
 from rns_ckks_polynomial_amd.api import SwitchKey, galois_rot
 
@@ -148,3 +148,35 @@ def test_level_not_prepared():
     torch.cuda.synchronize()
     assert not host(g.rotate(x, ge, key)).any()                  # zeros switch to zeros
     assert not host(g.mod_raise(x[:, :, :5].contiguous(), 299)).any()
+
+
+def test_count_unreduced():
+    """Residues are taken as reduced and never range-checked by the operations;
+    ckks_count_unreduced is the caller's check.  It counts every residue at or
+    above its prime (limb r against prime first_prime + r), and only those."""
+    import numpy as np
+    from rns_ckks_polynomial_amd import synth
+    g = gpu_ctx(*P)
+    n, pr = g.n, [int(q) for q in g.primes]
+    nl = 4
+    x = synth.uniform_mod(7, synth.TAG_POLY, np.arange(3 * nl), np.tile(np.array(pr[:nl], dtype=np.uint64), 3),
+                          n).reshape(3, nl, n)
+    say("count_unreduced: reduced input")
+    assert g.count_unreduced(dev(x)) == 0
+    y = x.copy()
+    y[0, 0, 5] = pr[0]                # exactly q
+    y[1, 2, 2047] = pr[2] + 7         # q + 7
+    y[2, 3, 0] = (1 << 64) - 1        # the largest word
+    y[2, 1, 9] = pr[1] - 1            # q - 1 is reduced
+    t = dev(y)
+    assert g.count_unreduced(t) == 3
+    # limb r is checked against prime first_prime + r (the chain is ascending)
+    z = x[:, :3].copy()
+    z[0, 0, 1] = pr[1]                # limb 0: >= pr[0] and >= pr[1]
+    z[0, 1, 1] = pr[1]                # limb 1: >= pr[1], below pr[2]
+    tz = dev(z)
+    assert g.count_unreduced(tz, first_prime=0) == 2
+    assert g.count_unreduced(tz, first_prime=1) == 1
+    assert g.count_unreduced(t[:0]) == 0
+    with pytest.raises(nat.CkksError):
+        g.count_unreduced(t, first_prime=g.L + g.K - 2)  # limbs past the last prime
