@@ -168,7 +168,9 @@ int ckks_pointwise_mul(const ckks_ctx *ctx, const uint64_t *a, const uint64_t *b
  * read of every input); a caller whose residues come from outside (files,
  * other processes) runs this first and rejects a non-zero count.  count = 0
  * or nlimbs = 0 writes 0.  Stream-ordered: the count is ready when the work
- * queued before it on `stream` is. */
+ * queued before it on `stream` is.  Errors: CKKS_EINVAL (null context or
+ * counter, negative sizes, limbs past the last prime), CKKS_EALIGN (x or the
+ * counter not 8-byte aligned). */
 int ckks_count_unreduced(const ckks_ctx *ctx, const uint64_t *x, int count, int first_prime, int nlimbs,
                          uint32_t *out_count, void *stream);
 
