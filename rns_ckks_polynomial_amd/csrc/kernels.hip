@@ -1059,7 +1059,7 @@ __global__ void k_inner(const uint64_t *__restrict__ d, size_t d_stride, const u
 //   out[b][c][i][k] = (acc[b][c][i][k] - NTT(conv)[b][c][i][k]) P^-1 + extra
 //   MODE 1: relin (c0: a0 b0, c1: a0 b1 + a1 b0); 2: rotate (c0: in[b][0][i][galois]);
 //   ACCUM: out += result instead of out = result.
-// blockIdx.y: pair index u = limb0 + y (MapPolyPairs order: the two polynomials of
+// Row index y: pair index u = limb0 + y (MapPolyPairs order: the two polynomials of
 // one (ciphertext, limb) are neighbours, so the workgroups that both read a0 and b0
 // of a relinearisation run back to back on one XCD and the second finds them in
 // L2); the NTT values meet their accumulator in registers instead of a round trip
@@ -1076,11 +1076,20 @@ __global__ __launch_bounds__(mp::NT) void k_rows_final(uint32_t limb0, const Pri
     using namespace mp;
     constexpr uint32_t n = MP_N1 * MP_N1;
     __shared__ uint64_t lds[V * VSTRIDE];
-    const uint32_t u = limb0 + blockIdx.y, c = u % 2, i = (u / 2) % l;
+    // MODE 2: the 32 row blocks of a pair of limbs (c0 and c1 of one ciphertext limb) share one XCD
+    // (workgroups are dealt to the 8 XCDs in turn), so the gather of c0 over its whole limb is served by
+    // that XCD's L2; a last group of fewer than 16 limbs keeps the plain order.
+    uint32_t by = blockIdx.y, bx = blockIdx.x;
+    if (MODE == 2 && by < (gridDim.y & ~15u)) {
+        const uint32_t id = by * 16 + bx, r = id & 255;
+        by = (id >> 8) * 16 + 2 * (r & 7) + (r >> 7);
+        bx = (r >> 3) & 15;
+    }
+    const uint32_t u = limb0 + by, c = u % 2, i = (u / 2) % l;
     const size_t b = u / (2 * l);
     const size_t limb = (b * 2 + c) * l + i;
     const uint64_t q = pc[i].q, mu = pc[i].mu;
-    const int r0 = blockIdx.x * V;
+    const int r0 = bx * V;
     // output lanes run across rows (128-byte runs of the limb); their accumulator values and extra
     // terms are requested and formed before the row transform, so the loads are in flight while
     // its butterflies run (its barriers keep the compiler from sinking them)
@@ -1110,7 +1119,7 @@ __global__ __launch_bounds__(mp::NT) void k_rows_final(uint32_t limb0, const Pri
     }
     {
         const BfConsts bc = bf_consts(q);
-        const uint64_t *in = scratch + (size_t)blockIdx.y * n;
+        const uint64_t *in = scratch + (size_t)by * n;
         const int t = threadIdx.x % 16, v = threadIdx.x / 16;  // lanes along a row
         uint64_t x[E];
 #pragma unroll
@@ -1139,8 +1148,8 @@ static int moddown_final_mp(const ckks_ctx *c, uint64_t *conv, const uint64_t *a
     if (!p || !mps) return CKKS_EUNSUPPORTED;
     const int nblk = (int)(nout * 2 * l);
     MapPolyPairs m{conv, c->n, (uint32_t)l};
-    for (int l0 = 0; l0 < nblk; l0 += MP_CHUNK) {
-        const dim3 grid(MP_N1 / mp::V, (unsigned)std::min<int>(MP_CHUNK, nblk - l0)), blk(mp::NT);
+    for (int l0 = 0, ch = mp_chunk(nblk); l0 < nblk; l0 += ch) {
+        const dim3 grid(MP_N1 / mp::V, (unsigned)std::min<int>(ch, nblk - l0)), blk(mp::NT);
         hipLaunchKernelGGL(mp::k_fwd_cols<MapPolyPairs>, grid, blk, 0, s, m, (uint32_t)l0, c->d_pc, p->d_tw256f,
                            p->d_taf, mps);
         hipLaunchKernelGGL((k_rows_final<MODE, ACCUM>), grid, blk, 0, s, (uint32_t)l0, c->d_pc, p->d_rowf,

@@ -30,7 +30,14 @@
 namespace ckks {
 
 constexpr uint32_t MP_N1 = 256, MP_LOG1 = 8;
-constexpr uint32_t MP_CHUNK = 256;  // limbs per transpose pass (256 x 512 KiB = 128 MiB)
+constexpr uint32_t MP_CHUNK = 320;  // most limbs per transpose pass (320 x 512 KiB = 160 MiB)
+
+// Limbs per pass for nblk limbs: the fewest passes of at most MP_CHUNK, evenly sized, so that
+// no pass is a short tail that leaves most of the chip idle.
+inline int mp_chunk(int nblk) {
+    const int passes = (nblk + (int)MP_CHUNK - 1) / (int)MP_CHUNK;
+    return passes > 1 ? (nblk + passes - 1) / passes : nblk;
+}
 
 struct MultipassPlan {
     uint64_t *d_tw256f = nullptr, *d_tw256i = nullptr;  // [ntot][256][2]  (psi^256)^(+-bitrev8(k)), Shoup

@@ -273,8 +273,8 @@ static int multipass_launch(const ckks_ctx *c, const Map &map, int nblk, bool in
                             uint64_t *scratch, uint32_t gal) {
     const MultipassPlan *p = c->mp;
     const dim3 blk(mp::NT);
-    for (int l0 = 0; l0 < nblk; l0 += MP_CHUNK) {
-        const dim3 grid(MP_N1 / mp::V, (unsigned)std::min<int>(MP_CHUNK, nblk - l0));
+    for (int l0 = 0, ch = mp_chunk(nblk); l0 < nblk; l0 += ch) {
+        const dim3 grid(MP_N1 / mp::V, (unsigned)std::min<int>(ch, nblk - l0));
         if (!inverse) {
             hipLaunchKernelGGL(mp::k_fwd_cols<Map>, grid, blk, 0, s, map, (uint32_t)l0, c->d_pc, p->d_tw256f,
                                p->d_taf, scratch);
