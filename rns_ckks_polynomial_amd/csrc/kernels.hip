@@ -595,8 +595,13 @@ __global__ __launch_bounds__(256, OCC == 3 ? 4 : OCC) void k_convert_mfma(const 
         const uint32_t t = conv_target<MODE>(ct, p, lo, m);
         const uint32_t slot = (MODE == 0 && t >= ct.L) ? ct.l + (t - ct.L) : t;
         uint64_t *ob = out + (s / lay.inner) * ct.out_so + (s % lay.inner) * ct.out_si + (size_t)slot * n + kb + 4 * grp;
+        if constexpr (OCC == 3) {  // one chunk of at most 32 rows
 #pragma unroll
-        for (int v = 0; v < 4; v++) ob[v] = mf_recombine(acc, v, w2, k);
+            for (int v = 0; v < 4; v++) ob[v] = mf_recombine32(acc, v, w2, k);
+        } else {
+#pragma unroll
+            for (int v = 0; v < 4; v++) ob[v] = mf_recombine(acc, v, w2, k);
+        }
     };
     mf_v4i acc[TT][15];
     // the flat sequence g = pass nch + ch over passes of TT tiles; rows are
@@ -1542,7 +1547,7 @@ __global__ __launch_bounds__(256, 2) void k_bsgs_mac_mfma(const uint64_t *__rest
             for (int d = 0; d < 15; d++) acc[d] = mf_v4i{0, 0, 0, 0};
             mf_mac_tile(acc, AW, H);
 #pragma unroll
-            for (int v = 0; v < 4; v++) res[qk][v] = mf_recombine(acc, v, w2, rk);
+            for (int v = 0; v < 4; v++) res[qk][v] = mf_recombine32(acc, v, w2, rk);  // at most 32 baby steps
         }
         __syncthreads();  // every wave is done with the diagonals
         // the sums of (giant step g0 + 4 grp + v, polynomial col) at sp[(g c)][k]

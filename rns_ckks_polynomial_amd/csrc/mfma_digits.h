@@ -181,4 +181,38 @@ __device__ __forceinline__ uint64_t mf_recombine(const mf_v4i (&acc)[15], int v,
     return (uint64_t)r;
 }
 
+// mf_recombine for contractions of at most 32 rows (one chunk): then |S_s| <= n_s 32 2^14, with
+// n_s = min(s, 14 - s) + 1 digit pairs on diagonal s, so neighbouring diagonals merge exactly
+// into int32 sums
+//   P_j = S_2j + 256 S_2j+1 (|P_j| < 2^30 + 2^22),  value = sum_j 2^16j P_j + 2^112 S_14,
+// which halves the 64-bit multiply-adds.
+__device__ __forceinline__ uint64_t mf_recombine32(const mf_v4i (&acc)[15], int v, const MfW2 &w2, const MfRecomb &k) {
+    int32_t p[7];
+#pragma unroll
+    for (int j = 0; j < 7; j++) p[j] = acc[2 * j][v] + acc[2 * j + 1][v] * 256;
+    // lo: weights 1, 2^16 and the low 30 bits of 2^16j mod t (j = 4, 5, 6, and 2^112 for S_14);
+    // hi: weights 2^2, 2^18 (2^32 = 2^30 2^2, 2^48 = 2^30 2^18) and the high bits (below 2^29.01,
+    // as t < 2^59.01).  With |P_4|, |P_5|, |P_6| below 0.76, 0.51, 0.26 2^30: |lo| < 1.52 2^60
+    // and |hi| < 0.77 2^60, so h1 below fits the 2^31 offset of mf_recombine
+    int64_t lo = (int64_t)p[0] + (int64_t)p[1] * (int64_t)w2.w[1];
+    int64_t hi = (int64_t)p[2] * (int64_t)w2.w[3] + (int64_t)p[3] * (int64_t)w2.w[5];
+#pragma unroll
+    for (int j = 4; j < 7; j++) {
+        lo += (int64_t)p[j] * (int64_t)k.clo[2 * (j - 4)];
+        hi += (int64_t)p[j] * (int64_t)k.chi[2 * (j - 4)];
+    }
+    lo += (int64_t)acc[14][v] * (int64_t)k.clo[6];
+    hi += (int64_t)acc[14][v] * (int64_t)k.chi[6];
+    // as in mf_recombine: 0 < x = lo + 2^30 h0 + [2^60 (h1 + 2^31)]_lazy + 8t - [2^91]_t < 8.6 2^60
+    const uint64_t h0 = (uint64_t)hi & M30;
+    const uint32_t h1b = (uint32_t)(hi >> 30) ^ 0x80000000u;
+    const uint64_t x = (uint64_t)lo + (h0 << 30) + shoup_lazy(h1b, k.r60, k.r60p, k.tq) + k.kfix;
+    // t in (2^59, 2^59 + 2^52) and x < 2^64: x / 2^59 exceeds x / t by less than 1/4, so
+    // x >> 59 is floor(x / t) or one more
+    const uint64_t qh = x >> 59;
+    int64_t r = (int64_t)(x - qh * k.tq);
+    r += (r >> 63) & (int64_t)k.tq;
+    return (uint64_t)r;
+}
+
 }  // namespace ckks
