@@ -45,24 +45,24 @@ LIMB = N * 8
 # counters (profiles/bench_step_n2048_l112_b8_hbm_counters.md).  Valid only for
 # the kernel sources they were taken on (hash of rns_ckks_polynomial_amd/csrc).
 MEASURED_TRAFFIC = {
-    "source_sha": "754dc6bff01b6173",
+    "source_sha": "0ee6985e7925197f",
     "bytes_per_launch": {
-        "ks_ntt_ext": 1356338712,
-        "ks_modup_convert": 855360664,
-        "bsgs_mac": 3758581339,
-        "rotate_final": 3191027712,
-        "ks_inner_product_sum": 2848776357,
-        "ks_inner_product_hoisted": 1870779136,
-        "giant_final": 304291182,
-        "ks_intt_modup": 326826990,
-        "ks_intt_moddown": 310288975,
-        "ks_inner_product": 462657737,
+        "ks_ntt_ext": 1355860687,
+        "ks_modup_convert": 809429742,
+        "bsgs_mac": 3758572581,
+        "rotate_final": 3190984046,
+        "ks_inner_product_sum": 2848879762,
+        "ks_inner_product_hoisted": 1871196343,
+        "giant_final": 304351397,
+        "ks_intt_modup": 326835383,
+        "ks_intt_moddown": 310300312,
+        "ks_inner_product": 462668571,
         "ntt_fwd": 62548992,
         "ntt_inv": 62589824,
-        "ks_moddown_u": 231747511,
-        "relin_final": 155773787,
-        "rescale_final": 118068398,
-        "ks_moddown_convert": 768896695
+        "ks_moddown_u": 231746395,
+        "relin_final": 154517303,
+        "rescale_final": 118329143,
+        "ks_moddown_convert": 746608384
     },
 }
 
@@ -73,9 +73,9 @@ MEASURED_TRAFFIC = {
 # its SIMD (wave64 on 16 lanes; the 32-bit multiplies included, as measured on this GPU), so
 # 1024 SIMDs x 2.4 GHz / 4 = 614.4 G wave-instructions/s is the issue ceiling.
 MEASURED_SQ = {
-    "source_sha": "754dc6bff01b6173",
+    "source_sha": "0ee6985e7925197f",
     "valu_per_launch": {
-        "ks_modup_convert": 105840640
+        "ks_modup_convert": 100597760
     },
 }
 VALU_ISSUE_PEAK_G = 1024 * 2.4e9 / 4 / 1e9
