@@ -122,7 +122,6 @@ struct Split3 {
     uint64_t a0, a1, a1b, a2;
 };
 __device__ __forceinline__ uint64_t split30(uint64_t v) { return (v & M30) | ((v >> 30) << 32); }
-__device__ __forceinline__ uint64_t unsplit30(uint64_t s) { return (s & M30) | ((s >> 32) << 30); }
 __device__ __forceinline__ void smac(Split3 &s, uint32_t xb, uint32_t xa, uint64_t ysplit) {
     const uint32_t yb = (uint32_t)ysplit, ya = (uint32_t)(ysplit >> 32);
     s.a0 += (uint64_t)xb * yb;
@@ -235,6 +234,10 @@ struct BasisDev {
 // every byte position, then flipping each byte's top bit, subtracts it back).
 __host__ __device__ __forceinline__ uint64_t digit_form(uint64_t v) {
     return (v + 0x8080808080808080ull) ^ 0x8080808080808080ull;
+}
+// The value back from its digit form.
+__host__ __device__ __forceinline__ uint64_t undigit(uint64_t z) {
+    return (z ^ 0x8080808080808080ull) - 0x8080808080808080ull;
 }
 constexpr uint32_t MF_MAX_ROWS = 2048;  // |S_s| <= 8 rows 2^14 <= 2^28
 

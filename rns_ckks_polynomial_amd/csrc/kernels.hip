@@ -42,7 +42,7 @@ static inline dim3 grid_for(size_t total) {
 // replaces n^-1 on the inverse.  src == nullptr skips the block.
 // =====================================================================
 struct MapStrided {  // [count][nl][n], limb r -> prime first + r
-    static constexpr bool split_out = false;
+    static constexpr bool digit_out = false;
     const uint64_t *src;
     uint64_t *dst;
     uint32_t n, nl, first;
@@ -57,7 +57,7 @@ struct MapStrided {  // [count][nl][n], limb r -> prime first + r
 };
 
 struct MapBatched {  // limb r of ciphertext b at src + b * src_stride + r * n -> dst [B][nl][n]
-    static constexpr bool split_out = true;  // ModUp inputs y: stored in split30 form
+    static constexpr bool digit_out = true;  // ModUp inputs y: stored in digit form (digit_form)
     const uint64_t *src;
     size_t src_stride;
     uint64_t *dst;
@@ -74,7 +74,7 @@ struct MapBatched {  // limb r of ciphertext b at src + b * src_stride + r * n -
 };
 
 struct MapExt {  // converted limbs [B][beta][l+K][n]; skips the digit's own primes
-    static constexpr bool split_out = false;
+    static constexpr bool digit_out = false;
     uint64_t *ext;
     uint32_t n, l, L, K, beta, alpha;
     __device__ __forceinline__ void get(int blk, const uint64_t *&s, uint64_t *&d, int &prime,
@@ -95,7 +95,7 @@ struct MapExt {  // converted limbs [B][beta][l+K][n]; skips the digit's own pri
 };
 
 struct MapPolyPairs {  // [B][2][l][n] in place, visited as u = (b l + i) 2 + c (the two polynomials adjacent)
-    static constexpr bool split_out = false;
+    static constexpr bool digit_out = false;
     uint64_t *x;
     uint32_t n, l;
     __device__ __forceinline__ void get(int blk, const uint64_t *&s, uint64_t *&d, int &prime,
@@ -109,7 +109,7 @@ struct MapPolyPairs {  // [B][2][l][n] in place, visited as u = (b l + i) 2 + c 
 };
 
 struct MapLast {  // last limb of each polynomial [P][l][n] -> dense [P][n]
-    static constexpr bool split_out = false;
+    static constexpr bool digit_out = false;
     const uint64_t *src;
     uint64_t *dst;
     uint32_t n, l;
@@ -123,7 +123,7 @@ struct MapLast {  // last limb of each polynomial [P][l][n] -> dense [P][n]
 };
 
 struct MapAccP {  // P limbs of acc [B][2][l+K][n], scaled inverse -> ModDown inputs
-    static constexpr bool split_out = true;  // ModDown inputs y: stored in split30 form
+    static constexpr bool digit_out = true;  // ModDown inputs y: stored in digit form (digit_form)
     uint64_t *acc;
     uint32_t n, l, L, K;
     const uint64_t *scale;  // [K][2]
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256) void k_ntt2048(Map map, const PrimeConsts *__r
 #pragma unroll
         for (int k = 0; k < 8; k++) {
             const uint64_t r = shoup(v[k], w, wp, q);
-            dst[t + 256 * k] = Map::split_out ? split30(r) : r;
+            dst[t + 256 * k] = Map::digit_out ? digit_form(r) : r;
         }
     }
 }
@@ -271,10 +271,10 @@ __global__ void k_prep_relin(const uint64_t *__restrict__ a, const uint64_t *__r
 __device__ __attribute__((noinline)) uint32_t exact_u_slow(const BasisDev &B, uint64_t *ycol, size_t stride,
                                                           uint32_t floor_s, const PrimeConsts *__restrict__ pc) {
     const uint32_t m = B.m;
-    // x_i = y_i [Bhat_i]_{b_i}, in place (y arrives in split30 form, x is plain)
+    // x_i = y_i [Bhat_i]_{b_i}, in place (y arrives in digit form, x is plain)
     for (uint32_t i = 0; i < m; i++) {
         const uint64_t bi = pc[B.first + i].q;
-        ycol[i * stride] = shoup(unsplit30(ycol[i * stride]), B.hat_mod[2 * i], B.hat_mod[2 * i + 1], bi);
+        ycol[i * stride] = shoup(undigit(ycol[i * stride]), B.hat_mod[2 * i], B.hat_mod[2 * i + 1], bi);
     }
     // Garner, in place: after step i, slot i holds mixed-radix digit a_i and
     // slots k > i hold (x - a_0 - ... ) / (b_0 ... b_i) mod b_k.
@@ -301,7 +301,7 @@ __device__ __attribute__((noinline)) uint32_t exact_u_slow(const BasisDev &B, ui
             ak = ak >= P.q ? ak - P.q : ak;
             r = addm(mulm(r, bk, P.q, P.mu), ak, P.q);
         }
-        ycol[i * stride] = split30(shoup(r, B.inv_hat[2 * i], B.inv_hat[2 * i + 1], P.q));
+        ycol[i * stride] = digit_form(shoup(r, B.inv_hat[2 * i], B.inv_hat[2 * i + 1], P.q));
     }
     return floor_s + (cmp > 0 ? 1u : 0u);
 }
@@ -339,7 +339,7 @@ __global__ void k_basis_u(const BasisDev *__restrict__ bases, SetLayout lay, uin
         for (int a = 0; a < 32; a++) asm volatile("" : "+v"(yv[a]));
 #pragma unroll
         for (int a = 0; a < 32; a++)
-            if ((uint32_t)a < m) add(unsplit30(yv[a]), gload(B.R + a));
+            if ((uint32_t)a < m) add(undigit(yv[a]), gload(B.R + a));
     }
     // the sum is exact integer arithmetic, so inputs are taken 8 at a time
     // with all 8 loads in flight before the first is used
@@ -348,7 +348,7 @@ __global__ void k_basis_u(const BasisDev *__restrict__ bases, SetLayout lay, uin
 #pragma unroll
         for (int a = 0; a < 8; a++) {
             const uint32_t i = min(i0 + a, m - 1);
-            yv[a] = unsplit30(yb[(size_t)i * n]);
+            yv[a] = undigit(yb[(size_t)i * n]);
             rv[a] = gload(B.R + i);
         }
 #pragma unroll
@@ -470,7 +470,7 @@ __global__ __launch_bounds__(256, OCC == 3 ? 4 : OCC) void k_convert_mfma(const 
         for (int j = 0; j < 8; j++) {
             const uint32_t r = min(r0 + j, m - 1);
             const uint64_t rr = r0 + j < m ? gload(B.R + r) : 0;
-            frac += mulhi64(unsplit30(raw[j]) << 4, rr);
+            frac += mulhi64(undigit(raw[j]) << 4, rr);
             ip += (uint32_t)(frac >> 63);
             frac &= M63;
         }
@@ -523,16 +523,16 @@ __global__ __launch_bounds__(256, OCC == 3 ? 4 : OCC) void k_convert_mfma(const 
     auto build_a = [&](const uint64_t(&raw)[8], uint32_t uraw, uint32_t ch) {
         if constexpr (FOLD_U) uraw = exact_u(raw, ch);
         const uint32_t r0 = (ch % cps) * 32 + 8 * grp;
-        // row r < m is input y_r, row m the u row, the rest zero: selected without branches, so
-        // that no lane-divergent block waits for every load in flight (the prefetched chunks)
+        // row r < m is input y_r (stored in digit form), row m the u row, the rest zero (whose digit
+        // form is 0): selected without branches, so that no lane-divergent block waits for every
+        // load in flight (the prefetched chunks)
+        const uint64_t zu = digit_form(uraw);
         uint64_t z[8];
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             const uint32_t r = r0 + j;
-            const uint64_t yv = unsplit30(raw[j]);
-            uint64_t v = r < m ? yv : (uint64_t)uraw;
-            v = r <= m ? v : 0;
-            z[j] = digit_form(v);
+            uint64_t v = r < m ? raw[j] : zu;
+            z[j] = r <= m ? v : 0;
         }
         long pl[8];
         mf_planes(z, pl);

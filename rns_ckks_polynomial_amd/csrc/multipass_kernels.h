@@ -262,7 +262,7 @@ __global__ __launch_bounds__(NT) void k_inv_cols(Map map, uint32_t limb0, const 
 #pragma unroll
     for (int k = 0; k < E; k++) {
         const uint64_t r = shoup(x[k], w, wp, P.q);
-        dst[(size_t)(t + 16 * k) * MP_N1 + c0 + v] = Map::split_out ? split30(r) : r;
+        dst[(size_t)(t + 16 * k) * MP_N1 + c0 + v] = Map::digit_out ? digit_form(r) : r;
     }
 }
 
