@@ -45,24 +45,24 @@ LIMB = N * 8
 # counters (profiles/bench_step_n2048_l112_b8_hbm_counters.md).  Valid only for
 # the kernel sources they were taken on (hash of rns_ckks_polynomial_amd/csrc).
 MEASURED_TRAFFIC = {
-    "source_sha": "0ee6985e7925197f",
+    "source_sha": "9044020cdb2450c8",
     "bytes_per_launch": {
-        "ks_ntt_ext": 1355860687,
-        "ks_modup_convert": 809429742,
-        "bsgs_mac": 3758572581,
-        "rotate_final": 3190984046,
-        "ks_inner_product_sum": 2848879762,
-        "ks_inner_product_hoisted": 1871196343,
-        "giant_final": 304351397,
-        "ks_intt_modup": 326835383,
-        "ks_intt_moddown": 310300312,
-        "ks_inner_product": 462668571,
+        "ks_ntt_ext": 1355563477,
+        "ks_modup_convert": 809505158,
+        "bsgs_mac": 3758571721,
+        "rotate_final": 3190957605,
+        "ks_inner_product_sum": 2848877623,
+        "ks_inner_product_hoisted": 1871104165,
+        "giant_final": 304220581,
+        "ks_intt_modup": 326835096,
+        "ks_intt_moddown": 310301147,
+        "ks_inner_product": 462657015,
         "ntt_fwd": 62548992,
-        "ntt_inv": 62589824,
-        "ks_moddown_u": 231746395,
-        "relin_final": 154517303,
-        "rescale_final": 118329143,
-        "ks_moddown_convert": 746608384
+        "ntt_inv": 62588800,
+        "ks_moddown_u": 231750418,
+        "relin_final": 154853943,
+        "rescale_final": 118064832,
+        "ks_moddown_convert": 747532794
     },
 }
 
@@ -73,9 +73,9 @@ MEASURED_TRAFFIC = {
 # its SIMD (wave64 on 16 lanes; the 32-bit multiplies included, as measured on this GPU), so
 # 1024 SIMDs x 2.4 GHz / 4 = 614.4 G wave-instructions/s is the issue ceiling.
 MEASURED_SQ = {
-    "source_sha": "0ee6985e7925197f",
+    "source_sha": "9044020cdb2450c8",
     "valu_per_launch": {
-        "ks_modup_convert": 100597760
+        "ks_modup_convert": 95600640
     },
 }
 VALU_ISSUE_PEAK_G = 1024 * 2.4e9 / 4 / 1e9
