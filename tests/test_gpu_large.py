@@ -85,6 +85,25 @@ def test_ring65536_ntt_round_trip():
     assert np.array_equal(host(p), o.ntt(pc, first=40))
 
 
+def test_ring65536_ntt_uneven_passes():
+    """680 limbs need more than one transposition pass (at most 320 limbs each), split
+    evenly into 227 + 227 + 226: the limbs on both sides of each pass boundary against
+    the oracle, and the inverse restores every limb."""
+    g, o = gpu_ctx(*C5), oracle_ctx(*C5)
+    seed = 0xC0DE0015
+    x = gfill(g, (17, 40, 65536), seed, synth.TAG_POLY)
+    y = x.clone()
+    say("ring65536 NTT, 680 limbs in three passes")
+    g.ntt_fwd(y)
+    yh = host(y).reshape(680, 65536)
+    for u in (0, 226, 227, 453, 454, 679):
+        r = u % 40
+        xu = synth.uniform_mod(seed, synth.TAG_POLY, np.array([u]), np.array([o.primes[r]]), o.n).reshape(1, o.n)
+        assert np.array_equal(yh[u], o.ntt(xu, first=r)[0]), u
+    g.ntt_inv(y)
+    assert np.array_equal(host(y), host(x))
+
+
 def test_ring65536_l40_relin_rotations_rescale():
     """4 pairs at l=40: p = relin(tensor(x, y)); r_i = rotate(p, 2^i), i < 16; the
     conjugation of p; rescale all.  Ciphertext 0 of every result and ciphertext 3
