@@ -45,24 +45,24 @@ LIMB = N * 8
 # counters (profiles/bench_step_n2048_l112_b8_hbm_counters.md).  Valid only for
 # the kernel sources they were taken on (hash of rns_ckks_polynomial_amd/csrc).
 MEASURED_TRAFFIC = {
-    "source_sha": "9044020cdb2450c8",
+    "source_sha": "5ae6451959d02f82",
     "bytes_per_launch": {
-        "ks_ntt_ext": 1355563477,
-        "ks_modup_convert": 809505158,
-        "bsgs_mac": 3758571721,
-        "rotate_final": 3190957605,
-        "ks_inner_product_sum": 2848877623,
-        "ks_inner_product_hoisted": 1871104165,
-        "giant_final": 304220581,
-        "ks_intt_modup": 326835096,
-        "ks_intt_moddown": 310301147,
-        "ks_inner_product": 462657015,
-        "ntt_fwd": 62548992,
-        "ntt_inv": 62588800,
-        "ks_moddown_u": 231750418,
-        "relin_final": 154853943,
-        "rescale_final": 118064832,
-        "ks_moddown_convert": 747532794
+        "ks_ntt_ext": 1357901990,
+        "ks_modup_convert": 809505611,
+        "bsgs_mac": 3758289747,
+        "rotate_final": 3190481055,
+        "ks_inner_product_sum": 2848543492,
+        "ks_inner_product_hoisted": 1870706106,
+        "giant_final": 304396161,
+        "ks_intt_modup": 326825340,
+        "ks_intt_moddown": 310284250,
+        "ks_inner_product": 462626102,
+        "ntt_fwd": 62542593,
+        "ntt_inv": 62584445,
+        "ks_moddown_u": 231727448,
+        "relin_final": 155729082,
+        "rescale_final": 118075203,
+        "ks_moddown_convert": 747683036
     },
 }
 
@@ -73,9 +73,24 @@ MEASURED_TRAFFIC = {
 # its SIMD (wave64 on 16 lanes; the 32-bit multiplies included, as measured on this GPU), so
 # 1024 SIMDs x 2.4 GHz / 4 = 614.4 G wave-instructions/s is the issue ceiling.
 MEASURED_SQ = {
-    "source_sha": "9044020cdb2450c8",
+    "source_sha": "5ae6451959d02f82",
     "valu_per_launch": {
-        "ks_modup_convert": 95600640
+        "ks_ntt_ext": 146578432,
+        "ks_modup_convert": 102412288,
+        "bsgs_mac": 169279488,
+        "rotate_final": 293758976,
+        "ks_inner_product_sum": 111356672,
+        "ks_inner_product_hoisted": 179894400,
+        "giant_final": 11640832,
+        "ks_intt_modup": 47821312,
+        "ks_intt_moddown": 45346560,
+        "ks_inner_product": 24222464,
+        "ntt_fwd": 6666240,
+        "ntt_inv": 8515584,
+        "ks_moddown_u": 9221632,
+        "relin_final": 12823552,
+        "rescale_final": 9583296,
+        "ks_moddown_convert": 70903125
     },
 }
 VALU_ISSUE_PEAK_G = 1024 * 2.4e9 / 4 / 1e9
@@ -757,6 +772,7 @@ def main():
 
     work = kernel_work()
     kernels = {}
+    sq_valid = csrc_sha() == MEASURED_SQ["source_sha"]
     for name, (cnt, tot, mn, mx) in prof.items():
         avg = tot / cnt
         w = work.get(name, {})
@@ -769,6 +785,9 @@ def main():
         if "products" in w:
             row["algo_Tproducts"] = w["products"] / (per_step * 1e-3) / 1e12
             row["algo_int8_TOPs"] = row["algo_Tproducts"] * I8_OPS_PER_PRODUCT
+        if sq_valid and name in MEASURED_SQ["valu_per_launch"]:
+            # counted VALU instructions per launch over this run's mean launch time
+            row["valu_issue"] = MEASURED_SQ["valu_per_launch"][name] / (avg * 1e-3) / 1e9 / VALU_ISSUE_PEAK_G
         kernels[name] = row
     for name in ("ntt_fwd", "ntt_inv"):
         if name in kernels:

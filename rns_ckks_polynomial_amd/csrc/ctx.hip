@@ -173,6 +173,7 @@ extern "C" int ckks_ctx_create(ckks_ctx **out, const ckks_params *params, int de
             c->psi[g] = host::min_root(n, c->primes[g]);
             host::prime_tables(n, c->primes[g], c->psi[g], pc[g], twf.data() + (size_t)g * n * 2,
                                twi.data() + (size_t)g * n * 2, iota[g]);
+            if (n == 2048) host::ntt2048_twiddle_order(twf.data() + (size_t)g * n * 2, twi.data() + (size_t)g * n * 2);
         }
         c->d_pc = dev_upload(pc, c->owned, &err);
         c->d_tw_fwd = dev_upload(twf, c->owned, &err);

@@ -105,6 +105,22 @@ void prime_tables(uint32_t n, uint64_t q, uint64_t psi, PrimeConsts &k, uint64_t
     }
 }
 
+static void permute_stage(uint64_t *tw, uint32_t s) {
+    const uint32_t c = 1u << (s - 8);
+    std::vector<uint64_t> old(tw + 2 * (1u << s), tw + 4 * (1u << s));
+    for (uint32_t t = 0; t < 256; t++)
+        for (uint32_t h = 0; h < c; h++)
+            for (uint32_t w = 0; w < 2; w++) tw[2 * ((1u << s) + c * t + h) + w] = old[2 * (c * bitrev(t, 8) + h) + w];
+}
+
+void ntt2048_twiddle_order(uint64_t *tf, uint64_t *ti) {
+    permute_stage(tf, 9);
+    permute_stage(tf, 10);
+    permute_stage(ti, 8);
+    permute_stage(ti, 9);
+    permute_stage(ti, 10);
+}
+
 // Little-endian multi-word helpers for (B-1)/2 in mixed radix.
 static void big_mul(std::vector<uint64_t> &a, uint64_t m) {
     h128 c = 0;

@@ -53,6 +53,13 @@ inline uint64_t digit_form(uint64_t v) { return (v + 0x8080808080808080ull) ^ 0x
 void prime_tables(uint32_t n, uint64_t q, uint64_t psi, PrimeConsts &pc, uint64_t *tw_fwd, uint64_t *tw_inv,
                   uint64_t &iota);
 
+// Entry order of the n = 2048 tables read by the one-workgroup transform.  In the
+// register pass next to the natural-order side (forward stages s = 9, 10; inverse
+// stages s = 8, 9, 10) thread t runs the bit-reversed indices 8 brev8(t) + k, so the
+// heap entry 2^s + c brev8(t) + h (c = 2^(s-8), h < c) is stored at 2^s + c t + h: each
+// thread's twiddles stay a contiguous run.  The other stages keep the heap order.
+void ntt2048_twiddle_order(uint64_t *tw_fwd, uint64_t *tw_inv);
+
 // Exact base conversion from the primes [first, first + m) of the chain
 // (L main primes, then K special primes) to other chain primes.
 struct BasisTables {

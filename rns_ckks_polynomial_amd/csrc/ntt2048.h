@@ -10,9 +10,13 @@
 // registers between LDS exchanges:
 //   forward  (merged-psi Cooley-Tukey, bits high -> low): [10 9 8] [7 6 5] [4 3 2] [1 0]
 //   inverse  (merged-psi Gentleman-Sande, bits low -> high): [0 1 2] [3 4 5] [6 7 8] [9 10]
-// The merged-psi forward leaves the result in bit-reversed order; the final
-// LDS exchange writes it back in natural order (and the inverse reads its
-// input through the same permutation), so no separate reorder pass exists.
+// The merged-psi forward works in bit-reversed order.  In the register pass
+// next to the natural-order side (the forward's last, the inverse's first)
+// thread t takes the bit-reversed indices 8 brev8(t) + k, which sit at the
+// natural positions t + 256 brev3(k): the order change is a renaming of
+// registers, with no LDS exchange of its own.  The twiddles of those passes'
+// stages are stored permuted to match (host::ntt2048_twiddle_order), so their
+// twiddle reads stay the same contiguous runs.
 // Twiddles are Shoup pairs (w, floor(w 2^64/q)) of psi^bitrev(k) (forward) and
 // psi^-bitrev(k) (inverse), interleaved [k][2].  Butterflies are Harvey's lazy
 // forms with a truncated Shoup quotient (see shoup_lazy4): the twiddle product
@@ -43,7 +47,17 @@ __device__ __forceinline__ int own(int t, int k) {
     return (t & ((1 << C) - 1)) | (k << C) | ((t >> C) << (C + 3));
 }
 
-__device__ __forceinline__ constexpr int brev(int i) { return (int)(__builtin_bitreverse32((uint32_t)i) >> (32 - LOGN)); }
+__device__ __forceinline__ constexpr int brev8(int i) { return (int)(__builtin_bitreverse32((uint32_t)i) >> 24); }
+__device__ __forceinline__ constexpr int brev3(int k) { return ((k & 1) << 2) | (k & 2) | ((k >> 2) & 1); }
+
+// v[k] <- v[brev3(k)] (an involution): a compile-time renaming of registers.
+__device__ __forceinline__ void swap_brev3(uint64_t (&v)[E]) {
+    const uint64_t t1 = v[1], t3 = v[3];
+    v[1] = v[4];
+    v[4] = t1;
+    v[3] = v[6];
+    v[6] = t3;
+}
 
 // One radix-2 stage (bit BIT of the index) on the 8 registers of a pass owning bits [C, C+3).
 template <int C, int BIT, bool INV, int RED = 4>
@@ -77,6 +91,7 @@ __device__ __forceinline__ void from_lds(const uint64_t *lds, uint64_t (&v)[E], 
 
 // Forward NTT.  On entry v[k] = a[t + 256 k] (natural order, values < 4q);
 // on exit v[k] = A[t + 256 k] in [0, 24q) (reduce_out finishes).  Uses lds[LDS_WORDS]; ends with a barrier.
+// tw: the prime's forward table in the order of host::ntt2048_twiddle_order.
 // Bounds: a stage without reduction maps inputs below B q to outputs below (B + 4) q.
 // From below 4q, six stages run unreduced (below 28q); the first stage of each of the
 // last two register passes reduces its top input below 16q, so no value reaches 28q
@@ -103,43 +118,31 @@ __device__ __forceinline__ void fwd(uint64_t (&v)[E], uint64_t *lds, const uint6
     __syncthreads();
     to_lds<2>(lds, v, t);
     __syncthreads();
-    from_lds<0>(lds, v, t);
+    // thread t takes the indices 8 brev8(t) + k (the stages' twiddle index uses t: the
+    // table's stage-9 and stage-10 entries are stored in that order)
+    from_lds<0>(lds, v, brev8(t));
     stage<0, 1, false, 16>(v, t, tw, q);   // a < 16q, < 20q
     stage<0, 0, false, 0>(v, t, tw, q);    //          < 24q
-    __syncthreads();
-    // coefficient own<0>(t,k) = 8t + k now holds A_{brev(8t+k)}: write back in natural order
-    // (brev(8t + k) = brev(8t) | brev(k))
-    {
-        uint64_t *b = lds + slot(brev(8 * t));
-#pragma unroll
-        for (int k = 0; k < E; k++) b[slot(brev(k))] = v[k];
-    }
-    __syncthreads();
-    {
-        const uint64_t *b = lds + slot(t);
-#pragma unroll
-        for (int k = 0; k < E; k++) v[k] = b[slot(NT * k)];
-    }
+    // v[k] holds A_{brev11(8 brev8(t) + k)} = A_{t + 256 brev3(k)}
+    swap_brev3(v);
     __syncthreads();
 }
 
 // Inverse NTT without the final n^-1 scaling.  On entry v[k] = A[t + 256 k]
-// (values < 4q); on exit v[k] = n a[t + 256 k] in [0, 4q).
+// (values < 4q); on exit v[k] = n a[t + 256 k] in [0, 4q).  lds must be free on entry
+// (its first access is a write); ends with a barrier.  tw: the prime's inverse table in
+// the order of host::ntt2048_twiddle_order.
 __device__ __forceinline__ void inv(uint64_t (&v)[E], uint64_t *lds, const uint64_t *__restrict__ tw, uint64_t qv) {
     const int t = threadIdx.x;
     const BfConsts q = bf_consts(qv);
-    {
-        uint64_t *b = lds + slot(brev(t));  // brev(t + 256 k) = brev(t) | brev(256 k)
-#pragma unroll
-        for (int k = 0; k < E; k++) b[slot(brev(NT * k))] = v[k];
-    }
-    __syncthreads();
-    from_lds<0>(lds, v, t);
+    // thread t takes the bit-reversed indices 8 brev8(t) + k, at the natural positions
+    // t + 256 brev3(k): v[brev3(k)] (the stages' twiddle index uses t: the table's stage-8, -9
+    // and -10 entries are stored in that order)
+    swap_brev3(v);
     stage<0, 0, true>(v, t, tw, q);
     stage<0, 1, true>(v, t, tw, q);
     stage<0, 2, true>(v, t, tw, q);
-    __syncthreads();
-    to_lds<0>(lds, v, t);
+    to_lds<0>(lds, v, brev8(t));
     __syncthreads();
     from_lds<3>(lds, v, t);
     stage<3, 3, true>(v, t, tw, q);

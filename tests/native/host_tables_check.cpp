@@ -66,6 +66,25 @@ static void check_prime_tables(uint32_t n, uint64_t q) {
         CHECK(tf[2 * k + 1] == shoup_ref(tf[2 * k], q), "forward Shoup %u", k);
         CHECK(mm(tf[2 * k], ti[2 * k], q) == 1 && ti[2 * k + 1] == shoup_ref(ti[2 * k], q), "inverse twiddle %u", k);
     }
+    if (n != 2048) return;
+    // the one-workgroup transform's order: stage s entries (s = 9, 10 forward; 8, 9, 10 inverse) at
+    // 2^s + c t + h hold the heap entries 2^s + c brev8(t) + h, c = 2^(s-8); every other entry stays
+    std::vector<uint64_t> pf(tf), pi(ti);
+    host::ntt2048_twiddle_order(pf.data(), pi.data());
+    for (uint32_t k = 0; k < n; k++) {
+        uint32_t s = 0;
+        while (k >> (s + 1)) s++;
+        uint32_t hf = k, hi = k;
+        if (k >= 256) {
+            const uint32_t c = 1u << (s - 8), t = (k - (1u << s)) / c, h = (k - (1u << s)) % c;
+            uint32_t bt = 0;
+            for (uint32_t b = 0; b < 8; b++) bt |= ((t >> b) & 1u) << (7 - b);
+            hi = (1u << s) + c * bt + h;
+            if (s >= 9) hf = hi;
+        }
+        CHECK(pf[2 * k] == tf[2 * hf] && pf[2 * k + 1] == tf[2 * hf + 1], "n = 2048 forward order %u", k);
+        CHECK(pi[2 * k] == ti[2 * hi] && pi[2 * k + 1] == ti[2 * hi + 1], "n = 2048 inverse order %u", k);
+    }
 }
 
 static void check_basis(const std::vector<uint64_t> &primes, uint32_t L, uint32_t K, uint32_t first, uint32_t m,
